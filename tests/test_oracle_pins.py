@@ -1,0 +1,486 @@
+"""Pins of the fp64 oracle against things other than itself (CPU only).
+
+Each routine in ``oracle`` is checked against an independent source of truth:
+hand-derived examples, PyTorch autograd + torch.optim.SGD running the inner
+loop the pages describe, brute-force O(L^2) sums, exact integer arithmetic,
+invariances (chunk size, causality, linearity) and tree-shaped scans.  The
+checks are chosen so that a dropped term, a sign flip, an exclusive/inclusive
+mix-up or a transposed state fails at least one of them.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+RNG = np.random.default_rng(12345)
+
+
+def rnd(*shape, rng=RNG):
+    return rng.standard_normal(shape)
+
+
+def small_case(B=2, H=3, L=37, dk=5, dv=7, beta=0.0, rng=RNG, s0=True, m0=False):
+    q, k, v = rnd(B, H, L, dk, rng=rng), rnd(B, H, L, dk, rng=rng), rnd(B, H, L, dv, rng=rng)
+    eta = rng.uniform(0.01, 0.2, (B, H, L))
+    S0 = rnd(B, H, dk, dv, rng=rng) * 0.1 if s0 else None
+    M0 = rnd(B, H, dk, dv, rng=rng) * 0.1 if m0 else None
+    return q, k, v, eta, S0, M0
+
+
+def close(a, b, tol=1e-12):
+    a, b = np.asarray(a), np.asarray(b)
+    scale = max(1.0, float(np.abs(b).max()))
+    assert np.abs(a - b).max() <= tol * scale, float(np.abs(a - b).max())
+
+
+# ----------------------------------------------------------------- golden (hand)
+def _golden():
+    with open(os.path.join(HERE, "golden", "hand_examples.json"), encoding="utf-8") as f:
+        return json.load(f)
+
+
+def test_golden_la_inclusive(oracle_mod):
+    g = _golden()["la_inclusive_2x2"]
+    a = lambda x: np.array(x, dtype=np.float64)[None, None]
+    out, Sf, _ = oracle_mod.token_causal(a(g["q"]), a(g["k"]), a(g["v"]), None, g["eta"], g["beta"])
+    assert np.array_equal(out[0, 0], np.array(g["out"], float))
+    assert np.array_equal(Sf[0, 0], np.array(g["S_final"], float))
+
+
+def test_golden_momentum_scalar(oracle_mod):
+    g = _golden()["momentum_scalar"]
+    a = lambda x: np.array(x, dtype=np.float64)[None, None]
+    out, Sf, Mf = oracle_mod.token_causal(a(g["q"]), a(g["k"]), a(g["v"]), None, g["eta"], g["beta"])
+    assert np.array_equal(out[0, 0], np.array(g["out"], float))
+    assert np.array_equal(Sf[0, 0], np.array(g["S_final"], float))
+    assert np.array_equal(Mf[0, 0], np.array(g["M_final"], float))
+    bf = oracle_mod.bruteforce_token_causal(a(g["q"]), a(g["k"]), a(g["v"]), None, g["eta"], g["beta"])
+    assert np.array_equal(bf[0, 0], np.array(g["out"], float))
+
+
+def test_golden_dual_minibatch(oracle_mod):
+    g = _golden()["dual_minibatch_scalar"]
+    a = lambda x: np.array(x, dtype=np.float64)[None, None]
+    out, Wf = oracle_mod.dual_primal(a(g["q"]), a(g["k"]), a(g["v"]), a(g["W0"]), g["eta"], g["minibatch"])
+    assert np.array_equal(out[0, 0], np.array(g["out"], float))
+    assert np.array_equal(Wf[0, 0], np.array(g["W_final"], float))
+    out2, Wf2 = oracle_mod.dual_form_matrix(a(g["q"]), a(g["k"]), a(g["v"]), a(g["W0"]), g["eta"], g["minibatch"])
+    assert np.array_equal(out2[0, 0], np.array(g["out"], float))
+
+
+# ------------------------------------------------------- autograd inner loop
+def _sgd_inner_loop(q, k, v, eta, beta, S0):
+    """Run the inner loop with torch autograd + torch.optim.SGD: inner model
+    f(x) = x W (linear, no bias), binding loss l_t = -eta_t <f(k_t), v_t>,
+    one SGD step per token (lr 1, momentum beta, no dampening), output read
+    from the updated model."""
+    L = q.shape[0]
+    W = torch.nn.Parameter(torch.tensor(S0, dtype=torch.float64).clone())
+    opt = torch.optim.SGD([W], lr=1.0, momentum=beta, dampening=0.0)
+    outs = []
+    for t in range(L):
+        opt.zero_grad()
+        kt = torch.tensor(k[t], dtype=torch.float64)[None]
+        vt = torch.tensor(v[t], dtype=torch.float64)[None]
+        loss = -float(eta[t]) * (kt @ W * vt).sum()
+        loss.backward()
+        opt.step()
+        with torch.no_grad():
+            outs.append((torch.tensor(q[t], dtype=torch.float64)[None] @ W)[0].numpy().copy())
+    return np.stack(outs), W.detach().numpy()
+
+
+def test_one_step_identity(oracle_mod):
+    """[P1] one gradient step of a bias-free linear last layer: o = q (S0 + k^T v)."""
+    rng = np.random.default_rng(7)
+    dk, dv = 6, 4
+    q, k, v, S0 = rnd(1, dk, rng=rng), rnd(1, dk, rng=rng), rnd(1, dv, rng=rng), rnd(dk, dv, rng=rng)
+    o_sgd, _ = _sgd_inner_loop(q, k, v, np.ones(1), 0.0, S0)
+    out, _, _ = oracle_mod.token_causal(q[None, None], k[None, None], v[None, None], None, 1.0, 0.0,
+                                        S0[None, None])
+    close(out[0, 0], o_sgd, 1e-13)
+    close(out[0, 0, 0], q[0] @ (S0 + np.outer(k[0], v[0])), 1e-13)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_recurrence_is_sgd_inner_loop(oracle_mod, beta):
+    """Per-token SGD (with momentum) on the binding loss == the oracle recurrence."""
+    rng = np.random.default_rng(11)
+    L, dk, dv = 9, 5, 3
+    q, k, v = rnd(L, dk, rng=rng), rnd(L, dk, rng=rng), rnd(L, dv, rng=rng)
+    eta = rng.uniform(0.05, 0.5, L)
+    S0 = rnd(dk, dv, rng=rng)
+    o_sgd, W_sgd = _sgd_inner_loop(q, k, v, eta, beta, S0)
+    out, Sf, _ = oracle_mod.token_causal(q[None, None], k[None, None], v[None, None], eta[None, None],
+                                         0.0, beta, S0[None, None])
+    close(out[0, 0], o_sgd, 1e-12)
+    close(Sf[0, 0], W_sgd, 1e-12)
+
+
+def test_chunk_causal_is_per_chunk_sgd(oracle_mod):
+    """[P2] one gradient step per chunk; the updated weight serves the next chunk."""
+    rng = np.random.default_rng(5)
+    L, dk, dv, C = 23, 6, 4, 5
+    z, vh = rnd(L, dk, rng=rng), rnd(L, dv, rng=rng)
+    W0 = rnd(dk, dv, rng=rng)
+    eta = 0.03
+    W = torch.nn.Parameter(torch.tensor(W0).clone())
+    opt = torch.optim.SGD([W], lr=eta)
+    ref = np.empty((L, dv))
+    for c0 in range(0, L, C):
+        c1 = min(c0 + C, L)
+        zc, vc = torch.tensor(z[c0:c1]), torch.tensor(vh[c0:c1])
+        with torch.no_grad():
+            ref[c0:c1] = (zc @ W).numpy()
+        opt.zero_grad()
+        (-(zc @ W * vc).sum()).backward()
+        opt.step()
+    out, Wf = oracle_mod.chunk_causal(z[None, None], z[None, None], vh[None, None], None, eta,
+                                      W0[None, None], C)
+    close(out[0, 0], ref, 1e-12)
+    close(Wf[0, 0], W.detach().numpy(), 1e-12)
+
+
+def test_dual_is_minibatch_sgd(oracle_mod):
+    """[P4] mini-batch TTT-Linear: every gradient of mini-batch n at W_n; the
+    output of token t uses the gradient of the mini-batch prefix up to t."""
+    rng = np.random.default_rng(9)
+    L, d, dv, b = 11, 4, 3, 4
+    q, k, v = rnd(L, d, rng=rng), rnd(L, d, rng=rng), rnd(L, dv, rng=rng)
+    W0 = rnd(d, dv, rng=rng)
+    eta = 0.07
+    Wn = torch.tensor(W0)
+    ref = np.empty((L, dv))
+    for n0 in range(0, L, b):
+        n1 = min(n0 + b, L)
+        for t in range(n0, n1):
+            W = Wn.clone().requires_grad_(True)
+            kk, vv = torch.tensor(k[n0:t + 1]), torch.tensor(v[n0:t + 1])
+            (0.5 * ((kk @ W - vv) ** 2).sum()).backward()
+            ref[t] = (torch.tensor(q[t])[None] @ (Wn - eta * W.grad))[0].numpy()
+        W = Wn.clone().requires_grad_(True)
+        kk, vv = torch.tensor(k[n0:n1]), torch.tensor(v[n0:n1])
+        (0.5 * ((kk @ W - vv) ** 2).sum()).backward()
+        Wn = (Wn - eta * W.grad).detach()
+    out, Wf = oracle_mod.dual_primal(q[None, None], k[None, None], v[None, None], W0[None, None], eta, b)
+    close(out[0, 0], ref, 1e-12)
+    close(Wf[0, 0], Wn.numpy(), 1e-12)
+
+
+def test_dual_b1_is_online_sgd(oracle_mod):
+    """Mini-batch size 1 is plain per-token SGD on 1/2||kW - v||^2 (torch.optim.SGD)."""
+    rng = np.random.default_rng(21)
+    L, d, dv = 10, 5, 5
+    q, k, v = rnd(L, d, rng=rng), rnd(L, d, rng=rng), rnd(L, dv, rng=rng)
+    W0 = rnd(d, dv, rng=rng)
+    eta = 0.05
+    W = torch.nn.Parameter(torch.tensor(W0).clone())
+    opt = torch.optim.SGD([W], lr=eta)
+    ref = []
+    for t in range(L):
+        opt.zero_grad()
+        (0.5 * ((torch.tensor(k[t])[None] @ W - torch.tensor(v[t])[None]) ** 2).sum()).backward()
+        opt.step()
+        with torch.no_grad():
+            ref.append((torch.tensor(q[t])[None] @ W)[0].numpy().copy())
+    out, _ = oracle_mod.dual_primal(q[None, None], k[None, None], v[None, None], W0[None, None], eta, 1)
+    close(out[0, 0], np.stack(ref), 1e-12)
+
+
+# ------------------------------------------------------------- brute force forms
+@pytest.mark.parametrize("beta", [0.0, 0.5, 0.9])
+def test_recurrence_vs_bruteforce(oracle_mod, beta):
+    q, k, v, eta, S0, M0 = small_case(beta=beta, m0=beta != 0.0)
+    out, _, _ = oracle_mod.token_causal(q, k, v, eta, 0.0, beta, S0, M0)
+    bf = oracle_mod.bruteforce_token_causal(q, k, v, eta, 0.0, beta, S0, M0)
+    close(out, bf, 1e-12)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+@pytest.mark.parametrize("C", [1, 2, 3, 8, 16, 37, 64])
+def test_chunk_size_invariance(oracle_mod, beta, C):
+    """Token-causal output and final state do not depend on the chunk size
+    (C = 1 is the recurrence, C >= L the brute force); ragged tails included."""
+    q, k, v, eta, S0, M0 = small_case(L=37, beta=beta, m0=beta != 0.0)
+    out, Sf, Mf = oracle_mod.token_causal(q, k, v, eta, 0.0, beta, S0, M0)
+    oc, Sc, Mc = oracle_mod.chunked_token_causal(q, k, v, eta, 0.0, beta, S0, M0, C)
+    close(oc, out, 1e-12)
+    close(Sc, Sf, 1e-12)
+    if beta != 0.0:
+        close(Mc, Mf, 1e-12)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_exact_integer_arithmetic(oracle_mod, beta):
+    """Integer q,k,v in {-2..2}, eta = 1/8, dyadic beta: every product and sum
+    is exact, so recurrence, brute force and chunked forms agree bit for bit."""
+    rng = np.random.default_rng(3)
+    B, H, L, dk, dv = 1, 2, 24, 4, 3
+    q = rng.integers(-2, 3, (B, H, L, dk)).astype(float)
+    k = rng.integers(-2, 3, (B, H, L, dk)).astype(float)
+    v = rng.integers(-2, 3, (B, H, L, dv)).astype(float)
+    S0 = rng.integers(-2, 3, (B, H, dk, dv)).astype(float)
+    out, Sf, _ = oracle_mod.token_causal(q, k, v, None, 0.125, beta, S0)
+    bf = oracle_mod.bruteforce_token_causal(q, k, v, None, 0.125, beta, S0)
+    assert np.array_equal(out, bf)
+    for C in (1, 5, 8, 24):
+        oc, Sc, _ = oracle_mod.chunked_token_causal(q, k, v, None, 0.125, beta, S0, None, C)
+        assert np.array_equal(oc, out)
+        assert np.array_equal(Sc, Sf)
+
+
+def test_causality_and_linearity(oracle_mod):
+    q, k, v, eta, S0, _ = small_case(L=20)
+    out, _, _ = oracle_mod.token_causal(q, k, v, eta, 0.0, 0.9, S0)
+    t = 11
+    k2, v2 = k.copy(), v.copy()
+    k2[:, :, t] += 1.0
+    v2[:, :, t] -= 2.0
+    out2, _, _ = oracle_mod.token_causal(q, k2, v2, eta, 0.0, 0.9, S0)
+    assert np.array_equal(out2[:, :, :t], out[:, :, :t])
+    assert np.abs(out2[:, :, t] - out[:, :, t]).max(axis=-1).min() > 0
+    # linear in V with S0 = 0; affine in S0: O(S0) - O(0) = Q S0
+    o1, _, _ = oracle_mod.token_causal(q, k, v, eta, 0.0, 0.9, None)
+    o3, _, _ = oracle_mod.token_causal(q, k, 3.0 * v, eta, 0.0, 0.9, None)
+    close(o3, 3.0 * o1, 1e-12)
+    close(out - o1, q @ S0, 1e-12)
+
+
+def test_state_isolation_between_heads(oracle_mod):
+    """[P4] states of different sequences in a batch do not mix."""
+    q, k, v, eta, S0, _ = small_case()
+    out, _, _ = oracle_mod.token_causal(q, k, v, eta, 0.0, 0.0, S0)
+    v2 = v.copy()
+    v2[1, 2] += 5.0
+    out2, _, _ = oracle_mod.token_causal(q, k, v2, eta, 0.0, 0.0, S0)
+    diff = np.abs(out2 - out).reshape(2, 3, -1).max(-1)
+    assert diff[1, 2] > 0 and np.count_nonzero(diff) == 1
+
+
+# ------------------------------------------------------------------- state scan
+def _scan_oracle_inputs(oracle_mod, beta, L=37, C=8):
+    q, k, v, eta, S0, M0 = small_case(L=L, beta=beta, m0=beta != 0.0)
+    dS, dM = oracle_mod.chunk_aggregates(k, v, eta, 0.0, beta, C)
+    return q, k, v, eta, S0, M0, dS, dM
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_chunk_aggregates_are_zero_start_recurrence(oracle_mod, beta):
+    """dS_c, dM_c = change of (S, m) over chunk c started from zero (run the
+    token recurrence on the chunk alone)."""
+    q, k, v, eta, S0, M0, dS, dM = _scan_oracle_inputs(oracle_mod, beta)
+    C, L = 8, 37
+    for c in range(dS.shape[2]):
+        c0, c1 = c * C, min(c * C + C, L)
+        _, Sf, Mf = oracle_mod.token_causal(q[:, :, c0:c1], k[:, :, c0:c1], v[:, :, c0:c1],
+                                            eta[:, :, c0:c1], 0.0, beta)
+        close(dS[:, :, c], Sf, 1e-12)
+        if beta != 0.0:
+            close(dM[:, :, c], Mf, 1e-12)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_scan_equals_recurrence_at_chunk_starts(oracle_mod, beta):
+    """[P2] the prefix combination of independent chunk updates equals the
+    sequential update: exclusive scan states = recurrence states after c*C tokens."""
+    q, k, v, eta, S0, M0, dS, dM = _scan_oracle_inputs(oracle_mod, beta)
+    C, L = 8, 37
+    Se, Me, Sf, Mf = oracle_mod.state_scan(dS, dM, beta, C, L, S0, M0)
+    for c in range(1, dS.shape[2]):
+        _, Sr, Mr = oracle_mod.token_causal(q[:, :, :c * C], k[:, :, :c * C], v[:, :, :c * C],
+                                            eta[:, :, :c * C], 0.0, beta, S0, M0)
+        close(Se[:, :, c], Sr, 1e-12)
+        if beta != 0.0:
+            close(Me[:, :, c], Mr, 1e-12)
+    close(Se[:, :, 0], S0, 0)
+    _, Sr, Mr = oracle_mod.token_causal(q, k, v, eta, 0.0, beta, S0, M0)
+    close(Sf, Sr, 1e-12)
+    if beta != 0.0:
+        close(Mf, Mr, 1e-12)
+
+
+def _affine_op(x, y, alpha_y, gamma_y):
+    """Compose chunk transition x then y; element = (dS, dM, alpha, gamma)."""
+    dSx, dMx, ax, gx = x
+    dSy, dMy, ay, gy = y
+    return (dSx + ay * dMx + dSy, gy * dMx + dMy, ax + ay * gx, gx * gy)
+
+
+def _tree_scans(elems):
+    """Hillis-Steele inclusive and Blelloch exclusive scans over a list of
+    chunk transitions (test-local, written from the textbook algorithms)."""
+    n = len(elems)
+    hs = list(elems)
+    step = 1
+    while step < n:
+        hs = [hs[i] if i < step else _affine_op(hs[i - step], hs[i], None, None) for i in range(n)]
+        step *= 2
+    size = 1
+    while size < n:
+        size *= 2
+    ident = (0.0 * elems[0][0], 0.0 * elems[0][1], 0.0, 1.0)
+    a = list(elems) + [ident] * (size - n)
+    d = 1
+    while d < size:
+        for i in range(2 * d - 1, size, 2 * d):
+            a[i] = _affine_op(a[i - d], a[i], None, None)
+        d *= 2
+    a[size - 1] = ident
+    d = size // 2
+    while d >= 1:
+        for i in range(2 * d - 1, size, 2 * d):
+            t = a[i - d]
+            a[i - d] = a[i]
+            a[i] = _affine_op(a[i], t, None, None)
+        d //= 2
+    return hs, a[:n]
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_scan_equals_tree_scans(oracle_mod, beta):
+    rng = np.random.default_rng(17)
+    B, H, L, C, dk, dv = 1, 1, 45, 4, 3, 2
+    N = (L + C - 1) // C
+    dS, dM = rnd(B, H, N, dk, dv, rng=rng), rnd(B, H, N, dk, dv, rng=rng)
+    S0, M0 = rnd(B, H, dk, dv, rng=rng), rnd(B, H, dk, dv, rng=rng)
+    Se, Me, Sf, Mf = oracle_mod.state_scan(dS, dM, beta, C, L, S0, M0)
+    elems = []
+    for c in range(N):
+        n = min(C, L - c * C)
+        alpha = sum(beta ** i for i in range(1, n + 1))
+        elems.append((dS[0, 0, c], dM[0, 0, c], alpha, beta ** n))
+    start = (S0[0, 0], M0[0, 0], 0.0, 0.0)
+    hs, bl = _tree_scans(elems)
+    for c in range(N):
+        ex = _affine_op(start, bl[c], None, None)
+        close(Se[0, 0, c], ex[0], 1e-13)
+        close(Me[0, 0, c], ex[1], 1e-13)
+    inc = _affine_op(start, hs[-1], None, None)
+    close(Sf[0, 0], inc[0], 1e-13)
+    close(Mf[0, 0], inc[1], 1e-13)
+
+
+def test_scan_integer_exact_and_plain_prefix_sum(oracle_mod):
+    """beta = 0: the scan is a plain exclusive prefix sum (bit-exact on integers)."""
+    rng = np.random.default_rng(2)
+    dS = rng.integers(-9, 10, (2, 2, 13, 3, 4)).astype(float)
+    S0 = rng.integers(-9, 10, (2, 2, 3, 4)).astype(float)
+    Se, _, Sf, _ = oracle_mod.state_scan(dS, None, 0.0, 16, 13 * 16, S0)
+    ref = np.concatenate([np.zeros_like(dS[:, :, :1]), np.cumsum(dS, axis=2)[:, :, :-1]], axis=2)
+    assert np.array_equal(Se, ref + S0[:, :, None])
+    assert np.array_equal(Sf, S0 + dS.sum(axis=2))
+
+
+def test_scan_split_composes(oracle_mod):
+    """Scanning the first chunks, then the rest from that final state, equals
+    one scan (the chunk transitions compose associatively)."""
+    rng = np.random.default_rng(8)
+    C, L = 6, 60
+    N = L // C
+    dS, dM = rnd(1, 2, N, 3, 3, rng=rng), rnd(1, 2, N, 3, 3, rng=rng)
+    S0, M0 = rnd(1, 2, 3, 3, rng=rng), rnd(1, 2, 3, 3, rng=rng)
+    Se, Me, Sf, Mf = oracle_mod.state_scan(dS, dM, 0.9, C, L, S0, M0)
+    h = 4
+    _, _, S1, M1 = oracle_mod.state_scan(dS[:, :, :h], dM[:, :, :h], 0.9, C, h * C, S0, M0)
+    Se2, Me2, S2, M2 = oracle_mod.state_scan(dS[:, :, h:], dM[:, :, h:], 0.9, C, L - h * C, S1, M1)
+    close(Se2, Se[:, :, h:], 1e-13)
+    close(S2, Sf, 1e-13)
+    close(M2, Mf, 1e-13)
+
+
+# ---------------------------------------------------------------- chunk-causal
+def test_chunk_causal_vs_bruteforce(oracle_mod):
+    rng = np.random.default_rng(4)
+    B, H, L, dk, dv, C = 2, 2, 50, 6, 5, 8
+    q, k, v = rnd(B, H, L, dk, rng=rng), rnd(B, H, L, dk, rng=rng), rnd(B, H, L, dv, rng=rng)
+    eta = rng.uniform(0.0, 0.1, (B, H, L))
+    S0 = rnd(B, H, dk, dv, rng=rng)
+    out, Wf = oracle_mod.chunk_causal(q, k, v, eta, 0.0, S0, C)
+    close(out, oracle_mod.bruteforce_chunk_causal(q, k, v, eta, 0.0, S0, C), 1e-12)
+    # the final state equals the token-causal final state (same update, other readout)
+    _, Sf, _ = oracle_mod.token_causal(q, k, v, eta, 0.0, 0.0, S0)
+    close(Wf, Sf, 1e-12)
+    # first chunk reads only S0; eta = 0 gives a plain product
+    close(out[:, :, :C], q[:, :, :C] @ S0, 1e-13)
+    o0, _ = oracle_mod.chunk_causal(q, k, v, None, 0.0, S0, C)
+    close(o0, q @ S0, 1e-13)
+
+
+def test_chunk_causal_C1_is_exclusive_recurrence(oracle_mod):
+    """C = 1: o_t = q_t S_{t-1}, with S_{t-1} the token recurrence after t tokens."""
+    rng = np.random.default_rng(6)
+    L, dk, dv = 9, 4, 3
+    q, k, v = rnd(1, 1, L, dk, rng=rng), rnd(1, 1, L, dk, rng=rng), rnd(1, 1, L, dv, rng=rng)
+    S0 = rnd(1, 1, dk, dv, rng=rng)
+    out, _ = oracle_mod.chunk_causal(q, k, v, None, 0.3, S0, 1)
+    for t in range(L):
+        if t == 0:
+            S = S0
+        else:
+            _, S, _ = oracle_mod.token_causal(q[:, :, :t], k[:, :, :t], v[:, :, :t], None, 0.3, 0.0, S0)
+        close(out[0, 0, t], q[0, 0, t] @ S[0, 0], 1e-12)
+
+
+def test_chunk_causal_rows(oracle_mod):
+    rng = np.random.default_rng(10)
+    L, dk, dv, C = 70, 8, 5, 16
+    z, vh = rnd(L, dk, rng=rng), rnd(L, dv, rng=rng)
+    W0 = rnd(dk, dv, rng=rng)
+    out, _ = oracle_mod.chunk_causal(z[None, None], z[None, None], vh[None, None], None, 0.01,
+                                     W0[None, None], C)
+    rows = np.array([0, 5, 15, 16, 33, 47, 48, 69])
+    got = oracle_mod.chunk_causal_rows(z, z, vh, rows, 0.01, W0, C, block=7)
+    close(got, out[0, 0, rows], 1e-12)
+
+
+# ------------------------------------------------------------------- dual form
+@pytest.mark.parametrize("b", [1, 3, 4, 16, 40])
+def test_dual_primal_vs_matrix_form(oracle_mod, b):
+    rng = np.random.default_rng(13)
+    B, H, L, d, dv = 2, 2, 37, 5, 6
+    q, k, v = rnd(B, H, L, d, rng=rng), rnd(B, H, L, d, rng=rng), rnd(B, H, L, dv, rng=rng)
+    W0 = rnd(B, H, d, dv, rng=rng)
+    out, Wf = oracle_mod.dual_primal(q, k, v, W0, 0.03, b)
+    out2, Wf2 = oracle_mod.dual_form_matrix(q, k, v, W0, 0.03, b)
+    close(out, out2, 1e-12)
+    close(Wf, Wf2, 1e-12)
+
+
+def test_dual_special_cases(oracle_mod):
+    rng = np.random.default_rng(14)
+    B, H, L, d = 1, 2, 20, 6
+    q, k = rnd(B, H, L, d, rng=rng), rnd(B, H, L, d, rng=rng)
+    W0 = np.broadcast_to(0.5 * np.eye(d), (B, H, d, d)).copy()
+    # fixed point: v = k W0 makes every gradient zero
+    out, Wf = oracle_mod.dual_primal(q, k, 0.5 * k, W0, 0.1, 4)
+    close(out, 0.5 * q, 0)
+    close(Wf, W0, 0)
+    # eta = 0 reads W0
+    v = rnd(B, H, L, d, rng=rng)
+    out, _ = oracle_mod.dual_primal(q, k, v, W0, 0.0, 4)
+    close(out, q @ W0, 1e-14)
+
+
+def test_dual_is_la_with_corrected_values(oracle_mod):
+    """Inside one mini-batch the dual form is token-causal linear attention that
+    starts from W_n with values -eta (k_s W_n - v_s); its end state is W_{n+1}.
+    Cross-checks the two C routines against each other."""
+    rng = np.random.default_rng(15)
+    L, d, dv, b, eta = 24, 5, 4, 8, 0.05
+    q, k, v = rnd(1, 1, L, d, rng=rng), rnd(1, 1, L, d, rng=rng), rnd(1, 1, L, dv, rng=rng)
+    W0 = rnd(1, 1, d, dv, rng=rng)
+    out, Wf = oracle_mod.dual_primal(q, k, v, W0, eta, b)
+    W = W0
+    for n0 in range(0, L, b):
+        sl = slice(n0, n0 + b)
+        vt = -eta * (k[:, :, sl] @ W - v[:, :, sl])
+        o, Wn, _ = oracle_mod.token_causal(q[:, :, sl], k[:, :, sl], vt, None, 1.0, 0.0, W)
+        close(o, out[:, :, sl], 1e-12)
+        # affine form of the mini-batch step
+        K, V = k[0, 0, sl], v[0, 0, sl]
+        close(Wn[0, 0], (np.eye(d) - eta * K.T @ K) @ W[0, 0] + eta * K.T @ V, 1e-12)
+        W = Wn
+    close(W, Wf, 1e-12)
