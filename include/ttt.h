@@ -1,0 +1,208 @@
+/*
+ * ttt.h -- C ABI of the MI355X (gfx950) chunked TTT fast-weight forward.
+ *
+ * The library computes the forward pass of a test-time-training fast-weight
+ * layer read as linear attention.  Per (batch b, head h) a state S (dk x dv,
+ * fp32) takes one gradient step per token or per chunk; outputs read the
+ * state.  Three entry points:
+ *
+ *   ttt_fwd_chunked       token-causal (optionally with momentum) and
+ *                         chunk-causal (In-Place TTT) forward
+ *   ttt_chunk_state_scan  the associative scan over per-chunk state deltas
+ *   ttt_dual_form_fwd     the non-associative TTT-Linear mini-batch update
+ *                         (MSE reconstruction loss), dual form
+ *
+ * Sources (cited by page title and paragraph or section):
+ *  [P1] "KV 바인딩 기반 테스트 시간 학습은 사실상 선형 어텐션이다"
+ *       (aitrends.kr/articles/4698)
+ *  [P2] "In-Place 테스트 시점 학습: LLM을 위한 원활한 동적 적응 프레임워크"
+ *       (aitrends.kr/articles/40879)
+ *  [P4] "RNN의 기억을 작은 모델로 바꾼다면: Test-Time Training 읽기" (ariser.io)
+ *  [P5] "LaCT (Large Chunk Test-Time Training)" (aisparkup.com/wiki/lact)
+ *
+ * Conventions shared by every entry point
+ *  - All pointers are DEVICE pointers (hipMalloc'd or equivalent) owned by the
+ *    caller; the library never allocates, frees or keeps a pointer after the
+ *    call returns.  Scratch memory comes in through `workspace`.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL =
+ *    the default stream).  Argument validation is synchronous and happens
+ *    before any launch: on any error nothing has been enqueued.
+ *  - Row vectors: q_t, k_t in R^dk, v_t, o_t in R^dv; S in R^{dk x dv}, stored
+ *    row-major (dv contiguous).  Activations are [B,H,L,d] tensors addressed
+ *    through element strides for the B, H and L dimensions; the last
+ *    dimension must be contiguous.
+ *  - Base pointers must be 16-byte aligned; the L strides of q, k, v and out
+ *    must be multiples of 8 elements (16 bytes of bf16); S0/M0/W0/S_final
+ *    etc. are contiguous [dk, dv] fp32 blocks per (b, h).
+ *  - `out` must not overlap any input.  q and k may be the same tensor.
+ *  - Errors never abort and never throw across the ABI; launch failures are
+ *    reported as TTT_ERR_HIP.  Calls on different streams with different
+ *    workspaces may run concurrently; the library has no global state.
+ */
+#ifndef TTT_MI355X_H
+#define TTT_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TTT_OK = 0,
+    TTT_ERR_NULL = 1,        /* a required pointer is NULL                       */
+    TTT_ERR_SHAPE = 2,       /* a size or stride is out of range / inconsistent  */
+    TTT_ERR_DTYPE = 3,       /* unknown dtype value                              */
+    TTT_ERR_ALIGN = 4,       /* pointer or stride misaligned                     */
+    TTT_ERR_UNSUPPORTED = 5, /* valid arguments this build has no kernel for     */
+    TTT_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
+    TTT_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed       */
+    TTT_ERR_ALIAS = 8,       /* out overlaps an input                            */
+    TTT_ERR_VALUE = 9        /* a scalar is out of range (beta not in [0,1), ...) */
+} ttt_status_t;
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype_t;
+
+typedef enum {
+    /* o_t reads the state after token t's own update: S_t = S_{t-1} + m_t,
+     * m_t = beta m_{t-1} + eta_t k_t^T v_t, o_t = q_t S_t.  The chunk length
+     * is only a tiling choice here: results do not depend on it. */
+    TTT_TOKEN_CAUSAL = 0,
+    /* In-Place TTT ([P2], paragraphs on the chunk-wise Wdown update and on
+     * the associative scan): token t of chunk i reads the state left by the
+     * previous chunks, o_t = q_t S_{i-1}, then S_i = S_{i-1} + K_i^T diag(eta_i) V_i.
+     * The chunk length is part of the semantics.  beta must be 0. */
+    TTT_CHUNK_CAUSAL = 1
+} ttt_mode_t;
+
+/* Arguments of ttt_fwd_chunked.  All strides are in elements. */
+typedef struct ttt_fwd_args {
+    int32_t B, H, L;          /* batch, heads, sequence length (L >= 1)          */
+    int32_t dk, dv;           /* key / value head dims                           */
+    int32_t chunk;            /* chunk length C >= 1                             */
+    int32_t mode;             /* ttt_mode_t                                      */
+    int32_t dtype;            /* ttt_dtype_t of q, k, v and out                  */
+    const void* q;            /* [B,H,L,dk]                                      */
+    const void* k;            /* [B,H,L,dk]                                      */
+    const void* v;            /* [B,H,L,dv]                                      */
+    int64_t q_stride[3];      /* strides of the B, H, L dims                     */
+    int64_t k_stride[3];
+    int64_t v_stride[3];
+    const float* eta;         /* [B,H,L] fp32 per-token step size, or NULL       */
+    int64_t eta_stride[3];    /* strides of eta (ignored when eta is NULL)       */
+    float eta_scalar;         /* step size of every token when eta == NULL       */
+    float beta;               /* momentum in [0,1); 0 = plain update             */
+    const float* S0;          /* [B,H,dk,dv] initial state, NULL = zero          */
+    int64_t S0_stride[2];     /* B, H strides of S0; 0 broadcasts                */
+    const float* M0;          /* [B,H,dk,dv] initial momentum, NULL = zero       */
+    int64_t M0_stride[2];
+    void* out;                /* [B,H,L,dv], dtype `dtype`                       */
+    int64_t out_stride[3];
+    float* S_final;           /* [B,H,dk,dv] contiguous, NULL = not written      */
+    float* M_final;           /* [B,H,dk,dv] contiguous, NULL = not written;
+                                 only written when beta != 0                    */
+    void* workspace;          /* device scratch, >= ttt_fwd_workspace_size bytes */
+    size_t workspace_bytes;
+    void* stream;             /* hipStream_t                                     */
+} ttt_fwd_args;
+
+/*
+ * ttt_fwd_chunked -- chunked forward of the fast-weight layer.
+ *
+ * TOKEN_CAUSAL ([P1], paragraphs on the state-matrix update, momentum SGD as
+ * weighted linear attention, associativity without weight normalisation,
+ * per-token rates folded into the values; [P4] section on the inner update
+ * rule): with g_t = eta_t k_t^T v_t,
+ *     m_t = beta m_{t-1} + g_t,  S_t = S_{t-1} + m_t,  o_t = q_t S_t,
+ * S_{-1} = S0, m_{-1} = M0.  Computed chunk by chunk: the readout of the
+ * state at the chunk start, a causal intra-chunk term, then the chunk's
+ * aggregate update; equal (up to rounding) to the per-token recurrence.
+ *
+ * CHUNK_CAUSAL ([P2]): o_t = q_t S_{i-1} for t in chunk i, then
+ *     S_i = S_{i-1} + K_i^T diag(eta_i) V_i.
+ * For the In-Place setting pass q = k = Z (activations), v = V-hat, S0 = W0.
+ *
+ * Precision: bf16 inputs are contracted on bf16 MFMA with fp32
+ * accumulation; the state is accumulated in fp32 and read through a bf16
+ * copy; out is rounded once to the input dtype.  fp32 inputs use fp32 MFMA
+ * end to end.
+ *
+ * Supported (else TTT_ERR_UNSUPPORTED): dk, dv in {32, 64, 128} for both
+ * dtypes and both modes; CHUNK_CAUSAL with bf16 also dk, dv multiples of 256
+ * (large fast weights, e.g. the In-Place Wdown) with chunk a multiple of 256.
+ * CHUNK_CAUSAL with small dims needs chunk a multiple of 64 (bf16) or 32
+ * (fp32).  Returns TTT_ERR_WORKSPACE if the workspace is too small.
+ */
+ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* args);
+
+/* Bytes of workspace ttt_fwd_chunked needs for these arguments (pointers
+ * need not be set).  0 is a valid answer (workspace may then be NULL). */
+ttt_status_t ttt_fwd_workspace_size(const ttt_fwd_args* args, size_t* bytes);
+
+/*
+ * ttt_chunk_state_scan -- exclusive scan of per-chunk state deltas.
+ *
+ * [P1] paragraph on removing weight normalisation: state updates become
+ * associative and a parallel prefix scan replaces the sequential walk; [P2]
+ * paragraph on the associative scan: chunk updates computed independently
+ * are combined by a prefix sum, identical to the sequential update.
+ *
+ * Inputs dS, dM [B,H,N,dk,dv] fp32 (contiguous) are the change of (S, m)
+ * over chunk c when that chunk starts from S = m = 0.  The chunk transition
+ * for a chunk of n tokens is
+ *     S' = S + alpha_n m + dS_c,  alpha_n = beta + ... + beta^n
+ *     m' = beta^n m + dM_c
+ * (beta = 0: S' = S + dS_c and dM is ignored, may be NULL).  Chunks hold
+ * `chunk` tokens except the last, which holds L - (N-1)*chunk; N must equal
+ * ceil(L / chunk).  Outputs the state at the start of every chunk, S_excl /
+ * M_excl [B,H,N,dk,dv] (M_excl may be NULL), and the state after the last
+ * chunk, S_final / M_final [B,H,dk,dv] (each may be NULL).  S0 / M0 are the
+ * incoming state (NULL = zero).  fp32 throughout.  Any dk, dv >= 1 with
+ * dk*dv a multiple of 4.  Needs no workspace (ws may be NULL).
+ */
+ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk,
+                                  int32_t dk, int32_t dv,
+                                  const float* dS, const float* dM, float beta,
+                                  const float* S0, const float* M0,
+                                  float* S_excl, float* M_excl,
+                                  float* S_final, float* M_final,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ttt_dual_form_fwd -- TTT-Linear mini-batch forward, dual form.
+ *
+ * [P4] section on turning the gradient into an efficient layer: tokens are
+ * grouped into mini-batches of `minibatch` tokens; inside a mini-batch every
+ * gradient is taken at the weights W_n the mini-batch started from, and the
+ * output of token t uses the gradient of the mini-batch prefix up to t:
+ *     W_{n,t} = W_n - eta sum_{s<=t, s in n} k_s^T (k_s W_n - v_s),  o_t = q_t W_{n,t},
+ *     W_{n+1} = W_{n,last}.
+ * Inner model f(k) = k W (linear, no bias, no normalisation); loss
+ * 1/2 ||k W - v||^2.  This update is not associative; the mini-batches run
+ * in order ([P5] background: small online mini-batches; key idea: large
+ * chunks).
+ *
+ * q, k [B,H,L,d], v, out [B,H,L,dv] contiguous, dtype `dtype`; W0
+ * [B,H,d,dv] fp32 (W0_stride_bh elements between heads, 0 broadcasts one
+ * W0); W_final [B,H,d,dv] fp32 contiguous or NULL.  Supported: d = 64,
+ * dv = 64, bf16 or fp32, minibatch >= 1 a multiple of 16 (the last
+ * mini-batch may be shorter).  Needs no workspace.
+ */
+ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
+                               int32_t minibatch, int32_t dtype,
+                               const void* q, const void* k, const void* v,
+                               const float* W0, int64_t W0_stride_bh, float eta,
+                               void* out, float* W_final,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* ttt_status_string(ttt_status_t status);
+
+/* sizeof(ttt_fwd_args) as compiled into the library (ABI check for bindings). */
+size_t ttt_fwd_args_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_MI355X_H */

@@ -1,0 +1,239 @@
+"""Python binding of the MI355X chunked TTT fast-weight forward library.
+
+Thin ctypes layer over ``liblinear_attention_chunked_amd.so`` (C ABI in
+``include/ttt.h``).  It only marshals arguments: PyTorch tensors provide
+device memory, strides and the current HIP stream; every step of the
+computation runs in the library's HIP kernels.  There is no CPU fallback:
+if the library is missing or the device is not a GPU the calls raise.
+
+Entry points (same names as the C ABI):
+    fwd_chunked(q, k, v, ...)          token-causal / chunk-causal forward
+    chunk_state_scan(dS, dM, ...)      exclusive scan of chunk-state deltas
+    dual_form_fwd(q, k, v, W0, ...)    TTT-Linear mini-batch dual form
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinear_attention_chunked_amd.so")
+
+TTT_F32, TTT_BF16 = 0, 1
+TOKEN_CAUSAL, CHUNK_CAUSAL = 0, 1
+_MODES = {"token_causal": TOKEN_CAUSAL, "chunk_causal": CHUNK_CAUSAL}
+
+_vp = ctypes.c_void_p
+_i64x3 = ctypes.c_int64 * 3
+_i64x2 = ctypes.c_int64 * 2
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"ttt status {status}: {msg}")
+        self.status = status
+
+
+class FwdArgs(ctypes.Structure):
+    """Mirror of ``ttt_fwd_args`` (include/ttt.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+        ("dk", ctypes.c_int32), ("dv", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("q", _vp), ("k", _vp), ("v", _vp),
+        ("q_stride", _i64x3), ("k_stride", _i64x3), ("v_stride", _i64x3),
+        ("eta", _vp), ("eta_stride", _i64x3), ("eta_scalar", ctypes.c_float),
+        ("beta", ctypes.c_float),
+        ("S0", _vp), ("S0_stride", _i64x2),
+        ("M0", _vp), ("M0_stride", _i64x2),
+        ("out", _vp), ("out_stride", _i64x3),
+        ("S_final", _vp), ("M_final", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("stream", _vp),
+    ]
+
+
+_lib = None
+
+
+def load_library():
+    """Load the in-tree HIP library (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not built: run `python -m linear_attention_chunked_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.ttt_fwd_chunked.argtypes = [ctypes.POINTER(FwdArgs)]
+    lib.ttt_fwd_chunked.restype = ctypes.c_int
+    lib.ttt_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ttt_fwd_workspace_size.restype = ctypes.c_int
+    i32, f32 = ctypes.c_int32, ctypes.c_float
+    lib.ttt_chunk_state_scan.argtypes = [i32, i32, i32, i32, i32, i32, _vp, _vp, f32, _vp, _vp,
+                                         _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.ttt_chunk_state_scan.restype = ctypes.c_int
+    lib.ttt_dual_form_fwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp,
+                                      ctypes.c_int64, f32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.ttt_dual_form_fwd.restype = ctypes.c_int
+    lib.ttt_status_string.argtypes = [ctypes.c_int]
+    lib.ttt_status_string.restype = ctypes.c_char_p
+    lib.ttt_fwd_args_size.argtypes = []
+    lib.ttt_fwd_args_size.restype = ctypes.c_size_t
+    if lib.ttt_fwd_args_size() != ctypes.sizeof(FwdArgs):
+        raise RuntimeError("ttt_fwd_args layout mismatch between library and binding")
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise TTTError(status, load_library().ttt_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TTT_F32
+    if t.dtype == torch.bfloat16:
+        return TTT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU (no CPU path exists)")
+
+
+def _bhl_strides(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B,H,L,d]")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+    return _i64x3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _state_strides(t: torch.Tensor | None, name: str):
+    if t is None:
+        return _i64x2(0, 0)
+    if t.dim() != 4 or t.dtype != torch.float32:
+        raise ValueError(f"{name} must be fp32 [B,H,dk,dv]")
+    if t.stride(-1) != 1 or t.stride(-2) != t.shape[-1]:
+        raise ValueError(f"{name}: each [dk,dv] block must be contiguous")
+    return _i64x2(t.stride(0), t.stride(1))
+
+
+def fwd_chunked(q, k, v, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None, chunk=64,
+                mode="token_causal", out=None, return_state=False, stream=None):
+    """Chunked fast-weight forward (``ttt_fwd_chunked``).
+
+    q, k: [B,H,L,dk]; v: [B,H,L,dv] (fp32 or bf16, same dtype; q may be k);
+    eta: [B,H,L] fp32 per-token step size or None (eta_scalar for all tokens);
+    beta: momentum (token-causal only); S0, M0: fp32 [B,H,dk,dv] or None.
+    Returns out [B,H,L,dv] (input dtype), plus (S_final, M_final) when
+    return_state (M_final is None unless beta != 0)."""
+    lib = load_library()
+    _require_gpu(q, k, v, eta, S0, M0, out)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    a = FwdArgs()
+    a.B, a.H, a.L, a.dk, a.dv, a.chunk = B, H, L, dk, dv, int(chunk)
+    a.mode = _MODES[mode] if isinstance(mode, str) else int(mode)
+    a.dtype = _dtype_code(q)
+    if k.dtype != q.dtype or v.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k, v and out must share one dtype")
+    a.q, a.k, a.v, a.out = _ptr(q), _ptr(k), _ptr(v), _ptr(out)
+    a.q_stride, a.k_stride = _bhl_strides(q, "q"), _bhl_strides(k, "k")
+    a.v_stride, a.out_stride = _bhl_strides(v, "v"), _bhl_strides(out, "out")
+    if eta is not None:
+        if eta.dtype != torch.float32 or eta.dim() != 3:
+            raise ValueError("eta must be fp32 [B,H,L]")
+        a.eta = _ptr(eta)
+        a.eta_stride = _i64x3(*eta.stride())
+    a.eta_scalar = float(eta_scalar)
+    a.beta = float(beta)
+    a.S0, a.S0_stride = _ptr(S0), _state_strides(S0, "S0")
+    a.M0, a.M0_stride = _ptr(M0), _state_strides(M0, "M0")
+    S_final = M_final = None
+    if return_state:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+        if beta != 0.0:
+            M_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    a.S_final, a.M_final = _ptr(S_final), _ptr(M_final)
+    ws = ctypes.c_size_t(0)
+    _check(lib.ttt_fwd_workspace_size(ctypes.byref(a), ctypes.byref(ws)))
+    work = None
+    if ws.value:
+        work = torch.empty(ws.value, dtype=torch.uint8, device=q.device)
+    a.workspace, a.workspace_bytes = _ptr(work), ws.value
+    a.stream = _stream(stream)
+    _check(lib.ttt_fwd_chunked(ctypes.byref(a)))
+    if return_state:
+        return out, S_final, M_final
+    return out
+
+
+def chunk_state_scan(dS, dM=None, *, beta=0.0, chunk, L, S0=None, M0=None, stream=None):
+    """Exclusive scan of chunk-state deltas (``ttt_chunk_state_scan``).
+
+    dS, dM: fp32 [B,H,N,dk,dv] contiguous.  Returns (S_excl, M_excl, S_final,
+    M_final); the M outputs are None when beta == 0."""
+    lib = load_library()
+    _require_gpu(dS, dM, S0, M0)
+    B, H, N, dk, dv = dS.shape
+    for t in (dS, dM, S0, M0):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("scan operands must be contiguous fp32")
+    S_excl = torch.empty_like(dS)
+    S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dS.device)
+    M_excl = M_final = None
+    if beta != 0.0:
+        M_excl = torch.empty_like(dS)
+        M_final = torch.empty_like(S_final)
+    _check(lib.ttt_chunk_state_scan(B, H, int(L), int(chunk), dk, dv, _ptr(dS), _ptr(dM), float(beta),
+                                    _ptr(S0), _ptr(M0), _ptr(S_excl), _ptr(M_excl), _ptr(S_final),
+                                    _ptr(M_final), None, 0, _stream(stream)))
+    return S_excl, M_excl, S_final, M_final
+
+
+def dual_form_fwd(q, k, v, W0, *, eta, minibatch, out=None, return_state=False, stream=None):
+    """TTT-Linear mini-batch forward, dual form (``ttt_dual_form_fwd``).
+
+    q, k: [B,H,L,d]; v: [B,H,L,dv] contiguous, fp32 or bf16; W0 fp32
+    [B,H,d,dv] (or [d,dv] broadcast).  Returns out (and W_final)."""
+    lib = load_library()
+    _require_gpu(q, k, v, W0, out)
+    B, H, L, d = q.shape
+    dv = v.shape[-1]
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        if not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous")
+    if W0.dtype != torch.float32 or not W0.is_contiguous():
+        raise ValueError("W0 must be contiguous fp32")
+    w_stride = 0 if W0.dim() == 2 else d * dv
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
+    W_final = torch.empty((B, H, d, dv), dtype=torch.float32, device=q.device) if return_state else None
+    _check(lib.ttt_dual_form_fwd(B, H, L, d, dv, int(minibatch), _dtype_code(q), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(W0), w_stride, float(eta), _ptr(out), _ptr(W_final),
+                                 None, 0, _stream(stream)))
+    if return_state:
+        return out, W_final
+    return out
+
+
+__all__ = ["fwd_chunked", "chunk_state_scan", "dual_form_fwd", "load_library", "TTTError",
+           "FwdArgs", "LIB_PATH"]

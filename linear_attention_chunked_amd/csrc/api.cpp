@@ -1,0 +1,222 @@
+// api.cpp -- the extern "C" boundary: argument validation and dispatch.
+//
+// Validation is complete before the first HIP call, so a rejected call has
+// enqueued nothing.  No allocation, no global mutable state.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "../../include/ttt.h"
+#include "internal.h"
+
+namespace {
+
+using ttt::MODE_CC;
+using ttt::MODE_MOM;
+using ttt::MODE_TC;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(int dtype) { return dtype == TTT_BF16 ? 2 : 4; }
+
+// [lo, hi) byte range touched by a [B,H,L,d] strided tensor
+void span(const void* base, const int64_t* st, int B, int H, int L, int d, size_t es,
+          uintptr_t* lo, uintptr_t* hi) {
+    const int64_t last = (int64_t)(B - 1) * st[0] + (int64_t)(H - 1) * st[1] + (int64_t)(L - 1) * st[2] + d;
+    *lo = reinterpret_cast<uintptr_t>(base);
+    *hi = *lo + (uintptr_t)last * es;
+}
+
+bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+ttt_status_t check_tensor(const void* p, const int64_t* st, int d, int dtype) {
+    if (!p) return TTT_ERR_NULL;
+    if (!aligned16(p)) return TTT_ERR_ALIGN;
+    const int64_t vec = 16 / (int64_t)esize(dtype);
+    for (int i = 0; i < 3; ++i) {
+        if (st[i] < 0) return TTT_ERR_SHAPE;
+        if (st[i] % vec != 0) return TTT_ERR_ALIGN;
+    }
+    if (st[2] < d) return TTT_ERR_SHAPE;  // rows must not overlap
+    return TTT_OK;
+}
+
+ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
+    if (!a) return TTT_ERR_NULL;
+    if (a->dtype != TTT_F32 && a->dtype != TTT_BF16) return TTT_ERR_DTYPE;
+    if (a->B < 1 || a->H < 1 || a->L < 1 || a->dk < 1 || a->dv < 1 || a->chunk < 1)
+        return TTT_ERR_SHAPE;
+    if (a->mode != TTT_TOKEN_CAUSAL && a->mode != TTT_CHUNK_CAUSAL) return TTT_ERR_VALUE;
+    if (!(a->beta >= 0.f && a->beta < 1.f)) return TTT_ERR_VALUE;
+    if (a->mode == TTT_CHUNK_CAUSAL && a->beta != 0.f) return TTT_ERR_VALUE;
+    ttt_status_t s;
+    if ((s = check_tensor(a->q, a->q_stride, a->dk, a->dtype)) != TTT_OK) return s;
+    if ((s = check_tensor(a->k, a->k_stride, a->dk, a->dtype)) != TTT_OK) return s;
+    if ((s = check_tensor(a->v, a->v_stride, a->dv, a->dtype)) != TTT_OK) return s;
+    if ((s = check_tensor(a->out, a->out_stride, a->dv, a->dtype)) != TTT_OK) return s;
+    if (a->eta) {
+        for (int i = 0; i < 3; ++i)
+            if (a->eta_stride[i] < 0) return TTT_ERR_SHAPE;
+    }
+    if (a->S0 && (a->S0_stride[0] < 0 || a->S0_stride[1] < 0)) return TTT_ERR_SHAPE;
+    if (a->M0 && (a->M0_stride[0] < 0 || a->M0_stride[1] < 0)) return TTT_ERR_SHAPE;
+    // out must not overlap an input
+    uintptr_t o0, o1, x0, x1;
+    const size_t es = esize(a->dtype);
+    span(a->out, a->out_stride, a->B, a->H, a->L, a->dv, es, &o0, &o1);
+    span(a->q, a->q_stride, a->B, a->H, a->L, a->dk, es, &x0, &x1);
+    if (overlap(o0, o1, x0, x1)) return TTT_ERR_ALIAS;
+    span(a->k, a->k_stride, a->B, a->H, a->L, a->dk, es, &x0, &x1);
+    if (overlap(o0, o1, x0, x1)) return TTT_ERR_ALIAS;
+    span(a->v, a->v_stride, a->B, a->H, a->L, a->dv, es, &x0, &x1);
+    if (overlap(o0, o1, x0, x1)) return TTT_ERR_ALIAS;
+
+    const int mode = (a->mode == TTT_CHUNK_CAUSAL) ? MODE_CC : (a->beta != 0.f ? MODE_MOM : MODE_TC);
+    if (!ttt::tc_fwd_supported(a->dtype, mode, a->dk, a->dv, a->chunk)) return TTT_ERR_UNSUPPORTED;
+    *mode_out = mode;
+    return TTT_OK;
+}
+
+ttt_status_t from_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ttt_status_string(ttt_status_t s) {
+    switch (s) {
+        case TTT_OK: return "ok";
+        case TTT_ERR_NULL: return "required pointer is NULL";
+        case TTT_ERR_SHAPE: return "size or stride out of range";
+        case TTT_ERR_DTYPE: return "unknown dtype";
+        case TTT_ERR_ALIGN: return "pointer or stride not 16-byte aligned";
+        case TTT_ERR_UNSUPPORTED: return "no kernel for these dimensions";
+        case TTT_ERR_WORKSPACE: return "workspace missing or too small";
+        case TTT_ERR_HIP: return "HIP runtime or launch error";
+        case TTT_ERR_ALIAS: return "output overlaps an input";
+        case TTT_ERR_VALUE: return "scalar argument out of range";
+    }
+    return "unknown status";
+}
+
+size_t ttt_fwd_args_size(void) { return sizeof(ttt_fwd_args); }
+
+ttt_status_t ttt_fwd_workspace_size(const ttt_fwd_args* a, size_t* bytes) {
+    if (!bytes) return TTT_ERR_NULL;
+    int mode = 0;
+    ttt_fwd_args tmp;
+    if (!a) return TTT_ERR_NULL;
+    std::memcpy(&tmp, a, sizeof(tmp));
+    // sizing needs no real pointers: substitute aligned dummies
+    static const float dummy[8] = {0};
+    const void* d = reinterpret_cast<const void*>(
+        (reinterpret_cast<uintptr_t>(dummy) + 15u) & ~static_cast<uintptr_t>(15u));
+    if (!tmp.q) tmp.q = d;
+    if (!tmp.k) tmp.k = d;
+    if (!tmp.v) tmp.v = d;
+    if (!tmp.out) tmp.out = reinterpret_cast<void*>(reinterpret_cast<uintptr_t>(d) + (1u << 20));
+    ttt_status_t s = validate_fwd(&tmp, &mode);
+    if (s != TTT_OK && s != TTT_ERR_ALIAS) return s;
+    *bytes = 0;
+    return TTT_OK;
+}
+
+ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* a) {
+    int mode = 0;
+    ttt_status_t s = validate_fwd(a, &mode);
+    if (s != TTT_OK) return s;
+    ttt::TcParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v;
+    p.out = a->out;
+    for (int i = 0; i < 3; ++i) {
+        p.qs[i] = a->q_stride[i];
+        p.ks[i] = a->k_stride[i];
+        p.vs[i] = a->v_stride[i];
+        p.os[i] = a->out_stride[i];
+        p.es[i] = a->eta ? a->eta_stride[i] : 0;
+    }
+    p.eta = a->eta;
+    p.eta_scalar = a->eta_scalar;
+    p.beta = a->beta;
+    p.S0 = a->S0;
+    p.s0s[0] = a->S0_stride[0];
+    p.s0s[1] = a->S0_stride[1];
+    p.M0 = a->M0;
+    p.m0s[0] = a->M0_stride[0];
+    p.m0s[1] = a->M0_stride[1];
+    p.S_final = a->S_final;
+    p.M_final = (mode == MODE_MOM) ? a->M_final : nullptr;
+    p.B = a->B;
+    p.H = a->H;
+    p.L = a->L;
+    p.dk = a->dk;
+    p.dv = a->dv;
+    p.chunk = a->chunk;
+    return from_hip(ttt::launch_tc_fwd(p, a->dtype, mode, reinterpret_cast<hipStream_t>(a->stream)));
+}
+
+ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk, int32_t dk,
+                                  int32_t dv, const float* dS, const float* dM, float beta,
+                                  const float* S0, const float* M0, float* S_excl, float* M_excl,
+                                  float* S_final, float* M_final, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (B < 1 || H < 1 || L < 1 || chunk < 1 || dk < 1 || dv < 1) return TTT_ERR_SHAPE;
+    if (((int64_t)dk * dv) % 4 != 0) return TTT_ERR_UNSUPPORTED;
+    if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_VALUE;
+    if (!dS) return TTT_ERR_NULL;
+    if (beta != 0.f && !dM) return TTT_ERR_NULL;
+    const void* ptrs[] = {dS, dM, S0, M0, S_excl, M_excl, S_final, M_final};
+    for (const void* q : ptrs)
+        if (q && !aligned16(q)) return TTT_ERR_ALIGN;
+    return from_hip(ttt::launch_state_scan(B, H, L, chunk, dk, dv, dS, beta != 0.f ? dM : nullptr, beta,
+                                           S0, beta != 0.f ? M0 : nullptr, S_excl, M_excl, S_final,
+                                           M_final, reinterpret_cast<hipStream_t>(stream)));
+}
+
+ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
+                               int32_t minibatch, int32_t dtype, const void* q, const void* k,
+                               const void* v, const float* W0, int64_t W0_stride_bh, float eta,
+                               void* out, float* W_final, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    (void)workspace;
+    (void)workspace_bytes;
+    if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
+    if (B < 1 || H < 1 || L < 1 || d < 1 || dv < 1 || minibatch < 1 || W0_stride_bh < 0)
+        return TTT_ERR_SHAPE;
+    if (!q || !k || !v || !W0 || !out) return TTT_ERR_NULL;
+    const void* ptrs[] = {q, k, v, W0, out, W_final};
+    for (const void* x : ptrs)
+        if (x && !aligned16(x)) return TTT_ERR_ALIGN;
+    if (!ttt::dual_supported(dtype, d, dv, minibatch)) return TTT_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + (size_t)B * H * L * dv * es;
+    const struct { const void* p; size_t n; } ins[] = {
+        {q, (size_t)B * H * L * d * es}, {k, (size_t)B * H * L * d * es}, {v, (size_t)B * H * L * dv * es}};
+    for (const auto& in : ins) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(in.p);
+        if (overlap(o0, o1, a0, a0 + in.n)) return TTT_ERR_ALIAS;
+    }
+    ttt::DualParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.W0 = W0;
+    p.W0_stride = W0_stride_bh;
+    p.W_final = W_final;
+    p.eta = eta;
+    p.B = B;
+    p.H = H;
+    p.L = L;
+    p.d = d;
+    p.dv = dv;
+    p.minibatch = minibatch;
+    return from_hip(ttt::launch_dual_fwd(p, dtype, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,61 @@
+// internal.h -- launcher interfaces between the C-ABI layer (api.cpp) and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ttt {
+
+enum { MODE_TC = 0, MODE_MOM = 1, MODE_CC = 2 };
+
+// Arguments of the small-head token-/chunk-causal kernel (dk, dv <= 128).
+struct TcParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    int64_t qs[3], ks[3], vs[3], os[3];
+    const float* eta;
+    int64_t es[3];
+    float eta_scalar;
+    float beta;
+    const float* S0;
+    int64_t s0s[2];
+    const float* M0;
+    int64_t m0s[2];
+    float* S_final;
+    float* M_final;
+    int B, H, L, dk, dv, chunk;
+    int n_vt;     // dv tiles per head
+    int xcd_map;  // 1: keep the dv tiles of one head on one XCD
+};
+
+// dtype: 0 fp32, 1 bf16.  mode: MODE_*.  Returns hipSuccess or the launch error;
+// hipErrorInvalidValue when no kernel is instantiated for the shape.
+hipError_t launch_tc_fwd(const TcParams& p, int dtype, int mode, hipStream_t stream);
+bool tc_fwd_supported(int dtype, int mode, int dk, int dv, int chunk);
+
+// Chunk-state scan: element-parallel walk over chunks.
+hipError_t launch_state_scan(int B, int H, int L, int chunk, int dk, int dv,
+                             const float* dS, const float* dM, float beta,
+                             const float* S0, const float* M0,
+                             float* S_excl, float* M_excl, float* S_final, float* M_final,
+                             hipStream_t stream);
+
+// Dual form (TTT-Linear mini-batch, MSE).
+struct DualParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    const float* W0;
+    int64_t W0_stride;
+    float* W_final;
+    float eta;
+    int B, H, L, d, dv, minibatch;
+};
+hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t stream);
+bool dual_supported(int dtype, int d, int dv, int minibatch);
+
+}  // namespace ttt

@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+that include/ttt.h declares, the binding's struct matches the C layout, and
+invalid arguments are rejected with the documented status before any launch
+(validation never touches the HIP runtime, so these run on a CPU host)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+import linear_attention_chunked_amd as lac  # noqa: E402
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_ALIAS, ERR_VALUE = range(10)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lac.LIB_PATH):
+        from linear_attention_chunked_amd import build
+        build.build(verbose=False)
+    return lac.load_library()
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ttt_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"ttt_fwd_chunked", "ttt_chunk_state_scan", "ttt_dual_form_fwd"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout(lib):
+    assert lib.ttt_fwd_args_size() == ctypes.sizeof(lac.FwdArgs)
+
+
+def test_status_strings(lib):
+    for s in range(10):
+        assert len(lib.ttt_status_string(s)) > 0
+    assert lib.ttt_status_string(123) == b"unknown status"
+
+
+FAKE = 1 << 32  # aligned fake device addresses; never dereferenced by validation
+
+
+def fwd_args(**kw):
+    a = lac.FwdArgs()
+    B, H, L, dk, dv = kw.get("B", 2), kw.get("H", 2), kw.get("L", 128), kw.get("dk", 64), kw.get("dv", 64)
+    a.B, a.H, a.L, a.dk, a.dv, a.chunk = B, H, L, dk, dv, kw.get("chunk", 64)
+    a.mode, a.dtype = kw.get("mode", 0), kw.get("dtype", 1)
+    size_q, size_v = B * H * L * dk * 2, B * H * L * dv * 2
+    a.q = kw.get("q", FAKE)
+    a.k = kw.get("k", FAKE + size_q + 4096)
+    a.v = kw.get("v", FAKE + 2 * (size_q + 4096))
+    a.out = kw.get("out", FAKE + 2 * (size_q + 4096) + size_v + 4096)
+    a.q_stride = lac._i64x3(H * L * dk, L * dk, dk)
+    a.k_stride = lac._i64x3(H * L * dk, L * dk, dk)
+    a.v_stride = lac._i64x3(H * L * dv, L * dv, dv)
+    a.out_stride = lac._i64x3(H * L * dv, L * dv, dv)
+    for name, val in kw.items():
+        if name.endswith("_stride"):
+            setattr(a, name, lac._i64x3(*val))
+    a.eta_scalar = 0.1
+    a.beta = kw.get("beta", 0.0)
+    return a
+
+
+def status(lib, a):
+    return lib.ttt_fwd_chunked(ctypes.byref(a))
+
+
+def test_fwd_rejects_before_launch(lib):
+    assert status(lib, fwd_args(q=None)) == ERR_NULL
+    assert status(lib, fwd_args(out=None)) == ERR_NULL
+    assert status(lib, fwd_args(L=0)) == ERR_SHAPE
+    assert status(lib, fwd_args(B=-1)) == ERR_SHAPE
+    assert status(lib, fwd_args(chunk=0)) == ERR_SHAPE
+    assert status(lib, fwd_args(dtype=7)) == ERR_DTYPE
+    assert status(lib, fwd_args(mode=5)) == ERR_VALUE
+    assert status(lib, fwd_args(beta=1.0)) == ERR_VALUE
+    assert status(lib, fwd_args(beta=-0.1)) == ERR_VALUE
+    assert status(lib, fwd_args(mode=1, beta=0.5)) == ERR_VALUE
+    assert status(lib, fwd_args(q=FAKE + 2)) == ERR_ALIGN
+    assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 68))) == ERR_ALIGN
+    assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 56))) == ERR_SHAPE
+    assert status(lib, fwd_args(dk=48)) == ERR_UNSUP
+    assert status(lib, fwd_args(dv=256)) == ERR_UNSUP
+    assert status(lib, fwd_args(mode=1, chunk=100)) == ERR_UNSUP
+    # out overlapping an input
+    a = fwd_args()
+    a.out = a.v
+    assert status(lib, a) == ERR_ALIAS
+    a = fwd_args()
+    a.out = a.q
+    assert status(lib, a) == ERR_ALIAS
+
+
+def test_workspace_query(lib):
+    a = fwd_args()
+    ws = ctypes.c_size_t(123)
+    assert lib.ttt_fwd_workspace_size(ctypes.byref(a), ctypes.byref(ws)) == OK
+    assert lib.ttt_fwd_workspace_size(ctypes.byref(a), None) == ERR_NULL
+    assert lib.ttt_fwd_workspace_size(ctypes.byref(fwd_args(dk=48)), ctypes.byref(ws)) == ERR_UNSUP
+
+
+def test_scan_rejects_before_launch(lib):
+    f = lib.ttt_chunk_state_scan
+    args = lambda **kw: [kw.get("B", 1), 1, kw.get("L", 64), kw.get("chunk", 16), kw.get("dk", 8), kw.get("dv", 8),
+                         kw.get("dS", FAKE), kw.get("dM", FAKE + 65536), kw.get("beta", 0.5), None, None,
+                         FAKE + 2 * 65536, None, None, None, None, 0, None]
+    assert f(*args(B=0)) == ERR_SHAPE
+    assert f(*args(chunk=0)) == ERR_SHAPE
+    assert f(*args(dS=None)) == ERR_NULL
+    assert f(*args(dM=None)) == ERR_NULL
+    assert f(*args(beta=1.5)) == ERR_VALUE
+    assert f(*args(dS=FAKE + 4)) == ERR_ALIGN
+    assert f(*args(dk=3, dv=3)) == ERR_UNSUP
+
+
+def test_dual_rejects_before_launch(lib):
+    f = lib.ttt_dual_form_fwd
+    n = 4 * 64 * 64 * 2
+
+    def args(**kw):
+        return [1, 1, 64, kw.get("d", 64), 64, kw.get("mb", 16), kw.get("dtype", 1),
+                kw.get("q", FAKE), FAKE + n, FAKE + 2 * n, kw.get("W0", FAKE + 3 * n), 0, 0.01,
+                kw.get("out", FAKE + 4 * n), None, None, 0, None]
+    assert f(*args(dtype=3)) == ERR_DTYPE
+    assert f(*args(mb=0)) == ERR_SHAPE
+    assert f(*args(q=None)) == ERR_NULL
+    assert f(*args(W0=None)) == ERR_NULL
+    assert f(*args(q=FAKE + 8)) == ERR_ALIGN
+    assert f(*args(d=32)) == ERR_UNSUP
+    assert f(*args(out=FAKE + n)) == ERR_ALIAS
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(ValueError):
+        lac.fwd_chunked(q, q, q)

@@ -1,0 +1,327 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (relative L2 over the whole compared tensor, fp64): fp32 inputs
+<= 1e-5, bf16 inputs <= 1e-2.  Integer-valued fp32 inputs whose every
+partial sum is exact must match bit for bit.  Full-size workloads are run
+in the launch configuration the benchmark times and checked on sampled
+(batch, head) slices that the oracle recomputes whole.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import linear_attention_chunked_amd as lac
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 1e-2}
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def to_dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def run_fwd(inp: W.TokenCausalInputs, mode="token_causal", chunk=None):
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    if inp.q is inp.k:
+        k = q
+    out, Sf, Mf = lac.fwd_chunked(q, k, v, eta=to_dev(inp.eta), eta_scalar=inp.eta_scalar,
+                                  beta=inp.beta, S0=to_dev(inp.S0), M0=to_dev(inp.M0),
+                                  chunk=chunk or inp.chunk, mode=mode, return_state=True)
+    torch.cuda.synchronize()
+    return out.cpu(), Sf.cpu(), (Mf.cpu() if Mf is not None else None)
+
+
+def sl(t, b, h):
+    return None if t is None else t[b:b + 1, h:h + 1]
+
+
+def oracle_tc(inp, heads=None, mode="token_causal", chunk=None):
+    """Oracle on all heads or on a list of (b, h)."""
+    if heads is None:
+        heads = [(b, h) for b in range(inp.q.shape[0]) for h in range(inp.q.shape[1])]
+    res = []
+    for b, h in heads:
+        args = (sl(inp.q, b, h), sl(inp.k, b, h), sl(inp.v, b, h))
+        if mode == "token_causal":
+            o, S, M = oracle.token_causal(*args, eta=sl(inp.eta, b, h), eta_scalar=inp.eta_scalar,
+                                          beta=inp.beta, S0=sl(inp.S0, b, h), M0=sl(inp.M0, b, h))
+        else:
+            o, S = oracle.chunk_causal(*args, eta=sl(inp.eta, b, h), eta_scalar=inp.eta_scalar,
+                                       S0=sl(inp.S0, b, h), chunk=chunk or inp.chunk)
+            M = None
+        res.append((b, h, o, S, M))
+    return res
+
+
+def check(inp, got, ref, tol, what=""):
+    out, Sf, Mf = got
+    for b, h, o, S, M in ref:
+        e = oracle.rel_l2(out[b, h].float(), o[0, 0])
+        assert e <= tol, f"{what} out (b={b},h={h}) rel-L2 {e:.3e} > {tol}"
+        e = oracle.rel_l2(Sf[b, h], S[0, 0])
+        assert e <= tol, f"{what} S_final (b={b},h={h}) rel-L2 {e:.3e} > {tol}"
+        if Mf is not None and M is not None:
+            e = oracle.rel_l2(Mf[b, h], M[0, 0])
+            assert e <= tol, f"{what} M_final (b={b},h={h}) rel-L2 {e:.3e} > {tol}"
+
+
+def whole_rel(inp, got, ref):
+    out = got[0]
+    num = den = 0.0
+    for b, h, o, _, _ in ref:
+        d = out[b, h].double().numpy() - o[0, 0]
+        num += float((d * d).sum())
+        den += float((o[0, 0] ** 2).sum())
+    return (num / den) ** 0.5
+
+
+# ------------------------------------------------------------- token-causal
+def test_c1_token_causal_fp32():
+    inp = W.gen_c1()
+    say("c1 fp32 B1 H2 L256 d32 C64")
+    got = run_fwd(inp)
+    ref = oracle_tc(inp)
+    check(inp, got, ref, TOL["f32"], "c1")
+    # the O(L^2) brute force agrees too
+    bf = oracle.bruteforce_token_causal(inp.q, inp.k, inp.v, eta_scalar=inp.eta_scalar)
+    assert oracle.rel_l2(got[0], bf) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("L,d,dv", [(250, 32, 32), (97, 64, 64), (300, 128, 128), (64, 128, 64), (1, 64, 32)])
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_token_causal_fp32_shapes(L, d, dv, beta):
+    g = torch.Generator().manual_seed(L * 7 + d + int(beta * 10))
+    B, H = 2, 3
+    q = torch.randn(B, H, L, d, generator=g) / d ** 0.5
+    k = torch.randn(B, H, L, d, generator=g) / d ** 0.5
+    v = torch.randn(B, H, L, dv, generator=g)
+    eta = 0.1 * torch.sigmoid(torch.randn(B, H, L, generator=g))
+    S0 = 0.05 * torch.randn(B, H, d, dv, generator=g)
+    M0 = 0.05 * torch.randn(B, H, d, dv, generator=g) if beta else None
+    inp = W.TokenCausalInputs(q, k, v, eta, 0.0, W.f32(beta), S0, M0, 32, "f32")
+    say(f"fp32 token-causal L{L} d{d} dv{dv} beta{beta}")
+    check(inp, run_fwd(inp), oracle_tc(inp), TOL["f32"], "fp32")
+
+
+def test_token_causal_fp32_integer_exact():
+    """Integer inputs, eta = 1/8: every fp32 partial sum is exact, so the GPU
+    output equals the oracle bit for bit regardless of summation order."""
+    g = torch.Generator().manual_seed(99)
+    B, H, L, d = 2, 2, 160, 32
+    q = torch.randint(-2, 3, (B, H, L, d), generator=g).float()
+    k = torch.randint(-2, 3, (B, H, L, d), generator=g).float()
+    v = torch.randint(-2, 3, (B, H, L, d), generator=g).float()
+    S0 = torch.randint(-2, 3, (B, H, d, d), generator=g).float()
+    inp = W.TokenCausalInputs(q, k, v, None, 0.125, 0.0, S0, None, 32, "f32")
+    say("fp32 integer exact")
+    out, Sf, _ = run_fwd(inp)
+    for b, h, o, S, _ in oracle_tc(inp):
+        assert np.array_equal(out[b, h].double().numpy(), o[0, 0])
+        assert np.array_equal(Sf[b, h].double().numpy(), S[0, 0])
+
+
+def test_c2_small_bf16_ragged():
+    inp = W.gen_c2(B=2, H=3, L=250, d=128)
+    say("c2-recipe bf16 B2 H3 L250 d128")
+    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "c2 small")
+
+
+@pytest.mark.parametrize("d,dv", [(64, 64), (32, 32), (128, 64), (64, 128)])
+def test_token_causal_bf16_shapes(d, dv):
+    inp = W.gen_c2(B=1, H=4, L=200, d=d)
+    if dv != d:
+        g = torch.Generator().manual_seed(5)
+        inp.v = torch.randn(1, 4, 200, dv, generator=g).to(torch.bfloat16)
+        inp.S0 = 0.02 * torch.randn(1, 4, d, dv, generator=g)
+    say(f"bf16 token-causal d{d} dv{dv}")
+    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "bf16 shapes")
+
+
+def test_c2_full_sampled_heads():
+    """Full LM-scale workload (B8 H16 L4096 d128 C64) in the benchmark's launch
+    configuration; sampled heads checked against the oracle."""
+    inp = W.gen_c2()
+    say("c2 full B8 H16 L4096 d128")
+    got = run_fwd(inp)
+    heads = [(0, 0), (3, 7), (5, 15), (7, 9)]
+    ref = oracle_tc(inp, heads)
+    check(inp, got, ref, TOL["bf16"], "c2 full")
+    assert torch.isfinite(got[0].float()).all()
+
+
+def test_c4_momentum_small():
+    inp = W.gen_c4(B=2, H=2, L=700, d=128)
+    say("c4-recipe momentum bf16 B2 H2 L700")
+    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "c4 small")
+
+
+def test_c4_full_sampled_heads():
+    inp = W.gen_c4()
+    say("c4 full B4 H8 L16384 d128 beta0.9")
+    got = run_fwd(inp)
+    ref = oracle_tc(inp, [(0, 0), (2, 5), (3, 7)])
+    check(inp, got, ref, TOL["bf16"], "c4 full")
+
+
+# ------------------------------------------------------------- chunk-causal
+@pytest.mark.parametrize("dtype,C", [("bf16", 64), ("bf16", 192), ("f32", 32), ("f32", 96)])
+def test_chunk_causal_small(dtype, C):
+    g = torch.Generator().manual_seed(C)
+    B, H, L, d, dv = 2, 2, 333, 64, 128
+    z = torch.randn(B, H, L, d, generator=g) / 8
+    vh = torch.randn(B, H, L, dv, generator=g)
+    eta = 0.05 * torch.rand(B, H, L, generator=g)
+    W0 = 0.02 * torch.randn(B, H, d, dv, generator=g)
+    if dtype == "bf16":
+        z, vh = z.to(torch.bfloat16), vh.to(torch.bfloat16)
+    inp = W.TokenCausalInputs(z, z, vh, eta, 0.0, 0.0, W0, None, C, dtype)
+    say(f"chunk-causal {dtype} C{C}")
+    got = run_fwd(inp, mode="chunk_causal")
+    check(inp, got, oracle_tc(inp, mode="chunk_causal"), TOL[dtype], "chunk-causal")
+
+
+# ------------------------------------------------------------- state scan
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_state_scan(beta):
+    B, H, L, C, dk, dv = 2, 3, 1000, 64, 32, 48
+    N = (L + C - 1) // C
+    dS, dM = W.gen_state_deltas(B, H, N, dk, dv, seed=6000)
+    S0, M0 = W.gen_state_deltas(B, H, 1, dk, dv, seed=6100)
+    S0, M0 = S0[:, :, 0].contiguous(), M0[:, :, 0].contiguous()
+    say(f"state scan beta{beta}")
+    Se, Me, Sf, Mf = lac.chunk_state_scan(dS.to(DEV), dM.to(DEV), beta=W.f32(beta), chunk=C, L=L,
+                                          S0=S0.to(DEV), M0=M0.to(DEV))
+    torch.cuda.synchronize()
+    rSe, rMe, rSf, rMf = oracle.state_scan(dS, dM if beta else None, W.f32(beta), C, L, S0, M0 if beta else None)
+    assert oracle.rel_l2(Se.cpu(), rSe) <= 1e-5
+    assert oracle.rel_l2(Sf.cpu(), rSf) <= 1e-5
+    if beta:
+        assert oracle.rel_l2(Me.cpu(), rMe) <= 1e-5
+        assert oracle.rel_l2(Mf.cpu(), rMf) <= 1e-5
+
+
+def test_state_scan_integer_exact():
+    B, H, L, C, dk, dv = 1, 2, 640, 64, 16, 16
+    dS, _ = W.gen_state_deltas(B, H, L // C, dk, dv, integer=True)
+    say("state scan integer exact")
+    Se, _, Sf, _ = lac.chunk_state_scan(dS.to(DEV), beta=0.0, chunk=C, L=L)
+    torch.cuda.synchronize()
+    rSe, _, rSf, _ = oracle.state_scan(dS, None, 0.0, C, L)
+    assert np.array_equal(Se.cpu().double().numpy(), rSe)
+    assert np.array_equal(Sf.cpu().double().numpy(), rSf)
+
+
+def test_scan_matches_fused_forward_states():
+    """Chunk aggregates scanned on the GPU reproduce the state the fused
+    forward kernel carries (momentum, ragged tail)."""
+    inp = W.gen_c4(B=1, H=2, L=300, d=32)
+    inp.q, inp.k, inp.v = inp.q.float(), inp.k.float(), inp.v.float()
+    dS, dM = oracle.chunk_aggregates(inp.k, inp.v, None, inp.eta_scalar, inp.beta, 32)
+    dS, dM = torch.from_numpy(dS).float(), torch.from_numpy(dM).float()
+    _, _, Sf, Mf = lac.chunk_state_scan(dS.to(DEV), dM.to(DEV), beta=inp.beta, chunk=32, L=300)
+    _, Sg, Mg = run_fwd(inp, chunk=32)
+    assert oracle.rel_l2(Sf.cpu(), Sg) <= 1e-5
+    assert oracle.rel_l2(Mf.cpu(), Mg) <= 1e-5
+
+
+# ------------------------------------------------------------- dual form
+def run_dual(inp: W.DualInputs):
+    out, Wf = lac.dual_form_fwd(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.W0),
+                                eta=inp.eta, minibatch=inp.minibatch, return_state=True)
+    torch.cuda.synchronize()
+    return out.cpu(), Wf.cpu()
+
+
+def check_dual(inp, got, heads, tol, what):
+    out, Wf = got
+    for b, h in heads:
+        o, Wr = oracle.dual_primal(sl(inp.q, b, h), sl(inp.k, b, h), sl(inp.v, b, h), sl(inp.W0, b, h),
+                                   inp.eta, inp.minibatch)
+        e = oracle.rel_l2(out[b, h].float(), o[0, 0])
+        assert e <= tol, f"{what} out (b={b},h={h}) rel-L2 {e:.3e}"
+        e = oracle.rel_l2(Wf[b, h], Wr[0, 0])
+        assert e <= tol, f"{what} W_final (b={b},h={h}) rel-L2 {e:.3e}"
+
+
+@pytest.mark.parametrize("mb,L", [(16, 300), (64, 1000), (2048, 4096), (1, 70), (48, 200)])
+def test_dual_small(mb, L):
+    inp = W.gen_c5(B=1, H=2, L=L, minibatch=mb)
+    say(f"dual bf16 b{mb} L{L}")
+    check_dual(inp, run_dual(inp), [(0, 0), (0, 1)], TOL["bf16"], "dual")
+
+
+@pytest.mark.parametrize("mb", [16, 40])
+def test_dual_fp32(mb):
+    inp = W.gen_c5(B=1, H=2, L=256, minibatch=mb)
+    inp.q, inp.k, inp.v = inp.q.float(), inp.k.float(), inp.v.float()
+    say(f"dual fp32 b{mb}")
+    check_dual(inp, run_dual(inp), [(0, 0), (0, 1)], TOL["f32"], "dual fp32")
+
+
+@pytest.mark.parametrize("mb", [16, 2048])
+def test_c5_full_sampled_heads(mb):
+    inp = W.gen_c5(minibatch=mb)
+    say(f"c5 full B4 H16 L8192 d64 b{mb}")
+    check_dual(inp, run_dual(inp), [(0, 0), (1, 9), (3, 15)], TOL["bf16"], f"c5 b{mb}")
+
+
+def test_dual_fixed_point_exact():
+    """v = k W0 makes every gradient zero: out = q W0 exactly (fp32)."""
+    inp = W.gen_c5(B=1, H=2, L=200, minibatch=16)
+    q, k = inp.q.float(), inp.k.float()
+    out, Wf = lac.dual_form_fwd(q.to(DEV), k.to(DEV), (0.5 * k).to(DEV), inp.W0.to(DEV), eta=inp.eta,
+                                minibatch=16, return_state=True)
+    torch.cuda.synchronize()
+    assert oracle.rel_l2(out.cpu(), 0.5 * q) <= 1e-6
+    assert oracle.rel_l2(Wf.cpu(), inp.W0) <= 1e-6
+
+
+# ------------------------------------------------------------- properties
+def test_head_isolation_and_determinism():
+    inp = W.gen_c2(B=2, H=4, L=256, d=64)
+    o1 = run_fwd(inp)[0]
+    o2 = run_fwd(inp)[0]
+    assert torch.equal(o1, o2), "repeated calls must be bit-identical"
+    inp.v = inp.v.clone()
+    inp.v[1, 2] += 1
+    o3 = run_fwd(inp)[0]
+    diff = (o3.float() - o1.float()).abs().flatten(2).amax(-1)
+    assert diff[1, 2] > 0 and int((diff > 0).sum()) == 1
+
+
+def test_continuation_equals_one_call():
+    """fwd(L1) then fwd(L2, S0 = S_final) equals fwd(L1 + L2) (fixed-size state)."""
+    g = torch.Generator().manual_seed(3)
+    B, H, L1, L2, d = 1, 2, 96, 160, 64
+    q = torch.randn(B, H, L1 + L2, d, generator=g) / 8
+    k = torch.randn(B, H, L1 + L2, d, generator=g) / 8
+    v = torch.randn(B, H, L1 + L2, d, generator=g)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    full, Sf, Mf = lac.fwd_chunked(qd, kd, vd, eta_scalar=0.1, beta=0.5, return_state=True)
+    a, Sa, Ma = lac.fwd_chunked(qd[:, :, :L1], kd[:, :, :L1], vd[:, :, :L1], eta_scalar=0.1, beta=0.5,
+                                return_state=True)
+    b, Sb, Mb = lac.fwd_chunked(qd[:, :, L1:], kd[:, :, L1:], vd[:, :, L1:], eta_scalar=0.1, beta=0.5,
+                                S0=Sa, M0=Ma, return_state=True)
+    torch.cuda.synchronize()
+    assert oracle.rel_l2(torch.cat([a, b], 2).cpu(), full.cpu()) <= 1e-5
+    assert oracle.rel_l2(Sb.cpu(), Sf.cpu()) <= 1e-5
+
+
+def test_strided_inputs():
+    """q, k, v as views of a packed [B, L, H, 3, d] projection give the same result."""
+    g = torch.Generator().manual_seed(8)
+    B, L, H, d = 2, 130, 3, 64
+    qkv = torch.randn(B, L, H, 3, d, generator=g).to(torch.bfloat16).to(DEV)
+    q, k, v = (qkv[:, :, :, i].permute(0, 2, 1, 3) for i in range(3))
+    o1 = lac.fwd_chunked(q, k, v, eta_scalar=0.05)
+    o2 = lac.fwd_chunked(q.contiguous(), k.contiguous(), v.contiguous(), eta_scalar=0.05)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
