@@ -1,0 +1,257 @@
+"""Benchmark of the chunked TTT fast-weight forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+One step = one full pass of the hot path over one batch of synthetic input
+(all inputs resident in HBM before timing): for the default LM-scale
+workload, one ttt_fwd_chunked call (token-causal, per-token eta, S0 in,
+outputs and final state out).  Prints ONE JSON line.
+
+Roofline: the dominant kernel's average launch duration is measured with
+HIP events recorded on the launch stream around every timed step; achieved
+bandwidth = algorithmic bytes per launch / that duration.  HBM traffic
+counted by rocprofv3 (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's
+counters) is read from profiles/traffic.json when it was measured on the
+current kernel source, else reported as null.
+
+cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on this host on
+the same seeded inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # dense fp32 MFMA / vector
+
+METRIC = "tokens/s + TFLOP/s (MFMA % of peak) for chunked TTT fast-weight forward, 1 GPU"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_attention_chunked_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------- workloads
+def setup_workload(name: str, dev: str):
+    """Returns (step_fn, info) with inputs already on the device."""
+    import torch
+    import workloads as W
+    import linear_attention_chunked_amd as lac
+
+    if name in ("c1", "c2", "c4"):
+        gen = {"c1": W.gen_c1, "c2": W.gen_c2, "c4": W.gen_c4}[name]
+        inp = gen()
+        B, H, L, dk = inp.q.shape
+        dv = inp.v.shape[-1]
+        q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+        eta = inp.eta.to(dev) if inp.eta is not None else None
+        S0 = inp.S0.to(dev) if inp.S0 is not None else None
+        out = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
+        es = q.element_size()
+        C = inp.chunk
+        mom = inp.beta != 0.0
+
+        def step():
+            return lac.fwd_chunked(q, k, v, eta=eta, eta_scalar=inp.eta_scalar, beta=inp.beta, S0=S0,
+                                   chunk=C, out=out, return_state=True)
+
+        nstate = 2 if mom else 1
+        bytes_alg = (B * H * L * (2 * dk + dv) * es                 # q, k, v
+                     + (B * H * L * 4 if eta is not None else 0)    # eta
+                     + (B * H * dk * dv * 4 if S0 is not None else 0)
+                     + B * H * L * dv * es                          # out
+                     + nstate * B * H * dk * dv * 4)                # final state(s)
+        flop_alg = B * H * L * (4 * nstate * dk * dv + (C + 1) * (dk + dv))
+        info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, mode="token_causal",
+                    beta=inp.beta, eta="per-token" if eta is not None else inp.eta_scalar,
+                    dtype=inp.dtype, tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
+                    kernel="tc_fwd_kernel", inputs=inp)
+        return step, info
+    if name in ("c3a", "c3b"):
+        L = 32768 if name == "c3a" else 131072
+        d_ff, d_model = 9728, 2560
+        Z = torch.empty((1, 1, L, d_ff), dtype=torch.bfloat16, device=dev)
+        V = torch.empty((1, 1, L, d_model), dtype=torch.bfloat16, device=dev)
+        inp = W.gen_c3(L=L, out=(Z, V))
+        W0 = inp.S0.to(dev)
+        out = torch.empty((1, 1, L, d_model), dtype=torch.bfloat16, device=dev)
+
+        def step():
+            return lac.fwd_chunked(Z, Z, V, eta_scalar=inp.eta_scalar, S0=W0, chunk=1024,
+                                   mode="chunk_causal", out=out, return_state=True)
+
+        bytes_alg = L * (d_ff + 2 * d_model) * 2 + 2 * d_ff * d_model * 4
+        flop_alg = 4 * L * d_ff * d_model
+        info = dict(workload=name, B=1, H=1, L=L, d_ff=d_ff, d_model=d_model, chunk=1024,
+                    mode="chunk_causal", eta=inp.eta_scalar, dtype="bf16", tokens=L,
+                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="ip_update_kernel+ip_readout_kernel",
+                    inputs=None)
+        return step, info
+    if name in ("c5a", "c5b"):
+        mb = 16 if name == "c5a" else 2048
+        inp = W.gen_c5(minibatch=mb)
+        B, H, L, d = inp.q.shape
+        q, k, v, W0 = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.W0.to(dev)
+        out = torch.empty_like(v)
+
+        def step():
+            return lac.dual_form_fwd(q, k, v, W0, eta=inp.eta, minibatch=mb, out=out, return_state=True)
+
+        bytes_alg = B * H * L * 4 * d * 2 + 2 * B * H * d * d * 4
+        flop_alg = B * H * L * (6 * d * d + (mb + 1) * 2 * d)
+        info = dict(workload=name, B=B, H=H, L=L, d=d, minibatch=mb, dtype="bf16", tokens=B * L,
+                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="dual_fwd_kernel", inputs=inp)
+        return step, info
+    raise SystemExit(f"unknown workload {name}")
+
+
+# --------------------------------------------------------------- CPU baseline
+def cpu_baseline(info) -> dict:
+    """fp64 oracle on the same seeded inputs (whole workload when it fits
+    ~10-30 s of host work, else a head subset scaled to the whole)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+
+    inp = info["inputs"]
+    if inp is None:
+        return None
+    B, H = inp.q.shape[:2]
+    L = inp.q.shape[2]
+    heads = B * H
+    if info["workload"] == "c4":
+        heads = min(heads, 8)
+    if info["workload"] in ("c5a", "c5b"):
+        heads = min(heads, 32)
+    bsel = max(1, heads // H)
+    hsel = min(H, heads)
+    sl = lambda t: None if t is None else W.to_f64(t[:bsel, :hsel])
+    args = [sl(inp.q), sl(inp.k), sl(inp.v)]
+    if info["workload"] in ("c5a", "c5b"):
+        W0 = sl(inp.W0)
+        t0 = time.perf_counter()
+        oracle.dual_primal(*args, W0, inp.eta, inp.minibatch)
+        dt = time.perf_counter() - t0
+    else:
+        eta, S0 = sl(inp.eta), sl(inp.S0)
+        t0 = time.perf_counter()
+        oracle.token_causal(*args, eta=eta, eta_scalar=inp.eta_scalar, beta=inp.beta, S0=S0)
+        dt = time.perf_counter() - t0
+    frac = (bsel * hsel) / (B * H)
+    tokens_per_s = info["tokens"] * frac / dt
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{bsel * hsel} of {B * H} (b,h) heads, full L={L}, fp64 per-token recurrence; "
+                      f"{dt:.2f} s; tokens/s scaled by the head fraction"}
+
+
+def load_traffic(kernel: str, workload: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    e = t.get(f"{kernel}:{workload}")
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", help="c2 (default, LM-scale), c1, c3a, c3b, c4, c5a, c5b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "
+              "(multi-GPU sharding is design-only). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return
+
+    step, info = setup_workload(args.workload, dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    ms_per_step = wall * 1000.0 / args.steps
+
+    tokens = info["tokens"]
+    value = tokens / (ms_per_step / 1000.0)
+    gbs = info["bytes_alg"] / (launch_ms / 1000.0) / 1e9
+    tflops = info["flop_alg"] / (launch_ms / 1000.0) / 1e12
+    peak_f = PEAK_BF16_TFLOPS if info["dtype"] == "bf16" else PEAK_FP32_TFLOPS
+    roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic(info["kernel"], info["workload"]),
+                "kernel": info["kernel"], "launch_ms": round(launch_ms, 5),
+                "bytes_alg_per_launch": info["bytes_alg"]}
+    if info["flop_alg"] / peak_f / 1e12 > info["bytes_alg"] / PEAK_HBM_GBS / 1e9:
+        roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_f,
+                         "unit": "TFLOP/s", "frac": round(tflops / peak_f, 4)})
+
+    cfg = {k: info[k] for k in info if k not in ("inputs", "bytes_alg", "flop_alg", "kernel", "tokens")}
+    res = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": info["dtype"], "data": "synthetic (seeded Gaussian inputs of the workload's shapes)",
+        "config": cfg,
+        "tflops": round(tflops, 3), "mfma_frac": round(tflops / peak_f, 5),
+        "hbm_gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(info)
+        if cb is not None:
+            res["cpu_baseline"] = cb
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -41,7 +41,17 @@ ttt_status_t check_tensor(const void* p, const int64_t* st, int d, int dtype) {
     return TTT_OK;
 }
 
-ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
+// the large-fast-weight chunk-causal path (needs a snapshot workspace)
+bool use_inplace(const ttt_fwd_args* a, int mode) {
+    return mode == MODE_CC && !ttt::tc_fwd_supported(a->dtype, mode, a->dk, a->dv, a->chunk);
+}
+
+size_t workspace_bytes_for(const ttt_fwd_args* a, int mode) {
+    return use_inplace(a, mode) ? ttt::inplace_workspace(a->B, a->H, a->L, a->dk, a->dv, a->chunk) : 0;
+}
+
+// sizes, dtype, mode and scalars only (no pointers): also serves the workspace query
+ttt_status_t validate_shapes(const ttt_fwd_args* a, int* mode_out) {
     if (!a) return TTT_ERR_NULL;
     if (a->dtype != TTT_F32 && a->dtype != TTT_BF16) return TTT_ERR_DTYPE;
     if (a->B < 1 || a->H < 1 || a->L < 1 || a->dk < 1 || a->dv < 1 || a->chunk < 1)
@@ -49,7 +59,17 @@ ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
     if (a->mode != TTT_TOKEN_CAUSAL && a->mode != TTT_CHUNK_CAUSAL) return TTT_ERR_VALUE;
     if (!(a->beta >= 0.f && a->beta < 1.f)) return TTT_ERR_VALUE;
     if (a->mode == TTT_CHUNK_CAUSAL && a->beta != 0.f) return TTT_ERR_VALUE;
-    ttt_status_t s;
+    const int mode = (a->mode == TTT_CHUNK_CAUSAL) ? MODE_CC : (a->beta != 0.f ? MODE_MOM : MODE_TC);
+    if (!ttt::tc_fwd_supported(a->dtype, mode, a->dk, a->dv, a->chunk) &&
+        !(mode == MODE_CC && ttt::inplace_supported(a->dtype, a->dk, a->dv, a->chunk)))
+        return TTT_ERR_UNSUPPORTED;
+    *mode_out = mode;
+    return TTT_OK;
+}
+
+ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
+    ttt_status_t s = validate_shapes(a, mode_out);
+    if (s != TTT_OK) return s;
     if ((s = check_tensor(a->q, a->q_stride, a->dk, a->dtype)) != TTT_OK) return s;
     if ((s = check_tensor(a->k, a->k_stride, a->dk, a->dtype)) != TTT_OK) return s;
     if ((s = check_tensor(a->v, a->v_stride, a->dv, a->dtype)) != TTT_OK) return s;
@@ -70,12 +90,13 @@ ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
     if (overlap(o0, o1, x0, x1)) return TTT_ERR_ALIAS;
     span(a->v, a->v_stride, a->B, a->H, a->L, a->dv, es, &x0, &x1);
     if (overlap(o0, o1, x0, x1)) return TTT_ERR_ALIAS;
-
-    const int mode = (a->mode == TTT_CHUNK_CAUSAL) ? MODE_CC : (a->beta != 0.f ? MODE_MOM : MODE_TC);
-    if (!ttt::tc_fwd_supported(a->dtype, mode, a->dk, a->dv, a->chunk)) return TTT_ERR_UNSUPPORTED;
-    *mode_out = mode;
+    const size_t need = workspace_bytes_for(a, *mode_out);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return TTT_ERR_WORKSPACE;
+    if (a->workspace && !aligned16(a->workspace)) return TTT_ERR_ALIGN;
     return TTT_OK;
 }
+
+
 
 ttt_status_t from_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
 
@@ -102,22 +123,11 @@ const char* ttt_status_string(ttt_status_t s) {
 size_t ttt_fwd_args_size(void) { return sizeof(ttt_fwd_args); }
 
 ttt_status_t ttt_fwd_workspace_size(const ttt_fwd_args* a, size_t* bytes) {
-    if (!bytes) return TTT_ERR_NULL;
+    if (!a || !bytes) return TTT_ERR_NULL;
     int mode = 0;
-    ttt_fwd_args tmp;
-    if (!a) return TTT_ERR_NULL;
-    std::memcpy(&tmp, a, sizeof(tmp));
-    // sizing needs no real pointers: substitute aligned dummies
-    static const float dummy[8] = {0};
-    const void* d = reinterpret_cast<const void*>(
-        (reinterpret_cast<uintptr_t>(dummy) + 15u) & ~static_cast<uintptr_t>(15u));
-    if (!tmp.q) tmp.q = d;
-    if (!tmp.k) tmp.k = d;
-    if (!tmp.v) tmp.v = d;
-    if (!tmp.out) tmp.out = reinterpret_cast<void*>(reinterpret_cast<uintptr_t>(d) + (1u << 20));
-    ttt_status_t s = validate_fwd(&tmp, &mode);
-    if (s != TTT_OK && s != TTT_ERR_ALIAS) return s;
-    *bytes = 0;
+    const ttt_status_t s = validate_shapes(a, &mode);
+    if (s != TTT_OK) return s;
+    *bytes = workspace_bytes_for(a, mode);
     return TTT_OK;
 }
 
@@ -155,7 +165,9 @@ ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* a) {
     p.dk = a->dk;
     p.dv = a->dv;
     p.chunk = a->chunk;
-    return from_hip(ttt::launch_tc_fwd(p, a->dtype, mode, reinterpret_cast<hipStream_t>(a->stream)));
+    const hipStream_t st = reinterpret_cast<hipStream_t>(a->stream);
+    if (use_inplace(a, mode)) return from_hip(ttt::launch_inplace(p, a->workspace, st));
+    return from_hip(ttt::launch_tc_fwd(p, a->dtype, mode, st));
 }
 
 ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk, int32_t dk,

@@ -36,6 +36,12 @@ struct TcParams {
 hipError_t launch_tc_fwd(const TcParams& p, int dtype, int mode, hipStream_t stream);
 bool tc_fwd_supported(int dtype, int mode, int dk, int dv, int chunk);
 
+// Chunk-causal forward for large fast weights (dk, dv multiples of 256, bf16):
+// update walk with bf16 W snapshots in `workspace`, then a batched readout.
+bool inplace_supported(int dtype, int dk, int dv, int chunk);
+size_t inplace_workspace(int B, int H, int L, int dk, int dv, int chunk);
+hipError_t launch_inplace(const TcParams& p, void* workspace, hipStream_t stream);
+
 // Chunk-state scan: element-parallel walk over chunks.
 hipError_t launch_state_scan(int B, int H, int L, int chunk, int dk, int dv,
                              const float* dS, const float* dM, float beta,

@@ -67,8 +67,15 @@ def _load():
         lib.ttt_oracle_state_scan.argtypes = [i, i, i, i, i, i, _dp, _dp, d, _dp, _dp,
                                               _dp, _dp, _dp, _dp]
         lib.ttt_oracle_state_scan.restype = None
+        lib.ttt_oracle_threads.argtypes = []
+        lib.ttt_oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
+
+
+def threads() -> int:
+    """Host threads the C oracle's OpenMP loops use."""
+    return int(_load().ttt_oracle_threads())
 
 
 def _f64(x):

@@ -205,3 +205,16 @@ void ttt_oracle_state_scan(int B, int H, int L, int chunk, int dk, int dv,
         free(m);
     }
 }
+
+/* Number of host threads the OpenMP loops above use (for reporting). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int ttt_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
