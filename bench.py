@@ -36,14 +36,22 @@ PEAK_FP32_TFLOPS = 157.3       # dense fp32 MFMA / vector
 METRIC = "tokens/s + TFLOP/s (MFMA % of peak) for chunked TTT fast-weight forward, 1 GPU"
 
 
-def kernel_source_hash() -> str:
+KERNEL_SOURCES = {
+    "tc_fwd_kernel": ("tc_fwd.hip", "common.h"),
+    "ip_update_kernel+ip_readout_kernel": ("inplace.hip", "common.h"),
+    "dual_fwd_kernel": ("dual.hip", "common.h"),
+}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the source files a kernel is built from (traffic counters are
+    only reported while they match)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_attention_chunked_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode())
-                h.update(f.read())
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -167,7 +175,7 @@ def load_traffic(kernel: str, workload: str):
     with open(path) as f:
         t = json.load(f)
     e = t.get(f"{kernel}:{workload}")
-    if not e or e.get("source_hash") != kernel_source_hash():
+    if not e or e.get("source_hash") != kernel_source_hash(kernel):
         return None
     return e.get("bytes_per_launch")
 
