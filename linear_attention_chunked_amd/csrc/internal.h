@@ -35,6 +35,9 @@ struct TcParams {
 // hipErrorInvalidValue when no kernel is instantiated for the shape.
 hipError_t launch_tc_fwd(const TcParams& p, int dtype, int mode, hipStream_t stream);
 bool tc_fwd_supported(int dtype, int mode, int dk, int dv, int chunk);
+// gfx950-tuned bf16 variant (dk in {64,128}, dv in {64,128}); chosen by launch_tc_fwd
+bool tcb_supported(int dtype, int dk, int dv);
+hipError_t launch_tcb_fwd(const TcParams& p, int mode, hipStream_t stream);
 
 // Chunk-causal forward for large fast weights (dk, dv multiples of 256, bf16):
 // update walk with bf16 W snapshots in `workspace`, then a batched readout.

@@ -402,6 +402,7 @@ bool tc_fwd_supported(int dtype, int mode, int dk, int dv, int chunk) {
 
 hipError_t launch_tc_fwd(const TcParams& pin, int dtype, int mode, hipStream_t s) {
     if (!tc_fwd_supported(dtype, mode, pin.dk, pin.dv, pin.chunk)) return hipErrorInvalidValue;
+    if (tcb_supported(dtype, pin.dk, pin.dv)) return launch_tcb_fwd(pin, mode, s);
     TcParams p = pin;
     const int dvt = pick_dvt(p.dv);
     p.n_vt = p.dv / dvt;
