@@ -1,25 +1,30 @@
 // tcb_fwd.hip -- bf16 chunked fast-weight forward for d_k in {64, 128} and
-// d_v tiles of 64 (the LM-scale and momentum shapes).
+// 64-column d_v tiles (the LM-scale and momentum shapes).
 //
-// Same mathematics as tc_fwd.hip (see its header for the pages' passages and
-// the momentum algebra); this is the gfx950-tuned form of it:
-//   * Q, K, V chunks are staged in LDS as plain row copies; the transposed
-//     operands K^T (state update) and V (intra term and update) are read out
-//     of the row-major tiles with ds_read_b64_tr_b16, so staging is a copy.
-//   * Rows are XOR-swizzled at 16-byte granularity (swz below), which makes
-//     the row reads, the paired 8-byte reads, the transposing reads and the
-//     staging writes all free of LDS bank conflicts.
-//   * LDS is double-buffered: chunk c+1 is loaded into registers while chunk
-//     c computes and written to the other buffer at the end, so each chunk
-//     costs two barriers.
-//   * eta (and the momentum weights) scale the V fragment in registers; the
-//     same fragment feeds the intra-chunk term and the state update.
-//   * The fp32 state lives in MFMA accumulators for the whole sequence and
-//     feeds the readout straight from registers (accperm k-assignment).
-// One workgroup = (b, h, 64-column dv tile), 4 waves; wave w owns state and
-// output columns [16w, 16w+16) of the tile.  Chunk tile = 64 tokens.
+// Same mathematics as tc_fwd.hip (its header cites the pages' passages and
+// derives the momentum algebra); this is the gfx950-tuned form:
+//   * 8 waves per workgroup = 2 per SIMD.  Wave w owns state columns
+//     [16(w%4), +16) of the 64-column tile and one half of the d_k rows
+//     (w/4); the two halves of a column tile add their readout partial sums
+//     through LDS at the top of the next chunk, so no extra barrier is needed.
+//   * Q, K, V chunks are staged as plain row copies in a K-block-major
+//     layout [block of 32 features][token][32] with a 16-byte XOR swizzle
+//     (swz below): row reads, paired 8-byte reads and the transposing reads
+//     (ds_read_b64_tr_b16, which give K^T and V operands straight from the
+//     token-major tiles) are all bank-conflict free, and every fragment
+//     address is a per-lane base computed once plus a compile-time offset.
+//   * LDS is double-buffered; chunk c+2 is fetched into registers while c
+//     computes, chunk c+1 is written to LDS at the end: two barriers per chunk.
+//   * The output tile is summed over the two d_k halves, rounded and parked
+//     in LDS, then written as full 128-byte row segments by all threads.
+//   * eta and the momentum weights scale the V fragment in registers; the
+//     fp32 state is held in MFMA accumulators for the whole sequence and
+//     feeds the readout from registers.
+// Chunk tile = 64 tokens.
 #include "common.h"
 #include "internal.h"
+
+#include <type_traits>
 
 namespace ttt {
 
@@ -27,42 +32,20 @@ namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte-chunk swizzle of a row-major bf16 tile with NCH chunks per row
-template <int NCH> TTT_DEV int swz(int r);
-template <> TTT_DEV int swz<16>(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-template <> TTT_DEV int swz<8>(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
-template <int NCH> TTT_DEV int so(int r, int e) {       // element offset of (row r, element e)
-    return r * (NCH * 8) + ((((e >> 3) ^ swz<NCH>(r))) << 3) + (e & 7);
-}
+constexpr int CS = 64;                 // tokens per chunk tile
+constexpr int BLK = CS * 32;           // elements of one [token][32] block
 
-// operand fragment, contig k-assignment: row r, k = kb0 + 8g .. +7
-template <int NCH> TTT_DEV bf16x8 fr_contig(const bf16_t* t, int r, int kb0, int g) {
-    return *reinterpret_cast<const bf16x8*>(t + so<NCH>(r, kb0 + 8 * g));
-}
-// operand fragment, accperm k-assignment: row r, k = kb0 + 4g + {0..3}, kb0 + 16 + 4g + {0..3}
-template <int NCH> TTT_DEV bf16x8 fr_accperm(const bf16_t* t, int r, int kb0, int g) {
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(t + so<NCH>(r, kb0 + 4 * g));
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(t + so<NCH>(r, kb0 + 16 + 4 * g));
-    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
+TTT_DEV int swz(int r) { return (((r >> 2) & 1) << 1) | ((r >> 3) & 1); }
+// element offset of (row r, feature e) in a [e/32][row][32] tile
+TTT_DEV int lofs(int r, int e) { return (e >> 5) * BLK + r * 32 + 8 * (((e >> 3) & 3) ^ swz(r)) + (e & 7); }
+
 TTT_DEV u32x2 tr_read(const bf16_t* p) {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
-// Transposed operand: lane l <-> tile column c0 + l%16, k = tile rows in the
-// accperm assignment starting at row kb0.  ds_read_b64_tr_b16: in each group
-// of 16 lanes, lane a loads 4 consecutive values and lane i receives, in slot
-// j, the value lane 4j + i/4 loaded in its slot i%4; lane a therefore points
-// at row kb0 + 4g + a/4, columns c0 + 4(a%4) .. +3.
-template <int NCH> TTT_DEV bf16x8 fr_tr(const bf16_t* t, int c0, int kb0, int lane) {
-    const int g = lane >> 4, a = lane & 15;
-    const int col = c0 + 4 * (a & 3);
-    const int r = kb0 + 4 * g + (a >> 2);
-    const u32x2 lo = tr_read(t + so<NCH>(r, col));
-    const u32x2 hi = tr_read(t + so<NCH>(r + 16, col));
+TTT_DEV bf16x8 join(const u32x2& lo, const u32x2& hi) {
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
-// scale the 8 bf16 values of a fragment by per-slot factors
 TTT_DEV bf16x8 scale_frag(const bf16x8& f, const f32x4& s_lo, const f32x4& s_hi) {
     const u32x4 w = __builtin_bit_cast(u32x4, f);
     const u32x4 o = u32x4{pack2bf(__uint_as_float(w[0] << 16) * s_lo[0], __uint_as_float(w[0] & 0xffff0000u) * s_lo[1]),
@@ -75,28 +58,30 @@ TTT_DEV bf16x8 scale_frag(const bf16x8& f, const f32x4& s_lo, const f32x4& s_hi)
 }  // namespace
 
 template <int DK, int MODE>
-__global__ __launch_bounds__(256) void tcb_fwd_kernel(TcParams p) {
-    constexpr int CS = 64, DVT = 64, NW = 4, NT = 256;
-    constexpr int NCQ = DK / 8;             // 16-byte chunks per Q/K row
-    constexpr int NCV = DVT / 8;            // ... per V row
-    constexpr int LP = CS + 8;              // sP row stride (padded)
+__global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
+    constexpr int DVT = 64, NT = 512;
+    constexpr int NKB = DK / 32;            // feature blocks of Q / K
+    constexpr int DKH = DK / 2;             // d_k rows per wave
+    constexpr int NTH = DKH / 16;           // state tiles per wave
+    constexpr int NKH = DKH / 32;           // K-blocks per wave
+    constexpr int LP = CS + 8;              // sP row stride
     constexpr bool MOM = (MODE == MODE_MOM);
     constexpr bool HAS_P = (MODE != MODE_CC);
     constexpr int NV = MOM ? 3 : 1;         // eta | eta*w_{n-1-j} | eta*beta^{n-1-j}
-    constexpr int NTD = DK / 16;            // state tiles along dk
-    constexpr int NKB = DK / 32;            // K-blocks along dk
-    constexpr int UQ = CS * NCQ / NT;       // staged chunks per thread (Q and K each)
-    constexpr int UV = CS * NCV / NT;
+    constexpr int UQ = CS * DK / 8 / NT;    // 16-byte chunks per thread (Q and K each)
 
-    __shared__ __attribute__((aligned(16))) bf16_t sQ[2][CS * DK];
-    __shared__ __attribute__((aligned(16))) bf16_t sK[2][CS * DK];
-    __shared__ __attribute__((aligned(16))) bf16_t sV[2][CS * DVT];
+    __shared__ __attribute__((aligned(16))) bf16_t sQ[2][NKB * BLK];
+    __shared__ __attribute__((aligned(16))) bf16_t sK[2][NKB * BLK];
+    __shared__ __attribute__((aligned(16))) bf16_t sV[2][2 * BLK];
     __shared__ __attribute__((aligned(16))) float sE[2][NV][CS];
     __shared__ __attribute__((aligned(16))) bf16_t sP[HAS_P ? CS * LP : 8];
-    __shared__ float sTab[3 * (CS + 1)];    // w_p | beta^p | a_p
+    __shared__ __attribute__((aligned(16))) f32x4 sX[4][4][64];   // half-1 readout partials
+    __shared__ __attribute__((aligned(16))) bf16_t sO[CS * DVT];  // finished output tile
+    __shared__ float sTab[3 * (CS + 1)];                           // w_p | beta^p | a_p
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
+    const int nt = wave & 3, hf = wave >> 2;
 
     int bh, vt;
     {
@@ -131,141 +116,202 @@ __global__ __launch_bounds__(256) void tcb_fwd_kernel(TcParams p) {
             sTab[2 * (CS + 1) + pp] = (float)(be * (1.0 - bp1) / (1.0 - be));
         }
     }
-    if (HAS_P) {  // strictly-upper P tiles stay zero
-        for (int x = tid; x < CS * LP / 8; x += NT)
-            reinterpret_cast<u32x4*>(sP)[x] = u32x4{0, 0, 0, 0};
+    if (HAS_P) {
+        for (int x = tid; x < CS * LP / 8; x += NT) reinterpret_cast<u32x4*>(sP)[x] = u32x4{0, 0, 0, 0};
     }
 
-    // ---- state accumulators S[16t + 4g + r][16*wave + c16] (and m)
-    f32x4 Sacc[NTD];
-    f32x4 Macc[MOM ? NTD : 1];
+    // ---- per-lane LDS bases (elements)
+    // row reads of rows r0 + c16: contig k = 8g..; accperm k = 4g.., 16 + 4g..
+    const int sw_l = swz(c16);
+    const int b_contig = c16 * 32 + 8 * (g ^ sw_l);
+    const int b_ap0 = c16 * 32 + 8 * ((g >> 1) ^ sw_l) + 4 * (g & 1);
+    const int b_ap1 = c16 * 32 + 8 * ((2 + (g >> 1)) ^ sw_l) + 4 * (g & 1);
+    // transposing reads: lane (g, a) -> row 4g + a/4, column 16*par + 4(a%4) of a block
+    const int a_tr = lane & 15;
+    const int r_tr = 4 * g + (a_tr >> 2);
+    const int b_tr0 = r_tr * 32 + 8 * ((0 | ((a_tr & 3) >> 1)) ^ swz(r_tr)) + 4 * (a_tr & 1);
+    const int b_tr1 = r_tr * 32 + 8 * ((2 | ((a_tr & 3) >> 1)) ^ swz(r_tr)) + 4 * (a_tr & 1);
+    // V fragment of this wave's columns 16*nt: block nt/2, parity nt&1
+    const int b_v = (nt >> 1) * BLK + ((nt & 1) ? b_tr1 : b_tr0);
+
+    // ---- state accumulators S[DKH*hf + 16t + 4g + r][16*nt + c16]
+    f32x4 Sacc[NTH];
+    f32x4 Macc[MOM ? NTH : 1];
     {
         const float* S0 = p.S0 ? p.S0 + b * p.s0s[0] + h * p.s0s[1] : nullptr;
         const float* M0 = (MOM && p.M0) ? p.M0 + b * p.m0s[0] + h * p.m0s[1] : nullptr;
-        const int col = n0 + 16 * wave + c16;
+        const int col = n0 + 16 * nt + c16;
 #pragma unroll
-        for (int t = 0; t < NTD; ++t)
+        for (int t = 0; t < NTH; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * t + 4 * g + r;
+                const int row = DKH * hf + 16 * t + 4 * g + r;
                 Sacc[t][r] = S0 ? S0[(int64_t)row * p.dv + col] : 0.f;
                 if (MOM) Macc[t][r] = M0 ? M0[(int64_t)row * p.dv + col] : 0.f;
             }
     }
-    bf16x8 Sop[NKB], Mop[MOM ? NKB : 1];
+    bf16x8 Sop[NKH], Mop[MOM ? NKH : 1];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) Sop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
+    for (int kk = 0; kk < NKH; ++kk) Sop[kk] = acc_to_frag_bf16(Sacc[2 * kk], Sacc[2 * kk + 1]);
     if (MOM) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) Mop[kb] = acc_to_frag_bf16(Macc[2 * kb], Macc[2 * kb + 1]);
+        for (int kk = 0; kk < NKH; ++kk) Mop[kk] = acc_to_frag_bf16(Macc[2 * kk], Macc[2 * kk + 1]);
     }
 
-    // ---- staging registers
-    u32x4 rq[UQ], rk[UQ], rv[UV];
-    float re = 0.f;
-    auto load = [&](int c) {
+    // ---- staging: thread -> linear 16-byte chunk u of the [blk][row][4] layout
+    // register sets for chunks in flight: PF = 2 keeps two chunks of loads
+    // outstanding per workgroup (momentum keeps one: its VGPRs are taken)
+    constexpr int PF = MOM ? 1 : 2;
+    u32x4 rq[PF][UQ], rk[PF][UQ], rv[PF];
+    float re[PF];
+    int goff_q[UQ], goff_v;
+#pragma unroll
+    for (int x = 0; x < UQ; ++x) {
+        const int u = tid + x * NT, blk = u >> 8, row = (u >> 2) & 63, pos = u & 3;
+        goff_q[x] = row * (int)qL + 32 * blk + 8 * (pos ^ swz(row));   // token offset added per chunk
+    }
+    {
+        const int u = tid, blk = u >> 8, row = (u >> 2) & 63, pos = u & 3;
+        goff_v = row * (int)vL + 32 * blk + 8 * (pos ^ swz(row));
+    }
+    const int kq_same = (qL == kL);
+    auto load = [&](int c, auto SET) {
+        constexpr int st = decltype(SET)::value;
         const int t0 = c * CS;
+        const bool full = (t0 + CS <= L);
+        const bf16_t* Qc = Qg + (int64_t)t0 * qL;
+        const bf16_t* Kc = Kg + (int64_t)t0 * kL;
 #pragma unroll
         for (int x = 0; x < UQ; ++x) {
-            const int u = tid + x * NT, r = u / NCQ, ch = u % NCQ, t = t0 + r;
-            const bool ok = t < L;
-            rq[x] = ok ? *reinterpret_cast<const u32x4*>(Qg + t * qL + 8 * ch) : u32x4{0, 0, 0, 0};
-            rk[x] = ok ? *reinterpret_cast<const u32x4*>(Kg + t * kL + 8 * ch) : u32x4{0, 0, 0, 0};
+            const int u = tid + x * NT, row = (u >> 2) & 63;
+            const bool ok = full || (t0 + row < L);
+            const int ko = kq_same ? goff_q[x] : (row * (int)kL + (goff_q[x] - row * (int)qL));
+            rq[st][x] = ok ? *reinterpret_cast<const u32x4*>(Qc + goff_q[x]) : u32x4{0, 0, 0, 0};
+            rk[st][x] = ok ? *reinterpret_cast<const u32x4*>(Kc + ko) : u32x4{0, 0, 0, 0};
         }
-#pragma unroll
-        for (int x = 0; x < UV; ++x) {
-            const int u = tid + x * NT, r = u / NCV, ch = u % NCV, t = t0 + r;
-            rv[x] = (t < L) ? *reinterpret_cast<const u32x4*>(Vg + t * vL + 8 * ch) : u32x4{0, 0, 0, 0};
+        {
+            const int row = (tid >> 2) & 63;
+            const bool ok = full || (t0 + row < L);
+            rv[st] = ok ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)t0 * vL + goff_v) : u32x4{0, 0, 0, 0};
         }
         if (tid < CS) {
             const int t = t0 + tid;
-            re = (t < L) ? (Eg ? Eg[t * eL] : p.eta_scalar) : 0.f;
+            re[st] = (t < L) ? (Eg ? Eg[t * eL] : p.eta_scalar) : 0.f;
         }
     };
-    auto store = [&](int c, int buf) {
+    auto store = [&](int c, int buf, auto SET) {
+        constexpr int st = decltype(SET)::value;
 #pragma unroll
         for (int x = 0; x < UQ; ++x) {
-            const int u = tid + x * NT, r = u / NCQ, ch = u % NCQ;
-            *reinterpret_cast<u32x4*>(&sQ[buf][so<NCQ>(r, 8 * ch)]) = rq[x];
-            *reinterpret_cast<u32x4*>(&sK[buf][so<NCQ>(r, 8 * ch)]) = rk[x];
+            const int u = tid + x * NT;
+            *reinterpret_cast<u32x4*>(&sQ[buf][8 * u]) = rq[st][x];
+            *reinterpret_cast<u32x4*>(&sK[buf][8 * u]) = rk[st][x];
         }
-#pragma unroll
-        for (int x = 0; x < UV; ++x) {
-            const int u = tid + x * NT, r = u / NCV, ch = u % NCV;
-            *reinterpret_cast<u32x4*>(&sV[buf][so<NCV>(r, 8 * ch)]) = rv[x];
-        }
+        *reinterpret_cast<u32x4*>(&sV[buf][8 * tid]) = rv[st];
         if (tid < CS) {
-            sE[buf][0][tid] = re;
+            sE[buf][0][tid] = re[st];
             if (MOM) {
                 const int n = min(CS, L - c * CS);
                 const int pw = n - 1 - tid;
-                sE[buf][1][tid] = (pw >= 0) ? re * sTab[pw] : 0.f;
-                sE[buf][2][tid] = (pw >= 0) ? re * sTab[(CS + 1) + pw] : 0.f;
+                sE[buf][1][tid] = (pw >= 0) ? re[st] * sTab[pw] : 0.f;
+                sE[buf][2][tid] = (pw >= 0) ? re[st] * sTab[(CS + 1) + pw] : 0.f;
             }
         }
     };
 
+    // P^T tile assignment (query tile ti; key tiles tjA, tjB; -1 = none), grouped by
+    // query tile so a wave reuses its Q fragments
+    int p_ti = -1, p_tjA = -1, p_tjB = -1;
+    switch (wave) {
+        case 0: p_ti = 3; p_tjA = 1; p_tjB = 2; break;
+        case 1: p_ti = 3; p_tjA = 0; p_tjB = 3; break;
+        case 2: p_ti = 2; p_tjA = 0; p_tjB = 1; break;
+        case 3: p_ti = 2; p_tjA = 2; break;
+        case 4: p_ti = 1; p_tjA = 0; p_tjB = 1; break;
+        case 5: p_ti = 0; p_tjA = 0; break;
+        default: break;
+    }
+
+    f32x4 oacc[4];    // this wave's readout partial of the previous chunk (half 0 keeps it)
+    int prev_base = 0, prev_n = 0;
+    // half 0: add half 1's partial, round, and park the tile in sO (rows of 128 B,
+    // 16-byte chunks swizzled by (row/2)%8: conflict-free for both sides)
+    auto combine = [&]() {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            const int i = 16 * ti + c16;
+            const f32x4 o = oacc[ti] + sX[nt][ti][lane];
+            const int ch = (2 * nt + (g >> 1)) ^ ((i >> 1) & 7);
+            st4(&sO[i * DVT + 8 * ch + 4 * (g & 1)], o);
+        }
+    };
+    // all threads: write the parked tile out as full 128-byte row segments
+    auto write_out = [&]() {
+        const int row = tid >> 3, ch = tid & 7;
+        if (row < prev_n) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[row * DVT + 8 * (ch ^ ((row >> 1) & 7))]);
+            *reinterpret_cast<u32x4*>(&Og[(int64_t)(prev_base + row) * oL + 8 * ch]) = w;
+        }
+    };
+
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, PF - 1>;
     const int ntiles = (L + CS - 1) / CS;
-    load(0);
-    __syncthreads();  // tables ready
-    store(0, 0);
+    load(0, I0{});
+    __syncthreads();   // tables ready
+    store(0, 0, I0{});
+    if (PF == 2 && ntiles > 1) load(1, I1{});
     __syncthreads();
 
-    for (int c = 0; c < ntiles; ++c) {
+    // chunk k travels in register set k % PF; chunk c+PF is requested while
+    // chunk c computes, chunk c+1 is written to the other LDS buffer at the end
+    auto iter = [&](int c, auto LSET, auto SSET) {
+        if (c + PF < ntiles) load(c + PF, LSET);
         const int cur = c & 1;
         const int tbase = c * CS;
         const int n = min(CS, L - tbase);
-        if (c + 1 < ntiles) load(c + 1);
         const bf16_t* Q = sQ[cur];
         const bf16_t* K = sK[cur];
         const bf16_t* V = sV[cur];
 
-        // ------------- intra scores P^T = K Q^T (lower-triangular 16x16 tiles)
-        if (HAS_P) {
-            // tiles grouped by query tile so a wave reuses its Q fragments:
-            // w0: (1,3)(2,3)(3,3)  w1: (0,2)(1,2)(2,2)  w2: (0,1)(1,1)(0,0)  w3: (0,3)
-            int ti, tj0, ntj;
-            if (wave == 0) { ti = 3; tj0 = 1; ntj = 3; }
-            else if (wave == 1) { ti = 2; tj0 = 0; ntj = 3; }
-            else if (wave == 2) { ti = 1; tj0 = 0; ntj = 2; }
-            else { ti = 3; tj0 = 0; ntj = 1; }
-            for (int pass = 0; pass < 2; ++pass) {
-                if (pass == 1) {                 // wave 2 also owns (0,0)
-                    if (wave != 2) break;
-                    ti = 0; tj0 = 0; ntj = 1;
-                }
-                f32x4 pa[3] = {zero4(), zero4(), zero4()};
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const bf16x8 bq = fr_contig<NCQ>(Q, 16 * ti + c16, 32 * kb, g);
-#pragma unroll
-                    for (int x = 0; x < 3; ++x)
-                        if (x < ntj) mma(pa[x], fr_contig<NCQ>(K, 16 * (tj0 + x) + c16, 32 * kb, g), bq);
-                }
-                const int i = 16 * ti + c16;
-#pragma unroll
-                for (int x = 0; x < 3; ++x) {
-                    if (x >= ntj) break;
-                    const int tj = tj0 + x;
-                    f32x4 v = pa[x];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * tj + 4 * g + r;
-                        float val = (j <= i) ? v[r] : 0.f;
-                        if (MOM && j <= i) val *= sTab[i - j];
-                        v[r] = val;
-                    }
-                    st4(&sP[i * LP + 16 * tj + 4 * g], v);
-                }
-            }
-            __syncthreads();
-        }
+        if (hf == 0 && c > 0) combine();
 
-        // ------------- value fragments: raw V^T (accperm over tokens), scaled in registers
+        // ------------- intra scores P^T = K Q^T (lower-triangular 16x16 tiles)
+        if (HAS_P && p_ti >= 0) {
+            f32x4 pa = zero4(), pb = zero4();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8 bq = *reinterpret_cast<const bf16x8*>(Q + kb * BLK + p_ti * 512 + b_contig);
+                mma(pa, *reinterpret_cast<const bf16x8*>(K + kb * BLK + p_tjA * 512 + b_contig), bq);
+                if (p_tjB >= 0)
+                    mma(pb, *reinterpret_cast<const bf16x8*>(K + kb * BLK + p_tjB * 512 + b_contig), bq);
+            }
+            const int i = 16 * p_ti + c16;
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int tj = x ? p_tjB : p_tjA;
+                if (tj < 0) break;
+                f32x4 v = x ? pb : pa;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = 16 * tj + 4 * g + r;
+                    float val = (j <= i) ? v[r] : 0.f;
+                    if (MOM && j <= i) val *= sTab[i - j];
+                    v[r] = val;
+                }
+                st4(&sP[i * LP + 16 * tj + 4 * g], v);
+            }
+        }
+        // P^T complete; the previous chunk's output tile is parked in sO and
+        // half 0 has read half 1's partials before they are overwritten below
+        __syncthreads();
+        if (c > 0) write_out();
+
+        // ------------- value fragments (tokens in accperm order) scaled in registers
         bf16x8 VB[2], VS[MOM ? 2 : 1], VM[MOM ? 2 : 1];
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
-            const bf16x8 raw = fr_tr<NCV>(V, 16 * wave, 32 * jb, lane);
+            const bf16x8 raw = join(tr_read(V + b_v + (32 * jb) * 32), tr_read(V + b_v + (32 * jb + 16) * 32));
             const float* e0 = &sE[cur][0][32 * jb + 4 * g];
             VB[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e0), *reinterpret_cast<const f32x4*>(e0 + 16));
             if (MOM) {
@@ -276,7 +322,7 @@ __global__ __launch_bounds__(256) void tcb_fwd_kernel(TcParams p) {
             }
         }
 
-        // ------------- readout O^T = S^T Q^T (+ a_i m^T Q^T) + V~^T P^T
+        // ------------- readout partial: O^T = S_h^T Q_h^T (+ a_i m_h^T Q_h^T) (+ V~^T P^T share)
         {
             f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
             f32x4 acc2[MOM ? 4 : 1];
@@ -284,53 +330,57 @@ __global__ __launch_bounds__(256) void tcb_fwd_kernel(TcParams p) {
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) acc2[ti] = zero4();
             }
+            const bf16_t* Qh = Q + hf * NKH * BLK;
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                bf16x8 bq[4];
-#pragma unroll
-                for (int ti = 0; ti < 4; ++ti) bq[ti] = fr_accperm<NCQ>(Q, 16 * ti + c16, 32 * kb, g);
+            for (int kk = 0; kk < NKH; ++kk) {
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
-                    mma(acc[ti], Sop[kb], bq[ti]);
-                    if (MOM) mma(acc2[ti], Mop[kb], bq[ti]);
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap0);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap1);
+                    const bf16x8 bq = join(lo, hi);
+                    mma(acc[ti], Sop[kk], bq);
+                    if (MOM) mma(acc2[ti], Mop[kk], bq);
                 }
             }
             if (HAS_P) {
+                // half 0 takes key block 0 of every query tile, half 1 key block 1 (ti >= 2)
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti) {
                     const bf16_t* prow = &sP[(16 * ti + c16) * LP];
-                    mma(acc[ti], VB[0], ld_accperm(prow, 0, g));
-                    if (ti >= 2) mma(acc[ti], VB[1], ld_accperm(prow, 32, g));
+                    if (hf == 0) mma(acc[ti], VB[0], ld_accperm(prow, 0, g));
+                    else if (ti >= 2) mma(acc[ti], VB[1], ld_accperm(prow, 32, g));
                 }
             }
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
-                const int i = 16 * ti + c16;
                 f32x4 o = acc[ti];
-                if (MOM) {
-                    const float a = sTab[2 * (CS + 1) + i];
-                    for (int r = 0; r < 4; ++r) o[r] += a * acc2[ti][r];
-                }
-                if (i < n) st4(&Og[(int64_t)(tbase + i) * oL + 16 * wave + 4 * g], o);
+                if (MOM) o += sTab[2 * (CS + 1) + 16 * ti + c16] * acc2[ti];
+                if (hf == 0) oacc[ti] = o;
+                else sX[nt][ti][lane] = o;
             }
         }
+        // (prev_* are read by write_out above, so they advance only here)
+        prev_base = tbase;
+        prev_n = n;
 
-        // ------------- state update S += K^T V~  (momentum: affine chunk transition)
+        // ------------- state update (own d_k half)
         {
             if (MOM) {
                 const float alpha = sTab[2 * (CS + 1) + (n - 1)];
                 const float gamma = sTab[(CS + 1) + n];
 #pragma unroll
-                for (int t = 0; t < NTD; ++t) {
+                for (int t = 0; t < NTH; ++t) {
                     Sacc[t] += alpha * Macc[t];
                     Macc[t] *= gamma;
                 }
             }
+            const bf16_t* Kh = K + (hf * NTH / 2) * BLK;   // d_k half -> feature blocks
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
-                for (int t = 0; t < NTD; ++t) {
-                    const bf16x8 a = fr_tr<NCQ>(K, 16 * t, 32 * jb, lane);
+                for (int t = 0; t < NTH; ++t) {
+                    const int base = (t >> 1) * BLK + ((t & 1) ? b_tr1 : b_tr0) + (32 * jb) * 32;
+                    const bf16x8 a = join(tr_read(Kh + base), tr_read(Kh + base + 16 * 32));
                     mma(Sacc[t], a, MOM ? VS[jb] : VB[jb]);
                     if (MOM) mma(Macc[t], a, VM[jb]);
                 }
@@ -342,31 +392,38 @@ __global__ __launch_bounds__(256) void tcb_fwd_kernel(TcParams p) {
             }
             if (refresh) {
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) Sop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
+                for (int kk = 0; kk < NKH; ++kk) Sop[kk] = acc_to_frag_bf16(Sacc[2 * kk], Sacc[2 * kk + 1]);
                 if (MOM) {
 #pragma unroll
-                    for (int kb = 0; kb < NKB; ++kb) Mop[kb] = acc_to_frag_bf16(Macc[2 * kb], Macc[2 * kb + 1]);
+                    for (int kk = 0; kk < NKH; ++kk) Mop[kk] = acc_to_frag_bf16(Macc[2 * kk], Macc[2 * kk + 1]);
                 }
             }
         }
-        if (c + 1 < ntiles) store(c + 1, cur ^ 1);
+        if (c + 1 < ntiles) store(c + 1, cur ^ 1, SSET);
         __syncthreads();
+    };
+    for (int c = 0; c < ntiles; c += 2) {
+        iter(c, I0{}, I1{});
+        if (c + 1 < ntiles) iter(c + 1, I1{}, I0{});
     }
+    if (hf == 0) combine();
+    __syncthreads();
+    write_out();
 
-    const int col = n0 + 16 * wave + c16;
+    const int col = n0 + 16 * nt + c16;
     if (p.S_final) {
         float* Sf = p.S_final + (int64_t)bh * p.dk * p.dv;
 #pragma unroll
-        for (int t = 0; t < NTD; ++t)
+        for (int t = 0; t < NTH; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sf[(int64_t)(16 * t + 4 * g + r) * p.dv + col] = Sacc[t][r];
+            for (int r = 0; r < 4; ++r) Sf[(int64_t)(DKH * hf + 16 * t + 4 * g + r) * p.dv + col] = Sacc[t][r];
     }
     if (MOM && p.M_final) {
         float* Mf = p.M_final + (int64_t)bh * p.dk * p.dv;
 #pragma unroll
-        for (int t = 0; t < NTD; ++t)
+        for (int t = 0; t < NTH; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Mf[(int64_t)(16 * t + 4 * g + r) * p.dv + col] = Macc[t][r];
+            for (int r = 0; r < 4; ++r) Mf[(int64_t)(DKH * hf + 16 * t + 4 * g + r) * p.dv + col] = Macc[t][r];
     }
 }
 
@@ -378,7 +435,7 @@ hipError_t launch_tcb_fwd(const TcParams& pin, int mode, hipStream_t s) {
     TcParams p = pin;
     p.n_vt = p.dv / 64;
     p.xcd_map = ((p.B * p.H) % 8 == 0) ? 1 : 0;
-    const dim3 grid(p.B * p.H * p.n_vt), block(256);
+    const dim3 grid(p.B * p.H * p.n_vt), block(512);
 #define TTT_L(DK_, M_) hipLaunchKernelGGL((tcb_fwd_kernel<DK_, M_>), grid, block, 0, s, p)
     if (p.dk == 128) {
         if (mode == MODE_TC) TTT_L(128, MODE_TC);
