@@ -32,8 +32,11 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 TTT_DEV float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 // round-to-nearest-even fp32 -> bf16 (hardware conversion on gfx950)
 TTT_DEV uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (bf16_t)x); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even)
 TTT_DEV uint32_t pack2bf(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 TTT_DEV f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }

@@ -33,11 +33,13 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CS = 64;                 // tokens per chunk tile
-constexpr int BLK = CS * 32;           // elements of one [token][32] block
+constexpr int BLK = CS * 32 + 32;      // Q/K block stride: [token][32] + 64 B pad
+constexpr int BLKV = CS * 32 + 64;     // V block stride: [token][32] + 128 B pad
+// (the pads keep the row-order staging writes conflict free; reads never
+//  cross a block within one instruction)
 
 TTT_DEV int swz(int r) { return (((r >> 2) & 1) << 1) | ((r >> 3) & 1); }
-// element offset of (row r, feature e) in a [e/32][row][32] tile
-TTT_DEV int lofs(int r, int e) { return (e >> 5) * BLK + r * 32 + 8 * (((e >> 3) & 3) ^ swz(r)) + (e & 7); }
+// (row r, feature e) of a tile lives at element (e/32)*BLK + r*32 + 8*(((e/8)%4) ^ swz(r)) + e%8
 
 TTT_DEV u32x2 tr_read(const bf16_t* p) {
     typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
 
     __shared__ __attribute__((aligned(16))) bf16_t sQ[2][NKB * BLK];
     __shared__ __attribute__((aligned(16))) bf16_t sK[2][NKB * BLK];
-    __shared__ __attribute__((aligned(16))) bf16_t sV[2][2 * BLK];
+    __shared__ __attribute__((aligned(16))) bf16_t sV[2][2 * BLKV];
     __shared__ __attribute__((aligned(16))) float sE[2][NV][CS];
     __shared__ __attribute__((aligned(16))) bf16_t sP[HAS_P ? CS * LP : 8];
     __shared__ __attribute__((aligned(16))) f32x4 sX[4][4][64];   // half-1 readout partials
@@ -132,7 +134,7 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
     const int b_tr0 = r_tr * 32 + 8 * ((0 | ((a_tr & 3) >> 1)) ^ swz(r_tr)) + 4 * (a_tr & 1);
     const int b_tr1 = r_tr * 32 + 8 * ((2 | ((a_tr & 3) >> 1)) ^ swz(r_tr)) + 4 * (a_tr & 1);
     // V fragment of this wave's columns 16*nt: block nt/2, parity nt&1
-    const int b_v = (nt >> 1) * BLK + ((nt & 1) ? b_tr1 : b_tr0);
+    const int b_v = (nt >> 1) * BLKV + ((nt & 1) ? b_tr1 : b_tr0);
 
     // ---- state accumulators S[DKH*hf + 16t + 4g + r][16*nt + c16]
     f32x4 Sacc[NTH];
@@ -164,35 +166,47 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
     constexpr int PF = MOM ? 1 : 2;
     u32x4 rq[PF][UQ], rk[PF][UQ], rv[PF];
     float re[PF];
-    int goff_q[UQ], goff_v;
+    // staging: 16 lanes load one 256-byte Q/K row (8 lanes one 128-byte V row);
+    // chunk c of row r lands in block c/4 at swizzled position (c%4)^swz(r)
+    int goff_q[UQ], loff_q[UQ], goff_v, loff_v;
 #pragma unroll
     for (int x = 0; x < UQ; ++x) {
-        const int u = tid + x * NT, blk = u >> 8, row = (u >> 2) & 63, pos = u & 3;
-        goff_q[x] = row * (int)qL + 32 * blk + 8 * (pos ^ swz(row));   // token offset added per chunk
+        const int u = tid + x * NT, row = u / (DK / 8), ch = u % (DK / 8);
+        goff_q[x] = row * (int)qL + 8 * ch;                          // token offset added per chunk
+        loff_q[x] = (ch >> 2) * BLK + row * 32 + 8 * ((ch & 3) ^ swz(row));
     }
     {
-        const int u = tid, blk = u >> 8, row = (u >> 2) & 63, pos = u & 3;
-        goff_v = row * (int)vL + 32 * blk + 8 * (pos ^ swz(row));
+        const int row = tid >> 3, ch = tid & 7;
+        goff_v = row * (int)vL + 8 * ch;
+        loff_v = (ch >> 2) * BLKV + row * 32 + 8 * ((ch & 3) ^ swz(row));
     }
     const int kq_same = (qL == kL);
     auto load = [&](int c, auto SET) {
         constexpr int st = decltype(SET)::value;
         const int t0 = c * CS;
-        const bool full = (t0 + CS <= L);
         const bf16_t* Qc = Qg + (int64_t)t0 * qL;
         const bf16_t* Kc = Kg + (int64_t)t0 * kL;
+        const bf16_t* Vc = Vg + (int64_t)t0 * vL;
+        if (t0 + CS <= L) {          // whole chunk in range (uniform): plain loads
 #pragma unroll
-        for (int x = 0; x < UQ; ++x) {
-            const int u = tid + x * NT, row = (u >> 2) & 63;
-            const bool ok = full || (t0 + row < L);
-            const int ko = kq_same ? goff_q[x] : (row * (int)kL + (goff_q[x] - row * (int)qL));
-            rq[st][x] = ok ? *reinterpret_cast<const u32x4*>(Qc + goff_q[x]) : u32x4{0, 0, 0, 0};
-            rk[st][x] = ok ? *reinterpret_cast<const u32x4*>(Kc + ko) : u32x4{0, 0, 0, 0};
-        }
-        {
-            const int row = (tid >> 2) & 63;
-            const bool ok = full || (t0 + row < L);
-            rv[st] = ok ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)t0 * vL + goff_v) : u32x4{0, 0, 0, 0};
+            for (int x = 0; x < UQ; ++x) {
+                const int row = (tid + x * NT) / (DK / 8);
+                const int ko = kq_same ? goff_q[x] : (row * (int)kL + (goff_q[x] - row * (int)qL));
+                rq[st][x] = *reinterpret_cast<const u32x4*>(Qc + goff_q[x]);
+                rk[st][x] = *reinterpret_cast<const u32x4*>(Kc + ko);
+            }
+            rv[st] = *reinterpret_cast<const u32x4*>(Vc + goff_v);
+        } else {                     // ragged last chunk: zero-fill rows past L
+#pragma unroll
+            for (int x = 0; x < UQ; ++x) {
+                const int row = (tid + x * NT) / (DK / 8);
+                const bool ok = t0 + row < L;
+                const int ko = kq_same ? goff_q[x] : (row * (int)kL + (goff_q[x] - row * (int)qL));
+                rq[st][x] = ok ? *reinterpret_cast<const u32x4*>(Qc + goff_q[x]) : u32x4{0, 0, 0, 0};
+                rk[st][x] = ok ? *reinterpret_cast<const u32x4*>(Kc + ko) : u32x4{0, 0, 0, 0};
+            }
+            const bool ok = t0 + (tid >> 3) < L;
+            rv[st] = ok ? *reinterpret_cast<const u32x4*>(Vc + goff_v) : u32x4{0, 0, 0, 0};
         }
         if (tid < CS) {
             const int t = t0 + tid;
@@ -203,11 +217,10 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
         constexpr int st = decltype(SET)::value;
 #pragma unroll
         for (int x = 0; x < UQ; ++x) {
-            const int u = tid + x * NT;
-            *reinterpret_cast<u32x4*>(&sQ[buf][8 * u]) = rq[st][x];
-            *reinterpret_cast<u32x4*>(&sK[buf][8 * u]) = rk[st][x];
+            *reinterpret_cast<u32x4*>(&sQ[buf][loff_q[x]]) = rq[st][x];
+            *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = rk[st][x];
         }
-        *reinterpret_cast<u32x4*>(&sV[buf][8 * tid]) = rv[st];
+        *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = rv[st];
         if (tid < CS) {
             sE[buf][0][tid] = re[st];
             if (MOM) {
@@ -266,7 +279,6 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
     // chunk k travels in register set k % PF; chunk c+PF is requested while
     // chunk c computes, chunk c+1 is written to the other LDS buffer at the end
     auto iter = [&](int c, auto LSET, auto SSET) {
-        if (c + PF < ntiles) load(c + PF, LSET);
         const int cur = c & 1;
         const int tbase = c * CS;
         const int n = min(CS, L - tbase);
@@ -306,6 +318,10 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
         // half 0 has read half 1's partials before they are overwritten below
         __syncthreads();
         if (c > 0) write_out();
+        // Prefetch after the output store: the memory counter retires in
+        // order, so a later wait on the store's registers leaves these loads
+        // in flight instead of draining them.
+        if (c + PF < ntiles) load(c + PF, LSET);
 
         // ------------- value fragments (tokens in accperm order) scaled in registers
         bf16x8 VB[2], VS[MOM ? 2 : 1], VM[MOM ? 2 : 1];
