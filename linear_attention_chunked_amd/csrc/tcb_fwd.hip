@@ -1,12 +1,14 @@
 // tcb_fwd.hip -- bf16 chunked fast-weight forward for d_k in {64, 128} and
-// 64-column d_v tiles (the LM-scale and momentum shapes).
+// d_v tiles of 32 or 64 columns (the LM-scale and momentum shapes).
 //
 // Same mathematics as tc_fwd.hip (its header cites the pages' passages and
 // derives the momentum algebra); this is the gfx950-tuned form:
-//   * 8 waves per workgroup = 2 per SIMD.  Wave w owns state columns
-//     [16(w%4), +16) of the 64-column tile and one half of the d_k rows
-//     (w/4); the two halves of a column tile add their readout partial sums
-//     through LDS at the top of the next chunk, so no extra barrier is needed.
+//   * Wave w owns state columns [16(w%NNT), +16) of the column tile and one
+//     half of the d_k rows (w/NNT); the two halves of a column tile add their
+//     readout partial sums through LDS at the top of the next chunk, so no
+//     extra barrier is needed.  Tiles: CS tokens x DVT columns; the 32 x 32
+//     form (4 waves, ~50 KB LDS) runs two workgroups per CU with independent
+//     barriers, the 64 x 64 form (8 waves) one.
 //   * Q, K, V chunks are staged as plain row copies in a K-block-major
 //     layout [block of 32 features][token][32] with a 16-byte XOR swizzle
 //     (swz below): row reads, paired 8-byte reads and the transposing reads
@@ -20,7 +22,6 @@
 //   * eta and the momentum weights scale the V fragment in registers; the
 //     fp32 state is held in MFMA accumulators for the whole sequence and
 //     feeds the readout from registers.
-// Chunk tile = 64 tokens.
 #include "common.h"
 #include "internal.h"
 
@@ -32,11 +33,13 @@ namespace {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int CS = 64;                 // tokens per chunk tile
-constexpr int BLK = CS * 32 + 32;      // Q/K block stride: [token][32] + 64 B pad
-constexpr int BLKV = CS * 32 + 64;     // V block stride: [token][32] + 128 B pad
-// (the pads keep the row-order staging writes conflict free; reads never
-//  cross a block within one instruction)
+// Block strides (elements) of the [token][32] blocks: the pads keep the
+// row-order staging writes conflict free; reads never cross a block within
+// one instruction.
+template <int CS> constexpr int blk_qk() { return CS * 32 + 32; }
+template <int CS, int DVT> constexpr int blk_v() { return DVT == 64 ? CS * 32 + 64 : CS * 32; }
+// output tile swizzle: 16-byte chunk position of row i (rows of DVT columns)
+template <int DVT> TTT_DEV int oswz(int i) { return DVT == 64 ? ((i >> 1) & 7) : ((i >> 2) & 3); }
 
 TTT_DEV int swz(int r) { return (((r >> 2) & 1) << 1) | ((r >> 3) & 1); }
 // (row r, feature e) of a tile lives at element (e/32)*BLK + r*32 + 8*(((e/8)%4) ^ swz(r)) + e%8
@@ -59,9 +62,16 @@ TTT_DEV bf16x8 scale_frag(const bf16x8& f, const f32x4& s_lo, const f32x4& s_hi)
 
 }  // namespace
 
-template <int DK, int MODE>
-__global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
-    constexpr int DVT = 64, NT = 512;
+template <int DK, int MODE, int CS, int DVT>
+__global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
+    constexpr int NNT = DVT / 16;           // column tiles per workgroup
+    constexpr int NW = 2 * NNT, NT = 64 * NW;
+    static_assert((CS == 64 && DVT == 64) || (CS == 32 && DVT == 32), "tile forms: 64x64, 32x32");
+    constexpr int NTI = CS / 16;            // token tiles per chunk
+    constexpr int NJB = CS / 32;            // token K-blocks per chunk
+    constexpr int BLK = blk_qk<CS>();
+    constexpr int BLKV = blk_v<CS, DVT>();
+    constexpr int NVC = CS * DVT / 8;       // 16-byte chunks of a V tile
     constexpr int NKB = DK / 32;            // feature blocks of Q / K
     constexpr int DKH = DK / 2;             // d_k rows per wave
     constexpr int NTH = DKH / 16;           // state tiles per wave
@@ -74,16 +84,16 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
 
     __shared__ __attribute__((aligned(16))) bf16_t sQ[2][NKB * BLK];
     __shared__ __attribute__((aligned(16))) bf16_t sK[2][NKB * BLK];
-    __shared__ __attribute__((aligned(16))) bf16_t sV[2][2 * BLKV];
+    __shared__ __attribute__((aligned(16))) bf16_t sV[2][(DVT / 32) * BLKV];
     __shared__ __attribute__((aligned(16))) float sE[2][NV][CS];
     __shared__ __attribute__((aligned(16))) bf16_t sP[HAS_P ? CS * LP : 8];
-    __shared__ __attribute__((aligned(16))) f32x4 sX[4][4][64];   // half-1 readout partials
+    __shared__ __attribute__((aligned(16))) f32x4 sX[NNT][NTI][64];   // half-1 readout partials
     __shared__ __attribute__((aligned(16))) bf16_t sO[CS * DVT];  // finished output tile
     __shared__ float sTab[3 * (CS + 1)];                           // w_p | beta^p | a_p
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int nt = wave & 3, hf = wave >> 2;
+    const int nt = wave % NNT, hf = wave / NNT;
 
     int bh, vt;
     {
@@ -160,9 +170,12 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
         for (int kk = 0; kk < NKH; ++kk) Mop[kk] = acc_to_frag_bf16(Macc[2 * kk], Macc[2 * kk + 1]);
     }
 
-    // ---- staging: thread -> linear 16-byte chunk u of the [blk][row][4] layout
-    // register sets for chunks in flight: PF = 2 keeps two chunks of loads
-    // outstanding per workgroup (momentum keeps one: its VGPRs are taken)
+    // ---- staging: each 16-byte piece of a row goes to its swizzled slot of the
+    // K-block-major layout (16 lanes cover one 256-byte Q/K row)
+    // register sets for chunks in flight: chunk c+PF is requested after the
+    // output store of iteration c (the memory counter retires in order, so a
+    // later wait on the store leaves these loads in flight); momentum keeps
+    // one set, its VGPRs are taken by the second state
     constexpr int PF = MOM ? 1 : 2;
     u32x4 rq[PF][UQ], rk[PF][UQ], rv[PF];
     float re[PF];
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
         loff_q[x] = (ch >> 2) * BLK + row * 32 + 8 * ((ch & 3) ^ swz(row));
     }
     {
-        const int row = tid >> 3, ch = tid & 7;
+        const int row = tid / (DVT / 8), ch = tid % (DVT / 8);
         goff_v = row * (int)vL + 8 * ch;
         loff_v = (ch >> 2) * BLKV + row * 32 + 8 * ((ch & 3) ^ swz(row));
     }
@@ -187,25 +200,27 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
         const bf16_t* Qc = Qg + (int64_t)t0 * qL;
         const bf16_t* Kc = Kg + (int64_t)t0 * kL;
         const bf16_t* Vc = Vg + (int64_t)t0 * vL;
-        if (t0 + CS <= L) {          // whole chunk in range (uniform): plain loads
+        const bool full = (t0 + CS <= L);
+        if (full) {                  // whole chunk in range (uniform): plain loads
 #pragma unroll
             for (int x = 0; x < UQ; ++x) {
                 const int row = (tid + x * NT) / (DK / 8);
-                const int ko = kq_same ? goff_q[x] : (row * (int)kL + (goff_q[x] - row * (int)qL));
+                const int64_t ko = kq_same ? goff_q[x] : (int64_t)row * kL + 8 * ((tid + x * NT) % (DK / 8));
                 rq[st][x] = *reinterpret_cast<const u32x4*>(Qc + goff_q[x]);
                 rk[st][x] = *reinterpret_cast<const u32x4*>(Kc + ko);
             }
-            rv[st] = *reinterpret_cast<const u32x4*>(Vc + goff_v);
         } else {                     // ragged last chunk: zero-fill rows past L
 #pragma unroll
             for (int x = 0; x < UQ; ++x) {
                 const int row = (tid + x * NT) / (DK / 8);
                 const bool ok = t0 + row < L;
-                const int ko = kq_same ? goff_q[x] : (row * (int)kL + (goff_q[x] - row * (int)qL));
+                const int64_t ko = kq_same ? goff_q[x] : (int64_t)row * kL + 8 * ((tid + x * NT) % (DK / 8));
                 rq[st][x] = ok ? *reinterpret_cast<const u32x4*>(Qc + goff_q[x]) : u32x4{0, 0, 0, 0};
                 rk[st][x] = ok ? *reinterpret_cast<const u32x4*>(Kc + ko) : u32x4{0, 0, 0, 0};
             }
-            const bool ok = t0 + (tid >> 3) < L;
+        }
+        {
+            const bool ok = tid < NVC && (full || t0 + tid / (DVT / 8) < L);
             rv[st] = ok ? *reinterpret_cast<const u32x4*>(Vc + goff_v) : u32x4{0, 0, 0, 0};
         }
         if (tid < CS) {
@@ -220,7 +235,7 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
             *reinterpret_cast<u32x4*>(&sQ[buf][loff_q[x]]) = rq[st][x];
             *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = rk[st][x];
         }
-        *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = rv[st];
+        if (tid < NVC) *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = rv[st];
         if (tid < CS) {
             sE[buf][0][tid] = re[st];
             if (MOM) {
@@ -235,34 +250,39 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
     // P^T tile assignment (query tile ti; key tiles tjA, tjB; -1 = none), grouped by
     // query tile so a wave reuses its Q fragments
     int p_ti = -1, p_tjA = -1, p_tjB = -1;
-    switch (wave) {
-        case 0: p_ti = 3; p_tjA = 1; p_tjB = 2; break;
-        case 1: p_ti = 3; p_tjA = 0; p_tjB = 3; break;
-        case 2: p_ti = 2; p_tjA = 0; p_tjB = 1; break;
-        case 3: p_ti = 2; p_tjA = 2; break;
-        case 4: p_ti = 1; p_tjA = 0; p_tjB = 1; break;
-        case 5: p_ti = 0; p_tjA = 0; break;
-        default: break;
+    if (CS == 64) {
+        switch (wave) {
+            case 0: p_ti = 3; p_tjA = 1; p_tjB = 2; break;
+            case 1: p_ti = 3; p_tjA = 0; p_tjB = 3; break;
+            case 2: p_ti = 2; p_tjA = 0; p_tjB = 1; break;
+            case 3: p_ti = 2; p_tjA = 2; break;
+            case 4: p_ti = 1; p_tjA = 0; p_tjB = 1; break;
+            case 5: p_ti = 0; p_tjA = 0; break;
+            default: break;
+        }
+    } else {
+        if (wave == 0) { p_ti = 1; p_tjA = 0; p_tjB = 1; }
+        else if (wave == 1) { p_ti = 0; p_tjA = 0; }
     }
 
-    f32x4 oacc[4];    // this wave's readout partial of the previous chunk (half 0 keeps it)
+    f32x4 oacc[NTI];  // this wave's readout partial of the previous chunk (half 0 keeps it)
     int prev_base = 0, prev_n = 0;
     // half 0: add half 1's partial, round, and park the tile in sO (rows of 128 B,
     // 16-byte chunks swizzled by (row/2)%8: conflict-free for both sides)
     auto combine = [&]() {
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
+        for (int ti = 0; ti < NTI; ++ti) {
             const int i = 16 * ti + c16;
             const f32x4 o = oacc[ti] + sX[nt][ti][lane];
-            const int ch = (2 * nt + (g >> 1)) ^ ((i >> 1) & 7);
+            const int ch = (2 * nt + (g >> 1)) ^ oswz<DVT>(i);
             st4(&sO[i * DVT + 8 * ch + 4 * (g & 1)], o);
         }
     };
     // all threads: write the parked tile out as full 128-byte row segments
     auto write_out = [&]() {
-        const int row = tid >> 3, ch = tid & 7;
-        if (row < prev_n) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[row * DVT + 8 * (ch ^ ((row >> 1) & 7))]);
+        const int row = tid / (DVT / 8), ch = tid % (DVT / 8);
+        if (tid < NVC && row < prev_n) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[row * DVT + 8 * (ch ^ oswz<DVT>(row))]);
             *reinterpret_cast<u32x4*>(&Og[(int64_t)(prev_base + row) * oL + 8 * ch]) = w;
         }
     };
@@ -273,11 +293,11 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
     load(0, I0{});
     __syncthreads();   // tables ready
     store(0, 0, I0{});
-    if (PF == 2 && ntiles > 1) load(1, I1{});
+    if (ntiles > 1) load(1, I1{});
     __syncthreads();
 
-    // chunk k travels in register set k % PF; chunk c+PF is requested while
-    // chunk c computes, chunk c+1 is written to the other LDS buffer at the end
+    // chunk k travels in register set k % PF; chunk c+1 is written to the
+    // other LDS buffer at the end of iteration c
     auto iter = [&](int c, auto LSET, auto SSET) {
         const int cur = c & 1;
         const int tbase = c * CS;
@@ -318,15 +338,12 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
         // half 0 has read half 1's partials before they are overwritten below
         __syncthreads();
         if (c > 0) write_out();
-        // Prefetch after the output store: the memory counter retires in
-        // order, so a later wait on the store's registers leaves these loads
-        // in flight instead of draining them.
-        if (c + PF < ntiles) load(c + PF, LSET);
+        if (PF == 2 && c + 2 < ntiles) load(c + 2, LSET);
 
         // ------------- value fragments (tokens in accperm order) scaled in registers
-        bf16x8 VB[2], VS[MOM ? 2 : 1], VM[MOM ? 2 : 1];
+        bf16x8 VB[NJB], VS[MOM ? NJB : 1], VM[MOM ? NJB : 1];
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
+        for (int jb = 0; jb < NJB; ++jb) {
             const bf16x8 raw = join(tr_read(V + b_v + (32 * jb) * 32), tr_read(V + b_v + (32 * jb + 16) * 32));
             const float* e0 = &sE[cur][0][32 * jb + 4 * g];
             VB[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e0), *reinterpret_cast<const f32x4*>(e0 + 16));
@@ -340,17 +357,18 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
 
         // ------------- readout partial: O^T = S_h^T Q_h^T (+ a_i m_h^T Q_h^T) (+ V~^T P^T share)
         {
-            f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-            f32x4 acc2[MOM ? 4 : 1];
-            if (MOM) {
+            f32x4 acc[NTI];
+            f32x4 acc2[MOM ? NTI : 1];
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) acc2[ti] = zero4();
+            for (int ti = 0; ti < NTI; ++ti) {
+                acc[ti] = zero4();
+                if (MOM) acc2[ti] = zero4();
             }
             const bf16_t* Qh = Q + hf * NKH * BLK;
 #pragma unroll
             for (int kk = 0; kk < NKH; ++kk) {
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
+                for (int ti = 0; ti < NTI; ++ti) {
                     const u32x2 lo = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap0);
                     const u32x2 hi = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap1);
                     const bf16x8 bq = join(lo, hi);
@@ -361,14 +379,14 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
             if (HAS_P) {
                 // half 0 takes key block 0 of every query tile, half 1 key block 1 (ti >= 2)
 #pragma unroll
-                for (int ti = 0; ti < 4; ++ti) {
+                for (int ti = 0; ti < NTI; ++ti) {
                     const bf16_t* prow = &sP[(16 * ti + c16) * LP];
                     if (hf == 0) mma(acc[ti], VB[0], ld_accperm(prow, 0, g));
-                    else if (ti >= 2) mma(acc[ti], VB[1], ld_accperm(prow, 32, g));
+                    else if (NJB > 1 && ti >= 2) mma(acc[ti], VB[NJB - 1], ld_accperm(prow, 32, g));
                 }
             }
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
+            for (int ti = 0; ti < NTI; ++ti) {
                 f32x4 o = acc[ti];
                 if (MOM) o += sTab[2 * (CS + 1) + 16 * ti + c16] * acc2[ti];
                 if (hf == 0) oacc[ti] = o;
@@ -392,7 +410,7 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
             }
             const bf16_t* Kh = K + (hf * NTH / 2) * BLK;   // d_k half -> feature blocks
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
+            for (int jb = 0; jb < NJB; ++jb) {
 #pragma unroll
                 for (int t = 0; t < NTH; ++t) {
                     const int base = (t >> 1) * BLK + ((t & 1) ? b_tr1 : b_tr0) + (32 * jb) * 32;
@@ -416,6 +434,7 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
             }
         }
         if (c + 1 < ntiles) store(c + 1, cur ^ 1, SSET);
+        if (PF == 1 && c + 2 < ntiles) load(c + 2, LSET);
         __syncthreads();
     };
     for (int c = 0; c < ntiles; c += 2) {
@@ -444,26 +463,45 @@ __global__ __launch_bounds__(512) void tcb_fwd_kernel(TcParams p) {
 }
 
 bool tcb_supported(int dtype, int dk, int dv) {
-    return dtype == 1 && (dk == 64 || dk == 128) && (dv == 64 || dv == 128);
+    return dtype == 1 && (dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128);
 }
 
-hipError_t launch_tcb_fwd(const TcParams& pin, int mode, hipStream_t s) {
+// cs / dvt: chunk tile and column tile (64 x 64 or 32 x 32)
+hipError_t launch_tcb_fwd_cfg(const TcParams& pin, int mode, int cs, int dvt, hipStream_t s) {
     TcParams p = pin;
-    p.n_vt = p.dv / 64;
+    if (p.dv % dvt != 0) return hipErrorInvalidValue;
+    p.n_vt = p.dv / dvt;
     p.xcd_map = ((p.B * p.H) % 8 == 0) ? 1 : 0;
-    const dim3 grid(p.B * p.H * p.n_vt), block(512);
-#define TTT_L(DK_, M_) hipLaunchKernelGGL((tcb_fwd_kernel<DK_, M_>), grid, block, 0, s, p)
-    if (p.dk == 128) {
-        if (mode == MODE_TC) TTT_L(128, MODE_TC);
-        else if (mode == MODE_MOM) TTT_L(128, MODE_MOM);
-        else TTT_L(128, MODE_CC);
-    } else {
-        if (mode == MODE_TC) TTT_L(64, MODE_TC);
-        else if (mode == MODE_MOM) TTT_L(64, MODE_MOM);
-        else TTT_L(64, MODE_CC);
+    const dim3 grid(p.B * p.H * p.n_vt), block(dvt / 16 * 128);
+#define TTT_L(DK_, M_, CS_, DVT_) hipLaunchKernelGGL((tcb_fwd_kernel<DK_, M_, CS_, DVT_>), grid, block, 0, s, p)
+#define TTT_M(CS_, DVT_)                                              \
+    if (cs == CS_ && dvt == DVT_) {                                    \
+        if (p.dk == 128) {                                             \
+            if (mode == MODE_TC) TTT_L(128, MODE_TC, CS_, DVT_);       \
+            else if (mode == MODE_MOM) TTT_L(128, MODE_MOM, CS_, DVT_); \
+            else TTT_L(128, MODE_CC, CS_, DVT_);                       \
+        } else {                                                       \
+            if (mode == MODE_TC) TTT_L(64, MODE_TC, CS_, DVT_);        \
+            else if (mode == MODE_MOM) TTT_L(64, MODE_MOM, CS_, DVT_);  \
+            else TTT_L(64, MODE_CC, CS_, DVT_);                        \
+        }                                                              \
+        return hipGetLastError();                                      \
     }
+    TTT_M(64, 64)
+    TTT_M(32, 32)
+#undef TTT_M
 #undef TTT_L
-    return hipGetLastError();
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_tcb_fwd(const TcParams& p, int mode, hipStream_t s) {
+    // chunk-causal needs the tile to divide the semantic chunk
+    // 64 x 64 tiles whenever they fit: measured faster than 32 x 32 tiles with
+    // two workgroups per CU on the LM-scale and momentum shapes (the 32-token
+    // chunk doubles the per-chunk synchronisation)
+    const bool cc32 = (mode == MODE_CC) && (p.chunk % 64 != 0);
+    if (p.dv % 64 != 0 || cc32) return launch_tcb_fwd_cfg(p, mode, 32, 32, s);
+    return launch_tcb_fwd_cfg(p, mode, 64, 64, s);
 }
 
 }  // namespace ttt

@@ -157,6 +157,16 @@ def test_c2_full_sampled_heads():
     assert torch.isfinite(got[0].float()).all()
 
 
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_token_causal_bf16_wide_grid(beta):
+    """B*H*d_v/64 >= 512 selects the 64-token x 64-column tiling (8 waves)."""
+    inp = W.gen_c2(B=16, H=16, L=150, d=128)
+    inp.beta = W.f32(beta)
+    say(f"bf16 token-causal wide grid B16 H16 L150 beta{beta}")
+    got = run_fwd(inp)
+    check(inp, got, oracle_tc(inp, [(0, 0), (7, 3), (15, 15)]), TOL["bf16"], "wide grid")
+
+
 def test_c4_momentum_small():
     inp = W.gen_c4(B=2, H=2, L=700, d=128)
     say("c4-recipe momentum bf16 B2 H2 L700")
