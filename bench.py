@@ -1,6 +1,6 @@
 """Benchmark of the chunked TTT fast-weight forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm-scale]
 
 One step = one full pass of the hot path over one batch of synthetic input
 (all inputs resident in HBM before timing): for the default LM-scale
@@ -38,6 +38,7 @@ METRIC = "tokens/s + TFLOP/s (MFMA % of peak) for chunked TTT fast-weight forwar
 
 KERNEL_SOURCES = {
     "tc_fwd_kernel": ("tc_fwd.hip", "common.h"),
+    "tcb_fwd_kernel": ("tcb_fwd.hip", "common.h"),
     "ip_update_kernel+ip_readout_kernel": ("inplace.hip", "common.h"),
     "dual_fwd_kernel": ("dual.hip", "common.h"),
 }
@@ -62,8 +63,8 @@ def setup_workload(name: str, dev: str):
     import workloads as W
     import linear_attention_chunked_amd as lac
 
-    if name in ("c1", "c2", "c4"):
-        gen = {"c1": W.gen_c1, "c2": W.gen_c2, "c4": W.gen_c4}[name]
+    if name in ("small-f32", "lm-scale", "momentum"):
+        gen = {"small-f32": W.gen_small_f32, "lm-scale": W.gen_lm_scale, "momentum": W.gen_momentum}[name]
         inp = gen()
         B, H, L, dk = inp.q.shape
         dv = inp.v.shape[-1]
@@ -89,14 +90,14 @@ def setup_workload(name: str, dev: str):
         info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, mode="token_causal",
                     beta=inp.beta, eta="per-token" if eta is not None else inp.eta_scalar,
                     dtype=inp.dtype, tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
-                    kernel="tc_fwd_kernel", inputs=inp)
+                    kernel="tcb_fwd_kernel" if inp.dtype == "bf16" else "tc_fwd_kernel", inputs=inp)
         return step, info
-    if name in ("c3a", "c3b"):
-        L = 32768 if name == "c3a" else 131072
+    if name in ("inplace-32k", "inplace-128k"):
+        L = 32768 if name == "inplace-32k" else 131072
         d_ff, d_model = 9728, 2560
         Z = torch.empty((1, 1, L, d_ff), dtype=torch.bfloat16, device=dev)
         V = torch.empty((1, 1, L, d_model), dtype=torch.bfloat16, device=dev)
-        inp = W.gen_c3(L=L, out=(Z, V))
+        inp = W.gen_inplace(L=L, out=(Z, V))
         W0 = inp.S0.to(dev)
         out = torch.empty((1, 1, L, d_model), dtype=torch.bfloat16, device=dev)
 
@@ -111,9 +112,9 @@ def setup_workload(name: str, dev: str):
                     bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="ip_update_kernel+ip_readout_kernel",
                     inputs=None)
         return step, info
-    if name in ("c5a", "c5b"):
-        mb = 16 if name == "c5a" else 2048
-        inp = W.gen_c5(minibatch=mb)
+    if name in ("dual-b16", "dual-b2048"):
+        mb = 16 if name == "dual-b16" else 2048
+        inp = W.gen_dual(minibatch=mb)
         B, H, L, d = inp.q.shape
         q, k, v, W0 = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.W0.to(dev)
         out = torch.empty_like(v)
@@ -143,15 +144,15 @@ def cpu_baseline(info) -> dict:
     B, H = inp.q.shape[:2]
     L = inp.q.shape[2]
     heads = B * H
-    if info["workload"] == "c4":
+    if info["workload"] == "momentum":
         heads = min(heads, 8)
-    if info["workload"] in ("c5a", "c5b"):
+    if info["workload"] in ("dual-b16", "dual-b2048"):
         heads = min(heads, 32)
     bsel = max(1, heads // H)
     hsel = min(H, heads)
     sl = lambda t: None if t is None else W.to_f64(t[:bsel, :hsel])
     args = [sl(inp.q), sl(inp.k), sl(inp.v)]
-    if info["workload"] in ("c5a", "c5b"):
+    if info["workload"] in ("dual-b16", "dual-b2048"):
         W0 = sl(inp.W0)
         t0 = time.perf_counter()
         oracle.dual_primal(*args, W0, inp.eta, inp.minibatch)
@@ -185,7 +186,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", help="c2 (default, LM-scale), c1, c3a, c3b, c4, c5a, c5b")
+    ap.add_argument("--workload", default="lm-scale",
+                    help="lm-scale (default), small-f32, inplace-32k, inplace-128k, momentum, dual-b16, dual-b2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")

@@ -186,8 +186,9 @@ ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk
  * q, k [B,H,L,d], v, out [B,H,L,dv] contiguous, dtype `dtype`; W0
  * [B,H,d,dv] fp32 (W0_stride_bh elements between heads, 0 broadcasts one
  * W0); W_final [B,H,d,dv] fp32 contiguous or NULL.  Supported: d = 64,
- * dv = 64, bf16 or fp32, minibatch >= 1 a multiple of 16 (the last
- * mini-batch may be shorter).  Needs no workspace.
+ * dv = 64, bf16 or fp32, any minibatch >= 1 (the last mini-batch holds
+ * the remaining L - (ceil(L/minibatch)-1)*minibatch tokens).  Needs no
+ * workspace.
  */
 ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
                                int32_t minibatch, int32_t dtype,

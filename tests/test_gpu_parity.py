@@ -84,12 +84,12 @@ def whole_rel(inp, got, ref):
 
 
 # ------------------------------------------------------------- token-causal
-def test_c1_token_causal_fp32():
-    inp = W.gen_c1()
-    say("c1 fp32 B1 H2 L256 d32 C64")
+def test_small_f32_token_causal():
+    inp = W.gen_small_f32()
+    say("small fp32 B1 H2 L256 d32 C64")
     got = run_fwd(inp)
     ref = oracle_tc(inp)
-    check(inp, got, ref, TOL["f32"], "c1")
+    check(inp, got, ref, TOL["f32"], "small fp32")
     # the O(L^2) brute force agrees too
     bf = oracle.bruteforce_token_causal(inp.q, inp.k, inp.v, eta_scalar=inp.eta_scalar)
     assert oracle.rel_l2(got[0], bf) <= TOL["f32"]
@@ -128,15 +128,15 @@ def test_token_causal_fp32_integer_exact():
         assert np.array_equal(Sf[b, h].double().numpy(), S[0, 0])
 
 
-def test_c2_small_bf16_ragged():
-    inp = W.gen_c2(B=2, H=3, L=250, d=128)
-    say("c2-recipe bf16 B2 H3 L250 d128")
-    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "c2 small")
+def test_lm_recipe_small_bf16_ragged():
+    inp = W.gen_lm_scale(B=2, H=3, L=250, d=128)
+    say("LM recipe bf16 B2 H3 L250 d128")
+    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "LM recipe small")
 
 
 @pytest.mark.parametrize("d,dv", [(64, 64), (32, 32), (128, 64), (64, 128)])
 def test_token_causal_bf16_shapes(d, dv):
-    inp = W.gen_c2(B=1, H=4, L=200, d=d)
+    inp = W.gen_lm_scale(B=1, H=4, L=200, d=d)
     if dv != d:
         g = torch.Generator().manual_seed(5)
         inp.v = torch.randn(1, 4, 200, dv, generator=g).to(torch.bfloat16)
@@ -145,40 +145,40 @@ def test_token_causal_bf16_shapes(d, dv):
     check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "bf16 shapes")
 
 
-def test_c2_full_sampled_heads():
+def test_lm_scale_full_sampled_heads():
     """Full LM-scale workload (B8 H16 L4096 d128 C64) in the benchmark's launch
     configuration; sampled heads checked against the oracle."""
-    inp = W.gen_c2()
-    say("c2 full B8 H16 L4096 d128")
+    inp = W.gen_lm_scale()
+    say("LM-scale full B8 H16 L4096 d128")
     got = run_fwd(inp)
     heads = [(0, 0), (3, 7), (5, 15), (7, 9)]
     ref = oracle_tc(inp, heads)
-    check(inp, got, ref, TOL["bf16"], "c2 full")
+    check(inp, got, ref, TOL["bf16"], "LM-scale full")
     assert torch.isfinite(got[0].float()).all()
 
 
 @pytest.mark.parametrize("beta", [0.0, 0.9])
 def test_token_causal_bf16_wide_grid(beta):
     """B*H*d_v/64 >= 512 selects the 64-token x 64-column tiling (8 waves)."""
-    inp = W.gen_c2(B=16, H=16, L=150, d=128)
+    inp = W.gen_lm_scale(B=16, H=16, L=150, d=128)
     inp.beta = W.f32(beta)
     say(f"bf16 token-causal wide grid B16 H16 L150 beta{beta}")
     got = run_fwd(inp)
     check(inp, got, oracle_tc(inp, [(0, 0), (7, 3), (15, 15)]), TOL["bf16"], "wide grid")
 
 
-def test_c4_momentum_small():
-    inp = W.gen_c4(B=2, H=2, L=700, d=128)
-    say("c4-recipe momentum bf16 B2 H2 L700")
-    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "c4 small")
+def test_momentum_small():
+    inp = W.gen_momentum(B=2, H=2, L=700, d=128)
+    say("momentum recipe bf16 B2 H2 L700")
+    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "momentum small")
 
 
-def test_c4_full_sampled_heads():
-    inp = W.gen_c4()
-    say("c4 full B4 H8 L16384 d128 beta0.9")
+def test_momentum_full_sampled_heads():
+    inp = W.gen_momentum()
+    say("momentum full B4 H8 L16384 d128 beta0.9")
     got = run_fwd(inp)
     ref = oracle_tc(inp, [(0, 0), (2, 5), (3, 7)])
-    check(inp, got, ref, TOL["bf16"], "c4 full")
+    check(inp, got, ref, TOL["bf16"], "momentum full")
 
 
 # ------------------------------------------------------------- chunk-causal
@@ -232,7 +232,7 @@ def test_state_scan_integer_exact():
 def test_scan_matches_fused_forward_states():
     """Chunk aggregates scanned on the GPU reproduce the state the fused
     forward kernel carries (momentum, ragged tail)."""
-    inp = W.gen_c4(B=1, H=2, L=300, d=32)
+    inp = W.gen_momentum(B=1, H=2, L=300, d=32)
     inp.q, inp.k, inp.v = inp.q.float(), inp.k.float(), inp.v.float()
     dS, dM = oracle.chunk_aggregates(inp.k, inp.v, None, inp.eta_scalar, inp.beta, 32)
     dS, dM = torch.from_numpy(dS).float(), torch.from_numpy(dM).float()
@@ -263,29 +263,29 @@ def check_dual(inp, got, heads, tol, what):
 
 @pytest.mark.parametrize("mb,L", [(16, 300), (64, 1000), (2048, 4096), (1, 70), (48, 200)])
 def test_dual_small(mb, L):
-    inp = W.gen_c5(B=1, H=2, L=L, minibatch=mb)
+    inp = W.gen_dual(B=1, H=2, L=L, minibatch=mb)
     say(f"dual bf16 b{mb} L{L}")
     check_dual(inp, run_dual(inp), [(0, 0), (0, 1)], TOL["bf16"], "dual")
 
 
 @pytest.mark.parametrize("mb", [16, 40])
 def test_dual_fp32(mb):
-    inp = W.gen_c5(B=1, H=2, L=256, minibatch=mb)
+    inp = W.gen_dual(B=1, H=2, L=256, minibatch=mb)
     inp.q, inp.k, inp.v = inp.q.float(), inp.k.float(), inp.v.float()
     say(f"dual fp32 b{mb}")
     check_dual(inp, run_dual(inp), [(0, 0), (0, 1)], TOL["f32"], "dual fp32")
 
 
 @pytest.mark.parametrize("mb", [16, 2048])
-def test_c5_full_sampled_heads(mb):
-    inp = W.gen_c5(minibatch=mb)
-    say(f"c5 full B4 H16 L8192 d64 b{mb}")
-    check_dual(inp, run_dual(inp), [(0, 0), (1, 9), (3, 15)], TOL["bf16"], f"c5 b{mb}")
+def test_dual_full_sampled_heads(mb):
+    inp = W.gen_dual(minibatch=mb)
+    say(f"dual full B4 H16 L8192 d64 b{mb}")
+    check_dual(inp, run_dual(inp), [(0, 0), (1, 9), (3, 15)], TOL["bf16"], f"dual b{mb}")
 
 
 def test_dual_fixed_point_exact():
     """v = k W0 makes every gradient zero: out = q W0 exactly (fp32)."""
-    inp = W.gen_c5(B=1, H=2, L=200, minibatch=16)
+    inp = W.gen_dual(B=1, H=2, L=200, minibatch=16)
     q, k = inp.q.float(), inp.k.float()
     out, Wf = lac.dual_form_fwd(q.to(DEV), k.to(DEV), (0.5 * k).to(DEV), inp.W0.to(DEV), eta=inp.eta,
                                 minibatch=16, return_state=True)
@@ -296,7 +296,7 @@ def test_dual_fixed_point_exact():
 
 # ------------------------------------------------------------- properties
 def test_head_isolation_and_determinism():
-    inp = W.gen_c2(B=2, H=4, L=256, d=64)
+    inp = W.gen_lm_scale(B=2, H=4, L=256, d=64)
     o1 = run_fwd(inp)[0]
     o2 = run_fwd(inp)[0]
     assert torch.equal(o1, o2), "repeated calls must be bit-identical"
@@ -380,7 +380,7 @@ def test_inplace_full_sampled_rows(L):
     Vd = torch.empty((1, 1, L, 2560), dtype=torch.bfloat16, device=DEV)
     Zc = torch.empty((1, 1, L, 9728), dtype=torch.bfloat16)
     Vc = torch.empty((1, 1, L, 2560), dtype=torch.bfloat16)
-    inp = W.gen_c3(L=L, out=(Zc, Vc))
+    inp = W.gen_inplace(L=L, out=(Zc, Vc))
     Zd.copy_(Zc)
     Vd.copy_(Vc)
     say("in-place full: running")

@@ -16,12 +16,12 @@ workload is drawn chunk by chunk (``seed = 3_000_000 + 4*i + j`` for chunk
 ``i``; j = 0 a, 1 b, 2 V-hat) so a host never holds fp32 copies of the
 long-context tensors.
 
-Workloads (shapes of the pages' settings; see the design doc for the recipe):
-  c1  token-causal fp32, B1 H2 L256 d32, C64, eta 0.1, S0 0
-  c2  token-causal bf16, B8 H16 L4096 d128, C64, per-token eta, S0 ~ N(0, 0.02^2)
-  c3  In-Place chunk-causal Wdown update, L 32768 / 131072, d_ff 9728, d_model 2560, C1024
-  c4  momentum token-causal bf16, B4 H8 L16384 d128, C128, eta 0.05, beta 0.9
-  c5  TTT-Linear mini-batch dual form, B4 H16 L8192 d64, b 16 and 2048, W0 0.5 I
+Workloads (shapes of the pages' settings):
+  small-f32   token-causal fp32, B1 H2 L256 d32, C64, eta 0.1, S0 0
+  lm-scale    token-causal bf16, B8 H16 L4096 d128, C64, per-token eta, S0 ~ N(0, 0.02^2)
+  inplace     In-Place chunk-causal Wdown update, L 32768 / 131072, d_ff 9728, d_model 2560, C1024
+  momentum    momentum token-causal bf16, B4 H8 L16384 d128, C128, eta 0.05, beta 0.9
+  dual        TTT-Linear mini-batch dual form, B4 H16 L8192 d64, b 16 and 2048, W0 0.5 I
 """
 from __future__ import annotations
 
@@ -75,19 +75,19 @@ class DualInputs:
     meta: dict = field(default_factory=dict)
 
 
-# --------------------------------------------------------------------------- c1
-def gen_c1(B=1, H=2, L=256, d=32, chunk=64, seed_base=1000) -> TokenCausalInputs:
+# ------------------------------------------------------------------ small fp32
+def gen_small_f32(B=1, H=2, L=256, d=32, chunk=64, seed_base=1000) -> TokenCausalInputs:
     """fp32 q,k,v ~ N(0,1)/sqrt(d); constant eta 0.1; S0 = 0."""
     s = 1.0 / math.sqrt(d)
     q = _randn((B, H, L, d), seed_base + 0) * s
     k = _randn((B, H, L, d), seed_base + 1) * s
     v = _randn((B, H, L, d), seed_base + 2) * s
     return TokenCausalInputs(q, k, v, None, f32(0.1), 0.0, None, None, chunk, "f32",
-                             dict(workload="c1", B=B, H=H, L=L, dk=d, dv=d))
+                             dict(workload="small-f32", B=B, H=H, L=L, dk=d, dv=d))
 
 
-# --------------------------------------------------------------------------- c2
-def gen_c2(B=8, H=16, L=4096, d=128, chunk=64, seed_base=2000) -> TokenCausalInputs:
+# ------------------------------------------------------------------ LM-scale
+def gen_lm_scale(B=8, H=16, L=4096, d=128, chunk=64, seed_base=2000) -> TokenCausalInputs:
     """bf16 q,v ~ N(0,1); k ~ N(0,1) L2-normalised per token in fp32, then bf16;
     per-token eta = 0.1*sigmoid(N(0,1)) kept in fp32; S0 ~ N(0, 0.02^2) fp32."""
     q = _randn((B, H, L, d), seed_base + 0).to(torch.bfloat16)
@@ -98,29 +98,29 @@ def gen_c2(B=8, H=16, L=4096, d=128, chunk=64, seed_base=2000) -> TokenCausalInp
     eta = (0.1 * torch.sigmoid(_randn((B, H, L), seed_base + 3))).float()
     S0 = _randn((B, H, d, d), seed_base + 4) * 0.02
     return TokenCausalInputs(q, k, v, eta, 0.0, 0.0, S0, None, chunk, "bf16",
-                             dict(workload="c2", B=B, H=H, L=L, dk=d, dv=d))
+                             dict(workload="lm-scale", B=B, H=H, L=L, dk=d, dv=d))
 
 
-# --------------------------------------------------------------------------- c3
-C3_SEED = 3_000_000
+# ------------------------------------------------------------------ In-Place
+INPLACE_SEED = 3_000_000
 
 
-def gen_c3_chunk(i: int, rows: int, d_ff=9728, d_model=2560):
+def gen_inplace_chunk(i: int, rows: int, d_ff=9728, d_model=2560):
     """Chunk i of the In-Place workload: Z_i = silu(a)*b (from bf16 a, b, computed
     in fp32, rounded to bf16) and the target V-hat_i ~ N(0,1) bf16."""
-    a = _randn((rows, d_ff), C3_SEED + 4 * i + 0).to(torch.bfloat16).float()
-    b = _randn((rows, d_ff), C3_SEED + 4 * i + 1).to(torch.bfloat16).float()
+    a = _randn((rows, d_ff), INPLACE_SEED + 4 * i + 0).to(torch.bfloat16).float()
+    b = _randn((rows, d_ff), INPLACE_SEED + 4 * i + 1).to(torch.bfloat16).float()
     z = (torch.nn.functional.silu(a) * b).to(torch.bfloat16)
     del a, b
-    vh = _randn((rows, d_model), C3_SEED + 4 * i + 2).to(torch.bfloat16)
+    vh = _randn((rows, d_model), INPLACE_SEED + 4 * i + 2).to(torch.bfloat16)
     return z, vh
 
 
-def gen_c3_W0(d_ff=9728, d_model=2560, seed=3000):
+def gen_inplace_W0(d_ff=9728, d_model=2560, seed=3000):
     return _randn((d_ff, d_model), seed) * 0.02
 
 
-def gen_c3(L=32768, d_ff=9728, d_model=2560, chunk=1024, gen_block=1024, out=None):
+def gen_inplace(L=32768, d_ff=9728, d_model=2560, chunk=1024, gen_block=1024, out=None):
     """Whole In-Place workload.  Z, V-hat are [1,1,L,d] bf16 (B=H=1); the same
     tensor Z serves as both query and key.  ``out`` may give preallocated
     (Z, V) tensors (on any device) that are filled block by block."""
@@ -133,27 +133,27 @@ def gen_c3(L=32768, d_ff=9728, d_model=2560, chunk=1024, gen_block=1024, out=Non
     for i in range(nblk):
         r0 = i * gen_block
         rows = min(gen_block, L - r0)
-        z, vh = gen_c3_chunk(i, rows, d_ff, d_model)
+        z, vh = gen_inplace_chunk(i, rows, d_ff, d_model)
         Z[0, 0, r0:r0 + rows].copy_(z)
         V[0, 0, r0:r0 + rows].copy_(vh)
-    W0 = gen_c3_W0(d_ff, d_model).reshape(1, 1, d_ff, d_model)
+    W0 = gen_inplace_W0(d_ff, d_model).reshape(1, 1, d_ff, d_model)
     return TokenCausalInputs(Z, Z, V, None, f32(1e-3), 0.0, W0, None, chunk, "bf16",
-                             dict(workload="c3", B=1, H=1, L=L, dk=d_ff, dv=d_model))
+                             dict(workload="inplace", B=1, H=1, L=L, dk=d_ff, dv=d_model))
 
 
-# --------------------------------------------------------------------------- c4
-def gen_c4(B=4, H=8, L=16384, d=128, chunk=128, seed_base=4000) -> TokenCausalInputs:
+# ------------------------------------------------------------------ momentum
+def gen_momentum(B=4, H=8, L=16384, d=128, chunk=128, seed_base=4000) -> TokenCausalInputs:
     """bf16 q,k,v ~ N(0,1)/sqrt(d); eta 0.05; beta 0.9; S0 = M0 = 0."""
     s = 1.0 / math.sqrt(d)
     q = (_randn((B, H, L, d), seed_base + 0) * s).to(torch.bfloat16)
     k = (_randn((B, H, L, d), seed_base + 1) * s).to(torch.bfloat16)
     v = (_randn((B, H, L, d), seed_base + 2) * s).to(torch.bfloat16)
     return TokenCausalInputs(q, k, v, None, f32(0.05), f32(0.9), None, None, chunk, "bf16",
-                             dict(workload="c4", B=B, H=H, L=L, dk=d, dv=d))
+                             dict(workload="momentum", B=B, H=H, L=L, dk=d, dv=d))
 
 
-# --------------------------------------------------------------------------- c5
-def gen_c5(B=4, H=16, L=8192, d=64, minibatch=16, seed_base=5000) -> DualInputs:
+# ------------------------------------------------------------------ dual form
+def gen_dual(B=4, H=16, L=8192, d=64, minibatch=16, seed_base=5000) -> DualInputs:
     """bf16 q,k,v ~ N(0,1)/sqrt(d); W0 = 0.5*I fp32 per (b,h); eta = 1/d."""
     s = 1.0 / math.sqrt(d)
     q = (_randn((B, H, L, d), seed_base + 0) * s).to(torch.bfloat16)
@@ -161,7 +161,7 @@ def gen_c5(B=4, H=16, L=8192, d=64, minibatch=16, seed_base=5000) -> DualInputs:
     v = (_randn((B, H, L, d), seed_base + 2) * s).to(torch.bfloat16)
     W0 = (0.5 * torch.eye(d, dtype=torch.float32)).expand(B, H, d, d).contiguous()
     return DualInputs(q, k, v, W0, f32(1.0 / d), minibatch, "bf16",
-                      dict(workload="c5", B=B, H=H, L=L, d=d))
+                      dict(workload="dual", B=B, H=H, L=L, d=d))
 
 
 def gen_state_deltas(B, H, N, dk, dv, seed=6000, scale=1.0, integer=False):
