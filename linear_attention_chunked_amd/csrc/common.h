@@ -41,6 +41,16 @@ TTT_DEV uint32_t pack2bf(float lo, float hi) {
 
 TTT_DEV f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// The dispatcher hands workgroups to the 8 XCDs round-robin in linear
+// workgroup order (XCD = id % 8), and each XCD has its own L2.  This maps the
+// hardware id to a logical id such that every XCD runs one contiguous range
+// of logical ids; ordering tiles by logical id then keeps tiles that share
+// operands on one L2.  A bijection on [0, n).
+TTT_DEV int xcd_logical(int id, int n) {
+    const int q = n >> 3, r = n & 7, x = id & 7, k = id >> 3;
+    return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
+}
+
 // ---------------------------------------------------------------- type traits
 template <typename T> struct Tr;
 

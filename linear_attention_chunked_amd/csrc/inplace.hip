@@ -98,9 +98,12 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 waves, 128 x 64 each
     const int tiles_n = p.dv / IPU_BN;
-    const int tile = blockIdx.x;
+    // logical order (bh, dk tile, dv tile): the workgroups one XCD runs at a
+    // time share a few Z column slices and stream them through one L2
+    const int lid = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+    const int tile = lid % gridDim.x;
     const int m0 = (tile / tiles_n) * IP_BM, n0 = (tile % tiles_n) * IPU_BN;
-    const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+    const int bh = lid / gridDim.x, b = bh / p.H, h = bh % p.H;
     const bf16_t* Zg = p.k + b * p.ks[0] + h * p.ks[1] + m0;
     const bf16_t* Vg = p.v + b * p.vs[0] + h * p.vs[1] + n0;
     const float* Eg = p.eta ? p.eta + b * p.es[0] + h * p.es[1] : nullptr;
@@ -262,14 +265,18 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_n = p.dv / IP_BM;                 // dv tiles
     const int tiles_t = p.chunk / IP_BN;              // token tiles per chunk
-    int x = blockIdx.x;
+    // logical order (bh, chunk, token tile, dv tile): one XCD runs the tiles
+    // of one chunk together, so they share the chunk's Z rows and snapshot
+    // columns through its L2
+    const int lid = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+    int x = lid % gridDim.x;
     const int nt = x % tiles_n;
     x /= tiles_n;
     const int tt = x % tiles_t;
     const int chunk = x / tiles_t;
     const int n0 = nt * IP_BM;                        // dv offset
     const int t0 = chunk * p.chunk + tt * IP_BN;      // token offset
-    const int bh = blockIdx.y, b = bh / p.H, h = bh % p.H;
+    const int bh = lid / gridDim.x, b = bh / p.H, h = bh % p.H;
     if (t0 >= p.L) return;                            // whole tile past the end (uniform)
     const bf16_t* S = p.snap + ((int64_t)bh * p.nchunks + chunk) * p.dk * p.dv + (int64_t)n0 * p.dk;
     const bf16_t* Zg = p.q + b * p.qs[0] + h * p.qs[1];
