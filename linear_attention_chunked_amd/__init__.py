@@ -186,6 +186,21 @@ def fwd_chunked(q, k, v, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None
     return out
 
 
+def fwd_workspace_size(B, H, L, dk, dv, *, dtype=torch.bfloat16, beta=0.0, chunk=64,
+                       mode="token_causal") -> int:
+    """Bytes of device workspace ``ttt_fwd_chunked`` needs for these sizes
+    (``ttt_fwd_workspace_size``; no tensors, no GPU needed)."""
+    lib = load_library()
+    a = FwdArgs()
+    a.B, a.H, a.L, a.dk, a.dv, a.chunk = int(B), int(H), int(L), int(dk), int(dv), int(chunk)
+    a.mode = _MODES[mode] if isinstance(mode, str) else int(mode)
+    a.dtype = TTT_F32 if dtype == torch.float32 else TTT_BF16
+    a.beta = float(beta)
+    ws = ctypes.c_size_t(0)
+    _check(lib.ttt_fwd_workspace_size(ctypes.byref(a), ctypes.byref(ws)))
+    return int(ws.value)
+
+
 def chunk_state_scan(dS, dM=None, *, beta=0.0, chunk, L, S0=None, M0=None, stream=None):
     """Exclusive scan of chunk-state deltas (``ttt_chunk_state_scan``).
 

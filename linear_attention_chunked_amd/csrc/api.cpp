@@ -47,7 +47,10 @@ bool use_inplace(const ttt_fwd_args* a, int mode) {
 }
 
 size_t workspace_bytes_for(const ttt_fwd_args* a, int mode) {
-    return use_inplace(a, mode) ? ttt::inplace_workspace(a->B, a->H, a->L, a->dk, a->dv, a->chunk) : 0;
+    if (use_inplace(a, mode)) return ttt::inplace_workspace(a->B, a->H, a->L, a->dk, a->dv, a->chunk);
+    if (ttt::tcb_supported(a->dtype, a->dk, a->dv))
+        return ttt::tcb_workspace(a->B, a->H, a->L, a->dk, a->dv, mode, a->chunk);
+    return 0;
 }
 
 // sizes, dtype, mode and scalars only (no pointers): also serves the workspace query
@@ -135,7 +138,7 @@ ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* a) {
     int mode = 0;
     ttt_status_t s = validate_fwd(a, &mode);
     if (s != TTT_OK) return s;
-    ttt::TcParams p;
+    ttt::TcParams p{};
     std::memset(&p, 0, sizeof(p));
     p.q = a->q;
     p.k = a->k;
@@ -165,6 +168,7 @@ ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* a) {
     p.dk = a->dk;
     p.dv = a->dv;
     p.chunk = a->chunk;
+    p.workspace = a->workspace;
     const hipStream_t st = reinterpret_cast<hipStream_t>(a->stream);
     if (use_inplace(a, mode)) return from_hip(ttt::launch_inplace(p, a->workspace, st));
     return from_hip(ttt::launch_tc_fwd(p, a->dtype, mode, st));

@@ -29,6 +29,15 @@ struct TcParams {
     int B, H, L, dk, dv, chunk;
     int n_vt;     // dv tiles per head
     int xcd_map;  // 1: keep the dv tiles of one head on one XCD
+    // sequence segmentation with decoupled look-back (bf16 kernel only):
+    // nseg segments of seg_tiles chunk tiles per (head, dv tile); lb_flags
+    // holds one flag per workgroup plus the ticket counter, lb_data two state
+    // blocks (aggregate, inclusive) of lb_stride floats per workgroup
+    int nseg, seg_tiles;
+    int* lb_flags;
+    float* lb_data;
+    int64_t lb_stride;
+    void* workspace;
 };
 
 // dtype: 0 fp32, 1 bf16.  mode: MODE_*.  Returns hipSuccess or the launch error;
@@ -38,6 +47,9 @@ bool tc_fwd_supported(int dtype, int mode, int dk, int dv, int chunk);
 // gfx950-tuned bf16 variant (dk in {64,128}, dv in {64,128}); chosen by launch_tc_fwd
 bool tcb_supported(int dtype, int dk, int dv);
 hipError_t launch_tcb_fwd(const TcParams& p, int mode, hipStream_t stream);
+// workspace of the bf16 kernel (look-back flags and states when the sequence
+// is segmented; 0 otherwise)
+size_t tcb_workspace(int B, int H, int L, int dk, int dv, int mode, int chunk);
 
 // Chunk-causal forward for large fast weights (dk, dv multiples of 256, bf16):
 // update walk with bf16 W snapshots in `workspace`, then a batched readout.

@@ -95,8 +95,24 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     const int g = lane >> 4, c16 = lane & 15;
     const int nt = wave % NNT, hf = wave / NNT;
 
-    int bh, vt;
-    {
+    // ---- which (head, dv tile, segment) this workgroup runs
+    const int ntiles = (p.L + CS - 1) / CS;
+    const int nbv = p.B * p.H * p.n_vt;
+    const bool segmented = p.nseg > 1;
+    int bh, vt, seg = 0, c_begin = 0, c_end = ntiles;
+    __shared__ int sTicket;
+    if (segmented) {
+        // tickets hand out segments in order, so a workgroup only ever waits
+        // for workgroups that took a ticket before it and are running
+        if (tid == 0) sTicket = atomicAdd(p.lb_flags + (int64_t)nbv * p.nseg, 1);
+        __syncthreads();
+        const int t = sTicket, bv = t % nbv;
+        seg = t / nbv;
+        bh = bv / p.n_vt;
+        vt = bv % p.n_vt;
+        c_begin = seg * p.seg_tiles;
+        c_end = min(c_begin + p.seg_tiles, ntiles);
+    } else {
         const int i = blockIdx.x;
         if (p.xcd_map) {
             const int grp = i / (8 * p.n_vt), rem = i % (8 * p.n_vt);
@@ -149,7 +165,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     // ---- state accumulators S[DKH*hf + 16t + 4g + r][16*nt + c16]
     f32x4 Sacc[NTH];
     f32x4 Macc[MOM ? NTH : 1];
-    {
+    auto load_initial = [&](f32x4* S, f32x4* M) {
         const float* S0 = p.S0 ? p.S0 + b * p.s0s[0] + h * p.s0s[1] : nullptr;
         const float* M0 = (MOM && p.M0) ? p.M0 + b * p.m0s[0] + h * p.m0s[1] : nullptr;
         const int col = n0 + 16 * nt + c16;
@@ -158,17 +174,12 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = DKH * hf + 16 * t + 4 * g + r;
-                Sacc[t][r] = S0 ? S0[(int64_t)row * p.dv + col] : 0.f;
-                if (MOM) Macc[t][r] = M0 ? M0[(int64_t)row * p.dv + col] : 0.f;
+                S[t][r] = S0 ? S0[(int64_t)row * p.dv + col] : 0.f;
+                if (MOM) M[t][r] = M0 ? M0[(int64_t)row * p.dv + col] : 0.f;
             }
-    }
+    };
+    if (!segmented) load_initial(Sacc, Macc);
     bf16x8 Sop[NKH], Mop[MOM ? NKH : 1];
-#pragma unroll
-    for (int kk = 0; kk < NKH; ++kk) Sop[kk] = acc_to_frag_bf16(Sacc[2 * kk], Sacc[2 * kk + 1]);
-    if (MOM) {
-#pragma unroll
-        for (int kk = 0; kk < NKH; ++kk) Mop[kk] = acc_to_frag_bf16(Macc[2 * kk], Macc[2 * kk + 1]);
-    }
 
     // ---- staging: each 16-byte piece of a row goes to its swizzled slot of the
     // K-block-major layout (16 lanes cover one 256-byte Q/K row)
@@ -181,68 +192,62 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     float re[PF];
     // staging: 16 lanes load one 256-byte Q/K row (8 lanes one 128-byte V row);
     // chunk c of row r lands in block c/4 at swizzled position (c%4)^swz(r)
-    int goff_q[UQ], loff_q[UQ], goff_v, loff_v;
+    int loff_q[UQ], loff_v;
 #pragma unroll
     for (int x = 0; x < UQ; ++x) {
         const int u = tid + x * NT, row = u / (DK / 8), ch = u % (DK / 8);
-        goff_q[x] = row * (int)qL + 8 * ch;                          // token offset added per chunk
         loff_q[x] = (ch >> 2) * BLK + row * 32 + 8 * ((ch & 3) ^ swz(row));
     }
     {
         const int row = tid / (DVT / 8), ch = tid % (DVT / 8);
-        goff_v = row * (int)vL + 8 * ch;
         loff_v = (ch >> 2) * BLKV + row * 32 + 8 * ((ch & 3) ^ swz(row));
     }
     const int kq_same = (qL == kL);
-    auto load = [&](int c, auto SET) {
+    // Every lane issues the same loads for every chunk: rows past L read row
+    // L-1 again (their eta is zero, so they add nothing; their outputs are
+    // never stored) and a chunk index past the end refetches the last chunk.
+    // With no load under a branch, the memory counter advances uniformly and
+    // the compiler's waits before the LDS writes drain only the oldest set.
+    auto load = [&](int c, auto SET, auto WITHQ) {
         constexpr int st = decltype(SET)::value;
-        const int t0 = c * CS;
-        const bf16_t* Qc = Qg + (int64_t)t0 * qL;
-        const bf16_t* Kc = Kg + (int64_t)t0 * kL;
-        const bf16_t* Vc = Vg + (int64_t)t0 * vL;
+        constexpr bool wq = decltype(WITHQ)::value;
+        const int t0 = min(c, ntiles - 1) * CS;
         const bool full = (t0 + CS <= L);
-        if (full) {                  // whole chunk in range (uniform): plain loads
-#pragma unroll
-            for (int x = 0; x < UQ; ++x) {
-                const int row = (tid + x * NT) / (DK / 8);
-                const int64_t ko = kq_same ? goff_q[x] : (int64_t)row * kL + 8 * ((tid + x * NT) % (DK / 8));
-                rq[st][x] = *reinterpret_cast<const u32x4*>(Qc + goff_q[x]);
-                rk[st][x] = *reinterpret_cast<const u32x4*>(Kc + ko);
-            }
-        } else {                     // ragged last chunk: zero-fill rows past L
-#pragma unroll
-            for (int x = 0; x < UQ; ++x) {
-                const int row = (tid + x * NT) / (DK / 8);
-                const bool ok = t0 + row < L;
-                const int64_t ko = kq_same ? goff_q[x] : (int64_t)row * kL + 8 * ((tid + x * NT) % (DK / 8));
-                rq[st][x] = ok ? *reinterpret_cast<const u32x4*>(Qc + goff_q[x]) : u32x4{0, 0, 0, 0};
-                rk[st][x] = ok ? *reinterpret_cast<const u32x4*>(Kc + ko) : u32x4{0, 0, 0, 0};
-            }
-        }
-        {
-            const bool ok = tid < NVC && (full || t0 + tid / (DVT / 8) < L);
-            rv[st] = ok ? *reinterpret_cast<const u32x4*>(Vc + goff_v) : u32x4{0, 0, 0, 0};
-        }
-        if (tid < CS) {
-            const int t = t0 + tid;
-            re[st] = (t < L) ? (Eg ? Eg[t * eL] : p.eta_scalar) : 0.f;
-        }
-    };
-    auto store = [&](int c, int buf, auto SET) {
-        constexpr int st = decltype(SET)::value;
 #pragma unroll
         for (int x = 0; x < UQ; ++x) {
-            *reinterpret_cast<u32x4*>(&sQ[buf][loff_q[x]]) = rq[st][x];
+            const int row = (tid + x * NT) / (DK / 8);
+            const int rr = full ? row : min(row, L - 1 - t0);
+            const int64_t qo = (int64_t)(t0 + rr) * qL + 8 * ((tid + x * NT) % (DK / 8));
+            const int64_t ko = kq_same ? qo : (int64_t)(t0 + rr) * kL + 8 * ((tid + x * NT) % (DK / 8));
+            if (wq) rq[st][x] = *reinterpret_cast<const u32x4*>(Qg + qo);
+            rk[st][x] = *reinterpret_cast<const u32x4*>(Kg + ko);
+        }
+        {
+            const int u = tid % NVC, row = u / (DVT / 8), ch = u % (DVT / 8);
+            const int rr = full ? row : min(row, L - 1 - t0);
+            rv[st] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)(t0 + rr) * vL + 8 * ch);
+        }
+        // (tokens past L get eta 0 when the chunk is written to LDS: a select
+        // here would make the compiler wait for this load right away)
+        re[st] = Eg ? Eg[min(t0 + (tid % CS), L - 1) * eL] : p.eta_scalar;
+    };
+    auto store = [&](int c, int buf, auto SET, auto WITHQ) {
+        constexpr int st = decltype(SET)::value;
+        constexpr bool wq = decltype(WITHQ)::value;
+#pragma unroll
+        for (int x = 0; x < UQ; ++x) {
+            if (wq) *reinterpret_cast<u32x4*>(&sQ[buf][loff_q[x]]) = rq[st][x];
             *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = rk[st][x];
         }
         if (tid < NVC) *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = rv[st];
         if (tid < CS) {
-            sE[buf][0][tid] = re[st];
+            const int n = min(CS, L - c * CS);
+            const float e = (tid < n) ? re[st] : 0.f;
+            sE[buf][0][tid] = e;
             if (MOM) {
-                const int n = min(CS, L - c * CS);
                 const int pw = n - 1 - tid;
-                sE[buf][1][tid] = (pw >= 0) ? re[st] * sTab[pw] : 0.f;
-                sE[buf][2][tid] = (pw >= 0) ? re[st] * sTab[(CS + 1) + pw] : 0.f;
+                sE[buf][1][tid] = (pw >= 0) ? e * sTab[pw] : 0.f;
+                sE[buf][2][tid] = (pw >= 0) ? e * sTab[(CS + 1) + pw] : 0.f;
             }
         }
     };
@@ -289,24 +294,285 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
 
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, PF - 1>;
-    const int ntiles = (L + CS - 1) / CS;
-    load(0, I0{});
+    using WQ = std::true_type;
+    using NQ = std::false_type;
+
+    // value fragments of the staged chunk (tokens in accperm order), scaled
+    // in registers by eta (VB) and, with momentum, eta*w_{n-1-j} (VS) and
+    // eta*beta^{n-1-j} (VM)
+    auto vfrags = [&](int cur, bf16x8* VB, bf16x8* VS, bf16x8* VM) {
+        const bf16_t* V = sV[cur];
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+            const bf16x8 raw = join(tr_read(V + b_v + (32 * jb) * 32), tr_read(V + b_v + (32 * jb + 16) * 32));
+            const float* e0 = &sE[cur][0][32 * jb + 4 * g];
+            VB[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e0), *reinterpret_cast<const f32x4*>(e0 + 16));
+            if (MOM) {
+                const float* e1 = &sE[cur][1][32 * jb + 4 * g];
+                const float* e2 = &sE[cur][2][32 * jb + 4 * g];
+                VS[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e1), *reinterpret_cast<const f32x4*>(e1 + 16));
+                VM[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e2), *reinterpret_cast<const f32x4*>(e2 + 16));
+            }
+        }
+    };
+    // S (and m) over one staged chunk of n tokens, this wave's d_k half
+    auto state_update = [&](int cur, int n, const bf16x8* VB, const bf16x8* VS, const bf16x8* VM) {
+        if (MOM) {
+            const float alpha = sTab[2 * (CS + 1) + (n - 1)];
+            const float gamma = sTab[(CS + 1) + n];
+#pragma unroll
+            for (int t = 0; t < NTH; ++t) {
+                Sacc[t] += alpha * Macc[t];
+                Macc[t] *= gamma;
+            }
+        }
+        const bf16_t* Kh = sK[cur] + (hf * NTH / 2) * BLK;   // d_k half -> feature blocks
+#pragma unroll
+        for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+            for (int t = 0; t < NTH; ++t) {
+                const int base = (t >> 1) * BLK + ((t & 1) ? b_tr1 : b_tr0) + (32 * jb) * 32;
+                const bf16x8 a = join(tr_read(Kh + base), tr_read(Kh + base + 16 * 32));
+                mma(Sacc[t], a, MOM ? VS[jb] : VB[jb]);
+                if (MOM) mma(Macc[t], a, VM[jb]);
+            }
+        }
+    };
+    auto refresh_ops = [&]() {
+#pragma unroll
+        for (int kk = 0; kk < NKH; ++kk) Sop[kk] = acc_to_frag_bf16(Sacc[2 * kk], Sacc[2 * kk + 1]);
+        if (MOM) {
+#pragma unroll
+            for (int kk = 0; kk < NKH; ++kk) Mop[kk] = acc_to_frag_bf16(Macc[2 * kk], Macc[2 * kk + 1]);
+        }
+    };
+
+    if (segmented) {
+        // ================= decoupled look-back over sequence segments =================
+        // A segment of n tokens maps the state (S, m) it starts from to
+        //     (S + a_n m + X, beta^n m + Y),  a_n = beta + ... + beta^n,
+        // where (X, Y) is the segment's own result from a zero start (its
+        // aggregate).  Segment s publishes its aggregate, then walks back over
+        // segments s-1, s-2, ...: an inclusive state (published by a segment
+        // that has finished its look-back) ends the walk, an aggregate is
+        // composed into the running map T and the walk continues; past
+        // segment 0 the map is applied to (S0, M0).  Exchange blocks use the
+        // accumulator layout itself (lane-private f32x4 slots), so publishing
+        // and reading are coalesced 16-byte accesses with no reshuffle.
+        constexpr int NSTATE = MOM ? 2 : 1;
+        const int my_id = seg * nbv + bh * p.n_vt + vt;
+        auto slot = [&](int id, int which, int st, int t) -> f32x4* {
+            return reinterpret_cast<f32x4*>(p.lb_data + ((int64_t)id * 2 + which) * p.lb_stride) +
+                   ((wave * NSTATE + st) * NTH + t) * 64 + lane;
+        };
+        // Publishing: every wave waits for its own stores to reach L2, then one
+        // thread makes them visible device-wide (one agent-scope release: an
+        // L2 write-back) and raises the flag.  Agent-scope fences in every wave
+        // would write back and invalidate the XCD's L2 once per wave.
+        auto publish = [&](int which, const f32x4* S, const f32x4* M) {
+#pragma unroll
+            for (int t = 0; t < NTH; ++t) {
+                *slot(my_id, which, 0, t) = S[t];
+                if (MOM) *slot(my_id, which, 1, t) = M[t];
+            }
+            __builtin_amdgcn_s_waitcnt(0);   // this wave's stores are complete
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(p.lb_flags + my_id, which + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        __shared__ int sFlag;
+        // Waiting: one thread polls the flag with agent-scope acquire loads (the
+        // acquire invalidates this CU's L1 and the stale lines of the XCD's L2,
+        // which the other waves' loads go through after the barrier).  The wait
+        // is bounded: a flag that never arrives ends it (results are then
+        // wrong, but every wave still finishes).
+        auto wait_flag = [&](int id) -> int {
+            if (tid == 0) {
+                int v = 0;
+                for (int spin = 0; spin < (1 << 22); ++spin) {
+                    v = __hip_atomic_load(p.lb_flags + id, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                    if (v != 0) break;
+                    __builtin_amdgcn_s_sleep(2);
+                }
+                sFlag = v;
+            }
+            __syncthreads();
+            const int v = sFlag;
+            __syncthreads();   // sFlag is reused by the next wait
+            return v;
+        };
+        const int seg_len = p.seg_tiles * CS;           // every segment but the last is full
+        float a_seg = 0.f, g_seg = 1.f;
+        if (MOM) {
+            const double be = (double)p.beta, bn = pow(be, (double)seg_len);
+            a_seg = (float)(be * (1.0 - bn) / (1.0 - be));
+            g_seg = (float)bn;
+        }
+
+        // ---- pass 1: this segment's aggregate (K, V, eta only)
+#pragma unroll
+        for (int t = 0; t < NTH; ++t) {
+            Sacc[t] = zero4();
+            if (MOM) Macc[t] = zero4();
+        }
+        __syncthreads();   // tables ready
+        const bool last = (seg == p.nseg - 1);
+        if (!last) {
+            // K, V and eta only, three chunks in flight: register set k % 3
+            // carries chunk c_begin + k until it is written to LDS buffer k % 2
+            constexpr int D = 3;
+            u32x4 ak[D][UQ], av[D];
+            float ae[D];
+            // Every lane issues the same loads in every step (past the segment end
+            // the last chunk is fetched again, V and eta lanes wrap): the memory
+            // counter then advances uniformly and a wait before an LDS write
+            // only drains the oldest set instead of all three.
+            auto kv_load = [&](int c, auto SET) {
+                constexpr int st = decltype(SET)::value;
+                const int t0 = min(c, c_end - 1) * CS;   // segments before the last hold only whole chunks
+                const bf16_t* Kc = Kg + (int64_t)t0 * kL;
+#pragma unroll
+                for (int x = 0; x < UQ; ++x) {
+                    const int row = (tid + x * NT) / (DK / 8);
+                    const int64_t ko = (int64_t)row * kL + 8 * ((tid + x * NT) % (DK / 8));
+                    ak[st][x] = *reinterpret_cast<const u32x4*>(Kc + ko);
+                }
+                {
+                    const int u = tid % NVC, row = u / (DVT / 8), ch = u % (DVT / 8);
+                    av[st] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)(t0 + row) * vL + 8 * ch);
+                }
+                ae[st] = Eg ? Eg[(t0 + (tid % CS)) * eL] : p.eta_scalar;
+            };
+            auto kv_store = [&](int buf, auto SET) {
+                constexpr int st = decltype(SET)::value;
+#pragma unroll
+                for (int x = 0; x < UQ; ++x) *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = ak[st][x];
+                if (tid < NVC) *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = av[st];
+                if (tid < CS) {
+                    sE[buf][0][tid] = ae[st];
+                    if (MOM) {
+                        sE[buf][1][tid] = ae[st] * sTab[CS - 1 - tid];
+                        sE[buf][2][tid] = ae[st] * sTab[(CS + 1) + CS - 1 - tid];
+                    }
+                }
+            };
+            using J0 = std::integral_constant<int, 0>;
+            using J1 = std::integral_constant<int, 1>;
+            using J2 = std::integral_constant<int, 2>;
+            kv_load(c_begin, J0{});
+            kv_load(c_begin + 1, J1{});
+            kv_load(c_begin + 2, J2{});
+            kv_store(0, J0{});
+            __syncthreads();
+            auto step = [&](int c, auto CUR, auto NXT) {
+                const int buf = (c - c_begin) & 1;
+                kv_load(c + 3, CUR);
+                bf16x8 VB[NJB], VS[MOM ? NJB : 1], VM[MOM ? NJB : 1];
+                vfrags(buf, VB, VS, VM);
+                state_update(buf, CS, VB, VS, VM);
+                if (c + 1 < c_end) kv_store(buf ^ 1, NXT);
+                __syncthreads();
+            };
+            for (int c = c_begin; c < c_end; c += D) {
+                step(c, J0{}, J1{});
+                if (c + 1 < c_end) step(c + 1, J1{}, J2{});
+                if (c + 2 < c_end) step(c + 2, J2{}, J0{});
+            }
+            publish(0, Sacc, Macc);
+        }
+
+        // ---- look-back: T(S, m) = (S + aT m + XT, gT m + YT)
+        f32x4 XT[NTH], YT[MOM ? NTH : 1];
+        float aT = 0.f, gT = 1.f;
+#pragma unroll
+        for (int t = 0; t < NTH; ++t) {
+            XT[t] = zero4();
+            if (MOM) YT[t] = zero4();
+        }
+        bool have_base = false;
+        for (int j = seg - 1; j >= 0 && !have_base; --j) {
+            const int id = j * nbv + bh * p.n_vt + vt;
+            if (wait_flag(id) == 2) {
+                // inclusive state after segment j: the base of the walk
+#pragma unroll
+                for (int t = 0; t < NTH; ++t) {
+                    const f32x4 Sb = *slot(id, 1, 0, t);
+                    if (MOM) {
+                        const f32x4 Mb = *slot(id, 1, 1, t);
+                        XT[t] += Sb + aT * Mb;
+                        YT[t] += gT * Mb;
+                    } else {
+                        XT[t] += Sb;
+                    }
+                }
+                have_base = true;
+            } else {
+                // aggregate of segment j: T <- T o f_j
+#pragma unroll
+                for (int t = 0; t < NTH; ++t) {
+                    const f32x4 X = *slot(id, 0, 0, t);
+                    if (MOM) {
+                        const f32x4 Y = *slot(id, 0, 1, t);
+                        XT[t] += X + aT * Y;
+                        YT[t] += gT * Y;
+                    } else {
+                        XT[t] += X;
+                    }
+                }
+                aT = a_seg + aT * g_seg;
+                gT = gT * g_seg;
+            }
+        }
+        if (!have_base) {
+            // past segment 0: apply T to the initial state
+            f32x4 S0v[NTH], M0v[MOM ? NTH : 1];
+            load_initial(S0v, M0v);
+#pragma unroll
+            for (int t = 0; t < NTH; ++t) {
+                if (MOM) {
+                    XT[t] += S0v[t] + aT * M0v[t];
+                    YT[t] += gT * M0v[t];
+                } else {
+                    XT[t] += S0v[t];
+                }
+            }
+        }
+        // XT, YT = state at the segment start; publish the state at its end
+        if (!last) {
+#pragma unroll
+            for (int t = 0; t < NTH; ++t) {
+                if (MOM) {
+                    Sacc[t] += XT[t] + a_seg * YT[t];
+                    Macc[t] += g_seg * YT[t];
+                } else {
+                    Sacc[t] += XT[t];
+                }
+            }
+            publish(1, Sacc, Macc);
+        }
+#pragma unroll
+        for (int t = 0; t < NTH; ++t) {
+            Sacc[t] = XT[t];
+            if (MOM) Macc[t] = YT[t];
+        }
+    }
+    refresh_ops();
+
+    load(c_begin, I0{}, WQ{});
     __syncthreads();   // tables ready
-    store(0, 0, I0{});
-    if (ntiles > 1) load(1, I1{});
+    store(c_begin, 0, I0{}, WQ{});
+    load(c_begin + 1, I1{}, WQ{});
     __syncthreads();
 
-    // chunk k travels in register set k % PF; chunk c+1 is written to the
-    // other LDS buffer at the end of iteration c
+    // chunk c_begin + k travels in register set k % PF; chunk c+1 is written
+    // to the other LDS buffer at the end of iteration c
     auto iter = [&](int c, auto LSET, auto SSET) {
-        const int cur = c & 1;
+        const int cur = (c - c_begin) & 1;
         const int tbase = c * CS;
         const int n = min(CS, L - tbase);
         const bf16_t* Q = sQ[cur];
         const bf16_t* K = sK[cur];
-        const bf16_t* V = sV[cur];
 
-        if (hf == 0 && c > 0) combine();
+        if (hf == 0 && c > c_begin) combine();
 
         // ------------- intra scores P^T = K Q^T (lower-triangular 16x16 tiles)
         if (HAS_P && p_ti >= 0) {
@@ -337,23 +603,11 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         // P^T complete; the previous chunk's output tile is parked in sO and
         // half 0 has read half 1's partials before they are overwritten below
         __syncthreads();
-        if (c > 0) write_out();
-        if (PF == 2 && c + 2 < ntiles) load(c + 2, LSET);
+        if (c > c_begin) write_out();
+        if (PF == 2) load(c + 2, LSET, WQ{});
 
-        // ------------- value fragments (tokens in accperm order) scaled in registers
         bf16x8 VB[NJB], VS[MOM ? NJB : 1], VM[MOM ? NJB : 1];
-#pragma unroll
-        for (int jb = 0; jb < NJB; ++jb) {
-            const bf16x8 raw = join(tr_read(V + b_v + (32 * jb) * 32), tr_read(V + b_v + (32 * jb + 16) * 32));
-            const float* e0 = &sE[cur][0][32 * jb + 4 * g];
-            VB[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e0), *reinterpret_cast<const f32x4*>(e0 + 16));
-            if (MOM) {
-                const float* e1 = &sE[cur][1][32 * jb + 4 * g];
-                const float* e2 = &sE[cur][2][32 * jb + 4 * g];
-                VS[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e1), *reinterpret_cast<const f32x4*>(e1 + 16));
-                VM[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e2), *reinterpret_cast<const f32x4*>(e2 + 16));
-            }
-        }
+        vfrags(cur, VB, VS, VM);
 
         // ------------- readout partial: O^T = S_h^T Q_h^T (+ a_i m_h^T Q_h^T) (+ V~^T P^T share)
         {
@@ -398,53 +652,26 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         prev_n = n;
 
         // ------------- state update (own d_k half)
-        {
-            if (MOM) {
-                const float alpha = sTab[2 * (CS + 1) + (n - 1)];
-                const float gamma = sTab[(CS + 1) + n];
-#pragma unroll
-                for (int t = 0; t < NTH; ++t) {
-                    Sacc[t] += alpha * Macc[t];
-                    Macc[t] *= gamma;
-                }
-            }
-            const bf16_t* Kh = K + (hf * NTH / 2) * BLK;   // d_k half -> feature blocks
-#pragma unroll
-            for (int jb = 0; jb < NJB; ++jb) {
-#pragma unroll
-                for (int t = 0; t < NTH; ++t) {
-                    const int base = (t >> 1) * BLK + ((t & 1) ? b_tr1 : b_tr0) + (32 * jb) * 32;
-                    const bf16x8 a = join(tr_read(Kh + base), tr_read(Kh + base + 16 * 32));
-                    mma(Sacc[t], a, MOM ? VS[jb] : VB[jb]);
-                    if (MOM) mma(Macc[t], a, VM[jb]);
-                }
-            }
-            bool refresh = true;
-            if (MODE == MODE_CC) {
-                const int end = tbase + CS;
-                refresh = (end % p.chunk == 0) || (end >= L);
-            }
-            if (refresh) {
-#pragma unroll
-                for (int kk = 0; kk < NKH; ++kk) Sop[kk] = acc_to_frag_bf16(Sacc[2 * kk], Sacc[2 * kk + 1]);
-                if (MOM) {
-#pragma unroll
-                    for (int kk = 0; kk < NKH; ++kk) Mop[kk] = acc_to_frag_bf16(Macc[2 * kk], Macc[2 * kk + 1]);
-                }
-            }
+        state_update(cur, n, VB, VS, VM);
+        bool refresh = true;
+        if (MODE == MODE_CC) {
+            const int end = tbase + CS;
+            refresh = (end % p.chunk == 0) || (end >= L);
         }
-        if (c + 1 < ntiles) store(c + 1, cur ^ 1, SSET);
-        if (PF == 1 && c + 2 < ntiles) load(c + 2, LSET);
+        if (refresh) refresh_ops();
+        if (c + 1 < c_end) store(c + 1, cur ^ 1, SSET, WQ{});
+        if (PF == 1) load(c + 2, LSET, WQ{});
         __syncthreads();
     };
-    for (int c = 0; c < ntiles; c += 2) {
+    for (int c = c_begin; c < c_end; c += 2) {
         iter(c, I0{}, I1{});
-        if (c + 1 < ntiles) iter(c + 1, I1{}, I0{});
+        if (c + 1 < c_end) iter(c + 1, I1{}, I0{});
     }
     if (hf == 0) combine();
     __syncthreads();
     write_out();
 
+    if (segmented && seg != p.nseg - 1) return;   // final states come from the last segment
     const int col = n0 + 16 * nt + c16;
     if (p.S_final) {
         float* Sf = p.S_final + (int64_t)bh * p.dk * p.dv;
@@ -466,16 +693,94 @@ bool tcb_supported(int dtype, int dk, int dv) {
     return dtype == 1 && (dk == 64 || dk == 128) && (dv == 32 || dv == 64 || dv == 128);
 }
 
-// cs / dvt: chunk tile and column tile (64 x 64 or 32 x 32)
-hipError_t launch_tcb_fwd_cfg(const TcParams& pin, int mode, int cs, int dvt, hipStream_t s) {
+namespace {
+
+// Launch plan: tile form, and how many segments each (head, dv tile) is cut
+// into.  The grid should cover the chip (256 CUs; the 32 x 32 form runs two
+// workgroups per CU); a segment costs one extra pass over its K and V, so
+// segments are only used when the (head, dv tile) grid is short of that and
+// each segment keeps at least 1024 tokens.
+struct TcbPlan {
+    int cs, dvt, n_vt, nseg, seg_tiles;
+};
+constexpr int kCUs = 256;
+constexpr int kMinSegTokens = 1024;
+
+TcbPlan tcb_plan(int B, int H, int L, int dv, int mode, int chunk) {
+    TcbPlan pl{};
+    // chunk-causal needs the tile to divide the semantic chunk; 64 x 64 tiles
+    // whenever they fit (measured faster than 32 x 32 with two workgroups
+    // per CU: the 32-token tile doubles the per-chunk synchronisation)
+    const bool cc32 = (mode == MODE_CC) && (chunk % 64 != 0);
+    pl.cs = pl.dvt = (dv % 64 != 0 || cc32) ? 32 : 64;
+    pl.n_vt = dv / pl.dvt;
+    const int ntiles = (L + pl.cs - 1) / pl.cs;
+    const int64_t nbv = (int64_t)B * H * pl.n_vt;
+    const int slots = kCUs * (pl.cs == 32 ? 2 : 1);
+    pl.nseg = 1;
+    pl.seg_tiles = ntiles;
+    if (nbv < slots) {
+        // segment length: a whole number of tiles (and of chunks when the
+        // chunk is part of the semantics)
+        int unit = 1;
+        if (mode == MODE_CC) unit = chunk / pl.cs;
+        const int min_tiles = ((kMinSegTokens / pl.cs + unit - 1) / unit) * unit;
+        const int want = (int)((slots + nbv - 1) / nbv);
+        int seg_tiles = (ntiles + want - 1) / want;
+        seg_tiles = ((seg_tiles + unit - 1) / unit) * unit;
+        if (seg_tiles < min_tiles) seg_tiles = min_tiles;
+        const int nseg = (ntiles + seg_tiles - 1) / seg_tiles;
+        if (nseg > 1) {
+            pl.nseg = nseg;
+            pl.seg_tiles = seg_tiles;
+        }
+    }
+    return pl;
+}
+
+// floats per workgroup state block (S, and m with momentum)
+int64_t lb_block(int dk, int dvt, int mode) { return (int64_t)dk * dvt * (mode == MODE_MOM ? 2 : 1); }
+
+size_t lb_flag_bytes(int64_t nwg) { return (size_t)(((nwg + 1) * 4 + 255) / 256 * 256); }
+
+__global__ void lb_clear_kernel(int* flags, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) flags[i] = 0;
+}
+
+}  // namespace
+
+size_t tcb_workspace(int B, int H, int L, int dk, int dv, int mode, int chunk) {
+    const TcbPlan pl = tcb_plan(B, H, L, dv, mode, chunk);
+    if (pl.nseg <= 1) return 0;
+    const int64_t nwg = (int64_t)B * H * pl.n_vt * pl.nseg;
+    return lb_flag_bytes(nwg) + (size_t)nwg * 2 * lb_block(dk, pl.dvt, mode) * sizeof(float);
+}
+
+hipError_t launch_tcb_fwd(const TcParams& pin, int mode, hipStream_t s) {
     TcParams p = pin;
-    if (p.dv % dvt != 0) return hipErrorInvalidValue;
-    p.n_vt = p.dv / dvt;
-    p.xcd_map = ((p.B * p.H) % 8 == 0) ? 1 : 0;
-    const dim3 grid(p.B * p.H * p.n_vt), block(dvt / 16 * 128);
+    const TcbPlan pl = tcb_plan(p.B, p.H, p.L, p.dv, mode, p.chunk);
+    p.n_vt = pl.n_vt;
+    p.nseg = pl.nseg;
+    p.seg_tiles = pl.seg_tiles;
+    p.xcd_map = (pl.nseg == 1 && (p.B * p.H) % 8 == 0) ? 1 : 0;
+    const int64_t nwg = (int64_t)p.B * p.H * pl.n_vt * pl.nseg;
+    if (pl.nseg > 1) {
+        if (!p.workspace) return hipErrorInvalidValue;
+        p.lb_flags = reinterpret_cast<int*>(p.workspace);
+        p.lb_data = reinterpret_cast<float*>(reinterpret_cast<char*>(p.workspace) + lb_flag_bytes(nwg));
+        p.lb_stride = lb_block(p.dk, pl.dvt, mode);
+        // flags and the ticket counter start at zero (a fill kernel, not a
+        // memset node, so the call stays valid inside a captured graph)
+        const int nflags = (int)nwg + 1;
+        hipLaunchKernelGGL(lb_clear_kernel, dim3((nflags + 255) / 256), dim3(256), 0, s, p.lb_flags, nflags);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)nwg), block(pl.dvt / 16 * 128);
 #define TTT_L(DK_, M_, CS_, DVT_) hipLaunchKernelGGL((tcb_fwd_kernel<DK_, M_, CS_, DVT_>), grid, block, 0, s, p)
 #define TTT_M(CS_, DVT_)                                              \
-    if (cs == CS_ && dvt == DVT_) {                                    \
+    if (pl.cs == CS_ && pl.dvt == DVT_) {                              \
         if (p.dk == 128) {                                             \
             if (mode == MODE_TC) TTT_L(128, MODE_TC, CS_, DVT_);       \
             else if (mode == MODE_MOM) TTT_L(128, MODE_MOM, CS_, DVT_); \
@@ -492,16 +797,6 @@ hipError_t launch_tcb_fwd_cfg(const TcParams& pin, int mode, int cs, int dvt, hi
 #undef TTT_M
 #undef TTT_L
     return hipErrorInvalidValue;
-}
-
-hipError_t launch_tcb_fwd(const TcParams& p, int mode, hipStream_t s) {
-    // chunk-causal needs the tile to divide the semantic chunk
-    // 64 x 64 tiles whenever they fit: measured faster than 32 x 32 tiles with
-    // two workgroups per CU on the LM-scale and momentum shapes (the 32-token
-    // chunk doubles the per-chunk synchronisation)
-    const bool cc32 = (mode == MODE_CC) && (p.chunk % 64 != 0);
-    if (p.dv % 64 != 0 || cc32) return launch_tcb_fwd_cfg(p, mode, 32, 32, s);
-    return launch_tcb_fwd_cfg(p, mode, 64, 64, s);
 }
 
 }  // namespace ttt

@@ -146,3 +146,14 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64)
     with pytest.raises(ValueError):
         lac.fwd_chunked(q, q, q)
+
+
+def test_workspace_plan_segments_short_grids():
+    """Few (head, column tile) pairs on a long sequence get look-back
+    workspace (segmented); a grid that fills the chip needs none."""
+    import torch
+    assert lac.fwd_workspace_size(4, 8, 16384, 128, 128, beta=0.9) > 0
+    assert lac.fwd_workspace_size(8, 16, 4096, 128, 128) == 0
+    assert lac.fwd_workspace_size(1, 2, 500, 128, 128) == 0          # too short to cut
+    assert lac.fwd_workspace_size(1, 1, 3000, 64, 32, beta=0.5) > 0  # 32 x 32 tile form
+    assert lac.fwd_workspace_size(1, 2, 4096, 128, 128, dtype=torch.float32) == 0

@@ -181,6 +181,67 @@ def test_momentum_full_sampled_heads():
     check(inp, got, ref, TOL["bf16"], "momentum full")
 
 
+# ------------------------------------------------- segmented sequences (look-back)
+def _seeded(shape, seed, scale):
+    return scale * torch.randn(*shape, generator=torch.Generator().manual_seed(seed))
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_segmented_sequence_lookback(beta):
+    """Two heads of 5000 tokens: too few (head, column tile) pairs to fill the
+    chip, so the sequence is cut into segments that run concurrently and
+    chain their states through the decoupled look-back (ragged last segment,
+    non-zero S0 and, with momentum, M0)."""
+    inp = W.gen_lm_scale(B=1, H=2, L=5000, d=128)
+    inp.beta = W.f32(beta)
+    if beta:
+        inp.M0 = _seeded((1, 2, 128, 128), 7001, 0.01)
+    assert lac.fwd_workspace_size(1, 2, 5000, 128, 128, beta=inp.beta) > 0, "shape is not segmented"
+    say(f"segmented look-back bf16 B1 H2 L5000 d128 beta{beta}")
+    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "segmented")
+
+
+def test_segmented_narrow_columns():
+    """d_v = 32 (32 x 32 tile form, two workgroups per CU) with segmentation."""
+    g = torch.Generator().manual_seed(7100)
+    B, H, L, dk, dv = 1, 1, 3000, 64, 32
+    q = torch.randn(B, H, L, dk, generator=g).to(torch.bfloat16)
+    k = (torch.randn(B, H, L, dk, generator=g) / 8).to(torch.bfloat16)
+    v = torch.randn(B, H, L, dv, generator=g).to(torch.bfloat16)
+    S0 = 0.02 * torch.randn(B, H, dk, dv, generator=g)
+    inp = W.TokenCausalInputs(q, k, v, None, W.f32(0.05), W.f32(0.8), S0, None, 64, "bf16")
+    assert lac.fwd_workspace_size(B, H, L, dk, dv, beta=inp.beta) > 0, "shape is not segmented"
+    say("segmented d_v=32 momentum B1 H1 L3000 dk64")
+    check(inp, run_fwd(inp), oracle_tc(inp), TOL["bf16"], "segmented dv32")
+
+
+def test_segmented_chunk_causal():
+    """Chunk-causal mode: segment boundaries fall on chunk boundaries."""
+    g = torch.Generator().manual_seed(7200)
+    B, H, L, d, dv, C = 1, 2, 4500, 64, 64, 192
+    z = (torch.randn(B, H, L, d, generator=g) / 8).to(torch.bfloat16)
+    vh = torch.randn(B, H, L, dv, generator=g).to(torch.bfloat16)
+    eta = 0.05 * torch.rand(B, H, L, generator=g)
+    W0 = 0.02 * torch.randn(B, H, d, dv, generator=g)
+    inp = W.TokenCausalInputs(z, z, vh, eta, 0.0, 0.0, W0, None, C, "bf16")
+    assert lac.fwd_workspace_size(B, H, L, d, dv, chunk=C, mode="chunk_causal") > 0
+    say("segmented chunk-causal bf16 B1 H2 L4500 C192")
+    got = run_fwd(inp, mode="chunk_causal")
+    check(inp, got, oracle_tc(inp, mode="chunk_causal"), TOL["bf16"], "segmented chunk-causal")
+
+
+def test_segmented_repeat_calls_agree():
+    """Back-to-back calls reuse the workspace (flags are cleared per call);
+    results agree to fp32 state rounding (the look-back may combine a
+    predecessor's aggregate or its inclusive state, whichever is ready)."""
+    inp = W.gen_momentum(B=1, H=1, L=6000, d=128)
+    say("segmented repeat B1 H1 L6000 momentum")
+    a = run_fwd(inp)
+    b = run_fwd(inp)
+    assert oracle.rel_l2(a[0].float(), b[0].double().numpy()) <= 1e-3
+    assert oracle.rel_l2(a[1], b[1].double().numpy()) <= 1e-5
+
+
 # ------------------------------------------------------------- chunk-causal
 @pytest.mark.parametrize("dtype,C", [("bf16", 64), ("bf16", 192), ("f32", 32), ("f32", 96)])
 def test_chunk_causal_small(dtype, C):
