@@ -32,7 +32,7 @@ FLAGS = [
 
 # Kernels whose MFMA accumulators fit the 256 architectural VGPRs keep them
 # there (no v_accvgpr moves between AGPR and VGPR in the hot loop).
-VGPR_FORM = {"tcb_fwd.hip", "tc_fwd.hip", "dual.hip"}
+VGPR_FORM = {"tcb_fwd.hip", "tc_fwd.hip"}
 
 
 def _compile(src: str) -> str:

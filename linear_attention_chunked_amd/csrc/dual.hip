@@ -25,6 +25,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace ttt {
 
 template <typename T> struct DSeg;
@@ -261,12 +263,207 @@ __global__ __launch_bounds__(DV / 16 * 64) void dual_fwd_kernel(DualParams p) {
     }
 }
 
+// ------------------------------------------------------------------------
+// dual_chain_kernel: bf16, d = dv = 64, mini-batches of a multiple of 16.
+//
+// The columns of W evolve independently under the linear MSE update (column
+// j of E, V~ and S~ only involves column j of W and V), so each wave owns 16
+// state columns of one (b, h) and runs its own chain with no barriers: 4 x
+// (B*H) independent waves.  A step covers 16 tokens (never across a
+// mini-batch boundary):
+//     E = K W_n,  V~ = eta (V - E),  P^T = tril(K Q^T),
+//     O^T = S~^T Q^T + V~^T P^T,  S~ += K^T V~,
+// with W_{n+1} = S~ at the mini-batch end.  The critical path per step is
+// E -> V~ -> S~ -> bf16(S~) -> next E; everything else hangs off it.
+//
+// Feature order: accumulator row position p = 32kb + 16h + 4g + i of the
+// state holds feature d(p) = 32kb + 8g + 4h + i.  With that order the
+// operand fragment of lane (g, row) for feature block kb is the 16 contiguous
+// bytes X[row][32kb + 8g .. +8], so K and Q rows load straight into MFMA
+// operands (one 16-byte load each), and the state accumulators feed the next
+// contraction from registers.  The 16 x 64 K tile and the 16 x 16 V tile go
+// through wave-private LDS only for the two transposes the chain needs (V in
+// the E layout, K^T for the state update), read back with ds_read_b64_tr_b16.
+// Every lane issues the same loads each step (rows past L re-read row L-1;
+// their V~ is zeroed), DEPTH steps ahead.
+typedef short s16x4d __attribute__((ext_vector_type(4)));
+
+TTT_DEV u32x2 tr_read_d(const bf16_t* p) {
+    typedef __attribute__((address_space(3))) s16x4d lds_s16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+TTT_DEV void mma16(f32x4& acc, const u32x2& a, const u32x2& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4d, a), __builtin_bit_cast(s16x4d, b),
+                                                   acc, 0, 0, 0);
+}
+// 8-byte chunk swizzle of the [16 tokens][64] K tile (rows of 16 chunks; bit 0
+// untouched so 16-byte pairs stay whole): conflict-free row writes, at most
+// two-way conflicts on the transposing reads
+TTT_DEV int kswz(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) | (((r >> 2) & 1) << 3); }
+// feature of state row position p
+TTT_DEV int feat(int p) { return (p & ~31) + 8 * ((p >> 2) & 3) + 4 * ((p >> 4) & 1) + (p & 3); }
+
+template <int DEPTH>
+__global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
+    constexpr int D = 64, DV = 64;
+    __shared__ __attribute__((aligned(16))) bf16_t sK[16 * D];   // [token][d], 8-byte chunks swizzled
+    __shared__ __attribute__((aligned(16))) bf16_t sV[16 * 16];  // [token][16 columns]
+
+    const int lane = threadIdx.x, g = lane >> 4, c16 = lane & 15;
+    // the 4 column waves of a head run on one XCD (shared Q/K rows in its L2)
+    const int lid = xcd_logical(blockIdx.x, gridDim.x);
+    const int bh = lid >> 2, w = lid & 3;
+    const int L = p.L, mb = p.minibatch;
+    const float eta = p.eta;
+    const bf16_t* Qg = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)bh * L * D;
+    const bf16_t* Kg = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)bh * L * D;
+    const bf16_t* Vg = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)bh * L * DV + 16 * w;
+    bf16_t* Og = reinterpret_cast<bf16_t*>(p.out) + (int64_t)bh * L * DV + 16 * w;
+
+    // S~[feat(16t + 4g + r)][16w + c16], fp32
+    f32x4 Sacc[4];
+    {
+        const float* W0 = p.W0 + (int64_t)bh * p.W0_stride;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Sacc[t][r] = W0[feat(16 * t + 4 * g + r) * DV + 16 * w + c16];
+    }
+    bf16x8 Sop[2], Wop[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) Sop[kb] = Wop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
+
+    // per-lane pieces of a step: row c16, features 32kb + 8g .. +8 of Q and K;
+    // columns 4g .. +4 of this wave's V tile
+    u32x4 rq[DEPTH][2], rk[DEPTH][2];
+    u32x2 rv[DEPTH];
+    auto load = [&](int s, auto SET) {
+        constexpr int st = decltype(SET)::value;
+        const int t = min(16 * s + c16, L - 1);
+        const bf16_t* q = Qg + (int64_t)t * D + 8 * g;
+        const bf16_t* k = Kg + (int64_t)t * D + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            rq[st][kb] = *reinterpret_cast<const u32x4*>(q + 32 * kb);
+            rk[st][kb] = *reinterpret_cast<const u32x4*>(k + 32 * kb);
+        }
+        rv[st] = *reinterpret_cast<const u32x2*>(Vg + (int64_t)t * DV + 4 * g);
+    };
+
+    // LDS addresses (elements)
+    const int kw = c16 * D, ksw = kswz(c16);                 // K row writes
+    const int vw = c16 * 16 + 4 * g;                         // V tile write
+    const int rr = 4 * g + (c16 >> 2), cq = c16 & 3;         // transposing reads: row, chunk quad
+    const int vr = rr * 16 + 4 * cq;
+    const int kr = rr * D, krs = kswz(rr);
+
+    const int nsteps = (L + 15) / 16;
+    const int nrun = (nsteps + DEPTH - 1) / DEPTH * DEPTH;   // whole rounds; extra steps are empty
+
+    auto step = [&](int s, auto SET) {
+        constexpr int st = decltype(SET)::value;
+        const int t0 = 16 * s;
+        const bf16x8 Kf0 = __builtin_bit_cast(bf16x8, rk[st][0]), Kf1 = __builtin_bit_cast(bf16x8, rk[st][1]);
+        const bf16x8 Qf0 = __builtin_bit_cast(bf16x8, rq[st][0]), Qf1 = __builtin_bit_cast(bf16x8, rq[st][1]);
+        // stage the two transposes
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            *reinterpret_cast<u32x4*>(&sK[kw + 4 * ((8 * kb + 2 * g) ^ ksw)]) = rk[st][kb];
+        *reinterpret_cast<u32x2*>(&sV[vw]) = rv[st];
+
+        // E[token 4g+r][col c16] = K W_n
+        f32x4 e = zero4();
+        mma(e, Kf0, Wop[0]);
+        mma(e, Kf1, Wop[1]);
+        // P^T[j 4g+r][i c16] = K Q^T, causal j <= i
+        f32x4 pt = zero4();
+        mma(pt, Kf0, Qf0);
+        mma(pt, Kf1, Qf1);
+        // O^T partial: S~^T Q^T with S~ as of the step start
+        f32x4 o = zero4();
+        mma(o, Sop[0], Qf0);
+        mma(o, Sop[1], Qf1);
+        // the refill of this register set goes after every read of its old
+        // contents: the new loads then land in the same registers and the
+        // loop carries no copies of in-flight data (a copy would wait for it)
+        __builtin_amdgcn_sched_barrier(0);
+        load(s + DEPTH, SET);
+
+        // V in the E layout; V~ = eta (V - E), zero past L
+        const u32x2 vraw = tr_read_d(&sV[vr]);
+        f32x4 vt;
+        vt[0] = __uint_as_float(vraw[0] << 16);
+        vt[1] = __uint_as_float(vraw[0] & 0xffff0000u);
+        vt[2] = __uint_as_float(vraw[1] << 16);
+        vt[3] = __uint_as_float(vraw[1] & 0xffff0000u);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vt[r] = (t0 + 4 * g + r < L) ? eta * (vt[r] - e[r]) : 0.f;
+        const u32x2 VB = u32x2{pack2bf(vt[0], vt[1]), pack2bf(vt[2], vt[3])};
+
+        // S~ += K^T V~ : K^T tile t (positions 16t..) through the transposing read
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int chunk = 8 * (t >> 1) + 2 * cq + (t & 1);
+            mma16(Sacc[t], tr_read_d(&sK[kr + 4 * (chunk ^ krs)]), VB);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Sop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
+        const int t1 = t0 + 16;
+        if (t1 % mb == 0 || t1 >= L) {   // mini-batch end: W_{n+1} = S~
+            Wop[0] = Sop[0];
+            Wop[1] = Sop[1];
+        }
+
+        // O^T += V~^T P^T, store O rows (4 consecutive columns per lane)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pt[r] = (4 * g + r <= c16) ? pt[r] : 0.f;
+        mma16(o, VB, u32x2{pack2bf(pt[0], pt[1]), pack2bf(pt[2], pt[3])});
+        if (t0 + c16 < L)
+            *reinterpret_cast<u32x2*>(&Og[(int64_t)(t0 + c16) * DV + 4 * g]) = u32x2{pack2bf(o[0], o[1]), pack2bf(o[2], o[3])};
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using S2 = std::integral_constant<int, 2>;
+    using S3 = std::integral_constant<int, 3>;
+    using S4 = std::integral_constant<int, 4>;
+    using S5 = std::integral_constant<int, 5>;
+    static_assert(DEPTH == 6, "the step sequence below is written for six register sets");
+    load(0, S0{});
+    load(1, S1{});
+    load(2, S2{});
+    load(3, S3{});
+    load(4, S4{});
+    load(5, S5{});
+    for (int s = 0; s < nrun; s += DEPTH) {
+        step(s, S0{});
+        step(s + 1, S1{});
+        step(s + 2, S2{});
+        step(s + 3, S3{});
+        step(s + 4, S4{});
+        step(s + 5, S5{});
+    }
+
+    if (p.W_final) {
+        float* Wf = p.W_final + (int64_t)bh * D * DV;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Wf[feat(16 * t + 4 * g + r) * DV + 16 * w + c16] = Sacc[t][r];
+    }
+}
+
 bool dual_supported(int dtype, int d, int dv, int minibatch) {
     return (dtype == 0 || dtype == 1) && d == 64 && dv == 64 && minibatch >= 1;
 }
 
 hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t s) {
     if (!dual_supported(dtype, p.d, p.dv, p.minibatch)) return hipErrorInvalidValue;
+    if (dtype == 1 && p.minibatch % 16 == 0) {
+        // one wave per (b, h, 16-column tile)
+        hipLaunchKernelGGL((dual_chain_kernel<6>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+        return hipGetLastError();
+    }
     const int grid = p.B * p.H;
     if (dtype == 1)
         hipLaunchKernelGGL((dual_fwd_kernel<bf16_t, 64, 64>), dim3(grid), dim3(256), 0, s, p);
