@@ -30,15 +30,10 @@ FLAGS = [
 ]
 
 
-# Kernels whose MFMA accumulators fit the 256 architectural VGPRs keep them
-# there (no v_accvgpr moves between AGPR and VGPR in the hot loop).
-VGPR_FORM = {"tcb_fwd.hip", "tc_fwd.hip"}
-
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    extra = ["-mllvm", "-amdgpu-mfma-vgpr-form"] if os.path.basename(src) in VGPR_FORM else []
-    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
