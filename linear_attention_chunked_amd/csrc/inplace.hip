@@ -23,6 +23,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <type_traits>
+
 namespace ttt {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -127,73 +129,83 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
     }
 
     // staging: per K-step 32 tokens x 256 of Z (4 x 16 B per thread) and
-    // 32 tokens x 128 of V (2 x 16 B per thread)
-    u32x4 ra[4], rb[2];
-    float re = 0.f;
-    auto load = [&](int t0) {
+    // 32 tokens x 128 of V (2 x 16 B per thread).  NS register sets are in
+    // flight: the loads of step s+NS are issued at the top of step s and
+    // written to LDS at the end of step s+NS-1.  Every lane issues the same
+    // loads each step (token rows past L re-read row L-1 and are zeroed when
+    // written to LDS), so the compiler's waits only drain the oldest set.
+    constexpr int NS = 4;
+    u32x4 ra[NS][4], rb[NS][2];
+    float re[NS];
+    uint32_t zoff[4], voff[2];
+    int zrow[4], vrow[2];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int u = tid + x * IP_NT;              // 0..1023
+        zrow[x] = u >> 5;
+        zoff[x] = (uint32_t)((u & 31) * 8);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int u = tid + x * IP_NT;              // 0..511
+        vrow[x] = u >> 4;
+        voff[x] = (uint32_t)((u & 15) * 8);
+    }
+    const int kpc = p.chunk / IP_BK;                // K-steps per chunk
+    const int total_steps = p.nchunks * kpc;
+    auto step_t0 = [&](int st) { return (st / kpc) * p.chunk + (st % kpc) * IP_BK; };
+    auto load = [&](int st, auto SET) __attribute__((always_inline)) {
+        constexpr int k = decltype(SET)::value;
+        const int t0 = step_t0(min(st, total_steps - 1));
+#pragma unroll
         for (int x = 0; x < 4; ++x) {
-            const int u = tid + x * IP_NT;          // 0..1023
-            const int kr = u >> 5, c = (u & 31) * 8;
-            const int t = t0 + kr;
-            ra[x] = (t < L) ? *reinterpret_cast<const u32x4*>(Zg + t * p.ks[2] + c) : u32x4{0, 0, 0, 0};
+            const int t = min(t0 + zrow[x], L - 1);
+            ra[k][x] = *reinterpret_cast<const u32x4*>(Zg + (int64_t)t * p.ks[2] + zoff[x]);
         }
+#pragma unroll
         for (int x = 0; x < 2; ++x) {
-            const int u = tid + x * IP_NT;          // 0..511
-            const int kr = u >> 4, c = (u & 15) * 8;
-            const int t = t0 + kr;
-            rb[x] = (t < L) ? *reinterpret_cast<const u32x4*>(Vg + t * p.vs[2] + c) : u32x4{0, 0, 0, 0};
+            const int t = min(t0 + vrow[x], L - 1);
+            rb[k][x] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)t * p.vs[2] + voff[x]);
         }
-        if (PT && tid < IP_BK) {
-            const int t = t0 + tid;
-            re = (t < L) ? (Eg ? Eg[t * p.es[2]] : p.eta_scalar) : 0.f;
-        }
+        if (PT) re[k] = Eg ? Eg[(int64_t)min(t0 + (tid & (IP_BK - 1)), L - 1) * p.es[2]] : p.eta_scalar;
     };
-    auto stage = [&](int buf) {
+    auto stage = [&](int st, int buf, auto SET) __attribute__((always_inline)) {
+        constexpr int k = decltype(SET)::value;
+        const int t0 = step_t0(st);
+        const u32x4 z4 = u32x4{0, 0, 0, 0};
+#pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int u = tid + x * IP_NT;
-            const int kr = u >> 5, c = (u & 31) * 8;
-            *reinterpret_cast<u32x4*>(&sA[buf][kr * LDA + c]) = ra[x];
+            *reinterpret_cast<u32x4*>(&sA[buf][zrow[x] * LDA + (u & 31) * 8]) = (t0 + zrow[x] < L) ? ra[k][x] : z4;
         }
+#pragma unroll
         for (int x = 0; x < 2; ++x) {
             const int u = tid + x * IP_NT;
-            const int kr = u >> 4, c = (u & 15) * 8;
-            *reinterpret_cast<u32x4*>(&sB[buf][kr * LDB + c]) = rb[x];
+            *reinterpret_cast<u32x4*>(&sB[buf][vrow[x] * LDB + (u & 15) * 8]) = (t0 + vrow[x] < L) ? rb[k][x] : z4;
         }
-        if (PT && tid < IP_BK) sE[buf][tid] = re;
+        if (PT && tid < IP_BK) sE[buf][tid] = (t0 + tid < L) ? re[k] : 0.f;
     };
     const float out_scale = PT ? 1.f : p.eta_scalar;   // acc -> W
-
-    const int ksteps_per_chunk = p.chunk / IP_BK;
-    const int total_steps = p.nchunks * ksteps_per_chunk;
     bf16_t* snap = p.snap + (int64_t)bh * p.nchunks * p.dk * p.dv;
 
-    load(0);
-    stage(0);
-    __syncthreads();
-    for (int s = 0; s < total_steps; ++s) {
-        const int buf = s & 1;
-        const int chunk = s / ksteps_per_chunk;
-        if (s % ksteps_per_chunk == 0) {
-            // snapshot W_{chunk-1}^T (bf16) of this tile: [n][m] layout
-            bf16_t* sp = snap + (int64_t)chunk * p.dk * p.dv;
+    // snapshot W_{chunk-1}^T (bf16) of this tile: [n][m] layout
+    auto snapshot = [&](int chunk) __attribute__((always_inline)) {
+        bf16_t* sp = snap + (int64_t)chunk * p.dk * p.dv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+            for (int j = 0; j < 2; ++j) {
+                const int col = n0 + 64 * wn + 32 * j + (lane & 31);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int row = m0 + 128 * wm + 32 * i + 8 * q + 4 * (lane >> 5);
-                        const f32x4 v4 = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                               acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                        st4(sp + (int64_t)col * p.dk + row, v4 * out_scale);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const int row = m0 + 128 * wm + 32 * i + 8 * q + 4 * (lane >> 5);
+                    const f32x4 v4 = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                    st4(sp + (int64_t)col * p.dk + row, v4 * out_scale);
                 }
-        }
-        if (s + 1 < total_steps) {
-            const int ns = s + 1;
-            load((ns / ksteps_per_chunk) * p.chunk + (ns % ksteps_per_chunk) * IP_BK);
-        }
+            }
+    };
+    auto compute = [&](int buf) __attribute__((always_inline)) {
         const bf16_t* A = sA[buf];
         const bf16_t* Bt = sB[buf];
 #pragma unroll
@@ -225,8 +237,35 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j) mma32(acc[i][j], af[i], bfr[j]);
         }
-        if (s + 1 < total_steps) stage(buf ^ 1);
+    };
+
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    using K3 = std::integral_constant<int, 3>;
+    static_assert(NS == 4, "the step sequence below is written for four register sets");
+    load(0, K0{});
+    load(1, K1{});
+    load(2, K2{});
+    load(3, K3{});
+    stage(0, 0, K0{});
+    __syncthreads();
+    // step st: refill the set step st just freed, compute from LDS, write step
+    // st+1 to the other LDS buffer
+    auto step = [&](int st, auto CUR, auto NXT) __attribute__((always_inline)) {
+        if (st >= total_steps) return;               // (uniform)
+        if (st % kpc == 0) snapshot(st / kpc);
+        load(st + NS, CUR);
+        compute(st & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 < total_steps) stage(st + 1, (st + 1) & 1, NXT);
         __syncthreads();
+    };
+    for (int st = 0; st < total_steps; st += NS) {
+        step(st, K0{}, K1{});
+        step(st + 1, K1{}, K2{});
+        step(st + 2, K2{}, K3{});
+        step(st + 3, K3{}, K0{});
     }
 
     if (p.S_final) {
