@@ -33,7 +33,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int IP_BM = 256, IP_BN = 256, IP_BK = 32;
 constexpr int IPU_BN = 128;           // update pass: 256 x 128 tiles (waves 128 x 64)
 constexpr int IP_NT = 256;             // threads per workgroup
-constexpr int IP_PADN = 8;             // [row][k] tiles: 16-byte row pad
 constexpr int IP_PADT = 32;            // [k][row] tiles: 64-byte row pad
 
 TTT_DEV void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
@@ -54,7 +53,7 @@ TTT_DEV u32x2 ds_read_tr(const bf16_t* p) {
 
 // Operand fragment (32 rows x 16 k) of a 32x32x16 MFMA from a [k][row] LDS
 // tile with row stride ld (elements).  Lane l gets row r0 + l%32 and
-// k = k0 + 8*(l/32) + 0..7 (the same k assignment as frag_rows below).
+// k = k0 + 8*(l/32) + 0..7 (the k assignment the readout's row fragments use).
 TTT_DEV bf16x8 frag_tr(const bf16_t* s, int ld, int r0, int k0, int lane) {
     const int G = lane >> 4, a = lane & 15;
     const int h = G >> 1;                       // which 8-k half
@@ -63,10 +62,6 @@ TTT_DEV bf16x8 frag_tr(const bf16_t* s, int ld, int r0, int k0, int lane) {
     const u32x2 lo = ds_read_tr(s + (kk + 0) * ld + rbase);
     const u32x2 hi = ds_read_tr(s + (kk + 4) * ld + rbase);
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-// Operand fragment from a [row][k] LDS tile (k contiguous).
-TTT_DEV bf16x8 frag_rows(const bf16_t* s, int ld, int r0, int k0, int lane) {
-    return *reinterpret_cast<const bf16x8*>(s + (r0 + (lane & 31)) * ld + k0 + 8 * (lane >> 5));
 }
 
 // ------------------------------------------------------------------ pass 1
@@ -129,81 +124,70 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
     }
 
     // staging: per K-step 32 tokens x 256 of Z (4 x 16 B per thread) and
-    // 32 tokens x 128 of V (2 x 16 B per thread).  NS register sets are in
-    // flight: the loads of step s+NS are issued at the top of step s and
-    // written to LDS at the end of step s+NS-1.  Every lane issues the same
-    // loads each step (token rows past L re-read row L-1 and are zeroed when
-    // written to LDS), so the compiler's waits only drain the oldest set.
+    // 32 tokens x 128 of V (2 x 16 B per thread); K-step st covers tokens
+    // [32 st, 32 st + 32) (a chunk is a whole number of K-steps).  NS register
+    // sets are in flight: the loads of step st+NS are issued at the top of
+    // step st and written to LDS at the end of step st+NS-1.  Every lane issues
+    // the same loads each step (token rows past L re-read row L-1 and are
+    // zeroed when written to LDS), and the per-lane offsets are fixed.
     constexpr int NS = 4;
     u32x4 ra[NS][4], rb[NS][2];
     float re[NS];
     uint32_t zoff[4], voff[2];
-    int zrow[4], vrow[2];
+    int zrow[4], vrow[2], zlds[4], vlds[2];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-        const int u = tid + x * IP_NT;              // 0..1023
+        const int u = tid + x * IP_NT;              // 0..1023: 32 rows x 32 chunks
         zrow[x] = u >> 5;
-        zoff[x] = (uint32_t)((u & 31) * 8);
+        zoff[x] = (uint32_t)(zrow[x] * (int)p.ks[2] + (u & 31) * 8);
+        zlds[x] = zrow[x] * LDA + (u & 31) * 8;
     }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-        const int u = tid + x * IP_NT;              // 0..511
+        const int u = tid + x * IP_NT;              // 0..511: 32 rows x 16 chunks
         vrow[x] = u >> 4;
-        voff[x] = (uint32_t)((u & 15) * 8);
+        voff[x] = (uint32_t)(vrow[x] * (int)p.vs[2] + (u & 15) * 8);
+        vlds[x] = vrow[x] * LDB + (u & 15) * 8;
     }
     const int kpc = p.chunk / IP_BK;                // K-steps per chunk
     const int total_steps = p.nchunks * kpc;
-    auto step_t0 = [&](int st) { return (st / kpc) * p.chunk + (st % kpc) * IP_BK; };
+    const int full_steps = L / IP_BK;               // steps with all 32 tokens in range
     auto load = [&](int st, auto SET) __attribute__((always_inline)) {
         constexpr int k = decltype(SET)::value;
-        const int t0 = step_t0(min(st, total_steps - 1));
+        const int t0 = min(st, full_steps - 1) * IP_BK;  // whole steps only; see the tail below
+        const bf16_t* Zs = Zg + (int64_t)t0 * p.ks[2];
+        const bf16_t* Vs = Vg + (int64_t)t0 * p.vs[2];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int t = min(t0 + zrow[x], L - 1);
-            ra[k][x] = *reinterpret_cast<const u32x4*>(Zg + (int64_t)t * p.ks[2] + zoff[x]);
-        }
+        for (int x = 0; x < 4; ++x) ra[k][x] = *reinterpret_cast<const u32x4*>(Zs + zoff[x]);
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int t = min(t0 + vrow[x], L - 1);
-            rb[k][x] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)t * p.vs[2] + voff[x]);
-        }
-        if (PT) re[k] = Eg ? Eg[(int64_t)min(t0 + (tid & (IP_BK - 1)), L - 1) * p.es[2]] : p.eta_scalar;
+        for (int x = 0; x < 2; ++x) rb[k][x] = *reinterpret_cast<const u32x4*>(Vs + voff[x]);
+        if (PT) re[k] = Eg ? Eg[(int64_t)(t0 + (tid & (IP_BK - 1))) * p.es[2]] : p.eta_scalar;
     };
-    auto stage = [&](int st, int buf, auto SET) __attribute__((always_inline)) {
+    auto stage = [&](int buf, auto SET) __attribute__((always_inline)) {
         constexpr int k = decltype(SET)::value;
-        const int t0 = step_t0(st);
-        const u32x4 z4 = u32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int u = tid + x * IP_NT;
-            *reinterpret_cast<u32x4*>(&sA[buf][zrow[x] * LDA + (u & 31) * 8]) = (t0 + zrow[x] < L) ? ra[k][x] : z4;
-        }
+        for (int x = 0; x < 4; ++x) *reinterpret_cast<u32x4*>(&sA[buf][zlds[x]]) = ra[k][x];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int u = tid + x * IP_NT;
-            *reinterpret_cast<u32x4*>(&sB[buf][vrow[x] * LDB + (u & 15) * 8]) = (t0 + vrow[x] < L) ? rb[k][x] : z4;
-        }
-        if (PT && tid < IP_BK) sE[buf][tid] = (t0 + tid < L) ? re[k] : 0.f;
+        for (int x = 0; x < 2; ++x) *reinterpret_cast<u32x4*>(&sB[buf][vlds[x]]) = rb[k][x];
+        if (PT && tid < IP_BK) sE[buf][tid] = re[k];
     };
     const float out_scale = PT ? 1.f : p.eta_scalar;   // acc -> W
     bf16_t* snap = p.snap + (int64_t)bh * p.nchunks * p.dk * p.dv;
 
     // snapshot W_{chunk-1}^T (bf16) of this tile: [n][m] layout
     auto snapshot = [&](int chunk) __attribute__((always_inline)) {
-        bf16_t* sp = snap + (int64_t)chunk * p.dk * p.dv;
+        bf16_t* sp = snap + (int64_t)chunk * p.dk * p.dv + (int64_t)(n0 + 64 * wn + (lane & 31)) * p.dk +
+                     m0 + 128 * wm + 4 * (lane >> 5);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int col = n0 + 64 * wn + 32 * j + (lane & 31);
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int row = m0 + 128 * wm + 32 * i + 8 * q + 4 * (lane >> 5);
                     const f32x4 v4 = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
                                            acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    st4(sp + (int64_t)col * p.dk + row, v4 * out_scale);
+                    st4(sp + (int64_t)(32 * j) * p.dk + 32 * i + 8 * q, v4 * out_scale);
                 }
-            }
     };
     auto compute = [&](int buf) __attribute__((always_inline)) {
         const bf16_t* A = sA[buf];
@@ -244,28 +228,70 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
     using K2 = std::integral_constant<int, 2>;
     using K3 = std::integral_constant<int, 3>;
     static_assert(NS == 4, "the step sequence below is written for four register sets");
-    load(0, K0{});
-    load(1, K1{});
-    load(2, K2{});
-    load(3, K3{});
-    stage(0, 0, K0{});
+    if (full_steps > 0) {
+        load(0, K0{});
+        load(1, K1{});
+        load(2, K2{});
+        load(3, K3{});
+        stage(0, K0{});
+    }
     __syncthreads();
-    // step st: refill the set step st just freed, compute from LDS, write step
-    // st+1 to the other LDS buffer
+    // whole steps: refill the set this step just freed, compute from LDS,
+    // write step st+1 to the other LDS buffer
     auto step = [&](int st, auto CUR, auto NXT) __attribute__((always_inline)) {
-        if (st >= total_steps) return;               // (uniform)
-        if (st % kpc == 0) snapshot(st / kpc);
         load(st + NS, CUR);
         compute(st & 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (st + 1 < total_steps) stage(st + 1, (st + 1) & 1, NXT);
+        if (st + 1 < full_steps) stage((st + 1) & 1, NXT);
         __syncthreads();
     };
-    for (int st = 0; st < total_steps; st += NS) {
+    // chunk boundaries fall on multiples of kpc (a multiple of 8), so they
+    // only ever meet the first step of a group of four
+    int next_snap = 0, snap_idx = 0;
+    auto boundary = [&](int at) __attribute__((always_inline)) {
+        if (at == next_snap) {
+            snapshot(snap_idx);
+            ++snap_idx;
+            next_snap += kpc;
+        }
+    };
+    int st = 0;
+    for (; st + NS <= full_steps; st += NS) {
+        boundary(st);
         step(st, K0{}, K1{});
         step(st + 1, K1{}, K2{});
         step(st + 2, K2{}, K3{});
         step(st + 3, K3{}, K0{});
+    }
+    // up to three whole steps left: their data sit in sets 0, 1, 2
+    if (st < full_steps) {
+        boundary(st);
+        step(st, K0{}, K1{});
+        if (st + 1 < full_steps) step(st + 1, K1{}, K2{});
+        if (st + 2 < full_steps) step(st + 2, K2{}, K3{});
+    }
+    // a last step with fewer than 32 tokens: rows past L are zeroed
+    if (full_steps * IP_BK < L) {
+        const int t0 = full_steps * IP_BK;
+        boundary(full_steps);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int t = min(t0 + zrow[x], L - 1);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(Zg + (int64_t)(t - zrow[x]) * p.ks[2] + zoff[x]);
+            *reinterpret_cast<u32x4*>(&sA[0][zlds[x]]) = (t0 + zrow[x] < L) ? v : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int t = min(t0 + vrow[x], L - 1);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(Vg + (int64_t)(t - vrow[x]) * p.vs[2] + voff[x]);
+            *reinterpret_cast<u32x4*>(&sB[0][vlds[x]]) = (t0 + vrow[x] < L) ? v : u32x4{0, 0, 0, 0};
+        }
+        if (PT && tid < IP_BK) {
+            const int t = t0 + tid;
+            sE[0][tid] = (t < L) ? (Eg ? Eg[(int64_t)t * p.es[2]] : p.eta_scalar) : 0.f;
+        }
+        __syncthreads();
+        compute(0);
     }
 
     if (p.S_final) {
@@ -295,10 +321,14 @@ struct IpReadoutParams {
     int H, L, dk, dv, chunk, nchunks;
 };
 
+// Readout LDS tiles: [256 rows][32 k] bf16 with 64-byte rows (4 chunks of
+// 16 bytes), chunk c of row r stored at c ^ ((r >> 2) & 3): conflict-free for
+// the row-order staging writes and for the fragment reads (16 rows per pass).
+TTT_DEV int ro_swz(int r) { return (r >> 2) & 3; }
+
 __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
-    constexpr int LD = IP_BK + IP_PADN;
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2][IP_BM * LD];    // snap^T [n][k]
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2][IP_BN * LD];    // Z      [t][k]
+    __shared__ __attribute__((aligned(16))) bf16_t sA[2][IP_BM * IP_BK];    // snap^T [n][k]
+    __shared__ __attribute__((aligned(16))) bf16_t sB[2][IP_BN * IP_BK];    // Z      [t][k]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -318,7 +348,7 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
     const int bh = lid / gridDim.x, b = bh / p.H, h = bh % p.H;
     if (t0 >= p.L) return;                            // whole tile past the end (uniform)
     const bf16_t* S = p.snap + ((int64_t)bh * p.nchunks + chunk) * p.dk * p.dv + (int64_t)n0 * p.dk;
-    const bf16_t* Zg = p.q + b * p.qs[0] + h * p.qs[1];
+    const bf16_t* Zt = p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)t0 * p.qs[2];
     bf16_t* Og = p.out + b * p.os[0] + h * p.os[1];
     const int L = p.L;
 
@@ -330,46 +360,83 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    u32x4 ra[4], rb[4];
-    auto load = [&](int k0) {
-        for (int y = 0; y < 4; ++y) {
-            const int u = tid + y * IP_NT;            // 0..1023: 256 rows x 4 x 16 B
-            const int row = u >> 2, c = (u & 3) * 8;
-            ra[y] = *reinterpret_cast<const u32x4*>(S + (int64_t)row * p.dk + k0 + c);
-            const int t = t0 + row;
-            rb[y] = (t < L) ? *reinterpret_cast<const u32x4*>(Zg + t * p.qs[2] + k0 + c) : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto stage = [&](int buf) {
-        for (int y = 0; y < 4; ++y) {
-            const int u = tid + y * IP_NT;
-            const int row = u >> 2, c = (u & 3) * 8;
-            *reinterpret_cast<u32x4*>(&sA[buf][row * LD + c]) = ra[y];
-            *reinterpret_cast<u32x4*>(&sB[buf][row * LD + c]) = rb[y];
-        }
-    };
-
-    const int steps = p.dk / IP_BK;
-    load(0);
-    stage(0);
-    __syncthreads();
-    for (int s = 0; s < steps; ++s) {
-        const int buf = s & 1;
-        if (s + 1 < steps) load((s + 1) * IP_BK);
+    // staging: 256 rows x 4 chunks per operand, thread -> 4 (row, chunk) pairs;
+    // per-lane offsets are the same for every K-step (token rows past L read
+    // row L-1: their outputs are never stored)
+    constexpr int NS = 4;                             // K-steps of loads in flight
+    u32x4 ra[NS][4], rb[NS][4];
+    uint32_t aoff[4], boff[4];
+    int loff[4];
 #pragma unroll
-        for (int kk = 0; kk < IP_BK; kk += 16) {
+    for (int y = 0; y < 4; ++y) {
+        const int u = tid + y * IP_NT, row = u >> 2, c = u & 3;
+        aoff[y] = (uint32_t)(row * p.dk + 8 * c);
+        boff[y] = (uint32_t)(min(row, L - 1 - t0) * (int)p.qs[2] + 8 * c);
+        loff[y] = row * IP_BK + 8 * (c ^ ro_swz(row));
+    }
+    const int steps = p.dk / IP_BK;
+    auto load = [&](int st, auto SET) __attribute__((always_inline)) {
+        constexpr int k = decltype(SET)::value;
+        const int k0 = min(st, steps - 1) * IP_BK;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            ra[k][y] = *reinterpret_cast<const u32x4*>(S + aoff[y] + k0);
+            rb[k][y] = *reinterpret_cast<const u32x4*>(Zt + boff[y] + k0);
+        }
+    };
+    auto stage = [&](int buf, auto SET) __attribute__((always_inline)) {
+        constexpr int k = decltype(SET)::value;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+            *reinterpret_cast<u32x4*>(&sA[buf][loff[y]]) = ra[k][y];
+            *reinterpret_cast<u32x4*>(&sB[buf][loff[y]]) = rb[k][y];
+        }
+    };
+    // fragment reads: lane -> row r0 + lane%32 (r0 a multiple of 32), k half lane/32
+    const int lrow = lane & 31;
+    const int fb0 = lrow * IP_BK + 8 * ((lane >> 5) ^ ro_swz(lrow));        // kk = 0
+    const int fb1 = lrow * IP_BK + 8 * ((2 | (lane >> 5)) ^ ro_swz(lrow));  // kk = 16
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+        const bf16_t* A = sA[buf];
+        const bf16_t* B = sB[buf];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const int fb = kh ? fb1 : fb0;
             bf16x8 af[4], bfr[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = frag_rows(sA[buf], LD, 128 * wm + 32 * i, kk, lane);
+            for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(A + (128 * wm + 32 * i) * IP_BK + fb);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[j] = frag_rows(sB[buf], LD, 128 * wn + 32 * j, kk, lane);
+            for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(B + (128 * wn + 32 * j) * IP_BK + fb);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) mma32(acc[i][j], af[i], bfr[j]);
         }
-        if (s + 1 < steps) stage(buf ^ 1);
+    };
+
+    using K0 = std::integral_constant<int, 0>;
+    using K1 = std::integral_constant<int, 1>;
+    using K2 = std::integral_constant<int, 2>;
+    using K3 = std::integral_constant<int, 3>;
+    load(0, K0{});
+    load(1, K1{});
+    load(2, K2{});
+    load(3, K3{});
+    stage(0, K0{});
+    __syncthreads();
+    auto step = [&](int st, auto CUR, auto NXT) __attribute__((always_inline)) {
+        load(st + NS, CUR);
+        compute(st & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 < steps) stage((st + 1) & 1, NXT);
         __syncthreads();
+    };
+    // steps is a multiple of 8 (dk a multiple of 256)
+    for (int st = 0; st < steps; st += NS) {
+        step(st, K0{}, K1{});
+        step(st + 1, K1{}, K2{});
+        step(st + 2, K2{}, K3{});
+        step(st + 3, K3{}, K0{});
     }
 
     // acc[i][j]: O^T[n][t], lane = token column, 4 consecutive n per group
