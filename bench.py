@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "tcb_fwd_kernel": ("tcb_fwd.hip", "common.h"),
     "ip_update_kernel+ip_readout_kernel": ("inplace.hip", "common.h"),
     "dual_fwd_kernel": ("dual.hip", "common.h"),
+    "dual_chain_kernel": ("dual.hip", "common.h"),
 }
 
 
@@ -125,7 +126,7 @@ def setup_workload(name: str, dev: str):
         bytes_alg = B * H * L * 4 * d * 2 + 2 * B * H * d * d * 4
         flop_alg = B * H * L * (6 * d * d + (mb + 1) * 2 * d)
         info = dict(workload=name, B=B, H=H, L=L, d=d, minibatch=mb, dtype="bf16", tokens=B * L,
-                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="dual_fwd_kernel", inputs=inp)
+                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="dual_chain_kernel", inputs=inp)
         return step, info
     raise SystemExit(f"unknown workload {name}")
 
