@@ -31,9 +31,17 @@ FLAGS = [
 
 
 
+# Translation units whose MFMA accumulators stay in architectural VGPRs
+# (no v_accvgpr reads before each VALU use of a result).  Only for code that
+# uses no 16x16x16 MFMA: for that form the compiler left too few wait states
+# between the MFMA and a VALU read of its result.
+VGPR_FORM = {"dual.hip"}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
+    extra = ["-mllvm", "-amdgpu-mfma-vgpr-form"] if os.path.basename(src) in VGPR_FORM else []
+    cmd = [HIPCC, *FLAGS, *extra, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

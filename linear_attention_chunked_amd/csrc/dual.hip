@@ -292,9 +292,13 @@ TTT_DEV u32x2 tr_read_d(const bf16_t* p) {
     typedef __attribute__((address_space(3))) s16x4d lds_s16x4;
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
 }
+// 16 x 16 x 16 product (k = 4g + j in lane group g) issued as a 16x16x32 MFMA
+// whose upper k half is zero: lane slot j < 4 of both operands carries k =
+// 4g + j, slots 4..7 are 0
 TTT_DEV void mma16(f32x4& acc, const u32x2& a, const u32x2& b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4d, a), __builtin_bit_cast(s16x4d, b),
-                                                   acc, 0, 0, 0);
+    const bf16x8 A = __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], 0u, 0u});
+    const bf16x8 B = __builtin_bit_cast(bf16x8, u32x4{b[0], b[1], 0u, 0u});
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
 }
 // 8-byte chunk swizzle of the [16 tokens][64] K tile (rows of 16 chunks; bit 0
 // untouched so 16-byte pairs stay whole): conflict-free row writes, at most
@@ -303,7 +307,8 @@ TTT_DEV int kswz(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) |
 // feature of state row position p
 TTT_DEV int feat(int p) { return (p & ~31) + 8 * ((p >> 2) & 3) + 4 * ((p >> 4) & 1) + (p & 3); }
 
-template <int DEPTH>
+// ONESTEP: every mini-batch is exactly one 16-token step (W_n is S~ itself)
+template <int DEPTH, bool ONESTEP>
 __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
     constexpr int D = 64, DV = 64;
     __shared__ __attribute__((aligned(16))) bf16_t sK[16 * D];   // [token][d], 8-byte chunks swizzled
@@ -337,18 +342,37 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
     // columns 4g .. +4 of this wave's V tile
     u32x4 rq[DEPTH][2], rk[DEPTH][2];
     u32x2 rv[DEPTH];
+    // whole steps address a uniform row base plus a fixed lane offset; the
+    // last, partial step clamps rows to L-1 (both paths issue the same loads)
+    const uint32_t qko = (uint32_t)(c16 * D + 8 * g), vo = (uint32_t)(c16 * DV + 4 * g);
     auto load = [&](int s, auto SET) {
         constexpr int st = decltype(SET)::value;
-        const int t = min(16 * s + c16, L - 1);
-        const bf16_t* q = Qg + (int64_t)t * D + 8 * g;
-        const bf16_t* k = Kg + (int64_t)t * D + 8 * g;
+        const int t0 = 16 * s;
+        if (t0 + 16 <= L) {
+            const bf16_t* q = Qg + (int64_t)t0 * D;
+            const bf16_t* k = Kg + (int64_t)t0 * D;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            rq[st][kb] = *reinterpret_cast<const u32x4*>(q + 32 * kb);
-            rk[st][kb] = *reinterpret_cast<const u32x4*>(k + 32 * kb);
+            for (int kb = 0; kb < 2; ++kb) {
+                rq[st][kb] = *reinterpret_cast<const u32x4*>(q + qko + 32 * kb);
+                rk[st][kb] = *reinterpret_cast<const u32x4*>(k + qko + 32 * kb);
+            }
+            rv[st] = *reinterpret_cast<const u32x2*>(Vg + (int64_t)t0 * DV + vo);
+        } else {
+            const int t = min(t0 + c16, L - 1);
+            const bf16_t* q = Qg + (int64_t)t * D + 8 * g;
+            const bf16_t* k = Kg + (int64_t)t * D + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                rq[st][kb] = *reinterpret_cast<const u32x4*>(q + 32 * kb);
+                rk[st][kb] = *reinterpret_cast<const u32x4*>(k + 32 * kb);
+            }
+            rv[st] = *reinterpret_cast<const u32x2*>(Vg + (int64_t)t * DV + 4 * g);
         }
-        rv[st] = *reinterpret_cast<const u32x2*>(Vg + (int64_t)t * DV + 4 * g);
     };
+    // causal mask of the P^T tile (j = 4g + r <= i = c16), fixed per lane
+    f32x4 pmask;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pmask[r] = (4 * g + r <= c16) ? 1.f : 0.f;
 
     // LDS addresses (elements)
     const int kw = c16 * D, ksw = kswz(c16);                 // K row writes
@@ -373,8 +397,8 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
 
         // E[token 4g+r][col c16] = K W_n
         f32x4 e = zero4();
-        mma(e, Kf0, Wop[0]);
-        mma(e, Kf1, Wop[1]);
+        mma(e, Kf0, ONESTEP ? Sop[0] : Wop[0]);
+        mma(e, Kf1, ONESTEP ? Sop[1] : Wop[1]);
         // P^T[j 4g+r][i c16] = K Q^T, causal j <= i
         f32x4 pt = zero4();
         mma(pt, Kf0, Qf0);
@@ -397,7 +421,11 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
         vt[2] = __uint_as_float(vraw[1] << 16);
         vt[3] = __uint_as_float(vraw[1] & 0xffff0000u);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vt[r] = (t0 + 4 * g + r < L) ? eta * (vt[r] - e[r]) : 0.f;
+        for (int r = 0; r < 4; ++r) vt[r] = eta * (vt[r] - e[r]);
+        if (t0 + 16 > L) {   // partial or empty step (uniform)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vt[r] = (t0 + 4 * g + r < L) ? vt[r] : 0.f;
+        }
         const u32x2 VB = u32x2{pack2bf(vt[0], vt[1]), pack2bf(vt[2], vt[3])};
 
         // S~ += K^T V~ : K^T tile t (positions 16t..) through the transposing read
@@ -408,15 +436,16 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) Sop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
-        const int t1 = t0 + 16;
-        if (t1 % mb == 0 || t1 >= L) {   // mini-batch end: W_{n+1} = S~
-            Wop[0] = Sop[0];
-            Wop[1] = Sop[1];
+        if (!ONESTEP) {
+            const int t1 = t0 + 16;
+            if (t1 % mb == 0 || t1 >= L) {   // mini-batch end: W_{n+1} = S~
+                Wop[0] = Sop[0];
+                Wop[1] = Sop[1];
+            }
         }
 
         // O^T += V~^T P^T, store O rows (4 consecutive columns per lane)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pt[r] = (4 * g + r <= c16) ? pt[r] : 0.f;
+        pt *= pmask;
         mma16(o, VB, u32x2{pack2bf(pt[0], pt[1]), pack2bf(pt[2], pt[3])});
         if (t0 + c16 < L)
             *reinterpret_cast<u32x2*>(&Og[(int64_t)(t0 + c16) * DV + 4 * g]) = u32x2{pack2bf(o[0], o[1]), pack2bf(o[2], o[3])};
@@ -461,7 +490,10 @@ hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t s) {
     if (!dual_supported(dtype, p.d, p.dv, p.minibatch)) return hipErrorInvalidValue;
     if (dtype == 1 && p.minibatch % 16 == 0) {
         // one wave per (b, h, 16-column tile)
-        hipLaunchKernelGGL((dual_chain_kernel<6>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+        if (p.minibatch == 16)
+            hipLaunchKernelGGL((dual_chain_kernel<6, true>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+        else
+            hipLaunchKernelGGL((dual_chain_kernel<6, false>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
         return hipGetLastError();
     }
     const int grid = p.B * p.H;
