@@ -342,37 +342,31 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
     // columns 4g .. +4 of this wave's V tile
     u32x4 rq[DEPTH][2], rk[DEPTH][2];
     u32x2 rv[DEPTH];
-    // whole steps address a uniform row base plus a fixed lane offset; the
-    // last, partial step clamps rows to L-1 (both paths issue the same loads)
-    const uint32_t qko = (uint32_t)(c16 * D + 8 * g), vo = (uint32_t)(c16 * DV + 4 * g);
+    // Buffer accesses: one descriptor per tensor of this head (the range is
+    // the head's rows), a fixed 32-bit lane offset and the step's row offset
+    // in a scalar.  Rows past L fall outside the range: loads return zero
+    // (a zero K row gives E = 0 and V~ = 0, so it adds nothing) and stores
+    // are dropped, so no step needs a clamp or a mask.
+    const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)Qg, 0, L * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, L * D * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, L * DV * 2 - 32 * w, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)Og, 0, L * DV * 2 - 32 * w, 0x00020000);
+    const int qko = (c16 * D + 8 * g) * 2, vo = (c16 * DV + 4 * g) * 2;   // bytes
     auto load = [&](int s, auto SET) {
         constexpr int st = decltype(SET)::value;
-        const int t0 = 16 * s;
-        if (t0 + 16 <= L) {
-            const bf16_t* q = Qg + (int64_t)t0 * D;
-            const bf16_t* k = Kg + (int64_t)t0 * D;
+        const int rowb = s * 16 * D * 2;   // (D == DV)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                rq[st][kb] = *reinterpret_cast<const u32x4*>(q + qko + 32 * kb);
-                rk[st][kb] = *reinterpret_cast<const u32x4*>(k + qko + 32 * kb);
-            }
-            rv[st] = *reinterpret_cast<const u32x2*>(Vg + (int64_t)t0 * DV + vo);
-        } else {
-            const int t = min(t0 + c16, L - 1);
-            const bf16_t* q = Qg + (int64_t)t * D + 8 * g;
-            const bf16_t* k = Kg + (int64_t)t * D + 8 * g;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                rq[st][kb] = *reinterpret_cast<const u32x4*>(q + 32 * kb);
-                rk[st][kb] = *reinterpret_cast<const u32x4*>(k + 32 * kb);
-            }
-            rv[st] = *reinterpret_cast<const u32x2*>(Vg + (int64_t)t * DV + 4 * g);
+        for (int kb = 0; kb < 2; ++kb) {
+            rq[st][kb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qko + 64 * kb, rowb, 0));
+            rk[st][kb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, qko + 64 * kb, rowb, 0));
         }
+        rv[st] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rV, vo, rowb, 0));
     };
-    // causal mask of the P^T tile (j = 4g + r <= i = c16), fixed per lane
-    f32x4 pmask;
+    // causal mask of the packed bf16 P^T pieces (j = 4g + r <= i = c16), fixed per lane
+    u32x2 pmask;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pmask[r] = (4 * g + r <= c16) ? 1.f : 0.f;
+    for (int h = 0; h < 2; ++h)
+        pmask[h] = ((4 * g + 2 * h <= c16) ? 0x0000ffffu : 0u) | ((4 * g + 2 * h + 1 <= c16) ? 0xffff0000u : 0u);
 
     // LDS addresses (elements)
     const int kw = c16 * D, ksw = kswz(c16);                 // K row writes
@@ -422,10 +416,6 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
         vt[3] = __uint_as_float(vraw[1] & 0xffff0000u);
 #pragma unroll
         for (int r = 0; r < 4; ++r) vt[r] = eta * (vt[r] - e[r]);
-        if (t0 + 16 > L) {   // partial or empty step (uniform)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vt[r] = (t0 + 4 * g + r < L) ? vt[r] : 0.f;
-        }
         const u32x2 VB = u32x2{pack2bf(vt[0], vt[1]), pack2bf(vt[2], vt[3])};
 
         // S~ += K^T V~ : K^T tile t (positions 16t..) through the transposing read
@@ -445,10 +435,9 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
         }
 
         // O^T += V~^T P^T, store O rows (4 consecutive columns per lane)
-        pt *= pmask;
-        mma16(o, VB, u32x2{pack2bf(pt[0], pt[1]), pack2bf(pt[2], pt[3])});
-        if (t0 + c16 < L)
-            *reinterpret_cast<u32x2*>(&Og[(int64_t)(t0 + c16) * DV + 4 * g]) = u32x2{pack2bf(o[0], o[1]), pack2bf(o[2], o[3])};
+        mma16(o, VB, u32x2{pack2bf(pt[0], pt[1]) & pmask[0], pack2bf(pt[2], pt[3]) & pmask[1]});
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, u32x2{pack2bf(o[0], o[1]), pack2bf(o[2], o[3])}),
+                                              rO, vo, t0 * DV * 2, 0);
     };
 
     using S0 = std::integral_constant<int, 0>;
