@@ -11,6 +11,8 @@
  *   ttt_chunk_state_scan  the associative scan over per-chunk state deltas
  *   ttt_dual_form_fwd     the non-associative TTT-Linear mini-batch update
  *                         (MSE reconstruction loss), dual form
+ *   ttt_decode_step       one recurrent token per sequence (inference):
+ *                         state update and readout with the state in HBM
  *
  * Sources (cited by page title and paragraph or section):
  *  [P1] "KV 바인딩 기반 테스트 시간 학습은 사실상 선형 어텐션이다"
@@ -196,6 +198,38 @@ ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32
                                const float* W0, int64_t W0_stride_bh, float eta,
                                void* out, float* W_final,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ttt_decode_step -- one token of the token-causal recurrence per (b, h),
+ * with the state updated in place.
+ *
+ * [P1] paragraphs on the state-matrix update and the one-step output
+ * identity; [P4] section on the inner update rule and the fixed-size state
+ * that replaces a growing cache.  With g = eta k^T v:
+ *     m <- beta m + g,  S <- S + m,  o = q S   (o reads the updated state),
+ * i.e. exactly ttt_fwd_chunked in TOKEN_CAUSAL mode for L = 1 with
+ * S0 = S, M0 = M and S_final = S.  Calling it for t = 0..L-1 reproduces the
+ * chunked forward over the L tokens.
+ *
+ * q, k [B,H,dk] and v, out [B,H,dv] are contiguous, dtype `dtype` (out in
+ * that dtype).  eta [B,H] fp32 or NULL (eta_scalar for every sequence).
+ * S [B,H,dk,dv] fp32 contiguous, read and written in place; M the same shape,
+ * required when beta != 0 (ignored and may be NULL otherwise).  out must not
+ * overlap q, k, v, S or M.  Supported: dk in [1, 1024], dv a multiple of 4.
+ * The state is read and written once (memory-bound); the update is fp32.
+ * All pointers are caller-owned device memory, 16-byte aligned; stream is a
+ * hipStream_t (NULL = default stream).  Nothing is allocated.
+ *
+ * Errors (checked before anything is enqueued): TTT_ERR_DTYPE, TTT_ERR_SHAPE
+ * (a size < 1), TTT_ERR_VALUE (beta outside [0, 1)), TTT_ERR_NULL (q, k, v, S
+ * or out NULL, or M NULL with beta != 0), TTT_ERR_ALIGN, TTT_ERR_UNSUPPORTED
+ * (dk or dv outside the supported set), TTT_ERR_ALIAS (out overlaps an input,
+ * or S overlaps M with beta != 0); TTT_ERR_HIP if the launch fails.
+ */
+ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t dtype,
+                             const void* q, const void* k, const void* v,
+                             const float* eta, float eta_scalar, float beta,
+                             float* S, float* M, void* out, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* ttt_status_string(ttt_status_t status);

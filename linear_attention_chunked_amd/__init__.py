@@ -10,6 +10,7 @@ Entry points (same names as the C ABI):
     fwd_chunked(q, k, v, ...)          token-causal / chunk-causal forward
     chunk_state_scan(dS, dM, ...)      exclusive scan of chunk-state deltas
     dual_form_fwd(q, k, v, W0, ...)    TTT-Linear mini-batch dual form
+    decode_step(q, k, v, S, M, ...)    one recurrent token, state updated in place
 """
 from __future__ import annotations
 
@@ -77,6 +78,9 @@ def load_library():
     lib.ttt_dual_form_fwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp,
                                       ctypes.c_int64, f32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.ttt_dual_form_fwd.restype = ctypes.c_int
+    lib.ttt_decode_step.argtypes = [i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, f32, _vp, _vp,
+                                    _vp, _vp]
+    lib.ttt_decode_step.restype = ctypes.c_int
     lib.ttt_status_string.argtypes = [ctypes.c_int]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_fwd_args_size.argtypes = []
@@ -250,5 +254,37 @@ def dual_form_fwd(q, k, v, W0, *, eta, minibatch, out=None, return_state=False, 
     return out
 
 
-__all__ = ["fwd_chunked", "chunk_state_scan", "dual_form_fwd", "load_library", "TTTError",
+def decode_step(q, k, v, S, M=None, *, eta=None, eta_scalar=0.0, beta=0.0, out=None, stream=None):
+    """One recurrent token per (b, h) (``ttt_decode_step``).
+
+    q, k: [B,H,dk]; v: [B,H,dv] contiguous, fp32 or bf16; eta fp32 [B,H] or
+    None (then eta_scalar).  S (and M when beta != 0): fp32 [B,H,dk,dv]
+    contiguous, updated in place.  Returns out [B,H,dv] in q's dtype."""
+    lib = load_library()
+    _require_gpu(q, k, v, S, M, eta, out)
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, H, dv):
+        raise ValueError("k must match q and v must be [B,H,dv]")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        if not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{nm} must be contiguous and of q's dtype")
+    for t, nm in ((S, "S"), (M, "M")):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()
+                              or t.shape != (B, H, dk, dv)):
+            raise ValueError(f"{nm} must be contiguous fp32 [B,H,dk,dv]")
+    if eta is not None and (eta.dtype != torch.float32 or not eta.is_contiguous()
+                            or eta.numel() != B * H):
+        raise ValueError("eta must be contiguous fp32 [B,H]")
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    _check(lib.ttt_decode_step(B, H, dk, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                               float(eta_scalar), float(beta), _ptr(S), _ptr(M), _ptr(out),
+                               _stream(stream)))
+    return out
+
+
+__all__ = ["fwd_chunked", "chunk_state_scan", "dual_form_fwd", "decode_step", "load_library", "TTTError",
            "FwdArgs", "LIB_PATH"]

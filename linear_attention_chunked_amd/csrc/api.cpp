@@ -235,4 +235,48 @@ ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32
     return from_hip(ttt::launch_dual_fwd(p, dtype, reinterpret_cast<hipStream_t>(stream)));
 }
 
+ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,
+                             const void* k, const void* v, const float* eta, float eta_scalar, float beta,
+                             float* S, float* M, void* out, void* stream) {
+    if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
+    if (B < 1 || H < 1 || dk < 1 || dv < 1) return TTT_ERR_SHAPE;
+    if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_VALUE;
+    if (!q || !k || !v || !S || !out) return TTT_ERR_NULL;
+    if (beta != 0.f && !M) return TTT_ERR_NULL;
+    const void* ptrs[] = {q, k, v, S, out, eta, beta != 0.f ? M : nullptr};
+    for (const void* x : ptrs)
+        if (x && !aligned16(x)) return TTT_ERR_ALIGN;
+    if (!ttt::decode_supported(dtype, dk, dv)) return TTT_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + (size_t)B * H * dv * es;
+    const struct { const void* p; size_t n; } ins[] = {
+        {q, (size_t)B * H * dk * es}, {k, (size_t)B * H * dk * es}, {v, (size_t)B * H * dv * es},
+        {S, (size_t)B * H * dk * dv * 4}, {beta != 0.f ? M : nullptr, (size_t)B * H * dk * dv * 4}};
+    for (const auto& in : ins) {
+        if (!in.p) continue;
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(in.p);
+        if (overlap(o0, o1, a0, a0 + in.n)) return TTT_ERR_ALIAS;
+    }
+    if (beta != 0.f) {   // S and M are both written: they must not overlap either
+        const uintptr_t s0 = reinterpret_cast<uintptr_t>(S), m0 = reinterpret_cast<uintptr_t>(M);
+        const size_t n = (size_t)B * H * dk * dv * 4;
+        if (overlap(s0, s0 + n, m0, m0 + n)) return TTT_ERR_ALIAS;
+    }
+    ttt::DecodeParams p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.out = out;
+    p.eta = eta;
+    p.eta_scalar = eta_scalar;
+    p.beta = beta;
+    p.S = S;
+    p.M = beta != 0.f ? M : nullptr;
+    p.B = B;
+    p.H = H;
+    p.dk = dk;
+    p.dv = dv;
+    return from_hip(ttt::launch_decode(p, dtype, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -79,4 +79,20 @@ struct DualParams {
 hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t stream);
 bool dual_supported(int dtype, int d, int dv, int minibatch);
 
+// Recurrent decode step (one token per (b, h), state in place).
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    const float* eta;
+    float eta_scalar;
+    float beta;
+    float* S;
+    float* M;
+    int B, H, dk, dv;
+};
+hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream);
+bool decode_supported(int dtype, int dk, int dv);
+
 }  // namespace ttt

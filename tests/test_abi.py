@@ -141,6 +141,26 @@ def test_dual_rejects_before_launch(lib):
     assert f(*args(out=FAKE + n)) == ERR_ALIAS
 
 
+def test_decode_rejects_before_launch(lib):
+    f = lib.ttt_decode_step
+    n = 1 << 20
+
+    def args(**kw):
+        return [kw.get("B", 2), 2, kw.get("dk", 64), kw.get("dv", 64), kw.get("dtype", 1),
+                kw.get("q", FAKE), FAKE + n, FAKE + 2 * n, None, 0.1, kw.get("beta", 0.5),
+                kw.get("S", FAKE + 3 * n), kw.get("M", FAKE + 4 * n), kw.get("out", FAKE + 5 * n), None]
+    assert f(*args(dtype=2)) == ERR_DTYPE
+    assert f(*args(B=0)) == ERR_SHAPE
+    assert f(*args(beta=1.0)) == ERR_VALUE
+    assert f(*args(q=None)) == ERR_NULL
+    assert f(*args(M=None)) == ERR_NULL               # momentum needs M
+    assert f(*args(S=FAKE + 3 * n + 4)) == ERR_ALIGN
+    assert f(*args(dv=30)) == ERR_UNSUP
+    assert f(*args(dk=2048)) == ERR_UNSUP
+    assert f(*args(out=FAKE + 3 * n + 256)) == ERR_ALIAS  # out inside S
+    assert f(*args(M=FAKE + 3 * n + 512)) == ERR_ALIAS    # M overlapping S
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 1, 64, 64)

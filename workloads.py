@@ -11,7 +11,7 @@ here.
 Every tensor comes from ``torch.Generator('cpu').manual_seed(seed)``: values
 are drawn in fp32, transformed in fp32, then rounded (round-to-nearest-even)
 to the workload dtype.  The tensor index ``j`` in ``seed = 1000*cfg + j``
-follows the order q, k, v, eta-logits, S0.  The In-Place (chunk-causal)
+follows the order q, k, v, eta-logits, S0, M0.  The In-Place (chunk-causal)
 workload is drawn chunk by chunk (``seed = 3_000_000 + 4*i + j`` for chunk
 ``i``; j = 0 a, 1 b, 2 V-hat) so a host never holds fp32 copies of the
 long-context tensors.
@@ -22,6 +22,7 @@ Workloads (shapes of the pages' settings):
   inplace     In-Place chunk-causal Wdown update, L 32768 / 131072, d_ff 9728, d_model 2560, C1024
   momentum    momentum token-causal bf16, B4 H8 L16384 d128, C128, eta 0.05, beta 0.9
   dual        TTT-Linear mini-batch dual form, B4 H16 L8192 d64, b 16 and 2048, W0 0.5 I
+  decode      one recurrent token per sequence, B256 H16 d128, state S0 (and M0) carried in
 """
 from __future__ import annotations
 
@@ -162,6 +163,23 @@ def gen_dual(B=4, H=16, L=8192, d=64, minibatch=16, seed_base=5000) -> DualInput
     W0 = (0.5 * torch.eye(d, dtype=torch.float32)).expand(B, H, d, d).contiguous()
     return DualInputs(q, k, v, W0, f32(1.0 / d), minibatch, "bf16",
                       dict(workload="dual", B=B, H=H, L=L, d=d))
+
+
+# ------------------------------------------------------------------ decode step
+def gen_decode(B=256, H=16, d=128, beta=0.0, seed_base=7000) -> TokenCausalInputs:
+    """One decode token per sequence (L = 1) against a carried state, LM-scale
+    heads: bf16 q,v ~ N(0,1); k ~ N(0,1) L2-normalised in fp32, then bf16;
+    eta = 0.1*sigmoid(N(0,1)) fp32 per (b,h); S0 ~ N(0, 0.02^2) fp32;
+    with momentum, M0 ~ N(0, 0.002^2) fp32."""
+    q = _randn((B, H, 1, d), seed_base + 0).to(torch.bfloat16)
+    kr = _randn((B, H, 1, d), seed_base + 1)
+    k = (kr / kr.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    v = _randn((B, H, 1, d), seed_base + 2).to(torch.bfloat16)
+    eta = (0.1 * torch.sigmoid(_randn((B, H, 1), seed_base + 3))).float()
+    S0 = _randn((B, H, d, d), seed_base + 4) * 0.02
+    M0 = _randn((B, H, d, d), seed_base + 5) * 0.002 if beta else None
+    return TokenCausalInputs(q, k, v, eta, 0.0, f32(beta), S0, M0, 1, "bf16",
+                             dict(workload="decode", B=B, H=H, L=1, dk=d, dv=d))
 
 
 def gen_state_deltas(B, H, N, dk, dv, seed=6000, scale=1.0, integer=False):
