@@ -7,6 +7,10 @@ One step = one full pass of the hot path over one batch of synthetic input
 workload, one ttt_fwd_chunked call (token-causal, per-token eta, S0 in,
 outputs and final state out).  Prints ONE JSON line.
 
+Warm-up: the W warm-up steps are extended until at least --min-warmup-s
+seconds of steps have run (the count actually run is reported), so that the
+timed steps see the GPU's steady clocks rather than its ramp.
+
 Roofline: the dominant kernel's average launch duration is measured with
 HIP events recorded on the launch stream around every timed step; achieved
 bandwidth = algorithmic bytes per launch / that duration.  HBM traffic
@@ -217,6 +221,8 @@ def main():
     ap.add_argument("--workload", default="lm-scale",
                     help="lm-scale (default), small-f32, inplace-32k, inplace-128k, momentum, dual-b16, "
                          "dual-b2048, decode, decode-momentum")
+    ap.add_argument("--min-warmup-s", type=float, default=0.5,
+                    help="keep warming up until this many seconds of steps have run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
@@ -243,9 +249,21 @@ def main():
 
     step, info = setup_workload(args.workload, dev)
     stream = torch.cuda.current_stream()
+    # W warm-up steps, continued until the GPU has run the step for at least
+    # --min-warmup-s seconds: its clocks take a few hundred ms of load to reach
+    # their steady level, and a cold start reads up to 25 % slow
+    t_w = time.perf_counter()
+    n_warm = 0
     for _ in range(args.warmup):
         step()
+        n_warm += 1
     torch.cuda.synchronize()
+    while time.perf_counter() - t_w < args.min_warmup_s:
+        for _ in range(10):
+            step()
+            n_warm += 1
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -277,7 +295,8 @@ def main():
     cfg = {k: info[k] for k in info if k not in ("inputs", "bytes_alg", "flop_alg", "kernel", "tokens")}
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
+        "warmup_s": round(warm_s, 3), "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": info["dtype"], "data": "synthetic (seeded Gaussian inputs of the workload's shapes)",
         "config": cfg,

@@ -91,7 +91,8 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     __shared__ __attribute__((aligned(16))) bf16_t sO[CS * DVT];  // finished output tile
     __shared__ float sTab[3 * (CS + 1)];                           // w_p | beta^p | a_p
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is made uniform (scalar), so branches on it are scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int nt = wave % NNT, hf = wave / NNT;
 
@@ -253,21 +254,23 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     };
 
     // P^T tile assignment (query tile ti; key tiles tjA, tjB; -1 = none), grouped by
-    // query tile so a wave reuses its Q fragments
+    // query tile so a wave reuses its Q fragments.  The waves of d_k half 1
+    // take the pairs: half 0 also sums the previous output tile before the
+    // first barrier, so it gets at most one tile.
     int p_ti = -1, p_tjA = -1, p_tjB = -1;
     if (CS == 64) {
         switch (wave) {
-            case 0: p_ti = 3; p_tjA = 1; p_tjB = 2; break;
-            case 1: p_ti = 3; p_tjA = 0; p_tjB = 3; break;
-            case 2: p_ti = 2; p_tjA = 0; p_tjB = 1; break;
-            case 3: p_ti = 2; p_tjA = 2; break;
-            case 4: p_ti = 1; p_tjA = 0; p_tjB = 1; break;
-            case 5: p_ti = 0; p_tjA = 0; break;
+            case 4: p_ti = 3; p_tjA = 1; p_tjB = 2; break;
+            case 5: p_ti = 3; p_tjA = 0; p_tjB = 3; break;
+            case 6: p_ti = 2; p_tjA = 0; p_tjB = 1; break;
+            case 7: p_ti = 1; p_tjA = 0; p_tjB = 1; break;
+            case 0: p_ti = 2; p_tjA = 2; break;
+            case 1: p_ti = 0; p_tjA = 0; break;
             default: break;
         }
     } else {
-        if (wave == 0) { p_ti = 1; p_tjA = 0; p_tjB = 1; }
-        else if (wave == 1) { p_ti = 0; p_tjA = 0; }
+        if (wave == 2) { p_ti = 1; p_tjA = 0; p_tjB = 1; }
+        else if (wave == 3) { p_ti = 0; p_tjA = 0; }
     }
 
     f32x4 oacc[NTI];  // this wave's readout partial of the previous chunk (half 0 keeps it)
@@ -576,13 +579,21 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
 
         // ------------- intra scores P^T = K Q^T (lower-triangular 16x16 tiles)
         if (HAS_P && p_ti >= 0) {
+            // all fragments are read before the first product (a wave with one
+            // key tile computes its tile twice rather than branch in between)
+            const int tjB = p_tjB >= 0 ? p_tjB : p_tjA;
+            bf16x8 fq[NKB], fa[NKB], fb[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                fq[kb] = *reinterpret_cast<const bf16x8*>(Q + kb * BLK + p_ti * 512 + b_contig);
+                fa[kb] = *reinterpret_cast<const bf16x8*>(K + kb * BLK + p_tjA * 512 + b_contig);
+                fb[kb] = *reinterpret_cast<const bf16x8*>(K + kb * BLK + tjB * 512 + b_contig);
+            }
             f32x4 pa = zero4(), pb = zero4();
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8 bq = *reinterpret_cast<const bf16x8*>(Q + kb * BLK + p_ti * 512 + b_contig);
-                mma(pa, *reinterpret_cast<const bf16x8*>(K + kb * BLK + p_tjA * 512 + b_contig), bq);
-                if (p_tjB >= 0)
-                    mma(pb, *reinterpret_cast<const bf16x8*>(K + kb * BLK + p_tjB * 512 + b_contig), bq);
+                mma(pa, fa[kb], fq[kb]);
+                mma(pb, fb[kb], fq[kb]);
             }
             const int i = 16 * p_ti + c16;
 #pragma unroll
@@ -631,13 +642,16 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 }
             }
             if (HAS_P) {
-                // half 0 takes key block 0 of every query tile, half 1 key block 1 (ti >= 2)
+                // half 0 takes key block 0 of every query tile, half 1 key block 1
+                // (query tiles 2, 3 only); score fragments are read first
+                const int pc = (NJB > 1 && hf) ? 32 : 0;
+                bf16x8 pf[NTI];
 #pragma unroll
-                for (int ti = 0; ti < NTI; ++ti) {
-                    const bf16_t* prow = &sP[(16 * ti + c16) * LP];
-                    if (hf == 0) mma(acc[ti], VB[0], ld_accperm(prow, 0, g));
-                    else if (NJB > 1 && ti >= 2) mma(acc[ti], VB[NJB - 1], ld_accperm(prow, 32, g));
-                }
+                for (int ti = 0; ti < NTI; ++ti) pf[ti] = ld_accperm(&sP[(16 * ti + c16) * LP], pc, g);
+                const bf16x8 vb = (NJB > 1 && hf) ? VB[NJB - 1] : VB[0];
+#pragma unroll
+                for (int ti = 0; ti < NTI; ++ti)
+                    if (hf == 0 || (NJB > 1 && ti >= 2)) mma(acc[ti], vb, pf[ti]);
             }
 #pragma unroll
             for (int ti = 0; ti < NTI; ++ti) {
