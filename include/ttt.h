@@ -34,7 +34,8 @@
  *    through element strides for the B, H and L dimensions; the last
  *    dimension must be contiguous.
  *  - Base pointers must be 16-byte aligned; the L strides of q, k, v and out
- *    must be multiples of 8 elements (16 bytes of bf16); S0/M0/W0/S_final
+ *    must be multiples of 8 elements (16 bytes of bf16) and below 2^24
+ *    elements (eta's L stride too); S0/M0/W0/S_final
  *    etc. are contiguous [dk, dv] fp32 blocks per (b, h).
  *  - `out` must not overlap any input.  q and k may be the same tensor.
  *  - Errors never abort and never throw across the ABI; launch failures are

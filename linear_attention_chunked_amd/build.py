@@ -59,6 +59,13 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    # a kernel template whose host-side instantiation failed leaves its launch
+    # stub undefined, which the shared-library link accepts: refuse that here
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError("kernel launch stubs missing from the library: " + ", ".join(missing[:4]))
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -38,6 +38,7 @@ ttt_status_t check_tensor(const void* p, const int64_t* st, int d, int dtype) {
         if (st[i] % vec != 0) return TTT_ERR_ALIGN;
     }
     if (st[2] < d) return TTT_ERR_SHAPE;  // rows must not overlap
+    if (st[2] >= (int64_t(1) << 24)) return TTT_ERR_SHAPE;  // in-chunk row offsets use 24-bit products
     return TTT_OK;
 }
 
@@ -80,6 +81,7 @@ ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
     if (a->eta) {
         for (int i = 0; i < 3; ++i)
             if (a->eta_stride[i] < 0) return TTT_ERR_SHAPE;
+        if (a->eta_stride[2] >= (int64_t(1) << 24)) return TTT_ERR_SHAPE;
     }
     if (a->S0 && (a->S0_stride[0] < 0 || a->S0_stride[1] < 0)) return TTT_ERR_SHAPE;
     if (a->M0 && (a->M0_stride[0] < 0 || a->M0_stride[1] < 0)) return TTT_ERR_SHAPE;

@@ -203,34 +203,39 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         const int row = tid / (DVT / 8), ch = tid % (DVT / 8);
         loff_v = (ch >> 2) * BLKV + row * 32 + 8 * ((ch & 3) ^ swz(row));
     }
-    const int kq_same = (qL == kL);
     // Every lane issues the same loads for every chunk: rows past L read row
     // L-1 again (their eta is zero, so they add nothing; their outputs are
     // never stored) and a chunk index past the end refetches the last chunk.
     // With no load under a branch, the memory counter advances uniformly and
     // the compiler's waits before the LDS writes drain only the oldest set.
+    // The chunk base is a scalar 64-bit pointer; a lane's offset within the
+    // chunk is a 24-bit product (L strides are below 2^24 elements).
+    int row_q[UQ], pc_q[UQ];
+#pragma unroll
+    for (int x = 0; x < UQ; ++x) {
+        row_q[x] = (tid + x * NT) / (DK / 8);
+        pc_q[x] = 8 * ((tid + x * NT) % (DK / 8));
+    }
+    const int row_v = (tid % NVC) / (DVT / 8), pc_v = 8 * ((tid % NVC) % (DVT / 8));
+    const unsigned qL24 = (unsigned)qL, kL24 = (unsigned)kL, vL24 = (unsigned)vL, eL24 = (unsigned)eL;
     auto load = [&](int c, auto SET, auto WITHQ) {
         constexpr int st = decltype(SET)::value;
         constexpr bool wq = decltype(WITHQ)::value;
         const int t0 = min(c, ntiles - 1) * CS;
-        const bool full = (t0 + CS <= L);
+        const int lim = min(CS, L - t0) - 1;      // last row of this chunk
+        const bf16_t* Qc = Qg + (int64_t)t0 * qL;
+        const bf16_t* Kc = Kg + (int64_t)t0 * kL;
+        const bf16_t* Vc = Vg + (int64_t)t0 * vL;
 #pragma unroll
         for (int x = 0; x < UQ; ++x) {
-            const int row = (tid + x * NT) / (DK / 8);
-            const int rr = full ? row : min(row, L - 1 - t0);
-            const int64_t qo = (int64_t)(t0 + rr) * qL + 8 * ((tid + x * NT) % (DK / 8));
-            const int64_t ko = kq_same ? qo : (int64_t)(t0 + rr) * kL + 8 * ((tid + x * NT) % (DK / 8));
-            if (wq) rq[st][x] = *reinterpret_cast<const u32x4*>(Qg + qo);
-            rk[st][x] = *reinterpret_cast<const u32x4*>(Kg + ko);
+            const unsigned rr = (unsigned)min(row_q[x], lim);
+            if (wq) rq[st][x] = *reinterpret_cast<const u32x4*>(Qc + (__umul24(rr, qL24) + (unsigned)pc_q[x]));
+            rk[st][x] = *reinterpret_cast<const u32x4*>(Kc + (__umul24(rr, kL24) + (unsigned)pc_q[x]));
         }
-        {
-            const int u = tid % NVC, row = u / (DVT / 8), ch = u % (DVT / 8);
-            const int rr = full ? row : min(row, L - 1 - t0);
-            rv[st] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)(t0 + rr) * vL + 8 * ch);
-        }
+        rv[st] = *reinterpret_cast<const u32x4*>(Vc + (__umul24((unsigned)min(row_v, lim), vL24) + (unsigned)pc_v));
         // (tokens past L get eta 0 when the chunk is written to LDS: a select
         // here would make the compiler wait for this load right away)
-        re[st] = Eg ? Eg[min(t0 + (tid % CS), L - 1) * eL] : p.eta_scalar;
+        re[st] = Eg ? (Eg + (int64_t)t0 * eL)[__umul24((unsigned)min(tid % CS, lim), eL24)] : p.eta_scalar;
     };
     auto store = [&](int c, int buf, auto SET, auto WITHQ) {
         constexpr int st = decltype(SET)::value;
@@ -291,7 +296,8 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         const int row = tid / (DVT / 8), ch = tid % (DVT / 8);
         if (tid < NVC && row < prev_n) {
             const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[row * DVT + 8 * (ch ^ oswz<DVT>(row))]);
-            *reinterpret_cast<u32x4*>(&Og[(int64_t)(prev_base + row) * oL + 8 * ch]) = w;
+            bf16_t* Oc = Og + (int64_t)prev_base * oL;
+            *reinterpret_cast<u32x4*>(Oc + (__umul24((unsigned)row, (unsigned)oL) + 8u * ch)) = w;
         }
     };
 

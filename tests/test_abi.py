@@ -90,6 +90,7 @@ def test_fwd_rejects_before_launch(lib):
     assert status(lib, fwd_args(q=FAKE + 2)) == ERR_ALIGN
     assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 68))) == ERR_ALIGN
     assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 56))) == ERR_SHAPE
+    assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 1 << 24))) == ERR_SHAPE  # L stride bound
     assert status(lib, fwd_args(dk=48)) == ERR_UNSUP
     assert status(lib, fwd_args(dv=256)) == ERR_UNSUP
     assert status(lib, fwd_args(mode=1, chunk=100)) == ERR_UNSUP
