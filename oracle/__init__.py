@@ -67,6 +67,9 @@ def _load():
         lib.ttt_oracle_state_scan.argtypes = [i, i, i, i, i, i, _dp, _dp, d, _dp, _dp,
                                               _dp, _dp, _dp, _dp]
         lib.ttt_oracle_state_scan.restype = None
+        lib.ttt_oracle_token_causal_bwd.argtypes = [i, i, i, i, i, _dp, _dp, _dp, _dp, d, d, _dp, _dp,
+                                                    _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
+        lib.ttt_oracle_token_causal_bwd.restype = None
         lib.ttt_oracle_threads.argtypes = []
         lib.ttt_oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -111,6 +114,31 @@ def token_causal(q, k, v, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None):
                                     float(eta_scalar), float(beta), _ptr(S0), _ptr(M0),
                                     _ptr(out), _ptr(Sf), _ptr(Mf))
     return out, Sf, Mf
+
+
+def token_causal_bwd(q, k, v, dout, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None,
+                     dS_final=None, dM_final=None):
+    """Backward pass of ``token_causal`` (C, fp64): the plain adjoint of the
+    per-token recurrence (the pages give the forward rule and train through
+    it, [P4] section "가중치가 두 종류라는 점"; the derivative is the chain rule).
+
+    Returns (dq, dk, dv, deta, dS0, dM0); deta is per token [B,H,L] even for a
+    scalar eta (whose gradient is its sum over tokens)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    eta, S0, M0, dSf, dMf = _f64(eta), _f64(S0), _f64(M0), _f64(dS_final), _f64(dM_final)
+    dq = np.empty((B, H, L, dk))
+    dkk = np.empty((B, H, L, dk))
+    dvv = np.empty((B, H, L, dv))
+    deta = np.empty((B, H, L))
+    dS0 = np.empty((B, H, dk, dv))
+    dM0 = np.empty((B, H, dk, dv))
+    _load().ttt_oracle_token_causal_bwd(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                        float(eta_scalar), float(beta), _ptr(S0), _ptr(M0), _ptr(dout),
+                                        _ptr(dSf), _ptr(dMf), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(deta),
+                                        _ptr(dS0), _ptr(dM0))
+    return dq, dkk, dvv, deta, dS0, dM0
 
 
 def dual_primal(q, k, v, W0, eta, minibatch):

@@ -206,6 +206,121 @@ void ttt_oracle_state_scan(int B, int H, int L, int chunk, int dk, int dv,
     }
 }
 
+/*
+ * Backward pass of the token-causal recurrence above: the exact adjoint of
+ * ttt_oracle_token_causal, written out from the chain rule.  The pages give
+ * the forward rule and state that the fast weights are trained through it
+ * ([P4], section on the two kinds of weights: the outer loop learns through
+ * the inner updates); the backward pass itself is not printed anywhere, so
+ * this is the plain derivative of the recurrence, nothing more.
+ *
+ * Given dout (dL/do_t) and optional dS_final, dM_final (gradients of the
+ * final states), two sweeps per (b, h):
+ *   forward sweep (same recurrence as the forward pass):
+ *       dq_t = do_t S_t^T                         (o_t = q_t S_t)
+ *   reverse sweep, t = L-1 .. 0, adjoints Sa (of S_t) and ma (of m_t):
+ *       Sa  += q_t^T do_t                         (o_t reads S_t)
+ *       ma  += Sa                                 (S_t = S_{t-1} + m_t)
+ *       dv_t   = eta_t k_t ma,  dk_t = eta_t ma v_t^T,
+ *       deta_t = k_t ma v_t^T                      (m_t = beta m_{t-1} + g_t)
+ *       ma   = beta ma                            (adjoint of m_{t-1})
+ *   with Sa = dS_final, ma = dM_final at the start (zero if NULL), and
+ *   dS0 = Sa, dM0 = ma at the end.
+ * deta is per token even when the forward used a scalar eta (its gradient
+ * is then the sum over tokens).  Any output pointer may be NULL.
+ */
+void ttt_oracle_token_causal_bwd(int B, int H, int L, int dk, int dv,
+                                 const double* q, const double* k, const double* v,
+                                 const double* eta, double eta_scalar, double beta,
+                                 const double* S0, const double* M0,
+                                 const double* dout, const double* dS_final, const double* dM_final,
+                                 double* dq, double* dkk, double* dvv, double* deta,
+                                 double* dS0, double* dM0)
+{
+    const long nbh = (long)B * H;
+    const long sz = (long)dk * dv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        double* S = (double*)malloc(sizeof(double) * sz);
+        double* m = (double*)malloc(sizeof(double) * sz);
+        double* Sa = (double*)malloc(sizeof(double) * sz);
+        double* ma = (double*)malloc(sizeof(double) * sz);
+        double* kr = (double*)malloc(sizeof(double) * dv);
+        /* forward sweep: S_t, then dq_t = do_t S_t^T */
+        for (long e = 0; e < sz; ++e) {
+            S[e] = S0 ? S0[bh * sz + e] : 0.0;
+            m[e] = M0 ? M0[bh * sz + e] : 0.0;
+        }
+        for (int t = 0; t < L; ++t) {
+            const double* kt = k + (bh * L + t) * dk;
+            const double* vt = v + (bh * L + t) * dv;
+            const double* dot = dout + (bh * L + t) * dv;
+            const double et = eta ? eta[bh * L + t] : eta_scalar;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) {
+                    m[(long)i * dv + j] = beta * m[(long)i * dv + j] + et * kt[i] * vt[j];
+                    S[(long)i * dv + j] += m[(long)i * dv + j];
+                }
+            if (dq) {
+                double* dqt = dq + (bh * L + t) * dk;
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) acc += dot[j] * S[(long)i * dv + j];
+                    dqt[i] = acc;
+                }
+            }
+        }
+        /* reverse sweep */
+        for (long e = 0; e < sz; ++e) {
+            Sa[e] = dS_final ? dS_final[bh * sz + e] : 0.0;
+            ma[e] = dM_final ? dM_final[bh * sz + e] : 0.0;
+        }
+        for (int t = L - 1; t >= 0; --t) {
+            const double* qt = q + (bh * L + t) * dk;
+            const double* kt = k + (bh * L + t) * dk;
+            const double* vt = v + (bh * L + t) * dv;
+            const double* dot = dout + (bh * L + t) * dv;
+            const double et = eta ? eta[bh * L + t] : eta_scalar;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) {
+                    Sa[(long)i * dv + j] += qt[i] * dot[j];
+                    ma[(long)i * dv + j] += Sa[(long)i * dv + j];
+                }
+            /* kr = k_t ma (a row of length dv) */
+            for (int j = 0; j < dv; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < dk; ++i) acc += kt[i] * ma[(long)i * dv + j];
+                kr[j] = acc;
+            }
+            if (dvv) {
+                double* dvt = dvv + (bh * L + t) * dv;
+                for (int j = 0; j < dv; ++j) dvt[j] = et * kr[j];
+            }
+            if (deta) {
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) acc += kr[j] * vt[j];
+                deta[bh * L + t] = acc;
+            }
+            if (dkk) {
+                double* dkt = dkk + (bh * L + t) * dk;
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) acc += ma[(long)i * dv + j] * vt[j];
+                    dkt[i] = et * acc;
+                }
+            }
+            for (long e = 0; e < sz; ++e) ma[e] *= beta;
+        }
+        if (dS0) memcpy(dS0 + bh * sz, Sa, sizeof(double) * sz);
+        if (dM0) memcpy(dM0 + bh * sz, ma, sizeof(double) * sz);
+        free(S);
+        free(m);
+        free(Sa);
+        free(ma);
+        free(kr);
+    }
+}
+
 /* Number of host threads the OpenMP loops above use (for reporting). */
 #ifdef _OPENMP
 #include <omp.h>

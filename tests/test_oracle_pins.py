@@ -484,3 +484,101 @@ def test_dual_is_la_with_corrected_values(oracle_mod):
         close(Wn[0, 0], (np.eye(d) - eta * K.T @ K) @ W[0, 0] + eta * K.T @ V, 1e-12)
         W = Wn
     close(W, Wf, 1e-12)
+
+
+# ----------------------------------------------------------------- backward
+def _bwd_case(beta, rng, B=1, H=2, L=6, dk=3, dv=4):
+    q, k, v, eta, S0, M0 = small_case(B, H, L, dk, dv, beta=beta, rng=rng, m0=beta != 0.0)
+    dout = rnd(B, H, L, dv, rng=rng)
+    dSf = rnd(B, H, dk, dv, rng=rng)
+    dMf = rnd(B, H, dk, dv, rng=rng) if beta != 0.0 else None
+    return q, k, v, eta, S0, M0, dout, dSf, dMf
+
+
+def _objective(oracle_mod, beta, dout, dSf, dMf, q, k, v, eta, S0, M0):
+    """<out, dout> + <S_final, dSf> + <M_final, dMf>: its gradient is what the
+    backward pass returns for these cotangents."""
+    out, Sf, Mf = oracle_mod.token_causal(q, k, v, eta, 0.0, beta, S0, M0)
+    f = float(np.sum(out * dout) + np.sum(Sf * dSf))
+    if dMf is not None:
+        f += float(np.sum(Mf * dMf))
+    return f
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.7])
+def test_bwd_finite_differences(oracle_mod, beta):
+    """Directional derivatives of the forward oracle by central differences
+    match the backward oracle for every input (q, k, v, eta, S0, M0).  The
+    objective is a cubic polynomial in each input, so the only error is
+    rounding."""
+    rng = np.random.default_rng(41)
+    q, k, v, eta, S0, M0, dout, dSf, dMf = _bwd_case(beta, rng)
+    dq, dk_, dv_, deta, dS0, dM0 = oracle_mod.token_causal_bwd(q, k, v, dout, eta, 0.0, beta, S0, M0, dSf, dMf)
+    inputs = {"q": q, "k": k, "v": v, "eta": eta, "S0": S0}
+    grads = {"q": dq, "k": dk_, "v": dv_, "eta": deta, "S0": dS0}
+    if beta != 0.0:
+        inputs["M0"], grads["M0"] = M0, dM0
+    h = 1e-5
+    for name, x in inputs.items():
+        for _ in range(3):
+            u = rng.standard_normal(x.shape)
+            args = dict(inputs)
+            args[name] = x + h * u
+            fp = _objective(oracle_mod, beta, dout, dSf, dMf, args["q"], args["k"], args["v"], args["eta"],
+                            args["S0"], args.get("M0"))
+            args[name] = x - h * u
+            fm = _objective(oracle_mod, beta, dout, dSf, dMf, args["q"], args["k"], args["v"], args["eta"],
+                            args["S0"], args.get("M0"))
+            fd = (fp - fm) / (2 * h)
+            an = float(np.sum(grads[name] * u))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (name, fd, an)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_bwd_matches_autograd(oracle_mod, beta):
+    """PyTorch autograd through a plain fp64 loop of the recurrence (written
+    here, not the oracle's code) gives the same gradients."""
+    rng = np.random.default_rng(43)
+    q, k, v, eta, S0, M0, dout, dSf, dMf = _bwd_case(beta, rng, B=2, H=2, L=9, dk=4, dv=3)
+    T = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+         for n, a in dict(q=q, k=k, v=v, eta=eta, S0=S0).items()}
+    if beta != 0.0:
+        T["M0"] = torch.tensor(M0, dtype=torch.float64, requires_grad=True)
+    S = T["S0"]
+    m = T["M0"] if beta != 0.0 else torch.zeros_like(S)
+    outs = []
+    for t in range(q.shape[2]):
+        g = T["eta"][:, :, t, None, None] * T["k"][:, :, t, :, None] * T["v"][:, :, t, None, :]
+        m = beta * m + g
+        S = S + m
+        outs.append(torch.einsum("bhi,bhij->bhj", T["q"][:, :, t], S))
+    out = torch.stack(outs, dim=2)
+    f = (out * torch.tensor(dout)).sum() + (S * torch.tensor(dSf)).sum()
+    if beta != 0.0:
+        f = f + (m * torch.tensor(dMf)).sum()
+    f.backward()
+    dq, dk_, dv_, deta, dS0, dM0 = oracle_mod.token_causal_bwd(q, k, v, dout, eta, 0.0, beta, S0, M0, dSf, dMf)
+    for name, a in (("q", dq), ("k", dk_), ("v", dv_), ("eta", deta), ("S0", dS0)):
+        close(a, T[name].grad.numpy(), 1e-11)
+    if beta != 0.0:
+        close(dM0, T["M0"].grad.numpy(), 1e-11)
+
+
+def test_bwd_single_token_closed_form(oracle_mod):
+    """L = 1, no momentum: o = q (S0 + eta k^T v).  With D = q^T do + dS_final:
+    dq = do (S0 + eta k^T v)^T, dv = eta k D, dk = eta D v^T, deta = k D v^T,
+    dS0 = D -- written out with matrix products."""
+    rng = np.random.default_rng(44)
+    dk, dv = 5, 3
+    q, k, v = rnd(1, 1, 1, dk, rng=rng), rnd(1, 1, 1, dk, rng=rng), rnd(1, 1, 1, dv, rng=rng)
+    S0, dSf, dout = rnd(1, 1, dk, dv, rng=rng), rnd(1, 1, dk, dv, rng=rng), rnd(1, 1, 1, dv, rng=rng)
+    eta = 0.3
+    dq, dk_, dv_, deta, dS0, _ = oracle_mod.token_causal_bwd(q, k, v, dout, None, eta, 0.0, S0, None, dSf)
+    qv, kv, vv, dov = q[0, 0, 0], k[0, 0, 0], v[0, 0, 0], dout[0, 0, 0]
+    S1 = S0[0, 0] + eta * np.outer(kv, vv)
+    D = np.outer(qv, dov) + dSf[0, 0]
+    close(dq[0, 0, 0], S1 @ dov)
+    close(dv_[0, 0, 0], eta * (kv @ D))
+    close(dk_[0, 0, 0], eta * (D @ vv))
+    close(deta[0, 0, 0], kv @ D @ vv)
+    close(dS0[0, 0], D)
