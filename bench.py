@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "dual_fwd_kernel": ("dual.hip", "common.h"),
     "dual_chain_kernel": ("dual.hip", "common.h"),
     "decode_kernel": ("decode.hip", "common.h"),
+    "tcb_fwd_kernel+bwd_epilogue_kernel": ("tcb_fwd.hip", "bwd.hip", "common.h"),
 }
 
 
@@ -132,6 +133,28 @@ def setup_workload(name: str, dev: str):
         flop_alg = B * H * L * (6 * d * d + (mb + 1) * 2 * d)
         info = dict(workload=name, B=B, H=H, L=L, d=d, minibatch=mb, dtype="bf16", tokens=B * L,
                     bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="dual_chain_kernel", inputs=inp)
+        return step, info
+    if name == "bwd":
+        inp = W.gen_lm_scale()
+        dout, dSf = W.gen_lm_scale_cotangents()
+        B, H, L, dk = inp.q.shape
+        dv = inp.v.shape[-1]
+        q, k, v, eta, S0 = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.eta.to(dev), inp.S0.to(dev)
+        do, dS = dout.to(dev), dSf.to(dev)
+
+        def step():
+            return lac.bwd_chunked(q, k, v, do, eta=eta, S0=S0, dS_final=dS)
+
+        es = 2
+        bytes_alg = (B * H * L * (2 * dk + 2 * dv) * es      # q, k, v, dout
+                     + B * H * L * (2 * dk + dv) * es        # dq, dk, dv
+                     + B * H * L * 4 * 2                     # eta, deta
+                     + 3 * B * H * dk * dv * 4)              # S0, dS_final, dS0
+        C = inp.chunk
+        flop_alg = 3 * B * H * L * (4 * dk * dv + (C + 1) * (dk + dv))
+        info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, mode="token_causal backward",
+                    eta="per-token", dtype="bf16", tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
+                    kernel="tcb_fwd_kernel+bwd_epilogue_kernel", inputs=None)
         return step, info
     if name in ("decode", "decode-momentum"):
         inp = W.gen_decode(beta=0.9 if name == "decode-momentum" else 0.0)
@@ -220,7 +243,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lm-scale",
                     help="lm-scale (default), small-f32, inplace-32k, inplace-128k, momentum, dual-b16, "
-                         "dual-b2048, decode, decode-momentum")
+                         "dual-b2048, decode, decode-momentum, bwd")
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this many seconds of steps have run")
     ap.add_argument("--no-cpu-baseline", action="store_true")

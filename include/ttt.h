@@ -13,6 +13,7 @@
  *                         (MSE reconstruction loss), dual form
  *   ttt_decode_step       one recurrent token per sequence (inference):
  *                         state update and readout with the state in HBM
+ *   ttt_bwd_chunked       backward pass of the token-causal forward (beta 0)
  *
  * Sources (cited by page title and paragraph or section):
  *  [P1] "KV 바인딩 기반 테스트 시간 학습은 사실상 선형 어텐션이다"
@@ -34,7 +35,7 @@
  *    through element strides for the B, H and L dimensions; the last
  *    dimension must be contiguous.
  *  - Base pointers must be 16-byte aligned; the L strides of q, k, v and out
- *    must be multiples of 8 elements (16 bytes of bf16) and below 2^24
+ *    must be multiples of 8 elements (16 bytes of bf16) and below 2^23
  *    elements (eta's L stride too); S0/M0/W0/S_final
  *    etc. are contiguous [dk, dv] fp32 blocks per (b, h).
  *  - `out` must not overlap any input.  q and k may be the same tensor.
@@ -231,6 +232,38 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
                              const void* q, const void* k, const void* v,
                              const float* eta, float eta_scalar, float beta,
                              float* S, float* M, void* out, void* stream);
+
+/*
+ * ttt_bwd_chunked -- backward pass of ttt_fwd_chunked in TOKEN_CAUSAL mode
+ * without momentum (beta = 0).
+ *
+ * [P1] paragraphs on the state-matrix update and on the one-step output
+ * identity give the forward S_t = S_{t-1} + eta_t k_t^T v_t, o_t = q_t S_t
+ * (from S0); [P4] section on the two kinds of weights trains the outer model
+ * through these updates, which needs their gradients.  Given dout = dL/do
+ * and dS_final = dL/dS_final (NULL: zero), with D_t = dS_final +
+ * sum_{u >= t} q_u^T do_u:
+ *     dq_t = do_t S_t^T,  dk_t = eta_t D_t v_t^T,  dv_t = eta_t k_t D_t,
+ *     deta_t = k_t D_t v_t^T (per token, also for a scalar eta: its gradient
+ *     is the sum over tokens),  dS0 = D_0.
+ *
+ * All tensors are contiguous: q, k, dq, dk [B,H,L,dk]; v, dout, dv
+ * [B,H,L,dv] in `dtype`; eta [B,H,L] fp32 or NULL (eta_scalar); S0,
+ * dS_final, dS0 [B,H,dk,dv] fp32 or NULL (S0, dS_final: zero).  deta and
+ * dS0 may be NULL (not computed).  Supported: dk, dv in {32, 64, 128}.
+ * Outputs must not overlap any input or each other.  workspace: device
+ * memory of ttt_bwd_workspace_size bytes (0 possible), caller-owned.
+ * Errors (before anything is enqueued): TTT_ERR_NULL, TTT_ERR_DTYPE,
+ * TTT_ERR_SHAPE, TTT_ERR_ALIGN (16 bytes), TTT_ERR_UNSUPPORTED,
+ * TTT_ERR_WORKSPACE, TTT_ERR_ALIAS; TTT_ERR_HIP if a launch fails.
+ */
+ttt_status_t ttt_bwd_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
+                                    size_t* bytes);
+ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
+                             const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                             const float* S0, const void* dout, const float* dS_final,
+                             void* dq, void* dk_out, void* dv_out, float* deta, float* dS0,
+                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* ttt_status_string(ttt_status_t status);

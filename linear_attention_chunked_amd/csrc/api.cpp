@@ -38,7 +38,7 @@ ttt_status_t check_tensor(const void* p, const int64_t* st, int d, int dtype) {
         if (st[i] % vec != 0) return TTT_ERR_ALIGN;
     }
     if (st[2] < d) return TTT_ERR_SHAPE;  // rows must not overlap
-    if (st[2] >= (int64_t(1) << 24)) return TTT_ERR_SHAPE;  // in-chunk row offsets use 24-bit products
+    if (st[2] >= (int64_t(1) << 23)) return TTT_ERR_SHAPE;  // in-chunk row offsets use 24-bit products
     return TTT_OK;
 }
 
@@ -81,7 +81,7 @@ ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
     if (a->eta) {
         for (int i = 0; i < 3; ++i)
             if (a->eta_stride[i] < 0) return TTT_ERR_SHAPE;
-        if (a->eta_stride[2] >= (int64_t(1) << 24)) return TTT_ERR_SHAPE;
+        if (a->eta_stride[2] >= (int64_t(1) << 23)) return TTT_ERR_SHAPE;
     }
     if (a->S0 && (a->S0_stride[0] < 0 || a->S0_stride[1] < 0)) return TTT_ERR_SHAPE;
     if (a->M0 && (a->M0_stride[0] < 0 || a->M0_stride[1] < 0)) return TTT_ERR_SHAPE;
@@ -235,6 +235,76 @@ ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32
     p.dv = dv;
     p.minibatch = minibatch;
     return from_hip(ttt::launch_dual_fwd(p, dtype, reinterpret_cast<hipStream_t>(stream)));
+}
+
+ttt_status_t ttt_bwd_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
+                                    size_t* bytes) {
+    if (!bytes) return TTT_ERR_NULL;
+    if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
+    if (B < 1 || H < 1 || L < 1 || dk < 1 || dv < 1) return TTT_ERR_SHAPE;
+    if (!ttt::bwd_supported(dtype, dk, dv)) return TTT_ERR_UNSUPPORTED;
+    *bytes = ttt::bwd_workspace(B, H, L, dk, dv, dtype);
+    return TTT_OK;
+}
+
+ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
+                             const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                             const float* S0, const void* dout, const float* dS_final, void* dq, void* dk_out,
+                             void* dv_out, float* deta, float* dS0, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    size_t need = 0;
+    const ttt_status_t st = ttt_bwd_workspace_size(B, H, L, dk, dv, dtype, &need);
+    if (st != TTT_OK) return st;
+    if (!q || !k || !v || !dout || !dq || !dk_out || !dv_out) return TTT_ERR_NULL;
+    if (need > 0 && (!workspace || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
+    const size_t es = esize(dtype);
+    const size_t nq = (size_t)B * H * L * dk * es, nv = (size_t)B * H * L * dv * es;
+    const size_t ne = (size_t)B * H * L * 4, ns = (size_t)B * H * dk * dv * 4;
+    struct Buf { const void* p; size_t n; };
+    const Buf ins[] = {{q, nq}, {k, nq}, {v, nv}, {dout, nv}, {eta, ne}, {S0, ns}, {dS_final, ns}};
+    const Buf outs[] = {{dq, nq}, {dk_out, nq}, {dv_out, nv}, {deta, ne}, {dS0, ns}, {workspace, need}};
+    for (const Buf& b : ins)
+        if (b.p && !aligned16(b.p)) return TTT_ERR_ALIGN;
+    for (const Buf& b : outs)
+        if (b.p && !aligned16(b.p)) return TTT_ERR_ALIGN;
+    // outputs overlap neither the inputs nor each other
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+        if (!outs[i].p || outs[i].n == 0) continue;
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(outs[i].p), a1 = a0 + outs[i].n;
+        for (const Buf& b : ins) {
+            if (!b.p) continue;
+            const uintptr_t b0 = reinterpret_cast<uintptr_t>(b.p);
+            if (overlap(a0, a1, b0, b0 + b.n)) return TTT_ERR_ALIAS;
+        }
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j) {
+            if (!outs[j].p || outs[j].n == 0) continue;
+            const uintptr_t b0 = reinterpret_cast<uintptr_t>(outs[j].p);
+            if (overlap(a0, a1, b0, b0 + outs[j].n)) return TTT_ERR_ALIAS;
+        }
+    }
+    ttt::BwdParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.B = B;
+    p.H = H;
+    p.L = L;
+    p.dk_dim = dk;
+    p.dv_dim = dv;
+    p.dtype = dtype;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.eta = eta;
+    p.eta_scalar = eta_scalar;
+    p.S0 = S0;
+    p.dout = dout;
+    p.dS_final = dS_final;
+    p.dq = dq;
+    p.dk = dk_out;
+    p.dv = dv_out;
+    p.deta = deta;
+    p.dS0 = dS0;
+    p.workspace = workspace;
+    return from_hip(ttt::launch_bwd(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,

@@ -38,6 +38,9 @@ struct TcParams {
     float* lb_data;
     int64_t lb_stride;
     void* workspace;
+    // S0 (and M0) stored transposed: element (i, j) of a head's [dk, dv]
+    // state at j * dk + i (the backward pass reads a state this way)
+    int s0_trans;
 };
 
 // dtype: 0 fp32, 1 bf16.  mode: MODE_*.  Returns hipSuccess or the launch error;
@@ -93,6 +96,30 @@ struct DecodeParams {
     int B, H, dk, dv;
 };
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream);
+
+// Backward of the token-causal forward (beta = 0), contiguous [B,H,L,d]
+// tensors.  dk and dv (the gradient buffers) receive intermediate results
+// before the final scaling, so they must not alias any input.
+struct BwdParams {
+    int B, H, L, dk_dim, dv_dim, dtype;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* eta;
+    float eta_scalar;
+    const float* S0;
+    const void* dout;
+    const float* dS_final;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* deta;
+    float* dS0;
+    void* workspace;
+};
+bool bwd_supported(int dtype, int dk, int dv);
+size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype);
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 bool decode_supported(int dtype, int dk, int dv);
 
 }  // namespace ttt

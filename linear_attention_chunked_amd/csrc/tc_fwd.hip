@@ -157,8 +157,9 @@ __global__ __launch_bounds__(DVT / 16 * 64) void tc_fwd_kernel(TcParams p) {
         for (int t = 0; t < NTD; ++t) {
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * t + 4 * g + r;
-                Sacc[t][r] = S0 ? S0[(int64_t)row * p.dv + col] : 0.f;
-                if (MOM) Macc[t][r] = M0 ? M0[(int64_t)row * p.dv + col] : 0.f;
+                const int64_t e = p.s0_trans ? (int64_t)col * p.dk + row : (int64_t)row * p.dv + col;
+                Sacc[t][r] = S0 ? S0[e] : 0.f;
+                if (MOM) Macc[t][r] = M0 ? M0[e] : 0.f;
             }
         }
     }

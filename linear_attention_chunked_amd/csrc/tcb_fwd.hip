@@ -175,8 +175,9 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = DKH * hf + 16 * t + 4 * g + r;
-                S[t][r] = S0 ? S0[(int64_t)row * p.dv + col] : 0.f;
-                if (MOM) M[t][r] = M0 ? M0[(int64_t)row * p.dv + col] : 0.f;
+                const int64_t e = p.s0_trans ? (int64_t)col * p.dk + row : (int64_t)row * p.dv + col;
+                S[t][r] = S0 ? S0[e] : 0.f;
+                if (MOM) M[t][r] = M0 ? M0[e] : 0.f;
             }
     };
     if (!segmented) load_initial(Sacc, Macc);
@@ -209,7 +210,8 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     // With no load under a branch, the memory counter advances uniformly and
     // the compiler's waits before the LDS writes drain only the oldest set.
     // The chunk base is a scalar 64-bit pointer; a lane's offset within the
-    // chunk is a 24-bit product (L strides are below 2^24 elements).
+    // chunk is a signed 24-bit product (|L stride| < 2^23 elements; a
+    // negative stride walks the sequence backwards).
     int row_q[UQ], pc_q[UQ];
 #pragma unroll
     for (int x = 0; x < UQ; ++x) {
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         pc_q[x] = 8 * ((tid + x * NT) % (DK / 8));
     }
     const int row_v = (tid % NVC) / (DVT / 8), pc_v = 8 * ((tid % NVC) % (DVT / 8));
-    const unsigned qL24 = (unsigned)qL, kL24 = (unsigned)kL, vL24 = (unsigned)vL, eL24 = (unsigned)eL;
+    const int qL24 = (int)qL, kL24 = (int)kL, vL24 = (int)vL, eL24 = (int)eL;
     auto load = [&](int c, auto SET, auto WITHQ) {
         constexpr int st = decltype(SET)::value;
         constexpr bool wq = decltype(WITHQ)::value;
@@ -228,14 +230,14 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         const bf16_t* Vc = Vg + (int64_t)t0 * vL;
 #pragma unroll
         for (int x = 0; x < UQ; ++x) {
-            const unsigned rr = (unsigned)min(row_q[x], lim);
-            if (wq) rq[st][x] = *reinterpret_cast<const u32x4*>(Qc + (__umul24(rr, qL24) + (unsigned)pc_q[x]));
-            rk[st][x] = *reinterpret_cast<const u32x4*>(Kc + (__umul24(rr, kL24) + (unsigned)pc_q[x]));
+            const int rr = min(row_q[x], lim);
+            if (wq) rq[st][x] = *reinterpret_cast<const u32x4*>(Qc + (__mul24(rr, qL24) + pc_q[x]));
+            rk[st][x] = *reinterpret_cast<const u32x4*>(Kc + (__mul24(rr, kL24) + pc_q[x]));
         }
-        rv[st] = *reinterpret_cast<const u32x4*>(Vc + (__umul24((unsigned)min(row_v, lim), vL24) + (unsigned)pc_v));
+        rv[st] = *reinterpret_cast<const u32x4*>(Vc + (__mul24(min(row_v, lim), vL24) + pc_v));
         // (tokens past L get eta 0 when the chunk is written to LDS: a select
         // here would make the compiler wait for this load right away)
-        re[st] = Eg ? (Eg + (int64_t)t0 * eL)[__umul24((unsigned)min(tid % CS, lim), eL24)] : p.eta_scalar;
+        re[st] = Eg ? (Eg + (int64_t)t0 * eL)[__mul24(min(tid % CS, lim), eL24)] : p.eta_scalar;
     };
     auto store = [&](int c, int buf, auto SET, auto WITHQ) {
         constexpr int st = decltype(SET)::value;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         if (tid < NVC && row < prev_n) {
             const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[row * DVT + 8 * (ch ^ oswz<DVT>(row))]);
             bf16_t* Oc = Og + (int64_t)prev_base * oL;
-            *reinterpret_cast<u32x4*>(Oc + (__umul24((unsigned)row, (unsigned)oL) + 8u * ch)) = w;
+            *reinterpret_cast<u32x4*>(Oc + (__mul24(row, (int)oL) + 8 * ch)) = w;
         }
     };
 

@@ -90,7 +90,7 @@ def test_fwd_rejects_before_launch(lib):
     assert status(lib, fwd_args(q=FAKE + 2)) == ERR_ALIGN
     assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 68))) == ERR_ALIGN
     assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 56))) == ERR_SHAPE
-    assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 1 << 24))) == ERR_SHAPE  # L stride bound
+    assert status(lib, fwd_args(q_stride=(2 * 128 * 64, 128 * 64, 1 << 23))) == ERR_SHAPE  # L stride bound
     assert status(lib, fwd_args(dk=48)) == ERR_UNSUP
     assert status(lib, fwd_args(dv=256)) == ERR_UNSUP
     assert status(lib, fwd_args(mode=1, chunk=100)) == ERR_UNSUP
@@ -160,6 +160,25 @@ def test_decode_rejects_before_launch(lib):
     assert f(*args(dk=2048)) == ERR_UNSUP
     assert f(*args(out=FAKE + 3 * n + 256)) == ERR_ALIAS  # out inside S
     assert f(*args(M=FAKE + 3 * n + 512)) == ERR_ALIAS    # M overlapping S
+
+
+def test_bwd_rejects_before_launch(lib):
+    f = lib.ttt_bwd_chunked
+    n = 2 * 2 * 64 * 64 * 2       # bytes of one [2,2,64,64] bf16 tensor
+
+    def args(**kw):
+        base = [FAKE + i * (n + 4096) for i in range(12)]
+        return [2, 2, 64, kw.get("dk", 64), 64, kw.get("dtype", 1),
+                kw.get("q", base[0]), base[1], base[2], None, 0.1, None, base[3], None,
+                kw.get("dq", base[4]), base[5], base[6], None, None, None, 0, None]
+    assert f(*args(dtype=4)) == ERR_DTYPE
+    assert f(*args(dk=48)) == ERR_UNSUP
+    assert f(*args(q=None)) == ERR_NULL
+    assert f(*args(q=FAKE + 8)) == ERR_ALIGN
+    assert f(*args(dq=FAKE + 256)) == ERR_ALIAS          # gradient buffer inside q
+    ws = ctypes.c_size_t(7)
+    assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, ctypes.byref(ws)) == OK
+    assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, None) == ERR_NULL
 
 
 def test_binding_refuses_cpu_tensors():

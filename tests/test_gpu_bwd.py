@@ -1,0 +1,140 @@
+"""GPU parity of the backward pass (``ttt_bwd_chunked``) against the fp64
+oracle's adjoint sweeps (``oracle.token_causal_bwd``), which are themselves
+pinned by finite differences and autograd on the CPU.
+
+Tolerances (relative L2 over each compared tensor): fp32 inputs <= 1e-5;
+bf16 inputs <= 1e-2 for dq, dk, dv, deta (the intermediate P, R are rounded
+to bf16 once before the eta scaling) and <= 1e-4 for dS0 (exact bf16
+products summed in fp32 over L tokens).  Integer-valued fp32 inputs with a
+dyadic eta are exact and must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import linear_attention_chunked_amd as lac
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+NAMES = ("dq", "dk", "dv", "deta", "dS0")
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def dev(t):
+    return None if t is None else t.to(DEV).contiguous()
+
+
+def make(B, H, L, dk, dv, dtype, seed, per_token=True, s0=True, dsf=True):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, L, dk, generator=g).to(dtype)
+    k = (torch.randn(B, H, L, dk, generator=g) / dk ** 0.5).to(dtype)
+    v = torch.randn(B, H, L, dv, generator=g).to(dtype)
+    dout = (torch.randn(B, H, L, dv, generator=g) / L ** 0.5).to(dtype)
+    eta = (0.1 * torch.rand(B, H, L, generator=g)).float() if per_token else None
+    S0 = 0.02 * torch.randn(B, H, dk, dv, generator=g) if s0 else None
+    dSf = 0.05 * torch.randn(B, H, dk, dv, generator=g) if dsf else None
+    return q, k, v, dout, eta, S0, dSf
+
+
+def run_gpu(q, k, v, dout, eta, eta_scalar, S0, dSf):
+    res = lac.bwd_chunked(dev(q), dev(k), dev(v), dev(dout), eta=dev(eta), eta_scalar=eta_scalar,
+                          S0=dev(S0), dS_final=dev(dSf))
+    torch.cuda.synchronize()
+    return [r.cpu() for r in res]
+
+
+def run_oracle(q, k, v, dout, eta, eta_scalar, S0, dSf):
+    dq, dk_, dv_, deta, dS0, _ = oracle.token_causal_bwd(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(dout),
+                                                          W.to_f64(eta), eta_scalar, 0.0, W.to_f64(S0), None,
+                                                          W.to_f64(dSf))
+    return dq, dk_, dv_, deta, dS0
+
+
+def check(got, ref, dtype, what):
+    tol = {"dq": 1e-5, "dk": 1e-5, "dv": 1e-5, "deta": 1e-5, "dS0": 1e-5} if dtype == "f32" else \
+          {"dq": 1e-2, "dk": 1e-2, "dv": 1e-2, "deta": 1e-2, "dS0": 1e-4}
+    errs = {n: oracle.rel_l2(g.double(), r) for n, g, r in zip(NAMES, got, ref)}
+    say(f"{what}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
+    for n, e in errs.items():
+        assert e <= tol[n], (n, e)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L,dk,dv", [(150, 64, 64), (300, 128, 64), (77, 32, 128), (256, 128, 128)])
+def test_bwd_small(dtype, L, dk, dv):
+    """Ragged and whole chunks, dk != dv both ways, per-token eta, S0 and
+    dS_final given."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    args = make(2, 2, L, dk, dv, tdt, seed=L * 7 + dk + dv)
+    q, k, v, dout, eta, S0, dSf = args
+    say(f"bwd {dtype} L{L} dk{dk} dv{dv}")
+    check(run_gpu(q, k, v, dout, eta, 0.0, S0, dSf), run_oracle(q, k, v, dout, eta, 0.0, S0, dSf), dtype,
+          f"bwd {dtype} L{L} dk{dk} dv{dv}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bwd_scalar_eta_no_states(dtype):
+    """Scalar eta, no S0 and no dS_final (both zero)."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q, k, v, dout, _, _, _ = make(1, 3, 200, 64, 64, tdt, seed=5, per_token=False, s0=False, dsf=False)
+    eta = W.f32(0.05)
+    check(run_gpu(q, k, v, dout, None, eta, None, None), run_oracle(q, k, v, dout, None, eta, None, None), dtype,
+          f"bwd scalar eta {dtype}")
+
+
+def test_bwd_integer_exact():
+    """Small integers, eta = 1/8: every product and sum is exact in fp32."""
+    g = torch.Generator().manual_seed(23)
+    B, H, L, d = 1, 2, 70, 32
+    q, k, v, dout = (torch.randint(-2, 3, (B, H, L, d), generator=g).float() for _ in range(4))
+    S0 = torch.randint(-2, 3, (B, H, d, d), generator=g).float()
+    dSf = torch.randint(-2, 3, (B, H, d, d), generator=g).float()
+    got = run_gpu(q, k, v, dout, None, 0.125, S0, dSf)
+    ref = run_oracle(q, k, v, dout, None, 0.125, S0, dSf)
+    for n, a, r in zip(NAMES, got, ref):
+        assert np.array_equal(a.double().numpy(), r), n
+
+
+def test_bwd_segmented_sequence():
+    """Few heads on a long sequence: the bf16 forward passes cut the sequence
+    into segments joined by the look-back, also when time runs backwards."""
+    q, k, v, dout, eta, S0, dSf = make(1, 2, 5000, 128, 128, torch.bfloat16, seed=77)
+    assert lac.bwd_workspace_size(1, 2, 5000, 128, 128) > 0
+    check(run_gpu(q, k, v, dout, eta, 0.0, S0, dSf), run_oracle(q, k, v, dout, eta, 0.0, S0, dSf), "bf16",
+          "bwd segmented L5000")
+
+
+def test_bwd_lm_scale_sampled_heads():
+    """The LM-scale shape (B8 H16 L4096 d128, bf16, per-token eta, S0) with
+    seeded cotangents, in the benchmark's launch configuration; sampled
+    (b, h) heads recomputed whole by the oracle."""
+    inp = W.gen_lm_scale()
+    dout, dSf = W.gen_lm_scale_cotangents()
+    say("bwd lm-scale: running")
+    got = run_gpu(inp.q, inp.k, inp.v, dout, inp.eta, 0.0, inp.S0, dSf)
+    for b, h in ((0, 0), (3, 7), (7, 15)):
+        sl = lambda t: None if t is None else t[b:b + 1, h:h + 1]
+        ref = run_oracle(sl(inp.q), sl(inp.k), sl(inp.v), sl(dout), sl(inp.eta), 0.0, sl(inp.S0), sl(dSf))
+        check([g[b:b + 1, h:h + 1] for g in got], ref, "bf16", f"bwd lm-scale head ({b},{h})")
+
+
+def test_bwd_matches_forward_linearisation():
+    """Independent of the oracle's backward: for the fp32 path, <dout, J u>
+    from two GPU forward calls (central difference in a direction u of q)
+    equals <dq, u> from the GPU backward."""
+    q, k, v, dout, eta, S0, _ = make(1, 1, 96, 64, 64, torch.float64, seed=31, dsf=False)
+    q, k, v, dout = q.float(), k.float(), v.float(), dout.float()
+    u = torch.randn(q.shape, generator=torch.Generator().manual_seed(32))
+    h = 1e-2   # the forward is linear in q: the difference is exact up to rounding
+    op, _, _ = lac.fwd_chunked(dev(q + h * u), dev(k), dev(v), eta=dev(eta), S0=dev(S0), return_state=True)
+    om, _, _ = lac.fwd_chunked(dev(q - h * u), dev(k), dev(v), eta=dev(eta), S0=dev(S0), return_state=True)
+    fd = float(((op - om).double().cpu() * dout.double()).sum() / (2 * h))
+    dq = run_gpu(q, k, v, dout, eta, 0.0, S0, None)[0]
+    an = float((dq.double() * u.double()).sum())
+    assert abs(fd - an) <= 1e-4 * max(1.0, abs(an)), (fd, an)

@@ -11,7 +11,8 @@ here.
 Every tensor comes from ``torch.Generator('cpu').manual_seed(seed)``: values
 are drawn in fp32, transformed in fp32, then rounded (round-to-nearest-even)
 to the workload dtype.  The tensor index ``j`` in ``seed = 1000*cfg + j``
-follows the order q, k, v, eta-logits, S0, M0.  The In-Place (chunk-causal)
+follows the order q, k, v, eta-logits, S0, M0 (for the LM-scale backward,
+j = 5, 6 are its cotangents dout and dS_final).  The In-Place (chunk-causal)
 workload is drawn chunk by chunk (``seed = 3_000_000 + 4*i + j`` for chunk
 ``i``; j = 0 a, 1 b, 2 V-hat) so a host never holds fp32 copies of the
 long-context tensors.
@@ -23,6 +24,7 @@ Workloads (shapes of the pages' settings):
   momentum    momentum token-causal bf16, B4 H8 L16384 d128, C128, eta 0.05, beta 0.9
   dual        TTT-Linear mini-batch dual form, B4 H16 L8192 d64, b 16 and 2048, W0 0.5 I
   decode      one recurrent token per sequence, B256 H16 d128, state S0 (and M0) carried in
+  bwd         backward of lm-scale: its inputs plus cotangents dout, dS_final
 """
 from __future__ import annotations
 
@@ -100,6 +102,14 @@ def gen_lm_scale(B=8, H=16, L=4096, d=128, chunk=64, seed_base=2000) -> TokenCau
     S0 = _randn((B, H, d, d), seed_base + 4) * 0.02
     return TokenCausalInputs(q, k, v, eta, 0.0, 0.0, S0, None, chunk, "bf16",
                              dict(workload="lm-scale", B=B, H=H, L=L, dk=d, dv=d))
+
+
+def gen_lm_scale_cotangents(B=8, H=16, L=4096, d=128, seed_base=2000):
+    """Cotangents for the LM-scale backward: dout ~ N(0,1)/sqrt(L) bf16
+    [B,H,L,d] (j = 5); dS_final ~ N(0, 0.02^2) fp32 [B,H,d,d] (j = 6)."""
+    dout = (_randn((B, H, L, d), seed_base + 5) / math.sqrt(L)).to(torch.bfloat16)
+    dSf = _randn((B, H, d, d), seed_base + 6) * 0.02
+    return dout, dSf
 
 
 # ------------------------------------------------------------------ In-Place
