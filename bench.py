@@ -47,7 +47,7 @@ KERNEL_SOURCES = {
     "dual_fwd_kernel": ("dual.hip", "common.h"),
     "dual_chain_kernel": ("dual.hip", "common.h"),
     "decode_kernel": ("decode.hip", "common.h"),
-    "tcb_fwd_kernel+bwd_epilogue_kernel": ("tcb_fwd.hip", "bwd.hip", "common.h"),
+    "tcb_fwd_kernel+bwd_scale_kernels": ("tcb_fwd.hip", "bwd.hip", "common.h"),
 }
 
 
@@ -154,7 +154,7 @@ def setup_workload(name: str, dev: str):
         flop_alg = 3 * B * H * L * (4 * dk * dv + (C + 1) * (dk + dv))
         info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, mode="token_causal backward",
                     eta="per-token", dtype="bf16", tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
-                    kernel="tcb_fwd_kernel+bwd_epilogue_kernel", inputs=None)
+                    kernel="tcb_fwd_kernel+bwd_scale_kernels", inputs=None)
         return step, info
     if name in ("decode", "decode-momentum"):
         inp = W.gen_decode(beta=0.9 if name == "decode-momentum" else 0.0)

@@ -22,8 +22,9 @@
 //          time reversed
 // so the backward runs the forward kernels three times (time reversal is a
 // negative L stride with the base at the last token; the transposed states
-// are read in place) and one elementwise pass that scales P and R by eta and
-// forms deta.  The final state of the P pass is D_0 = dS0.
+// are read in place; the R pass scales its output rows by eta on the way
+// out) and one elementwise pass over 16-byte vectors that scales P by eta
+// and forms deta.  The final state of the P pass is D_0 = dS0.
 #include "common.h"
 #include "internal.h"
 
@@ -31,36 +32,71 @@ namespace ttt {
 
 namespace {
 
-TTT_DEV float to_f32(float x) { return x; }
-TTT_DEV float to_f32(bf16_t x) { return bf2f(__builtin_bit_cast(uint16_t, x)); }
-template <typename T> TTT_DEV T from_f32(float x);
-template <> TTT_DEV float from_f32<float>(float x) { return x; }
-template <> TTT_DEV bf16_t from_f32<bf16_t>(float x) { return __builtin_bit_cast(bf16_t, f2bf(x)); }
+// 16-byte vectors of a row of T
+template <typename T> struct Vec;
+template <> struct Vec<float> {
+    static constexpr int N = 4;
+    typedef f32x4 raw;
+    static TTT_DEV void unpack(const raw& r, float* x) { for (int i = 0; i < 4; ++i) x[i] = r[i]; }
+    static TTT_DEV raw pack(const float* x) { return raw{x[0], x[1], x[2], x[3]}; }
+};
+template <> struct Vec<bf16_t> {
+    static constexpr int N = 8;
+    typedef u32x4 raw;
+    static TTT_DEV void unpack(const raw& r, float* x) {
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(r[i] << 16);
+            x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+        }
+    }
+    static TTT_DEV raw pack(const float* x) {
+        return raw{pack2bf(x[0], x[1]), pack2bf(x[2], x[3]), pack2bf(x[4], x[5]), pack2bf(x[6], x[7])};
+    }
+};
 
-// one row (b, h, t) per 64-lane wave: deta = P . v (fp32), then dv = eta P,
-// dk = eta R in place
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_epilogue_kernel(BwdParams p) {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int64_t nrows = (int64_t)p.B * p.H * p.L;
-    if (row >= nrows) return;
-    T* P = reinterpret_cast<T*>(p.dv) + row * p.dv_dim;
-    T* R = reinterpret_cast<T*>(p.dk) + row * p.dk_dim;
-    const T* v = reinterpret_cast<const T*>(p.v) + row * p.dv_dim;
-    const float eta = p.eta ? p.eta[row] : p.eta_scalar;
-    float acc = 0.f;
-    for (int j = lane; j < p.dv_dim; j += 64) {
-        const float pj = to_f32(P[j]);
-        acc += pj * to_f32(v[j]);
-        P[j] = from_f32<T>(eta * pj);
-    }
-    for (int i = lane; i < p.dk_dim; i += 64) R[i] = from_f32<T>(eta * to_f32(R[i]));
-    if (p.deta) {
+// dv = eta P in place and deta = P . v: one thread per 16-byte vector of P;
+// the GV threads of a row (GV = dv / vector length, a power of two that
+// divides 64) sit in one wave and sum their partial dot products by shuffles
+template <typename T, int GV>
+__global__ __launch_bounds__(256) void bwd_scale_dv_kernel(BwdParams p) {
+    typedef Vec<T> VT;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nvec = (int64_t)p.B * p.H * p.L * GV;
+    float dot = 0.f;
+    const int64_t row = i / GV;
+    if (i < nvec) {
+        typename VT::raw* P = reinterpret_cast<typename VT::raw*>(p.dv) + i;
+        const typename VT::raw vr = reinterpret_cast<const typename VT::raw*>(p.v)[i];
+        const float eta = p.eta ? p.eta[row] : p.eta_scalar;
+        float x[VT::N], y[VT::N];
+        VT::unpack(*P, x);
+        VT::unpack(vr, y);
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-        if (lane == 0) p.deta[row] = acc;
+        for (int e = 0; e < VT::N; ++e) {
+            dot += x[e] * y[e];
+            x[e] *= eta;
+        }
+        *P = VT::pack(x);
     }
+#pragma unroll
+    for (int o = GV / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    if (p.deta && i < nvec && (i % GV) == 0) p.deta[row] = dot;
+}
+
+template <typename T>
+hipError_t launch_epilogue(const BwdParams& b, hipStream_t s) {
+    constexpr int N = Vec<T>::N;
+    const int64_t rows = (int64_t)b.B * b.H * b.L;
+    const int gv = b.dv_dim / N;
+    const dim3 block(256), gridv((unsigned)((rows * gv + 255) / 256));
+    switch (gv) {
+        case 4: hipLaunchKernelGGL((bwd_scale_dv_kernel<T, 4>), gridv, block, 0, s, b); break;
+        case 8: hipLaunchKernelGGL((bwd_scale_dv_kernel<T, 8>), gridv, block, 0, s, b); break;
+        case 16: hipLaunchKernelGGL((bwd_scale_dv_kernel<T, 16>), gridv, block, 0, s, b); break;
+        case 32: hipLaunchKernelGGL((bwd_scale_dv_kernel<T, 32>), gridv, block, 0, s, b); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 // contiguous [B, H, L, d] tensor, optionally walked from its last token
@@ -162,14 +198,17 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         p.s0s[0] = (int64_t)H * dk * dv;
         p.s0s[1] = (int64_t)dk * dv;
         p.s0_trans = 1;
+        // dk = eta R: the rows are scaled by eta on the way out (time reversed too)
+        p.use_oscale = 1;
+        p.oscale = b.eta ? b.eta + (L - 1) : nullptr;
+        p.ocs[0] = (int64_t)H * L;
+        p.ocs[1] = L;
+        p.ocs[2] = -1;
+        p.oscale_scalar = b.eta_scalar;
         if ((e = launch_tc_fwd(p, b.dtype, MODE_TC, s)) != hipSuccess) return e;
     }
-    // dv = eta P, dk = eta R, deta = P . v
-    const int64_t rows = (int64_t)b.B * H * L;
-    const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
-    if (b.dtype == 1) hipLaunchKernelGGL(bwd_epilogue_kernel<bf16_t>, grid, block, 0, s, b);
-    else hipLaunchKernelGGL(bwd_epilogue_kernel<float>, grid, block, 0, s, b);
-    return hipGetLastError();
+    // dv = eta P, deta = P . v
+    return b.dtype == 1 ? launch_epilogue<bf16_t>(b, s) : launch_epilogue<float>(b, s);
 }
 
 }  // namespace ttt

@@ -41,6 +41,12 @@ struct TcParams {
     // S0 (and M0) stored transposed: element (i, j) of a head's [dk, dv]
     // state at j * dk + i (the backward pass reads a state this way)
     int s0_trans;
+    // output rows scaled by a per-token factor (use_oscale = 1): oscale
+    // [B,H,L] with strides ocs, or oscale_scalar when oscale is NULL
+    int use_oscale;
+    const float* oscale;
+    int64_t ocs[3];
+    float oscale_scalar;
 };
 
 // dtype: 0 fp32, 1 bf16.  mode: MODE_*.  Returns hipSuccess or the launch error;

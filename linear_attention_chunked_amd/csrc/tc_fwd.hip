@@ -309,7 +309,12 @@ __global__ __launch_bounds__(DVT / 16 * 64) void tc_fwd_kernel(TcParams p) {
                     const float a = sTab[2 * (CS + 1) + i];
                     for (int r = 0; r < 4; ++r) acc[r] += a * acc2[r];
                 }
-                if (i < n) st4(&Og[(int64_t)(tbase + i) * oL + 16 * wave + 4 * g], acc);
+                if (i < n) {
+                    if (p.use_oscale)
+                        acc *= p.oscale ? p.oscale[b * p.ocs[0] + h * p.ocs[1] + (int64_t)(tbase + i) * p.ocs[2]]
+                                        : p.oscale_scalar;
+                    st4(&Og[(int64_t)(tbase + i) * oL + 16 * wave + 4 * g], acc);
+                }
             }
         }
 

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     __shared__ __attribute__((aligned(16))) bf16_t sK[2][NKB * BLK];
     __shared__ __attribute__((aligned(16))) bf16_t sV[2][(DVT / 32) * BLKV];
     __shared__ __attribute__((aligned(16))) float sE[2][NV][CS];
+    __shared__ __attribute__((aligned(16))) float sOS[2][CS];     // output row scales
     __shared__ __attribute__((aligned(16))) bf16_t sP[HAS_P ? CS * LP : 8];
     __shared__ __attribute__((aligned(16))) f32x4 sX[NNT][NTI][64];   // half-1 readout partials
     __shared__ __attribute__((aligned(16))) bf16_t sO[CS * DVT];  // finished output tile
@@ -191,7 +192,8 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     // one set, its VGPRs are taken by the second state
     constexpr int PF = MOM ? 1 : 2;
     u32x4 rq[PF][UQ], rk[PF][UQ], rv[PF];
-    float re[PF];
+    float re[PF], ros[PF];
+    const float* OSg = p.oscale ? p.oscale + b * p.ocs[0] + h * p.ocs[1] : nullptr;
     // staging: 16 lanes load one 256-byte Q/K row (8 lanes one 128-byte V row);
     // chunk c of row r lands in block c/4 at swizzled position (c%4)^swz(r)
     int loff_q[UQ], loff_v;
@@ -238,6 +240,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         // (tokens past L get eta 0 when the chunk is written to LDS: a select
         // here would make the compiler wait for this load right away)
         re[st] = Eg ? (Eg + (int64_t)t0 * eL)[__mul24(min(tid % CS, lim), eL24)] : p.eta_scalar;
+        ros[st] = OSg ? OSg[(int64_t)(t0 + min(tid % CS, lim)) * p.ocs[2]] : p.oscale_scalar;
     };
     auto store = [&](int c, int buf, auto SET, auto WITHQ) {
         constexpr int st = decltype(SET)::value;
@@ -252,6 +255,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             const int n = min(CS, L - c * CS);
             const float e = (tid < n) ? re[st] : 0.f;
             sE[buf][0][tid] = e;
+            if (p.use_oscale) sOS[buf][tid] = ros[st];
             if (MOM) {
                 const int pw = n - 1 - tid;
                 sE[buf][1][tid] = (pw >= 0) ? e * sTab[pw] : 0.f;
@@ -281,14 +285,15 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     }
 
     f32x4 oacc[NTI];  // this wave's readout partial of the previous chunk (half 0 keeps it)
-    int prev_base = 0, prev_n = 0;
+    int prev_base = 0, prev_n = 0, prev_buf = 0;
     // half 0: add half 1's partial, round, and park the tile in sO (rows of 128 B,
     // 16-byte chunks swizzled by (row/2)%8: conflict-free for both sides)
     auto combine = [&]() {
 #pragma unroll
         for (int ti = 0; ti < NTI; ++ti) {
             const int i = 16 * ti + c16;
-            const f32x4 o = oacc[ti] + sX[nt][ti][lane];
+            f32x4 o = oacc[ti] + sX[nt][ti][lane];
+            if (p.use_oscale) o *= sOS[prev_buf][i];
             const int ch = (2 * nt + (g >> 1)) ^ oswz<DVT>(i);
             st4(&sO[i * DVT + 8 * ch + 4 * (g & 1)], o);
         }
@@ -672,6 +677,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         // (prev_* are read by write_out above, so they advance only here)
         prev_base = tbase;
         prev_n = n;
+        prev_buf = cur;
 
         // ------------- state update (own d_k half)
         state_update(cur, n, VB, VS, VM);
