@@ -134,16 +134,20 @@ def setup_workload(name: str, dev: str):
         info = dict(workload=name, B=B, H=H, L=L, d=d, minibatch=mb, dtype="bf16", tokens=B * L,
                     bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="dual_chain_kernel", inputs=inp)
         return step, info
-    if name == "bwd":
-        inp = W.gen_lm_scale()
-        dout, dSf = W.gen_lm_scale_cotangents()
+    if name in ("bwd", "bwd-momentum"):
+        mom = name == "bwd-momentum"
+        inp = W.gen_momentum() if mom else W.gen_lm_scale()
         B, H, L, dk = inp.q.shape
         dv = inp.v.shape[-1]
-        q, k, v, eta, S0 = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.eta.to(dev), inp.S0.to(dev)
+        dout, dSf = W.gen_lm_scale_cotangents(B, H, L, dk, seed_base=4000 if mom else 2000)
+        q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+        eta = inp.eta.to(dev) if inp.eta is not None else None
+        S0 = inp.S0.to(dev) if inp.S0 is not None else None
         do, dS = dout.to(dev), dSf.to(dev)
 
         def step():
-            return lac.bwd_chunked(q, k, v, do, eta=eta, S0=S0, dS_final=dS)
+            return lac.bwd_chunked(q, k, v, do, eta=eta, eta_scalar=inp.eta_scalar, beta=inp.beta, S0=S0,
+                                   dS_final=dS, need_dM0=mom)
 
         es = 2
         bytes_alg = (B * H * L * (2 * dk + 2 * dv) * es      # q, k, v, dout
@@ -151,9 +155,13 @@ def setup_workload(name: str, dev: str):
                      + B * H * L * 4 * 2                     # eta, deta
                      + 3 * B * H * dk * dv * 4)              # S0, dS_final, dS0
         C = inp.chunk
-        flop_alg = 3 * B * H * L * (4 * dk * dv + (C + 1) * (dk + dv))
+        nst = 2 if mom else 1
+        if mom:
+            bytes_alg += B * H * dk * dv * 4          # dM0
+        flop_alg = 3 * B * H * L * (4 * nst * dk * dv + (C + 1) * (dk + dv))
         info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, mode="token_causal backward",
-                    eta="per-token", dtype="bf16", tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
+                    beta=inp.beta, eta="per-token" if eta is not None else inp.eta_scalar, dtype="bf16",
+                    tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
                     kernel="tcb_fwd_kernel+bwd_scale_kernels", inputs=None)
         return step, info
     if name in ("decode", "decode-momentum"):
@@ -243,7 +251,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lm-scale",
                     help="lm-scale (default), small-f32, inplace-32k, inplace-128k, momentum, dual-b16, "
-                         "dual-b2048, decode, decode-momentum, bwd")
+                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum")
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this many seconds of steps have run")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -13,7 +13,7 @@
  *                         (MSE reconstruction loss), dual form
  *   ttt_decode_step       one recurrent token per sequence (inference):
  *                         state update and readout with the state in HBM
- *   ttt_bwd_chunked       backward pass of the token-causal forward (beta 0)
+ *   ttt_bwd_chunked       backward pass of the token-causal forward
  *
  * Sources (cited by page title and paragraph or section):
  *  [P1] "KV 바인딩 기반 테스트 시간 학습은 사실상 선형 어텐션이다"
@@ -234,35 +234,41 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
                              float* S, float* M, void* out, void* stream);
 
 /*
- * ttt_bwd_chunked -- backward pass of ttt_fwd_chunked in TOKEN_CAUSAL mode
- * without momentum (beta = 0).
+ * ttt_bwd_chunked -- backward pass of ttt_fwd_chunked in TOKEN_CAUSAL mode,
+ * with or without momentum.
  *
- * [P1] paragraphs on the state-matrix update and on the one-step output
- * identity give the forward S_t = S_{t-1} + eta_t k_t^T v_t, o_t = q_t S_t
- * (from S0); [P4] section on the two kinds of weights trains the outer model
- * through these updates, which needs their gradients.  Given dout = dL/do
- * and dS_final = dL/dS_final (NULL: zero), with D_t = dS_final +
- * sum_{u >= t} q_u^T do_u:
- *     dq_t = do_t S_t^T,  dk_t = eta_t D_t v_t^T,  dv_t = eta_t k_t D_t,
- *     deta_t = k_t D_t v_t^T (per token, also for a scalar eta: its gradient
- *     is the sum over tokens),  dS0 = D_0.
+ * [P1] paragraphs on the state-matrix update, on the one-step output
+ * identity and on momentum give the forward g_t = eta_t k_t^T v_t,
+ * m_t = beta m_{t-1} + g_t, S_t = S_{t-1} + m_t, o_t = q_t S_t (from S0, M0);
+ * [P4] section on the two kinds of weights trains the outer model through
+ * these updates, which needs their gradients.  Given dout = dL/do,
+ * dS_final = dL/dS_final and dM_final = dL/dM_final (NULL: zero), with
+ * A_t the adjoint of m_t (the sum over u >= t of the momentum-weighted
+ * q_u^T do_u plus the boundary terms; beta = 0: dS_final + sum_{u>=t} q_u^T do_u):
+ *     dq_t = do_t S_t^T,  dk_t = eta_t A_t v_t^T,  dv_t = eta_t k_t A_t,
+ *     deta_t = k_t A_t v_t^T (per token, also for a scalar eta: its gradient
+ *     is the sum over tokens),  dS0 = dL/dS0,  dM0 = beta A_0.
+ * The gradient with respect to beta is not computed.
  *
  * All tensors are contiguous: q, k, dq, dk [B,H,L,dk]; v, dout, dv
- * [B,H,L,dv] in `dtype`; eta [B,H,L] fp32 or NULL (eta_scalar); S0,
- * dS_final, dS0 [B,H,dk,dv] fp32 or NULL (S0, dS_final: zero).  deta and
- * dS0 may be NULL (not computed).  Supported: dk, dv in {32, 64, 128}.
- * Outputs must not overlap any input or each other.  workspace: device
- * memory of ttt_bwd_workspace_size bytes (0 possible), caller-owned.
+ * [B,H,L,dv] in `dtype`; eta [B,H,L] fp32 or NULL (eta_scalar); S0, M0,
+ * dS_final, dM_final, dS0, dM0 [B,H,dk,dv] fp32 or NULL (inputs: zero; M0
+ * and dM_final ignored when beta = 0).  deta, dS0 and dM0 may be NULL (not
+ * computed).  beta in [0, 1).  Supported: dk, dv in {32, 64, 128}.  Outputs
+ * must not overlap any input or each other.  workspace: device memory of
+ * ttt_bwd_workspace_size bytes (0 possible), caller-owned.
  * Errors (before anything is enqueued): TTT_ERR_NULL, TTT_ERR_DTYPE,
- * TTT_ERR_SHAPE, TTT_ERR_ALIGN (16 bytes), TTT_ERR_UNSUPPORTED,
- * TTT_ERR_WORKSPACE, TTT_ERR_ALIAS; TTT_ERR_HIP if a launch fails.
+ * TTT_ERR_SHAPE, TTT_ERR_VALUE (beta), TTT_ERR_ALIGN (16 bytes),
+ * TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_ALIAS; TTT_ERR_HIP if a
+ * launch fails.
  */
 ttt_status_t ttt_bwd_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
-                                    size_t* bytes);
+                                    float beta, size_t* bytes);
 ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
                              const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
-                             const float* S0, const void* dout, const float* dS_final,
-                             void* dq, void* dk_out, void* dv_out, float* deta, float* dS0,
+                             float beta, const float* S0, const float* M0, const void* dout,
+                             const float* dS_final, const float* dM_final,
+                             void* dq, void* dk_out, void* dv_out, float* deta, float* dS0, float* dM0,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */

@@ -11,7 +11,7 @@ Entry points (same names as the C ABI):
     chunk_state_scan(dS, dM, ...)      exclusive scan of chunk-state deltas
     dual_form_fwd(q, k, v, W0, ...)    TTT-Linear mini-batch dual form
     decode_step(q, k, v, S, M, ...)    one recurrent token, state updated in place
-    bwd_chunked(q, k, v, dout, ...)    backward of the token-causal forward (beta 0)
+    bwd_chunked(q, k, v, dout, ...)    backward of the token-causal forward
 """
 from __future__ import annotations
 
@@ -82,10 +82,10 @@ def load_library():
     lib.ttt_decode_step.argtypes = [i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, f32, _vp, _vp,
                                     _vp, _vp]
     lib.ttt_decode_step.restype = ctypes.c_int
-    lib.ttt_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ttt_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, f32, ctypes.POINTER(ctypes.c_size_t)]
     lib.ttt_bwd_workspace_size.restype = ctypes.c_int
-    lib.ttt_bwd_chunked.argtypes = [i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, _vp, _vp, _vp,
-                                    _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.ttt_bwd_chunked.argtypes = [i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, f32, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.ttt_bwd_chunked.restype = ctypes.c_int
     lib.ttt_status_string.argtypes = [ctypes.c_int]
     lib.ttt_status_string.restype = ctypes.c_char_p
@@ -292,25 +292,25 @@ def decode_step(q, k, v, S, M=None, *, eta=None, eta_scalar=0.0, beta=0.0, out=N
     return out
 
 
-def bwd_workspace_size(B, H, L, dk, dv, *, dtype=torch.bfloat16):
+def bwd_workspace_size(B, H, L, dk, dv, *, dtype=torch.bfloat16, beta=0.0):
     """Workspace bytes ``bwd_chunked`` needs for this shape (0 possible)."""
     lib = load_library()
     ws = ctypes.c_size_t(0)
     _check(lib.ttt_bwd_workspace_size(B, H, L, dk, dv, TTT_BF16 if dtype == torch.bfloat16 else TTT_F32,
-                                      ctypes.byref(ws)))
+                                      float(beta), ctypes.byref(ws)))
     return int(ws.value)
 
 
-def bwd_chunked(q, k, v, dout, *, eta=None, eta_scalar=0.0, S0=None, dS_final=None, need_deta=True,
-                need_dS0=True, stream=None):
-    """Backward of the token-causal forward without momentum (``ttt_bwd_chunked``).
+def bwd_chunked(q, k, v, dout, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None, dS_final=None,
+                dM_final=None, need_deta=True, need_dS0=True, need_dM0=False, stream=None):
+    """Backward of the token-causal forward (``ttt_bwd_chunked``).
 
     q, k: [B,H,L,dk]; v, dout: [B,H,L,dv], contiguous, fp32 or bf16; eta fp32
-    [B,H,L] or None (eta_scalar); S0, dS_final fp32 [B,H,dk,dv] or None.
-    Returns (dq, dk, dv, deta, dS0); deta is per token (None unless
-    need_deta), dS0 None unless need_dS0."""
+    [B,H,L] or None (eta_scalar); S0, M0, dS_final, dM_final fp32
+    [B,H,dk,dv] or None.  Returns (dq, dk, dv, deta, dS0, dM0); deta is per
+    token; the optional outputs are None unless requested."""
     lib = load_library()
-    _require_gpu(q, k, v, dout, eta, S0, dS_final)
+    _require_gpu(q, k, v, dout, eta, S0, M0, dS_final, dM_final)
     if q.dim() != 4:
         raise ValueError("q must be [B,H,L,dk]")
     B, H, L, dk = q.shape
@@ -320,18 +320,22 @@ def bwd_chunked(q, k, v, dout, *, eta=None, eta_scalar=0.0, S0=None, dS_final=No
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         if not t.is_contiguous() or t.dtype != q.dtype:
             raise ValueError(f"{nm} must be contiguous and of q's dtype")
-    for t, nm, shp in ((eta, "eta", (B, H, L)), (S0, "S0", (B, H, dk, dv)), (dS_final, "dS_final", (B, H, dk, dv))):
+    st = (B, H, dk, dv)
+    for t, nm, shp in ((eta, "eta", (B, H, L)), (S0, "S0", st), (M0, "M0", st), (dS_final, "dS_final", st),
+                       (dM_final, "dM_final", st)):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.shape != shp):
             raise ValueError(f"{nm} must be contiguous fp32 {list(shp)}")
     dq, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     deta = torch.empty((B, H, L), dtype=torch.float32, device=q.device) if need_deta else None
-    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device) if need_dS0 else None
-    wsb = bwd_workspace_size(B, H, L, dk, dv, dtype=q.dtype)
+    dS0 = torch.empty(st, dtype=torch.float32, device=q.device) if need_dS0 else None
+    dM0 = torch.empty(st, dtype=torch.float32, device=q.device) if need_dM0 else None
+    wsb = bwd_workspace_size(B, H, L, dk, dv, dtype=q.dtype, beta=beta)
     ws = torch.empty(wsb, dtype=torch.uint8, device=q.device) if wsb else None
     _check(lib.ttt_bwd_chunked(B, H, L, dk, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
-                               float(eta_scalar), _ptr(S0), _ptr(dout), _ptr(dS_final), _ptr(dq), _ptr(dk_),
-                               _ptr(dv_), _ptr(deta), _ptr(dS0), _ptr(ws), wsb, _stream(stream)))
-    return dq, dk_, dv_, deta, dS0
+                               float(eta_scalar), float(beta), _ptr(S0), _ptr(M0), _ptr(dout), _ptr(dS_final),
+                               _ptr(dM_final), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(deta), _ptr(dS0), _ptr(dM0),
+                               _ptr(ws), wsb, _stream(stream)))
+    return dq, dk_, dv_, deta, dS0, dM0
 
 
 __all__ = ["fwd_chunked", "chunk_state_scan", "dual_form_fwd", "decode_step", "bwd_chunked", "bwd_workspace_size", "load_library", "TTTError",

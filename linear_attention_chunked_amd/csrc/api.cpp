@@ -238,22 +238,24 @@ ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32
 }
 
 ttt_status_t ttt_bwd_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
-                                    size_t* bytes) {
+                                    float beta, size_t* bytes) {
     if (!bytes) return TTT_ERR_NULL;
     if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
     if (B < 1 || H < 1 || L < 1 || dk < 1 || dv < 1) return TTT_ERR_SHAPE;
+    if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_VALUE;
     if (!ttt::bwd_supported(dtype, dk, dv)) return TTT_ERR_UNSUPPORTED;
-    *bytes = ttt::bwd_workspace(B, H, L, dk, dv, dtype);
+    *bytes = ttt::bwd_workspace(B, H, L, dk, dv, dtype, beta != 0.f);
     return TTT_OK;
 }
 
 ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
                              const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
-                             const float* S0, const void* dout, const float* dS_final, void* dq, void* dk_out,
-                             void* dv_out, float* deta, float* dS0, void* workspace, size_t workspace_bytes,
+                             float beta, const float* S0, const float* M0, const void* dout,
+                             const float* dS_final, const float* dM_final, void* dq, void* dk_out, void* dv_out,
+                             float* deta, float* dS0, float* dM0, void* workspace, size_t workspace_bytes,
                              void* stream) {
     size_t need = 0;
-    const ttt_status_t st = ttt_bwd_workspace_size(B, H, L, dk, dv, dtype, &need);
+    const ttt_status_t st = ttt_bwd_workspace_size(B, H, L, dk, dv, dtype, beta, &need);
     if (st != TTT_OK) return st;
     if (!q || !k || !v || !dout || !dq || !dk_out || !dv_out) return TTT_ERR_NULL;
     if (need > 0 && (!workspace || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
@@ -261,8 +263,9 @@ ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_
     const size_t nq = (size_t)B * H * L * dk * es, nv = (size_t)B * H * L * dv * es;
     const size_t ne = (size_t)B * H * L * 4, ns = (size_t)B * H * dk * dv * 4;
     struct Buf { const void* p; size_t n; };
-    const Buf ins[] = {{q, nq}, {k, nq}, {v, nv}, {dout, nv}, {eta, ne}, {S0, ns}, {dS_final, ns}};
-    const Buf outs[] = {{dq, nq}, {dk_out, nq}, {dv_out, nv}, {deta, ne}, {dS0, ns}, {workspace, need}};
+    const Buf ins[] = {{q, nq}, {k, nq}, {v, nv}, {dout, nv}, {eta, ne}, {S0, ns}, {M0, ns}, {dS_final, ns},
+                       {dM_final, ns}};
+    const Buf outs[] = {{dq, nq}, {dk_out, nq}, {dv_out, nv}, {deta, ne}, {dS0, ns}, {dM0, ns}, {workspace, need}};
     for (const Buf& b : ins)
         if (b.p && !aligned16(b.p)) return TTT_ERR_ALIGN;
     for (const Buf& b : outs)
@@ -295,14 +298,18 @@ ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_
     p.v = v;
     p.eta = eta;
     p.eta_scalar = eta_scalar;
+    p.beta = beta;
     p.S0 = S0;
+    p.M0 = beta != 0.f ? M0 : nullptr;
     p.dout = dout;
     p.dS_final = dS_final;
+    p.dM_final = beta != 0.f ? dM_final : nullptr;
     p.dq = dq;
     p.dk = dk_out;
     p.dv = dv_out;
     p.deta = deta;
     p.dS0 = dS0;
+    p.dM0 = dM0;
     p.workspace = workspace;
     return from_hip(ttt::launch_bwd(p, reinterpret_cast<hipStream_t>(stream)));
 }

@@ -1,4 +1,4 @@
-// bwd.hip -- backward pass of the token-causal fast-weight forward (beta = 0).
+// bwd.hip -- backward pass of the token-causal fast-weight forward.
 //
 // [P1] ("KV 바인딩 기반 테스트 시간 학습은 사실상 선형 어텐션이다",
 // aitrends.kr/articles/4698), paragraphs on the state-matrix update and the
@@ -25,6 +25,20 @@
 // are read in place; the R pass scales its output rows by eta on the way
 // out) and one elementwise pass over 16-byte vectors that scales P by eta
 // and forms deta.  The final state of the P pass is D_0 = dS0.
+//
+// With momentum (m_t = beta m_{t-1} + g_t, S_t = S_{t-1} + m_t) the gradients
+// of g_t are read from the adjoint of m_t,
+//     A_t = sum_{u >= t} w(u - t) q_u^T do_u + c_t dS_final + beta^{L-1-t} dM_final,
+//     w(n) = 1 + beta + ... + beta^n,  c_t = w(L - 1 - t),
+// which, in reversed time, is the state S' of the momentum forward itself run
+// on the increments q_u^T do_u from S0' = dM_final / beta and
+// M0' = (beta dS_final - (1 - beta) dM_final) / beta^2 (these match the
+// constant and the beta^{L-1-t} parts of the two boundary terms).  So dq, P = k A and
+// R = v A^T are three momentum forwards, dv = eta P, dk = eta R, deta = P . v
+// as before, and with S'_f, M'_f the P pass's final states:
+//     dS0 = (1 - beta) S'_f + beta M'_f   (the adjoint of S0: A_0 - beta A_1)
+//     dM0 = beta S'_f                     (m_0 = beta M0 + g_0).
+// (The gradient with respect to beta itself is not computed.)
 #include "common.h"
 #include "internal.h"
 
@@ -83,6 +97,32 @@ __global__ __launch_bounds__(256) void bwd_scale_dv_kernel(BwdParams p) {
     if (p.deta && i < nvec && (i % GV) == 0) p.deta[row] = dot;
 }
 
+// S0' = dM_final / beta, M0' = (beta dS_final - (1 - beta) dM_final) / beta^2,
+// elementwise (NULL inputs are zero)
+__global__ __launch_bounds__(256) void bwd_init_kernel(const float* dSf, const float* dMf, float beta, float* S0p,
+                                                       float* M0p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float a = dSf ? dSf[i] : 0.f, c = dMf ? dMf[i] : 0.f;
+    S0p[i] = c / beta;
+    M0p[i] = (beta * a - (1.f - beta) * c) / (beta * beta);
+}
+
+// dS0 = (1 - beta) S'_f + beta M'_f,  dM0 = beta S'_f
+__global__ __launch_bounds__(256) void bwd_state_kernel(const float* Sf, const float* Mf, float beta, float* dS0,
+                                                        float* dM0, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    const float sv = Sf[i];
+    if (dS0) dS0[i] = (1.f - beta) * sv + beta * Mf[i];
+    if (dM0) dM0[i] = beta * sv;
+}
+
+__global__ __launch_bounds__(256) void bwd_zero_kernel(float* out, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) out[i] = 0.f;
+}
+
 template <typename T>
 hipError_t launch_epilogue(const BwdParams& b, hipStream_t s) {
     constexpr int N = Vec<T>::N;
@@ -113,9 +153,24 @@ TcParams pass_params(const BwdParams& b) {
     p.H = b.H;
     p.L = b.L;
     p.chunk = 64;
-    p.beta = 0.f;
+    p.beta = b.beta;
     p.workspace = b.workspace;
     return p;
+}
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// workspace: [forward passes' look-back][S0'][M0'][S'_f][M'_f] (the last
+// four with momentum only)
+size_t fwd_ws(int B, int H, int L, int dk, int dv, int dtype, int mode) {
+    if (dtype != 1) return 0;
+    size_t w = 0;
+    if (tcb_supported(dtype, dv, dk)) w = tcb_workspace(B, H, L, dv, dk, mode, 64);   // dq and R
+    if (tcb_supported(dtype, dk, dv)) {
+        const size_t wp = tcb_workspace(B, H, L, dk, dv, mode, 64);                  // P
+        if (wp > w) w = wp;
+    }
+    return align256(w);
 }
 
 }  // namespace
@@ -124,14 +179,10 @@ bool bwd_supported(int dtype, int dk, int dv) {
     return tc_fwd_supported(dtype, MODE_TC, dk, dv, 64) && tc_fwd_supported(dtype, MODE_TC, dv, dk, 64);
 }
 
-size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype) {
-    if (dtype != 1) return 0;
-    size_t w = 0;
-    if (tcb_supported(dtype, dv, dk)) w = tcb_workspace(B, H, L, dv, dk, MODE_TC, 64);   // dq and R
-    if (tcb_supported(dtype, dk, dv)) {
-        const size_t wp = tcb_workspace(B, H, L, dk, dv, MODE_TC, 64);                  // P
-        if (wp > w) w = wp;
-    }
+size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype, bool momentum) {
+    const int mode = momentum ? MODE_MOM : MODE_TC;
+    size_t w = fwd_ws(B, H, L, dk, dv, dtype, mode);
+    if (momentum) w += 4 * align256((size_t)B * H * dk * dv * sizeof(float));
     return w;
 }
 
@@ -139,6 +190,20 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
     if (!bwd_supported(b.dtype, b.dk_dim, b.dv_dim)) return hipErrorInvalidValue;
     const size_t es = b.dtype == 1 ? 2 : 4;
     const int H = b.H, L = b.L, dk = b.dk_dim, dv = b.dv_dim;
+    const bool mom = b.beta != 0.f;
+    const int mode = mom ? MODE_MOM : MODE_TC;
+    const int64_t nst = (int64_t)b.B * H * dk * dv;
+    const dim3 sgrid((unsigned)((nst + 255) / 256)), sblock(256);
+    float *S0p = nullptr, *M0p = nullptr, *Sfp = nullptr, *Mfp = nullptr;
+    if (mom) {
+        char* w = static_cast<char*>(b.workspace) + fwd_ws(b.B, H, L, dk, dv, b.dtype, mode);
+        const size_t sb = align256((size_t)nst * sizeof(float));
+        S0p = reinterpret_cast<float*>(w);
+        M0p = reinterpret_cast<float*>(w + sb);
+        Sfp = reinterpret_cast<float*>(w + 2 * sb);
+        Mfp = reinterpret_cast<float*>(w + 3 * sb);
+        hipLaunchKernelGGL(bwd_init_kernel, sgrid, sblock, 0, s, b.dS_final, b.dM_final, b.beta, S0p, M0p, nst);
+    }
     hipError_t e;
 
     // dq: queries do, keys v, values k (rate eta), state S0^T
@@ -160,8 +225,11 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         p.S0 = b.S0;
         p.s0s[0] = (int64_t)H * dk * dv;
         p.s0s[1] = (int64_t)dk * dv;
+        p.M0 = b.M0;
+        p.m0s[0] = p.s0s[0];
+        p.m0s[1] = p.s0s[1];
         p.s0_trans = 1;
-        if ((e = launch_tc_fwd(p, b.dtype, MODE_TC, s)) != hipSuccess) return e;
+        if ((e = launch_tc_fwd(p, b.dtype, mode, s)) != hipSuccess) return e;
     }
     // P (into dv): queries k, keys q, values do, time reversed, state dS_final;
     // its final state is D_0 = dS0
@@ -176,11 +244,15 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         set_seq(p.os, &o, b.dv, H, L, dv, es, true);
         p.out = const_cast<void*>(o);
         p.eta_scalar = 1.f;
-        p.S0 = b.dS_final;
+        p.S0 = mom ? S0p : b.dS_final;
         p.s0s[0] = (int64_t)H * dk * dv;
         p.s0s[1] = (int64_t)dk * dv;
-        p.S_final = b.dS0;
-        if ((e = launch_tc_fwd(p, b.dtype, MODE_TC, s)) != hipSuccess) return e;
+        p.M0 = M0p;
+        p.m0s[0] = p.s0s[0];
+        p.m0s[1] = p.s0s[1];
+        p.S_final = mom ? Sfp : b.dS0;
+        p.M_final = Mfp;
+        if ((e = launch_tc_fwd(p, b.dtype, mode, s)) != hipSuccess) return e;
     }
     // R (into dk): queries v, keys do, values q, time reversed, state dS_final^T
     {
@@ -194,9 +266,12 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         set_seq(p.os, &o, b.dk, H, L, dk, es, true);
         p.out = const_cast<void*>(o);
         p.eta_scalar = 1.f;
-        p.S0 = b.dS_final;
+        p.S0 = mom ? S0p : b.dS_final;
         p.s0s[0] = (int64_t)H * dk * dv;
         p.s0s[1] = (int64_t)dk * dv;
+        p.M0 = M0p;
+        p.m0s[0] = p.s0s[0];
+        p.m0s[1] = p.s0s[1];
         p.s0_trans = 1;
         // dk = eta R: the rows are scaled by eta on the way out (time reversed too)
         p.use_oscale = 1;
@@ -205,8 +280,12 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         p.ocs[1] = L;
         p.ocs[2] = -1;
         p.oscale_scalar = b.eta_scalar;
-        if ((e = launch_tc_fwd(p, b.dtype, MODE_TC, s)) != hipSuccess) return e;
+        if ((e = launch_tc_fwd(p, b.dtype, mode, s)) != hipSuccess) return e;
     }
+    if (mom && (b.dS0 || b.dM0))
+        hipLaunchKernelGGL(bwd_state_kernel, sgrid, sblock, 0, s, Sfp, Mfp, b.beta, b.dS0, b.dM0, nst);
+    else if (b.dM0)   // no momentum: m_0 does not depend on M0
+        hipLaunchKernelGGL(bwd_zero_kernel, sgrid, sblock, 0, s, b.dM0, nst);
     // dv = eta P, deta = P . v
     return b.dtype == 1 ? launch_epilogue<bf16_t>(b, s) : launch_epilogue<float>(b, s);
 }

@@ -103,7 +103,7 @@ struct DecodeParams {
 };
 hipError_t launch_decode(const DecodeParams& p, int dtype, hipStream_t stream);
 
-// Backward of the token-causal forward (beta = 0), contiguous [B,H,L,d]
+// Backward of the token-causal forward (with or without momentum), contiguous [B,H,L,d]
 // tensors.  dk and dv (the gradient buffers) receive intermediate results
 // before the final scaling, so they must not alias any input.
 struct BwdParams {
@@ -113,18 +113,22 @@ struct BwdParams {
     const void* v;
     const float* eta;
     float eta_scalar;
+    float beta;
     const float* S0;
+    const float* M0;
     const void* dout;
     const float* dS_final;
+    const float* dM_final;
     void* dq;
     void* dk;
     void* dv;
     float* deta;
     float* dS0;
+    float* dM0;
     void* workspace;
 };
 bool bwd_supported(int dtype, int dk, int dv);
-size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype);
+size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype, bool momentum);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 bool decode_supported(int dtype, int dk, int dv);
 

@@ -169,16 +169,19 @@ def test_bwd_rejects_before_launch(lib):
     def args(**kw):
         base = [FAKE + i * (n + 4096) for i in range(12)]
         return [2, 2, 64, kw.get("dk", 64), 64, kw.get("dtype", 1),
-                kw.get("q", base[0]), base[1], base[2], None, 0.1, None, base[3], None,
-                kw.get("dq", base[4]), base[5], base[6], None, None, None, 0, None]
+                kw.get("q", base[0]), base[1], base[2], None, 0.1, kw.get("beta", 0.0), None, None, base[3],
+                None, None, kw.get("dq", base[4]), base[5], base[6], None, None, None, None, 0, None]
     assert f(*args(dtype=4)) == ERR_DTYPE
+    assert f(*args(beta=1.0)) == ERR_VALUE
     assert f(*args(dk=48)) == ERR_UNSUP
     assert f(*args(q=None)) == ERR_NULL
     assert f(*args(q=FAKE + 8)) == ERR_ALIGN
     assert f(*args(dq=FAKE + 256)) == ERR_ALIAS          # gradient buffer inside q
     ws = ctypes.c_size_t(7)
-    assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, ctypes.byref(ws)) == OK
-    assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, None) == ERR_NULL
+    assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, ctypes.c_float(0.0), ctypes.byref(ws)) == OK
+    assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, ctypes.c_float(0.9), ctypes.byref(ws)) == OK
+    assert ws.value > 0   # momentum keeps its adjoint start states in the workspace
+    assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, ctypes.c_float(0.0), None) == ERR_NULL
 
 
 def test_binding_refuses_cpu_tensors():

@@ -4,8 +4,9 @@ pinned by finite differences and autograd on the CPU.
 
 Tolerances (relative L2 over each compared tensor): fp32 inputs <= 1e-5;
 bf16 inputs <= 1e-2 for dq, dk, dv, deta (the intermediate P, R are rounded
-to bf16 once before the eta scaling) and <= 1e-4 for dS0 (exact bf16
-products summed in fp32 over L tokens).  Integer-valued fp32 inputs with a
+to bf16 once before the eta scaling) and <= 1e-4 for dS0 without momentum
+(exact bf16 products summed in fp32 over L tokens); with momentum the
+states carry bf16-level error too (<= 1e-2).  Integer-valued fp32 inputs with a
 dyadic eta are exact and must match bit for bit.
 """
 import numpy as np
@@ -19,7 +20,7 @@ import linear_attention_chunked_amd as lac
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-NAMES = ("dq", "dk", "dv", "deta", "dS0")
+NAMES = ("dq", "dk", "dv", "deta", "dS0", "dM0")
 
 
 def say(msg):
@@ -42,23 +43,28 @@ def make(B, H, L, dk, dv, dtype, seed, per_token=True, s0=True, dsf=True):
     return q, k, v, dout, eta, S0, dSf
 
 
-def run_gpu(q, k, v, dout, eta, eta_scalar, S0, dSf):
-    res = lac.bwd_chunked(dev(q), dev(k), dev(v), dev(dout), eta=dev(eta), eta_scalar=eta_scalar,
-                          S0=dev(S0), dS_final=dev(dSf))
+def run_gpu(q, k, v, dout, eta, eta_scalar, S0, dSf, beta=0.0, M0=None, dMf=None):
+    res = lac.bwd_chunked(dev(q), dev(k), dev(v), dev(dout), eta=dev(eta), eta_scalar=eta_scalar, beta=beta,
+                          S0=dev(S0), M0=dev(M0), dS_final=dev(dSf), dM_final=dev(dMf), need_dM0=beta != 0.0)
     torch.cuda.synchronize()
-    return [r.cpu() for r in res]
+    return [r.cpu() for r in res if r is not None]
 
 
-def run_oracle(q, k, v, dout, eta, eta_scalar, S0, dSf):
-    dq, dk_, dv_, deta, dS0, _ = oracle.token_causal_bwd(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(dout),
-                                                          W.to_f64(eta), eta_scalar, 0.0, W.to_f64(S0), None,
-                                                          W.to_f64(dSf))
-    return dq, dk_, dv_, deta, dS0
+def run_oracle(q, k, v, dout, eta, eta_scalar, S0, dSf, beta=0.0, M0=None, dMf=None):
+    dq, dk_, dv_, deta, dS0, dM0 = oracle.token_causal_bwd(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(dout),
+                                                            W.to_f64(eta), eta_scalar, beta, W.to_f64(S0),
+                                                            W.to_f64(M0), W.to_f64(dSf), W.to_f64(dMf))
+    return (dq, dk_, dv_, deta, dS0) + ((dM0,) if beta != 0.0 else ())
 
 
-def check(got, ref, dtype, what):
-    tol = {"dq": 1e-5, "dk": 1e-5, "dv": 1e-5, "deta": 1e-5, "dS0": 1e-5} if dtype == "f32" else \
-          {"dq": 1e-2, "dk": 1e-2, "dv": 1e-2, "deta": 1e-2, "dS0": 1e-4}
+def check(got, ref, dtype, what, momentum=False):
+    tol = {"dq": 1e-5, "dk": 1e-5, "dv": 1e-5, "deta": 1e-5, "dS0": 1e-5, "dM0": 1e-5} if dtype == "f32" else \
+          {"dq": 1e-2, "dk": 1e-2, "dv": 1e-2, "deta": 1e-2, "dS0": 1e-4, "dM0": 1e-4}
+    if momentum and dtype == "bf16":
+        # the momentum weights w(n) are folded into the bf16 value operand of
+        # the state update, one bf16 rounding per product: the states carry
+        # bf16-level error like every other output
+        tol["dS0"] = tol["dM0"] = 1e-2
     errs = {n: oracle.rel_l2(g.double(), r) for n, g, r in zip(NAMES, got, ref)}
     say(f"{what}: " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()))
     for n, e in errs.items():
@@ -86,6 +92,33 @@ def test_bwd_scalar_eta_no_states(dtype):
     eta = W.f32(0.05)
     check(run_gpu(q, k, v, dout, None, eta, None, None), run_oracle(q, k, v, dout, None, eta, None, None), dtype,
           f"bwd scalar eta {dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("beta", [0.9, 0.5])
+def test_bwd_momentum(dtype, beta):
+    """Momentum: the adjoint of m_t run as a reversed momentum forward from
+    the rescaled boundary states; M0 and dM_final given; dM0 checked too."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    beta = W.f32(beta)
+    q, k, v, dout, eta, S0, dSf = make(2, 2, 230, 64, 128, tdt, seed=int(beta * 100))
+    g = torch.Generator().manual_seed(9)
+    M0 = 0.01 * torch.randn(S0.shape, generator=g)
+    dMf = 0.05 * torch.randn(S0.shape, generator=g)
+    check(run_gpu(q, k, v, dout, eta, 0.0, S0, dSf, beta, M0, dMf),
+          run_oracle(q, k, v, dout, eta, 0.0, S0, dSf, beta, M0, dMf), dtype, f"bwd momentum {dtype} beta {beta}",
+          momentum=True)
+
+
+def test_bwd_momentum_segmented():
+    """Momentum on a long sequence of few heads (segmented forward passes
+    with the affine look-back, in reverse time)."""
+    q, k, v, dout, eta, S0, dSf = make(1, 2, 4500, 128, 128, torch.bfloat16, seed=78)
+    beta = W.f32(0.9)
+    assert lac.bwd_workspace_size(1, 2, 4500, 128, 128, beta=beta) > 0
+    check(run_gpu(q, k, v, dout, eta, 0.0, S0, dSf, beta, None, None),
+          run_oracle(q, k, v, dout, eta, 0.0, S0, dSf, beta, None, None), "bf16", "bwd momentum segmented",
+          momentum=True)
 
 
 def test_bwd_integer_exact():

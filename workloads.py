@@ -25,6 +25,7 @@ Workloads (shapes of the pages' settings):
   dual        TTT-Linear mini-batch dual form, B4 H16 L8192 d64, b 16 and 2048, W0 0.5 I
   decode      one recurrent token per sequence, B256 H16 d128, state S0 (and M0) carried in
   bwd         backward of lm-scale: its inputs plus cotangents dout, dS_final
+  bwd-momentum backward of momentum: its inputs plus cotangents (seeds 4005, 4006)
 """
 from __future__ import annotations
 
@@ -105,8 +106,9 @@ def gen_lm_scale(B=8, H=16, L=4096, d=128, chunk=64, seed_base=2000) -> TokenCau
 
 
 def gen_lm_scale_cotangents(B=8, H=16, L=4096, d=128, seed_base=2000):
-    """Cotangents for the LM-scale backward: dout ~ N(0,1)/sqrt(L) bf16
-    [B,H,L,d] (j = 5); dS_final ~ N(0, 0.02^2) fp32 [B,H,d,d] (j = 6)."""
+    """Cotangents for a backward workload (LM-scale by default; the momentum
+    workload uses its own seed base): dout ~ N(0,1)/sqrt(L) bf16 [B,H,L,d]
+    (j = 5); dS_final ~ N(0, 0.02^2) fp32 [B,H,d,d] (j = 6)."""
     dout = (_randn((B, H, L, d), seed_base + 5) / math.sqrt(L)).to(torch.bfloat16)
     dSf = _randn((B, H, d, d), seed_base + 6) * 0.02
     return dout, dSf
