@@ -200,6 +200,67 @@ def chunk_causal(q, k, v, eta=None, eta_scalar=0.0, S0=None, chunk=1024):
     return out, Wf
 
 
+# ------------------------------------------------------------ In-Place front end
+def inplace_gated_input(X, Wg, Wu):
+    """Input activation of the fast weight Wdown in the gated MLP ([P2]
+    paragraph on the Gated-MLP structure: Wup and Wgate stay fixed slow
+    weights, their output Z is what Wdown multiplies).  NumPy fp64:
+
+        Z = silu(X Wg^T) * (X Wu^T),   silu(a) = a / (1 + exp(-a))
+
+    X: [..., d_model]; Wg, Wu: [d_ff, d_model] (rows = output features)."""
+    X, Wg, Wu = _f64(X), _f64(Wg), _f64(Wu)
+    a = X @ Wg.T
+    b = X @ Wu.T
+    return a / (1.0 + np.exp(-a)) * b
+
+
+def lookahead_conv(X, c):
+    """The 1D convolution of the LM-aligned target ([P2] paragraph on the
+    LM-aligned objective: the target is built from the current and following
+    tokens so the update stores next-token information).  Depthwise, K taps
+    on tokens t .. t+K-1 of the same sequence, zero past its end:
+
+        Y[b, t] = sum_{j < K, t + j < L} c[j] * X[b, t + j]
+
+    X: [B, L, d]; c: [K, d]."""
+    X, c = _f64(X), _f64(c)
+    B, L, d = X.shape
+    K = c.shape[0]
+    Y = np.zeros_like(X)
+    for j in range(K):
+        Y[:, :L - j] += c[j] * X[:, j:]
+    return Y
+
+
+def lm_aligned_target(X, c, Wv):
+    """V-hat = lookahead_conv(X, c) Wv^T ([P2]: 1D convolution, then a
+    projection).  Wv: [d_model, d_model] (rows = output features)."""
+    return lookahead_conv(X, c) @ _f64(Wv).T
+
+
+def clip_scales(Z, V, chunk, eta, tau):
+    """Per-token learning rates with the update clipped ([P2] paragraph on
+    the limitations: a clipping mechanism keeps accumulated updates stable
+    over very long contexts).  For chunk i the update is
+    dW_i = eta Z_i^T V_i (formed explicitly here); it is scaled to Frobenius
+    norm at most tau:
+
+        s_i = min(1, tau / ||dW_i||_F)   (1 when dW_i = 0),  eta_t = eta s_i
+
+    Z: [B, L, d_ff]; V: [B, L, d_model].  Returns eta_t [B, L]."""
+    Z, V = _f64(Z), _f64(V)
+    B, L, _ = Z.shape
+    out = np.empty((B, L))
+    for b in range(B):
+        for c0 in range(0, L, chunk):
+            c1 = min(c0 + chunk, L)
+            nrm = float(np.linalg.norm(eta * (Z[b, c0:c1].T @ V[b, c0:c1])))
+            s = 1.0 if nrm == 0.0 or nrm <= tau else tau / nrm
+            out[b, c0:c1] = eta * s
+    return out
+
+
 # ============================================================ independent forms
 def momentum_weights(beta, n):
     """w_n = sum_{i=0..n} beta^i: weight of pair (s, t = s + n) under momentum

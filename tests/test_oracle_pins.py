@@ -582,3 +582,73 @@ def test_bwd_single_token_closed_form(oracle_mod):
     close(dk_[0, 0, 0], eta * (D @ vv))
     close(deta[0, 0, 0], kv @ D @ vv)
     close(dS0[0, 0], D)
+
+
+# ----------------------------------------------------------------- In-Place front end
+def test_gated_input_vs_torch(oracle_mod):
+    """Z = silu(X Wg^T) (X Wu^T) against torch's silu and linear in fp64, and
+    the closed forms silu(0) = 0, silu(a) -> a for large a."""
+    rng = np.random.default_rng(51)
+    X, Wg, Wu = rnd(2, 7, 6, rng=rng), rnd(5, 6, rng=rng), rnd(5, 6, rng=rng)
+    Z = oracle_mod.inplace_gated_input(X, Wg, Wu)
+    Xt = torch.tensor(X)
+    ref = torch.nn.functional.silu(torch.nn.functional.linear(Xt, torch.tensor(Wg))) * \
+        torch.nn.functional.linear(Xt, torch.tensor(Wu))
+    close(Z, ref.numpy(), 1e-13)
+    e = np.eye(3)
+    close(oracle_mod.inplace_gated_input(np.zeros((1, 3)), e, e), np.zeros((1, 3)))
+    big = oracle_mod.inplace_gated_input(np.array([[40.0, 0.0, 0.0]]), e, e)
+    close(big, np.array([[1600.0, 0.0, 0.0]]), 1e-12)
+
+
+def test_lookahead_conv_vs_torch(oracle_mod):
+    """Depthwise look-ahead convolution against torch.conv1d (groups = d,
+    right padding, reversed taps); K = 1 is an elementwise scale; a delta at
+    token t spreads only to tokens t-K+1 .. t of its own sequence."""
+    rng = np.random.default_rng(52)
+    B, L, d, K = 2, 11, 4, 3
+    X, c = rnd(B, L, d, rng=rng), rnd(K, d, rng=rng)
+    Y = oracle_mod.lookahead_conv(X, c)
+    xt = torch.nn.functional.pad(torch.tensor(X).transpose(1, 2), (0, K - 1))
+    w = torch.tensor(c).T.unsqueeze(1)                 # [d, 1, K]: tap j multiplies x[t + j]
+    ref = torch.nn.functional.conv1d(xt, w, groups=d).transpose(1, 2)
+    close(Y, ref.numpy(), 1e-13)
+    close(oracle_mod.lookahead_conv(X, c[:1]), c[0] * X)
+    delta = np.zeros((2, L, d))
+    delta[0, 5] = 1.0
+    Yd = oracle_mod.lookahead_conv(delta, c)
+    assert np.count_nonzero(Yd[1]) == 0
+    for t in range(L):
+        if 5 - K + 1 <= t <= 5:
+            close(Yd[0, t], c[5 - t])
+        else:
+            assert not np.any(Yd[0, t])
+
+
+def test_clip_scales(oracle_mod):
+    """Clipped per-token rates: the chunk update's norm by the Gram identity
+    ||Z^T V||_F^2 = sum_{s,t} (z_s . z_t)(v_s . v_t), a different computation;
+    clipped updates have norm tau; unclipped chunks keep eta; a zero chunk
+    keeps eta."""
+    rng = np.random.default_rng(53)
+    B, L, dff, dm, C, eta = 2, 23, 6, 5, 8, 0.3
+    Z, V = rnd(B, L, dff, rng=rng), rnd(B, L, dm, rng=rng)
+    Z[1, 16:] = 0.0                                     # last chunk of sequence 1 gives a zero update
+    norms = []
+    for b in range(B):
+        for c0 in range(0, L, C):
+            zs, vs = Z[b, c0:c0 + C], V[b, c0:c0 + C]
+            norms.append(eta * np.sqrt(max(float(np.sum((zs @ zs.T) * (vs @ vs.T))), 0.0)))
+    pos = sorted(n for n in norms if n > 0)
+    tau = 0.5 * (pos[len(pos) // 2 - 1] + pos[len(pos) // 2])   # between two chunk norms
+    e = oracle_mod.clip_scales(Z, V, C, eta, tau)
+    i = 0
+    for b in range(B):
+        for c0 in range(0, L, C):
+            s = e[b, c0:c0 + C]
+            assert np.all(s == s[0])
+            if norms[i] > tau:
+                close(s[0] * norms[i] / eta, tau)
+            else:
+                assert s[0] == eta
+            i += 1
