@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "dual_fwd_kernel": ("dual.hip", "common.h"),
     "dual_chain_kernel": ("dual.hip", "common.h"),
     "decode_kernel": ("decode.hip", "common.h"),
+    "fe_gemm_kernel": ("frontend.hip", "common.h"),
     "tcb_fwd_kernel+bwd_scale_kernels": ("tcb_fwd.hip", "bwd.hip", "common.h"),
 }
 
@@ -164,6 +165,25 @@ def setup_workload(name: str, dev: str):
                     tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
                     kernel="tcb_fwd_kernel+bwd_scale_kernels", inputs=None)
         return step, info
+    if name == "inplace-frontend":
+        T, dm, dff, taps, C = 32768, 2560, 9728, 4, 1024
+        X, Wg, Wu, cw, Wv = W.gen_inplace_frontend(T, dm, dff, taps, device=dev)
+        Z = torch.empty((1, T, dff), dtype=torch.bfloat16, device=dev)
+        V = torch.empty_like(X)
+        E = torch.empty((1, T), dtype=torch.float32, device=dev)
+
+        def step():
+            lac.inplace_gated_input(X, Wg, Wu, out=Z)
+            lac.inplace_lm_target(X, cw, Wv, out=V)
+            return lac.inplace_clip_eta(Z, V, chunk=C, eta=1e-3, tau=50.0, out=E)
+
+        # gated projection and target projection (the clipping norms are extra)
+        flop_alg = 2 * 2 * T * dm * dff + 2 * T * dm * dm
+        bytes_alg = (T * dm * 2 + 2 * dff * dm * 2 + dm * dm * 2 + taps * dm * 4   # X, weights
+                     + T * dff * 2 + T * dm * 2 + T * 4)                           # Z, V-hat, rates
+        info = dict(workload=name, T=T, d_model=dm, d_ff=dff, taps=taps, chunk=C, dtype="bf16", tokens=T,
+                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="fe_gemm_kernel", inputs=None)
+        return step, info
     if name in ("decode", "decode-momentum"):
         inp = W.gen_decode(beta=0.9 if name == "decode-momentum" else 0.0)
         B, H, _, dk = inp.q.shape
@@ -251,7 +271,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lm-scale",
                     help="lm-scale (default), small-f32, inplace-32k, inplace-128k, momentum, dual-b16, "
-                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum")
+                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, inplace-frontend")
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this many seconds of steps have run")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -14,6 +14,8 @@
  *   ttt_decode_step       one recurrent token per sequence (inference):
  *                         state update and readout with the state in HBM
  *   ttt_bwd_chunked       backward pass of the token-causal forward
+ *   ttt_inplace_*         In-Place TTT front end: gated input Z, LM-aligned
+ *                         target V-hat, clipped per-token rates
  *
  * Sources (cited by page title and paragraph or section):
  *  [P1] "KV 바인딩 기반 테스트 시간 학습은 사실상 선형 어텐션이다"
@@ -270,6 +272,55 @@ ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_
                              const float* dS_final, const float* dM_final,
                              void* dq, void* dk_out, void* dv_out, float* deta, float* dS0, float* dM0,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * In-Place TTT front end ([P2] "In-Place 테스트 시점 학습: LLM을 위한 원활한
+ * 동적 적응 프레임워크", aitrends.kr/articles/40879).  These produce the
+ * inputs of ttt_fwd_chunked in CHUNK_CAUSAL mode with q = k = Z, v = V-hat,
+ * S0 = Wdown and per-token eta.  All activations are bf16 and contiguous;
+ * weights use the row = output feature layout ([out, in], K contiguous).
+ *
+ * ttt_inplace_gated_input ([P2] paragraph on the Gated-MLP structure: Wgate
+ * and Wup are fixed slow weights, Wdown the fast weight that multiplies
+ * their output):
+ *     Z = silu(X Wg^T) * (X Wu^T),  silu(a) = a / (1 + exp(-a))
+ *   X [T, d_model], Wg, Wu [d_ff, d_model], Z [T, d_ff].  fp32 accumulation,
+ *   one rounding of Z to bf16.  Supported: d_model a multiple of 128, d_ff
+ *   a multiple of 128.  Z must not overlap the inputs.
+ *
+ * ttt_inplace_lm_target ([P2] paragraph on the LM-aligned objective: a 1D
+ * convolution over the current and following tokens, then a projection):
+ *     Y[b, t] = sum_{j < taps, t + j < L} conv_w[j] * X[b, t + j]   (depthwise)
+ *     V-hat = Y Wv^T
+ *   X, V-hat [B, L, d_model]; conv_w [taps, d_model] fp32 (1 <= taps <= 16);
+ *   Wv [d_model, d_model].  Y is kept in bf16 in `workspace`
+ *   (ttt_inplace_lm_target_workspace_size bytes).  Supported: d_model a
+ *   multiple of 256.
+ *
+ * ttt_inplace_clip_eta ([P2] paragraph on the limitations: clipping keeps
+ * accumulated updates stable): for each chunk i of each sequence,
+ *     eta_out[t] = eta * min(1, tau / ||eta Z_i^T V_i||_F)   (t in chunk i)
+ *   computed from the chunk's Gram products (Z_i Z_i^T, V_i V_i^T), without
+ *   forming the d_ff x d_model update.  Z [B, L, d_ff], V-hat [B, L, d_model],
+ *   eta_out [B, L] fp32; tau > 0.  workspace: ttt_inplace_clip_eta_workspace_size
+ *   bytes.  Supported: d_ff, d_model multiples of 128.
+ *
+ * Errors (before anything is enqueued): TTT_ERR_NULL, TTT_ERR_SHAPE,
+ * TTT_ERR_VALUE, TTT_ERR_ALIGN (16 bytes), TTT_ERR_UNSUPPORTED,
+ * TTT_ERR_WORKSPACE, TTT_ERR_ALIAS (an output overlaps an input or the
+ * workspace); TTT_ERR_HIP if a launch fails.  All pointers are caller-owned
+ * device memory; stream is a hipStream_t (NULL: default stream).
+ */
+ttt_status_t ttt_inplace_gated_input(int32_t T, int32_t d_model, int32_t d_ff, const void* X, const void* Wg,
+                                     const void* Wu, void* Z, void* stream);
+ttt_status_t ttt_inplace_lm_target_workspace_size(int32_t B, int32_t L, int32_t d_model, size_t* bytes);
+ttt_status_t ttt_inplace_lm_target(int32_t B, int32_t L, int32_t d_model, int32_t taps, const void* X,
+                                   const float* conv_w, const void* Wv, void* Vhat, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+ttt_status_t ttt_inplace_clip_eta_workspace_size(int32_t B, int32_t L, int32_t chunk, size_t* bytes);
+ttt_status_t ttt_inplace_clip_eta(int32_t B, int32_t L, int32_t d_ff, int32_t d_model, int32_t chunk,
+                                  const void* Z, const void* Vhat, float eta, float tau, float* eta_out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* ttt_status_string(ttt_status_t status);

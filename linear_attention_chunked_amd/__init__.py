@@ -12,6 +12,9 @@ Entry points (same names as the C ABI):
     dual_form_fwd(q, k, v, W0, ...)    TTT-Linear mini-batch dual form
     decode_step(q, k, v, S, M, ...)    one recurrent token, state updated in place
     bwd_chunked(q, k, v, dout, ...)    backward of the token-causal forward
+    inplace_gated_input(X, Wg, Wu)     In-Place front end: Z = silu(X Wg^T) (X Wu^T)
+    inplace_lm_target(X, conv_w, Wv)   In-Place front end: V-hat = conv(X) Wv^T
+    inplace_clip_eta(Z, Vhat, ...)     In-Place front end: clipped per-token rates
 """
 from __future__ import annotations
 
@@ -87,6 +90,18 @@ def load_library():
     lib.ttt_bwd_chunked.argtypes = [i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, f32, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.ttt_bwd_chunked.restype = ctypes.c_int
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    lib.ttt_inplace_gated_input.argtypes = [i32, i32, i32, _vp, _vp, _vp, _vp, _vp]
+    lib.ttt_inplace_gated_input.restype = ctypes.c_int
+    lib.ttt_inplace_lm_target_workspace_size.argtypes = [i32, i32, i32, sz]
+    lib.ttt_inplace_lm_target_workspace_size.restype = ctypes.c_int
+    lib.ttt_inplace_lm_target.argtypes = [i32, i32, i32, i32, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.ttt_inplace_lm_target.restype = ctypes.c_int
+    lib.ttt_inplace_clip_eta_workspace_size.argtypes = [i32, i32, i32, sz]
+    lib.ttt_inplace_clip_eta_workspace_size.restype = ctypes.c_int
+    lib.ttt_inplace_clip_eta.argtypes = [i32, i32, i32, i32, i32, _vp, _vp, f32, f32, _vp, _vp, ctypes.c_size_t,
+                                         _vp]
+    lib.ttt_inplace_clip_eta.restype = ctypes.c_int
     lib.ttt_status_string.argtypes = [ctypes.c_int]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_fwd_args_size.argtypes = []
@@ -338,5 +353,67 @@ def bwd_chunked(q, k, v, dout, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M
     return dq, dk_, dv_, deta, dS0, dM0
 
 
-__all__ = ["fwd_chunked", "chunk_state_scan", "dual_form_fwd", "decode_step", "bwd_chunked", "bwd_workspace_size", "load_library", "TTTError",
+def _bf16_contig(*pairs):
+    for t, nm in pairs:
+        if t.dtype != torch.bfloat16 or not t.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous bf16")
+
+
+def inplace_gated_input(X, Wg, Wu, *, out=None, stream=None):
+    """Z = silu(X Wg^T) * (X Wu^T) (``ttt_inplace_gated_input``).
+
+    X: [..., d_model] bf16; Wg, Wu: [d_ff, d_model] bf16.  Returns Z [..., d_ff]."""
+    lib = load_library()
+    _require_gpu(X, Wg, Wu, out)
+    _bf16_contig((X, "X"), (Wg, "Wg"), (Wu, "Wu"))
+    d_ff, d_model = Wg.shape
+    if Wu.shape != Wg.shape or X.shape[-1] != d_model:
+        raise ValueError("Wg, Wu must be [d_ff, d_model] and X [..., d_model]")
+    T = X.numel() // d_model
+    if out is None:
+        out = torch.empty(X.shape[:-1] + (d_ff,), dtype=torch.bfloat16, device=X.device)
+    _check(lib.ttt_inplace_gated_input(T, d_model, d_ff, _ptr(X), _ptr(Wg), _ptr(Wu), _ptr(out), _stream(stream)))
+    return out
+
+
+def inplace_lm_target(X, conv_w, Wv, *, out=None, stream=None):
+    """V-hat = lookahead_conv(X, conv_w) Wv^T (``ttt_inplace_lm_target``).
+
+    X: [B, L, d_model] bf16; conv_w: [taps, d_model] fp32; Wv: [d_model, d_model] bf16."""
+    lib = load_library()
+    _require_gpu(X, conv_w, Wv, out)
+    _bf16_contig((X, "X"), (Wv, "Wv"))
+    if conv_w.dtype != torch.float32 or not conv_w.is_contiguous():
+        raise ValueError("conv_w must be contiguous fp32")
+    B, L, d = X.shape
+    if out is None:
+        out = torch.empty_like(X)
+    ws = ctypes.c_size_t(0)
+    _check(lib.ttt_inplace_lm_target_workspace_size(B, L, d, ctypes.byref(ws)))
+    w = torch.empty(ws.value, dtype=torch.uint8, device=X.device)
+    _check(lib.ttt_inplace_lm_target(B, L, d, conv_w.shape[0], _ptr(X), _ptr(conv_w), _ptr(Wv), _ptr(out), _ptr(w),
+                                     ws.value, _stream(stream)))
+    return out
+
+
+def inplace_clip_eta(Z, Vhat, *, chunk, eta, tau, out=None, stream=None):
+    """Per-token rates eta * min(1, tau / ||eta Z_i^T V_i||_F) per chunk
+    (``ttt_inplace_clip_eta``).  Z: [B, L, d_ff], Vhat: [B, L, d_model] bf16.
+    Returns fp32 [B, L]."""
+    lib = load_library()
+    _require_gpu(Z, Vhat, out)
+    _bf16_contig((Z, "Z"), (Vhat, "Vhat"))
+    B, L, d_ff = Z.shape
+    d_model = Vhat.shape[-1]
+    if out is None:
+        out = torch.empty((B, L), dtype=torch.float32, device=Z.device)
+    ws = ctypes.c_size_t(0)
+    _check(lib.ttt_inplace_clip_eta_workspace_size(B, L, int(chunk), ctypes.byref(ws)))
+    w = torch.empty(max(ws.value, 16), dtype=torch.uint8, device=Z.device)
+    _check(lib.ttt_inplace_clip_eta(B, L, d_ff, d_model, int(chunk), _ptr(Z), _ptr(Vhat), float(eta), float(tau),
+                                    _ptr(out), _ptr(w), ws.value, _stream(stream)))
+    return out
+
+
+__all__ = ["inplace_gated_input", "inplace_lm_target", "inplace_clip_eta", "fwd_chunked", "chunk_state_scan", "dual_form_fwd", "decode_step", "bwd_chunked", "bwd_workspace_size", "load_library", "TTTError",
            "FwdArgs", "LIB_PATH"]

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <initializer_list>
+#include <utility>
 
 #include "../../include/ttt.h"
 #include "internal.h"
@@ -312,6 +314,123 @@ ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_
     p.dM0 = dM0;
     p.workspace = workspace;
     return from_hip(ttt::launch_bwd(p, reinterpret_cast<hipStream_t>(stream)));
+}
+
+namespace {
+// the output span [o, o + no) overlaps none of the inputs
+bool disjoint(const void* o, size_t no, std::initializer_list<std::pair<const void*, size_t>> ins) {
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(o), a1 = a0 + no;
+    for (const auto& in : ins) {
+        if (!in.first) continue;
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(in.first);
+        if (overlap(a0, a1, b0, b0 + in.second)) return false;
+    }
+    return true;
+}
+constexpr int kMaxConvTaps = 16;
+}  // namespace
+
+ttt_status_t ttt_inplace_gated_input(int32_t T, int32_t d_model, int32_t d_ff, const void* X, const void* Wg,
+                                     const void* Wu, void* Z, void* stream) {
+    if (T < 1 || d_model < 1 || d_ff < 1) return TTT_ERR_SHAPE;
+    if (!X || !Wg || !Wu || !Z) return TTT_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Wg) || !aligned16(Wu) || !aligned16(Z)) return TTT_ERR_ALIGN;
+    if (!ttt::fe_gemm_supported(d_model, 2 * d_ff)) return TTT_ERR_UNSUPPORTED;
+    const size_t nx = (size_t)T * d_model * 2, nw = (size_t)d_ff * d_model * 2, nz = (size_t)T * d_ff * 2;
+    if (!disjoint(Z, nz, {{X, nx}, {Wg, nw}, {Wu, nw}})) return TTT_ERR_ALIAS;
+    ttt::FeGemmParams p{};
+    p.A0 = Wg;
+    p.A1 = Wu;
+    p.B = X;
+    p.out = Z;
+    p.arows = 2 * d_ff;
+    p.K = d_model;
+    p.T = T;
+    p.ldb = d_model;
+    p.ldo = d_ff;
+    return from_hip(ttt::launch_fe_gemm(p, true, reinterpret_cast<hipStream_t>(stream)));
+}
+
+ttt_status_t ttt_inplace_lm_target_workspace_size(int32_t B, int32_t L, int32_t d_model, size_t* bytes) {
+    if (!bytes) return TTT_ERR_NULL;
+    if (B < 1 || L < 1 || d_model < 1) return TTT_ERR_SHAPE;
+    *bytes = (size_t)B * L * d_model * 2;
+    return TTT_OK;
+}
+
+ttt_status_t ttt_inplace_lm_target(int32_t B, int32_t L, int32_t d_model, int32_t taps, const void* X,
+                                   const float* conv_w, const void* Wv, void* Vhat, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (B < 1 || L < 1 || d_model < 1) return TTT_ERR_SHAPE;
+    if (taps < 1 || taps > kMaxConvTaps) return TTT_ERR_VALUE;
+    if (!X || !conv_w || !Wv || !Vhat) return TTT_ERR_NULL;
+    if (!aligned16(X) || !aligned16(conv_w) || !aligned16(Wv) || !aligned16(Vhat)) return TTT_ERR_ALIGN;
+    if (!ttt::fe_gemm_supported(d_model, d_model)) return TTT_ERR_UNSUPPORTED;
+    const size_t nx = (size_t)B * L * d_model * 2;
+    if (!workspace || workspace_bytes < nx) return TTT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TTT_ERR_ALIGN;
+    const size_t nw = (size_t)d_model * d_model * 2, nc = (size_t)taps * d_model * 4;
+    if (!disjoint(Vhat, nx, {{X, nx}, {conv_w, nc}, {Wv, nw}, {workspace, nx}})) return TTT_ERR_ALIAS;
+    if (!disjoint(workspace, nx, {{X, nx}, {conv_w, nc}, {Wv, nw}})) return TTT_ERR_ALIAS;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    ttt::FeConvParams c{};
+    c.X = X;
+    c.w = conv_w;
+    c.Y = workspace;
+    c.B = B;
+    c.L = L;
+    c.d = d_model;
+    c.K = taps;
+    hipError_t e = ttt::launch_fe_conv(c, st);
+    if (e != hipSuccess) return from_hip(e);
+    ttt::FeGemmParams p{};
+    p.A0 = Wv;
+    p.A1 = nullptr;
+    p.B = workspace;
+    p.out = Vhat;
+    p.arows = d_model;
+    p.K = d_model;
+    p.T = B * L;
+    p.ldb = d_model;
+    p.ldo = d_model;
+    return from_hip(ttt::launch_fe_gemm(p, false, st));
+}
+
+ttt_status_t ttt_inplace_clip_eta_workspace_size(int32_t B, int32_t L, int32_t chunk, size_t* bytes) {
+    if (!bytes) return TTT_ERR_NULL;
+    if (B < 1 || L < 1 || chunk < 1) return TTT_ERR_SHAPE;
+    *bytes = (size_t)B * ((L + chunk - 1) / chunk) * ttt::fe_gram_pairs(chunk) * sizeof(float);
+    return TTT_OK;
+}
+
+ttt_status_t ttt_inplace_clip_eta(int32_t B, int32_t L, int32_t d_ff, int32_t d_model, int32_t chunk, const void* Z,
+                                  const void* Vhat, float eta, float tau, float* eta_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    size_t need = 0;
+    ttt_status_t s = ttt_inplace_clip_eta_workspace_size(B, L, chunk, &need);
+    if (s != TTT_OK) return s;
+    if (d_ff < 1 || d_model < 1) return TTT_ERR_SHAPE;
+    if (!(tau > 0.f) || !(eta == eta)) return TTT_ERR_VALUE;
+    if (!Z || !Vhat || !eta_out) return TTT_ERR_NULL;
+    if (!aligned16(Z) || !aligned16(Vhat) || !aligned16(eta_out)) return TTT_ERR_ALIGN;
+    if (d_ff % 128 != 0 || d_model % 128 != 0) return TTT_ERR_UNSUPPORTED;
+    if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
+    const size_t nz = (size_t)B * L * d_ff * 2, nv = (size_t)B * L * d_model * 2, ne = (size_t)B * L * 4;
+    if (!disjoint(eta_out, ne, {{Z, nz}, {Vhat, nv}, {workspace, need}})) return TTT_ERR_ALIAS;
+    if (!disjoint(workspace, need, {{Z, nz}, {Vhat, nv}})) return TTT_ERR_ALIAS;
+    ttt::FeGramParams p{};
+    p.Z = Z;
+    p.V = Vhat;
+    p.B = B;
+    p.L = L;
+    p.chunk = chunk;
+    p.dz = d_ff;
+    p.dv = d_model;
+    p.eta = eta;
+    p.tau = tau;
+    p.partial = reinterpret_cast<float*>(workspace);
+    p.eta_out = eta_out;
+    return from_hip(ttt::launch_fe_clip(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32_t dtype, const void* q,

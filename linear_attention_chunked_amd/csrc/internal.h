@@ -127,6 +127,37 @@ struct BwdParams {
     float* dM0;
     void* workspace;
 };
+// In-Place front end (bf16).  Projections: out[t][f] from weight rows A
+// (K elements each; gated: A0 = Wgate, A1 = Wup, arows = 2 d_ff) and token
+// rows B (row stride ldb); out row stride ldo.
+struct FeGemmParams {
+    const void* A0;
+    const void* A1;
+    const void* B;
+    void* out;
+    int arows, K, T;
+    int64_t ldb, ldo;
+};
+struct FeConvParams {
+    const void* X;      // [B, L, d] bf16
+    const float* w;     // [K, d]
+    void* Y;            // [B, L, d] bf16
+    int B, L, d, K;
+};
+struct FeGramParams {
+    const void* Z;      // [B, L, dz] bf16
+    const void* V;      // [B, L, dv] bf16
+    int B, L, chunk, dz, dv, ntiles;
+    float eta, tau;
+    float* partial;     // [B, chunks, pairs]
+    float* eta_out;     // [B, L]
+};
+bool fe_gemm_supported(int K, int nfeat_rows);
+hipError_t launch_fe_gemm(const FeGemmParams& p, bool gated, hipStream_t stream);
+hipError_t launch_fe_conv(const FeConvParams& p, hipStream_t stream);
+int fe_gram_pairs(int chunk);
+hipError_t launch_fe_clip(const FeGramParams& p, hipStream_t stream);
+
 bool bwd_supported(int dtype, int dk, int dv);
 size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype, bool momentum);
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);

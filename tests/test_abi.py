@@ -184,6 +184,26 @@ def test_bwd_rejects_before_launch(lib):
     assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, ctypes.c_float(0.0), None) == ERR_NULL
 
 
+def test_frontend_rejects_before_launch(lib):
+    n = 1 << 24
+    g = lib.ttt_inplace_gated_input
+    assert g(0, 256, 256, FAKE, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, None) == ERR_SHAPE
+    assert g(64, 256, 256, None, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, None) == ERR_NULL
+    assert g(64, 256, 256, FAKE + 4, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, None) == ERR_ALIGN
+    assert g(64, 200, 256, FAKE, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, None) == ERR_UNSUP   # d_model % 128
+    assert g(64, 256, 256, FAKE, FAKE + n, FAKE + 2 * n, FAKE + 256, None) == ERR_ALIAS     # Z inside X
+    t = lib.ttt_inplace_lm_target
+    assert t(1, 64, 256, 0, FAKE, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, FAKE + 4 * n, n, None) == ERR_VALUE
+    assert t(1, 64, 256, 17, FAKE, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, FAKE + 4 * n, n, None) == ERR_VALUE
+    assert t(1, 64, 384, 4, FAKE, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, FAKE + 4 * n, n, None) == ERR_UNSUP
+    assert t(1, 64, 256, 4, FAKE, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, FAKE + 4 * n, 16, None) == ERR_WS
+    c = lib.ttt_inplace_clip_eta
+    assert c(1, 64, 256, 256, 64, FAKE, FAKE + n, ctypes.c_float(0.1), ctypes.c_float(0.0), FAKE + 2 * n,
+             FAKE + 3 * n, n, None) == ERR_VALUE                                            # tau must be > 0
+    assert c(1, 64, 256, 256, 64, FAKE, FAKE + n, ctypes.c_float(0.1), ctypes.c_float(1.0), FAKE + 2 * n,
+             None, 0, None) == ERR_WS
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 1, 64, 64)

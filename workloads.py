@@ -26,6 +26,7 @@ Workloads (shapes of the pages' settings):
   decode      one recurrent token per sequence, B256 H16 d128, state S0 (and M0) carried in
   bwd         backward of lm-scale: its inputs plus cotangents dout, dS_final
   bwd-momentum backward of momentum: its inputs plus cotangents (seeds 4005, 4006)
+  inplace-frontend  gated input, LM-aligned target and clipped rates, T 32768, d_model 2560, d_ff 9728
 """
 from __future__ import annotations
 
@@ -155,6 +156,29 @@ def gen_inplace(L=32768, d_ff=9728, d_model=2560, chunk=1024, gen_block=1024, ou
 
 
 # ------------------------------------------------------------------ momentum
+def gen_inplace_frontend(T=32768, d_model=2560, d_ff=9728, taps=4, seed_base=9000, device="cpu"):
+    """In-Place front end: X ~ N(0,1) bf16 [1, T, d_model]; Wg, Wu ~ N(0, 1/d_model)
+    bf16 [d_ff, d_model] (j = 1, 2); conv_w ~ N(0, 0.5^2) fp32 [taps, d_model]
+    (j = 3); Wv ~ N(0, 1/d_model) bf16 [d_model, d_model] (j = 4).  Drawn in
+    row blocks so a host never holds an fp32 copy of a whole large tensor;
+    ``device`` receives the bf16 tensors."""
+    def big(shape, seed, scale):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        g = _gen(seed)
+        rows = shape[-2]
+        flat = out.view(-1, shape[-1])
+        for r0 in range(0, flat.shape[0], 4096):
+            r1 = min(r0 + 4096, flat.shape[0])
+            flat[r0:r1].copy_((torch.randn((r1 - r0, shape[-1]), generator=g) * scale).to(torch.bfloat16))
+        return out
+    X = big((1, T, d_model), seed_base + 0, 1.0)
+    Wg = big((d_ff, d_model), seed_base + 1, d_model ** -0.5)
+    Wu = big((d_ff, d_model), seed_base + 2, d_model ** -0.5)
+    conv_w = (_randn((taps, d_model), seed_base + 3) * 0.5).to(device)
+    Wv = big((d_model, d_model), seed_base + 4, d_model ** -0.5)
+    return X, Wg, Wu, conv_w, Wv
+
+
 def gen_momentum(B=4, H=8, L=16384, d=128, chunk=128, seed_base=4000) -> TokenCausalInputs:
     """bf16 q,k,v ~ N(0,1)/sqrt(d); eta 0.05; beta 0.9; S0 = M0 = 0."""
     s = 1.0 / math.sqrt(d)
