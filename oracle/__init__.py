@@ -261,6 +261,78 @@ def clip_scales(Z, V, chunk, eta, tau):
     return out
 
 
+# ------------------------------------------------------ nonlinear fast weights
+def swiglu_apply(X, W1, W3, W2):
+    """The SwiGLU fast-weight MLP applied to token rows ([P5] section on the
+    core idea, row "nonlinear fast weights"; [P4] section on the
+    hidden state and update rule: the state is the weights of a small model):
+
+        f_W(x) = W2 (silu(W1 x) * (W3 x))
+
+    X: [n, d]; W1, W3: [m, d]; W2: [d, m] (rows = output features)."""
+    H1 = X @ W1.T
+    H3 = X @ W3.T
+    return (H1 / (1.0 + np.exp(-H1)) * H3) @ W2.T
+
+
+def swiglu_fast_weight(q, k, v, W1, W3, W2, eta=None, eta_scalar=0.0, chunk=2048, loss="dot"):
+    """Large-chunk SwiGLU fast weight, chunk-causal ([P5] sections on the
+    core idea: the fast weights take one update per large chunk, the chunk's
+    tokens acting as one big batch; [P4] section on the update rule:
+    W_t = W_{t-1} - eta grad_W l, output from the model; [P2] paragraph on the
+    chunk-wise update: chunk i reads the weights left by chunks < i).
+    For chunk i, with the weights W = (W1, W3, W2) after chunks < i:
+
+        O_i = f_W(Q_i)
+        W  <- W - grad_W  sum_{t in i} eta_t l_t(W)
+
+    l_t is the inner loss of token t on its key / value pair:
+        loss="dot": l_t = -<f_W(k_t), v_t>       (key-value binding; for a
+                     linear f it is the linear-attention update W += eta k^T v)
+        loss="mse": l_t = 1/2 ||f_W(k_t) - v_t||^2  (reconstruction)
+    The gradient is taken by the chain rule through the MLP, written out:
+        H1 = K W1^T, H3 = K W3^T, S = silu(H1), A = S * H3, Y = A W2^T
+        dY = diag(eta) dl/dY        (-V, or Y - V)
+        dW2 = dY^T A,  dA = dY W2
+        dH3 = dA * S,  dH1 = dA * H3 * silu'(H1),
+            silu'(h) = sigma(h) (1 + h (1 - sigma(h)))
+        dW1 = dH1^T K, dW3 = dH3^T K
+    q, k, v: [B, H, L, d]; W1, W3: [B, H, m, d]; W2: [B, H, d, m]; eta:
+    [B, H, L] or None (then eta_scalar).  NumPy fp64.
+    Returns (out [B, H, L, d], W1_final, W3_final, W2_final)."""
+    if loss not in ("dot", "mse"):
+        raise ValueError("loss must be 'dot' or 'mse'")
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, L, d = q.shape
+    eta = _f64(eta)
+    W1f, W3f, W2f = _f64(W1).copy(), _f64(W3).copy(), _f64(W2).copy()
+    out = np.empty((B, H, L, v.shape[-1]))
+    for b in range(B):
+        for h in range(H):
+            W1c, W3c, W2c = W1f[b, h], W3f[b, h], W2f[b, h]
+            for c0 in range(0, L, chunk):
+                c1 = min(c0 + chunk, L)
+                out[b, h, c0:c1] = swiglu_apply(q[b, h, c0:c1], W1c, W3c, W2c)
+                K, V = k[b, h, c0:c1], v[b, h, c0:c1]
+                e = eta[b, h, c0:c1] if eta is not None else np.full(c1 - c0, eta_scalar)
+                H1 = K @ W1c.T
+                H3 = K @ W3c.T
+                sg = 1.0 / (1.0 + np.exp(-H1))
+                S = H1 * sg
+                A = S * H3
+                Y = A @ W2c.T
+                G = -V if loss == "dot" else Y - V
+                dY = e[:, None] * G
+                dW2 = dY.T @ A
+                dA = dY @ W2c
+                dH3 = dA * S
+                dH1 = dA * H3 * sg * (1.0 + H1 * (1.0 - sg))
+                W1c -= dH1.T @ K
+                W3c -= dH3.T @ K
+                W2c -= dW2
+    return out, W1f, W3f, W2f
+
+
 # ============================================================ independent forms
 def momentum_weights(beta, n):
     """w_n = sum_{i=0..n} beta^i: weight of pair (s, t = s + n) under momentum

@@ -652,3 +652,130 @@ def test_clip_scales(oracle_mod):
             else:
                 assert s[0] == eta
             i += 1
+
+
+# ------------------------------------------------------ nonlinear fast weights
+def _swiglu_case(rng, B=1, H=2, L=13, d=4, m=6, scale=0.4):
+    q, k, v = rnd(B, H, L, d, rng=rng), rnd(B, H, L, d, rng=rng), rnd(B, H, L, d, rng=rng)
+    W1, W3 = scale * rnd(B, H, m, d, rng=rng), scale * rnd(B, H, m, d, rng=rng)
+    W2 = scale * rnd(B, H, d, m, rng=rng)
+    eta = rng.uniform(0.02, 0.2, (B, H, L))
+    return q, k, v, W1, W3, W2, eta
+
+
+def _torch_f(x, W1, W3, W2):
+    F = torch.nn.functional
+    return F.linear(F.silu(F.linear(x, W1)) * F.linear(x, W3), W2)
+
+
+def _torch_inner_loss(x, y, W1, W3, W2, e, loss):
+    f = _torch_f(x, W1, W3, W2)
+    per = -(f * y).sum(-1) if loss == "dot" else 0.5 * ((f - y) ** 2).sum(-1)
+    return (e * per).sum()
+
+
+@pytest.mark.parametrize("loss", ["dot", "mse"])
+def test_swiglu_chunk_step_matches_autograd(oracle_mod, loss):
+    """One whole-sequence chunk: the output is the MLP at the initial weights
+    (torch.nn.functional layers), and the final weights are one
+    torch.optim.SGD step (lr 1) on sum_t eta_t l_t by autograd."""
+    rng = np.random.default_rng(61)
+    q, k, v, W1, W3, W2, eta = _swiglu_case(rng)
+    out, W1f, W3f, W2f = oracle_mod.swiglu_fast_weight(q, k, v, W1, W3, W2, eta=eta, chunk=64, loss=loss)
+    for h in range(2):
+        ws = [torch.tensor(W[0, h], requires_grad=True) for W in (W1, W3, W2)]
+        close(out[0, h], _torch_f(torch.tensor(q[0, h]), *ws).detach().numpy(), 1e-12)
+        opt = torch.optim.SGD(ws, lr=1.0)
+        opt.zero_grad()
+        _torch_inner_loss(torch.tensor(k[0, h]), torch.tensor(v[0, h]), *ws, torch.tensor(eta[0, h]),
+                          loss).backward()
+        opt.step()
+        for got, w in zip((W1f, W3f, W2f), ws):
+            close(got[0, h], w.detach().numpy(), 1e-12)
+
+
+@pytest.mark.parametrize("loss", ["dot", "mse"])
+def test_swiglu_per_token_chunks_are_sequential_sgd(oracle_mod, loss):
+    """chunk = 1: read each token with the weights left by the earlier ones,
+    then take an SGD step on that token alone (autograd loop); chunk = 4 with
+    a scalar eta: the same loop stepping on groups of four tokens."""
+    rng = np.random.default_rng(62)
+    q, k, v, W1, W3, W2, eta = _swiglu_case(rng, L=9)
+    for chunk, e in ((1, eta), (4, None)):
+        es = eta if e is not None else np.full(eta.shape, 0.07)
+        out, W1f, W3f, W2f = oracle_mod.swiglu_fast_weight(q, k, v, W1, W3, W2, eta=e, eta_scalar=0.07,
+                                                           chunk=chunk, loss=loss)
+        for h in range(2):
+            ws = [torch.tensor(W[0, h], requires_grad=True) for W in (W1, W3, W2)]
+            opt = torch.optim.SGD(ws, lr=1.0)
+            for c0 in range(0, 9, chunk):
+                sl = slice(c0, c0 + chunk)
+                with torch.no_grad():
+                    close(out[0, h, sl], _torch_f(torch.tensor(q[0, h, sl]), *ws).numpy(), 1e-11)
+                opt.zero_grad()
+                _torch_inner_loss(torch.tensor(k[0, h, sl]), torch.tensor(v[0, h, sl]), *ws,
+                                  torch.tensor(es[0, h, sl]), loss).backward()
+                opt.step()
+            for got, w in zip((W1f, W3f, W2f), ws):
+                close(got[0, h], w.detach().numpy(), 1e-11)
+
+
+def test_swiglu_gradient_finite_differences(oracle_mod):
+    """The weight change of one chunk equals minus the gradient of
+    sum_t eta_t l_t, checked by central differences of that loss (computed
+    from swiglu_apply) along random directions of each weight."""
+    rng = np.random.default_rng(63)
+    q, k, v, W1, W3, W2, eta = _swiglu_case(rng, H=1, L=7)
+    K, V, e = k[0, 0], v[0, 0], eta[0, 0]
+    Ws = [W1[0, 0], W3[0, 0], W2[0, 0]]
+    for loss in ("dot", "mse"):
+        _, W1f, W3f, W2f = oracle_mod.swiglu_fast_weight(q, k, v, W1, W3, W2, eta=eta, chunk=7, loss=loss)
+        grads = [Ws[0] - W1f[0, 0], Ws[1] - W3f[0, 0], Ws[2] - W2f[0, 0]]
+
+        def L_of(ws):
+            f = oracle_mod.swiglu_apply(K, *ws)
+            per = -(f * V).sum(-1) if loss == "dot" else 0.5 * ((f - V) ** 2).sum(-1)
+            return float((e * per).sum())
+
+        for i in range(3):
+            u = rng.standard_normal(Ws[i].shape)
+            hstep = 1e-5
+            wp = [w.copy() for w in Ws]
+            wm = [w.copy() for w in Ws]
+            wp[i] += hstep * u
+            wm[i] -= hstep * u
+            fd = (L_of(wp) - L_of(wm)) / (2 * hstep)
+            an = float(np.sum(grads[i] * u))
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(an)), (loss, i, fd, an)
+
+
+def test_swiglu_chunk_properties(oracle_mod):
+    """Chunk-causal structure: permuting the tokens inside a chunk permutes
+    that chunk's outputs and leaves the others and the final weights
+    unchanged (one update per chunk, a sum over its tokens); changing the
+    values of the last chunk changes no output; eta = 0 keeps the weights and
+    reads every token with W0; W1 = 0 gives zero output."""
+    rng = np.random.default_rng(64)
+    q, k, v, W1, W3, W2, eta = _swiglu_case(rng, L=12)
+    C = 4
+    for loss in ("dot", "mse"):
+        ref = oracle_mod.swiglu_fast_weight(q, k, v, W1, W3, W2, eta=eta, chunk=C, loss=loss)
+        perm = np.arange(12)
+        perm[4:8] = perm[4:8][[2, 0, 3, 1]]
+        got = oracle_mod.swiglu_fast_weight(q[:, :, perm], k[:, :, perm], v[:, :, perm], W1, W3, W2,
+                                            eta=eta[:, :, perm], chunk=C, loss=loss)
+        close(got[0], ref[0][:, :, perm], 1e-12)
+        for a, b in zip(got[1:], ref[1:]):
+            close(a, b, 1e-12)
+        v2 = v.copy()
+        v2[:, :, 8:] += 1.0
+        got = oracle_mod.swiglu_fast_weight(q, k, v2, W1, W3, W2, eta=eta, chunk=C, loss=loss)
+        close(got[0], ref[0], 0.0)
+        assert not np.allclose(got[3], ref[3])
+    out, W1f, W3f, W2f = oracle_mod.swiglu_fast_weight(q, k, v, W1, W3, W2, eta_scalar=0.0, chunk=C)
+    for h in range(2):
+        close(out[0, h], oracle_mod.swiglu_apply(q[0, h], W1[0, h], W3[0, h], W2[0, h]), 1e-14)
+    close(W1f, W1, 0.0)
+    close(W2f, W2, 0.0)
+    out, _, _, _ = oracle_mod.swiglu_fast_weight(q, k, v, 0 * W1, W3, W2, eta_scalar=0.0, chunk=C)
+    close(out, np.zeros_like(out), 0.0)
