@@ -49,6 +49,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ("decode.hip", "common.h"),
     "fe_gemm_kernel": ("frontend.hip", "common.h"),
     "tcb_fwd_kernel+bwd_scale_kernels": ("tcb_fwd.hip", "bwd.hip", "common.h"),
+    "sw_fwd+sw_out+sw_bwda+sw_upd": ("swiglu.hip", "common.h"),
 }
 
 
@@ -184,6 +185,32 @@ def setup_workload(name: str, dev: str):
         info = dict(workload=name, T=T, d_model=dm, d_ff=dff, taps=taps, chunk=C, dtype="bf16", tokens=T,
                     bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="fe_gemm_kernel", inputs=None)
         return step, info
+    if name in ("swiglu", "swiglu-mse"):
+        loss = "mse" if name == "swiglu-mse" else "dot"
+        inp = W.gen_swiglu(loss=loss, device=dev)
+        B, H, L, dk = inp.q.shape
+        dv, m, C = inp.v.shape[-1], inp.W1.shape[-2], inp.chunk
+        W1, W3, W2 = inp.W1.clone(), inp.W3.clone(), inp.W2.clone()
+        out = torch.empty_like(inp.v)
+        ws = torch.empty(lac.swiglu_workspace_size(B, H, L, dk, dv, m, C), dtype=torch.uint8, device=dev)
+
+        def step():
+            # every step starts from W0 (the call updates the weights in place)
+            W1.copy_(inp.W1)
+            W3.copy_(inp.W3)
+            W2.copy_(inp.W2)
+            return lac.swiglu_fwd_chunked(inp.q, inp.k, inp.v, W1, W3, W2, eta=inp.eta, chunk=C, loss=loss,
+                                          out=out, workspace=ws)
+
+        # per token: [q; k] x W13 (2 x 2 m dk x 2), output (dv m x 2, twice for
+        # MSE), dA (m dv x 2), dW2 (dv m x 2), dW13 (2 m dk x 2)
+        flop_alg = B * H * L * (12 * m * dk + (8 if loss == "mse" else 6) * m * dv)
+        bytes_alg = (B * H * L * (2 * dk + 2 * dv) * 2 + B * H * L * 4     # q, k, v, out, eta
+                     + 2 * B * H * (2 * m * dk + dv * m) * 4)               # weights in and out
+        info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, m=m, chunk=C, loss=loss, eta="per-token",
+                    dtype="bf16", tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
+                    kernel="sw_fwd+sw_out+sw_bwda+sw_upd", inputs=inp)
+        return step, info
     if name in ("decode", "decode-momentum"):
         inp = W.gen_decode(beta=0.9 if name == "decode-momentum" else 0.0)
         B, H, _, dk = inp.q.shape
@@ -218,6 +245,17 @@ def cpu_baseline(info) -> dict:
     inp = info["inputs"]
     if inp is None:
         return None
+    if info["workload"] in ("swiglu", "swiglu-mse"):
+        B, H, L = inp.q.shape[:3]
+        f = lambda t: W.to_f64(t[:1, :1].cpu())
+        t0 = time.perf_counter()
+        oracle.swiglu_fast_weight(f(inp.q), f(inp.k), f(inp.v), f(inp.W1), f(inp.W3), f(inp.W2), eta=f(inp.eta),
+                                  chunk=inp.chunk, loss=inp.loss)
+        dt = time.perf_counter() - t0
+        return {"value": info["tokens"] / (B * H) / dt, "unit": "tokens/s", "cores": blas_threads(),
+                "kind": "oracle",
+                "sample": f"1 of {B * H} (b,h) heads, full L={L} ({L // inp.chunk} chunks), NumPy fp64 GEMMs; "
+                          f"{dt:.2f} s; tokens/s scaled by the head fraction"}
     B, H = inp.q.shape[:2]
     L = inp.q.shape[2]
     heads = B * H
@@ -252,6 +290,12 @@ def cpu_baseline(info) -> dict:
             "sample": what + "; tokens/s scaled by the head fraction"}
 
 
+def blas_threads() -> int:
+    """Threads NumPy's BLAS runs the oracle's GEMMs with."""
+    from threadpoolctl import threadpool_info
+    return max((p["num_threads"] for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+
+
 def load_traffic(kernel: str, workload: str):
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -271,7 +315,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lm-scale",
                     help="lm-scale (default), small-f32, inplace-32k, inplace-128k, momentum, dual-b16, "
-                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, inplace-frontend")
+                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, inplace-frontend, swiglu, swiglu-mse")
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this many seconds of steps have run")
     ap.add_argument("--no-cpu-baseline", action="store_true")

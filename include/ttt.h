@@ -322,6 +322,47 @@ ttt_status_t ttt_inplace_clip_eta(int32_t B, int32_t L, int32_t d_ff, int32_t d_
                                   const void* Z, const void* Vhat, float eta, float tau, float* eta_out,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Large-chunk SwiGLU fast weight ([P5] "LaCT (Large Chunk Test-Time
+ * Training)" wiki, aisparkup.com/wiki/lact, section on the core idea:
+ * nonlinear fast weights updated once per large chunk, the chunk's tokens
+ * forming one batch; [P4] "RNN의 기억을 작은 모델로 바꾼다면: Test-Time
+ * Training 읽기", ariser.io, section on the update rule: the state is the
+ * weights of a small model and takes gradient steps on an inner loss).
+ * Per (b, h) and chunk i of `chunk` tokens (the last one may be shorter),
+ * with W = (W1, W3, W2) the weights left by chunks < i:
+ *
+ *     out_i = f_W(q_i),   f_W(x) = W2 (silu(W1 x) * (W3 x))
+ *     W    <- W - grad_W sum_{t in i} eta_t l_t(W)
+ *     l_t   = -<f_W(k_t), v_t>          loss = TTT_LOSS_DOT
+ *     l_t   = 1/2 ||f_W(k_t) - v_t||^2  loss = TTT_LOSS_MSE
+ *
+ *   q, k [B, H, L, dk], v, out [B, H, L, dv]: bf16, contiguous.
+ *   eta [B, H, L] fp32 per-token step sizes, or NULL: eta_scalar for all.
+ *   W1, W3 [B, H, m, dk] and W2 [B, H, dv, m]: fp32, contiguous, row =
+ *   output feature; read as the initial weights and OVERWRITTEN with the
+ *   weights after the last chunk.
+ *   Arithmetic: bf16 MFMA operands (activations and a bf16 copy of the
+ *   weights, refreshed after every chunk), fp32 accumulation, fp32 weights.
+ *   workspace: ttt_swiglu_workspace_size bytes of device memory,
+ *   caller-owned, no initial contents needed (bf16 weight copies and one
+ *   chunk's activations).
+ * Supported (else TTT_ERR_UNSUPPORTED): dk, dv, m and chunk multiples of
+ * 128, and chunk * max(dk, dv, 2 m) below 2^31.  A chunk longer than the
+ * sequence acts as one chunk of the whole sequence.
+ * Errors (before anything is enqueued): TTT_ERR_NULL, TTT_ERR_SHAPE,
+ * TTT_ERR_VALUE (loss), TTT_ERR_ALIGN (16 bytes), TTT_ERR_UNSUPPORTED,
+ * TTT_ERR_WORKSPACE, TTT_ERR_ALIAS (out, a weight or the workspace overlaps
+ * another buffer); TTT_ERR_HIP if a launch fails.
+ */
+typedef enum { TTT_LOSS_DOT = 0, TTT_LOSS_MSE = 1 } ttt_loss_t;
+ttt_status_t ttt_swiglu_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t m,
+                                       int32_t chunk, size_t* bytes);
+ttt_status_t ttt_swiglu_fwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t m,
+                                    int32_t chunk, int32_t loss, const void* q, const void* k, const void* v,
+                                    const float* eta, float eta_scalar, float* W1, float* W3, float* W2,
+                                    void* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* ttt_status_string(ttt_status_t status);
 

@@ -102,6 +102,11 @@ def load_library():
     lib.ttt_inplace_clip_eta.argtypes = [i32, i32, i32, i32, i32, _vp, _vp, f32, f32, _vp, _vp, ctypes.c_size_t,
                                          _vp]
     lib.ttt_inplace_clip_eta.restype = ctypes.c_int
+    lib.ttt_swiglu_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, sz]
+    lib.ttt_swiglu_workspace_size.restype = ctypes.c_int
+    lib.ttt_swiglu_fwd_chunked.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, _vp, _vp,
+                                           _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.ttt_swiglu_fwd_chunked.restype = ctypes.c_int
     lib.ttt_status_string.argtypes = [ctypes.c_int]
     lib.ttt_status_string.restype = ctypes.c_char_p
     lib.ttt_fwd_args_size.argtypes = []
@@ -415,5 +420,52 @@ def inplace_clip_eta(Z, Vhat, *, chunk, eta, tau, out=None, stream=None):
     return out
 
 
-__all__ = ["inplace_gated_input", "inplace_lm_target", "inplace_clip_eta", "fwd_chunked", "chunk_state_scan", "dual_form_fwd", "decode_step", "bwd_chunked", "bwd_workspace_size", "load_library", "TTTError",
+_LOSS = {"dot": 0, "mse": 1}
+
+
+def swiglu_workspace_size(B, H, L, dk, dv, m, chunk):
+    """Bytes of workspace ``swiglu_fwd_chunked`` needs (``ttt_swiglu_workspace_size``)."""
+    ws = ctypes.c_size_t(0)
+    _check(load_library().ttt_swiglu_workspace_size(B, H, L, dk, dv, m, int(chunk), ctypes.byref(ws)))
+    return ws.value
+
+
+def swiglu_fwd_chunked(q, k, v, W1, W3, W2, *, eta=None, eta_scalar=0.0, chunk=2048, loss="dot", out=None,
+                       workspace=None, stream=None):
+    """Large-chunk SwiGLU fast weight (``ttt_swiglu_fwd_chunked``): per chunk,
+    out = W2 (silu(W1 q) * (W3 q)) with the current weights, then one gradient
+    step of the weights on sum_t eta_t l_t over the chunk's (k, v) pairs
+    (loss "dot": l = -<f(k), v>; "mse": l = 1/2 ||f(k) - v||^2).
+
+    q, k: [B,H,L,dk], v: [B,H,L,dv] contiguous bf16; W1, W3: [B,H,m,dk] and
+    W2: [B,H,dv,m] contiguous fp32, UPDATED IN PLACE to the final weights;
+    eta: [B,H,L] fp32 or None (eta_scalar).  Returns out [B,H,L,dv] bf16."""
+    lib = load_library()
+    _require_gpu(q, k, v, W1, W3, W2, eta, out, workspace)
+    _bf16_contig((q, "q"), (k, "k"), (v, "v"))
+    if loss not in _LOSS:
+        raise ValueError("loss must be 'dot' or 'mse'")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    m = W1.shape[-2]
+    if k.shape != q.shape or v.shape[:3] != (B, H, L):
+        raise ValueError("q, k must be [B,H,L,dk] and v [B,H,L,dv]")
+    for W, shp, nm in ((W1, (B, H, m, dk), "W1"), (W3, (B, H, m, dk), "W3"), (W2, (B, H, dv, m), "W2")):
+        if tuple(W.shape) != shp or W.dtype != torch.float32 or not W.is_contiguous():
+            raise ValueError(f"{nm} must be contiguous fp32 {list(shp)}")
+    if eta is not None and (tuple(eta.shape) != (B, H, L) or eta.dtype != torch.float32 or not eta.is_contiguous()):
+        raise ValueError("eta must be contiguous fp32 [B,H,L]")
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=torch.bfloat16, device=q.device)
+    need = swiglu_workspace_size(B, H, L, dk, dv, m, chunk)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.ttt_swiglu_fwd_chunked(B, H, L, dk, dv, m, int(chunk), _LOSS[loss], _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(eta), float(eta_scalar), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(out),
+                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _stream(stream)))
+    return out
+
+
+__all__ = ["swiglu_fwd_chunked", "swiglu_workspace_size", "inplace_gated_input", "inplace_lm_target", "inplace_clip_eta", "fwd_chunked", "chunk_state_scan", "dual_form_fwd", "decode_step", "bwd_chunked", "bwd_workspace_size", "load_library", "TTTError",
            "FwdArgs", "LIB_PATH"]

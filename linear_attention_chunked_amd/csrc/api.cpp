@@ -4,6 +4,7 @@
 // enqueued nothing.  No allocation, no global mutable state.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <initializer_list>
 #include <utility>
@@ -475,6 +476,70 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
     p.dk = dk;
     p.dv = dv;
     return from_hip(ttt::launch_decode(p, dtype, reinterpret_cast<hipStream_t>(stream)));
+}
+
+namespace {
+// chunk length the kernels run with: a chunk longer than the sequence is
+// the whole sequence (rounded up to the 128-token tiles)
+int64_t swiglu_chunk(int32_t L, int32_t chunk) { return std::min<int64_t>(chunk, ((int64_t)L + 127) / 128 * 128); }
+}  // namespace
+
+ttt_status_t ttt_swiglu_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t m,
+                                       int32_t chunk, size_t* bytes) {
+    if (!bytes) return TTT_ERR_NULL;
+    if (B < 1 || H < 1 || L < 1 || dk < 1 || dv < 1 || m < 1 || chunk < 1) return TTT_ERR_SHAPE;
+    const int64_t C = swiglu_chunk(L, chunk);
+    if (!ttt::swiglu_supported(dk, dv, m, (int)C)) return TTT_ERR_UNSUPPORTED;
+    const int64_t span = std::max({(int64_t)2 * m * dk, (int64_t)dv * m, C * std::max({(int64_t)dk, (int64_t)dv,
+                                                                                         (int64_t)2 * m})});
+    if (span >= ((int64_t)1 << 31)) return TTT_ERR_UNSUPPORTED;
+    *bytes = ttt::swiglu_workspace((int)((int64_t)B * H), dk, dv, m, (int)C);
+    return TTT_OK;
+}
+
+ttt_status_t ttt_swiglu_fwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t m,
+                                    int32_t chunk, int32_t loss, const void* q, const void* k, const void* v,
+                                    const float* eta, float eta_scalar, float* W1, float* W3, float* W2,
+                                    void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    size_t need = 0;
+    const ttt_status_t st = ttt_swiglu_workspace_size(B, H, L, dk, dv, m, chunk, &need);
+    if (st != TTT_OK) return st;
+    if (loss != TTT_LOSS_DOT && loss != TTT_LOSS_MSE) return TTT_ERR_VALUE;
+    if (!q || !k || !v || !W1 || !W3 || !W2 || !out) return TTT_ERR_NULL;
+    const void* ptrs[] = {q, k, v, eta, W1, W3, W2, out};
+    for (const void* x : ptrs)
+        if (x && !aligned16(x)) return TTT_ERR_ALIGN;
+    if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return TTT_ERR_ALIGN;
+    const size_t BH = (size_t)B * H;
+    const size_t nq = BH * L * dk * 2, nv = BH * L * dv * 2, ne = BH * L * 4;
+    const size_t n13 = BH * m * dk * 4, n2 = BH * dv * m * 4;
+    if (!disjoint(out, nv, {{q, nq}, {k, nq}, {v, nv}, {eta, ne}, {W1, n13}, {W3, n13}, {W2, n2}, {workspace, need}}))
+        return TTT_ERR_ALIAS;
+    if (!disjoint(W1, n13, {{q, nq}, {k, nq}, {v, nv}, {eta, ne}, {W3, n13}, {W2, n2}, {workspace, need}}))
+        return TTT_ERR_ALIAS;
+    if (!disjoint(W3, n13, {{q, nq}, {k, nq}, {v, nv}, {eta, ne}, {W2, n2}, {workspace, need}})) return TTT_ERR_ALIAS;
+    if (!disjoint(W2, n2, {{q, nq}, {k, nq}, {v, nv}, {eta, ne}, {workspace, need}})) return TTT_ERR_ALIAS;
+    if (!disjoint(workspace, need, {{q, nq}, {k, nq}, {v, nv}, {eta, ne}})) return TTT_ERR_ALIAS;
+    ttt::SwParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.eta = eta;
+    p.eta_scalar = eta_scalar;
+    p.W1 = W1;
+    p.W3 = W3;
+    p.W2 = W2;
+    p.out = out;
+    p.workspace = workspace;
+    p.BH = (int)BH;
+    p.L = L;
+    p.dk = dk;
+    p.dv = dv;
+    p.m = m;
+    p.chunk = (int)swiglu_chunk(L, chunk);
+    p.loss = loss;
+    return from_hip(ttt::launch_swiglu(p, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -163,4 +163,24 @@ size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype, bool moment
 hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
 bool decode_supported(int dtype, int dk, int dv);
 
+// Large-chunk SwiGLU fast weight (bf16 activations, fp32 master weights).
+// Per head: W1, W3 [m][dk] and W2 [dv][m] fp32, updated in place; the
+// workspace holds bf16 copies of the weights and one chunk's activations.
+struct SwParams {
+    const void* q;      // [BH][L][dk] bf16
+    const void* k;      // [BH][L][dk]
+    const void* v;      // [BH][L][dv]
+    const float* eta;   // [BH][L] or null (eta_scalar)
+    float eta_scalar;
+    float* W1;          // [BH][m][dk]
+    float* W3;          // [BH][m][dk]
+    float* W2;          // [BH][dv][m]
+    void* out;          // [BH][L][dv] bf16
+    void* workspace;
+    int BH, L, dk, dv, m, chunk, loss;   // loss: 0 = -<f(k), v>, 1 = 1/2 ||f(k) - v||^2
+};
+bool swiglu_supported(int dk, int dv, int m, int chunk);
+size_t swiglu_workspace(int BH, int dk, int dv, int m, int chunk);
+hipError_t launch_swiglu(const SwParams& p, hipStream_t stream);
+
 }  // namespace ttt

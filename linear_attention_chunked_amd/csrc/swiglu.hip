@@ -1,0 +1,636 @@
+// swiglu.hip -- large-chunk SwiGLU fast weight (nonlinear fast-weight state).
+//
+// [P5] ("LaCT (Large Chunk Test-Time Training)", aisparkup.com/wiki/lact),
+// section on the core idea: the fast weights are a nonlinear model whose
+// state can grow to a large share of the model's parameters, and they take
+// one update per large chunk whose tokens act as one big batch, which turns
+// the update into GEMMs.  [P4] ("RNN의 기억을 작은 모델로 바꾼다면: Test-Time
+// Training 읽기", ariser.io), section on the update rule: one gradient step
+// on the inner loss, W <- W - eta grad l.  Per head and chunk i, with the
+// weights left by chunks < i:
+//
+//     O_i = f_W(Q_i),   f_W(x) = W2 (silu(W1 x) * (W3 x))
+//     W  <- W - grad_W sum_{t in i} eta_t l_t(W),
+//     l_t = -<f_W(k_t), v_t>  (loss 0)   or   1/2 ||f_W(k_t) - v_t||^2  (loss 1)
+//
+// One chunk step is four launches over all heads, each a bf16 MFMA GEMM
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation, 128 x 128 block tiles of
+// four 64 x 64 waves) with its elementwise work fused into the epilogue:
+//
+//   sw_fwd   [Q_i; K_i] x W13^T   (K = dk)  -> A = silu(H1) * H3 for the Q rows
+//            (aq) and the K rows (ak; times eta_t for loss 0), and for the K
+//            rows the two factors of the SwiGLU derivative (cc):
+//            c1 = H3 silu'(H1), c3 = silu(H1).
+//   sw_out   A x W2^T            (K = m)   -> O_i (Q rows); for loss 1 also
+//            dY = eta_t (Y - V) (K rows).
+//   sw_bwda  dY x W2             (K = dv)  -> dA, then dH = (dA c1, dA c3)
+//            interleaved like W13; for loss 0, dY = -eta_t V is never formed:
+//            the GEMM reads V and the epilogue scales by -eta_t.
+//   sw_upd   dW2 = dY^T A_K and dW13 = dH^T K_i (K = chunk tokens), both in
+//            one launch; the epilogue updates the fp32 master weights and
+//            writes their bf16 copies for the next chunk.
+//
+// Layouts.  W13 interleaves the rows of W1 and W3 (row 2f = W1 row f,
+// row 2f + 1 = W3 row f), so the gate and up values of one hidden unit land
+// in consecutive accumulator registers of one lane and the SwiGLU epilogue
+// needs no exchange; dH uses the same interleave, so dW13 = dH^T K comes out
+// row-for-row in W13's layout.  The GEMMs contracting over features read
+// both operands K-contiguous; those contracting over the chunk's tokens
+// read token-major data through the gfx950 transposing LDS read.
+//
+// Tokens past the end of the sequence (a last, shorter chunk): loads are
+// clamped to the last token, and the K-row epilogues write zero A and zero
+// c1, c3 there, so those rows add nothing to the weight update.
+#include "common.h"
+#include "internal.h"
+
+#include <type_traits>
+
+namespace ttt {
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int SW_BK = 32;      // k per step
+constexpr int SW_NT = 256;     // threads per workgroup (2 x 2 waves)
+constexpr int SW_NS = 4;       // k-steps of loads in flight
+constexpr int SW_T = 2;        // 32 x 32 MFMA tiles per wave and dimension
+constexpr int SW_TILE = 64 * SW_T;   // block tile 128 x 128
+constexpr int SW_PAD = 32;     // [k][row] LDS tiles: 64-byte row pad
+
+TTT_DEV void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+TTT_DEV int swz(int r) { return (r >> 2) & 3; }
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane a loads 4 consecutive 16-bit values; lane i then holds the
+// values lanes 4j + i/4 loaded in slot i%4 (j = 0..3).
+TTT_DEV u32x2 ds_read_tr(const bf16_t* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p)));
+}
+
+// One operand of C = A B^T: R = 64 T rows of the block tile, K elements each.
+//   KROW = false: row-major, K contiguous ([row][k] in memory); LDS tile
+//                 [row][32] with a 16-byte XOR swizzle.
+//   KROW = true : token-major data contracted over tokens ([k][row] in
+//                 memory); LDS tile [32][row + pad], fragments by the
+//                 transposing read.
+// Both give lane l the fragment of row r0 + l % 32, k = k0 + 8 (l / 32) + 0..7.
+template <bool KROW, int T>
+struct Opnd {
+    static constexpr int R = 64 * T;
+    static constexpr int LD = KROW ? R + SW_PAD : SW_BK;
+    static constexpr int BUF = KROW ? SW_BK * LD : R * SW_BK;   // elements per LDS buffer
+    const bf16_t* base;   // wave-uniform
+    uint32_t off[T];      // element offsets of this thread's 16-byte pieces
+    int kr[T];
+    int lo[T];
+    uint32_t ld;
+    int lim;
+
+    // KROW = false: rows off0 .. off0 + R - 1 of a [rows][ld] matrix at b,
+    // rows >= rowlim clamped.  KROW = true: columns off0 .. off0 + R - 1 of
+    // a [k][ld] matrix at b, k rows >= rowlim clamped.  Offsets from b stay
+    // below 2^31 elements (checked by the launcher).
+    TTT_DEV void init(const bf16_t* b, int ld_, int off0, int rowlim, int tid) {
+        base = b;
+        ld = (uint32_t)ld_;
+        lim = rowlim;
+#pragma unroll
+        for (int y = 0; y < T; ++y) {
+            const int u = tid + y * SW_NT;
+            if (!KROW) {
+                const int r = u >> 2, c = u & 3;
+                off[y] = (uint32_t)min(off0 + r, rowlim - 1) * ld + 8 * c;
+                lo[y] = r * SW_BK + 8 * (c ^ swz(r));
+                kr[y] = 0;
+            } else {
+                const int kk = u / (8 * T), c = u % (8 * T);
+                off[y] = (uint32_t)(off0 + 8 * c);
+                kr[y] = kk;
+                lo[y] = kk * LD + 8 * c;
+            }
+        }
+    }
+    TTT_DEV u32x4 load(int y, int st) const {
+        if (!KROW) return *reinterpret_cast<const u32x4*>(base + (off[y] + (uint32_t)(st * SW_BK)));
+        const uint32_t t = (uint32_t)min(st * SW_BK + kr[y], lim - 1);
+        return *reinterpret_cast<const u32x4*>(base + (off[y] + t * ld));
+    }
+    TTT_DEV bf16x8 frag(const bf16_t* s, int r0, int k0, int lane) const {
+        if (!KROW) {
+            const int row = r0 + (lane & 31);
+            const int c = (k0 >> 3) + (lane >> 5);
+            return *reinterpret_cast<const bf16x8*>(s + row * SW_BK + 8 * (c ^ swz(row)));
+        }
+        const int G = lane >> 4, a = lane & 15;
+        const int rb = r0 + 16 * (G & 1) + 4 * (a & 3);
+        const int kk = k0 + 8 * (G >> 1) + (a >> 2);
+        const u32x2 lo2 = ds_read_tr(s + (kk + 0) * LD + rb);
+        const u32x2 hi2 = ds_read_tr(s + (kk + 4) * LD + rb);
+        return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+    }
+};
+
+using Acc = f32x16[SW_T][SW_T];
+
+TTT_DEV void zero(Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < SW_T; ++i)
+#pragma unroll
+        for (int j = 0; j < SW_T; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// acc += A B^T over `steps` k-steps of 32 (steps a multiple of 4): four
+// k-steps of global loads in flight in registers, two LDS buffers.
+template <bool AK, bool BKR>
+struct Loop {
+    using OA = Opnd<AK, SW_T>;
+    using OB = Opnd<BKR, SW_T>;
+    static constexpr int LDS = 2 * (OA::BUF + OB::BUF);
+
+    TTT_DEV static void run(Acc& acc, int steps, const OA& a, const OB& b, bf16_t* smem, int tid) {
+        bf16_t* sA = smem;
+        bf16_t* sB = smem + 2 * OA::BUF;
+        const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+        u32x4 ra[SW_NS][SW_T], rb[SW_NS][SW_T];
+        auto load = [&](int st, auto SET) __attribute__((always_inline)) {
+            constexpr int k = decltype(SET)::value;
+            const int s = min(st, steps - 1);
+#pragma unroll
+            for (int y = 0; y < SW_T; ++y) ra[k][y] = a.load(y, s);
+#pragma unroll
+            for (int y = 0; y < SW_T; ++y) rb[k][y] = b.load(y, s);
+        };
+        auto stage = [&](int buf, auto SET) __attribute__((always_inline)) {
+            constexpr int k = decltype(SET)::value;
+#pragma unroll
+            for (int y = 0; y < SW_T; ++y) *reinterpret_cast<u32x4*>(&sA[buf * OA::BUF + a.lo[y]]) = ra[k][y];
+#pragma unroll
+            for (int y = 0; y < SW_T; ++y) *reinterpret_cast<u32x4*>(&sB[buf * OB::BUF + b.lo[y]]) = rb[k][y];
+        };
+        auto compute = [&](int buf) __attribute__((always_inline)) {
+            const bf16_t* A = sA + buf * OA::BUF;
+            const bf16_t* B = sB + buf * OB::BUF;
+#pragma unroll
+            for (int kk = 0; kk < SW_BK; kk += 16) {
+                bf16x8 af[SW_T], bfr[SW_T];
+#pragma unroll
+                for (int i = 0; i < SW_T; ++i) af[i] = a.frag(A, 32 * SW_T * wm + 32 * i, kk, lane);
+#pragma unroll
+                for (int j = 0; j < SW_T; ++j) bfr[j] = b.frag(B, 32 * SW_T * wn + 32 * j, kk, lane);
+#pragma unroll
+                for (int i = 0; i < SW_T; ++i)
+#pragma unroll
+                    for (int j = 0; j < SW_T; ++j) mma32(acc[i][j], af[i], bfr[j]);
+            }
+        };
+        using K0 = std::integral_constant<int, 0>;
+        using K1 = std::integral_constant<int, 1>;
+        using K2 = std::integral_constant<int, 2>;
+        using K3 = std::integral_constant<int, 3>;
+        load(0, K0{});
+        load(1, K1{});
+        load(2, K2{});
+        load(3, K3{});
+        stage(0, K0{});
+        __syncthreads();
+        auto step = [&](int st, auto CUR, auto NXT) __attribute__((always_inline)) {
+            load(st + SW_NS, CUR);
+            compute(st & 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (st + 1 < steps) stage((st + 1) & 1, NXT);
+            __syncthreads();
+        };
+        for (int st = 0; st < steps; st += SW_NS) {
+            step(st, K0{}, K1{});
+            step(st + 1, K1{}, K2{});
+            step(st + 2, K2{}, K3{});
+            step(st + 3, K3{}, K0{});
+        }
+    }
+};
+
+// Workgroup -> (head, row tile, column tile).  Heads are contiguous ranges of
+// logical ids (xcd_logical: one XCD runs one contiguous range); within a
+// head, groups of 8 column tiles walk all row tiles.
+TTT_DEV void tile_id(int nrow, int ncol, int* bh, int* rt, int* ct) {
+    const int n = nrow * ncol;
+    const int lid = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+    *bh = lid / n;
+    const int t = lid % n;
+    constexpr int G = 8;
+    const int group = t / (G * nrow), first = group * G;
+    const int gsz = min(G, ncol - first);
+    const int r = t % (G * nrow);
+    *ct = first + r % gsz;
+    *rt = r / gsz;
+}
+
+// accumulator (i, j, r) -> row 64 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
+// column 64 wn + 32 j + lane % 32 of the block tile
+TTT_DEV int acc_row(int wm, int i, int q, int lane) { return 64 * wm + 32 * i + 8 * q + 4 * (lane >> 5); }
+TTT_DEV int acc_col(int wn, int j, int lane) { return 64 * wn + 32 * j + (lane & 31); }
+
+// Kernel arguments: base pointers (head 0) and per-head strides in elements.
+struct SwDev {
+    const bf16_t* q;
+    const bf16_t* k;
+    const bf16_t* v;
+    const float* eta;
+    float eta_scalar;
+    float* W1;
+    float* W3;
+    float* W2;
+    bf16_t* out;
+    bf16_t* w13;   // [2m][dk]  W1 / W3 rows interleaved
+    bf16_t* w2;    // [dv][m]
+    bf16_t* w2t;   // [m][dv]
+    bf16_t* aq;    // [C][m]    A of the Q rows
+    bf16_t* ak;    // [C][m]    A of the K rows (times eta_t for loss 0)
+    bf16_t* cc;    // [C][2m]   (c1, c3) per hidden unit, K rows
+    bf16_t* dy;    // [C][dv]   loss 1 only
+    bf16_t* dh;    // [C][2m]   (dH1, dH3) per hidden unit
+    int64_t s_w13, s_w2, s_act, s_cc, s_dy;
+    int L, dk, dv, m, C, c0, clen;
+};
+
+TTT_DEV float eta_at(const SwDev& p, int bh, int t) {
+    return p.eta ? p.eta[(int64_t)bh * p.L + t] : p.eta_scalar;
+}
+TTT_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// ------------------------------------------------------------ forward GEMM
+// tile (row tile of W13, token tile of [Q_i; K_i]); K = dk
+template <int LOSS>
+__global__ __launch_bounds__(SW_NT) void sw_fwd_kernel(SwDev p) {
+    using LP = Loop<false, false>;
+    __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const int nct = p.C / SW_TILE;
+    int bh, rt, ct;
+    tile_id(2 * p.m / SW_TILE, 2 * nct, &bh, &rt, &ct);
+    const bool isK = ct >= nct;
+    const int tok0 = (isK ? ct - nct : ct) * SW_TILE;
+    Acc acc;
+    zero(acc);
+    if (tok0 < p.clen) {
+        typename LP::OA a;
+        typename LP::OB b;
+        a.init(p.w13 + bh * p.s_w13, p.dk, rt * SW_TILE, 2 * p.m, tid);
+        b.init((isK ? p.k : p.q) + ((int64_t)bh * p.L + p.c0) * p.dk, p.dk, tok0, p.L - p.c0, tid);
+        LP::run(acc, p.dk / SW_BK, a, b, smem, tid);
+    }
+    bf16_t* dst = (isK ? p.ak : p.aq) + bh * p.s_act;
+    bf16_t* ccb = p.cc + bh * p.s_cc;
+#pragma unroll
+    for (int j = 0; j < SW_T; ++j) {
+        const int tc = tok0 + acc_col(wn, j, lane);
+        const bool live = tc < p.clen;
+        if (!isK && !live) continue;
+        const float e = (LOSS == 0 && isK && live) ? eta_at(p, bh, p.c0 + tc) : 1.f;
+        bf16_t* drow = dst + (int64_t)tc * p.m;
+        bf16_t* crow = ccb + (int64_t)tc * 2 * p.m;
+#pragma unroll
+        for (int i = 0; i < SW_T; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f0 = (rt * SW_TILE + acc_row(wm, i, q, lane)) >> 1;   // rows 2 f0 .. 2 f0 + 3
+                const float g0 = acc[i][j][4 * q], u0 = acc[i][j][4 * q + 1];
+                const float g1 = acc[i][j][4 * q + 2], u1 = acc[i][j][4 * q + 3];
+                const float sg0 = sigm(g0), sg1 = sigm(g1);
+                const float s0 = g0 * sg0, s1 = g1 * sg1;
+                if (!isK) {
+                    *reinterpret_cast<uint32_t*>(drow + f0) = pack2bf(s0 * u0, s1 * u1);
+                } else if (live) {
+                    *reinterpret_cast<uint32_t*>(drow + f0) = pack2bf(e * s0 * u0, e * s1 * u1);
+                    const float c10 = u0 * sg0 * (1.f + g0 * (1.f - sg0));
+                    const float c11 = u1 * sg1 * (1.f + g1 * (1.f - sg1));
+                    *reinterpret_cast<u32x2*>(crow + 2 * f0) = u32x2{pack2bf(c10, s0), pack2bf(c11, s1)};
+                } else {
+                    *reinterpret_cast<uint32_t*>(drow + f0) = 0u;
+                    *reinterpret_cast<u32x2*>(crow + 2 * f0) = u32x2{0u, 0u};
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------- output GEMM
+// tile (row tile of W2 = output features, token tile of A_Q, then of A_K for
+// loss 1); K = m
+template <int LOSS>
+__global__ __launch_bounds__(SW_NT) void sw_out_kernel(SwDev p) {
+    using LP = Loop<false, false>;
+    __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const int nct = p.C / SW_TILE;
+    int bh, rt, ct;
+    tile_id(p.dv / SW_TILE, LOSS ? 2 * nct : nct, &bh, &rt, &ct);
+    const bool isK = ct >= nct;
+    const int tok0 = (isK ? ct - nct : ct) * SW_TILE;
+    Acc acc;
+    zero(acc);
+    if (tok0 < p.clen) {
+        typename LP::OA a;
+        typename LP::OB b;
+        a.init(p.w2 + bh * p.s_w2, p.m, rt * SW_TILE, p.dv, tid);
+        b.init((isK ? p.ak : p.aq) + bh * p.s_act, p.m, tok0, p.C, tid);
+        LP::run(acc, p.m / SW_BK, a, b, smem, tid);
+    }
+#pragma unroll
+    for (int j = 0; j < SW_T; ++j) {
+        const int tc = tok0 + acc_col(wn, j, lane);
+        const bool live = tc < p.clen;
+        if (!isK) {
+            if (!live) continue;
+            bf16_t* orow = p.out + ((int64_t)bh * p.L + p.c0 + tc) * p.dv;
+#pragma unroll
+            for (int i = 0; i < SW_T; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = rt * SW_TILE + acc_row(wm, i, q, lane);
+                    st4(orow + n, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                        acc[i][j][4 * q + 3]});
+                }
+        } else {
+            // dY = eta_t (Y - V); zero past the sequence end
+            const float e = live ? eta_at(p, bh, p.c0 + tc) : 0.f;
+            const bf16_t* vrow = p.v + ((int64_t)bh * p.L + p.c0 + min(tc, p.clen - 1)) * p.dv;
+            bf16_t* yrow = p.dy + bh * p.s_dy + (int64_t)tc * p.dv;
+#pragma unroll
+            for (int i = 0; i < SW_T; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n = rt * SW_TILE + acc_row(wm, i, q, lane);
+                    const u32x2 vv = *reinterpret_cast<const u32x2*>(vrow + n);
+                    f32x4 d;
+                    d[0] = e * (acc[i][j][4 * q] - __uint_as_float(vv[0] << 16));
+                    d[1] = e * (acc[i][j][4 * q + 1] - __uint_as_float(vv[0] & 0xffff0000u));
+                    d[2] = e * (acc[i][j][4 * q + 2] - __uint_as_float(vv[1] << 16));
+                    d[3] = e * (acc[i][j][4 * q + 3] - __uint_as_float(vv[1] & 0xffff0000u));
+                    if (!live) d = zero4();
+                    st4(yrow + n, d);
+                }
+        }
+    }
+}
+
+// ----------------------------------------------------- dA and dH (K rows)
+// tile (row tile of W2^T = hidden units, token tile); K = dv.  loss 0 reads
+// V in place of dY and scales by -eta_t.
+template <int LOSS>
+__global__ __launch_bounds__(SW_NT) void sw_bwda_kernel(SwDev p) {
+    using LP = Loop<false, false>;
+    __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    int bh, rt, ct;
+    tile_id(p.m / SW_TILE, p.C / SW_TILE, &bh, &rt, &ct);
+    const int tok0 = ct * SW_TILE;
+    Acc acc;
+    zero(acc);
+    if (tok0 < p.clen) {
+        typename LP::OA a;
+        typename LP::OB b;
+        a.init(p.w2t + bh * p.s_w2, p.dv, rt * SW_TILE, p.m, tid);
+        if (LOSS == 0) b.init(p.v + ((int64_t)bh * p.L + p.c0) * p.dv, p.dv, tok0, p.L - p.c0, tid);
+        else b.init(p.dy + bh * p.s_dy, p.dv, tok0, p.C, tid);
+        LP::run(acc, p.dv / SW_BK, a, b, smem, tid);
+    }
+    const bf16_t* ccb = p.cc + bh * p.s_cc;
+    bf16_t* dhb = p.dh + bh * p.s_cc;
+#pragma unroll
+    for (int j = 0; j < SW_T; ++j) {
+        const int tc = tok0 + acc_col(wn, j, lane);
+        const bool live = tc < p.clen;
+        const float sc = !live ? 0.f : (LOSS == 0 ? -eta_at(p, bh, p.c0 + tc) : 1.f);
+        const bf16_t* crow = ccb + (int64_t)tc * 2 * p.m;
+        bf16_t* hrow = dhb + (int64_t)tc * 2 * p.m;
+#pragma unroll
+        for (int i = 0; i < SW_T; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int f0 = rt * SW_TILE + acc_row(wm, i, q, lane);   // hidden units f0 .. f0 + 3
+                const u32x4 c = *reinterpret_cast<const u32x4*>(crow + 2 * f0);
+                u32x4 o;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float da = sc * acc[i][j][4 * q + x];
+                    o[x] = live ? pack2bf(da * __uint_as_float(c[x] << 16), da * __uint_as_float(c[x] & 0xffff0000u))
+                                : 0u;
+                }
+                *reinterpret_cast<u32x4*>(hrow + 2 * f0) = o;
+            }
+    }
+}
+
+// ---------------------------------------------------------- weight update
+// One launch, two problems per head (K = the chunk's tokens):
+//   dW2[n][f]   = sum_t dY[t][n] A_K[t][f]   (loss 0: V and eta_t A_K, sign +)
+//   dW13[r][c]  = sum_t dH[t][r] K[t][c]
+// W <- W - dW in fp32, then the bf16 copies.
+template <int LOSS>
+__global__ __launch_bounds__(SW_NT) void sw_upd_kernel(SwDev p) {
+    using LP = Loop<true, true>;
+    __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const int n4r = p.dv / SW_TILE, n4c = p.m / SW_TILE;
+    const int n5r = 2 * p.m / SW_TILE, n5c = p.dk / SW_TILE;
+    const int n4 = n4r * n4c, n5 = n5r * n5c;
+    const int lid = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+    const int bh = lid / (n4 + n5), t = lid % (n4 + n5);
+    const bool is5 = t >= n4;
+    const int tt = is5 ? t - n4 : t, nc = is5 ? n5c : n4c;
+    const int rt = tt / nc, ct = tt % nc;
+    typename LP::OA a;
+    typename LP::OB b;
+    if (!is5) {
+        if (LOSS == 0) a.init(p.v + ((int64_t)bh * p.L + p.c0) * p.dv, p.dv, rt * SW_TILE, p.L - p.c0, tid);
+        else a.init(p.dy + bh * p.s_dy, p.dv, rt * SW_TILE, p.C, tid);
+        b.init(p.ak + bh * p.s_act, p.m, ct * SW_TILE, p.C, tid);
+    } else {
+        a.init(p.dh + bh * p.s_cc, 2 * p.m, rt * SW_TILE, p.C, tid);
+        b.init(p.k + ((int64_t)bh * p.L + p.c0) * p.dk, p.dk, ct * SW_TILE, p.L - p.c0, tid);
+    }
+    Acc acc;
+    zero(acc);
+    // tokens past the sequence end carry zero A_K and zero dH: the last,
+    // shorter chunk still runs whole 128-token groups
+    const int steps = ((p.clen + 127) / 128) * (128 / SW_BK);
+    LP::run(acc, steps, a, b, smem, tid);
+    if (!is5) {
+        const float sgn = LOSS == 0 ? 1.f : -1.f;
+        float* W = p.W2 + (int64_t)bh * p.dv * p.m;
+        bf16_t* w2 = p.w2 + bh * p.s_w2;
+        bf16_t* w2t = p.w2t + bh * p.s_w2;
+#pragma unroll
+        for (int i = 0; i < SW_T; ++i)
+#pragma unroll
+            for (int j = 0; j < SW_T; ++j) {
+                const int f = ct * SW_TILE + acc_col(wn, j, lane);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int n0 = rt * SW_TILE + acc_row(wm, i, q, lane);
+                    float w[4];
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        const int64_t idx = (int64_t)(n0 + x) * p.m + f;
+                        w[x] = W[idx] + sgn * acc[i][j][4 * q + x];
+                        W[idx] = w[x];
+                        w2[idx] = (bf16_t)w[x];
+                    }
+                    *reinterpret_cast<u32x2*>(w2t + (int64_t)f * p.dv + n0) =
+                        u32x2{pack2bf(w[0], w[1]), pack2bf(w[2], w[3])};
+                }
+            }
+    } else {
+        float* W1 = p.W1 + (int64_t)bh * p.m * p.dk;
+        float* W3 = p.W3 + (int64_t)bh * p.m * p.dk;
+        bf16_t* w13 = p.w13 + bh * p.s_w13;
+#pragma unroll
+        for (int i = 0; i < SW_T; ++i)
+#pragma unroll
+            for (int j = 0; j < SW_T; ++j) {
+                const int c = ct * SW_TILE + acc_col(wn, j, lane);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int R = rt * SW_TILE + acc_row(wm, i, r >> 2, lane) + (r & 3);
+                    float* Wm = (R & 1) ? W3 : W1;
+                    const int64_t idx = (int64_t)(R >> 1) * p.dk + c;
+                    const float w = Wm[idx] - acc[i][j][r];
+                    Wm[idx] = w;
+                    w13[(int64_t)R * p.dk + c] = (bf16_t)w;
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------- bf16 weight copies
+// w13 (interleaved W1 / W3 rows) and w2 from the fp32 weights; 4 elements per thread
+__global__ __launch_bounds__(256) void sw_copy_kernel(SwDev p, int BH) {
+    const int64_t n13 = (int64_t)BH * 2 * p.m * p.dk / 4, n2 = (int64_t)BH * p.dv * p.m / 4;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n13) {
+        const int64_t e = 4 * i;
+        const int64_t per = (int64_t)2 * p.m * p.dk;
+        const int64_t bh = e / per, rem = e % per;
+        const int R = (int)(rem / p.dk), c = (int)(rem % p.dk);
+        const float* src = ((R & 1) ? p.W3 : p.W1) + bh * p.m * p.dk + (int64_t)(R >> 1) * p.dk + c;
+        const f32x4 w = *reinterpret_cast<const f32x4*>(src);
+        *reinterpret_cast<u32x2*>(p.w13 + bh * p.s_w13 + rem) = u32x2{pack2bf(w[0], w[1]), pack2bf(w[2], w[3])};
+    } else if (i < n13 + n2) {
+        const int64_t e = 4 * (i - n13);
+        const int64_t per = (int64_t)p.dv * p.m;
+        const int64_t bh = e / per, rem = e % per;
+        const f32x4 w = *reinterpret_cast<const f32x4*>(p.W2 + e);
+        *reinterpret_cast<u32x2*>(p.w2 + bh * p.s_w2 + rem) = u32x2{pack2bf(w[0], w[1]), pack2bf(w[2], w[3])};
+    }
+}
+
+// w2t = W2^T in bf16, 32 x 32 tiles through LDS; grid (dv/32 * m/32, BH)
+__global__ __launch_bounds__(256) void sw_transpose_kernel(SwDev p) {
+    __shared__ float tile[32][33];
+    const int bh = blockIdx.y, nf = p.m / 32;
+    const int n0 = (blockIdx.x / nf) * 32, f0 = (blockIdx.x % nf) * 32;
+    const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    const float* W = p.W2 + (int64_t)bh * p.dv * p.m;
+    for (int r = ty; r < 32; r += 8) tile[r][tx] = W[(int64_t)(n0 + r) * p.m + f0 + tx];
+    __syncthreads();
+    bf16_t* o = p.w2t + bh * p.s_w2;
+    for (int r = ty; r < 32; r += 8) o[(int64_t)(f0 + r) * p.dv + n0 + tx] = (bf16_t)tile[tx][r];
+}
+
+// workspace layout: eight regions, each 256-byte aligned
+struct Layout {
+    int64_t off[8];
+    int64_t per[8];   // elements per head
+    size_t bytes;
+};
+Layout layout(int BH, int dk, int dv, int m, int C) {
+    Layout l{};
+    const int64_t per[8] = {(int64_t)2 * m * dk, (int64_t)dv * m, (int64_t)dv * m, (int64_t)C * m,
+                            (int64_t)C * m,      (int64_t)C * 2 * m, (int64_t)C * dv, (int64_t)C * 2 * m};
+    size_t at = 0;
+    for (int r = 0; r < 8; ++r) {
+        l.per[r] = per[r];
+        l.off[r] = (int64_t)at;
+        at += ((size_t)BH * per[r] * 2 + 255) / 256 * 256;
+    }
+    l.bytes = at;
+    return l;
+}
+
+}  // namespace
+
+bool swiglu_supported(int dk, int dv, int m, int chunk) {
+    return dk > 0 && dv > 0 && m > 0 && chunk > 0 && dk % SW_TILE == 0 && dv % SW_TILE == 0 && m % SW_TILE == 0 &&
+           chunk % SW_TILE == 0;
+}
+
+size_t swiglu_workspace(int BH, int dk, int dv, int m, int chunk) { return layout(BH, dk, dv, m, chunk).bytes; }
+
+hipError_t launch_swiglu(const SwParams& in, hipStream_t s) {
+    if (!swiglu_supported(in.dk, in.dv, in.m, in.chunk) || (in.loss != 0 && in.loss != 1)) return hipErrorInvalidValue;
+    const Layout l = layout(in.BH, in.dk, in.dv, in.m, in.chunk);
+    char* ws = reinterpret_cast<char*>(in.workspace);
+    SwDev p{};
+    p.q = reinterpret_cast<const bf16_t*>(in.q);
+    p.k = reinterpret_cast<const bf16_t*>(in.k);
+    p.v = reinterpret_cast<const bf16_t*>(in.v);
+    p.eta = in.eta;
+    p.eta_scalar = in.eta_scalar;
+    p.W1 = in.W1;
+    p.W3 = in.W3;
+    p.W2 = in.W2;
+    p.out = reinterpret_cast<bf16_t*>(in.out);
+    bf16_t** dst[8] = {&p.w13, &p.w2, &p.w2t, &p.aq, &p.ak, &p.cc, &p.dy, &p.dh};
+    for (int r = 0; r < 8; ++r) *dst[r] = reinterpret_cast<bf16_t*>(ws + l.off[r]);
+    p.s_w13 = l.per[0];
+    p.s_w2 = l.per[1];
+    p.s_act = l.per[3];
+    p.s_cc = l.per[5];
+    p.s_dy = l.per[6];
+    p.L = in.L;
+    p.dk = in.dk;
+    p.dv = in.dv;
+    p.m = in.m;
+    p.C = in.chunk;
+
+    const int64_t ncopy = ((int64_t)in.BH * 2 * in.m * in.dk + (int64_t)in.BH * in.dv * in.m) / 4;
+    hipLaunchKernelGGL(sw_copy_kernel, dim3((unsigned)((ncopy + 255) / 256)), dim3(256), 0, s, p, in.BH);
+    hipLaunchKernelGGL(sw_transpose_kernel, dim3((in.dv / 32) * (in.m / 32), in.BH), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    const int nct = in.chunk / SW_TILE;
+    const dim3 blk(SW_NT);
+    const dim3 g_fwd((2 * in.m / SW_TILE) * 2 * nct, in.BH);
+    const dim3 g_out((in.dv / SW_TILE) * (in.loss ? 2 : 1) * nct, in.BH);
+    const dim3 g_bwda((in.m / SW_TILE) * nct, in.BH);
+    const dim3 g_upd((in.dv / SW_TILE) * (in.m / SW_TILE) + (2 * in.m / SW_TILE) * (in.dk / SW_TILE), in.BH);
+    for (int c0 = 0; c0 < in.L; c0 += in.chunk) {
+        p.c0 = c0;
+        p.clen = min(in.chunk, in.L - c0);
+        if (in.loss == 0) {
+            hipLaunchKernelGGL((sw_fwd_kernel<0>), g_fwd, blk, 0, s, p);
+            hipLaunchKernelGGL((sw_out_kernel<0>), g_out, blk, 0, s, p);
+            hipLaunchKernelGGL((sw_bwda_kernel<0>), g_bwda, blk, 0, s, p);
+            hipLaunchKernelGGL((sw_upd_kernel<0>), g_upd, blk, 0, s, p);
+        } else {
+            hipLaunchKernelGGL((sw_fwd_kernel<1>), g_fwd, blk, 0, s, p);
+            hipLaunchKernelGGL((sw_out_kernel<1>), g_out, blk, 0, s, p);
+            hipLaunchKernelGGL((sw_bwda_kernel<1>), g_bwda, blk, 0, s, p);
+            hipLaunchKernelGGL((sw_upd_kernel<1>), g_upd, blk, 0, s, p);
+        }
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace ttt

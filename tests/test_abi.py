@@ -220,3 +220,44 @@ def test_workspace_plan_segments_short_grids():
     assert lac.fwd_workspace_size(1, 2, 500, 128, 128) == 0          # too short to cut
     assert lac.fwd_workspace_size(1, 1, 3000, 64, 32, beta=0.5) > 0  # 32 x 32 tile form
     assert lac.fwd_workspace_size(1, 2, 4096, 128, 128, dtype=torch.float32) == 0
+
+
+def test_swiglu_rejects_before_launch(lib):
+    B, H, L, dk, dv, m, C = 1, 2, 300, 128, 256, 256, 128
+    ws = ctypes.c_size_t(0)
+    assert lib.ttt_swiglu_workspace_size(B, H, L, dk, dv, m, C, ctypes.byref(ws)) == OK
+    # bf16 weight copies + activations of one 128-token chunk, per head
+    per = 2 * m * dk + 2 * dv * m + C * (6 * m + dv)
+    assert ws.value >= B * H * per * 2
+    assert lib.ttt_swiglu_workspace_size(B, H, L, dk, dv, m, C, None) == ERR_NULL
+    assert lib.ttt_swiglu_workspace_size(B, H, 0, dk, dv, m, C, ctypes.byref(ws)) == ERR_SHAPE
+    assert lib.ttt_swiglu_workspace_size(B, H, L, 96, dv, m, C, ctypes.byref(ws)) == ERR_UNSUP
+    assert lib.ttt_swiglu_workspace_size(B, H, L, dk, dv, 200, C, ctypes.byref(ws)) == ERR_UNSUP
+    assert lib.ttt_swiglu_workspace_size(B, H, L, dk, dv, m, 100, ctypes.byref(ws)) == ERR_UNSUP
+    big = ctypes.c_size_t(0)
+    assert lib.ttt_swiglu_workspace_size(B, H, L, dk, dv, m, 1 << 20, ctypes.byref(big)) == OK
+    assert lib.ttt_swiglu_workspace_size(B, H, 384, dk, dv, m, 1 << 20, ctypes.byref(ws)) == OK
+    assert big.value == ws.value          # a chunk past the sequence end is the whole sequence
+    assert lib.ttt_swiglu_workspace_size(1, 1, 1 << 20, 128, 128, 1 << 14, 1 << 20, ctypes.byref(ws)) == ERR_UNSUP
+    n = 1 << 26
+    need = ws.value
+
+    def call(**kw):
+        a = dict(B=B, H=H, L=L, dk=dk, dv=dv, m=m, C=C, loss=0, q=FAKE, k=FAKE + n, v=FAKE + 2 * n, eta=None,
+                 W1=FAKE + 3 * n, W3=FAKE + 4 * n, W2=FAKE + 5 * n, out=FAKE + 6 * n, ws=FAKE + 7 * n, wsb=1 << 30)
+        a.update(kw)
+        return lib.ttt_swiglu_fwd_chunked(a["B"], a["H"], a["L"], a["dk"], a["dv"], a["m"], a["C"], a["loss"], a["q"],
+                                          a["k"], a["v"], a["eta"], ctypes.c_float(0.01), a["W1"], a["W3"], a["W2"],
+                                          a["out"], a["ws"], a["wsb"], None)
+
+    assert call(loss=2) == ERR_VALUE
+    assert call(q=None) == ERR_NULL
+    assert call(W2=None) == ERR_NULL
+    assert call(out=FAKE + 6 * n + 8) == ERR_ALIGN
+    assert call(ws=None) == ERR_WS
+    assert call(wsb=16) == ERR_WS
+    assert call(dk=192) == ERR_UNSUP
+    assert call(out=FAKE + 2 * n + 512) == ERR_ALIAS     # out inside v
+    assert call(W3=FAKE + 3 * n + 1024) == ERR_ALIAS     # W3 overlaps W1
+    assert call(ws=FAKE + 5 * n) == ERR_ALIAS            # workspace on W2
+    assert call(eta=FAKE + 4 * n) == ERR_ALIAS           # eta inside W3 (written)

@@ -27,6 +27,8 @@ Workloads (shapes of the pages' settings):
   bwd         backward of lm-scale: its inputs plus cotangents dout, dS_final
   bwd-momentum backward of momentum: its inputs plus cotangents (seeds 4005, 4006)
   inplace-frontend  gated input, LM-aligned target and clipped rates, T 32768, d_model 2560, d_ff 9728
+  swiglu      large-chunk SwiGLU fast weight, B4 H4 L32768, d 512, hidden 2048, C2048,
+              per-token eta = sigmoid(N(0,1)) / C, dot inner loss (seeds 10000 + j)
 """
 from __future__ import annotations
 
@@ -229,6 +231,53 @@ def gen_state_deltas(B, H, N, dk, dv, seed=6000, scale=1.0, integer=False):
         dS = _randn((B, H, N, dk, dv), seed) * scale
         dM = _randn((B, H, N, dk, dv), seed + 1) * scale
     return dS, dM
+
+
+# --------------------------------------------------- SwiGLU fast weight
+@dataclass
+class SwigluInputs:
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    eta: torch.Tensor
+    W1: torch.Tensor
+    W3: torch.Tensor
+    W2: torch.Tensor
+    chunk: int
+    loss: str
+    config: dict = field(default_factory=dict)
+
+
+def gen_swiglu(B=4, H=4, L=32768, d=512, m=2048, chunk=2048, loss="dot", seed_base=10000, device="cpu",
+               dv=None, eta_scale=None) -> SwigluInputs:
+    """Large-chunk SwiGLU fast weight: q, k, v ~ N(0,1) bf16 [B,H,L,d] (j = 0,
+    1, 2; v has dv features, default d); eta_t = eta_scale * sigmoid(N(0,1))
+    fp32 (j = 3), eta_scale = 1 / chunk by default, which keeps the weights
+    bounded over many chunks at the benchmark's sizes; W1, W3 ~
+    N(0, 1/d) fp32 [B,H,m,d] (j = 4, 5); W2 ~ N(0, 1/m) fp32 [B,H,dv,m]
+    (j = 6).  The token tensors are drawn in row blocks so a host never holds
+    an fp32 copy of a whole large tensor; ``device`` receives every tensor."""
+    dv = d if dv is None else dv
+
+    def rows(shape, seed, scale, dtype):
+        out = torch.empty(shape, dtype=dtype, device=device)
+        g = _gen(seed)
+        flat = out.view(-1, shape[-1])
+        for r0 in range(0, flat.shape[0], 8192):
+            r1 = min(r0 + 8192, flat.shape[0])
+            flat[r0:r1].copy_((torch.randn((r1 - r0, shape[-1]), generator=g) * scale).to(dtype))
+        return out
+
+    q = rows((B, H, L, d), seed_base + 0, 1.0, torch.bfloat16)
+    k = rows((B, H, L, d), seed_base + 1, 1.0, torch.bfloat16)
+    v = rows((B, H, L, dv), seed_base + 2, 1.0, torch.bfloat16)
+    eta_scale = 1.0 / chunk if eta_scale is None else eta_scale
+    eta = (torch.sigmoid(_randn((B, H, L), seed_base + 3)) * eta_scale).to(device)
+    W1 = rows((B, H, m, d), seed_base + 4, d ** -0.5, torch.float32)
+    W3 = rows((B, H, m, d), seed_base + 5, d ** -0.5, torch.float32)
+    W2 = rows((B, H, dv, m), seed_base + 6, m ** -0.5, torch.float32)
+    return SwigluInputs(q, k, v, eta, W1, W3, W2, chunk, loss,
+                        dict(workload="swiglu", B=B, H=H, L=L, dk=d, dv=dv, m=m, chunk=chunk, loss=loss))
 
 
 def to_f64(t: torch.Tensor | None) -> np.ndarray | None:
