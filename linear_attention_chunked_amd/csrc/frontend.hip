@@ -216,8 +216,10 @@ __global__ __launch_bounds__(FE_NT) void fe_gemm_kernel(FeGemmParams p) {
                 if (GATED) {
                     // rows 2f, 2f+1 -> (gate, up) of feature f
                     const float g0 = a[4 * q], u0 = a[4 * q + 1], g1 = a[4 * q + 2], u1 = a[4 * q + 3];
-                    const float z0 = g0 / (1.f + __expf(-g0)) * u0;
-                    const float z1 = g1 / (1.f + __expf(-g1)) * u1;
+                    // silu with the hardware reciprocal (v_rcp_f32, 1 ulp), not an
+                    // IEEE division sequence
+                    const float z0 = g0 * __builtin_amdgcn_rcpf(1.f + __expf(-g0)) * u0;
+                    const float z1 = g1 * __builtin_amdgcn_rcpf(1.f + __expf(-g1)) * u1;
                     *reinterpret_cast<uint32_t*>(orow + (arow >> 1)) = pack2bf(z0, z1);
                 } else {
                     st4(orow + arow, f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]});

@@ -56,8 +56,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 constexpr int SW_BK = 32;      // k per step
 constexpr int SW_NT = 256;     // threads per workgroup (2 x 2 waves)
 constexpr int SW_NS = 4;       // k-steps of loads in flight
-constexpr int SW_T = 2;        // 32 x 32 MFMA tiles per wave and dimension
-constexpr int SW_TILE = 64 * SW_T;   // block tile 128 x 128
+constexpr int SW_TILE = 128;   // dimensions are multiples of the small block tile
 constexpr int SW_PAD = 32;     // [k][row] LDS tiles: 64-byte row pad
 
 TTT_DEV void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
@@ -136,83 +135,90 @@ struct Opnd {
     }
 };
 
-using Acc = f32x16[SW_T][SW_T];
+// TI x TJ accumulator tiles of 32 x 32 per wave: block tile (64 TI) x (64 TJ)
+template <int TI, int TJ>
+using Acc = f32x16[TI][TJ];
 
-TTT_DEV void zero(Acc& acc) {
+template <int TI, int TJ>
+TTT_DEV void zero(Acc<TI, TJ>& acc) {
 #pragma unroll
-    for (int i = 0; i < SW_T; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < SW_T; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
-// acc += A B^T over `steps` k-steps of 32 (steps a multiple of 4): four
+// acc += A B^T over `steps` k-steps of 32 (steps a multiple of 4): NS
 // k-steps of global loads in flight in registers, two LDS buffers.
-template <bool AK, bool BKR>
-struct Loop {
-    using OA = Opnd<AK, SW_T>;
-    using OB = Opnd<BKR, SW_T>;
-    static constexpr int LDS = 2 * (OA::BUF + OB::BUF);
+template <int K>
+using IC = std::integral_constant<int, K>;
 
-    TTT_DEV static void run(Acc& acc, int steps, const OA& a, const OB& b, bf16_t* smem, int tid) {
+template <bool AK, bool BKR, int TI, int TJ, int NS = SW_NS>
+struct Loop {
+    using OA = Opnd<AK, TI>;
+    using OB = Opnd<BKR, TJ>;
+    static constexpr int LDS = 2 * (OA::BUF + OB::BUF);
+    static_assert(NS >= 2 && NS <= 4, "2 to 4 register sets");
+
+    TTT_DEV static void run(Acc<TI, TJ>& acc, int steps, const OA& a, const OB& b, bf16_t* smem, int tid) {
         bf16_t* sA = smem;
         bf16_t* sB = smem + 2 * OA::BUF;
         const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-        u32x4 ra[SW_NS][SW_T], rb[SW_NS][SW_T];
+        u32x4 ra[NS][TI], rb[NS][TJ];
         auto load = [&](int st, auto SET) __attribute__((always_inline)) {
             constexpr int k = decltype(SET)::value;
             const int s = min(st, steps - 1);
 #pragma unroll
-            for (int y = 0; y < SW_T; ++y) ra[k][y] = a.load(y, s);
+            for (int y = 0; y < TI; ++y) ra[k][y] = a.load(y, s);
 #pragma unroll
-            for (int y = 0; y < SW_T; ++y) rb[k][y] = b.load(y, s);
+            for (int y = 0; y < TJ; ++y) rb[k][y] = b.load(y, s);
         };
         auto stage = [&](int buf, auto SET) __attribute__((always_inline)) {
             constexpr int k = decltype(SET)::value;
 #pragma unroll
-            for (int y = 0; y < SW_T; ++y) *reinterpret_cast<u32x4*>(&sA[buf * OA::BUF + a.lo[y]]) = ra[k][y];
+            for (int y = 0; y < TI; ++y) *reinterpret_cast<u32x4*>(&sA[buf * OA::BUF + a.lo[y]]) = ra[k][y];
 #pragma unroll
-            for (int y = 0; y < SW_T; ++y) *reinterpret_cast<u32x4*>(&sB[buf * OB::BUF + b.lo[y]]) = rb[k][y];
+            for (int y = 0; y < TJ; ++y) *reinterpret_cast<u32x4*>(&sB[buf * OB::BUF + b.lo[y]]) = rb[k][y];
         };
         auto compute = [&](int buf) __attribute__((always_inline)) {
             const bf16_t* A = sA + buf * OA::BUF;
             const bf16_t* B = sB + buf * OB::BUF;
 #pragma unroll
             for (int kk = 0; kk < SW_BK; kk += 16) {
-                bf16x8 af[SW_T], bfr[SW_T];
+                bf16x8 af[TI], bfr[TJ];
 #pragma unroll
-                for (int i = 0; i < SW_T; ++i) af[i] = a.frag(A, 32 * SW_T * wm + 32 * i, kk, lane);
+                for (int i = 0; i < TI; ++i) af[i] = a.frag(A, 32 * TI * wm + 32 * i, kk, lane);
 #pragma unroll
-                for (int j = 0; j < SW_T; ++j) bfr[j] = b.frag(B, 32 * SW_T * wn + 32 * j, kk, lane);
+                for (int j = 0; j < TJ; ++j) bfr[j] = b.frag(B, 32 * TJ * wn + 32 * j, kk, lane);
 #pragma unroll
-                for (int i = 0; i < SW_T; ++i)
+                for (int i = 0; i < TI; ++i)
 #pragma unroll
-                    for (int j = 0; j < SW_T; ++j) mma32(acc[i][j], af[i], bfr[j]);
+                    for (int j = 0; j < TJ; ++j) mma32(acc[i][j], af[i], bfr[j]);
             }
         };
-        using K0 = std::integral_constant<int, 0>;
-        using K1 = std::integral_constant<int, 1>;
-        using K2 = std::integral_constant<int, 2>;
-        using K3 = std::integral_constant<int, 3>;
-        load(0, K0{});
-        load(1, K1{});
-        load(2, K2{});
-        load(3, K3{});
-        stage(0, K0{});
+        load(0, IC<0>{});
+        load(1, IC<1>{});
+        if constexpr (NS > 2) load(2, IC<2>{});
+        if constexpr (NS > 3) load(3, IC<3>{});
+        stage(0, IC<0>{});
         __syncthreads();
+        // refill the set this step frees, compute from LDS, write step st+1
+        // to the other LDS buffer
         auto step = [&](int st, auto CUR, auto NXT) __attribute__((always_inline)) {
-            load(st + SW_NS, CUR);
+            load(st + NS, CUR);
             compute(st & 1);
             __builtin_amdgcn_sched_barrier(0);
             if (st + 1 < steps) stage((st + 1) & 1, NXT);
             __syncthreads();
         };
-        for (int st = 0; st < steps; st += SW_NS) {
-            step(st, K0{}, K1{});
-            step(st + 1, K1{}, K2{});
-            step(st + 2, K2{}, K3{});
-            step(st + 3, K3{}, K0{});
+        for (int st = 0; st < steps; st += NS) {
+            step(st, IC<0>{}, IC<1 % NS>{});
+            if (st + 1 < steps) step(st + 1, IC<1 % NS>{}, IC<2 % NS>{});
+            if constexpr (NS > 2)
+                if (st + 2 < steps) step(st + 2, IC<2 % NS>{}, IC<3 % NS>{});
+            if constexpr (NS > 3)
+                if (st + 3 < steps) step(st + 3, IC<3 % NS>{}, IC<4 % NS>{});
         }
     }
 };
@@ -233,10 +239,12 @@ TTT_DEV void tile_id(int nrow, int ncol, int* bh, int* rt, int* ct) {
     *rt = r / gsz;
 }
 
-// accumulator (i, j, r) -> row 64 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
-// column 64 wn + 32 j + lane % 32 of the block tile
-TTT_DEV int acc_row(int wm, int i, int q, int lane) { return 64 * wm + 32 * i + 8 * q + 4 * (lane >> 5); }
-TTT_DEV int acc_col(int wn, int j, int lane) { return 64 * wn + 32 * j + (lane & 31); }
+// accumulator (i, j, r) -> row 32 TI wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
+// column 32 TJ wn + 32 j + lane % 32 of the block tile
+template <int TI>
+TTT_DEV int acc_row(int wm, int i, int q, int lane) { return 32 * TI * wm + 32 * i + 8 * q + 4 * (lane >> 5); }
+template <int TJ>
+TTT_DEV int acc_col(int wn, int j, int lane) { return 32 * TJ * wn + 32 * j + (lane & 31); }
 
 // Kernel arguments: base pointers (head 0) and per-head strides in elements.
 struct SwDev {
@@ -264,97 +272,122 @@ struct SwDev {
 TTT_DEV float eta_at(const SwDev& p, int bh, int t) {
     return p.eta ? p.eta[(int64_t)bh * p.L + t] : p.eta_scalar;
 }
-TTT_DEV float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+// logistic sigmoid with the hardware reciprocal (v_rcp_f32, 1 ulp) instead of
+// an IEEE division sequence; exp(-x) = inf gives 0
+TTT_DEV float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 
 // ------------------------------------------------------------ forward GEMM
 // tile (row tile of W13, token tile of [Q_i; K_i]); K = dk
-template <int LOSS>
+template <int LOSS, int TI, int TJ>
 __global__ __launch_bounds__(SW_NT) void sw_fwd_kernel(SwDev p) {
-    using LP = Loop<false, false>;
-    __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
+    constexpr int BM = 64 * TI, BN = 64 * TJ;
+    using LP = Loop<false, false, TI, TJ>;
+    // epilogue staging: A [BN tokens][BM/2 + 4] and (K rows) c1, c3 [BN][BM + 4]
+    constexpr int AW = BM / 2, LA = AW + 4, LC = BM + 4;
+    constexpr int STAGE = BN * (LA + LC);
+    __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS > STAGE ? LP::LDS : STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const int nct = p.C / SW_TILE;
+    const int nct = p.C / BN;
     int bh, rt, ct;
-    tile_id(2 * p.m / SW_TILE, 2 * nct, &bh, &rt, &ct);
+    tile_id(2 * p.m / BM, 2 * nct, &bh, &rt, &ct);
     const bool isK = ct >= nct;
-    const int tok0 = (isK ? ct - nct : ct) * SW_TILE;
-    Acc acc;
+    const int tok0 = (isK ? ct - nct : ct) * BN;
+    Acc<TI, TJ> acc;
     zero(acc);
     if (tok0 < p.clen) {
         typename LP::OA a;
         typename LP::OB b;
-        a.init(p.w13 + bh * p.s_w13, p.dk, rt * SW_TILE, 2 * p.m, tid);
+        a.init(p.w13 + bh * p.s_w13, p.dk, rt * BM, 2 * p.m, tid);
         b.init((isK ? p.k : p.q) + ((int64_t)bh * p.L + p.c0) * p.dk, p.dk, tok0, p.L - p.c0, tid);
         LP::run(acc, p.dk / SW_BK, a, b, smem, tid);
     }
-    bf16_t* dst = (isK ? p.ak : p.aq) + bh * p.s_act;
-    bf16_t* ccb = p.cc + bh * p.s_cc;
+    // the SwiGLU values go through LDS ([token][feature]) so that the stores
+    // to the token-major buffers are whole row segments
+    __syncthreads();
+    bf16_t* sA = smem;
+    bf16_t* sC = smem + BN * LA;
 #pragma unroll
-    for (int j = 0; j < SW_T; ++j) {
-        const int tc = tok0 + acc_col(wn, j, lane);
+    for (int j = 0; j < TJ; ++j) {
+        const int tl = acc_col<TJ>(wn, j, lane), tc = tok0 + tl;
         const bool live = tc < p.clen;
-        if (!isK && !live) continue;
-        const float e = (LOSS == 0 && isK && live) ? eta_at(p, bh, p.c0 + tc) : 1.f;
-        bf16_t* drow = dst + (int64_t)tc * p.m;
-        bf16_t* crow = ccb + (int64_t)tc * 2 * p.m;
+        // K rows: eta_t folded in for loss 0; zero past the sequence end
+        const float e = !isK ? 1.f : !live ? 0.f : (LOSS == 0 ? eta_at(p, bh, p.c0 + tc) : 1.f);
 #pragma unroll
-        for (int i = 0; i < SW_T; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int f0 = (rt * SW_TILE + acc_row(wm, i, q, lane)) >> 1;   // rows 2 f0 .. 2 f0 + 3
+                const int fl = acc_row<TI>(wm, i, q, lane) >> 1;   // local features fl, fl + 1
                 const float g0 = acc[i][j][4 * q], u0 = acc[i][j][4 * q + 1];
                 const float g1 = acc[i][j][4 * q + 2], u1 = acc[i][j][4 * q + 3];
                 const float sg0 = sigm(g0), sg1 = sigm(g1);
                 const float s0 = g0 * sg0, s1 = g1 * sg1;
-                if (!isK) {
-                    *reinterpret_cast<uint32_t*>(drow + f0) = pack2bf(s0 * u0, s1 * u1);
-                } else if (live) {
-                    *reinterpret_cast<uint32_t*>(drow + f0) = pack2bf(e * s0 * u0, e * s1 * u1);
+                *reinterpret_cast<uint32_t*>(sA + tl * LA + fl) = pack2bf(e * s0 * u0, e * s1 * u1);
+                if (isK) {
                     const float c10 = u0 * sg0 * (1.f + g0 * (1.f - sg0));
                     const float c11 = u1 * sg1 * (1.f + g1 * (1.f - sg1));
-                    *reinterpret_cast<u32x2*>(crow + 2 * f0) = u32x2{pack2bf(c10, s0), pack2bf(c11, s1)};
-                } else {
-                    *reinterpret_cast<uint32_t*>(drow + f0) = 0u;
-                    *reinterpret_cast<u32x2*>(crow + 2 * f0) = u32x2{0u, 0u};
+                    *reinterpret_cast<u32x2*>(sC + tl * LC + 2 * fl) =
+                        live ? u32x2{pack2bf(c10, s0), pack2bf(c11, s1)} : u32x2{0u, 0u};
                 }
             }
+    }
+    __syncthreads();
+    // copy-out in 8-byte pieces, consecutive threads along a token's row
+    // (K rows past the sequence end hold zeros; Q rows past it are not stored)
+    const int f_base = rt * AW;
+    bf16_t* dst = (isK ? p.ak : p.aq) + bh * p.s_act;
+    constexpr int PA = AW / 4;
+    for (int x = tid; x < BN * PA; x += SW_NT) {
+        const int tl = x / PA, pc = x % PA, tc = tok0 + tl;
+        if (!isK && tc >= p.clen) continue;
+        *reinterpret_cast<u32x2*>(dst + (int64_t)tc * p.m + f_base + 4 * pc) =
+            *reinterpret_cast<const u32x2*>(sA + tl * LA + 4 * pc);
+    }
+    if (isK) {
+        bf16_t* ccb = p.cc + bh * p.s_cc;
+        constexpr int PC = BM / 4;
+        for (int x = tid; x < BN * PC; x += SW_NT) {
+            const int tl = x / PC, pc = x % PC, tc = tok0 + tl;
+            *reinterpret_cast<u32x2*>(ccb + (int64_t)tc * 2 * p.m + 2 * f_base + 4 * pc) =
+                *reinterpret_cast<const u32x2*>(sC + tl * LC + 4 * pc);
+        }
     }
 }
 
 // ------------------------------------------------------------- output GEMM
 // tile (row tile of W2 = output features, token tile of A_Q, then of A_K for
 // loss 1); K = m
-template <int LOSS>
+template <int LOSS, int TI, int TJ>
 __global__ __launch_bounds__(SW_NT) void sw_out_kernel(SwDev p) {
-    using LP = Loop<false, false>;
+    constexpr int BM = 64 * TI, BN = 64 * TJ;
+    using LP = Loop<false, false, TI, TJ>;
     __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const int nct = p.C / SW_TILE;
+    const int nct = p.C / BN;
     int bh, rt, ct;
-    tile_id(p.dv / SW_TILE, LOSS ? 2 * nct : nct, &bh, &rt, &ct);
+    tile_id(p.dv / BM, LOSS ? 2 * nct : nct, &bh, &rt, &ct);
     const bool isK = ct >= nct;
-    const int tok0 = (isK ? ct - nct : ct) * SW_TILE;
-    Acc acc;
+    const int tok0 = (isK ? ct - nct : ct) * BN;
+    Acc<TI, TJ> acc;
     zero(acc);
     if (tok0 < p.clen) {
         typename LP::OA a;
         typename LP::OB b;
-        a.init(p.w2 + bh * p.s_w2, p.m, rt * SW_TILE, p.dv, tid);
+        a.init(p.w2 + bh * p.s_w2, p.m, rt * BM, p.dv, tid);
         b.init((isK ? p.ak : p.aq) + bh * p.s_act, p.m, tok0, p.C, tid);
         LP::run(acc, p.m / SW_BK, a, b, smem, tid);
     }
 #pragma unroll
-    for (int j = 0; j < SW_T; ++j) {
-        const int tc = tok0 + acc_col(wn, j, lane);
+    for (int j = 0; j < TJ; ++j) {
+        const int tc = tok0 + acc_col<TJ>(wn, j, lane);
         const bool live = tc < p.clen;
         if (!isK) {
             if (!live) continue;
             bf16_t* orow = p.out + ((int64_t)bh * p.L + p.c0 + tc) * p.dv;
 #pragma unroll
-            for (int i = 0; i < SW_T; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int n = rt * SW_TILE + acc_row(wm, i, q, lane);
+                    const int n = rt * BM + acc_row<TI>(wm, i, q, lane);
                     st4(orow + n, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                                         acc[i][j][4 * q + 3]});
                 }
@@ -364,10 +397,10 @@ __global__ __launch_bounds__(SW_NT) void sw_out_kernel(SwDev p) {
             const bf16_t* vrow = p.v + ((int64_t)bh * p.L + p.c0 + min(tc, p.clen - 1)) * p.dv;
             bf16_t* yrow = p.dy + bh * p.s_dy + (int64_t)tc * p.dv;
 #pragma unroll
-            for (int i = 0; i < SW_T; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int n = rt * SW_TILE + acc_row(wm, i, q, lane);
+                    const int n = rt * BM + acc_row<TI>(wm, i, q, lane);
                     const u32x2 vv = *reinterpret_cast<const u32x2*>(vrow + n);
                     f32x4 d;
                     d[0] = e * (acc[i][j][4 * q] - __uint_as_float(vv[0] << 16));
@@ -384,20 +417,21 @@ __global__ __launch_bounds__(SW_NT) void sw_out_kernel(SwDev p) {
 // ----------------------------------------------------- dA and dH (K rows)
 // tile (row tile of W2^T = hidden units, token tile); K = dv.  loss 0 reads
 // V in place of dY and scales by -eta_t.
-template <int LOSS>
+template <int LOSS, int TI, int TJ>
 __global__ __launch_bounds__(SW_NT) void sw_bwda_kernel(SwDev p) {
-    using LP = Loop<false, false>;
+    constexpr int BM = 64 * TI, BN = 64 * TJ;
+    using LP = Loop<false, false, TI, TJ>;
     __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     int bh, rt, ct;
-    tile_id(p.m / SW_TILE, p.C / SW_TILE, &bh, &rt, &ct);
-    const int tok0 = ct * SW_TILE;
-    Acc acc;
+    tile_id(p.m / BM, p.C / BN, &bh, &rt, &ct);
+    const int tok0 = ct * BN;
+    Acc<TI, TJ> acc;
     zero(acc);
     if (tok0 < p.clen) {
         typename LP::OA a;
         typename LP::OB b;
-        a.init(p.w2t + bh * p.s_w2, p.dv, rt * SW_TILE, p.m, tid);
+        a.init(p.w2t + bh * p.s_w2, p.dv, rt * BM, p.m, tid);
         if (LOSS == 0) b.init(p.v + ((int64_t)bh * p.L + p.c0) * p.dv, p.dv, tok0, p.L - p.c0, tid);
         else b.init(p.dy + bh * p.s_dy, p.dv, tok0, p.C, tid);
         LP::run(acc, p.dv / SW_BK, a, b, smem, tid);
@@ -405,17 +439,17 @@ __global__ __launch_bounds__(SW_NT) void sw_bwda_kernel(SwDev p) {
     const bf16_t* ccb = p.cc + bh * p.s_cc;
     bf16_t* dhb = p.dh + bh * p.s_cc;
 #pragma unroll
-    for (int j = 0; j < SW_T; ++j) {
-        const int tc = tok0 + acc_col(wn, j, lane);
+    for (int j = 0; j < TJ; ++j) {
+        const int tc = tok0 + acc_col<TJ>(wn, j, lane);
         const bool live = tc < p.clen;
         const float sc = !live ? 0.f : (LOSS == 0 ? -eta_at(p, bh, p.c0 + tc) : 1.f);
         const bf16_t* crow = ccb + (int64_t)tc * 2 * p.m;
         bf16_t* hrow = dhb + (int64_t)tc * 2 * p.m;
 #pragma unroll
-        for (int i = 0; i < SW_T; ++i)
+        for (int i = 0; i < TI; ++i)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int f0 = rt * SW_TILE + acc_row(wm, i, q, lane);   // hidden units f0 .. f0 + 3
+                const int f0 = rt * BM + acc_row<TI>(wm, i, q, lane);   // hidden units f0 .. f0 + 3
                 const u32x4 c = *reinterpret_cast<const u32x4*>(crow + 2 * f0);
                 u32x4 o;
 #pragma unroll
@@ -434,13 +468,15 @@ __global__ __launch_bounds__(SW_NT) void sw_bwda_kernel(SwDev p) {
 //   dW2[n][f]   = sum_t dY[t][n] A_K[t][f]   (loss 0: V and eta_t A_K, sign +)
 //   dW13[r][c]  = sum_t dH[t][r] K[t][c]
 // W <- W - dW in fp32, then the bf16 copies.
-template <int LOSS>
-__global__ __launch_bounds__(SW_NT) void sw_upd_kernel(SwDev p) {
-    using LP = Loop<true, true>;
+template <int LOSS, int TI, int TJ>
+__global__ __launch_bounds__(SW_NT, 2) void sw_upd_kernel(SwDev p) {
+    constexpr int BM = 64 * TI, BN = 64 * TJ;
+    // three register sets in flight; the launch bound asks for two waves per SIMD
+    using LP = Loop<true, true, TI, TJ, (TI == 4 ? 3 : 4)>;
     __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const int n4r = p.dv / SW_TILE, n4c = p.m / SW_TILE;
-    const int n5r = 2 * p.m / SW_TILE, n5c = p.dk / SW_TILE;
+    const int n4r = p.dv / BM, n4c = p.m / BN;
+    const int n5r = 2 * p.m / BM, n5c = p.dk / BN;
     const int n4 = n4r * n4c, n5 = n5r * n5c;
     const int lid = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
     const int bh = lid / (n4 + n5), t = lid % (n4 + n5);
@@ -450,63 +486,70 @@ __global__ __launch_bounds__(SW_NT) void sw_upd_kernel(SwDev p) {
     typename LP::OA a;
     typename LP::OB b;
     if (!is5) {
-        if (LOSS == 0) a.init(p.v + ((int64_t)bh * p.L + p.c0) * p.dv, p.dv, rt * SW_TILE, p.L - p.c0, tid);
-        else a.init(p.dy + bh * p.s_dy, p.dv, rt * SW_TILE, p.C, tid);
-        b.init(p.ak + bh * p.s_act, p.m, ct * SW_TILE, p.C, tid);
+        if (LOSS == 0) a.init(p.v + ((int64_t)bh * p.L + p.c0) * p.dv, p.dv, rt * BM, p.L - p.c0, tid);
+        else a.init(p.dy + bh * p.s_dy, p.dv, rt * BM, p.C, tid);
+        b.init(p.ak + bh * p.s_act, p.m, ct * BN, p.C, tid);
     } else {
-        a.init(p.dh + bh * p.s_cc, 2 * p.m, rt * SW_TILE, p.C, tid);
-        b.init(p.k + ((int64_t)bh * p.L + p.c0) * p.dk, p.dk, ct * SW_TILE, p.L - p.c0, tid);
+        a.init(p.dh + bh * p.s_cc, 2 * p.m, rt * BM, p.C, tid);
+        b.init(p.k + ((int64_t)bh * p.L + p.c0) * p.dk, p.dk, ct * BN, p.L - p.c0, tid);
     }
-    Acc acc;
+    Acc<TI, TJ> acc;
     zero(acc);
     // tokens past the sequence end carry zero A_K and zero dH: the last,
     // shorter chunk still runs whole 128-token groups
     const int steps = ((p.clen + 127) / 128) * (128 / SW_BK);
     LP::run(acc, steps, a, b, smem, tid);
-    if (!is5) {
-        const float sgn = LOSS == 0 ? 1.f : -1.f;
-        float* W = p.W2 + (int64_t)bh * p.dv * p.m;
-        bf16_t* w2 = p.w2 + bh * p.s_w2;
-        bf16_t* w2t = p.w2t + bh * p.s_w2;
+
+    // Epilogue, one accumulator row block i at a time through LDS (64 rows x
+    // BN fp32): W_new = W + sign * dW with 16-byte read-modify-writes along
+    // the master rows, the bf16 copies from the same values.
+    constexpr int LDE = BN + 4;
+    static_assert(64 * LDE * 4 <= LP::LDS * 2, "epilogue staging fits the main loop's LDS");
+    float* sE = reinterpret_cast<float*>(smem);
+    const float sgn = (!is5 && LOSS == 0) ? 1.f : -1.f;
+    // staged row l (0..63) -> tile row: l < 32 from wave row 0, else wave row 1
+    auto tile_row = [&](int l, int i) { return (l < 32 ? 0 : 32 * TI - 32) + 32 * i + l; };
 #pragma unroll
-        for (int i = 0; i < SW_T; ++i)
+    for (int i = 0; i < TI; ++i) {
+        __syncthreads();
 #pragma unroll
-            for (int j = 0; j < SW_T; ++j) {
-                const int f = ct * SW_TILE + acc_col(wn, j, lane);
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int n0 = rt * SW_TILE + acc_row(wm, i, q, lane);
-                    float w[4];
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) {
-                        const int64_t idx = (int64_t)(n0 + x) * p.m + f;
-                        w[x] = W[idx] + sgn * acc[i][j][4 * q + x];
-                        W[idx] = w[x];
-                        w2[idx] = (bf16_t)w[x];
-                    }
-                    *reinterpret_cast<u32x2*>(w2t + (int64_t)f * p.dv + n0) =
-                        u32x2{pack2bf(w[0], w[1]), pack2bf(w[2], w[3])};
-                }
+            for (int r = 0; r < 16; ++r) {
+                const int l = 32 * wm + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                sE[l * LDE + acc_col<TJ>(wn, j, lane)] = acc[i][j][r];
             }
-    } else {
-        float* W1 = p.W1 + (int64_t)bh * p.m * p.dk;
-        float* W3 = p.W3 + (int64_t)bh * p.m * p.dk;
-        bf16_t* w13 = p.w13 + bh * p.s_w13;
-#pragma unroll
-        for (int i = 0; i < SW_T; ++i)
-#pragma unroll
-            for (int j = 0; j < SW_T; ++j) {
-                const int c = ct * SW_TILE + acc_col(wn, j, lane);
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int R = rt * SW_TILE + acc_row(wm, i, r >> 2, lane) + (r & 3);
-                    float* Wm = (R & 1) ? W3 : W1;
-                    const int64_t idx = (int64_t)(R >> 1) * p.dk + c;
-                    const float w = Wm[idx] - acc[i][j][r];
-                    Wm[idx] = w;
-                    w13[(int64_t)R * p.dk + c] = (bf16_t)w;
-                }
+        __syncthreads();
+        constexpr int P4 = BN / 4;
+        for (int x = tid; x < 64 * P4; x += SW_NT) {
+            const int l = x / P4, c4 = 4 * (x % P4);
+            const int R = rt * BM + tile_row(l, i), col = ct * BN + c4;
+            f32x4 d = *reinterpret_cast<const f32x4*>(sE + l * LDE + c4);
+            float* wp;
+            bf16_t* cp;
+            if (!is5) {
+                wp = p.W2 + (int64_t)bh * p.dv * p.m + (int64_t)R * p.m + col;
+                cp = p.w2 + bh * p.s_w2 + (int64_t)R * p.m + col;
+            } else {
+                wp = ((R & 1) ? p.W3 : p.W1) + (int64_t)bh * p.m * p.dk + (int64_t)(R >> 1) * p.dk + col;
+                cp = p.w13 + bh * p.s_w13 + (int64_t)R * p.dk + col;
             }
+            const f32x4 w = *reinterpret_cast<const f32x4*>(wp) + sgn * d;
+            *reinterpret_cast<f32x4*>(wp) = w;
+            *reinterpret_cast<u32x2*>(cp) = u32x2{pack2bf(w[0], w[1]), pack2bf(w[2], w[3])};
+            if (!is5) *reinterpret_cast<f32x4*>(sE + l * LDE + c4) = w;
+        }
+        if (!is5) {
+            // W2^T copy: 4 consecutive rows n of one column f per 8-byte store
+            __syncthreads();
+            for (int x = tid; x < 16 * BN; x += SW_NT) {
+                const int g = x % 16, fl = x / 16, l = 4 * g;
+                const int n0 = rt * BM + tile_row(l, i), f = ct * BN + fl;
+                const float* e = sE + l * LDE + fl;
+                *reinterpret_cast<u32x2*>(p.w2t + bh * p.s_w2 + (int64_t)f * p.dv + n0) =
+                    u32x2{pack2bf(e[0], e[LDE]), pack2bf(e[2 * LDE], e[3 * LDE])};
+            }
+        }
     }
 }
 
@@ -565,6 +608,26 @@ Layout layout(int BH, int dk, int dv, int m, int C) {
     return l;
 }
 
+// one chunk: forward, output, dA / dH, weight update.  The forward and
+// output GEMMs run 128 x 128 tiles (K = dk and m; their many small-row
+// epilogue stores favour more, smaller workgroups); with BIG the dA GEMM runs
+// 256 x 256 and the update 256 x 128 tiles (measured fastest per kernel).
+template <int LOSS, bool BIG>
+hipError_t chunk_step(const SwDev& p, const SwParams& in, hipStream_t s) {
+    constexpr int F = BIG ? 4 : 2;
+    const dim3 blk(SW_NT);
+    const int C = in.chunk;
+    const dim3 g_fwd((2 * in.m / 128) * (2 * C / 128), in.BH);
+    const dim3 g_out((in.dv / 128) * (LOSS ? 2 : 1) * (C / 128), in.BH);
+    const dim3 g_bwda((in.m / (64 * F)) * (C / (64 * F)), in.BH);
+    const dim3 g_upd((in.dv / (64 * F)) * (in.m / 128) + (2 * in.m / (64 * F)) * (in.dk / 128), in.BH);
+    hipLaunchKernelGGL((sw_fwd_kernel<LOSS, 2, 2>), g_fwd, blk, 0, s, p);
+    hipLaunchKernelGGL((sw_out_kernel<LOSS, 2, 2>), g_out, blk, 0, s, p);
+    hipLaunchKernelGGL((sw_bwda_kernel<LOSS, F, F>), g_bwda, blk, 0, s, p);
+    hipLaunchKernelGGL((sw_upd_kernel<LOSS, F, 2>), g_upd, blk, 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool swiglu_supported(int dk, int dv, int m, int chunk) {
@@ -607,27 +670,13 @@ hipError_t launch_swiglu(const SwParams& in, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    const int nct = in.chunk / SW_TILE;
-    const dim3 blk(SW_NT);
-    const dim3 g_fwd((2 * in.m / SW_TILE) * 2 * nct, in.BH);
-    const dim3 g_out((in.dv / SW_TILE) * (in.loss ? 2 : 1) * nct, in.BH);
-    const dim3 g_bwda((in.m / SW_TILE) * nct, in.BH);
-    const dim3 g_upd((in.dv / SW_TILE) * (in.m / SW_TILE) + (2 * in.m / SW_TILE) * (in.dk / SW_TILE), in.BH);
+    // big tiles (256-row / 256-token blocks) where the sizes allow, else 128 x 128
+    const bool big = in.m % 256 == 0 && in.dv % 256 == 0 && in.chunk % 256 == 0;
     for (int c0 = 0; c0 < in.L; c0 += in.chunk) {
         p.c0 = c0;
         p.clen = min(in.chunk, in.L - c0);
-        if (in.loss == 0) {
-            hipLaunchKernelGGL((sw_fwd_kernel<0>), g_fwd, blk, 0, s, p);
-            hipLaunchKernelGGL((sw_out_kernel<0>), g_out, blk, 0, s, p);
-            hipLaunchKernelGGL((sw_bwda_kernel<0>), g_bwda, blk, 0, s, p);
-            hipLaunchKernelGGL((sw_upd_kernel<0>), g_upd, blk, 0, s, p);
-        } else {
-            hipLaunchKernelGGL((sw_fwd_kernel<1>), g_fwd, blk, 0, s, p);
-            hipLaunchKernelGGL((sw_out_kernel<1>), g_out, blk, 0, s, p);
-            hipLaunchKernelGGL((sw_bwda_kernel<1>), g_bwda, blk, 0, s, p);
-            hipLaunchKernelGGL((sw_upd_kernel<1>), g_upd, blk, 0, s, p);
-        }
-        e = hipGetLastError();
+        if (in.loss == 0) e = big ? chunk_step<0, true>(p, in, s) : chunk_step<0, false>(p, in, s);
+        else e = big ? chunk_step<1, true>(p, in, s) : chunk_step<1, false>(p, in, s);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
