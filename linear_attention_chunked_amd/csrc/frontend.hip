@@ -127,7 +127,10 @@ struct Core {
             load(st + FE_NS, CUR);
             compute(st & 1);
             __builtin_amdgcn_sched_barrier(0);
-            if (st + 1 < steps) stage((st + 1) & 1, NXT);
+            // unconditional: after the last step it writes clamped, unused data to
+            // the idle buffer, and no path skips the wait for this set's loads
+            // (a skipped wait makes the compiler stall the next reuse of its registers)
+            stage((st + 1) & 1, NXT);
             __syncthreads();
         };
         // steps is a multiple of 4 (K a multiple of 128)

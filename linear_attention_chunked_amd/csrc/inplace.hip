@@ -242,7 +242,10 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
         load(st + NS, CUR);
         compute(st & 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (st + 1 < full_steps) stage((st + 1) & 1, NXT);
+        // unconditional: after the last whole step it writes clamped, unused
+        // data to the idle buffer (the tail below rewrites buffer 0 after a
+        // barrier), and no path skips the wait for this set's loads
+        stage((st + 1) & 1, NXT);
         __syncthreads();
     };
     // chunk boundaries fall on multiples of kpc (a multiple of 8), so they
@@ -428,7 +431,9 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
         load(st + NS, CUR);
         compute(st & 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (st + 1 < steps) stage((st + 1) & 1, NXT);
+        // unconditional (clamped, unused data after the last step): no path
+        // skips the wait for this set's loads
+        stage((st + 1) & 1, NXT);
         __syncthreads();
     };
     // steps is a multiple of 8 (dk a multiple of 256)

@@ -204,21 +204,34 @@ struct Loop {
         stage(0, IC<0>{});
         __syncthreads();
         // refill the set this step frees, compute from LDS, write step st+1
-        // to the other LDS buffer
+        // to the other LDS buffer.  The write is unconditional (after the last
+        // step it stores clamped, unused data into the idle buffer): a
+        // conditional write leaves a path on which the set's load was never
+        // waited for, and the wait the compiler then puts before the next
+        // reuse of those registers stalls every step.
         auto step = [&](int st, auto CUR, auto NXT) __attribute__((always_inline)) {
             load(st + NS, CUR);
             compute(st & 1);
             __builtin_amdgcn_sched_barrier(0);
-            if (st + 1 < steps) stage((st + 1) & 1, NXT);
+            stage((st + 1) & 1, NXT);
             __syncthreads();
         };
-        for (int st = 0; st < steps; st += NS) {
-            step(st, IC<0>{}, IC<1 % NS>{});
-            if (st + 1 < steps) step(st + 1, IC<1 % NS>{}, IC<2 % NS>{});
-            if constexpr (NS > 2)
-                if (st + 2 < steps) step(st + 2, IC<2 % NS>{}, IC<3 % NS>{});
-            if constexpr (NS > 3)
-                if (st + 3 < steps) step(st + 3, IC<3 % NS>{}, IC<4 % NS>{});
+        if constexpr (NS == 2 || NS == 4) {
+            // steps is a multiple of 4: whole groups, no branch inside
+            for (int st = 0; st < steps; st += NS) {
+                step(st, IC<0>{}, IC<1 % NS>{});
+                step(st + 1, IC<1 % NS>{}, IC<2 % NS>{});
+                if constexpr (NS > 3) {
+                    step(st + 2, IC<2>{}, IC<3>{});
+                    step(st + 3, IC<3>{}, IC<0>{});
+                }
+            }
+        } else {
+            for (int st = 0; st < steps; st += NS) {
+                step(st, IC<0>{}, IC<1>{});
+                if (st + 1 < steps) step(st + 1, IC<1>{}, IC<2>{});
+                if (st + 2 < steps) step(st + 2, IC<2>{}, IC<0>{});
+            }
         }
     }
 };
@@ -282,14 +295,15 @@ template <int LOSS, int TI, int TJ>
 __global__ __launch_bounds__(SW_NT) void sw_fwd_kernel(SwDev p) {
     constexpr int BM = 64 * TI, BN = 64 * TJ;
     using LP = Loop<false, false, TI, TJ>;
-    // epilogue staging: A [BN tokens][BM/2 + 4] and (K rows) c1, c3 [BN][BM + 4]
+    // epilogue staging: A [BN tokens][BM/2 + 4] and (K rows, loss 1) c1, c3 [BN][BM + 4]
     constexpr int AW = BM / 2, LA = AW + 4, LC = BM + 4;
-    constexpr int STAGE = BN * (LA + LC);
+    constexpr int STAGE = BN * (LA + (LOSS == 1 ? LC : 0));
     __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS > STAGE ? LP::LDS : STAGE];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     const int nct = p.C / BN;
     int bh, rt, ct;
-    tile_id(2 * p.m / BM, 2 * nct, &bh, &rt, &ct);
+    // the binding loss runs its K rows in sw_fwdk_kernel
+    tile_id(2 * p.m / BM, (LOSS == 0 ? 1 : 2) * nct, &bh, &rt, &ct);
     const bool isK = ct >= nct;
     const int tok0 = (isK ? ct - nct : ct) * BN;
     Acc<TI, TJ> acc;
@@ -350,6 +364,108 @@ __global__ __launch_bounds__(SW_NT) void sw_fwd_kernel(SwDev p) {
             *reinterpret_cast<u32x2*>(ccb + (int64_t)tc * 2 * p.m + 2 * f_base + 4 * pc) =
                 *reinterpret_cast<const u32x2*>(sC + tl * LC + 4 * pc);
         }
+    }
+}
+
+// ---------------------------------------- K rows, binding loss: forward + dA
+// For loss 0, dY = -eta_t V does not depend on the forward, so one workgroup
+// computes for its 128 K tokens and 64 hidden units both H = K W13^T (K = dk)
+// and dA = V W2 (K = dv, 64 x 128), and writes eta_t A and dH straight away:
+// no (c1, c3) buffer and no separate dA launch.  dA goes through LDS to meet
+// the forward's lane layout (a lane holds two hidden units of one token).
+__global__ __launch_bounds__(SW_NT) void sw_fwdk_kernel(SwDev p) {
+    constexpr int TI = 2, TJ = 2, BM = 128, BN = 128;
+    using LH = Loop<false, false, TI, TJ>;
+    using LDa = Loop<false, false, 1, TJ>;
+    constexpr int AW = BM / 2, LA = AW + 4, LHD = BM + 4, LDD = AW + 4;
+    constexpr int STAGE = BN * (LA + LHD);
+    constexpr int SM = LH::LDS > STAGE ? LH::LDS : STAGE;
+    static_assert(BN * LDD * 2 <= SM && LDa::LDS <= SM, "dA staging and its main loop fit");
+    __shared__ __attribute__((aligned(16))) bf16_t smem[SM];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    int bh, rt, ct;
+    tile_id(2 * p.m / BM, p.C / BN, &bh, &rt, &ct);
+    const int tok0 = ct * BN;
+    Acc<TI, TJ> acc;
+    Acc<1, TJ> dacc;
+    zero(acc);
+    zero(dacc);
+    if (tok0 < p.clen) {
+        {
+            typename LH::OA a;
+            typename LH::OB b;
+            a.init(p.w13 + bh * p.s_w13, p.dk, rt * BM, 2 * p.m, tid);
+            b.init(p.k + ((int64_t)bh * p.L + p.c0) * p.dk, p.dk, tok0, p.L - p.c0, tid);
+            LH::run(acc, p.dk / SW_BK, a, b, smem, tid);
+        }
+        {
+            typename LDa::OA a;
+            typename LDa::OB b;
+            a.init(p.w2t + bh * p.s_w2, p.dv, rt * AW, p.m, tid);
+            b.init(p.v + ((int64_t)bh * p.L + p.c0) * p.dv, p.dv, tok0, p.L - p.c0, tid);
+            LDa::run(dacc, p.dv / SW_BK, a, b, smem, tid);
+        }
+    }
+    __syncthreads();
+    float* sD = reinterpret_cast<float*>(smem);   // dA [token][unit]
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            sD[acc_col<TJ>(wn, j, lane) * LDD + acc_row<1>(wm, 0, r >> 2, lane) + (r & 3)] = dacc[0][j][r];
+    __syncthreads();
+    uint32_t oa[TI][TJ][4];
+    u32x2 oh[TI][TJ][4];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        const int tl = acc_col<TJ>(wn, j, lane), tc = tok0 + tl;
+        const float e = tc < p.clen ? eta_at(p, bh, p.c0 + tc) : 0.f;
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int fl = acc_row<TI>(wm, i, q, lane) >> 1;   // local units fl, fl + 1
+                const f32x2 da = *reinterpret_cast<const f32x2*>(sD + tl * LDD + fl);
+                const float g0 = acc[i][j][4 * q], u0 = acc[i][j][4 * q + 1];
+                const float g1 = acc[i][j][4 * q + 2], u1 = acc[i][j][4 * q + 3];
+                const float sg0 = sigm(g0), sg1 = sigm(g1);
+                const float s0 = g0 * sg0, s1 = g1 * sg1;
+                const float c10 = u0 * sg0 * (1.f + g0 * (1.f - sg0));
+                const float c11 = u1 * sg1 * (1.f + g1 * (1.f - sg1));
+                const float d0 = -e * da[0], d1 = -e * da[1];     // dA of the loss sum_t eta_t l_t
+                oa[i][j][q] = pack2bf(e * s0 * u0, e * s1 * u1);
+                oh[i][j][q] = u32x2{pack2bf(d0 * c10, d0 * s0), pack2bf(d1 * c11, d1 * s1)};
+            }
+    }
+    __syncthreads();
+    bf16_t* sA = smem;
+    bf16_t* sH = smem + BN * LA;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+        const int tl = acc_col<TJ>(wn, j, lane);
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int fl = acc_row<TI>(wm, i, q, lane) >> 1;
+                *reinterpret_cast<uint32_t*>(sA + tl * LA + fl) = oa[i][j][q];
+                *reinterpret_cast<u32x2*>(sH + tl * LHD + 2 * fl) = oh[i][j][q];
+            }
+    }
+    __syncthreads();
+    const int f_base = rt * AW;
+    bf16_t* ak = p.ak + bh * p.s_act;
+    bf16_t* dh = p.dh + bh * p.s_cc;
+    constexpr int PA = AW / 4, PH = BM / 4;
+    for (int x = tid; x < BN * PA; x += SW_NT) {
+        const int tl = x / PA, pc = x % PA;
+        *reinterpret_cast<u32x2*>(ak + (int64_t)(tok0 + tl) * p.m + f_base + 4 * pc) =
+            *reinterpret_cast<const u32x2*>(sA + tl * LA + 4 * pc);
+    }
+    for (int x = tid; x < BN * PH; x += SW_NT) {
+        const int tl = x / PH, pc = x % PH;
+        *reinterpret_cast<u32x2*>(dh + (int64_t)(tok0 + tl) * 2 * p.m + 2 * f_base + 4 * pc) =
+            *reinterpret_cast<const u32x2*>(sH + tl * LHD + 4 * pc);
     }
 }
 
@@ -608,22 +724,24 @@ Layout layout(int BH, int dk, int dv, int m, int C) {
     return l;
 }
 
-// one chunk: forward, output, dA / dH, weight update.  The forward and
-// output GEMMs run 128 x 128 tiles (K = dk and m; their many small-row
-// epilogue stores favour more, smaller workgroups); with BIG the dA GEMM runs
-// 256 x 256 and the update 256 x 128 tiles (measured fastest per kernel).
+// one chunk: forward (for loss 0 the Q rows here, the K rows fused with dA
+// in sw_fwdk_kernel), output, dA / dH (loss 1), weight update.  The forward
+// GEMMs run 128 x 128 tiles; with BIG the output and dA GEMMs run 256 x 256
+// and the update 256 x 128 tiles (each measured fastest among 128 / 256
+// choices for its kernel).
 template <int LOSS, bool BIG>
 hipError_t chunk_step(const SwDev& p, const SwParams& in, hipStream_t s) {
     constexpr int F = BIG ? 4 : 2;
     const dim3 blk(SW_NT);
     const int C = in.chunk;
-    const dim3 g_fwd((2 * in.m / 128) * (2 * C / 128), in.BH);
-    const dim3 g_out((in.dv / 128) * (LOSS ? 2 : 1) * (C / 128), in.BH);
+    const dim3 g_fwd((2 * in.m / 128) * ((LOSS ? 2 : 1) * C / 128), in.BH);
+    const dim3 g_out((in.dv / (64 * F)) * (LOSS ? 2 : 1) * (C / (64 * F)), in.BH);
     const dim3 g_bwda((in.m / (64 * F)) * (C / (64 * F)), in.BH);
     const dim3 g_upd((in.dv / (64 * F)) * (in.m / 128) + (2 * in.m / (64 * F)) * (in.dk / 128), in.BH);
     hipLaunchKernelGGL((sw_fwd_kernel<LOSS, 2, 2>), g_fwd, blk, 0, s, p);
-    hipLaunchKernelGGL((sw_out_kernel<LOSS, 2, 2>), g_out, blk, 0, s, p);
-    hipLaunchKernelGGL((sw_bwda_kernel<LOSS, F, F>), g_bwda, blk, 0, s, p);
+    if (LOSS == 0) hipLaunchKernelGGL(sw_fwdk_kernel, dim3((2 * in.m / 128) * (C / 128), in.BH), blk, 0, s, p);
+    hipLaunchKernelGGL((sw_out_kernel<LOSS, F, F>), g_out, blk, 0, s, p);
+    if (LOSS == 1) hipLaunchKernelGGL((sw_bwda_kernel<LOSS, F, F>), g_bwda, blk, 0, s, p);
     hipLaunchKernelGGL((sw_upd_kernel<LOSS, F, 2>), g_upd, blk, 0, s, p);
     return hipGetLastError();
 }
