@@ -49,7 +49,7 @@ KERNEL_SOURCES = {
     "decode_kernel": ("decode.hip", "common.h"),
     "fe_gemm_kernel": ("frontend.hip", "common.h"),
     "tcb_fwd_kernel+bwd_scale_kernels": ("tcb_fwd.hip", "bwd.hip", "common.h"),
-    "sw_fwd+sw_out+sw_bwda+sw_upd": ("swiglu.hip", "common.h"),
+    "swiglu_kernels": ("swiglu.hip", "common.h"),
 }
 
 
@@ -209,7 +209,7 @@ def setup_workload(name: str, dev: str):
                      + 2 * B * H * (2 * m * dk + dv * m) * 4)               # weights in and out
         info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, m=m, chunk=C, loss=loss, eta="per-token",
                     dtype="bf16", tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
-                    kernel="sw_fwd+sw_out+sw_bwda+sw_upd", inputs=inp)
+                    kernel="swiglu_kernels", inputs=inp)
         return step, info
     if name in ("decode", "decode-momentum"):
         inp = W.gen_decode(beta=0.9 if name == "decode-momentum" else 0.0)
