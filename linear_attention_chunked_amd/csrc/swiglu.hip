@@ -14,21 +14,25 @@
 //     l_t = -<f_W(k_t), v_t>  (loss 0)   or   1/2 ||f_W(k_t) - v_t||^2  (loss 1)
 //
 // One chunk step is four launches over all heads, each a bf16 MFMA GEMM
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation, 128 x 128 block tiles of
-// four 64 x 64 waves) with its elementwise work fused into the epilogue:
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation, 2 x 2 waves per workgroup)
+// with its elementwise work fused into the epilogue:
 //
 //   sw_fwd   [Q_i; K_i] x W13^T   (K = dk)  -> A = silu(H1) * H3 for the Q rows
-//            (aq) and the K rows (ak; times eta_t for loss 0), and for the K
-//            rows the two factors of the SwiGLU derivative (cc):
-//            c1 = H3 silu'(H1), c3 = silu(H1).
+//            (aq) and, for loss 1, the K rows (ak) with the two factors of
+//            the SwiGLU derivative (cc): c1 = H3 silu'(H1), c3 = silu(H1).
+//   sw_fwdk  loss 0, the K rows: K_i x W13^T and dA = V_i x W2 for the same
+//            hidden units in one workgroup -> eta_t A and dH = -eta_t dA (c1, c3)
+//            (dY = -eta_t V never formed, c1 and c3 never leave the chip).
 //   sw_out   A x W2^T            (K = m)   -> O_i (Q rows); for loss 1 also
 //            dY = eta_t (Y - V) (K rows).
-//   sw_bwda  dY x W2             (K = dv)  -> dA, then dH = (dA c1, dA c3)
-//            interleaved like W13; for loss 0, dY = -eta_t V is never formed:
-//            the GEMM reads V and the epilogue scales by -eta_t.
+//   sw_bwda  loss 1: dY x W2     (K = dv)  -> dA, then dH = (dA c1, dA c3).
 //   sw_upd   dW2 = dY^T A_K and dW13 = dH^T K_i (K = chunk tokens), both in
 //            one launch; the epilogue updates the fp32 master weights and
 //            writes their bf16 copies for the next chunk.
+//
+// The GEMMs contracting over features stream their operands with gfx950's
+// direct global-to-LDS loads (DLoop); the update, contracting over tokens,
+// stages its loads through registers (Loop), which measured faster there.
 //
 // Layouts.  W13 interleaves the rows of W1 and W3 (row 2f = W1 row f,
 // row 2f + 1 = W3 row f), so the gate and up values of one hidden unit land
@@ -236,6 +240,134 @@ struct Loop {
     }
 };
 
+// ------------------------------------------------ direct global -> LDS loads
+// The same GEMM loop with gfx950's 16-byte global_load_lds: each load
+// instruction writes the wave's 64 x 16 bytes to consecutive LDS addresses,
+// so the data never pass through VGPRs.  Three LDS buffers form a ring: at
+// step st the loads of step st + 2 are issued right after the barrier that
+// ends everyone's reads of step st - 1, and step st's loads are waited for
+// (s_waitcnt vmcnt, own loads) just before that barrier.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+TTT_DEV void dma16(const bf16_t* g, bf16_t* lds) {
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), (lds_void_t*)(lds), 16, 0, 0);
+}
+
+// KROW = false: LDS [R][32] with the 16-byte XOR swizzle of Opnd; lane l of
+// load y of wave w fills row 64 y + 16 w + l / 4, position l % 4, i.e. the
+// global chunk (l % 4) ^ swz(row).
+// KROW = true: LDS [32][R] without pad; logical 16-byte chunk c of k row kk
+// sits at position c ^ 2 (kk % 4), which keeps the transposing reads of four
+// consecutive k rows on distinct banks.  Load y of wave w fills k rows
+// (32 y + 8 w) / T + l / (8 T), lane l at position l % (8 T).
+template <bool KROW, int T>
+struct Dop {
+    static constexpr int R = 64 * T;
+    static constexpr int BUF = SW_BK * R;   // elements per LDS buffer, both layouts
+    const bf16_t* base;
+    uint32_t off[T];   // KROW = false: element offset at step 0; true: column offset
+    int kr[T];         // KROW = true: k row within a step
+    int dst[T];        // wave's LDS offset (elements) within a buffer
+    uint32_t ld;
+    int lim;
+
+    TTT_DEV void init(const bf16_t* b, int ld_, int off0, int rowlim, int tid) {
+        base = b;
+        ld = (uint32_t)ld_;
+        lim = rowlim;
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+#pragma unroll
+        for (int y = 0; y < T; ++y) {
+            if (!KROW) {
+                const int r = 64 * y + 16 * w + (l >> 2);
+                off[y] = (uint32_t)min(off0 + r, rowlim - 1) * ld + 8 * ((l & 3) ^ swz(r));
+                kr[y] = 0;
+                dst[y] = (64 * y + 16 * w) * SW_BK;
+            } else {
+                const int row0 = (32 * y + 8 * w) / T;
+                const int kk = row0 + l / (8 * T), pos = l % (8 * T);
+                off[y] = (uint32_t)(off0 + 8 * (pos ^ (2 * (kk & 3))));
+                kr[y] = kk;
+                dst[y] = row0 * R;
+            }
+        }
+    }
+    TTT_DEV void load(int st, bf16_t* buf) const {
+#pragma unroll
+        for (int y = 0; y < T; ++y) {
+            uint32_t e;
+            if (!KROW) e = off[y] + (uint32_t)(st * SW_BK);
+            else e = off[y] + (uint32_t)min(st * SW_BK + kr[y], lim - 1) * ld;
+            dma16(base + e, buf + dst[y]);
+        }
+    }
+    TTT_DEV bf16x8 frag(const bf16_t* s, int r0, int k0, int lane) const {
+        if (!KROW) {
+            const int row = r0 + (lane & 31);
+            const int c = (k0 >> 3) + (lane >> 5);
+            return *reinterpret_cast<const bf16x8*>(s + row * SW_BK + 8 * (c ^ swz(row)));
+        }
+        const int G = lane >> 4, a = lane & 15;
+        const int rb = r0 + 16 * (G & 1) + 4 * (a & 3);
+        const int kk = k0 + 8 * (G >> 1) + (a >> 2);
+        const int pos = 8 * ((rb >> 3) ^ (2 * (kk & 3))) + (rb & 7);
+        const u32x2 lo2 = ds_read_tr(s + (kk + 0) * R + pos);
+        const u32x2 hi2 = ds_read_tr(s + (kk + 4) * R + pos);
+        return __builtin_bit_cast(bf16x8, u32x4{lo2[0], lo2[1], hi2[0], hi2[1]});
+    }
+};
+
+template <bool AK, bool BKR, int TI, int TJ>
+struct DLoop {
+    using OA = Dop<AK, TI>;
+    using OB = Dop<BKR, TJ>;
+    static constexpr int NB = 3;
+    static constexpr int LDS = NB * (OA::BUF + OB::BUF);
+    static constexpr int NLOAD = TI + TJ;   // load instructions per thread and step
+
+    TTT_DEV static void run(Acc<TI, TJ>& acc, int steps, const OA& a, const OB& b, bf16_t* smem, int tid) {
+        bf16_t* sA = smem;
+        bf16_t* sB = smem + NB * OA::BUF;
+        const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+        auto issue = [&](int st) __attribute__((always_inline)) {
+            const int s = min(st, steps - 1), buf = st % NB;
+            a.load(s, sA + buf * OA::BUF);
+            b.load(s, sB + buf * OB::BUF);
+        };
+        auto compute = [&](int buf) __attribute__((always_inline)) {
+            const bf16_t* A = sA + buf * OA::BUF;
+            const bf16_t* B = sB + buf * OB::BUF;
+#pragma unroll
+            for (int kk = 0; kk < SW_BK; kk += 16) {
+                bf16x8 af[TI], bfr[TJ];
+#pragma unroll
+                for (int i = 0; i < TI; ++i) af[i] = a.frag(A, 32 * TI * wm + 32 * i, kk, lane);
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) bfr[j] = b.frag(B, 32 * TJ * wn + 32 * j, kk, lane);
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j) mma32(acc[i][j], af[i], bfr[j]);
+            }
+        };
+        // vmcnt field of s_waitcnt on gfx9: bits 3..0 and 15..14; lgkmcnt and
+        // expcnt left at their maxima (no wait)
+        constexpr int WAIT_ONE_STEP = (NLOAD & 15) | ((NLOAD >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+        issue(0);
+        issue(1);
+        for (int st = 0; st < steps; ++st) {
+            // this wave's loads of step st are done once only step st + 1's are left
+            __builtin_amdgcn_s_waitcnt(WAIT_ONE_STEP);
+            __builtin_amdgcn_s_barrier();
+            issue(st + 2);
+            compute(st % NB);
+        }
+        // drain the clamped loads still in flight before the LDS is reused
+        __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+        __builtin_amdgcn_s_barrier();
+    }
+};
+
 // Workgroup -> (head, row tile, column tile).  Heads are contiguous ranges of
 // logical ids (xcd_logical: one XCD runs one contiguous range); within a
 // head, groups of 8 column tiles walk all row tiles.
@@ -294,7 +426,7 @@ TTT_DEV float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 template <int LOSS, int TI, int TJ>
 __global__ __launch_bounds__(SW_NT) void sw_fwd_kernel(SwDev p) {
     constexpr int BM = 64 * TI, BN = 64 * TJ;
-    using LP = Loop<false, false, TI, TJ>;
+    using LP = DLoop<false, false, TI, TJ>;
     // epilogue staging: A [BN tokens][BM/2 + 4] and (K rows, loss 1) c1, c3 [BN][BM + 4]
     constexpr int AW = BM / 2, LA = AW + 4, LC = BM + 4;
     constexpr int STAGE = BN * (LA + (LOSS == 1 ? LC : 0));
@@ -375,8 +507,8 @@ __global__ __launch_bounds__(SW_NT) void sw_fwd_kernel(SwDev p) {
 // the forward's lane layout (a lane holds two hidden units of one token).
 __global__ __launch_bounds__(SW_NT) void sw_fwdk_kernel(SwDev p) {
     constexpr int TI = 2, TJ = 2, BM = 128, BN = 128;
-    using LH = Loop<false, false, TI, TJ>;
-    using LDa = Loop<false, false, 1, TJ>;
+    using LH = DLoop<false, false, TI, TJ>;
+    using LDa = DLoop<false, false, 1, TJ>;
     constexpr int AW = BM / 2, LA = AW + 4, LHD = BM + 4, LDD = AW + 4;
     constexpr int STAGE = BN * (LA + LHD);
     constexpr int SM = LH::LDS > STAGE ? LH::LDS : STAGE;
@@ -475,7 +607,7 @@ __global__ __launch_bounds__(SW_NT) void sw_fwdk_kernel(SwDev p) {
 template <int LOSS, int TI, int TJ>
 __global__ __launch_bounds__(SW_NT) void sw_out_kernel(SwDev p) {
     constexpr int BM = 64 * TI, BN = 64 * TJ;
-    using LP = Loop<false, false, TI, TJ>;
+    using LP = DLoop<false, false, TI, TJ>;
     __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     const int nct = p.C / BN;
@@ -536,7 +668,7 @@ __global__ __launch_bounds__(SW_NT) void sw_out_kernel(SwDev p) {
 template <int LOSS, int TI, int TJ>
 __global__ __launch_bounds__(SW_NT) void sw_bwda_kernel(SwDev p) {
     constexpr int BM = 64 * TI, BN = 64 * TJ;
-    using LP = Loop<false, false, TI, TJ>;
+    using LP = DLoop<false, false, TI, TJ>;
     __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     int bh, rt, ct;
@@ -587,7 +719,8 @@ __global__ __launch_bounds__(SW_NT) void sw_bwda_kernel(SwDev p) {
 template <int LOSS, int TI, int TJ>
 __global__ __launch_bounds__(SW_NT, 2) void sw_upd_kernel(SwDev p) {
     constexpr int BM = 64 * TI, BN = 64 * TJ;
-    // three register sets in flight; the launch bound asks for two waves per SIMD
+    // register-staged loads (measured faster here than the direct-to-LDS
+    // loop), three sets in flight; the launch bound asks for two waves per SIMD
     using LP = Loop<true, true, TI, TJ, (TI == 4 ? 3 : 4)>;
     __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
