@@ -54,10 +54,14 @@ def check(got, ref, W0, what):
 
 @pytest.mark.parametrize("loss", ["dot", "mse"])
 @pytest.mark.parametrize("L,C,dk,dv,m", [(300, 128, 128, 256, 256), (512, 256, 256, 128, 384),
-                                          (100, 128, 128, 128, 128), (1000, 384, 128, 128, 256)])
+                                          (100, 128, 128, 128, 128), (1000, 384, 128, 128, 256),
+                                          (700, 256, 128, 256, 512), (513, 512, 384, 256, 256)])
 def test_swiglu_small(loss, L, C, dk, dv, m):
     """Whole and ragged last chunks, a single partial chunk, dk != dv both
-    ways, hidden sizes that are not a power of two; per-token eta.  The step
+    ways, hidden sizes that are not a power of two; per-token eta.  The last
+    two shapes (hidden, dv and chunk multiples of 256) take the 256-wide
+    tiles of the output, dA and update GEMMs, the others the 128-wide ones;
+    the last has a 1-token final chunk.  The step
     size is kept below the stability limit of the MSE step (the top
     eigenvalue of sum_t eta_t a_t a_t^T stays well under 2), so rounding
     differences are not amplified from chunk to chunk."""
