@@ -25,133 +25,20 @@
 //                          forming the d_ff x d_model update.
 //   fe_clip_kernel         per chunk: eta_t = eta * min(1, tau / ||eta Z_i^T V_i||_F).
 //
-// GEMM tiles: 4 waves as 2 x 2, each wave 32 TI x 32 TJ outputs of
-// v_mfma_f32_32x32x16_bf16; K-steps of 32 with four steps of loads in flight;
-// LDS tiles [rows][32] bf16 with a 16-byte XOR swizzle (conflict-free for the
-// staging writes and the fragment reads).
+// GEMM main loops: gemm.h's DLoop (4 waves as 2 x 2, each wave 32 TI x 32 TJ
+// outputs of v_mfma_f32_32x32x16_bf16, K-steps of 32 streamed with direct
+// global-to-LDS loads into a ring of three swizzled [rows][32] LDS tiles).
 #include "common.h"
+#include "gemm.h"
 #include "internal.h"
-
-#include <type_traits>
 
 namespace ttt {
 
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+using namespace gemm;
 
-constexpr int FE_BK = 32;     // k per step
-constexpr int FE_NT = 256;    // threads per workgroup
-constexpr int FE_NS = 4;      // k-steps of loads in flight
-
-TTT_DEV void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-}
-TTT_DEV int fe_swz(int r) { return (r >> 2) & 3; }
-
-// Main loop of C[BM x BN] += A[BM x K] B[BN x K]^T over `steps` k-steps.
-// arow[y] / brow[y]: this thread's 16-byte piece of its staging rows (row
-// start + 8 c); rows past the data are the caller's business (clamped).
-template <int TI, int TJ>
-struct Core {
-    static constexpr int BM = 64 * TI, BN = 64 * TJ;
-    const bf16_t* arow[TI];
-    const bf16_t* brow[TJ];
-    int loffa[TI], loffb[TJ];
-
-    TTT_DEV void init(int tid) {
-#pragma unroll
-        for (int y = 0; y < TI; ++y) {
-            const int u = tid + y * FE_NT, row = u >> 2, c = u & 3;
-            loffa[y] = row * FE_BK + 8 * (c ^ fe_swz(row));
-        }
-#pragma unroll
-        for (int y = 0; y < TJ; ++y) {
-            const int u = tid + y * FE_NT, row = u >> 2, c = u & 3;
-            loffb[y] = row * FE_BK + 8 * (c ^ fe_swz(row));
-        }
-    }
-
-    TTT_DEV void run(f32x16 (&acc)[TI][TJ], int steps, bf16_t* sA, bf16_t* sB, int tid) {
-        const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-        u32x4 ra[FE_NS][TI], rb[FE_NS][TJ];
-        auto load = [&](int st, auto SET) __attribute__((always_inline)) {
-            constexpr int k = decltype(SET)::value;
-            const int k0 = min(st, steps - 1) * FE_BK;
-#pragma unroll
-            for (int y = 0; y < TI; ++y) ra[k][y] = *reinterpret_cast<const u32x4*>(arow[y] + k0);
-#pragma unroll
-            for (int y = 0; y < TJ; ++y) rb[k][y] = *reinterpret_cast<const u32x4*>(brow[y] + k0);
-        };
-        auto stage = [&](int buf, auto SET) __attribute__((always_inline)) {
-            constexpr int k = decltype(SET)::value;
-#pragma unroll
-            for (int y = 0; y < TI; ++y) *reinterpret_cast<u32x4*>(&sA[buf * BM * FE_BK + loffa[y]]) = ra[k][y];
-#pragma unroll
-            for (int y = 0; y < TJ; ++y) *reinterpret_cast<u32x4*>(&sB[buf * BN * FE_BK + loffb[y]]) = rb[k][y];
-        };
-        // fragment reads: lane -> row r0 + lane % 32, k half lane / 32
-        const int lrow = lane & 31;
-        const int fb0 = lrow * FE_BK + 8 * ((lane >> 5) ^ fe_swz(lrow));
-        const int fb1 = lrow * FE_BK + 8 * ((2 | (lane >> 5)) ^ fe_swz(lrow));
-        auto compute = [&](int buf) __attribute__((always_inline)) {
-            const bf16_t* A = sA + buf * BM * FE_BK;
-            const bf16_t* B = sB + buf * BN * FE_BK;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const int fb = kh ? fb1 : fb0;
-                bf16x8 af[TI], bfr[TJ];
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-                    af[i] = *reinterpret_cast<const bf16x8*>(A + (32 * TI * wm + 32 * i) * FE_BK + fb);
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-                    bfr[j] = *reinterpret_cast<const bf16x8*>(B + (32 * TJ * wn + 32 * j) * FE_BK + fb);
-#pragma unroll
-                for (int i = 0; i < TI; ++i)
-#pragma unroll
-                    for (int j = 0; j < TJ; ++j) mma32(acc[i][j], af[i], bfr[j]);
-            }
-        };
-        using K0 = std::integral_constant<int, 0>;
-        using K1 = std::integral_constant<int, 1>;
-        using K2 = std::integral_constant<int, 2>;
-        using K3 = std::integral_constant<int, 3>;
-        load(0, K0{});
-        load(1, K1{});
-        load(2, K2{});
-        load(3, K3{});
-        stage(0, K0{});
-        __syncthreads();
-        auto step = [&](int st, auto CUR, auto NXT) __attribute__((always_inline)) {
-            load(st + FE_NS, CUR);
-            compute(st & 1);
-            __builtin_amdgcn_sched_barrier(0);
-            // unconditional: after the last step it writes clamped, unused data to
-            // the idle buffer, and no path skips the wait for this set's loads
-            // (a skipped wait makes the compiler stall the next reuse of its registers)
-            stage((st + 1) & 1, NXT);
-            __syncthreads();
-        };
-        // steps is a multiple of 4 (K a multiple of 128)
-        for (int st = 0; st < steps; st += FE_NS) {
-            step(st, K0{}, K1{});
-            step(st + 1, K1{}, K2{});
-            step(st + 2, K2{}, K3{});
-            step(st + 3, K3{}, K0{});
-        }
-    }
-};
-
-template <int TI, int TJ>
-TTT_DEV void zero(f32x16 (&acc)[TI][TJ]) {
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-        for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-}
+constexpr int FE_NT = GM_NT;   // threads per workgroup
 
 // Tile order: groups of 8 token tiles walk all feature tiles, so the 32 or
 // so workgroups resident on one XCD share a few token and feature tiles
@@ -175,33 +62,28 @@ TTT_DEV void tile_of(int lid, int n_tok, int n_feat, int* tt, int* ft) {
 template <bool GATED>
 __global__ __launch_bounds__(FE_NT) void fe_gemm_kernel(FeGemmParams p) {
     constexpr int TI = 4, TJ = 4;
-    using C = Core<TI, TJ>;
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2 * C::BM * FE_BK];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2 * C::BN * FE_BK];
+    using LP = DLoop<false, false, TI, TJ>;
+    constexpr int BM = 64 * TI, BN = 64 * TJ;
+    __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-    const int n_feat = p.arows / C::BM, n_tok = (p.T + C::BN - 1) / C::BN;
+    const int n_feat = p.arows / BM, n_tok = (p.T + BN - 1) / BN;
     int tt, ft;
     tile_of(xcd_logical(blockIdx.x, gridDim.x), n_tok, n_feat, &tt, &ft);
-    const int a0 = ft * C::BM, t0 = tt * C::BN;
+    const int a0 = ft * BM, t0 = tt * BN;
 
-    C core;
-    core.init(tid);
-#pragma unroll
-    for (int y = 0; y < TI; ++y) {
-        const int u = tid + y * FE_NT, row = a0 + (u >> 2), c = u & 3;
-        const bf16_t* A0 = reinterpret_cast<const bf16_t*>(p.A0);
-        const bf16_t* A1 = reinterpret_cast<const bf16_t*>(p.A1);
-        const bf16_t* base = GATED ? ((row & 1) ? A1 : A0) + (int64_t)(row >> 1) * p.K : A0 + (int64_t)row * p.K;
-        core.arow[y] = base + 8 * c;
-    }
-#pragma unroll
-    for (int y = 0; y < TJ; ++y) {
-        const int u = tid + y * FE_NT, row = min(t0 + (u >> 2), p.T - 1), c = u & 3;
-        core.brow[y] = reinterpret_cast<const bf16_t*>(p.B) + (int64_t)row * p.ldb + 8 * c;
-    }
-    f32x16 acc[TI][TJ];
+    const bf16_t* A0 = reinterpret_cast<const bf16_t*>(p.A0);
+    const bf16_t* A1 = reinterpret_cast<const bf16_t*>(p.A1);
+    const bf16_t* Bm = reinterpret_cast<const bf16_t*>(p.B);
+    typename LP::OA a;
+    typename LP::OB b;
+    a.init_rows([&](int r) {
+        const int row = a0 + r;
+        return GATED ? ((row & 1) ? A1 : A0) + (int64_t)(row >> 1) * p.K : A0 + (int64_t)row * p.K;
+    }, tid);
+    b.init_rows([&](int r) { return Bm + (int64_t)min(t0 + r, p.T - 1) * p.ldb; }, tid);
+    Acc<TI, TJ> acc;
     zero(acc);
-    core.run(acc, p.K / FE_BK, sA, sB, tid);
+    LP::run(acc, p.K / GM_BK, a, b, smem, tid);
 
     // acc[i][j][r]: A row 32 TI wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4,
     // token 32 TJ wn + 32 j + lane % 32
@@ -260,9 +142,9 @@ __global__ __launch_bounds__(256) void fe_conv_kernel(FeConvParams p) {
 // partial = w * sum_{s in si, t in ti} (z_s . z_t)(v_s . v_t), w = 2 off the diagonal.
 __global__ __launch_bounds__(FE_NT) void fe_gram_kernel(FeGramParams p) {
     constexpr int TI = 2, TJ = 2;
-    using C = Core<TI, TJ>;
-    __shared__ __attribute__((aligned(16))) bf16_t sA[2 * C::BM * FE_BK];
-    __shared__ __attribute__((aligned(16))) bf16_t sB[2 * C::BN * FE_BK];
+    using LP = DLoop<false, false, TI, TJ>;
+    constexpr int BM = 64 * TI, BN = 64 * TJ;
+    __shared__ __attribute__((aligned(16))) bf16_t smem[LP::LDS];
     __shared__ float sRed[FE_NT / 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
     const int pair = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
@@ -275,31 +157,22 @@ __global__ __launch_bounds__(FE_NT) void fe_gram_kernel(FeGramParams p) {
     const int ti = si + rem;
     const int c0 = chunk * p.chunk;
     const int cend = min(c0 + p.chunk, p.L);
-    const int s0 = c0 + si * C::BM, u0 = c0 + ti * C::BN;
+    const int s0 = c0 + si * BM, u0 = c0 + ti * BN;
     float part = 0.f;
     if (s0 < cend && u0 < cend) {   // uniform
         const int64_t rowb = (int64_t)b * p.L;
-        auto set_rows = [&](C& core, const bf16_t* base, int ld) {
-#pragma unroll
-            for (int y = 0; y < TI; ++y) {
-                const int u = tid + y * FE_NT, r = min(s0 + (u >> 2), cend - 1), c = u & 3;
-                core.arow[y] = base + (rowb + r) * ld + 8 * c;
-            }
-#pragma unroll
-            for (int y = 0; y < TJ; ++y) {
-                const int u = tid + y * FE_NT, r = min(u0 + (u >> 2), cend - 1), c = u & 3;
-                core.brow[y] = base + (rowb + r) * ld + 8 * c;
-            }
-        };
-        C core;
-        core.init(tid);
-        f32x16 az[TI][TJ], av[TI][TJ];
+        Acc<TI, TJ> az, av;
         zero(az);
         zero(av);
-        set_rows(core, reinterpret_cast<const bf16_t*>(p.Z), p.dz);
-        core.run(az, p.dz / FE_BK, sA, sB, tid);
-        set_rows(core, reinterpret_cast<const bf16_t*>(p.V), p.dv);
-        core.run(av, p.dv / FE_BK, sA, sB, tid);
+        auto gram = [&](Acc<TI, TJ>& acc, const bf16_t* base, int ld) {
+            typename LP::OA oa;
+            typename LP::OB ob;
+            oa.init_rows([&](int r) { return base + (rowb + min(s0 + r, cend - 1)) * ld; }, tid);
+            ob.init_rows([&](int r) { return base + (rowb + min(u0 + r, cend - 1)) * ld; }, tid);
+            LP::run(acc, ld / GM_BK, oa, ob, smem, tid);
+        };
+        gram(az, reinterpret_cast<const bf16_t*>(p.Z), p.dz);
+        gram(av, reinterpret_cast<const bf16_t*>(p.V), p.dv);
         // rows (tokens s) past the chunk end were clamped: mask them out
 #pragma unroll
         for (int i = 0; i < TI; ++i)
