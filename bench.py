@@ -47,9 +47,9 @@ KERNEL_SOURCES = {
     "dual_fwd_kernel": ("dual.hip", "common.h"),
     "dual_chain_kernel": ("dual.hip", "common.h"),
     "decode_kernel": ("decode.hip", "common.h"),
-    "fe_gemm_kernel": ("frontend.hip", "common.h"),
+    "fe_gemm_kernel": ("frontend.hip", "gemm.h", "common.h"),
     "tcb_fwd_kernel+bwd_scale_kernels": ("tcb_fwd.hip", "bwd.hip", "common.h"),
-    "swiglu_kernels": ("swiglu.hip", "common.h"),
+    "swiglu_kernels": ("swiglu.hip", "gemm.h", "common.h"),
 }
 
 
