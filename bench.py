@@ -116,10 +116,19 @@ def setup_workload(name: str, dev: str):
 
         bytes_alg = L * (d_ff + 2 * d_model) * 2 + 2 * d_ff * d_model * 4
         flop_alg = 4 * L * d_ff * d_model
+        def cpu_sample():
+            # the first two chunks (all of W), NumPy fp64 GEMMs
+            import oracle
+            n = 2048
+            z = W.to_f64(Z[:, :, :n].cpu())
+            oracle.chunk_causal(z, z, W.to_f64(V[:, :, :n].cpu()), eta_scalar=inp.eta_scalar,
+                                S0=W.to_f64(inp.S0), chunk=1024)
+            return n, f"the first {n} of {L} tokens (2 of {L // 1024} chunks, the whole W), NumPy fp64 GEMMs"
+
         info = dict(workload=name, B=1, H=1, L=L, d_ff=d_ff, d_model=d_model, chunk=1024,
                     mode="chunk_causal", eta=inp.eta_scalar, dtype="bf16", tokens=L,
                     bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="ip_update_kernel+ip_readout_kernel",
-                    inputs=None)
+                    inputs=None, cpu_sample=cpu_sample)
         return step, info
     if name in ("dual-b16", "dual-b2048"):
         mb = 16 if name == "dual-b16" else 2048
@@ -161,10 +170,19 @@ def setup_workload(name: str, dev: str):
         if mom:
             bytes_alg += B * H * dk * dv * 4          # dM0
         flop_alg = 3 * B * H * L * (4 * nst * dk * dv + (C + 1) * (dk + dv))
+        def cpu_sample():
+            # 8 (b, h) heads, whole sequences, the C oracle's adjoint sweeps
+            import oracle
+            sl = lambda t: None if t is None else W.to_f64(t[:1, :8])
+            oracle.token_causal_bwd(sl(inp.q), sl(inp.k), sl(inp.v), sl(dout), sl(inp.eta), inp.eta_scalar,
+                                    inp.beta, sl(inp.S0), None, sl(dSf), None)
+            return (8 * L / H, f"8 of {B * H} (b,h) heads, full L={L}, fp64 adjoint sweeps in C "
+                    "(tokens scaled by the head fraction)", oracle.threads())
+
         info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, mode="token_causal backward",
                     beta=inp.beta, eta="per-token" if eta is not None else inp.eta_scalar, dtype="bf16",
                     tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
-                    kernel="tcb_fwd_kernel+bwd_scale_kernels", inputs=None)
+                    kernel="tcb_fwd_kernel+bwd_scale_kernels", inputs=None, cpu_sample=cpu_sample)
         return step, info
     if name == "inplace-frontend":
         T, dm, dff, taps, C = 32768, 2560, 9728, 4, 1024
@@ -182,8 +200,18 @@ def setup_workload(name: str, dev: str):
         flop_alg = 2 * 2 * T * dm * dff + 2 * T * dm * dm
         bytes_alg = (T * dm * 2 + 2 * dff * dm * 2 + dm * dm * 2 + taps * dm * 4   # X, weights
                      + T * dff * 2 + T * dm * 2 + T * 4)                           # Z, V-hat, rates
+        def cpu_sample():
+            # the first chunk of tokens through the whole front end, NumPy fp64
+            import oracle
+            x = W.to_f64(X[:, :C].cpu())
+            z = oracle.inplace_gated_input(x, W.to_f64(Wg.cpu()), W.to_f64(Wu.cpu()))
+            vh = oracle.lm_aligned_target(x, W.to_f64(cw.cpu()), W.to_f64(Wv.cpu()))
+            oracle.clip_scales(z, vh, C, 1e-3, 50.0)
+            return C, f"the first {C} of {T} tokens (one chunk), NumPy fp64"
+
         info = dict(workload=name, T=T, d_model=dm, d_ff=dff, taps=taps, chunk=C, dtype="bf16", tokens=T,
-                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="fe_gemm_kernel", inputs=None)
+                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="fe_gemm_kernel", inputs=None,
+                    cpu_sample=cpu_sample)
         return step, info
     if name in ("swiglu", "swiglu-mse"):
         loss = "mse" if name == "swiglu-mse" else "dot"
@@ -242,6 +270,14 @@ def cpu_baseline(info) -> dict:
     import oracle
     import workloads as W
 
+    if "cpu_sample" in info:
+        t0 = time.perf_counter()
+        res = info["cpu_sample"]()
+        dt = time.perf_counter() - t0
+        tokens, what = res[0], res[1]
+        cores = res[2] if len(res) > 2 else blas_threads()   # C oracle (OpenMP) or NumPy's BLAS
+        return {"value": tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                "sample": f"{what}; {dt:.2f} s"}
     inp = info["inputs"]
     if inp is None:
         return None
@@ -387,7 +423,7 @@ def main():
         roofline.update({"bound": "mfma", "achieved": round(tflops, 2), "peak": peak_f,
                          "unit": "TFLOP/s", "frac": round(tflops / peak_f, 4)})
 
-    cfg = {k: info[k] for k in info if k not in ("inputs", "bytes_alg", "flop_alg", "kernel", "tokens")}
+    cfg = {k: info[k] for k in info if k not in ("inputs", "bytes_alg", "flop_alg", "kernel", "tokens", "cpu_sample")}
     res = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
