@@ -687,14 +687,22 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             refresh = (end % p.chunk == 0) || (end >= L);
         }
         if (refresh) refresh_ops();
-        if (c + 1 < c_end) store(c + 1, cur ^ 1, SSET, WQ{});
+        // unconditional: after the last chunk it stages the refetched last
+        // chunk into the idle buffer (zero eta, never read).  A conditional
+        // store leaves a path on which this register set's loads are never
+        // waited for, and the compiler then drains every load in flight
+        // before the next reuse of those registers (the score reads).
+        store(c + 1, cur ^ 1, SSET, WQ{});
         if (PF == 1) load(c + 2, LSET, WQ{});
         __syncthreads();
     };
-    for (int c = c_begin; c < c_end; c += 2) {
+    // pairs of chunks with no branch inside the loop body; an odd last chunk after it
+    int c = c_begin;
+    for (; c + 1 < c_end; c += 2) {
         iter(c, I0{}, I1{});
-        if (c + 1 < c_end) iter(c + 1, I1{}, I0{});
+        iter(c + 1, I1{}, I0{});
     }
+    if (c < c_end) iter(c, I0{}, I1{});
     if (hf == 0) combine();
     __syncthreads();
     write_out();
