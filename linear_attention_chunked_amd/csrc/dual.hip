@@ -308,6 +308,15 @@ TTT_DEV int kswz(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) |
 TTT_DEV int feat(int p) { return (p & ~31) + 8 * ((p >> 2) & 3) + 4 * ((p >> 4) & 1) + (p & 3); }
 
 // ONESTEP: every mini-batch is exactly one 16-token step (W_n is S~ itself)
+// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
+template <int B, int E, class F>
+TTT_DEV void for_sets(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        for_sets<B + 1, E>(f);
+    }
+}
+
 template <int DEPTH, bool ONESTEP>
 __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
     constexpr int D = 64, DV = 64;
@@ -440,27 +449,9 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
                                               rO, vo, t0 * DV * 2, 0);
     };
 
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using S2 = std::integral_constant<int, 2>;
-    using S3 = std::integral_constant<int, 3>;
-    using S4 = std::integral_constant<int, 4>;
-    using S5 = std::integral_constant<int, 5>;
-    static_assert(DEPTH == 6, "the step sequence below is written for six register sets");
-    load(0, S0{});
-    load(1, S1{});
-    load(2, S2{});
-    load(3, S3{});
-    load(4, S4{});
-    load(5, S5{});
-    for (int s = 0; s < nrun; s += DEPTH) {
-        step(s, S0{});
-        step(s + 1, S1{});
-        step(s + 2, S2{});
-        step(s + 3, S3{});
-        step(s + 4, S4{});
-        step(s + 5, S5{});
-    }
+    static_assert(DEPTH >= 2 && DEPTH <= 16, "two to sixteen register sets");
+    for_sets<0, DEPTH>([&](auto SET) { load(decltype(SET)::value, SET); });
+    for (int s = 0; s < nrun; s += DEPTH) for_sets<0, DEPTH>([&](auto SET) { step(s + decltype(SET)::value, SET); });
 
     if (p.W_final) {
         float* Wf = p.W_final + (int64_t)bh * D * DV;
@@ -480,9 +471,9 @@ hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t s) {
     if (dtype == 1 && p.minibatch % 16 == 0) {
         // one wave per (b, h, 16-column tile)
         if (p.minibatch == 16)
-            hipLaunchKernelGGL((dual_chain_kernel<6, true>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+            hipLaunchKernelGGL((dual_chain_kernel<8, true>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
         else
-            hipLaunchKernelGGL((dual_chain_kernel<6, false>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+            hipLaunchKernelGGL((dual_chain_kernel<8, false>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
         return hipGetLastError();
     }
     const int grid = p.B * p.H;
