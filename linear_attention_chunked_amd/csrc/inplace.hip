@@ -34,6 +34,7 @@ constexpr int IP_BM = 256, IP_BN = 256, IP_BK = 32;
 constexpr int IPU_BN = 128;           // update pass: 256 x 128 tiles (waves 128 x 64)
 constexpr int IP_NT = 256;             // threads per workgroup
 constexpr int IP_PADT = 32;            // [k][row] tiles: 64-byte row pad
+constexpr int IP_SNR = IP_BM + 8;      // snapshot staging row: 256 m values + pad
 
 TTT_DEV void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
@@ -91,6 +92,7 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
     __shared__ __attribute__((aligned(16))) bf16_t sA[2][IP_BK * LDA];   // Z slice  [k=token][m=dk]
     __shared__ __attribute__((aligned(16))) bf16_t sB[2][IP_BK * LDB];   // V slice  [k=token][n=dv]
     __shared__ float sE[2][IP_BK];
+    __shared__ __attribute__((aligned(16))) bf16_t sS[IPU_BN * IP_SNR];   // snapshot staging [n][m]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 waves, 128 x 64 each
@@ -174,10 +176,12 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
     const float out_scale = PT ? 1.f : p.eta_scalar;   // acc -> W
     bf16_t* snap = p.snap + (int64_t)bh * p.nchunks * p.dk * p.dv;
 
-    // snapshot W_{chunk-1}^T (bf16) of this tile: [n][m] layout
+    // snapshot W_{chunk-1}^T (bf16) of this tile: [n][m] layout.  A lane holds
+    // 4 consecutive m of one n, so the tile goes through LDS ([n][m] rows of
+    // 512 bytes) and leaves as whole 16-byte row pieces; the next snapshot is
+    // a chunk of K-steps (and their barriers) later, so one barrier suffices.
     auto snapshot = [&](int chunk) __attribute__((always_inline)) {
-        bf16_t* sp = snap + (int64_t)chunk * p.dk * p.dv + (int64_t)(n0 + 64 * wn + (lane & 31)) * p.dk +
-                     m0 + 128 * wm + 4 * (lane >> 5);
+        const int nl = 64 * wn + (lane & 31), ml = 128 * wm + 4 * (lane >> 5);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -186,8 +190,16 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
                 for (int q = 0; q < 4; ++q) {
                     const f32x4 v4 = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
                                            acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                    st4(sp + (int64_t)(32 * j) * p.dk + 32 * i + 8 * q, v4 * out_scale);
+                    st4(&sS[(nl + 32 * j) * IP_SNR + ml + 32 * i + 8 * q], v4 * out_scale);
                 }
+        __syncthreads();
+        bf16_t* sp = snap + (int64_t)chunk * p.dk * p.dv + (int64_t)n0 * p.dk + m0;
+        constexpr int PR = IP_BM / 8;   // 16-byte pieces per row
+        for (int x = tid; x < IPU_BN * PR; x += IP_NT) {
+            const int r = x / PR, c = x % PR;
+            *reinterpret_cast<u32x4*>(sp + (int64_t)r * p.dk + 8 * c) =
+                *reinterpret_cast<const u32x4*>(&sS[r * IP_SNR + 8 * c]);
+        }
     };
     auto compute = [&](int buf) __attribute__((always_inline)) {
         const bf16_t* A = sA[buf];
