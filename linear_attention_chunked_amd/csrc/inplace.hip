@@ -456,21 +456,36 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
         step(st + 3, K3{}, K0{});
     }
 
-    // acc[i][j]: O^T[n][t], lane = token column, 4 consecutive n per group
+    // acc[i][j]: O^T[n][t], lane = token column, 4 consecutive n per group.
+    // The output rows leave through LDS ([token][n], 512-byte rows) as whole
+    // 16-byte pieces, 32 tokens (one j of one wave column) per pass, in the
+    // K-loop's A buffers (free now).
+    constexpr int ORW = IP_BM + 8;   // staged row: 256 n values + pad
+    bf16_t* sO = &sA[0][0];
+    static_assert(32 * ORW <= 2 * IP_BM * IP_BK, "staging fits the A buffers");
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int pass = 0; pass < 8; ++pass) {
+        const int j = pass % 4;
+        __syncthreads();
+        if (wn == pass / 4) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int t = t0 + 128 * wn + 32 * j + (lane & 31);
-            if (t >= L) continue;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + 128 * wm + 32 * i + 8 * q + 4 * (lane >> 5);
-                const f32x4 v4 = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                       acc[i][j][4 * q + 3]};
-                st4(Og + t * p.os[2] + n, v4);
-            }
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 v4 = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                           acc[i][j][4 * q + 3]};
+                    st4(&sO[(lane & 31) * ORW + 128 * wm + 32 * i + 8 * q + 4 * (lane >> 5)], v4);
+                }
         }
+        __syncthreads();
+        constexpr int PR = IP_BM / 8;   // 16-byte pieces per row
+        for (int x = tid; x < 32 * PR; x += IP_NT) {
+            const int r = x / PR, c = x % PR, t = t0 + 32 * pass + r;
+            if (t < L)
+                *reinterpret_cast<u32x4*>(Og + t * p.os[2] + n0 + 8 * c) =
+                    *reinterpret_cast<const u32x4*>(&sO[r * ORW + 8 * c]);
+        }
+    }
 }
 
 bool inplace_supported(int dtype, int dk, int dv, int chunk) {
