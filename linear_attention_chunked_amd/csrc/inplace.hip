@@ -411,22 +411,34 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
     const int lrow = lane & 31;
     const int fb0 = lrow * IP_BK + 8 * ((lane >> 5) ^ ro_swz(lrow));        // kk = 0
     const int fb1 = lrow * IP_BK + 8 * ((2 | (lane >> 5)) ^ ro_swz(lrow));  // kk = 16
-    auto compute = [&](int buf) __attribute__((always_inline)) {
-        const bf16_t* A = sA[buf];
-        const bf16_t* B = sB[buf];
+    // The k = 0 fragments of a step are read right after the barrier that
+    // publishes its buffer, while the last row of the previous step's k = 16
+    // products is still to be issued: those products cover the LDS latency
+    // that would otherwise stall the matrix core after every barrier.
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    auto read_k0 = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const int fb = kh ? fb1 : fb0;
-            bf16x8 af[4], bfr[4];
+        for (int i = 0; i < 4; ++i) a0[i] = *reinterpret_cast<const bf16x8*>(sA[buf] + (128 * wm + 32 * i) * IP_BK + fb0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(A + (128 * wm + 32 * i) * IP_BK + fb);
+        for (int j = 0; j < 4; ++j) b0[j] = *reinterpret_cast<const bf16x8*>(sB[buf] + (128 * wn + 32 * j) * IP_BK + fb0);
+    };
+    auto compute_head = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[j] = *reinterpret_cast<const bf16x8*>(B + (128 * wn + 32 * j) * IP_BK + fb);
+        for (int i = 0; i < 4; ++i) a1[i] = *reinterpret_cast<const bf16x8*>(sA[buf] + (128 * wm + 32 * i) * IP_BK + fb1);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) b1[j] = *reinterpret_cast<const bf16x8*>(sB[buf] + (128 * wn + 32 * j) * IP_BK + fb1);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mma32(acc[i][j], af[i], bfr[j]);
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mma32(acc[i][j], a0[i], b0[j]);
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mma32(acc[i][j], a1[i], b1[j]);
+    };
+    auto compute_tail = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma32(acc[3][j], a1[3], b1[j]);
     };
 
     using K0 = std::integral_constant<int, 0>;
@@ -439,14 +451,19 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
     load(3, K3{});
     stage(0, K0{});
     __syncthreads();
+    read_k0(0);
     auto step = [&](int st, auto CUR, auto NXT) __attribute__((always_inline)) {
         load(st + NS, CUR);
-        compute(st & 1);
+        compute_head(st & 1);
         __builtin_amdgcn_sched_barrier(0);
         // unconditional (clamped, unused data after the last step): no path
         // skips the wait for this set's loads
         stage((st + 1) & 1, NXT);
         __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        read_k0((st + 1) & 1);     // after the last step: unused
+        compute_tail();
+        __builtin_amdgcn_sched_barrier(0);
     };
     // steps is a multiple of 8 (dk a multiple of 256)
     for (int st = 0; st < steps; st += NS) {
