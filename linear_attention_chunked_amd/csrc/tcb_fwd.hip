@@ -87,9 +87,13 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     __shared__ __attribute__((aligned(16))) bf16_t sV[2][(DVT / 32) * BLKV];
     __shared__ __attribute__((aligned(16))) float sE[2][NV][CS];
     __shared__ __attribute__((aligned(16))) float sOS[2][CS];     // output row scales
-    __shared__ __attribute__((aligned(16))) bf16_t sP[HAS_P ? CS * LP : 8];
-    __shared__ __attribute__((aligned(16))) f32x4 sX[NNT][NTI][64];   // half-1 readout partials
-    __shared__ __attribute__((aligned(16))) bf16_t sO[CS * DVT];  // finished output tile
+    // one barrier per chunk (64 x 64 form without momentum): the score, partial
+    // and output tiles are double-buffered, see the chunk loop
+    constexpr bool PIPE = (CS == 64) && !MOM;
+    constexpr int NPB = PIPE ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) bf16_t sP[NPB][HAS_P ? CS * LP : 8];
+    __shared__ __attribute__((aligned(16))) f32x4 sX[NPB][NNT][NTI][64];   // half-1 readout partials
+    __shared__ __attribute__((aligned(16))) bf16_t sO[NPB][CS * DVT];  // finished output tile
     __shared__ float sTab[3 * (CS + 1)];                           // w_p | beta^p | a_p
 
     // the wave index is made uniform (scalar), so branches on it are scalar
@@ -147,7 +151,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         }
     }
     if (HAS_P) {
-        for (int x = tid; x < CS * LP / 8; x += NT) reinterpret_cast<u32x4*>(sP)[x] = u32x4{0, 0, 0, 0};
+        for (int x = tid; x < NPB * CS * LP / 8; x += NT) reinterpret_cast<u32x4*>(&sP[0][0])[x] = u32x4{0, 0, 0, 0};
     }
 
     // ---- per-lane LDS bases (elements)
@@ -292,17 +296,17 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
 #pragma unroll
         for (int ti = 0; ti < NTI; ++ti) {
             const int i = 16 * ti + c16;
-            f32x4 o = oacc[ti] + sX[nt][ti][lane];
+            f32x4 o = oacc[ti] + sX[0][nt][ti][lane];
             if (p.use_oscale) o *= sOS[prev_buf][i];
             const int ch = (2 * nt + (g >> 1)) ^ oswz<DVT>(i);
-            st4(&sO[i * DVT + 8 * ch + 4 * (g & 1)], o);
+            st4(&sO[0][i * DVT + 8 * ch + 4 * (g & 1)], o);
         }
     };
     // all threads: write the parked tile out as full 128-byte row segments
     auto write_out = [&]() {
         const int row = tid / (DVT / 8), ch = tid % (DVT / 8);
         if (tid < NVC && row < prev_n) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[row * DVT + 8 * (ch ^ oswz<DVT>(row))]);
+            const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[0][row * DVT + 8 * (ch ^ oswz<DVT>(row))]);
             bf16_t* Oc = Og + (int64_t)prev_base * oL;
             *reinterpret_cast<u32x4*>(Oc + (__mul24(row, (int)oL) + 8 * ch)) = w;
         }
@@ -579,18 +583,9 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     load(c_begin + 1, I1{}, WQ{});
     __syncthreads();
 
-    // chunk c_begin + k travels in register set k % PF; chunk c+1 is written
-    // to the other LDS buffer at the end of iteration c
-    auto iter = [&](int c, auto LSET, auto SSET) {
-        const int cur = (c - c_begin) & 1;
-        const int tbase = c * CS;
-        const int n = min(CS, L - tbase);
-        const bf16_t* Q = sQ[cur];
-        const bf16_t* K = sK[cur];
-
-        if (hf == 0 && c > c_begin) combine();
-
-        // ------------- intra scores P^T = K Q^T (lower-triangular 16x16 tiles)
+    // intra scores P^T = K Q^T of one staged chunk (lower-triangular 16x16
+    // tiles) into the score tile P
+    auto scores = [&](const bf16_t* Q, const bf16_t* K, bf16_t* P) {
         if (HAS_P && p_ti >= 0) {
             // all fragments are read before the first product (a wave with one
             // key tile computes its tile twice rather than branch in between)
@@ -621,9 +616,23 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                     if (MOM && j <= i) val *= sTab[i - j];
                     v[r] = val;
                 }
-                st4(&sP[i * LP + 16 * tj + 4 * g], v);
+                st4(&P[i * LP + 16 * tj + 4 * g], v);
             }
         }
+    };
+
+    // chunk c_begin + k travels in register set k % PF; chunk c+1 is written
+    // to the other LDS buffer at the end of iteration c
+    auto iter = [&](int c, auto LSET, auto SSET) {
+        const int cur = (c - c_begin) & 1;
+        const int tbase = c * CS;
+        const int n = min(CS, L - tbase);
+        const bf16_t* Q = sQ[cur];
+        const bf16_t* K = sK[cur];
+
+        if (hf == 0 && c > c_begin) combine();
+
+        scores(Q, K, sP[0]);
         // P^T complete; the previous chunk's output tile is parked in sO and
         // half 0 has read half 1's partials before they are overwritten below
         __syncthreads();
@@ -660,7 +669,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 const int pc = (NJB > 1 && hf) ? 32 : 0;
                 bf16x8 pf[NTI];
 #pragma unroll
-                for (int ti = 0; ti < NTI; ++ti) pf[ti] = ld_accperm(&sP[(16 * ti + c16) * LP], pc, g);
+                for (int ti = 0; ti < NTI; ++ti) pf[ti] = ld_accperm(&sP[0][(16 * ti + c16) * LP], pc, g);
                 const bf16x8 vb = (NJB > 1 && hf) ? VB[NJB - 1] : VB[0];
 #pragma unroll
                 for (int ti = 0; ti < NTI; ++ti)
@@ -671,7 +680,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 f32x4 o = acc[ti];
                 if (MOM) o += sTab[2 * (CS + 1) + 16 * ti + c16] * acc2[ti];
                 if (hf == 0) oacc[ti] = o;
-                else sX[nt][ti][lane] = o;
+                else sX[0][nt][ti][lane] = o;
             }
         }
         // (prev_* are read by write_out above, so they advance only here)
@@ -697,15 +706,134 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         __syncthreads();
     };
     // pairs of chunks with no branch inside the loop body; an odd last chunk after it
-    int c = c_begin;
-    for (; c + 1 < c_end; c += 2) {
-        iter(c, I0{}, I1{});
-        iter(c + 1, I1{}, I0{});
+    if constexpr (!PIPE) {
+        int c = c_begin;
+        for (; c + 1 < c_end; c += 2) {
+            iter(c, I0{}, I1{});
+            iter(c + 1, I1{}, I0{});
+        }
+        if (c < c_end) iter(c, I0{}, I1{});
+        if (hf == 0) combine();
+        __syncthreads();
+        write_out();
+    } else {
+        // One barrier per chunk.  The interval that ends with the barrier of
+        // chunk c runs, in this order:
+        //   half 0: adds half 1's partial of chunk c-2 to its own, into sO[c-2]
+        //   all:    write chunk c-3's output tile from sO[c-3]
+        //   all:    the intra term of chunk c-1 (scores sP[c-1], its V
+        //           fragments kept in registers); half 1 parks its partial
+        //           in sX[c-1], half 0 keeps its own
+        //   all:    chunk c's scores into sP[c], its readout with the state
+        //           after chunk c-1, the state update, and staging of c+1
+        // (buffer index: chunk parity from c_begin).  Every tile is read in
+        // the interval after the one that writes it and written again only
+        // one interval later, so a double buffer of sP, sX and sO suffices.
+        // The row scales of chunk c are read in chunk c's interval, since its
+        // staging buffer is refilled in the next one.
+        f32x4 acc_p[NTI];     // chunk's readout partial, finished one interval later
+        bf16x8 VB_p[NJB];     // its eta-scaled V fragments
+        float os_p[NTI];      // its output row scales
+        bf16x8 VS_p[1], VM_p[1];
+        auto rel = [&](int cc) { return (cc - c_begin) & 1; };
+        auto combine_p = [&](int cc) {
+            const int xb = rel(cc);
+#pragma unroll
+            for (int ti = 0; ti < NTI; ++ti) {
+                const int i = 16 * ti + c16;
+                const f32x4 o = oacc[ti] + sX[xb][nt][ti][lane];
+                const int ch = (2 * nt + (g >> 1)) ^ oswz<DVT>(i);
+                st4(&sO[xb][i * DVT + 8 * ch + 4 * (g & 1)], o);
+            }
+        };
+        auto write_out_p = [&](int cc) {
+            const int ob = rel(cc), base = cc * CS, nn = min(CS, L - base);
+            const int row = tid / (DVT / 8), ch = tid % (DVT / 8);
+            if (tid < NVC && row < nn) {
+                const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[ob][row * DVT + 8 * (ch ^ oswz<DVT>(row))]);
+                bf16_t* Oc = Og + (int64_t)base * oL;
+                *reinterpret_cast<u32x4*>(Oc + (__mul24(row, (int)oL) + 8 * ch)) = w;
+            }
+        };
+        auto intra_p = [&](int cc) {
+            const int xb = rel(cc);
+            if (HAS_P) {
+                // half 0 takes key block 0 of every query tile, half 1 key
+                // block 1 (query tiles 2, 3 only)
+                const int pc = (NJB > 1 && hf) ? 32 : 0;
+                bf16x8 pf[NTI];
+#pragma unroll
+                for (int ti = 0; ti < NTI; ++ti) pf[ti] = ld_accperm(&sP[xb][(16 * ti + c16) * LP], pc, g);
+                const bf16x8 vb = (NJB > 1 && hf) ? VB_p[NJB - 1] : VB_p[0];
+#pragma unroll
+                for (int ti = 0; ti < NTI; ++ti)
+                    if (hf == 0 || (NJB > 1 && ti >= 2)) mma(acc_p[ti], vb, pf[ti]);
+            }
+#pragma unroll
+            for (int ti = 0; ti < NTI; ++ti) {
+                f32x4 o = acc_p[ti];
+                if (p.use_oscale) o *= os_p[ti];
+                if (hf == 0) oacc[ti] = o;
+                else sX[xb][nt][ti][lane] = o;
+            }
+        };
+        auto iter_p = [&](int c, auto LSET, auto SSET) {
+            const int cur = rel(c);
+            const int tbase = c * CS;
+            const int n = min(CS, L - tbase);
+            if (hf == 0 && c - 2 >= c_begin) combine_p(c - 2);
+            // the output store goes before this interval's loads: the memory
+            // counter retires in order, so a later wait on the store leaves
+            // the loads in flight
+            if (c - 3 >= c_begin) write_out_p(c - 3);
+            if (c - 1 >= c_begin) intra_p(c - 1);
+            scores(sQ[cur], sK[cur], sP[cur]);
+            load(c + 2, LSET, WQ{});
+            vfrags(cur, VB_p, VS_p, VM_p);
+            // readout partial with the state after chunk c-1: O^T = S_h^T Q_h^T
+#pragma unroll
+            for (int ti = 0; ti < NTI; ++ti) acc_p[ti] = zero4();
+            const bf16_t* Qh = sQ[cur] + hf * NKH * BLK;
+#pragma unroll
+            for (int kk = 0; kk < NKH; ++kk) {
+#pragma unroll
+                for (int ti = 0; ti < NTI; ++ti) {
+                    const u32x2 lo = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap0);
+                    const u32x2 hi = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap1);
+                    mma(acc_p[ti], Sop[kk], join(lo, hi));
+                }
+            }
+            if (p.use_oscale) {
+#pragma unroll
+                for (int ti = 0; ti < NTI; ++ti) os_p[ti] = sOS[cur][16 * ti + c16];
+            }
+            state_update(cur, n, VB_p, VS_p, VM_p);
+            bool refresh = true;
+            if (MODE == MODE_CC) {
+                const int end = tbase + CS;
+                refresh = (end % p.chunk == 0) || (end >= L);
+            }
+            if (refresh) refresh_ops();
+            // unconditional, as in the two-barrier loop above
+            store(c + 1, cur ^ 1, SSET, WQ{});
+            __syncthreads();
+        };
+        int c = c_begin;
+        for (; c + 1 < c_end; c += 2) {
+            iter_p(c, I0{}, I1{});
+            iter_p(c + 1, I1{}, I0{});
+        }
+        if (c < c_end) iter_p(c, I0{}, I1{});
+        // drain: the last three chunks' remaining stages
+        if (hf == 0 && c_end - 2 >= c_begin) combine_p(c_end - 2);
+        if (c_end - 3 >= c_begin) write_out_p(c_end - 3);
+        intra_p(c_end - 1);
+        __syncthreads();
+        if (hf == 0) combine_p(c_end - 1);
+        if (c_end - 2 >= c_begin) write_out_p(c_end - 2);
+        __syncthreads();
+        write_out_p(c_end - 1);
     }
-    if (c < c_end) iter(c, I0{}, I1{});
-    if (hf == 0) combine();
-    __syncthreads();
-    write_out();
 
     if (segmented && seg != p.nseg - 1) return;   // final states come from the last segment
     const int col = n0 + 16 * nt + c16;
