@@ -724,8 +724,8 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         //   all:    the intra term of chunk c-1 (scores sP[c-1], its V
         //           fragments kept in registers); half 1 parks its partial
         //           in sX[c-1], half 0 keeps its own
-        //   all:    chunk c's scores into sP[c], its readout with the state
-        //           after chunk c-1, the state update, and staging of c+1
+        //   all:    chunk c's readout with the state after chunk c-1, the
+        //           state update, its scores into sP[c], and staging of c+1
         // (buffer index: chunk parity from c_begin).  Every tile is read in
         // the interval after the one that writes it and written again only
         // one interval later, so a double buffer of sP, sX and sO suffices.
@@ -787,7 +787,6 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             // the loads in flight
             if (c - 3 >= c_begin) write_out_p(c - 3);
             if (c - 1 >= c_begin) intra_p(c - 1);
-            scores(sQ[cur], sK[cur], sP[cur]);
             load(c + 2, LSET, WQ{});
             vfrags(cur, VB_p, VS_p, VM_p);
             // readout partial with the state after chunk c-1: O^T = S_h^T Q_h^T
@@ -814,6 +813,9 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 refresh = (end % p.chunk == 0) || (end >= L);
             }
             if (refresh) refresh_ops();
+            // the scores go last: the readout and the state update, which
+            // the next interval waits on, start first
+            scores(sQ[cur], sK[cur], sP[cur]);
             // unconditional, as in the two-barrier loop above
             store(c + 1, cur ^ 1, SSET, WQ{});
             __syncthreads();
