@@ -51,6 +51,13 @@ TTT_DEV u32x2 tr_read(const bf16_t* p) {
 TTT_DEV bf16x8 join(const u32x2& lo, const u32x2& hi) {
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
+// 8 bf16 values of one row times one scale, rounded back to bf16
+TTT_DEV u32x4 scale_row(const u32x4& w, float e) {
+    return u32x4{pack2bf(__uint_as_float(w[0] << 16) * e, __uint_as_float(w[0] & 0xffff0000u) * e),
+                 pack2bf(__uint_as_float(w[1] << 16) * e, __uint_as_float(w[1] & 0xffff0000u) * e),
+                 pack2bf(__uint_as_float(w[2] << 16) * e, __uint_as_float(w[2] & 0xffff0000u) * e),
+                 pack2bf(__uint_as_float(w[3] << 16) * e, __uint_as_float(w[3] & 0xffff0000u) * e)};
+}
 TTT_DEV bf16x8 scale_frag(const bf16x8& f, const f32x4& s_lo, const f32x4& s_hi) {
     const u32x4 w = __builtin_bit_cast(u32x4, f);
     const u32x4 o = u32x4{pack2bf(__uint_as_float(w[0] << 16) * s_lo[0], __uint_as_float(w[0] & 0xffff0000u) * s_lo[1]),
@@ -254,7 +261,17 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             if (wq) *reinterpret_cast<u32x4*>(&sQ[buf][loff_q[x]]) = rq[st][x];
             *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = rk[st][x];
         }
-        if (tid < NVC) *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = rv[st];
+        if (tid < NVC) {
+            if (MOM) {
+                *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = rv[st];
+            } else {
+                // without momentum V is staged as diag(eta) V: the eta of
+                // token r sits in lane r of every wave (zero past the end)
+                const int n = min(CS, L - c * CS);
+                const float e = __shfl(re[st], row_v);
+                *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = scale_row(rv[st], row_v < n ? e : 0.f);
+            }
+        }
         if (tid < CS) {
             const int n = min(CS, L - c * CS);
             const float e = (tid < n) ? re[st] : 0.f;
@@ -325,9 +342,11 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
             const bf16x8 raw = join(tr_read(V + b_v + (32 * jb) * 32), tr_read(V + b_v + (32 * jb + 16) * 32));
-            const float* e0 = &sE[cur][0][32 * jb + 4 * g];
-            VB[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e0), *reinterpret_cast<const f32x4*>(e0 + 16));
-            if (MOM) {
+            if (!MOM) {
+                VB[jb] = raw;   // staged already scaled by eta
+            } else {
+                const float* e0 = &sE[cur][0][32 * jb + 4 * g];
+                VB[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e0), *reinterpret_cast<const f32x4*>(e0 + 16));
                 const float* e1 = &sE[cur][1][32 * jb + 4 * g];
                 const float* e2 = &sE[cur][2][32 * jb + 4 * g];
                 VS[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e1), *reinterpret_cast<const f32x4*>(e1 + 16));
@@ -466,7 +485,10 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 constexpr int st = decltype(SET)::value;
 #pragma unroll
                 for (int x = 0; x < UQ; ++x) *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = ak[st][x];
-                if (tid < NVC) *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = av[st];
+                if (tid < NVC) {
+                    if (MOM) *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = av[st];
+                    else *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = scale_row(av[st], __shfl(ae[st], row_v));
+                }
                 if (tid < CS) {
                     sE[buf][0][tid] = ae[st];
                     if (MOM) {
