@@ -69,7 +69,9 @@ TTT_DEV bf16x8 scale_frag(const bf16x8& f, const f32x4& s_lo, const f32x4& s_hi)
 
 }  // namespace
 
-template <int DK, int MODE, int CS, int DVT>
+// OSC: output rows are scaled by per-token factors (a compile-time switch, so
+// the forward carries no dead scaling code)
+template <int DK, int MODE, int CS, int DVT, bool OSC>
 __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     constexpr int NNT = DVT / 16;           // column tiles per workgroup
     constexpr int NW = 2 * NNT, NT = 64 * NW;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         // (tokens past L get eta 0 when the chunk is written to LDS: a select
         // here would make the compiler wait for this load right away)
         re[st] = Eg ? (Eg + (int64_t)t0 * eL)[__mul24(min(tid % CS, lim), eL24)] : p.eta_scalar;
-        ros[st] = OSg ? OSg[(int64_t)(t0 + min(tid % CS, lim)) * p.ocs[2]] : p.oscale_scalar;
+        if (OSC) ros[st] = OSg ? OSg[(int64_t)(t0 + min(tid % CS, lim)) * p.ocs[2]] : p.oscale_scalar;
     };
     auto store = [&](int c, int buf, auto SET, auto WITHQ) {
         constexpr int st = decltype(SET)::value;
@@ -276,7 +278,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             const int n = min(CS, L - c * CS);
             const float e = (tid < n) ? re[st] : 0.f;
             sE[buf][0][tid] = e;
-            if (p.use_oscale) sOS[buf][tid] = ros[st];
+            if (OSC) sOS[buf][tid] = ros[st];
             if (MOM) {
                 const int pw = n - 1 - tid;
                 sE[buf][1][tid] = (pw >= 0) ? e * sTab[pw] : 0.f;
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         for (int ti = 0; ti < NTI; ++ti) {
             const int i = 16 * ti + c16;
             f32x4 o = oacc[ti] + sX[0][nt][ti][lane];
-            if (p.use_oscale) o *= sOS[prev_buf][i];
+            if (OSC) o *= sOS[prev_buf][i];
             const int ch = (2 * nt + (g >> 1)) ^ oswz<DVT>(i);
             st4(&sO[0][i * DVT + 8 * ch + 4 * (g & 1)], o);
         }
@@ -753,17 +755,22 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         // one interval later, so a double buffer of sP, sX and sO suffices.
         // The row scales of chunk c are read in chunk c's interval, since its
         // staging buffer is refilled in the next one.
-        f32x4 acc_p[NTI];     // chunk's readout partial, finished one interval later
+        // readout partials by chunk parity (compile-time in the loop unrolled
+        // by two): a chunk's partial is started in its own interval, finished
+        // in the next and, in half 0, summed two intervals later, before the
+        // chunk two ahead restarts the same registers
+        f32x4 accs[2][NTI];
         bf16x8 VB_p[NJB];     // its eta-scaled V fragments
         float os_p[NTI];      // its output row scales
         bf16x8 VS_p[1], VM_p[1];
         auto rel = [&](int cc) { return (cc - c_begin) & 1; };
-        auto combine_p = [&](int cc) {
+        auto combine_p = [&](int cc, auto PAR) {
+            constexpr int q = decltype(PAR)::value;
             const int xb = rel(cc);
 #pragma unroll
             for (int ti = 0; ti < NTI; ++ti) {
                 const int i = 16 * ti + c16;
-                const f32x4 o = oacc[ti] + sX[xb][nt][ti][lane];
+                const f32x4 o = accs[q][ti] + sX[xb][nt][ti][lane];
                 const int ch = (2 * nt + (g >> 1)) ^ oswz<DVT>(i);
                 st4(&sO[xb][i * DVT + 8 * ch + 4 * (g & 1)], o);
             }
@@ -777,7 +784,9 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 *reinterpret_cast<u32x4*>(Oc + (__mul24(row, (int)oL) + 8 * ch)) = w;
             }
         };
-        auto intra_p = [&](int cc) {
+        auto intra_p = [&](int cc, auto PAR) {
+            constexpr int q = decltype(PAR)::value;
+            f32x4* acc_p = accs[q];
             const int xb = rel(cc);
             if (HAS_P) {
                 // half 0 takes key block 0 of every query tile, half 1 key
@@ -793,22 +802,24 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             }
 #pragma unroll
             for (int ti = 0; ti < NTI; ++ti) {
-                f32x4 o = acc_p[ti];
-                if (p.use_oscale) o *= os_p[ti];
-                if (hf == 0) oacc[ti] = o;
-                else sX[xb][nt][ti][lane] = o;
+                if (OSC) acc_p[ti] *= os_p[ti];
+                if (hf != 0) sX[xb][nt][ti][lane] = acc_p[ti];
             }
         };
         auto iter_p = [&](int c, auto LSET, auto SSET) {
+            constexpr int q = decltype(LSET)::value;   // parity of c - c_begin
+            using Q0 = std::integral_constant<int, q>;
+            using Q1 = std::integral_constant<int, q ^ 1>;
+            f32x4* acc_p = accs[q];
             const int cur = rel(c);
             const int tbase = c * CS;
             const int n = min(CS, L - tbase);
-            if (hf == 0 && c - 2 >= c_begin) combine_p(c - 2);
+            if (hf == 0 && c - 2 >= c_begin) combine_p(c - 2, Q0{});
             // the output store goes before this interval's loads: the memory
             // counter retires in order, so a later wait on the store leaves
             // the loads in flight
             if (c - 3 >= c_begin) write_out_p(c - 3);
-            if (c - 1 >= c_begin) intra_p(c - 1);
+            if (c - 1 >= c_begin) intra_p(c - 1, Q1{});
             load(c + 2, LSET, WQ{});
             vfrags(cur, VB_p, VS_p, VM_p);
             // readout partial with the state after chunk c-1: O^T = S_h^T Q_h^T
@@ -824,7 +835,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                     mma(acc_p[ti], Sop[kk], join(lo, hi));
                 }
             }
-            if (p.use_oscale) {
+            if (OSC) {
 #pragma unroll
                 for (int ti = 0; ti < NTI; ++ti) os_p[ti] = sOS[cur][16 * ti + c16];
             }
@@ -849,14 +860,20 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         }
         if (c < c_end) iter_p(c, I0{}, I1{});
         // drain: the last three chunks' remaining stages
-        if (hf == 0 && c_end - 2 >= c_begin) combine_p(c_end - 2);
-        if (c_end - 3 >= c_begin) write_out_p(c_end - 3);
-        intra_p(c_end - 1);
-        __syncthreads();
-        if (hf == 0) combine_p(c_end - 1);
-        if (c_end - 2 >= c_begin) write_out_p(c_end - 2);
-        __syncthreads();
-        write_out_p(c_end - 1);
+        auto drain = [&](auto PAR) {   // parity of the last chunk
+            using QL = decltype(PAR);
+            using QP = std::integral_constant<int, QL::value ^ 1>;
+            if (hf == 0 && c_end - 2 >= c_begin) combine_p(c_end - 2, QP{});
+            if (c_end - 3 >= c_begin) write_out_p(c_end - 3);
+            intra_p(c_end - 1, QL{});
+            __syncthreads();
+            if (hf == 0) combine_p(c_end - 1, QL{});
+            if (c_end - 2 >= c_begin) write_out_p(c_end - 2);
+            __syncthreads();
+            write_out_p(c_end - 1);
+        };
+        if ((c_end - 1 - c_begin) & 1) drain(std::integral_constant<int, 1>{});
+        else drain(std::integral_constant<int, 0>{});
     }
 
     if (segmented && seg != p.nseg - 1) return;   // final states come from the last segment
@@ -966,23 +983,30 @@ hipError_t launch_tcb_fwd(const TcParams& pin, int mode, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const dim3 grid((unsigned)nwg), block(pl.dvt / 16 * 128);
-#define TTT_L(DK_, M_, CS_, DVT_) hipLaunchKernelGGL((tcb_fwd_kernel<DK_, M_, CS_, DVT_>), grid, block, 0, s, p)
-#define TTT_M(CS_, DVT_)                                              \
-    if (pl.cs == CS_ && pl.dvt == DVT_) {                              \
-        if (p.dk == 128) {                                             \
-            if (mode == MODE_TC) TTT_L(128, MODE_TC, CS_, DVT_);       \
-            else if (mode == MODE_MOM) TTT_L(128, MODE_MOM, CS_, DVT_); \
-            else TTT_L(128, MODE_CC, CS_, DVT_);                       \
-        } else {                                                       \
-            if (mode == MODE_TC) TTT_L(64, MODE_TC, CS_, DVT_);        \
-            else if (mode == MODE_MOM) TTT_L(64, MODE_MOM, CS_, DVT_);  \
-            else TTT_L(64, MODE_CC, CS_, DVT_);                        \
-        }                                                              \
-        return hipGetLastError();                                      \
+    // row scales come only with the token-causal forms (the backward's passes)
+    if (mode == MODE_CC && p.use_oscale) return hipErrorInvalidValue;
+#define TTT_L(DK_, M_, CS_, DVT_, OS_) \
+    hipLaunchKernelGGL((tcb_fwd_kernel<DK_, M_, CS_, DVT_, OS_>), grid, block, 0, s, p)
+#define TTT_O(DK_, M_, CS_, DVT_)                  \
+    if (p.use_oscale) TTT_L(DK_, M_, CS_, DVT_, true); \
+    else TTT_L(DK_, M_, CS_, DVT_, false)
+#define TTT_M(CS_, DVT_)                                               \
+    if (pl.cs == CS_ && pl.dvt == DVT_) {                               \
+        if (p.dk == 128) {                                              \
+            if (mode == MODE_TC) { TTT_O(128, MODE_TC, CS_, DVT_); }     \
+            else if (mode == MODE_MOM) { TTT_O(128, MODE_MOM, CS_, DVT_); } \
+            else TTT_L(128, MODE_CC, CS_, DVT_, false);                 \
+        } else {                                                        \
+            if (mode == MODE_TC) { TTT_O(64, MODE_TC, CS_, DVT_); }      \
+            else if (mode == MODE_MOM) { TTT_O(64, MODE_MOM, CS_, DVT_); } \
+            else TTT_L(64, MODE_CC, CS_, DVT_, false);                  \
+        }                                                               \
+        return hipGetLastError();                                       \
     }
     TTT_M(64, 64)
     TTT_M(32, 32)
 #undef TTT_M
+#undef TTT_O
 #undef TTT_L
     return hipErrorInvalidValue;
 }
