@@ -682,6 +682,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 for (int ti = 0; ti < NTI; ++ti) {
                     const u32x2 lo = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap0);
                     const u32x2 hi = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap1);
+                    asm volatile("" ::: "memory");   // no pairing across tiles (see below)
                     const bf16x8 bq = join(lo, hi);
                     mma(acc[ti], Sop[kk], bq);
                     if (MOM) mma(acc2[ti], Mop[kk], bq);
@@ -832,6 +833,12 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 for (int ti = 0; ti < NTI; ++ti) {
                     const u32x2 lo = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap0);
                     const u32x2 hi = *reinterpret_cast<const u32x2*>(Qh + kk * BLK + ti * 512 + b_ap1);
+                    // keep each fragment's two reads apart from the next
+                    // tile's: left alone, the compiler pairs the reads of
+                    // neighbouring tiles (a constant 1 KB apart) into one
+                    // instruction and then shuffles the halves back into
+                    // operand order with 50 moves per two chunks
+                    asm volatile("" ::: "memory");
                     mma(acc_p[ti], Sop[kk], join(lo, hi));
                 }
             }
