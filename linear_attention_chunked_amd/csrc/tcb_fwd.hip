@@ -58,14 +58,6 @@ TTT_DEV u32x4 scale_row(const u32x4& w, float e) {
                  pack2bf(__uint_as_float(w[2] << 16) * e, __uint_as_float(w[2] & 0xffff0000u) * e),
                  pack2bf(__uint_as_float(w[3] << 16) * e, __uint_as_float(w[3] & 0xffff0000u) * e)};
 }
-TTT_DEV bf16x8 scale_frag(const bf16x8& f, const f32x4& s_lo, const f32x4& s_hi) {
-    const u32x4 w = __builtin_bit_cast(u32x4, f);
-    const u32x4 o = u32x4{pack2bf(__uint_as_float(w[0] << 16) * s_lo[0], __uint_as_float(w[0] & 0xffff0000u) * s_lo[1]),
-                          pack2bf(__uint_as_float(w[1] << 16) * s_lo[2], __uint_as_float(w[1] & 0xffff0000u) * s_lo[3]),
-                          pack2bf(__uint_as_float(w[2] << 16) * s_hi[0], __uint_as_float(w[2] & 0xffff0000u) * s_hi[1]),
-                          pack2bf(__uint_as_float(w[3] << 16) * s_hi[2], __uint_as_float(w[3] & 0xffff0000u) * s_hi[3])};
-    return __builtin_bit_cast(bf16x8, o);
-}
 
 }  // namespace
 
@@ -93,8 +85,8 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
 
     __shared__ __attribute__((aligned(16))) bf16_t sQ[2][NKB * BLK];
     __shared__ __attribute__((aligned(16))) bf16_t sK[2][NKB * BLK];
-    __shared__ __attribute__((aligned(16))) bf16_t sV[2][(DVT / 32) * BLKV];
-    __shared__ __attribute__((aligned(16))) float sE[2][NV][CS];
+    // V staged already scaled per token: eta | eta*w_{n-1-j} | eta*beta^{n-1-j}
+    __shared__ __attribute__((aligned(16))) bf16_t sV[2][NV][(DVT / 32) * BLKV];
     __shared__ __attribute__((aligned(16))) float sOS[2][CS];     // output row scales
     // one barrier per chunk (64 x 64 form without momentum): the score, partial
     // and output tiles are double-buffered, see the chunk loop
@@ -255,6 +247,17 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         re[st] = Eg ? (Eg + (int64_t)t0 * eL)[__mul24(min(tid % CS, lim), eL24)] : p.eta_scalar;
         if (OSC) ros[st] = OSg ? OSg[(int64_t)(t0 + min(tid % CS, lim)) * p.ocs[2]] : p.oscale_scalar;
     };
+    // one 16-byte piece of a V row (8 columns of token row_v) into the staged
+    // copies: times eta (e), and with momentum also times eta*w_{n-1-j} and
+    // eta*beta^{n-1-j}, each rounded to bf16 once
+    auto stage_v = [&](int buf, const u32x4& raw, float e, int n) {
+        *reinterpret_cast<u32x4*>(&sV[buf][0][loff_v]) = scale_row(raw, e);
+        if (MOM) {
+            const int pw = max(n - 1 - row_v, 0);   // rows past the end have e = 0
+            *reinterpret_cast<u32x4*>(&sV[buf][1 % NV][loff_v]) = scale_row(raw, e * sTab[pw]);
+            *reinterpret_cast<u32x4*>(&sV[buf][2 % NV][loff_v]) = scale_row(raw, e * sTab[(CS + 1) + pw]);
+        }
+    };
     auto store = [&](int c, int buf, auto SET, auto WITHQ) {
         constexpr int st = decltype(SET)::value;
         constexpr bool wq = decltype(WITHQ)::value;
@@ -264,27 +267,12 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = rk[st][x];
         }
         if (tid < NVC) {
-            if (MOM) {
-                *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = rv[st];
-            } else {
-                // without momentum V is staged as diag(eta) V: the eta of
-                // token r sits in lane r of every wave (zero past the end)
-                const int n = min(CS, L - c * CS);
-                const float e = __shfl(re[st], row_v);
-                *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = scale_row(rv[st], row_v < n ? e : 0.f);
-            }
-        }
-        if (tid < CS) {
+            // the eta of token r sits in lane r of every wave; zero past the end
             const int n = min(CS, L - c * CS);
-            const float e = (tid < n) ? re[st] : 0.f;
-            sE[buf][0][tid] = e;
-            if (OSC) sOS[buf][tid] = ros[st];
-            if (MOM) {
-                const int pw = n - 1 - tid;
-                sE[buf][1][tid] = (pw >= 0) ? e * sTab[pw] : 0.f;
-                sE[buf][2][tid] = (pw >= 0) ? e * sTab[(CS + 1) + pw] : 0.f;
-            }
+            const float e = __shfl(re[st], row_v);
+            stage_v(buf, rv[st], row_v < n ? e : 0.f, n);
         }
+        if (OSC && tid < CS) sOS[buf][tid] = ros[st];
     };
 
     // P^T tile assignment (query tile ti; key tiles tjA, tjB; -1 = none), grouped by
@@ -336,23 +324,20 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     using WQ = std::true_type;
     using NQ = std::false_type;
 
-    // value fragments of the staged chunk (tokens in accperm order), scaled
-    // in registers by eta (VB) and, with momentum, eta*w_{n-1-j} (VS) and
+    // value fragments of the staged chunk (tokens in accperm order), staged
+    // already scaled by eta (VB) and, with momentum, eta*w_{n-1-j} (VS) and
     // eta*beta^{n-1-j} (VM)
     auto vfrags = [&](int cur, bf16x8* VB, bf16x8* VS, bf16x8* VM) {
-        const bf16_t* V = sV[cur];
+        auto frag = [&](int k, int jb) {
+            const bf16_t* V = sV[cur][k];
+            return join(tr_read(V + b_v + (32 * jb) * 32), tr_read(V + b_v + (32 * jb + 16) * 32));
+        };
 #pragma unroll
         for (int jb = 0; jb < NJB; ++jb) {
-            const bf16x8 raw = join(tr_read(V + b_v + (32 * jb) * 32), tr_read(V + b_v + (32 * jb + 16) * 32));
-            if (!MOM) {
-                VB[jb] = raw;   // staged already scaled by eta
-            } else {
-                const float* e0 = &sE[cur][0][32 * jb + 4 * g];
-                VB[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e0), *reinterpret_cast<const f32x4*>(e0 + 16));
-                const float* e1 = &sE[cur][1][32 * jb + 4 * g];
-                const float* e2 = &sE[cur][2][32 * jb + 4 * g];
-                VS[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e1), *reinterpret_cast<const f32x4*>(e1 + 16));
-                VM[jb] = scale_frag(raw, *reinterpret_cast<const f32x4*>(e2), *reinterpret_cast<const f32x4*>(e2 + 16));
+            VB[jb] = frag(0, jb);
+            if (MOM) {
+                VS[jb] = frag(1 % NV, jb);
+                VM[jb] = frag(2 % NV, jb);
             }
         }
     };
@@ -487,17 +472,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 constexpr int st = decltype(SET)::value;
 #pragma unroll
                 for (int x = 0; x < UQ; ++x) *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = ak[st][x];
-                if (tid < NVC) {
-                    if (MOM) *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = av[st];
-                    else *reinterpret_cast<u32x4*>(&sV[buf][loff_v]) = scale_row(av[st], __shfl(ae[st], row_v));
-                }
-                if (tid < CS) {
-                    sE[buf][0][tid] = ae[st];
-                    if (MOM) {
-                        sE[buf][1][tid] = ae[st] * sTab[CS - 1 - tid];
-                        sE[buf][2][tid] = ae[st] * sTab[(CS + 1) + CS - 1 - tid];
-                    }
-                }
+                if (tid < NVC) stage_v(buf, av[st], __shfl(ae[st], row_v), CS);
             };
             using J0 = std::integral_constant<int, 0>;
             using J1 = std::integral_constant<int, 1>;
