@@ -40,6 +40,8 @@
 //     dM0 = beta S'_f                     (m_0 = beta M0 + g_0).
 // (The gradient with respect to beta itself is not computed.)
 #include "common.h"
+#include <mutex>
+
 #include "internal.h"
 
 namespace ttt {
@@ -186,6 +188,24 @@ size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype, bool moment
     return w;
 }
 
+// A helper stream per device (default priority, non-blocking), created on
+// first use: the epilogue runs on it beside the R pass.
+hipError_t side_stream(hipStream_t* out) {
+    static std::mutex mu;
+    static hipStream_t streams[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[dev]) {
+        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) return e;
+    }
+    *out = streams[dev];
+    return hipSuccess;
+}
+
 hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
     if (!bwd_supported(b.dtype, b.dk_dim, b.dv_dim)) return hipErrorInvalidValue;
     const size_t es = b.dtype == 1 ? 2 : 4;
@@ -254,6 +274,26 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         p.M_final = Mfp;
         if ((e = launch_tc_fwd(p, b.dtype, mode, s)) != hipSuccess) return e;
     }
+    // dv = eta P, deta = P . v: needs only P, so it runs on a helper stream
+    // beside the R pass (which writes only dk), and the caller's stream
+    // waits for it before the call's last kernel.  The R pass is bound by
+    // latency and leaves wave slots free on every CU.
+    struct Events {   // destroyed on every return; the runtime defers it until they complete
+        hipEvent_t p = nullptr, epi = nullptr;
+        ~Events() {
+            if (p) (void)hipEventDestroy(p);
+            if (epi) (void)hipEventDestroy(epi);
+        }
+    } ev;
+    hipStream_t s2 = nullptr;
+    if ((e = side_stream(&s2)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ev.p, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&ev.epi, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventRecord(ev.p, s)) != hipSuccess || (e = hipStreamWaitEvent(s2, ev.p, 0)) != hipSuccess)
+        return e;
+    if ((e = b.dtype == 1 ? launch_epilogue<bf16_t>(b, s2) : launch_epilogue<float>(b, s2)) != hipSuccess ||
+        (e = hipEventRecord(ev.epi, s2)) != hipSuccess)
+        return e;
     // R (into dk): queries v, keys do, values q, time reversed, state dS_final^T
     {
         TcParams p = pass_params(b);
@@ -286,8 +326,9 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         hipLaunchKernelGGL(bwd_state_kernel, sgrid, sblock, 0, s, Sfp, Mfp, b.beta, b.dS0, b.dM0, nst);
     else if (b.dM0)   // no momentum: m_0 does not depend on M0
         hipLaunchKernelGGL(bwd_zero_kernel, sgrid, sblock, 0, s, b.dM0, nst);
-    // dv = eta P, deta = P . v
-    return b.dtype == 1 ? launch_epilogue<bf16_t>(b, s) : launch_epilogue<float>(b, s);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // join: the caller's stream waits for the epilogue
+    return hipStreamWaitEvent(s, ev.epi, 0);
 }
 
 }  // namespace ttt
