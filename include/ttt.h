@@ -263,6 +263,12 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
  * TTT_ERR_SHAPE, TTT_ERR_VALUE (beta), TTT_ERR_ALIGN (16 bytes),
  * TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_ALIAS; TTT_ERR_HIP if a
  * launch fails.
+ * Streams: the dv/deta step runs on a library-owned helper stream of the
+ * current device (created on first use, default priority, non-blocking),
+ * forked from `stream` by an event and joined back before the call returns:
+ * all of the call's work is ordered before anything enqueued on `stream`
+ * afterwards, also inside a captured graph.  The helper stream is shared by
+ * concurrent calls on one device, which only serialises their dv/deta steps.
  */
 ttt_status_t ttt_bwd_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
                                     float beta, size_t* bytes);
