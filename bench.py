@@ -50,6 +50,7 @@ KERNEL_SOURCES = {
     "fe_gemm_kernel": ("frontend.hip", "gemm.h", "common.h"),
     "tcb_fwd_kernel+bwd_scale_kernels": ("tcb_fwd.hip", "bwd.hip", "common.h"),
     "swiglu_kernels": ("swiglu.hip", "gemm.h", "common.h"),
+    "state_scan_kernel": ("scan.hip", "common.h"),
 }
 
 
@@ -259,6 +260,36 @@ def setup_workload(name: str, dev: str):
                     dtype="bf16", tokens=B, bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="decode_kernel",
                     inputs=inp)
         return step, info
+    if name in ("scan", "scan-momentum"):
+        # the standalone chunk-state scan at the LM-scale shape: B8 H16, L 4096
+        # in 64-token chunks (N = 64), d_k = d_v = 128, fp32 aggregates
+        B, H, L, C, dk, dv = 8, 16, 4096, 64, 128, 128
+        N = L // C
+        beta = W.f32(0.9) if name == "scan-momentum" else 0.0
+        dS_c, dM_c = W.gen_state_deltas(B, H, N, dk, dv, seed=6200)
+        S0_c, M0_c = W.gen_state_deltas(B, H, 1, dk, dv, seed=6300)
+        S0_c, M0_c = S0_c[:, :, 0].contiguous(), M0_c[:, :, 0].contiguous()
+        dS = dS_c.to(dev)
+        dM = dM_c.to(dev) if beta else None
+        S0 = S0_c.to(dev)
+        M0 = M0_c.to(dev) if beta else None
+
+        def step():
+            return lac.chunk_state_scan(dS, dM, beta=beta, chunk=C, L=L, S0=S0, M0=M0)
+
+        nstate = 2 if beta else 1
+        bytes_alg = nstate * (2 * B * H * N + 2 * B * H) * dk * dv * 4
+        flop_alg = nstate * 2 * B * H * N * dk * dv
+
+        def cpu_sample():
+            import oracle
+            oracle.state_scan(dS_c, dM_c if beta else None, beta, C, L, S0_c, M0_c if beta else None)
+            return B * L, f"the whole workload ({B * H} heads, {N} chunks), fp64 sequential scan in C", oracle.threads()
+
+        info = dict(workload=name, B=B, H=H, L=L, N=N, chunk=C, dk=dk, dv=dv, beta=beta, dtype="fp32",
+                    tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="state_scan_kernel",
+                    inputs=None, cpu_sample=cpu_sample)
+        return step, info
     raise SystemExit(f"unknown workload {name}")
 
 
@@ -351,7 +382,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="lm-scale",
                     help="lm-scale (default), small-f32, inplace-32k, inplace-128k, momentum, dual-b16, "
-                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, inplace-frontend, swiglu, swiglu-mse")
+                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, inplace-frontend, swiglu, swiglu-mse, "
+                         "scan, scan-momentum")
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this many seconds of steps have run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
