@@ -392,7 +392,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the hot path on a single MI355X "
+        print("bench.py measures one GPU only: the hot path runs on a single MI355X "
               "(multi-GPU sharding is design-only). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

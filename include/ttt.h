@@ -61,7 +61,7 @@ typedef enum {
     TTT_ERR_SHAPE = 2,       /* a size or stride is out of range / inconsistent  */
     TTT_ERR_DTYPE = 3,       /* unknown dtype value                              */
     TTT_ERR_ALIGN = 4,       /* pointer or stride misaligned                     */
-    TTT_ERR_UNSUPPORTED = 5, /* valid arguments this build has no kernel for     */
+    TTT_ERR_UNSUPPORTED = 5, /* valid arguments the library has no kernel for    */
     TTT_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
     TTT_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed       */
     TTT_ERR_ALIAS = 8,       /* out overlaps an input                            */
