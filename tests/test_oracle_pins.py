@@ -625,6 +625,40 @@ def test_lookahead_conv_vs_torch(oracle_mod):
             assert not np.any(Yd[0, t])
 
 
+def test_lm_aligned_target_vs_torch(oracle_mod):
+    """V-hat = conv(X) Wv^T against torch's conv1d followed by
+    torch.nn.functional.linear (rows of Wv are output features) on ragged
+    B and L; and Wv's orientation by hand: a non-symmetric Wv with a
+    single-tap identity convolution gives X Wv^T, which the transposed
+    projection X Wv does not."""
+    rng = np.random.default_rng(54)
+    B, L, d, K = 3, 13, 5, 4
+    X, c, Wv = rnd(B, L, d, rng=rng), rnd(K, d, rng=rng), rnd(d, d, rng=rng)
+    Vh = oracle_mod.lm_aligned_target(X, c, Wv)
+    xt = torch.nn.functional.pad(torch.tensor(X).transpose(1, 2), (0, K - 1))
+    w = torch.tensor(c).T.unsqueeze(1)
+    Y = torch.nn.functional.conv1d(xt, w, groups=d).transpose(1, 2)
+    ref = torch.nn.functional.linear(Y, torch.tensor(Wv))
+    close(Vh, ref.numpy(), 1e-12)
+    # hand case: one token, one tap of ones, Wv = [[1, 2], [0, 1]]
+    # y = x = (3, 5); row i of V-hat is sum_j Wv[i, j] y_j -> (3 + 10, 5) = (13, 5)
+    Xh = np.array([[[3.0, 5.0]]])
+    Wh = np.array([[1.0, 2.0], [0.0, 1.0]])
+    got = oracle_mod.lm_aligned_target(Xh, np.ones((1, 2)), Wh)
+    close(got[0, 0], np.array([13.0, 5.0]), 0.0)
+    assert not np.allclose(got[0, 0], Xh[0, 0] @ Wh)        # a transposed projection gives (3, 11)
+
+
+def test_rel_l2(oracle_mod):
+    """The error measure of every parity test: 0 at x = ref, 1 at x = 2 ref or
+    x = 0, and ||x - ref|| / ||ref|| on a hand pair (3-4-5 triangle)."""
+    ref = np.array([[1.0, -2.0], [0.5, 4.0]])
+    assert oracle_mod.rel_l2(ref, ref) == 0.0
+    assert abs(oracle_mod.rel_l2(2 * ref, ref) - 1.0) < 1e-15
+    assert abs(oracle_mod.rel_l2(np.zeros_like(ref), ref) - 1.0) < 1e-15
+    assert abs(oracle_mod.rel_l2(np.array([3.0, 4.0]), np.array([0.0, 5.0])) - np.sqrt(10.0) / 5.0) < 1e-15
+
+
 def test_clip_scales(oracle_mod):
     """Clipped per-token rates: the chunk update's norm by the Gram identity
     ||Z^T V||_F^2 = sum_{s,t} (z_s . z_t)(v_s . v_t), a different computation;
