@@ -156,10 +156,11 @@ def setup_workload(name: str, dev: str):
         eta = inp.eta.to(dev) if inp.eta is not None else None
         S0 = inp.S0.to(dev) if inp.S0 is not None else None
         do, dS = dout.to(dev), dSf.to(dev)
+        side = torch.cuda.Stream()   # the dv/deta step runs beside the last pass
 
         def step():
             return lac.bwd_chunked(q, k, v, do, eta=eta, eta_scalar=inp.eta_scalar, beta=inp.beta, S0=S0,
-                                   dS_final=dS, need_dM0=mom)
+                                   dS_final=dS, need_dM0=mom, side_stream=side)
 
         es = 2
         bytes_alg = (B * H * L * (2 * dk + 2 * dv) * es      # q, k, v, dout

@@ -40,10 +40,20 @@
  *    must be multiples of 8 elements (16 bytes of bf16) and below 2^23
  *    elements (eta's L stride too); S0/M0/W0/S_final
  *    etc. are contiguous [dk, dv] fp32 blocks per (b, h).
- *  - `out` must not overlap any input.  q and k may be the same tensor.
+ *  - Size limits (TTT_ERR_SHAPE beyond them): sequence lengths, chunks,
+ *    mini-batches and token counts up to 2^30; up to 2^24 sequences
+ *    (B * H); head and feature sizes up to 2^16; no tensor spanning more
+ *    than 2^48 bytes through its strides.
+ *  - Written buffers (outputs, final states, the workspace) must not overlap
+ *    any input, each other, or themselves (an output's strides must give
+ *    every (b, h, t) its own row); TTT_ERR_ALIAS otherwise.  Inputs may
+ *    overlap each other (q and k may be the same tensor; a state may be
+ *    broadcast with stride 0).  In-place use is supported only where an
+ *    entry point says so (ttt_decode_step's S and M).
  *  - Errors never abort and never throw across the ABI; launch failures are
  *    reported as TTT_ERR_HIP.  Calls on different streams with different
- *    workspaces may run concurrently; the library has no global state.
+ *    workspaces may run concurrently; the library holds no global or static
+ *    state and creates no streams of its own.
  */
 #ifndef TTT_MI355X_H
 #define TTT_MI355X_H
@@ -64,8 +74,9 @@ typedef enum {
     TTT_ERR_UNSUPPORTED = 5, /* valid arguments the library has no kernel for    */
     TTT_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required          */
     TTT_ERR_HIP = 7,         /* a HIP runtime call or kernel launch failed       */
-    TTT_ERR_ALIAS = 8,       /* out overlaps an input                            */
-    TTT_ERR_VALUE = 9        /* a scalar is out of range (beta not in [0,1), ...) */
+    TTT_ERR_ALIAS = 8,       /* a written buffer overlaps an input or another    */
+    TTT_ERR_VALUE = 9,       /* a scalar is out of range (beta not in [0,1), ...) */
+    TTT_ERR_TIMEOUT = 10     /* a look-back wait gave up: results are invalid    */
 } ttt_status_t;
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype_t;
@@ -111,6 +122,10 @@ typedef struct ttt_fwd_args {
     void* workspace;          /* device scratch, >= ttt_fwd_workspace_size bytes */
     size_t workspace_bytes;
     void* stream;             /* hipStream_t                                     */
+    int32_t lookback_polls;   /* bound of each look-back wait of a segmented
+                                 call, in polls of ~0.1 us: 0 = the default
+                                 (2^22); < 0 = give up without polling (for
+                                 tests of the failure report)                   */
 } ttt_fwd_args;
 
 /*
@@ -138,13 +153,35 @@ typedef struct ttt_fwd_args {
  * dtypes and both modes; CHUNK_CAUSAL with bf16 also dk, dv multiples of 256
  * (large fast weights, e.g. the In-Place Wdown) with chunk a multiple of 256.
  * CHUNK_CAUSAL with small dims needs chunk a multiple of 64 (bf16) or 32
- * (fp32).  Returns TTT_ERR_WORKSPACE if the workspace is too small.
+ * (fp32).  Returns TTT_ERR_WORKSPACE if the workspace is too small, and
+ * TTT_ERR_ALIAS if out, S_final, M_final or the workspace overlaps an input
+ * (q, k, v, eta, S0, M0) or another of them, or if out's strides map two
+ * (b, h, t) onto overlapping rows.
  */
 ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* args);
 
 /* Bytes of workspace ttt_fwd_chunked needs for these arguments (pointers
  * need not be set).  0 is a valid answer (workspace may then be NULL). */
 ttt_status_t ttt_fwd_workspace_size(const ttt_fwd_args* args, size_t* bytes);
+
+/*
+ * ttt_fwd_lookback_status -- whether the last ttt_fwd_chunked call with
+ * these arguments and this workspace gave up a look-back wait.
+ *
+ * When the (head, value-column tile) grid is short of the chip, a long
+ * sequence is cut into segments that run concurrently and hand their states
+ * on through flags in the workspace ([P1] paragraph on associativity: the
+ * segment states compose; [P2] paragraph on the associative scan).  Each
+ * wait for a flag is bounded (args->lookback_polls); a wait that gives up
+ * lets the kernel finish with invalid results and raises an error word in
+ * the workspace.  This call waits for `args->stream`, reads that word and
+ * sets *gave_up to 1 if it was raised (0 otherwise, and always 0 for calls
+ * that were not segmented).  Not callable inside a graph capture (it
+ * synchronises the stream).  Errors: TTT_ERR_NULL, the shape errors of
+ * ttt_fwd_workspace_size, TTT_ERR_WORKSPACE (segmented and no workspace),
+ * TTT_ERR_HIP.
+ */
+ttt_status_t ttt_fwd_lookback_status(const ttt_fwd_args* args, int32_t* gave_up);
 
 /*
  * ttt_chunk_state_scan -- exclusive scan of per-chunk state deltas.
@@ -165,7 +202,9 @@ ttt_status_t ttt_fwd_workspace_size(const ttt_fwd_args* args, size_t* bytes);
  * M_excl [B,H,N,dk,dv] (M_excl may be NULL), and the state after the last
  * chunk, S_final / M_final [B,H,dk,dv] (each may be NULL).  S0 / M0 are the
  * incoming state (NULL = zero).  fp32 throughout.  Any dk, dv >= 1 with
- * dk*dv a multiple of 4.  Needs no workspace (ws may be NULL).
+ * dk*dv a multiple of 4.  Needs no workspace (ws may be NULL).  The outputs
+ * must not overlap the inputs or each other (no in-place scan):
+ * TTT_ERR_ALIAS.
  */
 ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk,
                                   int32_t dk, int32_t dv,
@@ -191,7 +230,9 @@ ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk
  *
  * q, k [B,H,L,d], v, out [B,H,L,dv] contiguous, dtype `dtype`; W0
  * [B,H,d,dv] fp32 (W0_stride_bh elements between heads, 0 broadcasts one
- * W0); W_final [B,H,d,dv] fp32 contiguous or NULL.  Supported: d = 64,
+ * W0); W_final [B,H,d,dv] fp32 contiguous or NULL; out and W_final
+ * overlap no input (q, k, v, W0) and not each other (TTT_ERR_ALIAS).
+ * Supported: d = 64,
  * dv = 64, bf16 or fp32, any minibatch >= 1 (the last mini-batch holds
  * the remaining L - (ceil(L/minibatch)-1)*minibatch tokens).  Needs no
  * workspace.
@@ -218,8 +259,9 @@ ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32
  * q, k [B,H,dk] and v, out [B,H,dv] are contiguous, dtype `dtype` (out in
  * that dtype).  eta [B,H] fp32 or NULL (eta_scalar for every sequence).
  * S [B,H,dk,dv] fp32 contiguous, read and written in place; M the same shape,
- * required when beta != 0 (ignored and may be NULL otherwise).  out must not
- * overlap q, k, v, S or M.  Supported: dk in [1, 1024], dv a multiple of 4.
+ * required when beta != 0 (ignored and may be NULL otherwise).  out, S and M
+ * (the written buffers) must not overlap q, k, v, eta or each other.
+ * Supported: dk in [1, 1024], dv a multiple of 4.
  * The state is read and written once (memory-bound); the update is fp32.
  * All pointers are caller-owned device memory, 16-byte aligned; stream is a
  * hipStream_t (NULL = default stream).  Nothing is allocated.
@@ -250,7 +292,8 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
  *     dq_t = do_t S_t^T,  dk_t = eta_t A_t v_t^T,  dv_t = eta_t k_t A_t,
  *     deta_t = k_t A_t v_t^T (per token, also for a scalar eta: its gradient
  *     is the sum over tokens),  dS0 = dL/dS0,  dM0 = beta A_0.
- * The gradient with respect to beta is not computed.
+ * Every beta in [0, 1) is handled without dividing by beta.  The gradient
+ * with respect to beta is not computed.
  *
  * All tensors are contiguous: q, k, dq, dk [B,H,L,dk]; v, dout, dv
  * [B,H,L,dv] in `dtype`; eta [B,H,L] fp32 or NULL (eta_scalar); S0, M0,
@@ -263,12 +306,14 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
  * TTT_ERR_SHAPE, TTT_ERR_VALUE (beta), TTT_ERR_ALIGN (16 bytes),
  * TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE, TTT_ERR_ALIAS; TTT_ERR_HIP if a
  * launch fails.
- * Streams: the dv/deta step runs on a library-owned helper stream of the
- * current device (created on first use, default priority, non-blocking),
- * forked from `stream` by an event and joined back before the call returns:
- * all of the call's work is ordered before anything enqueued on `stream`
- * afterwards, also inside a captured graph.  The helper stream is shared by
- * concurrent calls on one device, which only serialises their dv/deta steps.
+ * Streams: everything runs on `stream` when side_stream is NULL (or equal
+ * to `stream`).  Otherwise side_stream, a second stream of the caller on
+ * the same device, runs the dv/deta step beside the last pass: it is forked
+ * from `stream` by an event and joined back before the call returns, also
+ * on an error return after the fork, so all of the call's work is ordered
+ * before anything enqueued on `stream` afterwards, also inside a captured
+ * graph.  Work the caller enqueues on side_stream during the call runs
+ * after the fork point, like any other work ordered behind an event.
  */
 ttt_status_t ttt_bwd_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
                                     float beta, size_t* bytes);
@@ -277,7 +322,7 @@ ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_
                              float beta, const float* S0, const float* M0, const void* dout,
                              const float* dS_final, const float* dM_final,
                              void* dq, void* dk_out, void* dv_out, float* deta, float* dS0, float* dM0,
-                             void* workspace, size_t workspace_bytes, void* stream);
+                             void* workspace, size_t workspace_bytes, void* stream, void* side_stream);
 
 /*
  * In-Place TTT front end ([P2] "In-Place 테스트 시점 학습: LLM을 위한 원활한

@@ -27,6 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinear_attention_chunked_amd.so")
 
 TTT_F32, TTT_BF16 = 0, 1
+TTT_ERR_TIMEOUT = 10
 TOKEN_CAUSAL, CHUNK_CAUSAL = 0, 1
 _MODES = {"token_causal": TOKEN_CAUSAL, "chunk_causal": CHUNK_CAUSAL}
 
@@ -57,6 +58,7 @@ class FwdArgs(ctypes.Structure):
         ("S_final", _vp), ("M_final", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("stream", _vp),
+        ("lookback_polls", ctypes.c_int32),
     ]
 
 
@@ -74,6 +76,8 @@ def load_library():
     lib.ttt_fwd_chunked.argtypes = [ctypes.POINTER(FwdArgs)]
     lib.ttt_fwd_chunked.restype = ctypes.c_int
     lib.ttt_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ttt_fwd_lookback_status.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_int32)]
+    lib.ttt_fwd_lookback_status.restype = ctypes.c_int
     lib.ttt_fwd_workspace_size.restype = ctypes.c_int
     i32, f32 = ctypes.c_int32, ctypes.c_float
     lib.ttt_chunk_state_scan.argtypes = [i32, i32, i32, i32, i32, i32, _vp, _vp, f32, _vp, _vp,
@@ -88,7 +92,7 @@ def load_library():
     lib.ttt_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, f32, ctypes.POINTER(ctypes.c_size_t)]
     lib.ttt_bwd_workspace_size.restype = ctypes.c_int
     lib.ttt_bwd_chunked.argtypes = [i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, f32, _vp, _vp,
-                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+                                    _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp]
     lib.ttt_bwd_chunked.restype = ctypes.c_int
     sz = ctypes.POINTER(ctypes.c_size_t)
     lib.ttt_inplace_gated_input.argtypes = [i32, i32, i32, _vp, _vp, _vp, _vp, _vp]
@@ -165,14 +169,18 @@ def _state_strides(t: torch.Tensor | None, name: str):
 
 
 def fwd_chunked(q, k, v, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None, chunk=64,
-                mode="token_causal", out=None, return_state=False, stream=None):
+                mode="token_causal", out=None, return_state=False, stream=None, check_lookback=False,
+                lookback_polls=0):
     """Chunked fast-weight forward (``ttt_fwd_chunked``).
 
     q, k: [B,H,L,dk]; v: [B,H,L,dv] (fp32 or bf16, same dtype; q may be k);
     eta: [B,H,L] fp32 per-token step size or None (eta_scalar for all tokens);
     beta: momentum (token-causal only); S0, M0: fp32 [B,H,dk,dv] or None.
     Returns out [B,H,L,dv] (input dtype), plus (S_final, M_final) when
-    return_state (M_final is None unless beta != 0)."""
+    return_state (M_final is None unless beta != 0).  check_lookback: wait
+    for the call and raise TTTError (TTT_ERR_TIMEOUT) if a look-back wait of
+    a segmented call gave up (``ttt_fwd_lookback_status``); lookback_polls:
+    the bound of those waits (0: the library default)."""
     lib = load_library()
     _require_gpu(q, k, v, eta, S0, M0, out)
     B, H, L, dk = q.shape
@@ -210,7 +218,13 @@ def fwd_chunked(q, k, v, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None
         work = torch.empty(ws.value, dtype=torch.uint8, device=q.device)
     a.workspace, a.workspace_bytes = _ptr(work), ws.value
     a.stream = _stream(stream)
+    a.lookback_polls = int(lookback_polls)
     _check(lib.ttt_fwd_chunked(ctypes.byref(a)))
+    if check_lookback:
+        gave_up = ctypes.c_int32(0)
+        _check(lib.ttt_fwd_lookback_status(ctypes.byref(a), ctypes.byref(gave_up)))
+        if gave_up.value:
+            raise TTTError(TTT_ERR_TIMEOUT, lib.ttt_status_string(TTT_ERR_TIMEOUT).decode())
     if return_state:
         return out, S_final, M_final
     return out
@@ -322,13 +336,15 @@ def bwd_workspace_size(B, H, L, dk, dv, *, dtype=torch.bfloat16, beta=0.0):
 
 
 def bwd_chunked(q, k, v, dout, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None, dS_final=None,
-                dM_final=None, need_deta=True, need_dS0=True, need_dM0=False, stream=None):
+                dM_final=None, need_deta=True, need_dS0=True, need_dM0=False, stream=None, side_stream=None):
     """Backward of the token-causal forward (``ttt_bwd_chunked``).
 
     q, k: [B,H,L,dk]; v, dout: [B,H,L,dv], contiguous, fp32 or bf16; eta fp32
     [B,H,L] or None (eta_scalar); S0, M0, dS_final, dM_final fp32
     [B,H,dk,dv] or None.  Returns (dq, dk, dv, deta, dS0, dM0); deta is per
-    token; the optional outputs are None unless requested."""
+    token; the optional outputs are None unless requested.  side_stream: an
+    optional second torch.cuda.Stream on the same device that runs the dv/deta
+    step beside the last pass (forked from and joined back to `stream`)."""
     lib = load_library()
     _require_gpu(q, k, v, dout, eta, S0, M0, dS_final, dM_final)
     if q.dim() != 4:
@@ -354,7 +370,8 @@ def bwd_chunked(q, k, v, dout, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M
     _check(lib.ttt_bwd_chunked(B, H, L, dk, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
                                float(eta_scalar), float(beta), _ptr(S0), _ptr(M0), _ptr(dout), _ptr(dS_final),
                                _ptr(dM_final), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(deta), _ptr(dS0), _ptr(dM0),
-                               _ptr(ws), wsb, _stream(stream)))
+                               _ptr(ws), wsb, _stream(stream),
+                               None if side_stream is None else ctypes.c_void_p(side_stream.cuda_stream)))
     return dq, dk_, dv_, deta, dS0, dM0
 
 

@@ -22,17 +22,129 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t esize(int dtype) { return dtype == TTT_BF16 ? 2 : 4; }
 
-// [lo, hi) byte range touched by a [B,H,L,d] strided tensor
+// Largest byte extent any buffer may have (256 TiB, beyond any device): sizes
+// and strides are checked against it with exact 128-bit arithmetic, so no
+// extent computed below can overflow.
+constexpr unsigned __int128 kMaxBytes = (unsigned __int128)1 << 48;
+
+// bytes spanned by n0 x n1 x n2 rows of d elements at element strides s0..s2
+// (sizes >= 1, strides >= 0); false when the span exceeds kMaxBytes
+bool extent_bytes(int64_t n0, int64_t s0, int64_t n1, int64_t s1, int64_t n2, int64_t s2, int64_t d, size_t es,
+                  uint64_t* bytes) {
+    if (n0 < 1 || n1 < 1 || n2 < 1 || d < 0 || s0 < 0 || s1 < 0 || s2 < 0) return false;
+    const unsigned __int128 last = (unsigned __int128)(n0 - 1) * (uint64_t)s0 +
+                                   (unsigned __int128)(n1 - 1) * (uint64_t)s1 +
+                                   (unsigned __int128)(n2 - 1) * (uint64_t)s2 + (uint64_t)d;
+    const unsigned __int128 b = last * es;
+    if (b > kMaxBytes) return false;
+    *bytes = (uint64_t)b;
+    return true;
+}
+
+// bytes of a contiguous tensor of the given extents (each >= 0); false when
+// the product exceeds kMaxBytes
+bool dense_bytes(std::initializer_list<int64_t> dims, size_t es, size_t* bytes) {
+    unsigned __int128 n = es;
+    for (int64_t x : dims) {
+        if (x < 0) return false;
+        n *= (uint64_t)x;
+        if (n > kMaxBytes) return false;
+    }
+    *bytes = (size_t)n;
+    return true;
+}
+
+// Size limits of every entry point (TTT_ERR_SHAPE beyond them): sequence
+// lengths, chunks and token counts up to 2^30, up to 2^24 sequences (B * H),
+// feature and head sizes up to 2^16.  Within them every index computed on
+// the host or in a kernel fits its type.
+constexpr int64_t kMaxLen = int64_t(1) << 30;
+constexpr int64_t kMaxSeqs = int64_t(1) << 24;
+constexpr int64_t kMaxFeat = int64_t(1) << 16;
+bool within(int64_t x, int64_t hi) { return x >= 1 && x <= hi; }
+// B, H with B * H sequences; L; feature sizes
+bool shape_ok(int64_t B, int64_t H, int64_t L, std::initializer_list<int64_t> feats) {
+    if (!within(B, kMaxSeqs) || !within(H, kMaxSeqs) || !within(B * H, kMaxSeqs) || !within(L, kMaxLen))
+        return false;
+    for (int64_t f : feats)
+        if (!within(f, kMaxFeat)) return false;
+    return true;
+}
+
+// [lo, hi) byte range touched by a [B,H,L,d] strided tensor whose extent was
+// checked by extent_bytes
 void span(const void* base, const int64_t* st, int B, int H, int L, int d, size_t es,
           uintptr_t* lo, uintptr_t* hi) {
-    const int64_t last = (int64_t)(B - 1) * st[0] + (int64_t)(H - 1) * st[1] + (int64_t)(L - 1) * st[2] + d;
+    uint64_t n = 0;
+    (void)extent_bytes(B, st[0], H, st[1], L, st[2], d, es, &n);
     *lo = reinterpret_cast<uintptr_t>(base);
-    *hi = *lo + (uintptr_t)last * es;
+    *hi = *lo + (uintptr_t)n;
 }
 
 bool overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
-ttt_status_t check_tensor(const void* p, const int64_t* st, int d, int dtype) {
+// a byte range [lo, hi); lo = hi = 0 for an absent (NULL) buffer
+struct Range {
+    uintptr_t lo = 0, hi = 0;
+};
+
+Range rng(const void* p, size_t bytes) {
+    Range r;
+    if (p) {
+        r.lo = reinterpret_cast<uintptr_t>(p);
+        r.hi = r.lo + bytes;
+    }
+    return r;
+}
+
+bool overlap(const Range& a, const Range& b) { return a.hi > a.lo && b.hi > b.lo && overlap(a.lo, a.hi, b.lo, b.hi); }
+
+// [B, H, L, d] strided tensor
+Range tensor_range(const void* p, const int64_t* st, int B, int H, int L, int d, size_t es) {
+    Range r;
+    if (p) span(p, st, B, H, L, d, es, &r.lo, &r.hi);
+    return r;
+}
+
+// [B, H] blocks of n elements of `es` bytes with B / H strides (0
+// broadcasts); the extent was checked by extent_bytes
+Range block_range(const void* p, int64_t sb, int64_t sh, int B, int H, int64_t n, size_t es) {
+    uint64_t bytes = 0;
+    (void)extent_bytes(B, sb, H, sh, 1, 0, n, es, &bytes);
+    return rng(p, (size_t)bytes);
+}
+
+// true when two distinct (b, h, t) of a strided [B, H, L, d] tensor never
+// share an element: sorted by stride, every dimension of extent > 1 steps
+// past everything the smaller dimensions span (rows are d elements wide)
+bool injective(const int64_t* st, int B, int H, int L, int d) {
+    int64_t s[3] = {st[0], st[1], st[2]}, n[3] = {B, H, L};
+    for (int i = 0; i < 3; ++i)          // insertion sort by stride
+        for (int j = i; j > 0 && s[j] < s[j - 1]; --j) {
+            std::swap(s[j], s[j - 1]);
+            std::swap(n[j], n[j - 1]);
+        }
+    int64_t extent = d;
+    for (int i = 0; i < 3; ++i) {
+        if (n[i] == 1) continue;
+        if (s[i] < extent) return false;
+        extent = s[i] * (n[i] - 1) + extent;
+    }
+    return true;
+}
+
+// no written range overlaps a read range or another written range
+bool disjoint_sets(std::initializer_list<Range> written, std::initializer_list<Range> read) {
+    for (auto w = written.begin(); w != written.end(); ++w) {
+        for (const Range& r : read)
+            if (overlap(*w, r)) return false;
+        for (auto w2 = w + 1; w2 != written.end(); ++w2)
+            if (overlap(*w, *w2)) return false;
+    }
+    return true;
+}
+
+ttt_status_t check_tensor(const void* p, const int64_t* st, int B, int H, int L, int d, int dtype) {
     if (!p) return TTT_ERR_NULL;
     if (!aligned16(p)) return TTT_ERR_ALIGN;
     const int64_t vec = 16 / (int64_t)esize(dtype);
@@ -42,6 +154,8 @@ ttt_status_t check_tensor(const void* p, const int64_t* st, int d, int dtype) {
     }
     if (st[2] < d) return TTT_ERR_SHAPE;  // rows must not overlap
     if (st[2] >= (int64_t(1) << 23)) return TTT_ERR_SHAPE;  // in-chunk row offsets use 24-bit products
+    uint64_t n = 0;
+    if (!extent_bytes(B, st[0], H, st[1], L, st[2], d, esize(dtype), &n)) return TTT_ERR_SHAPE;
     return TTT_OK;
 }
 
@@ -61,8 +175,7 @@ size_t workspace_bytes_for(const ttt_fwd_args* a, int mode) {
 ttt_status_t validate_shapes(const ttt_fwd_args* a, int* mode_out) {
     if (!a) return TTT_ERR_NULL;
     if (a->dtype != TTT_F32 && a->dtype != TTT_BF16) return TTT_ERR_DTYPE;
-    if (a->B < 1 || a->H < 1 || a->L < 1 || a->dk < 1 || a->dv < 1 || a->chunk < 1)
-        return TTT_ERR_SHAPE;
+    if (!shape_ok(a->B, a->H, a->L, {a->dk, a->dv}) || !within(a->chunk, kMaxLen)) return TTT_ERR_SHAPE;
     if (a->mode != TTT_TOKEN_CAUSAL && a->mode != TTT_CHUNK_CAUSAL) return TTT_ERR_VALUE;
     if (!(a->beta >= 0.f && a->beta < 1.f)) return TTT_ERR_VALUE;
     if (a->mode == TTT_CHUNK_CAUSAL && a->beta != 0.f) return TTT_ERR_VALUE;
@@ -77,30 +190,42 @@ ttt_status_t validate_shapes(const ttt_fwd_args* a, int* mode_out) {
 ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
     ttt_status_t s = validate_shapes(a, mode_out);
     if (s != TTT_OK) return s;
-    if ((s = check_tensor(a->q, a->q_stride, a->dk, a->dtype)) != TTT_OK) return s;
-    if ((s = check_tensor(a->k, a->k_stride, a->dk, a->dtype)) != TTT_OK) return s;
-    if ((s = check_tensor(a->v, a->v_stride, a->dv, a->dtype)) != TTT_OK) return s;
-    if ((s = check_tensor(a->out, a->out_stride, a->dv, a->dtype)) != TTT_OK) return s;
+    if ((s = check_tensor(a->q, a->q_stride, a->B, a->H, a->L, a->dk, a->dtype)) != TTT_OK) return s;
+    if ((s = check_tensor(a->k, a->k_stride, a->B, a->H, a->L, a->dk, a->dtype)) != TTT_OK) return s;
+    if ((s = check_tensor(a->v, a->v_stride, a->B, a->H, a->L, a->dv, a->dtype)) != TTT_OK) return s;
+    if ((s = check_tensor(a->out, a->out_stride, a->B, a->H, a->L, a->dv, a->dtype)) != TTT_OK) return s;
+    uint64_t n = 0;
+    const int64_t st = (int64_t)a->dk * a->dv;
     if (a->eta) {
         for (int i = 0; i < 3; ++i)
             if (a->eta_stride[i] < 0) return TTT_ERR_SHAPE;
         if (a->eta_stride[2] >= (int64_t(1) << 23)) return TTT_ERR_SHAPE;
+        if (!extent_bytes(a->B, a->eta_stride[0], a->H, a->eta_stride[1], a->L, a->eta_stride[2], 1, 4, &n))
+            return TTT_ERR_SHAPE;
     }
-    if (a->S0 && (a->S0_stride[0] < 0 || a->S0_stride[1] < 0)) return TTT_ERR_SHAPE;
-    if (a->M0 && (a->M0_stride[0] < 0 || a->M0_stride[1] < 0)) return TTT_ERR_SHAPE;
-    // out must not overlap an input
-    uintptr_t o0, o1, x0, x1;
-    const size_t es = esize(a->dtype);
-    span(a->out, a->out_stride, a->B, a->H, a->L, a->dv, es, &o0, &o1);
-    span(a->q, a->q_stride, a->B, a->H, a->L, a->dk, es, &x0, &x1);
-    if (overlap(o0, o1, x0, x1)) return TTT_ERR_ALIAS;
-    span(a->k, a->k_stride, a->B, a->H, a->L, a->dk, es, &x0, &x1);
-    if (overlap(o0, o1, x0, x1)) return TTT_ERR_ALIAS;
-    span(a->v, a->v_stride, a->B, a->H, a->L, a->dv, es, &x0, &x1);
-    if (overlap(o0, o1, x0, x1)) return TTT_ERR_ALIAS;
+    if (a->S0 && !extent_bytes(a->B, a->S0_stride[0], a->H, a->S0_stride[1], 1, 0, st, 4, &n)) return TTT_ERR_SHAPE;
+    if (a->M0 && !extent_bytes(a->B, a->M0_stride[0], a->H, a->M0_stride[1], 1, 0, st, 4, &n)) return TTT_ERR_SHAPE;
+    size_t nstate = 0;
+    if (!dense_bytes({a->B, a->H, st}, 4, &nstate)) return TTT_ERR_SHAPE;
     const size_t need = workspace_bytes_for(a, *mode_out);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return TTT_ERR_WORKSPACE;
     if (a->workspace && !aligned16(a->workspace)) return TTT_ERR_ALIGN;
+    // the written buffers (out, the final states, the workspace) overlap no
+    // input and no other written buffer, and out does not overlap itself
+    if (!injective(a->out_stride, a->B, a->H, a->L, a->dv)) return TTT_ERR_ALIAS;
+    const size_t es = esize(a->dtype);
+    const Range out = tensor_range(a->out, a->out_stride, a->B, a->H, a->L, a->dv, es);
+    const Range sf = rng(a->S_final, nstate);
+    const Range mf = rng(*mode_out == MODE_MOM ? a->M_final : nullptr, nstate);
+    const Range ws = rng(need > 0 ? a->workspace : nullptr, need);
+    const Range q = tensor_range(a->q, a->q_stride, a->B, a->H, a->L, a->dk, es);
+    const Range k = tensor_range(a->k, a->k_stride, a->B, a->H, a->L, a->dk, es);
+    const Range v = tensor_range(a->v, a->v_stride, a->B, a->H, a->L, a->dv, es);
+    const Range eta = a->eta ? tensor_range(a->eta, a->eta_stride, a->B, a->H, a->L, 1, 4) : Range{};
+    const Range s0 = block_range(a->S0, a->S0_stride[0], a->S0_stride[1], a->B, a->H, st, 4);
+    const Range m0 = block_range(*mode_out == MODE_MOM ? a->M0 : nullptr, a->M0_stride[0], a->M0_stride[1], a->B,
+                                 a->H, st, 4);
+    if (!disjoint_sets({out, sf, mf, ws}, {q, k, v, eta, s0, m0})) return TTT_ERR_ALIAS;
     return TTT_OK;
 }
 
@@ -122,8 +247,9 @@ const char* ttt_status_string(ttt_status_t s) {
         case TTT_ERR_UNSUPPORTED: return "no kernel for these dimensions";
         case TTT_ERR_WORKSPACE: return "workspace missing or too small";
         case TTT_ERR_HIP: return "HIP runtime or launch error";
-        case TTT_ERR_ALIAS: return "output overlaps an input";
+        case TTT_ERR_ALIAS: return "a written buffer overlaps an input, another written buffer or itself";
         case TTT_ERR_VALUE: return "scalar argument out of range";
+        case TTT_ERR_TIMEOUT: return "a look-back wait gave up: results are invalid";
     }
     return "unknown status";
 }
@@ -174,9 +300,30 @@ ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* a) {
     p.dv = a->dv;
     p.chunk = a->chunk;
     p.workspace = a->workspace;
+    p.lb_max_polls = a->lookback_polls;
     const hipStream_t st = reinterpret_cast<hipStream_t>(a->stream);
     if (use_inplace(a, mode)) return from_hip(ttt::launch_inplace(p, a->workspace, st));
     return from_hip(ttt::launch_tc_fwd(p, a->dtype, mode, st));
+}
+
+ttt_status_t ttt_fwd_lookback_status(const ttt_fwd_args* a, int32_t* gave_up) {
+    if (!a || !gave_up) return TTT_ERR_NULL;
+    int mode = 0;
+    const ttt_status_t s = validate_shapes(a, &mode);
+    if (s != TTT_OK) return s;
+    *gave_up = 0;
+    if (use_inplace(a, mode) || !ttt::tcb_supported(a->dtype, a->dk, a->dv)) return TTT_OK;
+    const int64_t idx = ttt::tcb_error_word(a->B, a->H, a->L, a->dv, mode, a->chunk);
+    if (idx < 0) return TTT_OK;
+    if (!a->workspace) return TTT_ERR_WORKSPACE;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(a->stream);
+    int32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, static_cast<const int32_t*>(a->workspace) + idx, sizeof(v),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return TTT_ERR_HIP;
+    *gave_up = v != 0 ? 1 : 0;
+    return TTT_OK;
 }
 
 ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk, int32_t dk,
@@ -186,7 +333,7 @@ ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk
                                   size_t workspace_bytes, void* stream) {
     (void)workspace;
     (void)workspace_bytes;
-    if (B < 1 || H < 1 || L < 1 || chunk < 1 || dk < 1 || dv < 1) return TTT_ERR_SHAPE;
+    if (!shape_ok(B, H, L, {dk, dv}) || !within(chunk, kMaxLen)) return TTT_ERR_SHAPE;
     if (((int64_t)dk * dv) % 4 != 0) return TTT_ERR_UNSUPPORTED;
     if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_VALUE;
     if (!dS) return TTT_ERR_NULL;
@@ -194,6 +341,17 @@ ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk
     const void* ptrs[] = {dS, dM, S0, M0, S_excl, M_excl, S_final, M_final};
     for (const void* q : ptrs)
         if (q && !aligned16(q)) return TTT_ERR_ALIGN;
+    // outputs overlap neither the inputs nor each other (the kernel reads and
+    // writes through restrict-qualified pointers; in-place use is not supported)
+    {
+        const bool mom = beta != 0.f;
+        const size_t blk = (size_t)dk * dv * 4, N = (size_t)((L + chunk - 1) / chunk);
+        const size_t all = (size_t)B * H * N * blk, one = (size_t)B * H * blk;
+        if (!disjoint_sets({rng(S_excl, all), rng(mom ? M_excl : nullptr, all), rng(S_final, one),
+                            rng(mom ? M_final : nullptr, one)},
+                           {rng(dS, all), rng(mom ? dM : nullptr, all), rng(S0, one), rng(mom ? M0 : nullptr, one)}))
+            return TTT_ERR_ALIAS;
+    }
     return from_hip(ttt::launch_state_scan(B, H, L, chunk, dk, dv, dS, beta != 0.f ? dM : nullptr, beta,
                                            S0, beta != 0.f ? M0 : nullptr, S_excl, M_excl, S_final,
                                            M_final, reinterpret_cast<hipStream_t>(stream)));
@@ -207,21 +365,20 @@ ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32
     (void)workspace;
     (void)workspace_bytes;
     if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
-    if (B < 1 || H < 1 || L < 1 || d < 1 || dv < 1 || minibatch < 1 || W0_stride_bh < 0)
-        return TTT_ERR_SHAPE;
+    if (!shape_ok(B, H, L, {d, dv}) || !within(minibatch, kMaxLen) || W0_stride_bh < 0) return TTT_ERR_SHAPE;
+    uint64_t w0_bytes = 0;
+    if (!extent_bytes((int64_t)B * H, W0_stride_bh, 1, 0, 1, 0, (int64_t)d * dv, 4, &w0_bytes)) return TTT_ERR_SHAPE;
     if (!q || !k || !v || !W0 || !out) return TTT_ERR_NULL;
     const void* ptrs[] = {q, k, v, W0, out, W_final};
     for (const void* x : ptrs)
         if (x && !aligned16(x)) return TTT_ERR_ALIGN;
     if (!ttt::dual_supported(dtype, d, dv, minibatch)) return TTT_ERR_UNSUPPORTED;
     const size_t es = esize(dtype);
-    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + (size_t)B * H * L * dv * es;
-    const struct { const void* p; size_t n; } ins[] = {
-        {q, (size_t)B * H * L * d * es}, {k, (size_t)B * H * L * d * es}, {v, (size_t)B * H * L * dv * es}};
-    for (const auto& in : ins) {
-        const uintptr_t a0 = reinterpret_cast<uintptr_t>(in.p);
-        if (overlap(o0, o1, a0, a0 + in.n)) return TTT_ERR_ALIAS;
-    }
+    const size_t nq = (size_t)B * H * L * d * es, nv = (size_t)B * H * L * dv * es;
+    const size_t nw = (size_t)d * dv;
+    if (!disjoint_sets({rng(out, nv), rng(W_final, (size_t)B * H * nw * 4)},
+                       {rng(q, nq), rng(k, nq), rng(v, nv), block_range(W0, W0_stride_bh, 0, B * H, 1, nw, 4)}))
+        return TTT_ERR_ALIAS;
     ttt::DualParams p;
     p.q = q;
     p.k = k;
@@ -244,7 +401,7 @@ ttt_status_t ttt_bwd_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk,
                                     float beta, size_t* bytes) {
     if (!bytes) return TTT_ERR_NULL;
     if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
-    if (B < 1 || H < 1 || L < 1 || dk < 1 || dv < 1) return TTT_ERR_SHAPE;
+    if (!shape_ok(B, H, L, {dk, dv})) return TTT_ERR_SHAPE;
     if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_VALUE;
     if (!ttt::bwd_supported(dtype, dk, dv)) return TTT_ERR_UNSUPPORTED;
     *bytes = ttt::bwd_workspace(B, H, L, dk, dv, dtype, beta != 0.f);
@@ -256,7 +413,7 @@ ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_
                              float beta, const float* S0, const float* M0, const void* dout,
                              const float* dS_final, const float* dM_final, void* dq, void* dk_out, void* dv_out,
                              float* deta, float* dS0, float* dM0, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             void* stream, void* side_stream) {
     size_t need = 0;
     const ttt_status_t st = ttt_bwd_workspace_size(B, H, L, dk, dv, dtype, beta, &need);
     if (st != TTT_OK) return st;
@@ -314,7 +471,8 @@ ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_
     p.dS0 = dS0;
     p.dM0 = dM0;
     p.workspace = workspace;
-    return from_hip(ttt::launch_bwd(p, reinterpret_cast<hipStream_t>(stream)));
+    return from_hip(ttt::launch_bwd(p, reinterpret_cast<hipStream_t>(stream),
+                                    reinterpret_cast<hipStream_t>(side_stream)));
 }
 
 namespace {
@@ -333,7 +491,7 @@ constexpr int kMaxConvTaps = 16;
 
 ttt_status_t ttt_inplace_gated_input(int32_t T, int32_t d_model, int32_t d_ff, const void* X, const void* Wg,
                                      const void* Wu, void* Z, void* stream) {
-    if (T < 1 || d_model < 1 || d_ff < 1) return TTT_ERR_SHAPE;
+    if (!shape_ok(1, 1, T, {d_model, d_ff})) return TTT_ERR_SHAPE;
     if (!X || !Wg || !Wu || !Z) return TTT_ERR_NULL;
     if (!aligned16(X) || !aligned16(Wg) || !aligned16(Wu) || !aligned16(Z)) return TTT_ERR_ALIGN;
     if (!ttt::fe_gemm_supported(d_model, 2 * d_ff)) return TTT_ERR_UNSUPPORTED;
@@ -354,7 +512,7 @@ ttt_status_t ttt_inplace_gated_input(int32_t T, int32_t d_model, int32_t d_ff, c
 
 ttt_status_t ttt_inplace_lm_target_workspace_size(int32_t B, int32_t L, int32_t d_model, size_t* bytes) {
     if (!bytes) return TTT_ERR_NULL;
-    if (B < 1 || L < 1 || d_model < 1) return TTT_ERR_SHAPE;
+    if (!shape_ok(1, 1, (int64_t)B * L, {d_model}) || !within(B, kMaxLen)) return TTT_ERR_SHAPE;
     *bytes = (size_t)B * L * d_model * 2;
     return TTT_OK;
 }
@@ -362,7 +520,7 @@ ttt_status_t ttt_inplace_lm_target_workspace_size(int32_t B, int32_t L, int32_t 
 ttt_status_t ttt_inplace_lm_target(int32_t B, int32_t L, int32_t d_model, int32_t taps, const void* X,
                                    const float* conv_w, const void* Wv, void* Vhat, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-    if (B < 1 || L < 1 || d_model < 1) return TTT_ERR_SHAPE;
+    if (!shape_ok(1, 1, (int64_t)B * L, {d_model}) || !within(B, kMaxLen)) return TTT_ERR_SHAPE;
     if (taps < 1 || taps > kMaxConvTaps) return TTT_ERR_VALUE;
     if (!X || !conv_w || !Wv || !Vhat) return TTT_ERR_NULL;
     if (!aligned16(X) || !aligned16(conv_w) || !aligned16(Wv) || !aligned16(Vhat)) return TTT_ERR_ALIGN;
@@ -399,7 +557,7 @@ ttt_status_t ttt_inplace_lm_target(int32_t B, int32_t L, int32_t d_model, int32_
 
 ttt_status_t ttt_inplace_clip_eta_workspace_size(int32_t B, int32_t L, int32_t chunk, size_t* bytes) {
     if (!bytes) return TTT_ERR_NULL;
-    if (B < 1 || L < 1 || chunk < 1) return TTT_ERR_SHAPE;
+    if (!shape_ok(1, 1, (int64_t)B * L, {}) || !within(B, kMaxLen) || !within(chunk, kMaxLen)) return TTT_ERR_SHAPE;
     *bytes = (size_t)B * ((L + chunk - 1) / chunk) * ttt::fe_gram_pairs(chunk) * sizeof(float);
     return TTT_OK;
 }
@@ -410,7 +568,7 @@ ttt_status_t ttt_inplace_clip_eta(int32_t B, int32_t L, int32_t d_ff, int32_t d_
     size_t need = 0;
     ttt_status_t s = ttt_inplace_clip_eta_workspace_size(B, L, chunk, &need);
     if (s != TTT_OK) return s;
-    if (d_ff < 1 || d_model < 1) return TTT_ERR_SHAPE;
+    if (!within(d_ff, kMaxFeat) || !within(d_model, kMaxFeat)) return TTT_ERR_SHAPE;
     if (!(tau > 0.f) || !(eta == eta)) return TTT_ERR_VALUE;
     if (!Z || !Vhat || !eta_out) return TTT_ERR_NULL;
     if (!aligned16(Z) || !aligned16(Vhat) || !aligned16(eta_out)) return TTT_ERR_ALIGN;
@@ -438,7 +596,7 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
                              const void* k, const void* v, const float* eta, float eta_scalar, float beta,
                              float* S, float* M, void* out, void* stream) {
     if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
-    if (B < 1 || H < 1 || dk < 1 || dv < 1) return TTT_ERR_SHAPE;
+    if (!shape_ok(B, H, 1, {dk, dv})) return TTT_ERR_SHAPE;
     if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_VALUE;
     if (!q || !k || !v || !S || !out) return TTT_ERR_NULL;
     if (beta != 0.f && !M) return TTT_ERR_NULL;
@@ -447,20 +605,13 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
         if (x && !aligned16(x)) return TTT_ERR_ALIGN;
     if (!ttt::decode_supported(dtype, dk, dv)) return TTT_ERR_UNSUPPORTED;
     const size_t es = esize(dtype);
-    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out), o1 = o0 + (size_t)B * H * dv * es;
-    const struct { const void* p; size_t n; } ins[] = {
-        {q, (size_t)B * H * dk * es}, {k, (size_t)B * H * dk * es}, {v, (size_t)B * H * dv * es},
-        {S, (size_t)B * H * dk * dv * 4}, {beta != 0.f ? M : nullptr, (size_t)B * H * dk * dv * 4}};
-    for (const auto& in : ins) {
-        if (!in.p) continue;
-        const uintptr_t a0 = reinterpret_cast<uintptr_t>(in.p);
-        if (overlap(o0, o1, a0, a0 + in.n)) return TTT_ERR_ALIAS;
-    }
-    if (beta != 0.f) {   // S and M are both written: they must not overlap either
-        const uintptr_t s0 = reinterpret_cast<uintptr_t>(S), m0 = reinterpret_cast<uintptr_t>(M);
-        const size_t n = (size_t)B * H * dk * dv * 4;
-        if (overlap(s0, s0 + n, m0, m0 + n)) return TTT_ERR_ALIAS;
-    }
+    // out, S and M (the last two updated in place) are written: they overlap
+    // neither the read-only inputs nor each other
+    const size_t ns = (size_t)B * H * dk * dv * 4;
+    if (!disjoint_sets({rng(out, (size_t)B * H * dv * es), rng(S, ns), rng(beta != 0.f ? M : nullptr, ns)},
+                       {rng(q, (size_t)B * H * dk * es), rng(k, (size_t)B * H * dk * es),
+                        rng(v, (size_t)B * H * dv * es), rng(eta, (size_t)B * H * 4)}))
+        return TTT_ERR_ALIAS;
     ttt::DecodeParams p;
     p.q = q;
     p.k = k;
@@ -487,7 +638,7 @@ int64_t swiglu_chunk(int32_t L, int32_t chunk) { return std::min<int64_t>(chunk,
 ttt_status_t ttt_swiglu_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t m,
                                        int32_t chunk, size_t* bytes) {
     if (!bytes) return TTT_ERR_NULL;
-    if (B < 1 || H < 1 || L < 1 || dk < 1 || dv < 1 || m < 1 || chunk < 1) return TTT_ERR_SHAPE;
+    if (!shape_ok(B, H, L, {dk, dv, m}) || !within(chunk, kMaxLen)) return TTT_ERR_SHAPE;
     const int64_t C = swiglu_chunk(L, chunk);
     if (!ttt::swiglu_supported(dk, dv, m, (int)C)) return TTT_ERR_UNSUPPORTED;
     const int64_t span = std::max({(int64_t)2 * m * dk, (int64_t)dv * m, C * std::max({(int64_t)dk, (int64_t)dv,

@@ -30,17 +30,31 @@
 // of g_t are read from the adjoint of m_t,
 //     A_t = sum_{u >= t} w(u - t) q_u^T do_u + c_t dS_final + beta^{L-1-t} dM_final,
 //     w(n) = 1 + beta + ... + beta^n,  c_t = w(L - 1 - t),
-// which, in reversed time, is the state S' of the momentum forward itself run
-// on the increments q_u^T do_u from S0' = dM_final / beta and
-// M0' = (beta dS_final - (1 - beta) dM_final) / beta^2 (these match the
-// constant and the beta^{L-1-t} parts of the two boundary terms).  So dq, P = k A and
-// R = v A^T are three momentum forwards, dv = eta P, dk = eta R, deta = P . v
-// as before, and with S'_f, M'_f the P pass's final states:
-//     dS0 = (1 - beta) S'_f + beta M'_f   (the adjoint of S0: A_0 - beta A_1)
-//     dM0 = beta S'_f                     (m_0 = beta M0 + g_0).
+// which, in reversed time tau = L-1-t, is the state S' of the momentum
+// forward itself run on the increments q_u^T do_u.  Its start states decide
+// the boundary part.  The forward reaches only the shapes const and
+// beta^{tau+1} from a start state, while the boundary is
+// c_t dS_final + beta^tau dM_final = dS_final / (1 - beta) + beta^tau E,
+// E = dM_final - beta dS_final / (1 - beta).  Two ways in:
+//   beta >= kDirectBeta: S0' = dM_final / beta and
+//     M0' = (beta dS_final - (1 - beta) dM_final) / beta^2 give the whole
+//     boundary (their O(1/beta) parts cancel; above the threshold the
+//     cancellation costs at most a factor 1/beta^2 < 2 in the bf16 readout
+//     of the first reversed chunk);
+//   beta <  kDirectBeta: S0' = dS_final / (1 - beta), M0' = 0 give the
+//     constant, and the decaying beta^tau E is added exactly in fp32 to the
+//     rows of P and R of the last tokens where beta^tau is not negligible
+//     (bwd_tail_kernel; at most ~75 tokens per sequence).  No division by
+//     beta, so any beta in (0, 1) is well conditioned.
+// So dq, P = k A and R = v A^T are three momentum forwards, dv = eta P,
+// dk = eta R, deta = P . v as before, and with S'_f, M'_f the P pass's final
+// states:
+//     dS0 = (1 - beta) S'_f + beta M'_f   (the adjoint of S0: A_0 - beta A_1;
+//                                          the tail term cancels in it)
+//     dM0 = beta S'_f (+ beta^L E in the tail form)   (m_0 = beta M0 + g_0).
 // (The gradient with respect to beta itself is not computed.)
 #include "common.h"
-#include <mutex>
+#include <cmath>
 
 #include "internal.h"
 
@@ -99,25 +113,96 @@ __global__ __launch_bounds__(256) void bwd_scale_dv_kernel(BwdParams p) {
     if (p.deta && i < nvec && (i % GV) == 0) p.deta[row] = dot;
 }
 
-// S0' = dM_final / beta, M0' = (beta dS_final - (1 - beta) dM_final) / beta^2,
-// elementwise (NULL inputs are zero)
-__global__ __launch_bounds__(256) void bwd_init_kernel(const float* dSf, const float* dMf, float beta, float* S0p,
-                                                       float* M0p, int64_t n) {
+// momentum above which the reversed passes take the whole boundary from
+// their start states (below it: the tail correction)
+constexpr float kDirectBeta = 0.75f;
+
+// start states of the reversed passes, elementwise (NULL inputs are zero):
+//   direct: S0' = dM_final / beta, M0' = (beta dS_final - (1 - beta) dM_final) / beta^2
+//   tail:   S0' = dS_final / (1 - beta), M0' = 0
+__global__ __launch_bounds__(256) void bwd_init_kernel(const float* dSf, const float* dMf, float beta, int direct,
+                                                       float* S0p, float* M0p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const float a = dSf ? dSf[i] : 0.f, c = dMf ? dMf[i] : 0.f;
-    S0p[i] = c / beta;
-    M0p[i] = (beta * a - (1.f - beta) * c) / (beta * beta);
+    if (direct) {
+        S0p[i] = c / beta;
+        M0p[i] = (beta * a - (1.f - beta) * c) / (beta * beta);
+    } else {
+        S0p[i] = a / (1.f - beta);
+        M0p[i] = 0.f;
+    }
 }
 
-// dS0 = (1 - beta) S'_f + beta M'_f,  dM0 = beta S'_f
-__global__ __launch_bounds__(256) void bwd_state_kernel(const float* Sf, const float* Mf, float beta, float* dS0,
-                                                        float* dM0, int64_t n) {
+// The decaying boundary term of the momentum adjoint, added to the last
+// `tail` tokens of every sequence (tau = L-1-t < tail):
+//   which = 0:  P_t  += beta^tau k_t E          (in the dv buffer, before the epilogue)
+//   which = 1:  dk_t += eta_t beta^tau v_t E^T  (after the R pass)
+// with E = dM_final - beta / (1 - beta) dS_final (NULL inputs are zero).
+// One workgroup per (b, h): E is staged once in LDS (row stride dv + 1, so
+// the column walk of which = 1 is conflict free), then the tail tokens are
+// walked in order; thread j < n_out owns output column j of every token.
+constexpr int kTailMaxD = 128;   // dk, dv <= 128 (the backward's supported head sizes)
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_tail_kernel(BwdParams p, int tail, int which) {
+    __shared__ float E[kTailMaxD * (kTailMaxD + 1)];   // [dk][dv + 1]
+    __shared__ float x[kTailMaxD];                     // the token's k (which 0) or v (which 1)
+    const int dk = p.dk_dim, dv = p.dv_dim, ld = dv + 1;
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int64_t sbase = (int64_t)bh * dk * dv;
+    const float c = p.beta / (1.f - p.beta);
+    for (int e = tid; e < dk * dv; e += 256) {
+        const float a = p.dS_final ? p.dS_final[sbase + e] : 0.f;
+        const float m = p.dM_final ? p.dM_final[sbase + e] : 0.f;
+        E[(e / dv) * ld + (e % dv)] = m - c * a;
+    }
+    const int n_in = which == 0 ? dk : dv, n_out = which == 0 ? dv : dk;
+    const T* in = static_cast<const T*>(which == 0 ? p.k : p.v);
+    T* io = static_cast<T*>(which == 0 ? p.dv : p.dk);
+    float bt = 1.f;   // beta^tau
+    for (int tau = 0; tau < tail; ++tau, bt *= p.beta) {
+        const int64_t row = (int64_t)bh * p.L + (p.L - 1 - tau);
+        __syncthreads();   // E written / the previous token's x read
+        for (int i = tid; i < n_in; i += 256) x[i] = (float)in[row * n_in + i];
+        __syncthreads();
+        if (tid < n_out) {
+            float acc = 0.f;
+            if (which == 0) {
+                for (int i = 0; i < dk; ++i) acc += x[i] * E[i * ld + tid];
+            } else {
+                for (int j = 0; j < dv; ++j) acc += x[j] * E[tid * ld + j];
+                acc *= p.eta ? p.eta[row] : p.eta_scalar;
+            }
+            const int64_t o = row * n_out + tid;
+            io[o] = (T)((float)io[o] + bt * acc);
+        }
+    }
+}
+
+// tokens whose boundary weight beta^tau is above 2^-30 (beta in (0, 1))
+int tail_tokens(float beta, int L) {
+    int n = 1;
+    for (double w = beta; n < L && w >= 0x1p-30; w *= beta) ++n;
+    return n;
+}
+
+// dS0 = (1 - beta) S'_f + beta M'_f,  dM0 = beta S'_f + bL E, where bL =
+// beta^L in the tail form when its boundary term reaches token 0 (else 0)
+__global__ __launch_bounds__(256) void bwd_state_kernel(const float* Sf, const float* Mf, float beta, float bL,
+                                                        const float* dSf, const float* dMf, float* dS0, float* dM0,
+                                                        int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n) return;
     const float sv = Sf[i];
     if (dS0) dS0[i] = (1.f - beta) * sv + beta * Mf[i];
-    if (dM0) dM0[i] = beta * sv;
+    if (dM0) {
+        float d = beta * sv;
+        if (bL != 0.f) {
+            const float a = dSf ? dSf[i] : 0.f, m = dMf ? dMf[i] : 0.f;
+            d += bL * (m - beta / (1.f - beta) * a);
+        }
+        dM0[i] = d;
+    }
 }
 
 __global__ __launch_bounds__(256) void bwd_zero_kernel(float* out, int64_t n) {
@@ -188,25 +273,16 @@ size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype, bool moment
     return w;
 }
 
-// A helper stream per device (default priority, non-blocking), created on
-// first use: the epilogue runs on it beside the R pass.
-hipError_t side_stream(hipStream_t* out) {
-    static std::mutex mu;
-    static hipStream_t streams[64] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!streams[dev]) {
-        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
-        if (e != hipSuccess) return e;
-    }
-    *out = streams[dev];
-    return hipSuccess;
+hipError_t launch_tail(const BwdParams& b, int tail, int which, hipStream_t s) {
+    if (b.dk_dim > kTailMaxD || b.dv_dim > kTailMaxD) return hipErrorInvalidValue;
+    if (b.dtype == 1)
+        hipLaunchKernelGGL((bwd_tail_kernel<bf16_t>), dim3(b.B * b.H), dim3(256), 0, s, b, tail, which);
+    else
+        hipLaunchKernelGGL((bwd_tail_kernel<float>), dim3(b.B * b.H), dim3(256), 0, s, b, tail, which);
+    return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
+hipError_t launch_bwd(const BwdParams& b, hipStream_t s, hipStream_t s2) {
     if (!bwd_supported(b.dtype, b.dk_dim, b.dv_dim)) return hipErrorInvalidValue;
     const size_t es = b.dtype == 1 ? 2 : 4;
     const int H = b.H, L = b.L, dk = b.dk_dim, dv = b.dv_dim;
@@ -215,6 +291,9 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
     const int64_t nst = (int64_t)b.B * H * dk * dv;
     const dim3 sgrid((unsigned)((nst + 255) / 256)), sblock(256);
     float *S0p = nullptr, *M0p = nullptr, *Sfp = nullptr, *Mfp = nullptr;
+    // tail form: tokens that get the decaying boundary term (0: none)
+    const bool direct = b.beta >= kDirectBeta;
+    const int tail = (mom && !direct && (b.dS_final || b.dM_final)) ? tail_tokens(b.beta, L) : 0;
     if (mom) {
         char* w = static_cast<char*>(b.workspace) + fwd_ws(b.B, H, L, dk, dv, b.dtype, mode);
         const size_t sb = align256((size_t)nst * sizeof(float));
@@ -222,7 +301,8 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         M0p = reinterpret_cast<float*>(w + sb);
         Sfp = reinterpret_cast<float*>(w + 2 * sb);
         Mfp = reinterpret_cast<float*>(w + 3 * sb);
-        hipLaunchKernelGGL(bwd_init_kernel, sgrid, sblock, 0, s, b.dS_final, b.dM_final, b.beta, S0p, M0p, nst);
+        hipLaunchKernelGGL(bwd_init_kernel, sgrid, sblock, 0, s, b.dS_final, b.dM_final, b.beta, direct ? 1 : 0,
+                           S0p, M0p, nst);
     }
     hipError_t e;
 
@@ -274,10 +354,12 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         p.M_final = Mfp;
         if ((e = launch_tc_fwd(p, b.dtype, mode, s)) != hipSuccess) return e;
     }
-    // dv = eta P, deta = P . v: needs only P, so it runs on a helper stream
-    // beside the R pass (which writes only dk), and the caller's stream
-    // waits for it before the call's last kernel.  The R pass is bound by
-    // latency and leaves wave slots free on every CU.
+    if (tail > 0 && (e = launch_tail(b, tail, 0, s)) != hipSuccess) return e;
+    // dv = eta P, deta = P . v: needs only P.  With a caller's helper stream
+    // it runs there beside the R pass (which writes only dk), forked from
+    // `s` by an event and joined back before the call's last kernel: the R
+    // pass is bound by latency and leaves wave slots free on every CU.
+    // Without one it runs on `s` before the R pass.
     struct Events {   // destroyed on every return; the runtime defers it until they complete
         hipEvent_t p = nullptr, epi = nullptr;
         ~Events() {
@@ -285,15 +367,29 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
             if (epi) (void)hipEventDestroy(epi);
         }
     } ev;
-    hipStream_t s2 = nullptr;
-    if ((e = side_stream(&s2)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&ev.p, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventCreateWithFlags(&ev.epi, hipEventDisableTiming)) != hipSuccess ||
-        (e = hipEventRecord(ev.p, s)) != hipSuccess || (e = hipStreamWaitEvent(s2, ev.p, 0)) != hipSuccess)
+    const bool fork = s2 != nullptr && s2 != s;
+    if (fork) {
+        if ((e = hipEventCreateWithFlags(&ev.p, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventCreateWithFlags(&ev.epi, hipEventDisableTiming)) != hipSuccess ||
+            (e = hipEventRecord(ev.p, s)) != hipSuccess || (e = hipStreamWaitEvent(s2, ev.p, 0)) != hipSuccess)
+            return e;   // nothing is enqueued on s2 before its wait succeeded
+        // from here on s2 has forked off s: every return joins it back first
+        if ((e = b.dtype == 1 ? launch_epilogue<bf16_t>(b, s2) : launch_epilogue<float>(b, s2)) != hipSuccess) {
+            if (hipEventRecord(ev.epi, s2) == hipSuccess) (void)hipStreamWaitEvent(s, ev.epi, 0);
+            return e;
+        }
+        if ((e = hipEventRecord(ev.epi, s2)) != hipSuccess) return e;
+    } else if ((e = b.dtype == 1 ? launch_epilogue<bf16_t>(b, s) : launch_epilogue<float>(b, s)) != hipSuccess) {
         return e;
-    if ((e = b.dtype == 1 ? launch_epilogue<bf16_t>(b, s2) : launch_epilogue<float>(b, s2)) != hipSuccess ||
-        (e = hipEventRecord(ev.epi, s2)) != hipSuccess)
-        return e;
+    }
+    // the join of the fork (if any), also on the error paths below
+    auto join = [&](hipError_t err) {
+        if (fork) {
+            const hipError_t j = hipStreamWaitEvent(s, ev.epi, 0);
+            if (err == hipSuccess) err = j;
+        }
+        return err;
+    };
     // R (into dk): queries v, keys do, values q, time reversed, state dS_final^T
     {
         TcParams p = pass_params(b);
@@ -320,15 +416,17 @@ hipError_t launch_bwd(const BwdParams& b, hipStream_t s) {
         p.ocs[1] = L;
         p.ocs[2] = -1;
         p.oscale_scalar = b.eta_scalar;
-        if ((e = launch_tc_fwd(p, b.dtype, mode, s)) != hipSuccess) return e;
+        if ((e = launch_tc_fwd(p, b.dtype, mode, s)) != hipSuccess) return join(e);
     }
+    if (tail > 0 && (e = launch_tail(b, tail, 1, s)) != hipSuccess) return join(e);
+    // beta^L E reaches dM0 when the tail covers token 0
+    const float bL = (tail > 0 && tail >= L) ? (float)std::pow((double)b.beta, (double)L) : 0.f;
     if (mom && (b.dS0 || b.dM0))
-        hipLaunchKernelGGL(bwd_state_kernel, sgrid, sblock, 0, s, Sfp, Mfp, b.beta, b.dS0, b.dM0, nst);
+        hipLaunchKernelGGL(bwd_state_kernel, sgrid, sblock, 0, s, Sfp, Mfp, b.beta, bL, b.dS_final, b.dM_final,
+                           b.dS0, b.dM0, nst);
     else if (b.dM0)   // no momentum: m_0 does not depend on M0
         hipLaunchKernelGGL(bwd_zero_kernel, sgrid, sblock, 0, s, b.dM0, nst);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // join: the caller's stream waits for the epilogue
-    return hipStreamWaitEvent(s, ev.epi, 0);
+    return join(hipGetLastError());
 }
 
 }  // namespace ttt

@@ -37,6 +37,10 @@ struct TcParams {
     int* lb_flags;
     float* lb_data;
     int64_t lb_stride;
+    // a look-back wait gives up after lb_max_polls polls (0 on input: the
+    // default bound; negative: give up at once) and then raises *lb_error
+    int lb_max_polls;
+    int* lb_error;
     void* workspace;
     // S0 (and M0) stored transposed: element (i, j) of a head's [dk, dv]
     // state at j * dk + i (the backward pass reads a state this way)
@@ -59,6 +63,9 @@ hipError_t launch_tcb_fwd(const TcParams& p, int mode, hipStream_t stream);
 // workspace of the bf16 kernel (look-back flags and states when the sequence
 // is segmented; 0 otherwise)
 size_t tcb_workspace(int B, int H, int L, int dk, int dv, int mode, int chunk);
+// index (in ints from the workspace start) of the look-back error word, or
+// -1 when the call is not segmented
+int64_t tcb_error_word(int B, int H, int L, int dv, int mode, int chunk);
 
 // Chunk-causal forward for large fast weights (dk, dv multiples of 256, bf16):
 // update walk with bf16 W snapshots in `workspace`, then a batched readout.
@@ -160,7 +167,9 @@ hipError_t launch_fe_clip(const FeGramParams& p, hipStream_t stream);
 
 bool bwd_supported(int dtype, int dk, int dv);
 size_t bwd_workspace(int B, int H, int L, int dk, int dv, int dtype, bool momentum);
-hipError_t launch_bwd(const BwdParams& p, hipStream_t stream);
+// side: a second stream of the caller for the dv/deta step beside the R pass
+// (NULL or equal to `stream`: everything runs on `stream`)
+hipError_t launch_bwd(const BwdParams& p, hipStream_t stream, hipStream_t side);
 bool decode_supported(int dtype, int dk, int dv);
 
 // Large-chunk SwiGLU fast weight (bf16 activations, fp32 master weights).

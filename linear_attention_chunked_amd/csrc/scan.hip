@@ -18,6 +18,8 @@
 #include "common.h"
 #include "internal.h"
 
+#include <cmath>
+
 namespace ttt {
 
 __global__ __launch_bounds__(256) void state_scan_kernel(
@@ -58,14 +60,12 @@ __global__ __launch_bounds__(256) void state_scan_kernel(
     if (use_m && M_final) M_final[e] = M;
 }
 
+// alpha_n = beta + ... + beta^n = beta (1 - beta^n) / (1 - beta), gamma_n = beta^n
+// (closed forms in fp64; beta in [0, 1))
 static void affine_coeffs(double beta, int n, float* alpha, float* gamma) {
-    double p = 1.0, a = 0.0;
-    for (int i = 1; i <= n; ++i) {
-        p *= beta;
-        a += p;
-    }
-    *alpha = (float)a;
-    *gamma = (float)p;
+    const double bn = std::pow(beta, (double)n);
+    *alpha = (float)(beta * (1.0 - bn) / (1.0 - beta));
+    *gamma = (float)bn;
 }
 
 hipError_t launch_state_scan(int B, int H, int L, int chunk, int dk, int dv,

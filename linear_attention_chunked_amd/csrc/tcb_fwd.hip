@@ -374,18 +374,23 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     };
 
     if (segmented) {
-        // ================= decoupled look-back over sequence segments =================
+        // ================= look-back over sequence segments =================
         // A segment of n tokens maps the state (S, m) it starts from to
         //     (S + a_n m + X, beta^n m + Y),  a_n = beta + ... + beta^n,
         // where (X, Y) is the segment's own result from a zero start (its
         // aggregate).  Segment s publishes its aggregate, then walks back over
-        // segments s-1, s-2, ...: an inclusive state (published by a segment
-        // that has finished its look-back) ends the walk, an aggregate is
-        // composed into the running map T and the walk continues; past
-        // segment 0 the map is applied to (S0, M0).  Exchange blocks use the
-        // accumulator layout itself (lane-private f32x4 slots), so publishing
-        // and reading are coalesced 16-byte accesses with no reshuffle.
+        // segments s-1, s-2, ..., composing their aggregates into the running
+        // map T.  The walk has a fixed shape, so results never depend on
+        // timing: it ends at the inclusive state of segment s - kChain (the
+        // state after that segment, which it publishes once its own walk is
+        // done), or past segment 0, where T is applied to (S0, M0).  So a
+        // segment reads at most kChain - 1 aggregates and one inclusive
+        // state, and inclusive states form a chain of nseg / kChain links.
+        // Exchange blocks use the accumulator layout itself (lane-private
+        // f32x4 slots), so publishing and reading are coalesced 16-byte
+        // accesses with no reshuffle.
         constexpr int NSTATE = MOM ? 2 : 1;
+        constexpr int kChain = 8;   // segments per link of the inclusive-state chain
         const int my_id = seg * nbv + bh * p.n_vt + vt;
         auto slot = [&](int id, int which, int st, int t) -> f32x4* {
             return reinterpret_cast<f32x4*>(p.lb_data + ((int64_t)id * 2 + which) * p.lb_stride) +
@@ -405,26 +410,24 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             __syncthreads();
             if (tid == 0) __hip_atomic_store(p.lb_flags + my_id, which + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         };
-        __shared__ int sFlag;
         // Waiting: one thread polls the flag with agent-scope acquire loads (the
         // acquire invalidates this CU's L1 and the stale lines of the XCD's L2,
-        // which the other waves' loads go through after the barrier).  The wait
-        // is bounded: a flag that never arrives ends it (results are then
-        // wrong, but every wave still finishes).
-        auto wait_flag = [&](int id) -> int {
+        // which the other waves' loads go through after the barrier) until it
+        // reaches `want` (1: aggregate published, 2: inclusive state too).
+        // The wait is bounded by p.lb_max_polls: a flag that never arrives
+        // ends it, the error word in the workspace is raised (the host reads
+        // it back) and every wave still finishes, with wrong results.
+        auto wait_flag = [&](int id, int want) {
             if (tid == 0) {
                 int v = 0;
-                for (int spin = 0; spin < (1 << 22); ++spin) {
+                for (int spin = 0; spin < p.lb_max_polls; ++spin) {
                     v = __hip_atomic_load(p.lb_flags + id, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-                    if (v != 0) break;
+                    if (v >= want) break;
                     __builtin_amdgcn_s_sleep(2);
                 }
-                sFlag = v;
+                if (v < want) __hip_atomic_store(p.lb_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();
-            const int v = sFlag;
-            __syncthreads();   // sFlag is reused by the next wait
-            return v;
         };
         const int seg_len = p.seg_tiles * CS;           // every segment but the last is full
         float a_seg = 0.f, g_seg = 1.f;
@@ -510,7 +513,9 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         bool have_base = false;
         for (int j = seg - 1; j >= 0 && !have_base; --j) {
             const int id = j * nbv + bh * p.n_vt + vt;
-            if (wait_flag(id) == 2) {
+            const bool base = (seg - j == kChain);
+            wait_flag(id, base ? 2 : 1);
+            if (base) {
                 // inclusive state after segment j: the base of the walk
 #pragma unroll
                 for (int t = 0; t < NTH; ++t) {
@@ -556,7 +561,8 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             }
         }
         // XT, YT = state at the segment start; publish the state at its end
-        if (!last) {
+        // (read only by segment seg + kChain)
+        if (seg + kChain < p.nseg) {
 #pragma unroll
             for (int t = 0; t < NTH; ++t) {
                 if (MOM) {
@@ -892,6 +898,9 @@ struct TcbPlan {
 };
 constexpr int kCUs = 256;
 constexpr int kMinSegTokens = 1024;
+// polls of a look-back wait before it gives up (each poll sleeps ~0.1 us):
+// far beyond any real wait, which is bounded by one segment's first pass
+constexpr int kDefaultPolls = 1 << 22;
 
 TcbPlan tcb_plan(int B, int H, int L, int dv, int mode, int chunk) {
     TcbPlan pl{};
@@ -928,7 +937,8 @@ TcbPlan tcb_plan(int B, int H, int L, int dv, int mode, int chunk) {
 // floats per workgroup state block (S, and m with momentum)
 int64_t lb_block(int dk, int dvt, int mode) { return (int64_t)dk * dvt * (mode == MODE_MOM ? 2 : 1); }
 
-size_t lb_flag_bytes(int64_t nwg) { return (size_t)(((nwg + 1) * 4 + 255) / 256 * 256); }
+// flags (one per workgroup), the ticket counter and the error word
+size_t lb_flag_bytes(int64_t nwg) { return (size_t)(((nwg + 2) * 4 + 255) / 256 * 256); }
 
 __global__ void lb_clear_kernel(int* flags, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -936,6 +946,12 @@ __global__ void lb_clear_kernel(int* flags, int n) {
 }
 
 }  // namespace
+
+int64_t tcb_error_word(int B, int H, int L, int dv, int mode, int chunk) {
+    const TcbPlan pl = tcb_plan(B, H, L, dv, mode, chunk);
+    if (pl.nseg <= 1) return -1;
+    return (int64_t)B * H * pl.n_vt * pl.nseg + 1;
+}
 
 size_t tcb_workspace(int B, int H, int L, int dk, int dv, int mode, int chunk) {
     const TcbPlan pl = tcb_plan(B, H, L, dv, mode, chunk);
@@ -957,9 +973,13 @@ hipError_t launch_tcb_fwd(const TcParams& pin, int mode, hipStream_t s) {
         p.lb_flags = reinterpret_cast<int*>(p.workspace);
         p.lb_data = reinterpret_cast<float*>(reinterpret_cast<char*>(p.workspace) + lb_flag_bytes(nwg));
         p.lb_stride = lb_block(p.dk, pl.dvt, mode);
-        // flags and the ticket counter start at zero (a fill kernel, not a
-        // memset node, so the call stays valid inside a captured graph)
-        const int nflags = (int)nwg + 1;
+        p.lb_error = p.lb_flags + nwg + 1;
+        if (p.lb_max_polls == 0) p.lb_max_polls = kDefaultPolls;
+        else if (p.lb_max_polls < 0) p.lb_max_polls = 0;
+        // flags, the ticket counter and the error word start at zero (a fill
+        // kernel, not a memset node, so the call stays valid inside a
+        // captured graph)
+        const int nflags = (int)nwg + 2;
         hipLaunchKernelGGL(lb_clear_kernel, dim3((nflags + 255) / 256), dim3(256), 0, s, p.lb_flags, nflags);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "ttt.h")
 
 import linear_attention_chunked_amd as lac  # noqa: E402
 
-OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_ALIAS, ERR_VALUE = range(10)
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_UNSUP, ERR_WS, ERR_HIP, ERR_ALIAS, ERR_VALUE, ERR_TIMEOUT = range(11)
 
 
 @pytest.fixture(scope="module")
@@ -42,7 +42,7 @@ def test_struct_layout(lib):
 
 
 def test_status_strings(lib):
-    for s in range(10):
+    for s in range(11):
         assert len(lib.ttt_status_string(s)) > 0
     assert lib.ttt_status_string(123) == b"unknown status"
 
@@ -101,6 +101,83 @@ def test_fwd_rejects_before_launch(lib):
     a = fwd_args()
     a.out = a.q
     assert status(lib, a) == ERR_ALIAS
+
+
+def test_fwd_rejects_overlapping_written_buffers(lib):
+    """Every written buffer (out, S_final, M_final, the workspace) must miss
+    every input and every other written buffer, and out must not overlap
+    itself through its strides; inputs may share memory."""
+    far = FAKE + (1 << 28)
+    st = 2 * 2 * 64 * 64 * 4                       # bytes of one [2,2,64,64] fp32 state
+    a = fwd_args()
+    a.S0 = a.out                                   # out over S0
+    assert status(lib, a) == ERR_ALIAS
+    a = fwd_args()
+    a.S_final = a.q                                # S_final over q
+    assert status(lib, a) == ERR_ALIAS
+    a = fwd_args()
+    a.S0, a.S0_stride = far + 64 * 64 * 4 * 3, lac._i64x2(0, 0)   # one S0 for all heads ...
+    a.S_final = far                                # ... lying inside S_final's head 3
+    assert status(lib, a) == ERR_ALIAS
+    a = fwd_args(beta=0.5)
+    a.S_final, a.M_final = far, far + st - 256     # M_final overlaps S_final
+    assert status(lib, a) == ERR_ALIAS
+    a = fwd_args()
+    a.eta, a.eta_stride = a.out + 64, lac._i64x3(2 * 128, 128, 1)   # eta inside out
+    assert status(lib, a) == ERR_ALIAS
+    a = fwd_args()
+    a.S_final = a.out + 1024                       # S_final inside out
+    assert status(lib, a) == ERR_ALIAS
+    # out's strides map two heads onto the same rows
+    assert status(lib, fwd_args(out_stride=(2 * 128 * 64, 0, 64))) == ERR_ALIAS
+    assert status(lib, fwd_args(out_stride=(0, 128 * 64, 64))) == ERR_ALIAS
+    assert status(lib, fwd_args(out_stride=(2 * 128 * 64, 64 * 64, 64))) == ERR_ALIAS   # heads interleave rows
+    # a workspace (segmented look-back) over q
+    a = fwd_args(B=1, H=1, L=4096, dk=128, dv=128)
+    need = ctypes.c_size_t(0)
+    assert lib.ttt_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)) == OK and need.value > 0
+    a.workspace, a.workspace_bytes = a.q, need.value
+    assert status(lib, a) == ERR_ALIAS
+
+
+def test_scan_dual_decode_reject_overlaps(lib):
+    f = lib.ttt_chunk_state_scan
+    blk = 8 * 8 * 4
+    base = lambda **kw: [1, 1, 64, 16, 8, 8, kw.get("dS", FAKE), kw.get("dM", FAKE + 65536), 0.5,
+                         kw.get("S0", FAKE + 4 * 65536), None, kw.get("Se", FAKE + 2 * 65536), None,
+                         kw.get("Sf", FAKE + 3 * 65536), None, None, 0, None]
+    assert f(*base(Se=FAKE)) == ERR_ALIAS                       # in-place scan
+    assert f(*base(Sf=FAKE + 4 * 65536 + blk // 2)) == ERR_ALIAS  # S_final over S0
+    assert f(*base(Sf=FAKE + 2 * 65536 + blk)) == ERR_ALIAS     # S_final inside S_excl
+    d = lib.ttt_dual_form_fwd
+    n = 4 * 64 * 64 * 2
+
+    def dargs(**kw):
+        return [1, 1, 64, 64, 64, 16, 1, FAKE, FAKE + n, FAKE + 2 * n, kw.get("W0", FAKE + 3 * n), 0, 0.01,
+                kw.get("out", FAKE + 4 * n), kw.get("Wf", None), None, 0, None]
+    assert d(*dargs(Wf=FAKE + 3 * n)) == ERR_ALIAS               # W_final on W0 (broadcast)
+    assert d(*dargs(out=FAKE + 3 * n)) == ERR_ALIAS              # out on W0
+    assert d(*dargs(Wf=FAKE + 4 * n + 64)) == ERR_ALIAS          # W_final inside out
+    dec = lib.ttt_decode_step
+    m = 1 << 20
+
+    def cargs(**kw):
+        return [2, 2, 64, 64, 1, FAKE, FAKE + m, FAKE + 2 * m, kw.get("eta", None), 0.1, 0.5,
+                kw.get("S", FAKE + 3 * m), FAKE + 4 * m, kw.get("out", FAKE + 5 * m), None]
+    assert dec(*cargs(S=FAKE + 256)) == ERR_ALIAS                # S (written) over q
+    assert dec(*cargs(eta=FAKE + 5 * m)) == ERR_ALIAS            # eta under out
+
+
+def test_lookback_status_without_segments(lib):
+    """A call that is not segmented never waits: its status query answers 0
+    without touching the device; a segmented call without a workspace is
+    rejected before any device access."""
+    flag = ctypes.c_int32(7)
+    a = fwd_args()                                    # B2 H2 L128: one segment per head
+    assert lib.ttt_fwd_lookback_status(ctypes.byref(a), ctypes.byref(flag)) == OK and flag.value == 0
+    assert lib.ttt_fwd_lookback_status(ctypes.byref(a), None) == ERR_NULL
+    a = fwd_args(B=1, H=1, L=4096, dk=128, dv=128)   # segmented
+    assert lib.ttt_fwd_lookback_status(ctypes.byref(a), ctypes.byref(flag)) == ERR_WS
 
 
 def test_workspace_query(lib):
@@ -170,7 +247,7 @@ def test_bwd_rejects_before_launch(lib):
         base = [FAKE + i * (n + 4096) for i in range(12)]
         return [2, 2, 64, kw.get("dk", 64), 64, kw.get("dtype", 1),
                 kw.get("q", base[0]), base[1], base[2], None, 0.1, kw.get("beta", 0.0), None, None, base[3],
-                None, None, kw.get("dq", base[4]), base[5], base[6], None, None, None, None, 0, None]
+                None, None, kw.get("dq", base[4]), base[5], base[6], None, None, None, None, 0, None, None]
     assert f(*args(dtype=4)) == ERR_DTYPE
     assert f(*args(beta=1.0)) == ERR_VALUE
     assert f(*args(dk=48)) == ERR_UNSUP

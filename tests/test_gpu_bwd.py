@@ -110,6 +110,27 @@ def test_bwd_momentum(dtype, beta):
           momentum=True)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("beta", [0.7, 0.1, 0.01, 1e-3, 1e-30])
+@pytest.mark.parametrize("with_dmf", [False, True])
+@pytest.mark.parametrize("L", [40, 230])
+def test_bwd_momentum_small_beta(dtype, beta, with_dmf, L):
+    """Small momenta, with and without dM_final (large against the other
+    cotangents, so its boundary term dominates the last tokens): the
+    boundary is taken without dividing by beta, so the error stays at the
+    bf16 (fp32) level for every beta.  L = 40 is shorter than the tail
+    correction at beta = 0.7 (it reaches token 0 and dM0)."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    beta = W.f32(beta)
+    q, k, v, dout, eta, S0, dSf = make(1, 2, L, 64, 128, tdt, seed=L + 3)
+    g = torch.Generator().manual_seed(19)
+    M0 = 0.01 * torch.randn(S0.shape, generator=g)
+    dMf = torch.randn(S0.shape, generator=g) if with_dmf else None
+    check(run_gpu(q, k, v, dout, eta, 0.0, S0, dSf, beta, M0, dMf),
+          run_oracle(q, k, v, dout, eta, 0.0, S0, dSf, beta, M0, dMf), dtype,
+          f"bwd momentum {dtype} L{L} beta {beta:g} dM_final {with_dmf}", momentum=True)
+
+
 def test_bwd_momentum_segmented():
     """Momentum on a long sequence of few heads (segmented forward passes
     with the affine look-back, in reverse time)."""

@@ -1,8 +1,8 @@
 """The entry points inside captured HIP graphs.
 
 The segmented token-causal forward clears its look-back flags with a fill
-kernel (not a memset node), and the backward forks its dv/deta step onto a
-helper stream and joins it back through events.  Both must capture into a
+kernel (not a memset node), and the backward can fork its dv/deta step onto
+a caller's second stream and join it back through events.  Both must capture into a
 graph and replay correctly: each test replays the graph several times, with
 the inputs changed in place and eager work (an eager call on the same inputs)
 in between, and checks every replay against that eager result.
@@ -66,9 +66,12 @@ def test_segmented_forward_in_graph():
         assert eo <= 1e-3 and es <= 1e-5, (rep, eo, es)
 
 
-def test_backward_in_graph():
-    """B1 H2 L512 d64 bf16 backward (not segmented: results are reproducible)."""
+@pytest.mark.parametrize("side", [False, True])
+def test_backward_in_graph(side):
+    """B1 H2 L512 d64 bf16 backward (not segmented: results are reproducible),
+    on one stream and with the dv/deta step forked onto a second stream."""
     B, H, L, d = 1, 2, 512, 64
+    side_stream = torch.cuda.Stream() if side else None
     q, k, v = rand((B, H, L, d), 11), rand((B, H, L, d), 12, 1 / d ** 0.5), rand((B, H, L, d), 13)
     dout = rand((B, H, L, d), 14, 1 / L ** 0.5)
     eta = torch.sigmoid(rand((B, H, L), 15, dtype=torch.float32)) * 0.1
@@ -76,9 +79,9 @@ def test_backward_in_graph():
     dSf = rand((B, H, d, d), 17, 0.02, torch.float32)
 
     def call():
-        return lac.bwd_chunked(q, k, v, dout, eta=eta, S0=S0, dS_final=dSf)
+        return lac.bwd_chunked(q, k, v, dout, eta=eta, S0=S0, dS_final=dSf, side_stream=side_stream)
 
-    say("graph: backward, warm-up and capture")
+    say(f"graph: backward (helper stream: {side}), warm-up and capture")
     call()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
