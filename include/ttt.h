@@ -52,8 +52,9 @@
  *    entry point says so (ttt_decode_step's S and M).
  *  - Errors never abort and never throw across the ABI; launch failures are
  *    reported as TTT_ERR_HIP.  Calls on different streams with different
- *    workspaces may run concurrently; the library holds no global or static
- *    state and creates no streams of its own.
+ *    workspaces may run concurrently; the library creates no streams of its
+ *    own and holds no global or static state, except the scratch array of
+ *    ttt_fwd_chunked_noalloc and its device address per GPU.
  */
 #ifndef TTT_MI355X_H
 #define TTT_MI355X_H
@@ -163,6 +164,27 @@ ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* args);
 /* Bytes of workspace ttt_fwd_chunked needs for these arguments (pointers
  * need not be set).  0 is a valid answer (workspace may then be NULL). */
 ttt_status_t ttt_fwd_workspace_size(const ttt_fwd_args* args, size_t* bytes);
+
+/*
+ * ttt_fwd_chunked_noalloc -- ttt_fwd_chunked for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and kernels, with
+ * the look-back scratch of segmented calls in a static device array of
+ * TTT_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The caller still passes every input and output;
+ * args->workspace and args->workspace_bytes are ignored.
+ * Calls whose scratch need (ttt_fwd_workspace_size) exceeds the array
+ * return TTT_ERR_WORKSPACE before anything is enqueued: every token-causal
+ * and small-head chunk-causal call fits (their look-back needs < 64 MiB);
+ * the large-fast-weight chunk-causal (In-Place) path fits only while its
+ * bf16 weight snapshots do (not at the 9728 x 2560 In-Place sizes).  All calls on one GPU share its array:
+ * calls that overlap in time on one GPU (other streams, other threads) race
+ * on it and must be serialised by the caller.  The first call on a device
+ * looks up the array's device address (hipGetSymbolAddress); nothing is ever
+ * allocated or freed.  Other errors as ttt_fwd_chunked.
+ */
+#define TTT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ttt_status_t ttt_fwd_chunked_noalloc(const ttt_fwd_args* args);
 
 /*
  * ttt_fwd_lookback_status -- whether the last ttt_fwd_chunked call with

@@ -76,6 +76,8 @@ def load_library():
     lib.ttt_fwd_chunked.argtypes = [ctypes.POINTER(FwdArgs)]
     lib.ttt_fwd_chunked.restype = ctypes.c_int
     lib.ttt_fwd_workspace_size.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_size_t)]
+    lib.ttt_fwd_chunked_noalloc.argtypes = [ctypes.POINTER(FwdArgs)]
+    lib.ttt_fwd_chunked_noalloc.restype = ctypes.c_int
     lib.ttt_fwd_lookback_status.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(ctypes.c_int32)]
     lib.ttt_fwd_lookback_status.restype = ctypes.c_int
     lib.ttt_fwd_workspace_size.restype = ctypes.c_int
@@ -170,7 +172,7 @@ def _state_strides(t: torch.Tensor | None, name: str):
 
 def fwd_chunked(q, k, v, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None, chunk=64,
                 mode="token_causal", out=None, return_state=False, stream=None, check_lookback=False,
-                lookback_polls=0):
+                lookback_polls=0, no_alloc=False):
     """Chunked fast-weight forward (``ttt_fwd_chunked``).
 
     q, k: [B,H,L,dk]; v: [B,H,L,dv] (fp32 or bf16, same dtype; q may be k);
@@ -180,7 +182,10 @@ def fwd_chunked(q, k, v, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None
     return_state (M_final is None unless beta != 0).  check_lookback: wait
     for the call and raise TTTError (TTT_ERR_TIMEOUT) if a look-back wait of
     a segmented call gave up (``ttt_fwd_lookback_status``); lookback_polls:
-    the bound of those waits (0: the library default)."""
+    the bound of those waits (0: the library default).  no_alloc: call
+    ``ttt_fwd_chunked_noalloc`` (no workspace is allocated here; the
+    library's static scratch is used, and check_lookback is not available;
+    out and the final states must still be given or are allocated as usual)."""
     lib = load_library()
     _require_gpu(q, k, v, eta, S0, M0, out)
     B, H, L, dk = q.shape
@@ -211,14 +216,19 @@ def fwd_chunked(q, k, v, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M0=None
         if beta != 0.0:
             M_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
     a.S_final, a.M_final = _ptr(S_final), _ptr(M_final)
+    a.stream = _stream(stream)
+    a.lookback_polls = int(lookback_polls)
+    if no_alloc:
+        if check_lookback:
+            raise ValueError("check_lookback needs a caller workspace (not available with no_alloc)")
+        _check(lib.ttt_fwd_chunked_noalloc(ctypes.byref(a)))
+        return (out, S_final, M_final) if return_state else out
     ws = ctypes.c_size_t(0)
     _check(lib.ttt_fwd_workspace_size(ctypes.byref(a), ctypes.byref(ws)))
     work = None
     if ws.value:
         work = torch.empty(ws.value, dtype=torch.uint8, device=q.device)
     a.workspace, a.workspace_bytes = _ptr(work), ws.value
-    a.stream = _stream(stream)
-    a.lookback_polls = int(lookback_polls)
     _check(lib.ttt_fwd_chunked(ctypes.byref(a)))
     if check_lookback:
         gave_up = ctypes.c_int32(0)

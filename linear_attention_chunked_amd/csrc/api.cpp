@@ -233,6 +233,9 @@ ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
 
 ttt_status_t from_hip(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
 
+// launch a validated forward call
+ttt_status_t fwd_impl(const ttt_fwd_args* a, int mode);
+
 }  // namespace
 
 extern "C" {
@@ -269,6 +272,39 @@ ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* a) {
     int mode = 0;
     ttt_status_t s = validate_fwd(a, &mode);
     if (s != TTT_OK) return s;
+    return fwd_impl(a, mode);
+}
+
+ttt_status_t ttt_fwd_chunked_noalloc(const ttt_fwd_args* a) {
+    int mode = 0;
+    ttt_status_t s = validate_shapes(a, &mode);
+    if (s != TTT_OK) return s;
+    const size_t need = workspace_bytes_for(a, mode);
+    if (need > ttt::kNoAllocScratchBytes) return TTT_ERR_WORKSPACE;
+    // the caller's workspace fields are ignored: the static scratch takes their place
+    ttt_fwd_args b = *a;
+    b.workspace = nullptr;
+    b.workspace_bytes = 0;
+    if (need > 0) {
+        // a stand-in address for validation (the real one is looked up only
+        // after every argument check has passed): the scratch is disjoint
+        // from every caller buffer, which validate_fwd checks against it
+        b.workspace = reinterpret_cast<void*>(uintptr_t(1) << 62);
+        b.workspace_bytes = need;
+    }
+    if ((s = validate_fwd(&b, &mode)) != TTT_OK) return s;
+    if (need > 0) {
+        void* ptr = nullptr;
+        if (ttt::noalloc_scratch(&ptr) != hipSuccess) return TTT_ERR_HIP;
+        b.workspace = ptr;
+    }
+    return fwd_impl(&b, mode);
+}
+
+}  // extern "C"
+
+namespace {
+ttt_status_t fwd_impl(const ttt_fwd_args* a, int mode) {
     ttt::TcParams p{};
     std::memset(&p, 0, sizeof(p));
     p.q = a->q;
@@ -305,6 +341,9 @@ ttt_status_t ttt_fwd_chunked(const ttt_fwd_args* a) {
     if (use_inplace(a, mode)) return from_hip(ttt::launch_inplace(p, a->workspace, st));
     return from_hip(ttt::launch_tc_fwd(p, a->dtype, mode, st));
 }
+}  // namespace
+
+extern "C" {
 
 ttt_status_t ttt_fwd_lookback_status(const ttt_fwd_args* a, int32_t* gave_up) {
     if (!a || !gave_up) return TTT_ERR_NULL;

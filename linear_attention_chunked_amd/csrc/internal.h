@@ -67,6 +67,12 @@ size_t tcb_workspace(int B, int H, int L, int dk, int dv, int mode, int chunk);
 // -1 when the call is not segmented
 int64_t tcb_error_word(int B, int H, int L, int dv, int mode, int chunk);
 
+// Allocation-free forward: the look-back scratch in a static device array of
+// kNoAllocScratchBytes per GPU; noalloc_scratch gives its device address on
+// the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // Chunk-causal forward for large fast weights (dk, dv multiples of 256, bf16):
 // update walk with bf16 W snapshots in `workspace`, then a batched readout.
 bool inplace_supported(int dtype, int dk, int dv, int chunk);

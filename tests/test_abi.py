@@ -180,6 +180,27 @@ def test_lookback_status_without_segments(lib):
     assert lib.ttt_fwd_lookback_status(ctypes.byref(a), ctypes.byref(flag)) == ERR_WS
 
 
+def test_noalloc_rejects_oversized_scratch(lib):
+    """ttt_fwd_chunked_noalloc: a call whose scratch need exceeds the static
+    array (the In-Place fast weight, 9728 x 2560, 32 chunks of snapshots) is
+    rejected before any device access; its validation errors are those of
+    ttt_fwd_chunked."""
+    a = fwd_args(B=1, H=1, L=32768, dk=9728, dv=2560, chunk=1024, mode=1)
+    a.k = a.q
+    a.v = FAKE + (1 << 36)
+    a.out = FAKE + (1 << 37)
+    need = ctypes.c_size_t(0)
+    assert lib.ttt_fwd_workspace_size(ctypes.byref(a), ctypes.byref(need)) == OK
+    assert need.value > (64 << 20)
+    assert lib.ttt_fwd_chunked_noalloc(ctypes.byref(a)) == ERR_WS
+    assert lib.ttt_fwd_chunked_noalloc(ctypes.byref(fwd_args(q=None))) == ERR_NULL
+    assert lib.ttt_fwd_chunked_noalloc(ctypes.byref(fwd_args(dk=48))) == ERR_UNSUP
+    b = fwd_args()
+    b.out = b.v
+    assert lib.ttt_fwd_chunked_noalloc(ctypes.byref(b)) == ERR_ALIAS
+    assert lib.ttt_fwd_chunked_noalloc(None) == ERR_NULL
+
+
 def test_workspace_query(lib):
     a = fwd_args()
     ws = ctypes.c_size_t(123)
