@@ -1,22 +1,31 @@
 """Benchmark of the chunked TTT fast-weight forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm-scale]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload inplace-128k]
 
 One step = one full pass of the hot path over one batch of synthetic input
-(all inputs resident in HBM before timing): for the default LM-scale
-workload, one ttt_fwd_chunked call (token-causal, per-token eta, S0 in,
-outputs and final state out).  Prints ONE JSON line.
+(all inputs resident in HBM before timing).  The default workload is the
+largest single-GPU configuration: In-Place TTT chunk-causal forward of one
+Wdown fast weight (d_ff 9728 x d_model 2560, fp32) over L = 131072 tokens in
+chunks of 1024, one ttt_fwd_chunked call (the update walk and the batched
+readout).  Prints ONE JSON line.
 
 Warm-up: the W warm-up steps are extended until at least --min-warmup-s
 seconds of steps have run (the count actually run is reported), so that the
 timed steps see the GPU's steady clocks rather than its ramp.
 
-Roofline: the dominant kernel's average launch duration is measured with
-HIP events recorded on the launch stream around every timed step; achieved
-bandwidth = algorithmic bytes per launch / that duration.  HBM traffic
-counted by rocprofv3 (FETCH_SIZE / WRITE_SIZE, scaled by a plain copy's
-counters) is read from profiles/traffic.json when it was measured on the
-current kernel source, else reported as null.
+Timing: every timed step is bracketed by HIP events on the launch stream.
+Between steps, outside the events, a 512 MiB scratch buffer is written so
+that no input is still in the 256 MiB last-level cache (--no-evict turns it
+off).  value and ms_per_step use the mean event time of a step; the median
+and minimum are reported beside it, and so is the wall time per step with
+the eviction writes.  The GPU clock is read with rocm-smi before and after
+the timed steps (null when rocm-smi gives none).
+
+Roofline: the dominant kernel's average launch duration is the mean event
+time; achieved = algorithmic bytes (or FLOPs) per launch / that duration.
+HBM traffic counted by rocprofv3 (FETCH_SIZE / WRITE_SIZE, scaled by a plain
+copy's counters) is read from profiles/traffic.json when it was measured on
+the current kernel source, else reported as null.
 
 cpu_baseline: the fp64 oracle (C, OpenMP over heads) timed on this host on
 the same seeded inputs.
@@ -97,7 +106,10 @@ def setup_workload(name: str, dev: str):
                      + B * H * L * dv * es                          # out
                      + nstate * B * H * dk * dv * 4)                # final state(s)
         flop_alg = B * H * L * (4 * nstate * dk * dv + (C + 1) * (dk + dv))
-        info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, chunk=C, mode="token_causal",
+        # the kernel tiles token-causal work in 64-token chunks (32 for fp32)
+        # whatever C is: token-causal results do not depend on the chunk
+        info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, chunk=C,
+                    kernel_tile_tokens=64 if inp.dtype == "bf16" else 32, mode="token_causal",
                     beta=inp.beta, eta="per-token" if eta is not None else inp.eta_scalar,
                     dtype=inp.dtype, tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
                     kernel="tcb_fwd_kernel" if inp.dtype == "bf16" else "tc_fwd_kernel", inputs=inp)
@@ -358,6 +370,22 @@ def cpu_baseline(info) -> dict:
             "sample": what + "; tokens/s scaled by the head fraction"}
 
 
+def gpu_sclk_mhz():
+    """Current shader clock of GPU 0 in MHz from rocm-smi, or None."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    for ln in r.stdout.splitlines():
+        if "sclk" in ln.lower():
+            m = re.search(r"\((\d+)\s*Mhz\)", ln, flags=re.I)
+            if m:
+                return int(m.group(1))
+    return None
+
+
 def blas_threads() -> int:
     """Threads NumPy's BLAS runs the oracle's GEMMs with."""
     from threadpoolctl import threadpool_info
@@ -381,10 +409,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="lm-scale",
-                    help="lm-scale (default), small-f32, inplace-32k, inplace-128k, momentum, dual-b16, "
+    ap.add_argument("--workload", default="inplace-128k",
+                    help="inplace-128k (default), lm-scale, small-f32, inplace-32k, momentum, dual-b16, "
                          "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, inplace-frontend, swiglu, swiglu-mse, "
                          "scan, scan-momentum")
+    ap.add_argument("--no-evict", action="store_true",
+                    help="do not write the 512 MiB eviction buffer between timed steps")
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this many seconds of steps have run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -429,18 +459,28 @@ def main():
         torch.cuda.synchronize()
     warm_s = time.perf_counter() - t_w
 
+    # 512 MiB written between timed steps (outside the events): twice the
+    # last-level cache, so no step finds its inputs there
+    evict = None if args.no_evict else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    clk_before = gpu_sclk_mhz()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if evict is not None:
+            evict.fill_(i & 0xff)
         starts[i].record(stream)
         step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
-    ms_per_step = wall * 1000.0 / args.steps
+    clk_after = gpu_sclk_mhz()
+    step_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    launch_ms = sum(step_ms) / args.steps
+    ms_per_step = launch_ms
+    median_ms = step_ms[len(step_ms) // 2] if len(step_ms) % 2 else 0.5 * (step_ms[len(step_ms) // 2 - 1] +
+                                                                            step_ms[len(step_ms) // 2])
 
     tokens = info["tokens"]
     value = tokens / (ms_per_step / 1000.0)
@@ -461,6 +501,9 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
         "warmup_s": round(warm_s, 3), "ms_per_step": round(ms_per_step, 5),
+        "ms_median": round(median_ms, 5), "ms_min": round(step_ms[0], 5),
+        "wall_ms_per_step": round(wall * 1000.0 / args.steps, 5), "evict_bytes": 0 if evict is None else evict.numel(),
+        "sclk_mhz": {"before": clk_before, "after": clk_after},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": info["dtype"], "data": "synthetic (seeded Gaussian inputs of the workload's shapes)",
         "config": cfg,

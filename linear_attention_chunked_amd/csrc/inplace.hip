@@ -10,10 +10,16 @@
 //
 // The state (dk x dv, e.g. 9728 x 2560 fp32 = 99.6 MB) cannot stay on chip, so
 // the forward runs in two MFMA-bound passes:
-//   1. update walk: every workgroup owns a 256 x 256 tile of W in fp32
-//      accumulators and walks the chunks in order (the prefix sum of the
-//      chunk deltas happens in registers); before chunk i it writes the bf16
-//      snapshot W_{i-1}^T of its tile to the workspace.  K = chunk tokens.
+//   1. update walk: every workgroup owns a tile of W in fp32 accumulators
+//      and walks the chunks in order (the prefix sum of the chunk deltas
+//      happens in registers); before chunk i it writes the bf16 snapshot
+//      W_{i-1}^T of its tile to the workspace.  K = chunk tokens.
+//      Snapshots are stored blocked by 16 rows of W: element (n, m) of
+//      W_{i-1}^T at ((m / 16) dv + n) 16 + m % 16, i.e. [dk/16][dv][16].  The
+//      update's accumulators hold 4 consecutive m of one n per lane, so a
+//      lane group writes whole 32-byte blocks and a store instruction 512
+//      contiguous bytes; the readout still streams both operands along dk
+//      (a 32-wide k step of a row n is two 32-byte blocks).
 //   2. readout: O_i^T = W_{i-1}^T Z_i^T for all chunks at once, a batched GEMM
 //      over (chunk, token tile, dv tile), K = dk.
 // Both use v_mfma_f32_32x32x16_bf16 with fp32 accumulation, 256 x 256 block
@@ -176,9 +182,10 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
     const float out_scale = PT ? 1.f : p.eta_scalar;   // acc -> W
     bf16_t* snap = p.snap + (int64_t)bh * p.nchunks * p.dk * p.dv;
 
-    // snapshot W_{chunk-1}^T (bf16) of this tile: [n][m] layout.  A lane holds
-    // 4 consecutive m of one n, so the tile goes through LDS ([n][m] rows of
-    // 512 bytes) and leaves as whole 16-byte row pieces; the next snapshot is
+    // snapshot W_{chunk-1}^T (bf16) of this tile in the blocked layout.  A
+    // lane holds 4 consecutive m of one n, so the tile goes through LDS ([n][m]
+    // rows of 512 bytes) and leaves as 16-byte halves of the (m / 16, n)
+    // blocks, consecutive lanes on consecutive addresses; the next snapshot is
     // a chunk of K-steps (and their barriers) later, so one barrier suffices.
     auto snapshot = [&](int chunk) __attribute__((always_inline)) {
         const int nl = 64 * wn + (lane & 31), ml = 128 * wm + 4 * (lane >> 5);
@@ -193,12 +200,12 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
                     st4(&sS[(nl + 32 * j) * IP_SNR + ml + 32 * i + 8 * q], v4 * out_scale);
                 }
         __syncthreads();
-        bf16_t* sp = snap + (int64_t)chunk * p.dk * p.dv + (int64_t)n0 * p.dk + m0;
-        constexpr int PR = IP_BM / 8;   // 16-byte pieces per row
-        for (int x = tid; x < IPU_BN * PR; x += IP_NT) {
-            const int r = x / PR, c = x % PR;
-            *reinterpret_cast<u32x4*>(sp + (int64_t)r * p.dk + 8 * c) =
-                *reinterpret_cast<const u32x4*>(&sS[r * IP_SNR + 8 * c]);
+        bf16_t* sp = snap + (int64_t)chunk * p.dk * p.dv + ((int64_t)(m0 >> 4) * p.dv + n0) * 16;
+        // x -> (16-row block cb, column r, half hf): consecutive x, consecutive 16 bytes
+        for (int x = tid; x < IPU_BN * (IP_BM / 8); x += IP_NT) {
+            const int hf = x & 1, r = (x >> 1) % IPU_BN, cb = (x >> 1) / IPU_BN;
+            *reinterpret_cast<u32x4*>(sp + ((int64_t)cb * p.dv + r) * 16 + 8 * hf) =
+                *reinterpret_cast<const u32x4*>(&sS[r * IP_SNR + 16 * cb + 8 * hf]);
         }
     };
     auto compute = [&](int buf) __attribute__((always_inline)) {
@@ -324,8 +331,245 @@ __global__ __launch_bounds__(IP_NT) void ip_update_kernel(IpUpdateParams p) {
     }
 }
 
+// ------------------------------------------------- pass 1, wide tiles
+// The update walk with one workgroup per CU: a 304 x 320 tile of W
+// (d_ff 9728 = 32 x 304, d_model 2560 = 8 x 320 give exactly 256 tiles, one
+// wave of workgroups on 256 CUs).  Every token of the walk brings
+// (304 + 320) x 2 bytes from L2 for 304 x 320 x 2 FLOP: 156 FLOP per byte,
+// against 85 for the 256 x 128 tiles of ip_update_kernel, whose 760 tiles
+// fill the chip in three waves.
+//   - 8 waves, two per SIMD.  Wave w owns column tiles 5 (w % 4) .. +4
+//     (16 columns each) and row tiles 0..9 (w < 4) or 10..18 (w >= 4) of 16
+//     rows: waves w and w + 4 share a SIMD and together run its 95
+//     v_mfma_f32_16x16x32_bf16 per K-step of 32 tokens, with at most 50
+//     16 x 16 accumulators (200 registers) per wave.
+//   - Operands stream straight from global memory into LDS with gfx950's
+//     16-byte buffer loads to LDS, a ring of four K-step buffers (156 KB;
+//     loads three steps ahead), one barrier per step.  A wave-load instruction writes 64
+//     consecutive 16-byte LDS slots; which global piece each lane fetches
+//     sets the layout.
+//   - LDS A (Z): [32 k][304 m], 608-byte rows (38 pieces), logical token k
+//     in row k with bits 2 and 3 swapped: a half-wave's transposing fragment
+//     read then touches 8 consecutive rows, whose bank octets (3 row mod 8)
+//     are all distinct.  LDS B (V-hat): [32 k][320 n], 640-byte rows (40
+//     pieces); the four waves' blocks of 5 column tiles are rotated per row,
+//     block g of row k at block (g + rotB(k)) mod 4, so that the 8 rows of a
+//     half-wave read fall on distinct bank octets while a wave's 5 tiles stay
+//     contiguous (fragment addresses are one base plus constant offsets).
+//     Both layouts were checked conflict-free by a model of the 64 banks.
+//   - Scalar eta only (the accumulators hold W / eta, as in ip_update_kernel);
+//     L and the chunk a multiple of 32.  Other cases use ip_update_kernel.
+constexpr int IW_MT = 19;                  // 16-row tiles per workgroup tile
+constexpr int IW_MH = 10;                  // row tiles of the first half (waves 0..3)
+constexpr int IW_NTW = 5;                  // 16-column tiles per wave
+constexpr int IW_BM = 16 * IW_MT;          // 304
+constexpr int IW_BN = 4 * 16 * IW_NTW;     // 320
+constexpr int IW_BK = 32;
+constexpr int IW_NB = 4;                   // LDS ring stages (three K-steps of loads in flight)
+constexpr int IW_NT = 512;                 // threads per workgroup
+constexpr int IW_PA = IW_BM / 8;           // 38 pieces per A row
+constexpr int IW_PB = IW_BN / 8;           // 40 pieces per B row
+constexpr int IW_LA = IW_BK * IW_PA / 64;  // 19 wave-loads per step (A)
+constexpr int IW_LB = IW_BK * IW_PB / 64;  // 20 wave-loads per step (B)
+constexpr int IW_LW = 5;                   // wave-loads per wave and step (39 + 1 repeat)
+constexpr int IW_SA = IW_BK * IW_BM;       // elements per A stage
+constexpr int IW_SB = IW_BK * IW_BN;       // elements per B stage
+static_assert(IW_LA * 64 == IW_BK * IW_PA && IW_LB * 64 == IW_BK * IW_PB, "whole wave-loads");
+static_assert(8 * IW_LW == IW_LA + IW_LB + 1, "five wave-loads per wave");
+
+TTT_DEV int iw_rowA(int k) { return (k & ~12) | ((k >> 1) & 4) | ((k << 1) & 8); }   // an involution
+TTT_DEV int iw_rotB(int k) { return ((k >> 1) & 1) + 2 * ((k >> 3) & 1); }
+// physical piece of logical piece q (of 40) in B row k
+TTT_DEV int iw_pieceB(int k, int q) {
+    const int t = q >> 1, g = t / IW_NTW, j = t % IW_NTW;
+    return 2 * (IW_NTW * ((g + iw_rotB(k)) & 3) + j) + (q & 1);
+}
+
+typedef __attribute__((address_space(3))) void iw_lds_t;
+
+TTT_DEV void mma16(f32x4& acc, const bf16x8& a, const bf16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+bool ip_wide_supported(const IpUpdateParams& p, bool per_token) {
+    return !per_token && p.dk % IW_BM == 0 && p.dv % IW_BN == 0 && p.chunk % IW_BK == 0 && p.L % IW_BK == 0 &&
+           (int64_t)IW_BK * p.ks[2] * 2 < (int64_t(1) << 31) && (int64_t)IW_BK * p.vs[2] * 2 < (int64_t(1) << 31);
+}
+
+// One body for both halves of the row tiles: wave w runs row tiles
+// mbase .. mbase + mt - 1 (mt = 10 or 9, wave-uniform); the tenth
+// accumulator row of the second half stays unused (a uniform branch skips
+// its reads, products and stores), which keeps one register allocation.
+TTT_DEV void ip_wide_body(const IpUpdateParams& p, bf16_t* sA, bf16_t* sB, int wave, int lane, int m0, int n0,
+                          int bh, const bf16_t* Zg, const bf16_t* Vg) {
+    constexpr int MT = IW_MH;
+    const int mbase = wave < 4 ? 0 : IW_MH, mt = wave < 4 ? IW_MH : IW_MT - IW_MH;
+    const int G = lane >> 4, a16 = lane & 15, g = wave & 3;
+    const int ldz = (int)p.ks[2], ldv = (int)p.vs[2];
+    const int b = bh / p.H, h = bh % p.H;
+    const int ncol = n0 + 80 * g + a16;   // this lane's column in tile j: ncol + 16 j
+
+    // accumulators: acc[i][j] = W[m0 + 16 (mbase + i) + 4 G + r][ncol + 16 j] / eta
+    f32x4 acc[MT][IW_NTW];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < IW_NTW; ++j) acc[i][j] = zero4();
+    if (p.S0) {
+        const float inv_eta = 1.f / p.eta_scalar;
+        const float* W0 = p.S0 + b * p.s0s[0] + h * p.s0s[1] + (int64_t)(m0 + 16 * mbase + 4 * G) * p.dv + ncol;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if (i < mt) {
+#pragma unroll
+                for (int j = 0; j < IW_NTW; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] = W0[(int64_t)(16 * i + r) * p.dv + 16 * j] * inv_eta;
+            }
+        }
+    }
+
+    // this lane's five 16-byte pieces per K-step: wave-load y = 5 wave + x of
+    // the step's 39 (A: 0..18, B: 19..38; y = 39 repeats y = 38), each at a
+    // fixed byte offset from the step's first token row
+    uint32_t voff[IW_LW];
+#pragma unroll
+    for (int x = 0; x < IW_LW; ++x) {
+        const int y = min(IW_LW * wave + x, IW_LA + IW_LB - 1);
+        if (y < IW_LA) {
+            const int P = 64 * y + lane, R = P / IW_PA, piece = P % IW_PA;
+            voff[x] = (uint32_t)((iw_rowA(R) * ldz + 8 * piece) * 2);
+        } else {
+            // physical slot P holds the logical piece whose block rotates onto it
+            const int P = 64 * (y - IW_LA) + lane, R = P / IW_PB, piece = P % IW_PB;
+            const int t = piece >> 1, q = 2 * (IW_NTW * (((t / IW_NTW) - iw_rotB(R)) & 3) + t % IW_NTW) + (piece & 1);
+            voff[x] = (uint32_t)((R * ldv + 8 * q) * 2);
+        }
+    }
+    const int total_steps = p.L / IW_BK, kpc = p.chunk / IW_BK;
+    auto issue = [&](int st) __attribute__((always_inline)) {
+        const int s = min(st, total_steps - 1), buf = st % IW_NB;
+        const int64_t t0 = (int64_t)s * IW_BK;
+        const __amdgpu_buffer_rsrc_t rz =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(Zg + t0 * ldz), 0, IW_BK * ldz * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(Vg + t0 * ldv), 0, IW_BK * ldv * 2, 0x00020000);
+#pragma unroll
+        for (int x = 0; x < IW_LW; ++x) {
+            const int y = min(IW_LW * wave + x, IW_LA + IW_LB - 1);   // wave-uniform
+            if (y < IW_LA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (iw_lds_t*)(sA + buf * IW_SA + 512 * y), 16, voff[x], 0,
+                                                         0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (iw_lds_t*)(sB + buf * IW_SB + 512 * (y - IW_LA)), 16,
+                                                         voff[x], 0, 0, 0);
+        }
+    };
+
+    // fragment addresses (elements within a stage) for the k-half hk of a
+    // 16 x 32 operand: lane (G, a16) reads logical k = 8 G + 4 hk + a16 / 4
+    // (tile i of A and tile j of B at constant offsets 16 i, 16 j from them)
+    int aoff[2], boff[2];
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk) {
+        const int k = 8 * G + 4 * hk + (a16 >> 2);
+        aoff[hk] = iw_rowA(k) * IW_BM + 16 * mbase + 4 * (a16 & 3);
+        boff[hk] = k * IW_BN + 8 * iw_pieceB(k, 2 * IW_NTW * g + ((a16 & 3) >> 1)) + 4 * (a16 & 1);
+    }
+    auto frag = [&](const bf16_t* base, int o0, int o1) __attribute__((always_inline)) {
+        const u32x2 lo = ds_read_tr(base + o0);
+        const u32x2 hi = ds_read_tr(base + o1);
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    auto compute = [&](int buf) __attribute__((always_inline)) {
+        const bf16_t* A = sA + buf * IW_SA;
+        const bf16_t* Bs = sB + buf * IW_SB;
+        bf16x8 bf[IW_NTW];
+#pragma unroll
+        for (int j = 0; j < IW_NTW; ++j) bf[j] = frag(Bs, boff[0] + 16 * j, boff[1] + 16 * j);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if (i < mt) {
+                const bf16x8 af = frag(A, aoff[0] + 16 * i, aoff[1] + 16 * i);
+#pragma unroll
+                for (int j = 0; j < IW_NTW; ++j) mma16(acc[i][j], af, bf[j]);
+            }
+        }
+    };
+
+    bf16_t* snap = p.snap + (int64_t)bh * p.nchunks * p.dk * p.dv;
+    // W_{c-1}^T of this tile in the blocked layout: a lane's 4 values (4
+    // consecutive m of one n) leave as one 8-byte store, the 4 lane groups
+    // fill the 32-byte block of (m / 16, n), and the 16 columns of a tile
+    // are consecutive blocks: 512 contiguous bytes per store instruction
+    auto snapshot = [&](int c) __attribute__((always_inline)) {
+        bf16_t* sp = snap + (int64_t)c * p.dk * p.dv + ((int64_t)((m0 >> 4) + mbase) * p.dv + ncol) * 16 + 4 * G;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if (i < mt) {
+#pragma unroll
+                for (int j = 0; j < IW_NTW; ++j) {
+                    const f32x4 v = acc[i][j] * p.eta_scalar;
+                    *reinterpret_cast<u32x2*>(sp + (int64_t)i * p.dv * 16 + 256 * j) =
+                        u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
+                }
+            }
+        }
+    };
+
+    // vmcnt field of s_waitcnt (gfx9: bits 3..0 and 15..14); lgkmcnt and
+    // expcnt at their maxima
+    constexpr int AHEAD = IW_NB - 1;   // K-steps of loads in flight
+    constexpr int NW = IW_LW * (AHEAD - 1);
+    constexpr int WAIT_ONE_STEP = (NW & 15) | ((NW >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+#pragma unroll
+    for (int x = 0; x < AHEAD; ++x) issue(x);
+    for (int st = 0; st < total_steps; ++st) {
+        if (st % kpc == 0) snapshot(st / kpc);
+        // this wave's loads of step st are done once only the later steps' are left
+        __builtin_amdgcn_s_waitcnt(WAIT_ONE_STEP);
+        __builtin_amdgcn_s_barrier();
+        issue(st + AHEAD);
+        compute(st % IW_NB);
+    }
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));   // the clamped loads still in flight
+    __builtin_amdgcn_s_barrier();
+
+    if (p.S_final) {
+        float* Wf = p.S_final + (int64_t)bh * p.dk * p.dv + (int64_t)(m0 + 16 * mbase + 4 * G) * p.dv + ncol;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+            if (i < mt) {
+#pragma unroll
+                for (int j = 0; j < IW_NTW; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Wf[(int64_t)(16 * i + r) * p.dv + 16 * j] = acc[i][j][r] * p.eta_scalar;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(IW_NT) void ip_update_wide_kernel(IpUpdateParams p) {
+    __shared__ __attribute__((aligned(16))) bf16_t sA[IW_NB * IW_SA];
+    __shared__ __attribute__((aligned(16))) bf16_t sB[IW_NB * IW_SB];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tiles_n = p.dv / IW_BN;
+    // logical order (bh, row tile, column tile): an XCD runs a contiguous
+    // range, i.e. a few row tiles with all their column tiles, which share
+    // the row tiles' Z columns through its L2
+    const int lid = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+    const int tile = lid % gridDim.x;
+    const int m0 = (tile / tiles_n) * IW_BM, n0 = (tile % tiles_n) * IW_BN;
+    const int bh = lid / gridDim.x, b = bh / p.H, h = bh % p.H;
+    const bf16_t* Zg = p.k + b * p.ks[0] + h * p.ks[1] + m0;
+    const bf16_t* Vg = p.v + b * p.vs[0] + h * p.vs[1] + n0;
+    ip_wide_body(p, sA, sB, wave, lane, m0, n0, bh, Zg, Vg);
+}
+
 // ------------------------------------------------------------------ pass 2
-// O_c^T tile [256 dv][256 tokens] = snap_c^T [dv][dk] x Z_c^T; grid.x =
+// O_c^T tile [256 dv][256 tokens] = snap_c^T [dv][dk] x Z_c^T (snapshots in
+// the blocked [dk/16][dv][16] layout); grid.x =
 // nchunks * (chunk/256) * (dv/256), grid.y = B*H.
 struct IpReadoutParams {
     const bf16_t* q;          // Z [B,H,L,dk]
@@ -362,7 +606,7 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
     const int t0 = chunk * p.chunk + tt * IP_BN;      // token offset
     const int bh = lid / gridDim.x, b = bh / p.H, h = bh % p.H;
     if (t0 >= p.L) return;                            // whole tile past the end (uniform)
-    const bf16_t* S = p.snap + ((int64_t)bh * p.nchunks + chunk) * p.dk * p.dv + (int64_t)n0 * p.dk;
+    const bf16_t* S = p.snap + ((int64_t)bh * p.nchunks + chunk) * p.dk * p.dv + (int64_t)n0 * 16;
     const bf16_t* Zt = p.q + b * p.qs[0] + h * p.qs[1] + (int64_t)t0 * p.qs[2];
     bf16_t* Og = p.out + b * p.os[0] + h * p.os[1];
     const int L = p.L;
@@ -376,8 +620,9 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // staging: 256 rows x 4 chunks per operand, thread -> 4 (row, chunk) pairs;
-    // per-lane offsets are the same for every K-step (token rows past L read
-    // row L-1: their outputs are never stored)
+    // per-lane offsets are the same for every K-step, which moves them by 32
+    // elements (Z) or two 16-row blocks of the snapshot (token rows past L
+    // read row L-1: their outputs are never stored)
     constexpr int NS = 4;                             // K-steps of loads in flight
     u32x4 ra[NS][4], rb[NS][4];
     uint32_t aoff[4], boff[4];
@@ -385,17 +630,18 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
         const int u = tid + y * IP_NT, row = u >> 2, c = u & 3;
-        aoff[y] = (uint32_t)(row * p.dk + 8 * c);
+        aoff[y] = (uint32_t)((c >> 1) * 16 * p.dv + row * 16 + 8 * (c & 1));
         boff[y] = (uint32_t)(min(row, L - 1 - t0) * (int)p.qs[2] + 8 * c);
         loff[y] = row * IP_BK + 8 * (c ^ ro_swz(row));
     }
     const int steps = p.dk / IP_BK;
     auto load = [&](int st, auto SET) __attribute__((always_inline)) {
         constexpr int k = decltype(SET)::value;
-        const int k0 = min(st, steps - 1) * IP_BK;
+        const int s = min(st, steps - 1), k0 = s * IP_BK;
+        const uint32_t a0 = (uint32_t)s * (uint32_t)(IP_BK * p.dv);   // two 16-row blocks per step
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-            ra[k][y] = *reinterpret_cast<const u32x4*>(S + aoff[y] + k0);
+            ra[k][y] = *reinterpret_cast<const u32x4*>(S + (aoff[y] + a0));
             rb[k][y] = *reinterpret_cast<const u32x4*>(Zt + boff[y] + k0);
         }
     };
@@ -506,8 +752,9 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
 }
 
 bool inplace_supported(int dtype, int dk, int dv, int chunk) {
+    // IP_BN is a multiple of the update tile IPU_BN; snapshot offsets are 32-bit
     return dtype == 1 && dk % IP_BM == 0 && dv % IP_BN == 0 && chunk % IP_BN == 0 && dk >= IP_BM &&
-           dv >= IP_BN;  // IP_BN is a multiple of the update tile IPU_BN
+           dv >= IP_BN && (int64_t)dk * dv < (int64_t(1) << 31);
 }
 
 size_t inplace_workspace(int B, int H, int L, int dk, int dv, int chunk) {
@@ -538,11 +785,16 @@ hipError_t launch_inplace(const TcParams& p, void* workspace, hipStream_t s) {
     u.dv = p.dv;
     u.chunk = p.chunk;
     u.nchunks = N;
+    if (ip_wide_supported(u, p.eta || p.eta_scalar == 0.f)) {
+        const dim3 gw((p.dk / IW_BM) * (p.dv / IW_BN), p.B * p.H);
+        hipLaunchKernelGGL(ip_update_wide_kernel, gw, dim3(IW_NT), 0, s, u);
+    } else {
     const dim3 g1((p.dk / IP_BM) * (p.dv / IPU_BN), p.B * p.H);
     if (p.eta || p.eta_scalar == 0.f) {
         hipLaunchKernelGGL(ip_update_kernel<true>, g1, dim3(IP_NT), 0, s, u);
     } else {
         hipLaunchKernelGGL(ip_update_kernel<false>, g1, dim3(IP_NT), 0, s, u);
+    }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -462,6 +462,30 @@ def test_inplace_midsize_vs_oracle(L, C, per_token):
     assert oracle.rel_l2(out[0, 0, :C].cpu().float(), (Z[0, 0, :C].double() @ W0[0, 0].double()).numpy()) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("C", [512, 256])
+def test_inplace_wide_tiles_vs_oracle(C):
+    """d_k = 4864 = 16 x 304, d_v = 1280 = 4 x 320 with a scalar eta: the
+    update walk runs on the wide 304 x 320 tiles (the In-Place workload's
+    path, 64 tiles here); the whole output and the whole final weight against
+    the oracle, and the first chunk against its plain GEMM."""
+    g = torch.Generator().manual_seed(4864 + C)
+    L, dk, dv = 1024, 4864, 1280
+    a = torch.randn(1, 1, L, dk, generator=g).to(torch.bfloat16).float()
+    b = torch.randn(1, 1, L, dk, generator=g).to(torch.bfloat16).float()
+    Z = (torch.nn.functional.silu(a) * b).to(torch.bfloat16)
+    V = torch.randn(1, 1, L, dv, generator=g).to(torch.bfloat16)
+    W0 = 0.02 * torch.randn(1, 1, dk, dv, generator=g)
+    say(f"in-place wide tiles L{L} dk{dk} dv{dv} C{C}")
+    out, Wf = run_inplace(Z, V, W0, W.f32(1e-3), C, None)
+    ref, Wr = oracle.chunk_causal(Z, Z, V, eta=None, eta_scalar=W.f32(1e-3), S0=W0, chunk=C)
+    e = oracle.rel_l2(out.cpu().float(), ref)
+    ew = oracle.rel_l2(Wf.cpu(), Wr)
+    say(f"in-place wide tiles C{C}: out rel-L2 {e:.2e}, W_final rel-L2 {ew:.2e}")
+    assert e <= TOL["bf16"], e
+    assert ew <= 1e-5, ew
+    assert oracle.rel_l2(out[0, 0, :C].cpu().float(), (Z[0, 0, :C].double() @ W0[0, 0].double()).numpy()) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("L", [32768, 131072])
 def test_inplace_full_sampled_rows(L):
     """In-Place Wdown update at d_ff 9728, d_model 2560, C 1024 (B = H = 1),
@@ -487,14 +511,24 @@ def test_inplace_full_sampled_rows(L):
     e = oracle.rel_l2(got, ref)
     say(f"in-place full L{L}: sampled-row rel-L2 {e:.2e}")
     assert e <= TOL["bf16"], e
-    # final weight entries: W0 + eta * Z^T V (columns of Z against columns of V)
+    # final weight W0 + eta Z^T V: three whole rows (2560 entries each) and
+    # three whole columns (9728 entries each, through every row tile of the
+    # update), fp64 sums over blocks of tokens
     rr = [0, 4321, 9727]
     cc = [0, 1234, 2559]
-    Zs = Zc[0, 0][:, rr].double()
-    Vs = Vc[0, 0][:, cc].double()
-    Wref = inp.S0[0, 0][rr][:, cc].double() + inp.eta_scalar * (Zs.T @ Vs)
-    Wgot = Wf[0, 0][rr][:, cc].cpu().double()
-    e = oracle.rel_l2(Wgot, Wref)
-    say(f"in-place full L{L}: W_final entries rel-L2 {e:.2e}")
+    say("in-place full: final-weight rows and columns")
+    rows_ref = torch.zeros(len(rr), 2560, dtype=torch.float64)
+    cols_ref = torch.zeros(9728, len(cc), dtype=torch.float64)
+    for t0 in range(0, L, 8192):
+        Zb, Vb = Zc[0, 0, t0:t0 + 8192], Vc[0, 0, t0:t0 + 8192]
+        rows_ref += Zb[:, rr].double().T @ Vb.double()
+        cols_ref += Zb.double().T @ Vb[:, cc].double()
+    W0 = inp.S0[0, 0].double()
+    rows_ref = W0[rr] + inp.eta_scalar * rows_ref
+    cols_ref = W0[:, cc] + inp.eta_scalar * cols_ref
+    Wc = Wf[0, 0].cpu().double()
+    er, ec = oracle.rel_l2(Wc[rr], rows_ref), oracle.rel_l2(Wc[:, cc], cols_ref)
+    say(f"in-place full L{L}: W_final rows rel-L2 {er:.2e}, columns rel-L2 {ec:.2e} "
+        f"({len(rr) * 2560 + len(cc) * 9728} entries)")
     # scalar eta: the update sums exact bf16 x bf16 products in fp32
-    assert e <= 1e-4, e
+    assert er <= 1e-4 and ec <= 1e-4, (er, ec)
