@@ -53,6 +53,7 @@ KERNEL_SOURCES = {
     "tc_fwd_kernel": ("tc_fwd.hip", "common.h"),
     "tcb_fwd_kernel": ("tcb_fwd.hip", "common.h"),
     "ip_update_kernel+ip_readout_kernel": ("inplace.hip", "common.h"),
+    "ip_update_wide_kernel+ip_readout_kernel": ("inplace.hip", "common.h"),
     "dual_fwd_kernel": ("dual.hip", "common.h"),
     "dual_chain_kernel": ("dual.hip", "common.h"),
     "decode_kernel": ("decode.hip", "common.h"),
@@ -140,7 +141,7 @@ def setup_workload(name: str, dev: str):
 
         info = dict(workload=name, B=1, H=1, L=L, d_ff=d_ff, d_model=d_model, chunk=1024,
                     mode="chunk_causal", eta=inp.eta_scalar, dtype="bf16", tokens=L,
-                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="ip_update_kernel+ip_readout_kernel",
+                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="ip_update_wide_kernel+ip_readout_kernel",
                     inputs=None, cpu_sample=cpu_sample)
         return step, info
     if name in ("dual-b16", "dual-b2048"):
