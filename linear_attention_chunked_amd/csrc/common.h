@@ -51,6 +51,21 @@ TTT_DEV int xcd_logical(int id, int n) {
     return (x < r) ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
+// One step of a direct-to-LDS load ring: issue(wa, wb) starts the loads
+// that fill a later step's buffers, compute(ra, rb) reads this step's.  The
+// ring orders its loads before the reads itself (s_waitcnt vmcnt on the
+// wave's own loads, then a barrier).  The compiler, which cannot follow that,
+// makes an LDS read wait for every LDS-bound load still in flight unless it
+// can prove the two apart; it can when the written and the read buffers
+// reach it as distinct __restrict__ parameters of one inlined call.  Without
+// that proof every step would drain the whole ring before its first read.
+template <class Issue, class Compute>
+TTT_DEV void ring_step(bf16_t* __restrict__ wa, bf16_t* __restrict__ wb, const bf16_t* __restrict__ ra,
+                       const bf16_t* __restrict__ rb, Issue&& issue, Compute&& compute) {
+    issue(wa, wb);
+    compute(ra, rb);
+}
+
 // ---------------------------------------------------------------- type traits
 template <typename T> struct Tr;
 

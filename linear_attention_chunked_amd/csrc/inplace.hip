@@ -447,8 +447,9 @@ TTT_DEV void ip_wide_body(const IpUpdateParams& p, bf16_t* sA, bf16_t* sB, int w
         }
     }
     const int total_steps = p.L / IW_BK, kpc = p.chunk / IW_BK;
-    auto issue = [&](int st) __attribute__((always_inline)) {
-        const int s = min(st, total_steps - 1), buf = st % IW_NB;
+    // loads of K-step st into the stage buffers a, b
+    auto issue = [&](int st, bf16_t* a, bf16_t* b) __attribute__((always_inline)) {
+        const int s = min(st, total_steps - 1);
         const int64_t t0 = (int64_t)s * IW_BK;
         const __amdgpu_buffer_rsrc_t rz =
             __builtin_amdgcn_make_buffer_rsrc((void*)(Zg + t0 * ldz), 0, IW_BK * ldz * 2, 0x00020000);
@@ -458,11 +459,10 @@ TTT_DEV void ip_wide_body(const IpUpdateParams& p, bf16_t* sA, bf16_t* sB, int w
         for (int x = 0; x < IW_LW; ++x) {
             const int y = min(IW_LW * wave + x, IW_LA + IW_LB - 1);   // wave-uniform
             if (y < IW_LA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (iw_lds_t*)(sA + buf * IW_SA + 512 * y), 16, voff[x], 0,
-                                                         0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rz, (iw_lds_t*)(a + 512 * y), 16, voff[x], 0, 0, 0);
             else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (iw_lds_t*)(sB + buf * IW_SB + 512 * (y - IW_LA)), 16,
-                                                         voff[x], 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (iw_lds_t*)(b + 512 * (y - IW_LA)), 16, voff[x], 0, 0,
+                                                         0);
         }
     };
 
@@ -481,9 +481,7 @@ TTT_DEV void ip_wide_body(const IpUpdateParams& p, bf16_t* sA, bf16_t* sB, int w
         const u32x2 hi = ds_read_tr(base + o1);
         return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
-    auto compute = [&](int buf) __attribute__((always_inline)) {
-        const bf16_t* A = sA + buf * IW_SA;
-        const bf16_t* Bs = sB + buf * IW_SB;
+    auto compute = [&](const bf16_t* A, const bf16_t* Bs) __attribute__((always_inline)) {
         bf16x8 bf[IW_NTW];
 #pragma unroll
         for (int j = 0; j < IW_NTW; ++j) bf[j] = frag(Bs, boff[0] + 16 * j, boff[1] + 16 * j);
@@ -523,14 +521,17 @@ TTT_DEV void ip_wide_body(const IpUpdateParams& p, bf16_t* sA, bf16_t* sB, int w
     constexpr int NW = IW_LW * (AHEAD - 1);
     constexpr int WAIT_ONE_STEP = (NW & 15) | ((NW >> 4) << 14) | (0x7 << 4) | (0xf << 8);
 #pragma unroll
-    for (int x = 0; x < AHEAD; ++x) issue(x);
+    for (int x = 0; x < AHEAD; ++x) issue(x, sA + x * IW_SA, sB + x * IW_SB);
     for (int st = 0; st < total_steps; ++st) {
         if (st % kpc == 0) snapshot(st / kpc);
-        // this wave's loads of step st are done once only the later steps' are left
+        // this wave's loads of step st are done once only the later steps' are
+        // left; the barrier makes every wave's done, and ends every wave's
+        // reads of the buffer that step st + AHEAD refills
         __builtin_amdgcn_s_waitcnt(WAIT_ONE_STEP);
         __builtin_amdgcn_s_barrier();
-        issue(st + AHEAD);
-        compute(st % IW_NB);
+        const int rd = st % IW_NB, wr = (st + AHEAD) % IW_NB;
+        ring_step(sA + wr * IW_SA, sB + wr * IW_SB, sA + rd * IW_SA, sB + rd * IW_SB,
+                  [&](bf16_t* a, bf16_t* b) __attribute__((always_inline)) { issue(st + AHEAD, a, b); }, compute);
     }
     __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));   // the clamped loads still in flight
     __builtin_amdgcn_s_barrier();
