@@ -152,7 +152,8 @@ typedef struct ttt_fwd_args {
  *
  * Supported (else TTT_ERR_UNSUPPORTED): dk, dv in {32, 64, 128} for both
  * dtypes and both modes; CHUNK_CAUSAL with bf16 also dk, dv multiples of 256
- * (large fast weights, e.g. the In-Place Wdown) with chunk a multiple of 256.
+ * (large fast weights, e.g. the In-Place Wdown) with chunk a multiple of 256
+ * and row strides of q, k and v below 2^22 elements.
  * CHUNK_CAUSAL with small dims needs chunk a multiple of 64 (bf16) or 32
  * (fp32).  Returns TTT_ERR_WORKSPACE if the workspace is too small, and
  * TTT_ERR_ALIAS if out, S_final, M_final or the workspace overlaps an input

@@ -194,6 +194,8 @@ ttt_status_t validate_fwd(const ttt_fwd_args* a, int* mode_out) {
     if ((s = check_tensor(a->k, a->k_stride, a->B, a->H, a->L, a->dk, a->dtype)) != TTT_OK) return s;
     if ((s = check_tensor(a->v, a->v_stride, a->B, a->H, a->L, a->dv, a->dtype)) != TTT_OK) return s;
     if ((s = check_tensor(a->out, a->out_stride, a->B, a->H, a->L, a->dv, a->dtype)) != TTT_OK) return s;
+    if (use_inplace(a, *mode_out) && !ttt::inplace_strides_ok(a->q_stride[2], a->k_stride[2], a->v_stride[2]))
+        return TTT_ERR_UNSUPPORTED;
     uint64_t n = 0;
     const int64_t st = (int64_t)a->dk * a->dv;
     if (a->eta) {

@@ -59,10 +59,22 @@ TTT_DEV int xcd_logical(int id, int n) {
 // can prove the two apart; it can when the written and the read buffers
 // reach it as distinct __restrict__ parameters of one inlined call.  Without
 // that proof every step would drain the whole ring before its first read.
+// The buffers of a ring belong to one __shared__ array: the compiler tags
+// every access to an LDS array with that array, and tagged loads and reads
+// of one array look alike to it again.  The loads are issued before
+// anything of the computation (the scheduler would otherwise sink them).
+typedef __attribute__((address_space(3))) void lds_void_t;
+template <class Issue, class Compute>
+TTT_DEV void ring_step1(bf16_t* __restrict__ w, const bf16_t* __restrict__ r, Issue&& issue, Compute&& compute) {
+    issue(w);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(r);
+}
 template <class Issue, class Compute>
 TTT_DEV void ring_step(bf16_t* __restrict__ wa, bf16_t* __restrict__ wb, const bf16_t* __restrict__ ra,
                        const bf16_t* __restrict__ rb, Issue&& issue, Compute&& compute) {
     issue(wa, wb);
+    __builtin_amdgcn_sched_barrier(0);
     compute(ra, rb);
 }
 

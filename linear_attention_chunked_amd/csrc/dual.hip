@@ -264,7 +264,7 @@ __global__ __launch_bounds__(DV / 16 * 64) void dual_fwd_kernel(DualParams p) {
 }
 
 // ------------------------------------------------------------------------
-// dual_chain_kernel: bf16, d = dv = 64, mini-batches of a multiple of 16.
+// dual_ring_kernel: bf16, d = dv = 64, mini-batches of a multiple of 16.
 //
 // The columns of W evolve independently under the linear MSE update (column
 // j of E, V~ and S~ only involves column j of W and V), so each wave owns 16
@@ -279,13 +279,11 @@ __global__ __launch_bounds__(DV / 16 * 64) void dual_fwd_kernel(DualParams p) {
 // Feature order: accumulator row position p = 32kb + 16h + 4g + i of the
 // state holds feature d(p) = 32kb + 8g + 4h + i.  With that order the
 // operand fragment of lane (g, row) for feature block kb is the 16 contiguous
-// bytes X[row][32kb + 8g .. +8], so K and Q rows load straight into MFMA
-// operands (one 16-byte load each), and the state accumulators feed the next
-// contraction from registers.  The 16 x 64 K tile and the 16 x 16 V tile go
-// through wave-private LDS only for the two transposes the chain needs (V in
-// the E layout, K^T for the state update), read back with ds_read_b64_tr_b16.
-// Every lane issues the same loads each step (rows past L re-read row L-1;
-// their V~ is zeroed), DEPTH steps ahead.
+// bytes X[row][32kb + 8g .. +8], so K and Q rows are MFMA operands as they
+// sit in a row-major tile, and the state accumulators feed the next
+// contraction from registers.  The two transposes the chain needs (V in the
+// E layout, K^T for the state update) are ds_read_b64_tr_b16 reads of the
+// same tiles.
 typedef short s16x4d __attribute__((ext_vector_type(4)));
 
 TTT_DEV u32x2 tr_read_d(const bf16_t* p) {
@@ -307,21 +305,28 @@ TTT_DEV int kswz(int r) { return (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2) |
 // feature of state row position p
 TTT_DEV int feat(int p) { return (p & ~31) + 8 * ((p >> 2) & 3) + 4 * ((p >> 4) & 1) + (p & 3); }
 
-// ONESTEP: every mini-batch is exactly one 16-token step (W_n is S~ itself)
-// f(integral_constant<int, I>) for I = B .. E - 1, unrolled at compile time
-template <int B, int E, class F>
-TTT_DEV void for_sets(F&& f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        for_sets<B + 1, E>(f);
-    }
-}
 
-template <int DEPTH, bool ONESTEP>
-__global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
+// Operands reach LDS through a wave-private ring of DR_R stages of 32 tokens
+// (two steps), filled by 16-byte direct loads, so no VGPR holds data in
+// flight and nothing of the prefetch crosses the loop.  A stage holds the Q
+// and K rows [32][64], the 16-byte unit u of row r at position
+// u ^ (kswz(r mod 16) / 2), which gives row-fragment reads (MFMA operands of
+// K and Q) and the transposing K^T reads of the state update without bank
+// conflicts beyond two-way, and the wave's V tile [32][16] (read transposed
+// into the E layout).  Rows past L lie outside the buffer ranges: they load
+// as zero (a zero K row gives E = 0 and V~ = 0, so it adds nothing) and
+// their stores are dropped, so no step needs a clamp or a mask.
+constexpr int DR_R = 8;                         // ring stages
+constexpr int DR_T = 32;                        // tokens per stage
+constexpr int DR_QK = DR_T * 64;                // elements of the Q (or K) part
+constexpr int DR_STAGE = 2 * DR_QK + DR_T * 16; // elements per stage (9 KB)
+constexpr int DR_NL = 9;                        // load instructions per stage
+
+// ONESTEP: every mini-batch is exactly one 16-token step (W_n is S~ itself)
+template <bool ONESTEP>
+__global__ __launch_bounds__(64) void dual_ring_kernel(DualParams p) {
     constexpr int D = 64, DV = 64;
-    __shared__ __attribute__((aligned(16))) bf16_t sK[16 * D];   // [token][d], 8-byte chunks swizzled
-    __shared__ __attribute__((aligned(16))) bf16_t sV[16 * 16];  // [token][16 columns]
+    __shared__ __attribute__((aligned(16))) bf16_t ring[DR_R * DR_STAGE];
 
     const int lane = threadIdx.x, g = lane >> 4, c16 = lane & 15;
     // the 4 column waves of a head run on one XCD (shared Q/K rows in its L2)
@@ -347,57 +352,54 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) Sop[kb] = Wop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
 
-    // per-lane pieces of a step: row c16, features 32kb + 8g .. +8 of Q and K;
-    // columns 4g .. +4 of this wave's V tile
-    u32x4 rq[DEPTH][2], rk[DEPTH][2];
-    u32x2 rv[DEPTH];
-    // Buffer accesses: one descriptor per tensor of this head (the range is
-    // the head's rows), a fixed 32-bit lane offset and the step's row offset
-    // in a scalar.  Rows past L fall outside the range: loads return zero
-    // (a zero K row gives E = 0 and V~ = 0, so it adds nothing) and stores
-    // are dropped, so no step needs a clamp or a mask.
+    // one buffer descriptor per tensor of this head (range: the head's rows)
     const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)Qg, 0, L * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, L * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, L * DV * 2 - 32 * w, 0x00020000);
     const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)Og, 0, L * DV * 2 - 32 * w, 0x00020000);
-    const int qko = (c16 * D + 8 * g) * 2, vo = (c16 * DV + 4 * g) * 2;   // bytes
-    auto load = [&](int s, auto SET) {
-        constexpr int st = decltype(SET)::value;
-        const int rowb = s * 16 * D * 2;   // (D == DV)
+    // direct-load lane offsets (bytes from a stage's first token row): load i
+    // of Q or K fills rows 8i .. 8i + 7, lane l the position l % 8 of row
+    // 8i + l / 8; the V load fills the [32][16] tile, lane l half l % 2 of row l / 2
+    uint32_t qko[4];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            rq[st][kb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rQ, qko + 64 * kb, rowb, 0));
-            rk[st][kb] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rK, qko + 64 * kb, rowb, 0));
-        }
-        rv[st] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rV, vo, rowb, 0));
+    for (int i = 0; i < 4; ++i) {
+        const int row = 8 * i + (lane >> 3);
+        qko[i] = (uint32_t)(row * D * 2 + 16 * ((lane & 7) ^ (kswz(row & 15) >> 1)));
+    }
+    const uint32_t vdo = (uint32_t)((lane >> 1) * DV * 2 + 16 * (lane & 1));
+    const int nsteps = (L + 15) / 16, nst = (nsteps + 1) / 2;
+    auto issue = [&](int s, bf16_t* dst) __attribute__((always_inline)) {
+        const int sq = min(s, nst - 1) * DR_T * D * 2;   // bytes (D == DV)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_void_t*)(dst + 512 * i), 16, qko[i], sq, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void_t*)(dst + DR_QK + 512 * i), 16, qko[i], sq, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void_t*)(dst + 2 * DR_QK), 16, vdo, sq, 0, 0);
     };
+
     // causal mask of the packed bf16 P^T pieces (j = 4g + r <= i = c16), fixed per lane
     u32x2 pmask;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
         pmask[h] = ((4 * g + 2 * h <= c16) ? 0x0000ffffu : 0u) | ((4 * g + 2 * h + 1 <= c16) ? 0xffff0000u : 0u);
-
-    // LDS addresses (elements)
-    const int kw = c16 * D, ksw = kswz(c16);                 // K row writes
-    const int vw = c16 * 16 + 4 * g;                         // V tile write
+    // LDS addresses (elements within a step's rows)
+    const int fro = c16 * D, fsw = kswz(c16) >> 1;           // row fragments
     const int rr = 4 * g + (c16 >> 2), cq = c16 & 3;         // transposing reads: row, chunk quad
     const int vr = rr * 16 + 4 * cq;
     const int kr = rr * D, krs = kswz(rr);
+    const int vo = (c16 * DV + 4 * g) * 2;                   // output store (bytes)
 
-    const int nsteps = (L + 15) / 16;
-    const int nrun = (nsteps + DEPTH - 1) / DEPTH * DEPTH;   // whole rounds; extra steps are empty
-
-    auto step = [&](int s, auto SET) {
-        constexpr int st = decltype(SET)::value;
-        const int t0 = 16 * s;
-        const bf16x8 Kf0 = __builtin_bit_cast(bf16x8, rk[st][0]), Kf1 = __builtin_bit_cast(bf16x8, rk[st][1]);
-        const bf16x8 Qf0 = __builtin_bit_cast(bf16x8, rq[st][0]), Qf1 = __builtin_bit_cast(bf16x8, rq[st][1]);
-        // stage the two transposes
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            *reinterpret_cast<u32x4*>(&sK[kw + 4 * ((8 * kb + 2 * g) ^ ksw)]) = rk[st][kb];
-        *reinterpret_cast<u32x2*>(&sV[vw]) = rv[st];
-
+    // step s16 (tokens 16 s16 ..), rows 16 j .. of the stage at X
+    auto step = [&](const bf16_t* X, int j, int s16) __attribute__((always_inline)) {
+        const bf16_t* Qs = X + 16 * j * D;
+        const bf16_t* Ks = X + DR_QK + 16 * j * D;
+        const bf16_t* Vs = X + 2 * DR_QK + 256 * j;
+        const bf16x8 Kf0 = *reinterpret_cast<const bf16x8*>(Ks + fro + 8 * (g ^ fsw));
+        const bf16x8 Kf1 = *reinterpret_cast<const bf16x8*>(Ks + fro + 8 * ((4 + g) ^ fsw));
+        const bf16x8 Qf0 = *reinterpret_cast<const bf16x8*>(Qs + fro + 8 * (g ^ fsw));
+        const bf16x8 Qf1 = *reinterpret_cast<const bf16x8*>(Qs + fro + 8 * ((4 + g) ^ fsw));
         // E[token 4g+r][col c16] = K W_n
         f32x4 e = zero4();
         mma(e, Kf0, ONESTEP ? Sop[0] : Wop[0]);
@@ -410,14 +412,8 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
         f32x4 o = zero4();
         mma(o, Sop[0], Qf0);
         mma(o, Sop[1], Qf1);
-        // the refill of this register set goes after every read of its old
-        // contents: the new loads then land in the same registers and the
-        // loop carries no copies of in-flight data (a copy would wait for it)
-        __builtin_amdgcn_sched_barrier(0);
-        load(s + DEPTH, SET);
-
         // V in the E layout; V~ = eta (V - E), zero past L
-        const u32x2 vraw = tr_read_d(&sV[vr]);
+        const u32x2 vraw = tr_read_d(Vs + vr);
         f32x4 vt;
         vt[0] = __uint_as_float(vraw[0] << 16);
         vt[1] = __uint_as_float(vraw[0] & 0xffff0000u);
@@ -426,32 +422,50 @@ __global__ __launch_bounds__(64) void dual_chain_kernel(DualParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) vt[r] = eta * (vt[r] - e[r]);
         const u32x2 VB = u32x2{pack2bf(vt[0], vt[1]), pack2bf(vt[2], vt[3])};
-
         // S~ += K^T V~ : K^T tile t (positions 16t..) through the transposing read
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int chunk = 8 * (t >> 1) + 2 * cq + (t & 1);
-            mma16(Sacc[t], tr_read_d(&sK[kr + 4 * (chunk ^ krs)]), VB);
+            mma16(Sacc[t], tr_read_d(Ks + kr + 4 * (chunk ^ krs)), VB);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) Sop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
         if (!ONESTEP) {
-            const int t1 = t0 + 16;
+            const int t1 = 16 * s16 + 16;
             if (t1 % mb == 0 || t1 >= L) {   // mini-batch end: W_{n+1} = S~
                 Wop[0] = Sop[0];
                 Wop[1] = Sop[1];
             }
         }
-
         // O^T += V~^T P^T, store O rows (4 consecutive columns per lane)
         mma16(o, VB, u32x2{pack2bf(pt[0], pt[1]) & pmask[0], pack2bf(pt[2], pt[3]) & pmask[1]});
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, u32x2{pack2bf(o[0], o[1]), pack2bf(o[2], o[3])}),
-                                              rO, vo, t0 * DV * 2, 0);
+                                              rO, vo, 16 * s16 * DV * 2, 0);
     };
 
-    static_assert(DEPTH >= 2 && DEPTH <= 16, "two to sixteen register sets");
-    for_sets<0, DEPTH>([&](auto SET) { load(decltype(SET)::value, SET); });
-    for (int s = 0; s < nrun; s += DEPTH) for_sets<0, DEPTH>([&](auto SET) { step(s + decltype(SET)::value, SET); });
+    // vmcnt of s_waitcnt (gfx9: bits 3..0 and 15..14): in iteration s, after
+    // stage s's loads this wave issued (DR_R - 2) stages of loads, 2 stores
+    // per finished iteration and the stores of iteration s - DR_R + 1, never
+    // fewer than (DR_R - 2) * DR_NL operations: waiting for that many left
+    // has stage s in LDS (memory operations of a wave complete in order)
+    constexpr int NW = (DR_R - 2) * DR_NL;
+    static_assert(NW <= 63, "vmcnt holds 6 bits");
+    constexpr int WAIT_STAGE = (NW & 15) | ((NW >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+#pragma unroll
+    for (int s = 0; s < DR_R - 1; ++s) issue(s, ring + s * DR_STAGE);
+    for (int s = 0; s < nst; ++s) {
+        __builtin_amdgcn_s_waitcnt(WAIT_STAGE);
+        const int rd = s % DR_R, wr = (s + DR_R - 1) % DR_R;
+        // the stage refilled here was read in iteration s - 1 (its reads were
+        // consumed there); this step's reads go through their own pointer
+        ring_step1(ring + wr * DR_STAGE, ring + rd * DR_STAGE,
+                   [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + DR_R - 1, dst); },
+                   [&](const bf16_t* X) __attribute__((always_inline)) {
+                       step(X, 0, 2 * s);
+                       step(X, 1, 2 * s + 1);
+                   });
+    }
+    __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));   // the clamped loads still in flight
 
     if (p.W_final) {
         float* Wf = p.W_final + (int64_t)bh * D * DV;
@@ -471,9 +485,9 @@ hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t s) {
     if (dtype == 1 && p.minibatch % 16 == 0) {
         // one wave per (b, h, 16-column tile)
         if (p.minibatch == 16)
-            hipLaunchKernelGGL((dual_chain_kernel<8, true>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+            hipLaunchKernelGGL((dual_ring_kernel<true>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
         else
-            hipLaunchKernelGGL((dual_chain_kernel<8, false>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+            hipLaunchKernelGGL((dual_ring_kernel<false>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
         return hipGetLastError();
     }
     const int grid = p.B * p.H;

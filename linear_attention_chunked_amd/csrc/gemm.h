@@ -221,7 +221,6 @@ struct Loop {
 // step st the loads of step st + 2 are issued right after the barrier that
 // ends everyone's reads of step st - 1, and step st's loads are waited for
 // (s_waitcnt vmcnt, own loads) just before that barrier.
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 TTT_DEV void dma16(const bf16_t* g, bf16_t* lds) {
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(g), (lds_void_t*)(lds), 16, 0, 0);

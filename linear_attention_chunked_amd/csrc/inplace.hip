@@ -758,6 +758,12 @@ bool inplace_supported(int dtype, int dk, int dv, int chunk) {
            dv >= IP_BN && (int64_t)dk * dv < (int64_t(1) << 31);
 }
 
+// 256 token rows of any operand stay below 2^31 bytes from a tile's first row
+bool inplace_strides_ok(int64_t q_row, int64_t k_row, int64_t v_row) {
+    const int64_t lim = (int64_t(1) << 31) / (2 * IP_BN);
+    return q_row < lim && k_row < lim && v_row < lim;
+}
+
 size_t inplace_workspace(int B, int H, int L, int dk, int dv, int chunk) {
     const int64_t N = (L + chunk - 1) / chunk;
     return (size_t)B * H * N * dk * dv * sizeof(bf16_t);

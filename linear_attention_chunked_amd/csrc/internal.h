@@ -76,6 +76,8 @@ hipError_t noalloc_scratch(void** ptr);
 // Chunk-causal forward for large fast weights (dk, dv multiples of 256, bf16):
 // update walk with bf16 W snapshots in `workspace`, then a batched readout.
 bool inplace_supported(int dtype, int dk, int dv, int chunk);
+// row strides (elements) the In-Place kernels address with 32-bit lane offsets
+bool inplace_strides_ok(int64_t q_row, int64_t k_row, int64_t v_row);
 size_t inplace_workspace(int B, int H, int L, int dk, int dv, int chunk);
 hipError_t launch_inplace(const TcParams& p, void* workspace, hipStream_t stream);
 

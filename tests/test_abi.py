@@ -94,6 +94,10 @@ def test_fwd_rejects_before_launch(lib):
     assert status(lib, fwd_args(dk=48)) == ERR_UNSUP
     assert status(lib, fwd_args(dv=256)) == ERR_UNSUP
     assert status(lib, fwd_args(mode=1, chunk=100)) == ERR_UNSUP
+    # the In-Place kernels address 256 token rows with 32-bit offsets
+    big = dict(mode=1, dk=256, dv=256, chunk=256, L=256, B=1, H=1)
+    assert status(lib, fwd_args(q_stride=(256 << 22, 256 << 22, 1 << 22), **big)) == ERR_UNSUP
+    assert status(lib, fwd_args(v_stride=(256 << 22, 256 << 22, 1 << 22), **big)) == ERR_UNSUP
     # out overlapping an input
     a = fwd_args()
     a.out = a.v

@@ -361,6 +361,17 @@ def test_dual_small(mb, L):
     check_dual(inp, run_dual(inp), [(0, 0), (0, 1)], TOL["bf16"], "dual")
 
 
+@pytest.mark.parametrize("mb,L", [(256, 1000), (512, 1500), (768, 1536), (4096, 8192), (2048, 2100), (32, 4100)])
+def test_dual_large_minibatch(mb, L):
+    """Mini-batches of many 16-token steps with ragged ends: the last
+    mini-batch partial (1000, 1500, 2100 tokens), the last 32-token ring
+    stage holding one step and a partial tail (4100 tokens, b = 32: one
+    stage per mini-batch) and a mini-batch of the whole sequence (8192)."""
+    inp = W.gen_dual(B=1, H=3, L=L, minibatch=mb)
+    say(f"dual bf16 b{mb} L{L}")
+    check_dual(inp, run_dual(inp), [(0, 0), (0, 1), (0, 2)], TOL["bf16"], f"dual b{mb} L{L}")
+
+
 @pytest.mark.parametrize("mb", [16, 40])
 def test_dual_fp32(mb):
     inp = W.gen_dual(B=1, H=2, L=256, minibatch=mb)
@@ -385,6 +396,20 @@ def test_dual_fixed_point_exact():
     torch.cuda.synchronize()
     assert oracle.rel_l2(out.cpu(), 0.5 * q) <= 1e-6
     assert oracle.rel_l2(Wf.cpu(), inp.W0) <= 1e-6
+
+
+@pytest.mark.parametrize("mb", [16, 2048])
+def test_dual_fixed_point_exact_bf16(mb):
+    """The same fixed point in bf16 (v = k W0 with W0 = I/2 is exact in
+    bf16): every corrected value is exactly zero, so out = q/2 and
+    W_final = W0 bit for bit, with one-step and with 128-step mini-batches."""
+    inp = W.gen_dual(B=1, H=2, L=4096, minibatch=mb)
+    k = inp.k
+    out, Wf = lac.dual_form_fwd(inp.q.to(DEV), k.to(DEV), (0.5 * k.float()).to(torch.bfloat16).to(DEV),
+                                inp.W0.to(DEV), eta=inp.eta, minibatch=mb, return_state=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), (0.5 * inp.q.float()).to(torch.bfloat16))
+    assert torch.equal(Wf.cpu(), inp.W0)
 
 
 # ------------------------------------------------------------- properties
