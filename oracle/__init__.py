@@ -70,6 +70,9 @@ def _load():
         lib.ttt_oracle_token_causal_bwd.argtypes = [i, i, i, i, i, _dp, _dp, _dp, _dp, d, d, _dp, _dp,
                                                     _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp, _dp]
         lib.ttt_oracle_token_causal_bwd.restype = None
+        lib.ttt_oracle_token_causal_dbeta.argtypes = [i, i, i, i, i, _dp, _dp, _dp, _dp, d, d, _dp, _dp,
+                                                      _dp, _dp, _dp]
+        lib.ttt_oracle_token_causal_dbeta.restype = None
         lib.ttt_oracle_threads.argtypes = []
         lib.ttt_oracle_threads.restype = ctypes.c_int
         _lib = lib
@@ -139,6 +142,23 @@ def token_causal_bwd(q, k, v, dout, eta=None, eta_scalar=0.0, beta=0.0, S0=None,
                                         _ptr(dSf), _ptr(dMf), _ptr(dq), _ptr(dkk), _ptr(dvv), _ptr(deta),
                                         _ptr(dS0), _ptr(dM0))
     return dq, dkk, dvv, deta, dS0, dM0
+
+
+def token_causal_dbeta(q, k, v, dout, eta=None, eta_scalar=0.0, beta=0.0, M0=None, dS_final=None,
+                       dM_final=None):
+    """dL/dbeta of ``token_causal`` (C, fp64) for L = <dout, out> +
+    <dS_final, S_final> + <dM_final, M_final>: the forward-mode derivative of
+    the momentum recurrence ([P1] paragraph on momentum; [P4] section
+    "가중치가 두 종류라는 점" trains through the updates).  Returns [B,H]."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    eta, M0, dSf, dMf = _f64(eta), _f64(M0), _f64(dS_final), _f64(dM_final)
+    out = np.empty((B, H))
+    _load().ttt_oracle_token_causal_dbeta(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                          float(eta_scalar), float(beta), _ptr(M0), _ptr(dout), _ptr(dSf),
+                                          _ptr(dMf), _ptr(out))
+    return out
 
 
 def dual_primal(q, k, v, W0, eta, minibatch):

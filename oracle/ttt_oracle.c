@@ -321,6 +321,71 @@ void ttt_oracle_token_causal_bwd(int B, int H, int L, int dk, int dv,
     }
 }
 
+/*
+ * Derivative of the token-causal forward with respect to the momentum
+ * coefficient beta, taken in forward mode: every line of the recurrence of
+ * ttt_oracle_token_causal is differentiated with respect to beta.  [P1]
+ * (paragraph on momentum) makes beta part of the update; [P4] (section on the
+ * two kinds of weights) trains such parameters through the inner updates,
+ * which needs dL/dbeta.  The pages print no backward pass; this is the plain
+ * derivative.  With g_t = eta_t k_t^T v_t:
+ *     m_t  = beta m_{t-1} + g_t            m'_t = beta m'_{t-1} + m_{t-1}
+ *     S_t  = S_{t-1} + m_t                 S'_t = S'_{t-1} + m'_t
+ *     o_t  = q_t S_t                       o'_t = q_t S'_t
+ * from m_{-1} = M0, m'_{-1} = S'_{-1} = 0 (S0 does not depend on beta), and
+ *     dbeta = sum_t <dout_t, o'_t> + <dS_final, S'_{L-1}> + <dM_final, m'_{L-1}>
+ * (dS_final, dM_final NULL: zero).  dbeta is [B,H].
+ */
+void ttt_oracle_token_causal_dbeta(int B, int H, int L, int dk, int dv,
+                                   const double* q, const double* k, const double* v,
+                                   const double* eta, double eta_scalar, double beta,
+                                   const double* M0, const double* dout,
+                                   const double* dS_final, const double* dM_final, double* dbeta)
+{
+    const long nbh = (long)B * H;
+    const long sz = (long)dk * dv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long bh = 0; bh < nbh; ++bh) {
+        double* m = (double*)malloc(sizeof(double) * sz);
+        double* mt = (double*)malloc(sizeof(double) * sz);   /* m' */
+        double* St = (double*)malloc(sizeof(double) * sz);   /* S' */
+        for (long e = 0; e < sz; ++e) {
+            m[e] = M0 ? M0[bh * sz + e] : 0.0;
+            mt[e] = 0.0;
+            St[e] = 0.0;
+        }
+        double acc = 0.0;
+        for (int t = 0; t < L; ++t) {
+            const double* qt = q + (bh * L + t) * dk;
+            const double* kt = k + (bh * L + t) * dk;
+            const double* vt = v + (bh * L + t) * dv;
+            const double* dot = dout + (bh * L + t) * dv;
+            const double et = eta ? eta[bh * L + t] : eta_scalar;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) {
+                    const long e = (long)i * dv + j;
+                    mt[e] = beta * mt[e] + m[e];          /* uses m_{t-1} */
+                    m[e] = beta * m[e] + et * kt[i] * vt[j];
+                    St[e] += mt[e];
+                }
+            /* <dout_t, q_t S'_t> */
+            for (int j = 0; j < dv; ++j) {
+                double o = 0.0;
+                for (int i = 0; i < dk; ++i) o += qt[i] * St[(long)i * dv + j];
+                acc += dot[j] * o;
+            }
+        }
+        for (long e = 0; e < sz; ++e) {
+            if (dS_final) acc += dS_final[bh * sz + e] * St[e];
+            if (dM_final) acc += dM_final[bh * sz + e] * mt[e];
+        }
+        dbeta[bh] = acc;
+        free(m);
+        free(mt);
+        free(St);
+    }
+}
+
 /* Number of host threads the OpenMP loops above use (for reporting). */
 #ifdef _OPENMP
 #include <omp.h>

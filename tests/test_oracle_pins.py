@@ -584,6 +584,88 @@ def test_bwd_single_token_closed_form(oracle_mod):
     close(dS0[0, 0], D)
 
 
+# ----------------------------------------------------------------- dL/dbeta
+@pytest.mark.parametrize("beta", [0.0, 0.3, 0.9])
+def test_dbeta_finite_differences(oracle_mod, beta):
+    """dL/dbeta against central differences of the forward oracle's
+    objective in beta (a polynomial of degree L in beta: with h = 1e-5 the
+    difference is exact up to O(h^2) and rounding), with M0, dS_final and
+    dM_final all present."""
+    rng = np.random.default_rng(51)
+    q, k, v, eta, S0, M0, dout, dSf, dMf = _bwd_case(0.5, rng, B=2, H=2, L=7, dk=3, dv=4)
+    got = oracle_mod.token_causal_dbeta(q, k, v, dout, eta, 0.0, beta, M0, dSf, dMf)
+    h = 1e-5
+    for b in range(2):
+        for hh in range(2):
+            sl = lambda a: None if a is None else a[b:b + 1, hh:hh + 1]
+            f = lambda be: _objective(oracle_mod, be, sl(dout), sl(dSf), sl(dMf), sl(q), sl(k), sl(v), sl(eta),
+                                      sl(S0), sl(M0))
+            fd = (f(beta + h) - f(beta - h)) / (2 * h)
+            assert abs(fd - got[b, hh]) <= 1e-7 * max(1.0, abs(fd)), (b, hh, fd, got[b, hh])
+
+
+def test_dbeta_matches_autograd(oracle_mod):
+    """PyTorch autograd with beta as a leaf tensor, through a plain fp64 loop
+    of the recurrence written here."""
+    rng = np.random.default_rng(52)
+    q, k, v, eta, S0, M0, dout, dSf, dMf = _bwd_case(0.8, rng, B=2, H=3, L=10, dk=4, dv=5)
+    beta = torch.tensor(0.8, dtype=torch.float64, requires_grad=True)
+    S = torch.tensor(S0)
+    m = torch.tensor(M0)
+    Tq, Tk, Tv, Te = (torch.tensor(a) for a in (q, k, v, eta))
+    outs = []
+    for t in range(q.shape[2]):
+        m = beta * m + Te[:, :, t, None, None] * Tk[:, :, t, :, None] * Tv[:, :, t, None, :]
+        S = S + m
+        outs.append(torch.einsum("bhi,bhij->bhj", Tq[:, :, t], S))
+    out = torch.stack(outs, dim=2)
+    per_head = ((out * torch.tensor(dout)).sum(dim=(2, 3)) + (S * torch.tensor(dSf)).sum(dim=(2, 3))
+                + (m * torch.tensor(dMf)).sum(dim=(2, 3)))
+    want = np.array([[torch.autograd.grad(per_head[b, h], beta, retain_graph=True)[0].item()
+                      for h in range(per_head.shape[1])] for b in range(per_head.shape[0])])
+    close(oracle_mod.token_causal_dbeta(q, k, v, dout, eta, 0.0, 0.8, M0, dSf, dMf), want, 1e-11)
+
+
+def test_dbeta_equals_adjoint_sum(oracle_mod):
+    """The reverse-mode form of the same derivative: dL/dbeta =
+    sum_t <A_t, m_{t-1}>, A_t the adjoint of m_t from the backward oracle's
+    own sweep (A_t = dL/dm_t: its value at t = 0, times beta, is dM0), here
+    run as a Python loop over stored momenta."""
+    rng = np.random.default_rng(53)
+    beta = 0.6
+    q, k, v, eta, S0, M0, dout, dSf, dMf = _bwd_case(beta, rng, B=1, H=2, L=8, dk=3, dv=2)
+    B, H, L, dk = q.shape
+    want = np.zeros((B, H))
+    for b in range(B):
+        for h in range(H):
+            m = [M0[b, h]]
+            for t in range(L):
+                m.append(beta * m[-1] + eta[b, h, t] * np.outer(k[b, h, t], v[b, h, t]))
+            Sa, A = dSf[b, h].copy(), dMf[b, h].copy()
+            for t in range(L - 1, -1, -1):
+                Sa = Sa + np.outer(q[b, h, t], dout[b, h, t])
+                A = A + Sa                       # dL/dm_t
+                want[b, h] += np.sum(A * m[t])   # m[t] is m_{t-1}
+                A = beta * A
+            close(A, oracle_mod.token_causal_bwd(q, k, v, dout, eta, 0.0, beta, S0, M0, dSf, dMf)[5][b, h], 1e-12)
+    close(oracle_mod.token_causal_dbeta(q, k, v, dout, eta, 0.0, beta, M0, dSf, dMf), want, 1e-12)
+
+
+def test_dbeta_single_token_closed_form(oracle_mod):
+    """L = 1: m_0 = beta M0 + g_0, S_0 = S0 + m_0, so dS_0/dbeta = dm_0/dbeta =
+    M0 and dL/dbeta = q M0 do^T + <dS_final + dM_final, M0>.  Without M0 (or
+    with zero cotangents and do) it is exactly zero."""
+    rng = np.random.default_rng(54)
+    dk, dv = 4, 3
+    q, k, v = rnd(1, 1, 1, dk, rng=rng), rnd(1, 1, 1, dk, rng=rng), rnd(1, 1, 1, dv, rng=rng)
+    M0, dSf, dMf, dout = (rnd(1, 1, dk, dv, rng=rng), rnd(1, 1, dk, dv, rng=rng), rnd(1, 1, dk, dv, rng=rng),
+                          rnd(1, 1, 1, dv, rng=rng))
+    got = oracle_mod.token_causal_dbeta(q, k, v, dout, None, 0.4, 0.7, M0, dSf, dMf)
+    want = q[0, 0, 0] @ M0[0, 0] @ dout[0, 0, 0] + np.sum((dSf + dMf)[0, 0] * M0[0, 0])
+    close(got[0, 0], want)
+    assert oracle_mod.token_causal_dbeta(q, k, v, dout, None, 0.4, 0.7, None, dSf, dMf)[0, 0] == 0.0
+
+
 # ----------------------------------------------------------------- In-Place front end
 def test_gated_input_vs_torch(oracle_mod):
     """Z = silu(X Wg^T) (X Wu^T) against torch's silu and linear in fp64, and
