@@ -14,6 +14,7 @@
  *   ttt_decode_step       one recurrent token per sequence (inference):
  *                         state update and readout with the state in HBM
  *   ttt_bwd_chunked       backward pass of the token-causal forward
+ *   ttt_bwd_dbeta         gradient of the momentum coefficient
  *   ttt_inplace_*         In-Place TTT front end: gated input Z, LM-aligned
  *                         target V-hat, clipped per-token rates
  *
@@ -316,7 +317,7 @@ ttt_status_t ttt_decode_step(int32_t B, int32_t H, int32_t dk, int32_t dv, int32
  *     deta_t = k_t A_t v_t^T (per token, also for a scalar eta: its gradient
  *     is the sum over tokens),  dS0 = dL/dS0,  dM0 = beta A_0.
  * Every beta in [0, 1) is handled without dividing by beta.  The gradient
- * with respect to beta is not computed.
+ * with respect to beta comes from ttt_bwd_dbeta (same inputs).
  *
  * All tensors are contiguous: q, k, dq, dk [B,H,L,dk]; v, dout, dv
  * [B,H,L,dv] in `dtype`; eta [B,H,L] fp32 or NULL (eta_scalar); S0, M0,
@@ -346,6 +347,38 @@ ttt_status_t ttt_bwd_chunked(int32_t B, int32_t H, int32_t L, int32_t dk, int32_
                              const float* dS_final, const float* dM_final,
                              void* dq, void* dk_out, void* dv_out, float* deta, float* dS0, float* dM0,
                              void* workspace, size_t workspace_bytes, void* stream, void* side_stream);
+
+/*
+ * ttt_bwd_dbeta -- dL/dbeta, the gradient of the momentum coefficient, for
+ * the token-causal forward with momentum ([P1] paragraph on momentum: the
+ * update m_t = beta m_{t-1} + g_t; [P4] section on the two kinds of weights:
+ * the outer model learns through the inner updates, beta included when it
+ * is learned).  For L = sum_t <dout_t, o_t> + <dS_final, S_final> +
+ * <dM_final, M_final> it returns, per (b, h),
+ *     dbeta = sum_t q_t S'_t dout_t^T + <dS_final, S'_{L-1}> + <dM_final, m'_{L-1}>
+ * with the derivatives of the states m'_t = beta m'_{t-1} + m_{t-1},
+ * S'_t = S'_{t-1} + m'_t (from zero), i.e. the plain derivative of the
+ * recurrence; S0 does not enter.  It is a call of its own beside
+ * ttt_bwd_chunked (same inputs, same layouts: contiguous q, k [B,H,L,dk],
+ * v, dout [B,H,L,dv] in dtype, eta [B,H,L] fp32 or NULL (eta_scalar), M0,
+ * dS_final, dM_final fp32 [B,H,dk,dv] or NULL = zero).  Any beta in [0, 1)
+ * (the derivative at beta = 0 is defined too).  Output dbeta: fp32 [B,H],
+ * written in full; the sum over columns and tokens is taken in a fixed
+ * order (repeated calls agree bit for bit).  workspace: device memory of
+ * ttt_bwd_dbeta_workspace_size bytes, caller-owned, overwritten.
+ * Supported: dk in {32, 64, 128}, dv a multiple of 16 up to 1024, a head's
+ * rows below 2^31 bytes.  Errors (before anything is enqueued):
+ * TTT_ERR_NULL, TTT_ERR_DTYPE, TTT_ERR_SHAPE, TTT_ERR_VALUE (beta),
+ * TTT_ERR_ALIGN (16 bytes), TTT_ERR_UNSUPPORTED, TTT_ERR_WORKSPACE,
+ * TTT_ERR_ALIAS (dbeta or the workspace overlapping an input or each
+ * other); TTT_ERR_HIP if a launch fails.  Runs on `stream`.
+ */
+ttt_status_t ttt_bwd_dbeta_workspace_size(int32_t B, int32_t H, int32_t dv, size_t* bytes);
+ttt_status_t ttt_bwd_dbeta(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,
+                           const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                           float beta, const float* M0, const void* dout, const float* dS_final,
+                           const float* dM_final, float* dbeta, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /*
  * In-Place TTT front end ([P2] "In-Place 테스트 시점 학습: LLM을 위한 원활한

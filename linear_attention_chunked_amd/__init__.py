@@ -96,6 +96,11 @@ def load_library():
     lib.ttt_bwd_chunked.argtypes = [i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, f32, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp, _vp]
     lib.ttt_bwd_chunked.restype = ctypes.c_int
+    lib.ttt_bwd_dbeta_workspace_size.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ttt_bwd_dbeta_workspace_size.restype = ctypes.c_int
+    lib.ttt_bwd_dbeta.argtypes = [i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, f32, _vp, _vp, _vp, _vp,
+                                  _vp, _vp, ctypes.c_size_t, _vp]
+    lib.ttt_bwd_dbeta.restype = ctypes.c_int
     sz = ctypes.POINTER(ctypes.c_size_t)
     lib.ttt_inplace_gated_input.argtypes = [i32, i32, i32, _vp, _vp, _vp, _vp, _vp]
     lib.ttt_inplace_gated_input.restype = ctypes.c_int
@@ -383,6 +388,36 @@ def bwd_chunked(q, k, v, dout, *, eta=None, eta_scalar=0.0, beta=0.0, S0=None, M
                                _ptr(ws), wsb, _stream(stream),
                                None if side_stream is None else ctypes.c_void_p(side_stream.cuda_stream)))
     return dq, dk_, dv_, deta, dS0, dM0
+
+
+def bwd_dbeta(q, k, v, dout, *, eta=None, eta_scalar=0.0, beta=0.0, M0=None, dS_final=None, dM_final=None,
+              stream=None):
+    """dL/dbeta of the token-causal momentum forward (``ttt_bwd_dbeta``):
+    the same inputs and layouts as ``bwd_chunked``; returns fp32 [B,H]."""
+    lib = load_library()
+    _require_gpu(q, k, v, dout, eta, M0, dS_final, dM_final)
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,L,dk]")
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape != (B, H, L, dv) or dout.shape != v.shape:
+        raise ValueError("k must match q; v and dout must be [B,H,L,dv]")
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+        if not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{nm} must be contiguous and of q's dtype")
+    st = (B, H, dk, dv)
+    for t, nm, shp in ((eta, "eta", (B, H, L)), (M0, "M0", st), (dS_final, "dS_final", st),
+                       (dM_final, "dM_final", st)):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.shape != shp):
+            raise ValueError(f"{nm} must be contiguous fp32 {list(shp)}")
+    n = ctypes.c_size_t(0)
+    _check(lib.ttt_bwd_dbeta_workspace_size(B, H, dv, ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 16), dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check(lib.ttt_bwd_dbeta(B, H, L, dk, dv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                             float(eta_scalar), float(beta), _ptr(M0), _ptr(dout), _ptr(dS_final), _ptr(dM_final),
+                             _ptr(out), _ptr(ws), n.value, _stream(stream)))
+    return out
 
 
 def _bf16_contig(*pairs):

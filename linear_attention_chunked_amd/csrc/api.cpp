@@ -530,6 +530,58 @@ bool disjoint(const void* o, size_t no, std::initializer_list<std::pair<const vo
 constexpr int kMaxConvTaps = 16;
 }  // namespace
 
+ttt_status_t ttt_bwd_dbeta_workspace_size(int32_t B, int32_t H, int32_t dv, size_t* bytes) {
+    if (!bytes) return TTT_ERR_NULL;
+    if (!shape_ok(B, H, 1, {dv})) return TTT_ERR_SHAPE;
+    if (dv % 16 != 0) return TTT_ERR_UNSUPPORTED;
+    *bytes = ttt::dbeta_workspace(B, H, dv);
+    return TTT_OK;
+}
+
+ttt_status_t ttt_bwd_dbeta(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype, const void* q,
+                           const void* k, const void* v, const float* eta, float eta_scalar, float beta,
+                           const float* M0, const void* dout, const float* dS_final, const float* dM_final,
+                           float* dbeta, void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
+    if (!shape_ok(B, H, L, {dk, dv})) return TTT_ERR_SHAPE;
+    if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_VALUE;
+    if (!ttt::dbeta_supported(dtype, dk, dv)) return TTT_ERR_UNSUPPORTED;
+    const size_t es = esize(dtype);
+    // a head's rows are addressed with 32-bit byte offsets
+    if ((uint64_t)L * (uint64_t)std::max(dk, dv) * es >= (uint64_t(1) << 31)) return TTT_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !dout || !dbeta) return TTT_ERR_NULL;
+    const size_t need = ttt::dbeta_workspace(B, H, dv);
+    if (!workspace || workspace_bytes < need) return TTT_ERR_WORKSPACE;
+    const size_t nq = (size_t)B * H * L * dk * es, nv = (size_t)B * H * L * dv * es;
+    const size_t ne = (size_t)B * H * L * 4, ns = (size_t)B * H * dk * dv * 4, nb = (size_t)B * H * 4;
+    for (const void* b : {q, k, v, dout, (const void*)eta, (const void*)M0, (const void*)dS_final,
+                          (const void*)dM_final, (const void*)dbeta, (const void*)workspace})
+        if (b && !aligned16(b)) return TTT_ERR_ALIGN;
+    const std::initializer_list<std::pair<const void*, size_t>> ins = {
+        {q, nq}, {k, nq}, {v, nv}, {dout, nv}, {eta, ne}, {M0, ns}, {dS_final, ns}, {dM_final, ns}};
+    if (!disjoint(dbeta, nb, ins) || !disjoint(workspace, need, ins) || !disjoint(dbeta, nb, {{workspace, need}}))
+        return TTT_ERR_ALIAS;
+    ttt::DbetaParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.dout = dout;
+    p.eta = eta;
+    p.eta_scalar = eta_scalar;
+    p.M0 = M0;
+    p.dS_final = dS_final;
+    p.dM_final = dM_final;
+    p.partial = reinterpret_cast<float*>(workspace);
+    p.dbeta = dbeta;
+    p.B = B;
+    p.H = H;
+    p.L = L;
+    p.dk = dk;
+    p.dv = dv;
+    return from_hip(ttt::launch_dbeta(p, dtype, beta, reinterpret_cast<hipStream_t>(stream)));
+}
+
+
 ttt_status_t ttt_inplace_gated_input(int32_t T, int32_t d_model, int32_t d_ff, const void* X, const void* Wg,
                                      const void* Wu, void* Z, void* stream) {
     if (!shape_ok(1, 1, T, {d_model, d_ff})) return TTT_ERR_SHAPE;

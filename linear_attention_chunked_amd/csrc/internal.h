@@ -103,6 +103,29 @@ struct DualParams {
 hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t stream);
 bool dual_supported(int dtype, int d, int dv, int minibatch);
 
+// dL/dbeta of the token-causal momentum forward (contiguous tensors).
+struct DbetaParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* dout;
+    const float* eta;          // [B,H,L] or null (eta_scalar)
+    float eta_scalar;
+    const float* M0;           // [B,H,dk,dv] or null
+    const float* dS_final;     // [B,H,dk,dv] or null
+    const float* dM_final;     // [B,H,dk,dv] or null
+    float* partial;            // [B*H][dv/16] workspace
+    float* dbeta;              // [B,H]
+    int B, H, L, dk, dv;
+    // weight tables filled by launch_dbeta: beta^d, d beta^(d-1),
+    // F(d) = sum_{e<=d} e beta^(e-1) (d <= 16), beta (1 + .. + beta^i) (i < 16)
+    float bp[17], f1[17], F[17], bw[16];
+    float lb[3][16];   // the last block's token weights (bp, f1, F at n - 1 - j)
+};
+bool dbeta_supported(int dtype, int dk, int dv);
+size_t dbeta_workspace(int B, int H, int dv);
+hipError_t launch_dbeta(DbetaParams p, int dtype, float beta, hipStream_t stream);
+
 // Recurrent decode step (one token per (b, h), state in place).
 struct DecodeParams {
     const void* q;

@@ -55,6 +55,12 @@ bool decode_supported(int, int dk, int dv) { return dk >= 1 && dk <= 1024 && dv 
 bool bwd_supported(int, int dk, int dv) { return tc_fwd_supported(0, 0, dk, dv, 64); }
 size_t bwd_workspace(int B, int H, int, int dk, int dv, int, bool mom) { return mom ? (size_t)4 * B * H * dk * dv * 4 : 0; }
 hipError_t launch_bwd(const BwdParams&, hipStream_t, hipStream_t) { return hipSuccess; }
+bool dbeta_supported(int dtype, int dk, int dv) {
+    return (dtype == 0 || dtype == 1) && (dk == 32 || dk == 64 || dk == 128) && dv % 16 == 0 && dv >= 16 &&
+           dv <= 1024;
+}
+size_t dbeta_workspace(int B, int H, int dv) { return (size_t)B * H * (dv / 16) * 4; }
+hipError_t launch_dbeta(DbetaParams, int, float, hipStream_t) { return hipSuccess; }
 bool fe_gemm_supported(int K, int rows) { return K % 128 == 0 && rows % 128 == 0; }
 hipError_t launch_fe_gemm(const FeGemmParams&, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_fe_conv(const FeConvParams&, hipStream_t) { return hipSuccess; }

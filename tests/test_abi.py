@@ -286,6 +286,34 @@ def test_bwd_rejects_before_launch(lib):
     assert lib.ttt_bwd_workspace_size(2, 2, 64, 64, 64, 1, ctypes.c_float(0.0), None) == ERR_NULL
 
 
+def test_dbeta_rejects_before_launch(lib):
+    f = lib.ttt_bwd_dbeta
+    f.argtypes = None
+    n = 2 * 2 * 64 * 64 * 2       # bytes of one [2,2,64,64] bf16 tensor
+
+    def args(**kw):
+        base = [FAKE + i * (n + 4096) for i in range(12)]
+        return [2, 2, 64, kw.get("dk", 64), kw.get("dv", 64), kw.get("dtype", 1),
+                ctypes.c_void_p(kw.get("q", base[0])), ctypes.c_void_p(base[1]), ctypes.c_void_p(base[2]), None,
+                ctypes.c_float(0.1), ctypes.c_float(kw.get("beta", 0.9)), None, ctypes.c_void_p(base[3]), None, None,
+                ctypes.c_void_p(kw.get("dbeta", base[4])), ctypes.c_void_p(kw.get("ws", base[5])),
+                ctypes.c_size_t(kw.get("wsb", 64)), None]
+    assert f(*args(dtype=4)) == ERR_DTYPE
+    assert f(*args(beta=1.0)) == ERR_VALUE
+    assert f(*args(beta=-0.5)) == ERR_VALUE
+    assert f(*args(dk=48)) == ERR_UNSUP
+    assert f(*args(dv=40)) == ERR_UNSUP
+    assert f(*args(q=0)) == ERR_NULL
+    assert f(*args(dbeta=0)) == ERR_NULL
+    assert f(*args(q=FAKE + 8)) == ERR_ALIGN
+    assert f(*args(wsb=4)) == ERR_WS
+    assert f(*args(dbeta=FAKE + 256)) == ERR_ALIAS        # output inside q
+    assert f(*args(ws=FAKE + 4 * (n + 4096))) == ERR_ALIAS   # workspace on top of dbeta
+    ws = ctypes.c_size_t(0)
+    assert lib.ttt_bwd_dbeta_workspace_size(2, 2, 64, ctypes.byref(ws)) == OK and ws.value == 2 * 2 * 4 * 4
+    assert lib.ttt_bwd_dbeta_workspace_size(2, 2, 64, None) == ERR_NULL
+
+
 def test_frontend_rejects_before_launch(lib):
     n = 1 << 24
     g = lib.ttt_inplace_gated_input

@@ -192,3 +192,90 @@ def test_bwd_matches_forward_linearisation():
     dq = run_gpu(q, k, v, dout, eta, 0.0, S0, None)[0]
     an = float((dq.double() * u.double()).sum())
     assert abs(fd - an) <= 1e-4 * max(1.0, abs(an)), (fd, an)
+
+
+# ------------------------------------------------------------------ dL/dbeta
+def run_dbeta(q, k, v, dout, eta, eta_scalar, beta, M0, dSf, dMf):
+    res = lac.bwd_dbeta(dev(q), dev(k), dev(v), dev(dout), eta=dev(eta), eta_scalar=eta_scalar, beta=beta,
+                        M0=dev(M0), dS_final=dev(dSf), dM_final=dev(dMf))
+    torch.cuda.synchronize()
+    return res.cpu().double().numpy()
+
+
+def oracle_dbeta(q, k, v, dout, eta, eta_scalar, beta, M0, dSf, dMf):
+    return oracle.token_causal_dbeta(W.to_f64(q), W.to_f64(k), W.to_f64(v), W.to_f64(dout), W.to_f64(eta),
+                                     eta_scalar, beta, W.to_f64(M0), W.to_f64(dSf), W.to_f64(dMf))
+
+
+# rel-L2 over the (b, h) values: fp32 inputs run fp32 MFMA (1e-4: the
+# tangent state S' grows like t^2 and its readout sums L tokens); bf16 inputs
+# read the three states through bf16 copies, one rounding each (2e-2)
+DBETA_TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("L,dk,dv,beta", [(150, 64, 64, 0.9), (300, 128, 64, 0.5), (77, 32, 128, 0.9),
+                                          (256, 128, 128, 0.0), (33, 64, 32, 0.99), (16, 32, 16, 0.7)])
+def test_dbeta_small(dtype, L, dk, dv, beta):
+    """Ragged lengths (a partial last block, an empty second block of the
+    last 32-token stage, a single block), every supported dk, dv from 16 to
+    128, beta from 0 to 0.99; per-token eta, M0, dS_final and dM_final all
+    given."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    beta = W.f32(beta)
+    q, k, v, dout, eta, S0, dSf = make(2, 3, L, dk, dv, tdt, seed=L + dk + dv)
+    g = torch.Generator().manual_seed(L)
+    M0 = 0.01 * torch.randn(S0.shape, generator=g)
+    dMf = 0.05 * torch.randn(S0.shape, generator=g)
+    got = run_dbeta(q, k, v, dout, eta, 0.0, beta, M0, dSf, dMf)
+    ref = oracle_dbeta(q, k, v, dout, eta, 0.0, beta, M0, dSf, dMf)
+    err = oracle.rel_l2(torch.tensor(got), ref)
+    say(f"dbeta {dtype} L{L} dk{dk} dv{dv} beta {beta:g}: rel-L2 {err:.2e}")
+    assert err <= DBETA_TOL[dtype], err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dbeta_scalar_eta_no_states(dtype):
+    """Scalar eta, no M0 and no final-state cotangents (all zero)."""
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q, k, v, dout, _, _, _ = make(1, 2, 200, 64, 64, tdt, seed=9, per_token=False, s0=False, dsf=False)
+    got = run_dbeta(q, k, v, dout, None, W.f32(0.05), W.f32(0.8), None, None, None)
+    ref = oracle_dbeta(q, k, v, dout, None, W.f32(0.05), W.f32(0.8), None, None, None)
+    assert oracle.rel_l2(torch.tensor(got), ref) <= DBETA_TOL[dtype]
+
+
+def test_dbeta_integer_exact_at_zero():
+    """At beta = 0 every weight is 0 or 1, so small integers with eta = 1/8
+    keep every product and sum exact in fp32: bit-identical to the oracle."""
+    g = torch.Generator().manual_seed(29)
+    B, H, L, d = 1, 2, 70, 32
+    q, k, v, dout = (torch.randint(-2, 3, (B, H, L, d), generator=g).float() for _ in range(4))
+    M0, dSf, dMf = (torch.randint(-2, 3, (B, H, d, d), generator=g).float() for _ in range(3))
+    got = run_dbeta(q, k, v, dout, None, 0.125, 0.0, M0, dSf, dMf)
+    ref = oracle_dbeta(q, k, v, dout, None, 0.125, 0.0, M0, dSf, dMf)
+    assert np.array_equal(got, ref), (got, ref)
+
+
+def test_dbeta_repeat_bit_identical():
+    """The column-tile sums are added in a fixed order: repeated calls agree
+    bit for bit."""
+    q, k, v, dout, eta, _, dSf = make(2, 2, 500, 128, 128, torch.bfloat16, seed=12)
+    a = run_dbeta(q, k, v, dout, eta, 0.0, W.f32(0.9), None, dSf, None)
+    b = run_dbeta(q, k, v, dout, eta, 0.0, W.f32(0.9), None, dSf, None)
+    assert np.array_equal(a, b)
+
+
+def test_dbeta_momentum_shape_sampled_heads():
+    """The momentum workload's shape (B4 H8 L16384 d128, bf16, eta 0.05,
+    beta 0.9) with seeded cotangents; sampled heads recomputed by the oracle."""
+    inp = W.gen_momentum()
+    dout, dSf = W.gen_lm_scale_cotangents(4, 8, 16384, 128, seed_base=4000)
+    say("dbeta momentum shape: running")
+    got = run_dbeta(inp.q, inp.k, inp.v, dout, None, inp.eta_scalar, inp.beta, None, dSf, None)
+    for b, h in ((0, 0), (3, 7)):
+        sl = lambda t: None if t is None else t[b:b + 1, h:h + 1]
+        ref = oracle_dbeta(sl(inp.q), sl(inp.k), sl(inp.v), sl(dout), None, inp.eta_scalar, inp.beta, None,
+                           sl(dSf), None)
+        err = abs(got[b, h] - ref[0, 0]) / abs(ref[0, 0])
+        say(f"dbeta momentum head ({b},{h}): {got[b, h]:.6e} vs {ref[0, 0]:.6e} rel {err:.2e}")
+        assert err <= DBETA_TOL["bf16"], err
