@@ -61,6 +61,7 @@ KERNEL_SOURCES = {
     "tcb_fwd_kernel+bwd_scale_kernels": ("tcb_fwd.hip", "bwd.hip", "common.h"),
     "swiglu_kernels": ("swiglu.hip", "gemm.h", "common.h"),
     "state_scan_kernel": ("scan.hip", "common.h"),
+    "dbeta_kernel": ("dbeta.hip", "common.h"),
 }
 
 
@@ -198,6 +199,37 @@ def setup_workload(name: str, dev: str):
                     beta=inp.beta, eta="per-token" if eta is not None else inp.eta_scalar, dtype="bf16",
                     tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
                     kernel="tcb_fwd_kernel+bwd_scale_kernels", inputs=None, cpu_sample=cpu_sample)
+        return step, info
+    if name == "bwd-dbeta":
+        # dL/dbeta on the momentum shape (beside the momentum backward)
+        inp = W.gen_momentum()
+        B, H, L, dk = inp.q.shape
+        dv = inp.v.shape[-1]
+        dout, dSf = W.gen_lm_scale_cotangents(B, H, L, dk, seed_base=4000)
+        q, k, v, do, dS = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), dout.to(dev), dSf.to(dev)
+
+        def step():
+            return lac.bwd_dbeta(q, k, v, do, eta_scalar=inp.eta_scalar, beta=inp.beta, dS_final=dS)
+
+        # every column tile reads the full q and k rows (the algorithmic count
+        # reads each tensor once): q, k, v, dout, dS_final
+        bytes_alg = B * H * L * (2 * dk + 2 * dv) * 2 + B * H * dk * dv * 4
+        # per token: 3 state readouts and 3 weighted aggregates (2 dk dv each),
+        # the scores q . k and do . v against the 16 tokens of its block
+        # (each product counted once; the kernel recomputes the scores per
+        # 16-column tile)
+        flop_alg = B * H * L * (12 * dk * dv + 2 * 16 * (dk + dv))
+        def cpu_sample():
+            import oracle
+            sl = lambda t: None if t is None else W.to_f64(t[:1, :4])
+            oracle.token_causal_dbeta(sl(inp.q), sl(inp.k), sl(inp.v), sl(dout), None, inp.eta_scalar, inp.beta,
+                                      None, sl(dSf), None)
+            return (4 * L / H, f"4 of {B * H} (b,h) heads, full L={L}, fp64 tangent recurrence in C "
+                    "(tokens scaled by the head fraction)", oracle.threads())
+
+        info = dict(workload=name, B=B, H=H, L=L, dk=dk, dv=dv, mode="token_causal dL/dbeta", beta=inp.beta,
+                    eta=inp.eta_scalar, dtype="bf16", tokens=B * L, bytes_alg=bytes_alg, flop_alg=flop_alg,
+                    kernel="dbeta_kernel", inputs=None, cpu_sample=cpu_sample)
         return step, info
     if name == "inplace-frontend":
         T, dm, dff, taps, C = 32768, 2560, 9728, 4, 1024
@@ -412,7 +444,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="inplace-128k",
                     help="inplace-128k (default), lm-scale, small-f32, inplace-32k, momentum, dual-b16, "
-                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, inplace-frontend, swiglu, swiglu-mse, "
+                         "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, bwd-dbeta, inplace-frontend, swiglu, swiglu-mse, "
                          "scan, scan-momentum")
     ap.add_argument("--no-evict", action="store_true",
                     help="do not write the 512 MiB eviction buffer between timed steps")

@@ -35,7 +35,7 @@ FLAGS = [
 # (no v_accvgpr reads before each VALU use of a result).  Only for code that
 # uses no 16x16x16 MFMA: for that form the compiler left too few wait states
 # between the MFMA and a VALU read of its result.
-VGPR_FORM = {"dual.hip"}
+VGPR_FORM = {"dual.hip", "dbeta.hip"}
 
 
 def _compile(src: str) -> str:
