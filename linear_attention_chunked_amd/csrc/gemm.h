@@ -314,14 +314,13 @@ struct DLoop {
         bf16_t* sA = smem;
         bf16_t* sB = smem + NB * OA::BUF;
         const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-        auto issue = [&](int st) __attribute__((always_inline)) {
-            const int s = min(st, steps - 1), buf = st % NB;
-            a.load(s, sA + buf * OA::BUF);
-            b.load(s, sB + buf * OB::BUF);
+        // loads of step st into the stage buffers wa, wb
+        auto issue = [&](int st, bf16_t* wa, bf16_t* wb) __attribute__((always_inline)) {
+            const int s = min(st, steps - 1);
+            a.load(s, wa);
+            b.load(s, wb);
         };
-        auto compute = [&](int buf) __attribute__((always_inline)) {
-            const bf16_t* A = sA + buf * OA::BUF;
-            const bf16_t* B = sB + buf * OB::BUF;
+        auto compute = [&](const bf16_t* A, const bf16_t* B) __attribute__((always_inline)) {
 #pragma unroll
             for (int kk = 0; kk < GM_BK; kk += 16) {
                 bf16x8 af[TI], bfr[TJ];
@@ -338,14 +337,17 @@ struct DLoop {
         // vmcnt field of s_waitcnt on gfx9: bits 3..0 and 15..14; lgkmcnt and
         // expcnt left at their maxima (no wait)
         constexpr int WAIT_ONE_STEP = (NLOAD & 15) | ((NLOAD >> 4) << 14) | (0x7 << 4) | (0xf << 8);
-        issue(0);
-        issue(1);
+        issue(0, sA, sB);
+        issue(1, sA + OA::BUF, sB + OB::BUF);
         for (int st = 0; st < steps; ++st) {
-            // this wave's loads of step st are done once only step st + 1's are left
+            // this wave's loads of step st are done once only step st + 1's are
+            // left; the barrier makes everyone's done and ends everyone's reads
+            // of the buffer that step st + 2 refills
             __builtin_amdgcn_s_waitcnt(WAIT_ONE_STEP);
             __builtin_amdgcn_s_barrier();
-            issue(st + 2);
-            compute(st % NB);
+            const int rd = st % NB, wr = (st + 2) % NB;
+            ring_step(sA + wr * OA::BUF, sB + wr * OB::BUF, sA + rd * OA::BUF, sB + rd * OB::BUF,
+                      [&](bf16_t* wa, bf16_t* wb) __attribute__((always_inline)) { issue(st + 2, wa, wb); }, compute);
         }
         // drain the clamped loads still in flight before the LDS is reused
         __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
