@@ -316,14 +316,16 @@ TTT_DEV int feat(int p) { return (p & ~31) + 8 * ((p >> 2) & 3) + 4 * ((p >> 4) 
 // into the E layout).  Rows past L lie outside the buffer ranges: they load
 // as zero (a zero K row gives E = 0 and V~ = 0, so it adds nothing) and
 // their stores are dropped, so no step needs a clamp or a mask.
-constexpr int DR_R = 8;                         // ring stages
-constexpr int DR_T = 32;                        // tokens per stage
+constexpr int DR_R = 5;                         // ring stages
+constexpr int DR_T = 64;                        // tokens per stage (four steps)
 constexpr int DR_QK = DR_T * 64;                // elements of the Q (or K) part
-constexpr int DR_STAGE = 2 * DR_QK + DR_T * 16; // elements per stage (9 KB)
-constexpr int DR_NL = 9;                        // load instructions per stage
+constexpr int DR_STAGE = 2 * DR_QK + DR_T * 16; // elements per stage (18 KB)
+constexpr int DR_NL = 18;                       // load instructions per stage
 
-// ONESTEP: every mini-batch is exactly one 16-token step (W_n is S~ itself)
-template <bool ONESTEP>
+// ONESTEP: every mini-batch is exactly one 16-token step (W_n is S~ itself);
+// STAGEEND: mini-batches end only at ring-stage ends (b a multiple of 64), so
+// W_{n+1} = S~ is taken once per stage instead of tested every step
+template <bool ONESTEP, bool STAGEEND>
 __global__ __launch_bounds__(64) void dual_ring_kernel(DualParams p) {
     constexpr int D = 64, DV = 64;
     __shared__ __attribute__((aligned(16))) bf16_t ring[DR_R * DR_STAGE];
@@ -360,23 +362,26 @@ __global__ __launch_bounds__(64) void dual_ring_kernel(DualParams p) {
     // direct-load lane offsets (bytes from a stage's first token row): load i
     // of Q or K fills rows 8i .. 8i + 7, lane l the position l % 8 of row
     // 8i + l / 8; the V load fills the [32][16] tile, lane l half l % 2 of row l / 2
-    uint32_t qko[4];
+    uint32_t qko[DR_T / 8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < DR_T / 8; ++i) {
         const int row = 8 * i + (lane >> 3);
         qko[i] = (uint32_t)(row * D * 2 + 16 * ((lane & 7) ^ (kswz(row & 15) >> 1)));
     }
     const uint32_t vdo = (uint32_t)((lane >> 1) * DV * 2 + 16 * (lane & 1));
-    const int nsteps = (L + 15) / 16, nst = (nsteps + 1) / 2;
+    const int nsteps = (L + 15) / 16, nst = (nsteps + DR_T / 16 - 1) / (DR_T / 16);
     auto issue = [&](int s, bf16_t* dst) __attribute__((always_inline)) {
         const int sq = min(s, nst - 1) * DR_T * D * 2;   // bytes (D == DV)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < DR_T / 8; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rQ, (lds_void_t*)(dst + 512 * i), 16, qko[i], sq, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < DR_T / 8; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (lds_void_t*)(dst + DR_QK + 512 * i), 16, qko[i], sq, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void_t*)(dst + 2 * DR_QK), 16, vdo, sq, 0, 0);
+#pragma unroll
+        for (int i = 0; i < DR_T / 32; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rV, (lds_void_t*)(dst + 2 * DR_QK + 512 * i), 16, vdo, sq + 32 * DV * 2 * i,
+                                                     0, 0);
     };
 
     // causal mask of the packed bf16 P^T pieces (j = 4g + r <= i = c16), fixed per lane
@@ -430,7 +435,7 @@ __global__ __launch_bounds__(64) void dual_ring_kernel(DualParams p) {
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) Sop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
-        if (!ONESTEP) {
+        if (!ONESTEP && !STAGEEND) {
             const int t1 = 16 * s16 + 16;
             if (t1 % mb == 0 || t1 >= L) {   // mini-batch end: W_{n+1} = S~
                 Wop[0] = Sop[0];
@@ -461,9 +466,16 @@ __global__ __launch_bounds__(64) void dual_ring_kernel(DualParams p) {
         ring_step1(ring + wr * DR_STAGE, ring + rd * DR_STAGE,
                    [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + DR_R - 1, dst); },
                    [&](const bf16_t* X) __attribute__((always_inline)) {
-                       step(X, 0, 2 * s);
-                       step(X, 1, 2 * s + 1);
+#pragma unroll
+                       for (int j = 0; j < DR_T / 16; ++j) step(X, j, (DR_T / 16) * s + j);
                    });
+        if (STAGEEND) {
+            const int t1 = DR_T * (s + 1);
+            if (t1 % mb == 0 || t1 >= L) {   // mini-batch end: W_{n+1} = S~
+                Wop[0] = Sop[0];
+                Wop[1] = Sop[1];
+            }
+        }
     }
     __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));   // the clamped loads still in flight
 
@@ -485,9 +497,11 @@ hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t s) {
     if (dtype == 1 && p.minibatch % 16 == 0) {
         // one wave per (b, h, 16-column tile)
         if (p.minibatch == 16)
-            hipLaunchKernelGGL((dual_ring_kernel<true>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+            hipLaunchKernelGGL((dual_ring_kernel<true, false>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+        else if (p.minibatch % DR_T == 0)
+            hipLaunchKernelGGL((dual_ring_kernel<false, true>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
         else
-            hipLaunchKernelGGL((dual_ring_kernel<false>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
+            hipLaunchKernelGGL((dual_ring_kernel<false, false>), dim3(p.B * p.H * 4), dim3(64), 0, s, p);
         return hipGetLastError();
     }
     const int grid = p.B * p.H;
