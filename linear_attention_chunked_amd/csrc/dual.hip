@@ -458,12 +458,17 @@ __global__ __launch_bounds__(64) void dual_ring_kernel(DualParams p) {
     constexpr int WAIT_STAGE = (NW & 15) | ((NW >> 4) << 14) | (0x7 << 4) | (0xf << 8);
 #pragma unroll
     for (int s = 0; s < DR_R - 1; ++s) issue(s, ring + s * DR_STAGE);
+    // ring offsets (elements) of the stage read and the stage refilled,
+    // advanced with scalar adds (a modulo would cost vector address math)
+    int rdo = 0, wro = (DR_R - 1) * DR_STAGE;
     for (int s = 0; s < nst; ++s) {
         __builtin_amdgcn_s_waitcnt(WAIT_STAGE);
-        const int rd = s % DR_R, wr = (s + DR_R - 1) % DR_R;
+        const int rd_off = rdo, wr_off = wro;
+        rdo = (rdo + DR_STAGE == DR_R * DR_STAGE) ? 0 : rdo + DR_STAGE;
+        wro = (wro + DR_STAGE == DR_R * DR_STAGE) ? 0 : wro + DR_STAGE;
         // the stage refilled here was read in iteration s - 1 (its reads were
         // consumed there); this step's reads go through their own pointer
-        ring_step1(ring + wr * DR_STAGE, ring + rd * DR_STAGE,
+        ring_step1(ring + __builtin_amdgcn_readfirstlane(wr_off), ring + __builtin_amdgcn_readfirstlane(rd_off),
                    [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + DR_R - 1, dst); },
                    [&](const bf16_t* X) __attribute__((always_inline)) {
 #pragma unroll
