@@ -14,12 +14,17 @@ seconds of steps have run (the count actually run is reported), so that the
 timed steps see the GPU's steady clocks rather than its ramp.
 
 Timing: every timed step is bracketed by HIP events on the launch stream.
-Between steps, outside the events, a 512 MiB scratch buffer is written so
-that no input is still in the 256 MiB last-level cache (--no-evict turns it
-off).  value and ms_per_step use the mean event time of a step; the median
-and minimum are reported beside it, and so is the wall time per step with
-the eviction writes.  The GPU clock is read with rocm-smi before and after
-the timed steps (null when rocm-smi gives none).
+Between steps, outside the events, a 512 MiB scratch buffer is written and
+another 512 MiB buffer is read, so that no input is still in the 256 MiB
+last-level cache and no dirty line of the scratch write is left in it for the
+timed step to write back (--evict selects other modes).  value and
+ms_per_step use the mean event time of a step; the median and minimum are
+reported beside it, and so is the wall time per step with the eviction
+passes (it includes a spin kernel, run once before the timed steps, that
+holds the stream until the host has issued all of them: the host time to
+issue a step, also reported, can exceed the shorter kernels' durations, and
+an event interval must not time the GPU waiting for the host).  The GPU clock is read with rocm-smi before and after the timed steps
+(null when rocm-smi gives none).
 
 Roofline: the dominant kernel's average launch duration is the mean event
 time; achieved = algorithmic bytes (or FLOPs) per launch / that duration.
@@ -446,8 +451,10 @@ def main():
                     help="inplace-128k (default), lm-scale, small-f32, inplace-32k, momentum, dual-b16, "
                          "dual-b2048, decode, decode-momentum, bwd, bwd-momentum, bwd-dbeta, inplace-frontend, swiglu, swiglu-mse, "
                          "scan, scan-momentum")
-    ap.add_argument("--no-evict", action="store_true",
-                    help="do not write the 512 MiB eviction buffer between timed steps")
+    ap.add_argument("--evict", default="write-read", choices=("write-read", "write", "read", "none"),
+                    help="what runs between timed steps to clear the last-level cache: write one "
+                         "512 MiB buffer and then read another (default), only one of the two, or nothing")
+    ap.add_argument("--no-evict", action="store_true", help="same as --evict none")
     ap.add_argument("--min-warmup-s", type=float, default=0.5,
                     help="keep warming up until this many seconds of steps have run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -492,17 +499,57 @@ def main():
         torch.cuda.synchronize()
     warm_s = time.perf_counter() - t_w
 
-    # 512 MiB written between timed steps (outside the events): twice the
-    # last-level cache, so no step finds its inputs there
-    evict = None if args.no_evict else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # Between timed steps (outside the events) 512 MiB, twice the last-level
+    # cache, are written and then another 512 MiB are read: the write pushes
+    # out the previous step's inputs and outputs, the read then replaces the
+    # write's dirty lines with clean ones, so the timed step neither finds its
+    # inputs in the cache nor pays for writing back someone else's data
+    mode = "none" if args.no_evict else args.evict
+    evict_w = torch.empty(512 << 20, dtype=torch.uint8, device=dev) if "write" in mode else None
+    evict_r = torch.zeros(128 << 20, dtype=torch.float32, device=dev) if "read" in mode else None
+    evict_sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def evict_pass(i):
+        if evict_w is not None:
+            evict_w.fill_(i & 0xff)
+        if evict_r is not None:
+            torch.sum(evict_r, dim=0, out=evict_sink)
+
+    # host time to issue one step (eviction included), after a first pass that
+    # loads the eviction kernels
+    evict_pass(0)
+    step()
+    torch.cuda.synchronize()
+    t_h = time.perf_counter()
+    for i in range(10):
+        evict_pass(i)
+        step()
+    host_ms = (time.perf_counter() - t_h) * 1000.0 / 10
+    torch.cuda.synchronize()
+    # The timed steps are queued behind a spin kernel long enough for the host
+    # to issue all of them, so no event interval contains GPU idle time spent
+    # waiting for the host (the binding's host work per call is comparable to
+    # the shorter workloads' kernel times)
+    hold_cycles = 0
+    if hasattr(torch.cuda, "_sleep"):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        torch.cuda._sleep(1 << 22)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_cycle = max(c0.elapsed_time(c1), 1e-3) / (1 << 22)
+        hold_ms = min(2.0 * args.steps * host_ms + 2.0, 500.0)
+        hold_cycles = int(hold_ms / ms_per_cycle)
+
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     clk_before = gpu_sclk_mhz()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if hold_cycles:
+        torch.cuda._sleep(hold_cycles)
     for i in range(args.steps):
-        if evict is not None:
-            evict.fill_(i & 0xff)
+        evict_pass(i)
         starts[i].record(stream)
         step()
         ends[i].record(stream)
@@ -535,7 +582,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": n_warm,
         "warmup_s": round(warm_s, 3), "ms_per_step": round(ms_per_step, 5),
         "ms_median": round(median_ms, 5), "ms_min": round(step_ms[0], 5),
-        "wall_ms_per_step": round(wall * 1000.0 / args.steps, 5), "evict_bytes": 0 if evict is None else evict.numel(),
+        "wall_ms_per_step": round(wall * 1000.0 / args.steps, 5), "host_ms_per_step": round(host_ms, 4),
+        "evict": mode,
         "sclk_mhz": {"before": clk_before, "after": clk_after},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": info["dtype"], "data": "synthetic (seeded Gaussian inputs of the workload's shapes)",
