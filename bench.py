@@ -61,6 +61,7 @@ KERNEL_SOURCES = {
     "ip_update_wide_kernel+ip_readout_kernel": ("inplace.hip", "common.h"),
     "dual_fwd_kernel": ("dual.hip", "common.h"),
     "dual_ring_kernel": ("dual.hip", "common.h"),
+    "dual_seg_kernel": ("dual.hip", "common.h"),
     "decode_kernel": ("decode.hip", "common.h"),
     "fe_gemm_kernel": ("frontend.hip", "gemm.h", "common.h"),
     "tcb_fwd_kernel+bwd_scale_kernels": ("tcb_fwd.hip", "bwd.hip", "common.h"),
@@ -163,7 +164,7 @@ def setup_workload(name: str, dev: str):
         bytes_alg = B * H * L * 4 * d * 2 + 2 * B * H * d * d * 4
         flop_alg = B * H * L * (6 * d * d + (mb + 1) * 2 * d)
         info = dict(workload=name, B=B, H=H, L=L, d=d, minibatch=mb, dtype="bf16", tokens=B * L,
-                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="dual_ring_kernel", inputs=inp)
+                    bytes_alg=bytes_alg, flop_alg=flop_alg, kernel="dual_seg_kernel", inputs=inp)
         return step, info
     if name in ("bwd", "bwd-momentum"):
         mom = name == "bwd-momentum"

@@ -254,12 +254,26 @@ ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk
  *
  * q, k [B,H,L,d], v, out [B,H,L,dv] contiguous, dtype `dtype`; W0
  * [B,H,d,dv] fp32 (W0_stride_bh elements between heads, 0 broadcasts one
- * W0); W_final [B,H,d,dv] fp32 contiguous or NULL; out and W_final
- * overlap no input (q, k, v, W0) and not each other (TTT_ERR_ALIAS).
- * Supported: d = 64,
- * dv = 64, bf16 or fp32, any minibatch >= 1 (the last mini-batch holds
- * the remaining L - (ceil(L/minibatch)-1)*minibatch tokens).  Needs no
- * workspace.
+ * W0); W_final [B,H,d,dv] fp32 contiguous or NULL; out, W_final and the
+ * workspace overlap no input (q, k, v, W0) and not each other
+ * (TTT_ERR_ALIAS).  Supported: d = 64, dv = 64, bf16 or fp32, any
+ * minibatch >= 1 (the last mini-batch holds the remaining
+ * L - (ceil(L/minibatch)-1)*minibatch tokens).
+ *
+ * Segments.  Over one mini-batch the update is affine in the state,
+ * W_{n+1} = (I - eta K_n^T K_n) W_n + eta K_n^T V_n, so a run of whole
+ * mini-batches maps its start state W to A W + B.  For bf16 with minibatch
+ * a multiple of 16 and few sequences (B*H < 128), a call given a workspace
+ * of at least ttt_dual_form_workspace_size bytes cuts every sequence into
+ * segments of whole mini-batches that run concurrently: each segment
+ * computes its (A - I, B) from K and V alone, composes the maps of the
+ * segments before it onto W0 in order, then runs its own tokens.  The
+ * result equals the one-chain result up to fp32 rounding (the composed
+ * start states are not bit-identical to the chained ones; repeated calls
+ * are).  workspace NULL runs each sequence as one chain; a non-NULL
+ * workspace smaller than needed is TTT_ERR_WORKSPACE.  The waits between
+ * segments are bounded; ttt_dual_form_lookback_status reports one that gave
+ * up (TTT_ERR_TIMEOUT in the binding; its results are invalid).
  */
 ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
                                int32_t minibatch, int32_t dtype,
@@ -267,6 +281,22 @@ ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32
                                const float* W0, int64_t W0_stride_bh, float eta,
                                void* out, float* W_final,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace ttt_dual_form_fwd uses to run these sizes in segments;
+ * 0 when the shape runs as one chain anyway.  Sizes only, no GPU needed.
+ * Errors: TTT_ERR_NULL, TTT_ERR_DTYPE, TTT_ERR_SHAPE, TTT_ERR_UNSUPPORTED. */
+ttt_status_t ttt_dual_form_workspace_size(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
+                                          int32_t minibatch, int32_t dtype, size_t* bytes);
+
+/* After a segmented ttt_dual_form_fwd with the same sizes and workspace:
+ * waits for `stream` and sets *gave_up to 1 if a wait between segments gave
+ * up (the outputs are then invalid), else 0 (also when the call ran as one
+ * chain or workspace is NULL).  Errors: TTT_ERR_NULL (gave_up), the size
+ * errors of ttt_dual_form_workspace_size, TTT_ERR_WORKSPACE (too small),
+ * TTT_ERR_HIP. */
+ttt_status_t ttt_dual_form_lookback_status(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
+                                           int32_t minibatch, int32_t dtype, const void* workspace,
+                                           size_t workspace_bytes, void* stream, int32_t* gave_up);
 
 /*
  * ttt_decode_step -- one token of the token-causal recurrence per (b, h),

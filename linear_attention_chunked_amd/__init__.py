@@ -88,6 +88,11 @@ def load_library():
     lib.ttt_dual_form_fwd.argtypes = [i32, i32, i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp,
                                       ctypes.c_int64, f32, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.ttt_dual_form_fwd.restype = ctypes.c_int
+    lib.ttt_dual_form_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ttt_dual_form_workspace_size.restype = ctypes.c_int
+    lib.ttt_dual_form_lookback_status.argtypes = [i32, i32, i32, i32, i32, i32, i32, _vp, ctypes.c_size_t, _vp,
+                                                  ctypes.POINTER(ctypes.c_int32)]
+    lib.ttt_dual_form_lookback_status.restype = ctypes.c_int
     lib.ttt_decode_step.argtypes = [i32, i32, i32, i32, i32, _vp, _vp, _vp, _vp, f32, f32, _vp, _vp,
                                     _vp, _vp]
     lib.ttt_decode_step.restype = ctypes.c_int
@@ -283,11 +288,17 @@ def chunk_state_scan(dS, dM=None, *, beta=0.0, chunk, L, S0=None, M0=None, strea
     return S_excl, M_excl, S_final, M_final
 
 
-def dual_form_fwd(q, k, v, W0, *, eta, minibatch, out=None, return_state=False, stream=None):
+def dual_form_fwd(q, k, v, W0, *, eta, minibatch, out=None, return_state=False, stream=None,
+                  segmented=True, check_lookback=False):
     """TTT-Linear mini-batch forward, dual form (``ttt_dual_form_fwd``).
 
     q, k: [B,H,L,d]; v: [B,H,L,dv] contiguous, fp32 or bf16; W0 fp32
-    [B,H,d,dv] (or [d,dv] broadcast).  Returns out (and W_final)."""
+    [B,H,d,dv] (or [d,dv] broadcast).  Returns out (and W_final).
+    segmented: give the library the workspace it asks for
+    (``ttt_dual_form_workspace_size``), so that shapes with few sequences run
+    in concurrent segments; False runs every sequence as one chain.
+    check_lookback: wait for the call and raise TTTError (TTT_ERR_TIMEOUT) if
+    a wait between segments gave up (``ttt_dual_form_lookback_status``)."""
     lib = load_library()
     _require_gpu(q, k, v, W0, out)
     B, H, L, d = q.shape
@@ -301,12 +312,33 @@ def dual_form_fwd(q, k, v, W0, *, eta, minibatch, out=None, return_state=False, 
     if out is None:
         out = torch.empty((B, H, L, dv), dtype=q.dtype, device=q.device)
     W_final = torch.empty((B, H, d, dv), dtype=torch.float32, device=q.device) if return_state else None
-    _check(lib.ttt_dual_form_fwd(B, H, L, d, dv, int(minibatch), _dtype_code(q), _ptr(q), _ptr(k),
+    dt = _dtype_code(q)
+    ws = ctypes.c_size_t(0)
+    if segmented:
+        _check(lib.ttt_dual_form_workspace_size(B, H, L, d, dv, int(minibatch), dt, ctypes.byref(ws)))
+    work = torch.empty(ws.value, dtype=torch.uint8, device=q.device) if ws.value else None
+    _check(lib.ttt_dual_form_fwd(B, H, L, d, dv, int(minibatch), dt, _ptr(q), _ptr(k),
                                  _ptr(v), _ptr(W0), w_stride, float(eta), _ptr(out), _ptr(W_final),
-                                 None, 0, _stream(stream)))
+                                 _ptr(work), ws.value, _stream(stream)))
+    if check_lookback:
+        gave_up = ctypes.c_int32(0)
+        _check(lib.ttt_dual_form_lookback_status(B, H, L, d, dv, int(minibatch), dt, _ptr(work), ws.value,
+                                                 _stream(stream), ctypes.byref(gave_up)))
+        if gave_up.value:
+            raise TTTError(TTT_ERR_TIMEOUT, lib.ttt_status_string(TTT_ERR_TIMEOUT).decode())
     if return_state:
         return out, W_final
     return out
+
+
+def dual_form_workspace_size(B, H, L, d, dv, *, minibatch, dtype=torch.bfloat16) -> int:
+    """Bytes of workspace the segmented dual form uses at these sizes
+    (``ttt_dual_form_workspace_size``; 0: the shape runs as one chain)."""
+    lib = load_library()
+    ws = ctypes.c_size_t(0)
+    _check(lib.ttt_dual_form_workspace_size(int(B), int(H), int(L), int(d), int(dv), int(minibatch),
+                                            TTT_F32 if dtype == torch.float32 else TTT_BF16, ctypes.byref(ws)))
+    return int(ws.value)
 
 
 def decode_step(q, k, v, S, M=None, *, eta=None, eta_scalar=0.0, beta=0.0, out=None, stream=None):

@@ -398,29 +398,42 @@ ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk
                                            M_final, reinterpret_cast<hipStream_t>(stream)));
 }
 
+ttt_status_t ttt_dual_form_workspace_size(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
+                                          int32_t minibatch, int32_t dtype, size_t* bytes) {
+    if (!bytes) return TTT_ERR_NULL;
+    if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
+    if (!shape_ok(B, H, L, {d, dv}) || !within(minibatch, kMaxLen)) return TTT_ERR_SHAPE;
+    if (!ttt::dual_supported(dtype, d, dv, minibatch)) return TTT_ERR_UNSUPPORTED;
+    *bytes = ttt::dual_workspace(dtype, B, H, L, d, dv, minibatch);
+    return TTT_OK;
+}
+
 ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
                                int32_t minibatch, int32_t dtype, const void* q, const void* k,
                                const void* v, const float* W0, int64_t W0_stride_bh, float eta,
                                void* out, float* W_final, void* workspace, size_t workspace_bytes,
                                void* stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
     if (!shape_ok(B, H, L, {d, dv}) || !within(minibatch, kMaxLen) || W0_stride_bh < 0) return TTT_ERR_SHAPE;
     uint64_t w0_bytes = 0;
     if (!extent_bytes((int64_t)B * H, W0_stride_bh, 1, 0, 1, 0, (int64_t)d * dv, 4, &w0_bytes)) return TTT_ERR_SHAPE;
     if (!q || !k || !v || !W0 || !out) return TTT_ERR_NULL;
-    const void* ptrs[] = {q, k, v, W0, out, W_final};
+    const void* ptrs[] = {q, k, v, W0, out, W_final, workspace};
     for (const void* x : ptrs)
         if (x && !aligned16(x)) return TTT_ERR_ALIGN;
     if (!ttt::dual_supported(dtype, d, dv, minibatch)) return TTT_ERR_UNSUPPORTED;
+    // the segmented form runs when the caller gives a workspace; without one
+    // (NULL) the mini-batches of a sequence run in one chain
+    const size_t need = ttt::dual_workspace(dtype, B, H, L, d, dv, minibatch);
+    const bool seg = need > 0 && workspace != nullptr;
+    if (seg && workspace_bytes < need) return TTT_ERR_WORKSPACE;
     const size_t es = esize(dtype);
     const size_t nq = (size_t)B * H * L * d * es, nv = (size_t)B * H * L * dv * es;
     const size_t nw = (size_t)d * dv;
-    if (!disjoint_sets({rng(out, nv), rng(W_final, (size_t)B * H * nw * 4)},
+    if (!disjoint_sets({rng(out, nv), rng(W_final, (size_t)B * H * nw * 4), rng(seg ? workspace : nullptr, need)},
                        {rng(q, nq), rng(k, nq), rng(v, nv), block_range(W0, W0_stride_bh, 0, B * H, 1, nw, 4)}))
         return TTT_ERR_ALIAS;
-    ttt::DualParams p;
+    ttt::DualParams p{};
     p.q = q;
     p.k = k;
     p.v = v;
@@ -435,7 +448,29 @@ ttt_status_t ttt_dual_form_fwd(int32_t B, int32_t H, int32_t L, int32_t d, int32
     p.d = d;
     p.dv = dv;
     p.minibatch = minibatch;
+    p.workspace = seg ? workspace : nullptr;
+    p.workspace_bytes = seg ? workspace_bytes : 0;
     return from_hip(ttt::launch_dual_fwd(p, dtype, reinterpret_cast<hipStream_t>(stream)));
+}
+
+ttt_status_t ttt_dual_form_lookback_status(int32_t B, int32_t H, int32_t L, int32_t d, int32_t dv,
+                                           int32_t minibatch, int32_t dtype, const void* workspace,
+                                           size_t workspace_bytes, void* stream, int32_t* gave_up) {
+    if (!gave_up) return TTT_ERR_NULL;
+    size_t need = 0;
+    const ttt_status_t s = ttt_dual_form_workspace_size(B, H, L, d, dv, minibatch, dtype, &need);
+    if (s != TTT_OK) return s;
+    *gave_up = 0;
+    const int64_t idx = ttt::dual_error_word(dtype, B, H, L, d, dv, minibatch);
+    if (idx < 0 || !workspace) return TTT_OK;   // the call ran as one chain: nothing waited
+    if (workspace_bytes < need) return TTT_ERR_WORKSPACE;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    int32_t v = 0;
+    hipError_t e = hipMemcpyAsync(&v, static_cast<const int32_t*>(workspace) + idx, sizeof(v), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return TTT_ERR_HIP;
+    *gave_up = v != 0 ? 1 : 0;
+    return TTT_OK;
 }
 
 ttt_status_t ttt_bwd_workspace_size(int32_t B, int32_t H, int32_t L, int32_t dk, int32_t dv, int32_t dtype,

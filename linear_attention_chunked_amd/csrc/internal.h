@@ -99,9 +99,21 @@ struct DualParams {
     float* W_final;
     float eta;
     int B, H, L, d, dv, minibatch;
+    // segmented form (set by launch_dual_fwd from the workspace): flags (one
+    // per (b, h, segment), then the ticket counter and the error word) and
+    // the per-segment maps
+    void* workspace;            // null: the sequential form
+    size_t workspace_bytes;
+    int* flags;
+    float* maps;
+    int nseg, seg_len, max_polls;
 };
 hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t stream);
 bool dual_supported(int dtype, int d, int dv, int minibatch);
+// workspace bytes of the segmented form (0: the shape runs sequentially)
+size_t dual_workspace(int dtype, int B, int H, int L, int d, int dv, int minibatch);
+// int index of the look-back error word in the workspace, or -1 (sequential)
+int64_t dual_error_word(int dtype, int B, int H, int L, int d, int dv, int minibatch);
 
 // dL/dbeta of the token-causal momentum forward (contiguous tensors).
 struct DbetaParams {

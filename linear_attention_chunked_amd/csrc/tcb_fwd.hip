@@ -410,21 +410,25 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             __syncthreads();
             if (tid == 0) __hip_atomic_store(p.lb_flags + my_id, which + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         };
-        // Waiting: one thread polls the flag with agent-scope acquire loads (the
-        // acquire invalidates this CU's L1 and the stale lines of the XCD's L2,
-        // which the other waves' loads go through after the barrier) until it
-        // reaches `want` (1: aggregate published, 2: inclusive state too).
-        // The wait is bounded by p.lb_max_polls: a flag that never arrives
-        // ends it, the error word in the workspace is raised (the host reads
-        // it back) and every wave still finishes, with wrong results.
+        // Waiting: one thread polls the flag with relaxed agent-scope loads
+        // until it reaches `want` (1: aggregate published, 2: inclusive state
+        // too), then acquires once: the acquire invalidates this CU's L1 and
+        // the stale lines of the XCD's L2, which the other waves' loads go
+        // through after the barrier.  (An acquire load in the loop would
+        // invalidate the XCD's L2 on every poll, under the feet of every
+        // workgroup still computing there.)  The wait is bounded by
+        // p.lb_max_polls: a flag that never arrives ends it, the error word in
+        // the workspace is raised (the host reads it back) and every wave
+        // still finishes, with wrong results.
         auto wait_flag = [&](int id, int want) {
             if (tid == 0) {
                 int v = 0;
                 for (int spin = 0; spin < p.lb_max_polls; ++spin) {
-                    v = __hip_atomic_load(p.lb_flags + id, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+                    v = __hip_atomic_load(p.lb_flags + id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if (v >= want) break;
                     __builtin_amdgcn_s_sleep(2);
                 }
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
                 if (v < want) __hip_atomic_store(p.lb_error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             __syncthreads();

@@ -244,6 +244,45 @@ def test_dual_rejects_before_launch(lib):
     assert f(*args(out=FAKE + n)) == ERR_ALIAS
 
 
+def test_dual_segment_workspace(lib):
+    """The segmented dual form's workspace: asked for by few sequences with
+    bf16 mini-batches of a multiple of 16, none otherwise; a short or
+    overlapping workspace is rejected before any launch."""
+    q = ctypes.c_size_t(0)
+    ws = lambda B, H, L, mb, dt=1, d=64: (lib.ttt_dual_form_workspace_size(B, H, L, d, 64, mb, dt, ctypes.byref(q)), q.value)
+    st, need = ws(4, 16, 8192, 16)
+    # 4 segments of 2048 tokens: flags (256 + 2 words, in 256-byte units) and
+    # a 32 KB map (Delta as bf16 hi and lo, B in fp32) per (b, h, segment)
+    assert st == OK and need == 1280 + 64 * 4 * 32768
+    st, need2 = ws(4, 16, 8192, 2048)
+    assert st == OK and need2 == need                  # 4 segments of one mini-batch
+    assert ws(2, 64, 8192, 16) == (OK, 0)        # 128 sequences: one workgroup per CU unsegmented
+    assert ws(1, 3, 1000, 48) == (OK, 256 + 3 * 3 * 32768)    # 3 segments of 384 tokens
+    assert ws(4, 16, 8192, 40) == (OK, 0)        # mini-batches not of a multiple of 16
+    assert ws(4, 16, 8192, 16, dt=0) == (OK, 0)  # fp32
+    assert ws(1, 1, 200, 16) == (OK, 0)          # one segment
+    assert ws(4, 16, 8192, 16, d=32)[0] == ERR_UNSUP
+    assert lib.ttt_dual_form_workspace_size(4, 16, 8192, 64, 64, 16, 1, None) == ERR_NULL
+    f = lib.ttt_dual_form_fwd
+    B, H, L = 4, 16, 8192
+    n = B * H * L * 64 * 2
+    big = 1 << 40
+
+    def args(work, wbytes):
+        return [B, H, L, 64, 64, 16, 1, FAKE, FAKE + n, FAKE + 2 * n, FAKE + 3 * n, 0, 0.01,
+                FAKE + 4 * n, None, work, wbytes, None]
+    assert f(*args(big, need - 1)) == ERR_WS                    # too small
+    assert f(*args(big + 8, need)) == ERR_ALIGN
+    assert f(*args(FAKE + 2 * n, need)) == ERR_ALIAS            # on v
+    assert f(*args(FAKE + 4 * n + n // 2, need)) == ERR_ALIAS   # inside out
+    flag = ctypes.c_int32(7)
+    stat = lib.ttt_dual_form_lookback_status
+    assert stat(B, H, L, 64, 64, 16, 1, None, 0, None, ctypes.byref(flag)) == OK and flag.value == 0
+    assert stat(B, H, L, 64, 64, 16, 1, big, need, None, None) == ERR_NULL
+    assert stat(B, H, L, 64, 64, 16, 1, big, need - 1, None, ctypes.byref(flag)) == ERR_WS
+    assert stat(8, 16, L, 64, 64, 16, 1, big, 0, None, ctypes.byref(flag)) == OK and flag.value == 0
+
+
 def test_decode_rejects_before_launch(lib):
     f = lib.ttt_decode_step
     n = 1 << 20

@@ -336,11 +336,18 @@ def test_scan_matches_fused_forward_states():
 
 
 # ------------------------------------------------------------- dual form
-def run_dual(inp: W.DualInputs):
+def run_dual(inp: W.DualInputs, segmented=True):
     out, Wf = lac.dual_form_fwd(to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(inp.W0),
-                                eta=inp.eta, minibatch=inp.minibatch, return_state=True)
+                                eta=inp.eta, minibatch=inp.minibatch, return_state=True,
+                                segmented=segmented, check_lookback=segmented)
     torch.cuda.synchronize()
     return out.cpu(), Wf.cpu()
+
+
+def dual_segments(inp: W.DualInputs) -> bool:
+    B, H, L, d = inp.q.shape
+    return lac.dual_form_workspace_size(B, H, L, d, inp.v.shape[-1], minibatch=inp.minibatch,
+                                        dtype=inp.q.dtype) > 0
 
 
 def check_dual(inp, got, heads, tol, what):
@@ -354,22 +361,79 @@ def check_dual(inp, got, heads, tol, what):
         assert e <= tol, f"{what} W_final (b={b},h={h}) rel-L2 {e:.3e}"
 
 
+@pytest.mark.parametrize("segmented", [False, True])
 @pytest.mark.parametrize("mb,L", [(16, 300), (64, 1000), (2048, 4096), (1, 70), (48, 200)])
-def test_dual_small(mb, L):
+def test_dual_small(mb, L, segmented):
     inp = W.gen_dual(B=1, H=2, L=L, minibatch=mb)
-    say(f"dual bf16 b{mb} L{L}")
-    check_dual(inp, run_dual(inp), [(0, 0), (0, 1)], TOL["bf16"], "dual")
+    say(f"dual bf16 b{mb} L{L} segmented={segmented}")
+    check_dual(inp, run_dual(inp, segmented), [(0, 0), (0, 1)], TOL["bf16"], "dual")
 
 
+@pytest.mark.parametrize("segmented", [False, True])
 @pytest.mark.parametrize("mb,L", [(256, 1000), (512, 1500), (768, 1536), (4096, 8192), (2048, 2100), (32, 4100)])
-def test_dual_large_minibatch(mb, L):
+def test_dual_large_minibatch(mb, L, segmented):
     """Mini-batches of many 16-token steps with ragged ends: the last
     mini-batch partial (1000, 1500, 2100 tokens), the last 32-token ring
     stage holding one step and a partial tail (4100 tokens, b = 32: one
     stage per mini-batch) and a mini-batch of the whole sequence (8192)."""
     inp = W.gen_dual(B=1, H=3, L=L, minibatch=mb)
-    say(f"dual bf16 b{mb} L{L}")
-    check_dual(inp, run_dual(inp), [(0, 0), (0, 1), (0, 2)], TOL["bf16"], f"dual b{mb} L{L}")
+    say(f"dual bf16 b{mb} L{L} segmented={segmented}")
+    check_dual(inp, run_dual(inp, segmented), [(0, 0), (0, 1), (0, 2)], TOL["bf16"], f"dual b{mb} L{L}")
+
+
+@pytest.mark.parametrize("mb,L,B,H", [(16, 1000, 1, 2), (16, 4111, 1, 3), (48, 1003, 1, 2), (32, 1500, 2, 1),
+                                      (64, 2500, 1, 2), (2048, 8192, 1, 2), (16, 2048, 3, 5)])
+def test_dual_segmented(mb, L, B, H):
+    """The segmented form (each segment composes the affine maps of the
+    segments before it): several segments per head, ragged last segments
+    (L not a multiple of the segment, of 64 or of 16), one-step, per-step
+    and stage-end mini-batch ends; against the oracle and against the one-
+    chain form, with no look-back wait giving up."""
+    inp = W.gen_dual(B=B, H=H, L=L, minibatch=mb)
+    assert dual_segments(inp), "this shape should run in segments"
+    say(f"dual segmented bf16 B{B} H{H} b{mb} L{L}")
+    got = run_dual(inp, True)
+    heads = [(b, h) for b in range(B) for h in range(H)][:4]
+    check_dual(inp, got, heads, TOL["bf16"], f"dual seg b{mb} L{L}")
+    ref = run_dual(inp, False)
+    assert oracle.rel_l2(got[0].float(), ref[0].float()) <= 5e-3
+    assert oracle.rel_l2(got[1], ref[1]) <= 5e-3
+
+
+@pytest.mark.parametrize("mb", [16, 64, 48])
+def test_dual_many_sequences(mb):
+    """Enough sequences to fill the chip without segments (B*H = 128, more
+    than one wave per CU covers): one workgroup of four waves per sequence."""
+    inp = W.gen_dual(B=2, H=64, L=300, minibatch=mb)
+    assert not dual_segments(inp)
+    say(f"dual bf16 B2 H64 b{mb} L300")
+    check_dual(inp, run_dual(inp, True), [(0, 0), (1, 63), (1, 7)], TOL["bf16"], f"dual many b{mb}")
+
+
+def test_dual_segmented_alternating_inputs():
+    """Back-to-back calls with different inputs of one shape reuse the same
+    workspace memory: every call must read the maps its own segments
+    published, never a previous call's (which would put another sequence's
+    maps into the start states)."""
+    a = W.gen_dual(B=1, H=4, L=4096, minibatch=16, seed_base=5100)
+    b = W.gen_dual(B=1, H=4, L=4096, minibatch=16, seed_base=5200)
+    assert dual_segments(a)
+    ref = {id(x): run_dual(x, False) for x in (a, b)}
+    for x in (a, b, a, b, a):
+        got = run_dual(x, True)
+        assert oracle.rel_l2(got[0].float(), ref[id(x)][0].float()) <= 5e-3
+        assert oracle.rel_l2(got[1], ref[id(x)][1]) <= 5e-3
+
+
+def test_dual_segmented_repeat_bit_identical():
+    """Segments compose their predecessors' maps in a fixed order, so
+    repeated calls give the same bits whatever the timing."""
+    inp = W.gen_dual(B=1, H=4, L=4096, minibatch=16)
+    assert dual_segments(inp)
+    a = run_dual(inp, True)
+    for _ in range(5):
+        b = run_dual(inp, True)
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
 @pytest.mark.parametrize("mb", [16, 40])
@@ -402,14 +466,31 @@ def test_dual_fixed_point_exact():
 def test_dual_fixed_point_exact_bf16(mb):
     """The same fixed point in bf16 (v = k W0 with W0 = I/2 is exact in
     bf16): every corrected value is exactly zero, so out = q/2 and
-    W_final = W0 bit for bit, with one-step and with 128-step mini-batches."""
+    W_final = W0 bit for bit, with one-step and with 128-step mini-batches
+    (one chain per sequence)."""
     inp = W.gen_dual(B=1, H=2, L=4096, minibatch=mb)
     k = inp.k
     out, Wf = lac.dual_form_fwd(inp.q.to(DEV), k.to(DEV), (0.5 * k.float()).to(torch.bfloat16).to(DEV),
-                                inp.W0.to(DEV), eta=inp.eta, minibatch=mb, return_state=True)
+                                inp.W0.to(DEV), eta=inp.eta, minibatch=mb, return_state=True, segmented=False)
     torch.cuda.synchronize()
     assert torch.equal(out.cpu(), (0.5 * inp.q.float()).to(torch.bfloat16))
     assert torch.equal(Wf.cpu(), inp.W0)
+
+
+@pytest.mark.parametrize("mb", [16, 2048])
+def test_dual_fixed_point_segmented_bf16(mb):
+    """The fixed point through segments: a segment's start state is W0
+    composed with its predecessors' maps (A - I, B), which agree with W0 =
+    A W0 + B only up to the bf16 operand rounding of the maps' chains, so
+    out and W_final match q/2 and W0 to that level rather than bit for bit."""
+    inp = W.gen_dual(B=1, H=2, L=4096, minibatch=mb)
+    assert dual_segments(inp)
+    k = inp.k
+    out, Wf = lac.dual_form_fwd(inp.q.to(DEV), k.to(DEV), (0.5 * k.float()).to(torch.bfloat16).to(DEV),
+                                inp.W0.to(DEV), eta=inp.eta, minibatch=mb, return_state=True, check_lookback=True)
+    torch.cuda.synchronize()
+    assert oracle.rel_l2(out.cpu().float(), 0.5 * inp.q.float()) <= 2e-3
+    assert oracle.rel_l2(Wf.cpu(), inp.W0) <= 2e-3
 
 
 # ------------------------------------------------------------- properties
