@@ -263,7 +263,7 @@ ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk
  * Segments.  Over one mini-batch the update is affine in the state,
  * W_{n+1} = (I - eta K_n^T K_n) W_n + eta K_n^T V_n, so a run of whole
  * mini-batches maps its start state W to A W + B.  For bf16 with minibatch
- * a multiple of 16 and few sequences (B*H < 128), a call given a workspace
+ * a multiple of 16 and few sequences (B*H <= 128), a call given a workspace
  * of at least ttt_dual_form_workspace_size bytes cuts every sequence into
  * segments of whole mini-batches that run concurrently: each segment
  * computes its (A - I, B) from K and V alone, composes the maps of the

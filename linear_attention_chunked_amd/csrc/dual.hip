@@ -516,15 +516,14 @@ __global__ __launch_bounds__(64) void dual_ring_kernel(DualParams p) {
 //      (hi hi, lo hi, hi lo): about 16 bits of each operand.
 //   3. It runs the forward over its own tokens from that state, as the
 //      sequential kernel does.
-// Q, K and V reach LDS through a ring of DS_R stages of 64 tokens shared
-// by the four waves (direct 16-byte loads, one barrier per stage); a stage
-// is [64][64] Q, K and V tiles, 24 KB.
+// Q, K and V reach LDS through a ring of stages of 64 tokens shared by the
+// waves of the workgroup (direct 16-byte loads, one barrier per stage); a
+// stage is [64][64] Q, K and V tiles, 24 KB.
 // Workgroups take tickets in segment order, so a segment only waits for
 // workgroups that already run.
-#ifndef DS_RING
-#define DS_RING 4
-#endif
-constexpr int DS_R = DS_RING;                  // ring stages
+// ring stages: 4 with one four-wave workgroup per CU (96 KB), 3 with two
+// two-wave workgroups per CU (72 KB each)
+constexpr int dual_ring_stages(int nw) { return nw == 4 ? 4 : 3; }
 constexpr int DS_T = 64;                       // tokens per stage (four steps)
 constexpr int DS_TILE = DS_T * 64;             // elements of one [64][64] tile
 constexpr int DS_STAGE = 3 * DS_TILE;          // Q | K | V, elements per stage
@@ -549,6 +548,10 @@ TTT_DEV int vswz(int r) { return 2 * ((r >> 1) & 3); }
 TTT_DEV void dma16(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff, int soff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 0);
 }
+// the same, device-coherent (sc1)
+TTT_DEV void dma16_sc1(__amdgpu_buffer_rsrc_t r, bf16_t* lds, uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, voff, soff, 0, 16);
+}
 // x = hi + lo for the four values of an accumulator slice, both as bf16
 TTT_DEV void split4(const f32x4& x, u32x2& hi, u32x2& lo) {
     hi = u32x2{pack2bf(x[0], x[1]), pack2bf(x[2], x[3])};
@@ -566,13 +569,20 @@ TTT_DEV void* uniform_ptr(const void* p) {
 }
 
 // MBK: 0 = one-step mini-batches (b = 16), 1 = mini-batches ending only at
-// stage ends (b a multiple of 64), 2 = any multiple of 16 (per-step test)
-template <int MBK>
-__global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
+// stage ends (b a multiple of 64), 2 = any multiple of 16 (per-step test).
+// NW: waves per workgroup (4 or 2); wave w owns NCB = 4 / NW column blocks
+// of 16 (columns [16 NCB w, 16 NCB (w + 1))), whose chains share every K and
+// Q fragment and the score tile and interleave in the issue stream.
+template <int MBK, int NW>
+__global__ __launch_bounds__(64 * NW) void dual_seg_kernel(DualParams p) {
     constexpr int D = 64, DV = 64;
     constexpr bool ONE = (MBK == 0), SEND = (MBK == 1);
+    constexpr int NCB = 4 / NW;          // column blocks per wave
+    constexpr int R = dual_ring_stages(NW);
+    constexpr int NLQ = 8 / NW;          // direct loads per wave per [64][64] tile
+    constexpr int MB = DS_MB / NCB;      // maps staged per batch of the composition
     // the only LDS array (see ring_step1); its first word carries the ticket
-    __shared__ __attribute__((aligned(16))) bf16_t ring[DS_R * DS_STAGE];
+    __shared__ __attribute__((aligned(16))) bf16_t ring[R * DS_STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -591,31 +601,42 @@ __global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
     const int tok0 = seg * p.seg_len;
     const int len = min(p.seg_len, L - tok0);
     const float eta = p.eta;
+    const int col0 = 16 * NCB * w;       // first column of this wave
     const bf16_t* Qg = reinterpret_cast<const bf16_t*>(p.q) + (int64_t)bh * L * D;
     const bf16_t* Kg = reinterpret_cast<const bf16_t*>(p.k) + (int64_t)bh * L * D;
     const bf16_t* Vg = reinterpret_cast<const bf16_t*>(p.v) + (int64_t)bh * L * DV;
-    bf16_t* Og = reinterpret_cast<bf16_t*>(p.out) + (int64_t)bh * L * DV + 16 * w;
+    bf16_t* Og = reinterpret_cast<bf16_t*>(p.out) + (int64_t)bh * L * DV + col0;
     const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)Qg, 0, L * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, L * D * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, L * DV * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)Og, 0, L * DV * 2 - 32 * w, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rO = __builtin_amdgcn_make_buffer_rsrc((void*)Og, 0, L * DV * 2 - 2 * col0, 0x00020000);
 
     // direct-load lane offsets (bytes from the stage's first row): load i of
-    // wave w fills rows 16w + 8i .. + 7 of a tile, lane l position l % 8 of
-    // row 16w + 8i + l / 8, fetching the unit that belongs there
-    uint32_t qko[2], vdo[2];
+    // wave w is the tile's wave-load j = NLQ w + i, which fills rows 8j .. 8j
+    // + 7, lane l position l % 8 of row 8j + l / 8, fetching the unit that
+    // belongs there
+    uint32_t qko[NLQ], vdo[NLQ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 16 * w + 8 * i + (lane >> 3);
+    for (int i = 0; i < NLQ; ++i) {
+        const int row = 8 * (NLQ * w + i) + (lane >> 3);
         qko[i] = (uint32_t)(row * D * 2 + 16 * ((lane & 7) ^ (kswz(row & 15) >> 1)));
         vdo[i] = (uint32_t)(row * DV * 2 + 16 * ((lane & 7) ^ vswz(row)));
     }
+    auto load_tile = [&](__amdgpu_buffer_rsrc_t r, bf16_t* tile, const uint32_t* off, int sq) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < NLQ; ++i) dma16(r, tile + 512 * (NLQ * w + i), off[i], sq);
+    };
     // LDS read offsets within a step's 16 rows (elements)
     const int fro = c16 * D, fsw = kswz(c16) >> 1;           // row fragments
     const int rr = 4 * g + (c16 >> 2), cq = c16 & 3;         // transposing reads: row, chunk quad
     const int kr = rr * D, krs = kswz(rr);
-    const int kro = kr + 4 * ((4 * w + cq) ^ krs);            // K[.][16w + 4cq ..]
-    const int vro = rr * DV + 8 * ((2 * w + (cq >> 1)) ^ vswz(rr)) + 4 * (cq & 1);   // V[.][16w + 4cq ..]
+    int kro[NCB], vro[NCB];                                   // K[.][c + 4cq ..], V[.][c + 4cq ..] of column block c
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int c = NCB * w + cb;
+        kro[cb] = kr + 4 * ((4 * c + cq) ^ krs);
+        vro[cb] = rr * DV + 8 * ((2 * c + (cq >> 1)) ^ vswz(rr)) + 4 * (cq & 1);
+    }
     const int vo = (c16 * DV + 4 * g) * 2;                    // output store (bytes)
     u32x2 pmask;
 #pragma unroll
@@ -642,113 +663,134 @@ __global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
         __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
     };
     using V0 = std::integral_constant<int, 0>;
+    // the ring's scalar offsets of the stage read and the stage refilled
+    auto advance = [](int& o) { o = (o + DS_STAGE == R * DS_STAGE) ? 0 : o + DS_STAGE; };
 
     // per (b, h, segment) map block of 32 KB: Delta as two bf16 [64][64]
     // row-major arrays (hi, lo: Delta = hi + lo to about 16 bits), then B
-    // in this lane's accumulator slots (fp32)
+    // in accumulator slots (fp32): column block c, tile t, lane l at slot
+    // (4c + t) * 64 + l
     const int64_t id = (int64_t)bh * nseg + seg;
     char* maps = reinterpret_cast<char*>(p.maps);
 
     // ================= pass 1: the segment's map (Delta, B)
     if (seg < nseg - 1) {
-        f32x4 SB[4], SD[4];
+        f32x4 SB[NCB][4], SD[NCB][4];
+        bf16x8 BopS[NCB][2], DopS[NCB][2], BopW[NCB][2], DopW[NCB][2];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) SB[t] = SD[t] = zero4();
-        bf16x8 BopS[2], DopS[2], BopW[2], DopW[2];
+        for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) BopS[kb] = DopS[kb] = BopW[kb] = DopW[kb] = bf16x8{};
+            for (int t = 0; t < 4; ++t) SB[cb][t] = SD[cb][t] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) BopS[cb][kb] = DopS[cb][kb] = BopW[cb][kb] = DopW[cb][kb] = bf16x8{};
+        }
         const int nst = len / DS_T;   // segments before the last hold whole stages
         auto issue = [&](int s, bf16_t* dst) __attribute__((always_inline)) {
             const int sq = (tok0 + DS_T * min(s, nst - 1)) * D * 2;
-#pragma unroll
-            for (int i = 0; i < 2; ++i) dma16(rK, dst + DS_TILE + 512 * (2 * w + i), qko[i], sq);
-#pragma unroll
-            for (int i = 0; i < 2; ++i) dma16(rV, dst + 2 * DS_TILE + 512 * (2 * w + i), vdo[i], sq);
+            load_tile(rK, dst + DS_TILE, qko, sq);
+            load_tile(rV, dst + 2 * DS_TILE, vdo, sq);
         };
         auto step = [&](const bf16_t* X, int j, int s16) __attribute__((always_inline)) {
             const bf16_t* Ks = X + DS_TILE + 16 * j * D;
             const bf16_t* Vs = X + 2 * DS_TILE + 16 * j * DV;
             const bf16x8 Kf0 = kfrag(Ks, 0), Kf1 = kfrag(Ks, 1);
-            f32x4 eB = zero4(), eD = zero4();
-            mma(eB, Kf0, ONE ? BopS[0] : BopW[0]);
-            mma(eB, Kf1, ONE ? BopS[1] : BopW[1]);
-            mma(eD, Kf0, ONE ? DopS[0] : DopW[0]);
-            mma(eD, Kf1, ONE ? DopS[1] : DopW[1]);
-            const f32x4 ks = to4(tr_read_d(Ks + kro));   // K[4g + r][16w + c16]: the I share of K A
-            const f32x4 vv = to4(tr_read_d(Vs + vro));
-            f32x4 vb, vd;
+            u32x2 VBb[NCB], VDb[NCB];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                vb[r] = eta * (vv[r] - eB[r]);
-                vd[r] = -eta * (eD[r] + ks[r]);
+            for (int cb = 0; cb < NCB; ++cb) {
+                f32x4 eB = zero4(), eD = zero4();
+                mma(eB, Kf0, ONE ? BopS[cb][0] : BopW[cb][0]);
+                mma(eB, Kf1, ONE ? BopS[cb][1] : BopW[cb][1]);
+                mma(eD, Kf0, ONE ? DopS[cb][0] : DopW[cb][0]);
+                mma(eD, Kf1, ONE ? DopS[cb][1] : DopW[cb][1]);
+                const f32x4 ks = to4(tr_read_d(Ks + kro[cb]));   // the I share of K A: K[4g + r][c + c16]
+                const f32x4 vv = to4(tr_read_d(Vs + vro[cb]));
+                f32x4 vb, vd;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    vb[r] = eta * (vv[r] - eB[r]);
+                    vd[r] = -eta * (eD[r] + ks[r]);
+                }
+                VBb[cb] = u32x2{pack2bf(vb[0], vb[1]), pack2bf(vb[2], vb[3])};
+                VDb[cb] = u32x2{pack2bf(vd[0], vd[1]), pack2bf(vd[2], vd[3])};
             }
-            const u32x2 VBb = u32x2{pack2bf(vb[0], vb[1]), pack2bf(vb[2], vb[3])};
-            const u32x2 VDb = u32x2{pack2bf(vd[0], vd[1]), pack2bf(vd[2], vd[3])};
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
                 const u32x2 kt = kT(Ks, t);
-                mma16(SB[t], kt, VBb);
-                mma16(SD[t], kt, VDb);
-            }
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                BopS[kb] = acc_to_frag_bf16(SB[2 * kb], SB[2 * kb + 1]);
-                DopS[kb] = acc_to_frag_bf16(SD[2 * kb], SD[2 * kb + 1]);
-            }
-            if (MBK == 2 && mb_end(16 * s16 + 16)) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    BopW[kb] = BopS[kb];
-                    DopW[kb] = DopS[kb];
+                for (int cb = 0; cb < NCB; ++cb) {
+                    mma16(SB[cb][t], kt, VBb[cb]);
+                    mma16(SD[cb][t], kt, VDb[cb]);
                 }
             }
-        };
-        // loads of a wave per stage: 4; after the stage read in iteration s
-        // the wave has issued the loads of the R - 2 stages that follow it
 #pragma unroll
-        for (int s = 0; s < DS_R - 1; ++s) issue(s, ring + s * DS_STAGE);
-        int rdo = 0, wro = (DS_R - 1) * DS_STAGE;
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    BopS[cb][kb] = acc_to_frag_bf16(SB[cb][2 * kb], SB[cb][2 * kb + 1]);
+                    DopS[cb][kb] = acc_to_frag_bf16(SD[cb][2 * kb], SD[cb][2 * kb + 1]);
+                }
+            if (MBK == 2 && mb_end(16 * s16 + 16)) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        BopW[cb][kb] = BopS[cb][kb];
+                        DopW[cb][kb] = DopS[cb][kb];
+                    }
+            }
+        };
+        // a wave issues 2 NLQ loads per stage; after the stage read in
+        // iteration s it has issued the loads of the R - 2 stages that follow
+#pragma unroll
+        for (int s = 0; s < R - 1; ++s) issue(s, ring + s * DS_STAGE);
+        int rdo = 0, wro = (R - 1) * DS_STAGE;
         for (int s = 0; s < nst; ++s) {
-            wait_vm(std::integral_constant<int, 4 * (DS_R - 2)>{});
+            wait_vm(std::integral_constant<int, 2 * NLQ * (R - 2)>{});
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
             const int rd_off = rdo, wr_off = wro;
-            rdo = (rdo + DS_STAGE == DS_R * DS_STAGE) ? 0 : rdo + DS_STAGE;
-            wro = (wro + DS_STAGE == DS_R * DS_STAGE) ? 0 : wro + DS_STAGE;
+            advance(rdo);
+            advance(wro);
             ring_step1(ring + __builtin_amdgcn_readfirstlane(wr_off), ring + __builtin_amdgcn_readfirstlane(rd_off),
-                       [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + DS_R - 1, dst); },
+                       [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + R - 1, dst); },
                        [&](const bf16_t* X) __attribute__((always_inline)) {
 #pragma unroll
                            for (int j = 0; j < DS_T / 16; ++j) step(X, j, (tok0 >> 4) + 4 * s + j);
                        });
             if (SEND && mb_end(tok0 + DS_T * (s + 1))) {
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    BopW[kb] = BopS[kb];
-                    DopW[kb] = DopS[kb];
-                }
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) {
+                        BopW[cb][kb] = BopS[cb][kb];
+                        DopW[cb][kb] = DopS[cb][kb];
+                    }
             }
         }
         wait_vm(V0{});   // the clamped loads still in flight
         // publish: Delta row-major (row = feature of the state row, column =
-        // the input feature 16w + c16) as hi and lo, B in this lane's slots.
+        // the input feature c + c16) as hi and lo, B in accumulator slots.
         // The stores are device-coherent (sc1: written through to memory), so
         // once they are complete every XCD reads them with sc1 loads, and the
         // flag needs no release (which would write back this XCD's whole L2)
         const __amdgpu_buffer_rsrc_t rP =
             __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(maps + id * DS_MAP), 0, DS_MAP, 0x00020000);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, SB[t]), rP,
-                                                   (uint32_t)(DS_BOFF + 16 * ((w * 4 + t) * 64 + lane)), 0, DS_SC1);
-            u32x2 hi, lo;
-            split4(SD[t], hi, lo);
+        for (int cb = 0; cb < NCB; ++cb) {
+            const int c = NCB * w + cb;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint32_t e = 2u * (uint32_t)(feat(16 * t + 4 * g + r) * DV + 16 * w + c16);
-                const uint32_t sh = 16 * (r & 1);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hi[r >> 1] >> sh), rP, e, 0, DS_SC1);
-                __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(lo[r >> 1] >> sh), rP, e + 2 * D * DV, 0, DS_SC1);
+            for (int t = 0; t < 4; ++t) {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, SB[cb][t]), rP,
+                                                       (uint32_t)(DS_BOFF + 16 * ((c * 4 + t) * 64 + lane)), 0, DS_SC1);
+                u32x2 hi, lo;
+                split4(SD[cb][t], hi, lo);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t e = 2u * (uint32_t)(feat(16 * t + 4 * g + r) * DV + 16 * c + c16);
+                    const uint32_t sh = 16 * (r & 1);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(hi[r >> 1] >> sh), rP, e, 0, DS_SC1);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(lo[r >> 1] >> sh), rP, e + 2 * D * DV, 0, DS_SC1);
+                }
             }
         }
         wait_vm(V0{});   // this wave's stores are complete
@@ -757,13 +799,15 @@ __global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
     }
 
     // ================= the start state: W0, then the maps of segments 0 .. seg-1
-    f32x4 Sacc[4];
+    f32x4 Sacc[NCB][4];
     {
         const float* W0 = p.W0 + (int64_t)bh * p.W0_stride;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Sacc[t][r] = W0[feat(16 * t + 4 * g + r) * DV + 16 * w + c16];
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[cb][t][r] = W0[feat(16 * t + 4 * g + r) * DV + col0 + 16 * cb + c16];
     }
     if (seg > 0) {
         // every map this segment composes was published by a workgroup with
@@ -789,67 +833,77 @@ __global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
                 __hip_atomic_store(p.flags + (int64_t)nheads * nseg + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
-        // Delta_j (hi, lo) of up to DS_MB maps at a time go into the ring by
+        // Delta_j (hi, lo) of up to MB maps at a time go into the ring by
         // direct loads (16 KB per map; the 16-byte unit u of row r at position
         // u ^ (r & 7)), B_j into registers; then the maps are applied in order
         const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
             uniform_ptr(maps + (int64_t)bh * nseg * DS_MAP), 0, nseg * DS_MAP, 0x00020000);
-        uint32_t mo[4];
+        constexpr int NMO = 16 / NW;   // direct loads per wave per map (1024 slots of 16 bytes)
+        uint32_t mo[NMO];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int slot = 64 * (4 * w + i) + lane, row = (slot >> 3) & 63;
+        for (int i = 0; i < NMO; ++i) {
+            const int slot = 64 * (NMO * w + i) + lane, row = (slot >> 3) & 63;
             // slots 0..511: hi rows, 512..1023: lo rows
             mo[i] = (uint32_t)((slot >> 9) * D * DV * 2 + row * DV * 2 + 16 * ((slot & 7) ^ (row & 7)));
         }
-        for (int j0 = 0; j0 < seg; j0 += DS_MB) {
-            const int nb = min(DS_MB, seg - j0);
-            f32x4 bj[DS_MB][4];
+        for (int j0 = 0; j0 < seg; j0 += MB) {
+            const int nb = min(MB, seg - j0);
+            f32x4 bj[MB][NCB][4];
 #pragma unroll
-            for (int x = 0; x < DS_MB; ++x) {
+            for (int x = 0; x < MB; ++x) {
                 if (x < nb) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rM, (lds_void_t*)(ring + x * 2 * D * DV + 512 * (4 * w + i)),
-                                                                 16, mo[i], (j0 + x) * DS_MAP, 0, DS_SC1);
+                    for (int i = 0; i < NMO; ++i) dma16_sc1(rM, ring + x * 2 * D * DV + 512 * (NMO * w + i), mo[i], (j0 + x) * DS_MAP);
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        bj[x][t] = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       rM, (uint32_t)(DS_BOFF + 16 * ((w * 4 + t) * 64 + lane)), (j0 + x) * DS_MAP, DS_SC1));
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            bj[x][cb][t] = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rM, (uint32_t)(DS_BOFF + 16 * (((NCB * w + cb) * 4 + t) * 64 + lane)),
+                                           (j0 + x) * DS_MAP, DS_SC1));
                 }
             }
             wait_vm(V0{});
             __syncthreads();
 #pragma unroll
-            for (int x = 0; x < DS_MB; ++x) {
+            for (int x = 0; x < MB; ++x) {
                 if (x < nb) {
                     // Y = Delta_j W: A operand rows = state row positions
                     // 16t + c16, k = features 32kb + 8g ..; B operand = W in
                     // the accperm order, split into hi and lo
                     const bf16_t* Mh = ring + x * 2 * D * DV;
-                    bf16x8 whi[2], wlo[2];
+                    bf16x8 whi[NCB][2], wlo[NCB][2];
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        u32x2 h0, l0, h1, l1;
-                        split4(Sacc[2 * kb], h0, l0);
-                        split4(Sacc[2 * kb + 1], h1, l1);
-                        whi[kb] = join2(h0, h1);
-                        wlo[kb] = join2(l0, l1);
-                    }
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            u32x2 h0, l0, h1, l1;
+                            split4(Sacc[cb][2 * kb], h0, l0);
+                            split4(Sacc[cb][2 * kb + 1], h1, l1);
+                            whi[cb][kb] = join2(h0, h1);
+                            wlo[cb][kb] = join2(l0, l1);
+                        }
 #pragma unroll
                     for (int t = 0; t < 4; ++t) {
                         const int row = feat(16 * t + c16);
-                        f32x4 y = zero4();
+                        f32x4 y[NCB];
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) y[cb] = zero4();
 #pragma unroll
                         for (int kb = 0; kb < 2; ++kb) {
                             const int e = row * DV + 8 * ((4 * kb + g) ^ (row & 7));
                             const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(Mh + e);
                             const bf16x8 alo = *reinterpret_cast<const bf16x8*>(Mh + D * DV + e);
-                            mma(y, ahi, whi[kb]);
-                            mma(y, alo, whi[kb]);
-                            mma(y, ahi, wlo[kb]);
+#pragma unroll
+                            for (int cb = 0; cb < NCB; ++cb) {
+                                mma(y[cb], ahi, whi[cb][kb]);
+                                mma(y[cb], alo, whi[cb][kb]);
+                                mma(y[cb], ahi, wlo[cb][kb]);
+                            }
                         }
-                        Sacc[t] += y + bj[x][t];
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) Sacc[cb][t] += y[cb] + bj[x][cb][t];
                     }
                 }
             }
@@ -858,20 +912,19 @@ __global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
     }
 
     // ================= pass 3: the forward over this segment's tokens
-    bf16x8 Sop[2], Wop[2];
+    bf16x8 Sop[NCB][2], Wop[NCB][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) Sop[kb] = Wop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Sop[cb][kb] = Wop[cb][kb] = acc_to_frag_bf16(Sacc[cb][2 * kb], Sacc[cb][2 * kb + 1]);
     wait_vm(V0{});
     __syncthreads();   // every wave is past pass 1 before the ring is refilled
     const int nst = (len + DS_T - 1) / DS_T;
     auto issue = [&](int s, bf16_t* dst) __attribute__((always_inline)) {
         const int sq = (tok0 + DS_T * min(s, nst - 1)) * D * 2;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) dma16(rQ, dst + 512 * (2 * w + i), qko[i], sq);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) dma16(rK, dst + DS_TILE + 512 * (2 * w + i), qko[i], sq);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) dma16(rV, dst + 2 * DS_TILE + 512 * (2 * w + i), vdo[i], sq);
+        load_tile(rQ, dst, qko, sq);
+        load_tile(rK, dst + DS_TILE, qko, sq);
+        load_tile(rV, dst + 2 * DS_TILE, vdo, sq);
     };
     auto step = [&](const bf16_t* X, int j, int s16) __attribute__((always_inline)) {
         const bf16_t* Qs = X + 16 * j * D;
@@ -879,48 +932,67 @@ __global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
         const bf16_t* Vs = X + 2 * DS_TILE + 16 * j * DV;
         const bf16x8 Kf0 = kfrag(Ks, 0), Kf1 = kfrag(Ks, 1);
         const bf16x8 Qf0 = kfrag(Qs, 0), Qf1 = kfrag(Qs, 1);
-        // E = K W_n;  P^T = K Q^T (causal j <= i);  O^T partial = S~^T Q^T
-        f32x4 e = zero4(), pt = zero4(), o = zero4();
-        mma(e, Kf0, ONE ? Sop[0] : Wop[0]);
-        mma(e, Kf1, ONE ? Sop[1] : Wop[1]);
+        // P^T = K Q^T (causal j <= i), shared by the column blocks
+        f32x4 pt = zero4();
         mma(pt, Kf0, Qf0);
         mma(pt, Kf1, Qf1);
-        mma(o, Sop[0], Qf0);
-        mma(o, Sop[1], Qf1);
-        const f32x4 vv = to4(tr_read_d(Vs + vro));
-        f32x4 vt;
+        u32x2 VB[NCB];
+        f32x4 o[NCB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) vt[r] = eta * (vv[r] - e[r]);
-        const u32x2 VB = u32x2{pack2bf(vt[0], vt[1]), pack2bf(vt[2], vt[3])};
+        for (int cb = 0; cb < NCB; ++cb) {
+            // E = K W_n;  O^T partial = S~^T Q^T
+            f32x4 e = zero4();
+            o[cb] = zero4();
+            mma(e, Kf0, ONE ? Sop[cb][0] : Wop[cb][0]);
+            mma(e, Kf1, ONE ? Sop[cb][1] : Wop[cb][1]);
+            mma(o[cb], Sop[cb][0], Qf0);
+            mma(o[cb], Sop[cb][1], Qf1);
+            const f32x4 vv = to4(tr_read_d(Vs + vro[cb]));
+            f32x4 vt;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) mma16(Sacc[t], kT(Ks, t), VB);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) Sop[kb] = acc_to_frag_bf16(Sacc[2 * kb], Sacc[2 * kb + 1]);
-        if (MBK == 2 && mb_end(16 * s16 + 16)) {
-            Wop[0] = Sop[0];
-            Wop[1] = Sop[1];
+            for (int r = 0; r < 4; ++r) vt[r] = eta * (vv[r] - e[r]);
+            VB[cb] = u32x2{pack2bf(vt[0], vt[1]), pack2bf(vt[2], vt[3])};
         }
-        // O^T += V~^T P^T, store O rows (4 consecutive columns per lane)
-        mma16(o, VB, u32x2{pack2bf(pt[0], pt[1]) & pmask[0], pack2bf(pt[2], pt[3]) & pmask[1]});
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, u32x2{pack2bf(o[0], o[1]), pack2bf(o[2], o[3])}),
-                                              rO, vo, 16 * s16 * DV * 2, 0);
-    };
-    // loads of a wave per stage: 6, stores 4 (one per step).  Operations
-    // issued after the loads of the stage read in iteration s: for s < R - 1
-    // (stages of the prologue) the loads of prologue stages s + 1 .. R - 2
-    // and iterations 0 .. s - 1, 6 (R - 2) + 4 s; after that the stores of
-    // the iteration that issued them and R - 2 whole iterations, 4 + 10 (R - 2)
 #pragma unroll
-    for (int s = 0; s < DS_R - 1; ++s) issue(s, ring + s * DS_STAGE);
-    int rdo = 0, wro = (DS_R - 1) * DS_STAGE;
+        for (int t = 0; t < 4; ++t) {
+            const u32x2 kt = kT(Ks, t);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) mma16(Sacc[cb][t], kt, VB[cb]);
+        }
+        const u32x2 pm = u32x2{pack2bf(pt[0], pt[1]) & pmask[0], pack2bf(pt[2], pt[3]) & pmask[1]};
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) Sop[cb][kb] = acc_to_frag_bf16(Sacc[cb][2 * kb], Sacc[cb][2 * kb + 1]);
+            if (MBK == 2 && mb_end(16 * s16 + 16)) {
+                Wop[cb][0] = Sop[cb][0];
+                Wop[cb][1] = Sop[cb][1];
+            }
+            // O^T += V~^T P^T, store O rows (4 consecutive columns per lane)
+            mma16(o[cb], VB[cb], pm);
+            __builtin_amdgcn_raw_buffer_store_b64(
+                __builtin_bit_cast(u32x2, u32x2{pack2bf(o[cb][0], o[cb][1]), pack2bf(o[cb][2], o[cb][3])}), rO,
+                vo + 32 * cb, 16 * s16 * DV * 2, 0);
+        }
+    };
+    // a wave issues NL3 loads and NST stores (one per step and column block)
+    // per stage.  Operations issued after the loads of the stage read in
+    // iteration s: for s < R - 1 (stages of the prologue) the loads of
+    // prologue stages s + 1 .. R - 2 and iterations 0 .. s - 1,
+    // NL3 (R - 2) + NST s; after that the stores of the iteration that
+    // issued them and R - 2 whole iterations, NST + (NL3 + NST) (R - 2)
+    constexpr int NL3 = 3 * NLQ, NST = 4 * NCB;
+#pragma unroll
+    for (int s = 0; s < R - 1; ++s) issue(s, ring + s * DS_STAGE);
+    int rdo = 0, wro = (R - 1) * DS_STAGE;
     auto wait_stage = [&](int s) __attribute__((always_inline)) {
-        if (s >= DS_R - 1) {
-            wait_vm(std::integral_constant<int, 4 + 10 * (DS_R - 2)>{});
+        if (s >= R - 1) {
+            wait_vm(std::integral_constant<int, NST + (NL3 + NST) * (R - 2)>{});
             return;
         }
-        static_for<DS_R - 1>([&](auto I) __attribute__((always_inline)) {
+        static_for<R - 1>([&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
-            if (s == i) wait_vm(std::integral_constant<int, 6 * (DS_R - 2) + 4 * i>{});
+            if (s == i) wait_vm(std::integral_constant<int, NL3 * (R - 2) + NST * i>{});
         });
     };
     for (int s = 0; s < nst; ++s) {
@@ -928,17 +1000,20 @@ __global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         const int rd_off = rdo, wr_off = wro;
-        rdo = (rdo + DS_STAGE == DS_R * DS_STAGE) ? 0 : rdo + DS_STAGE;
-        wro = (wro + DS_STAGE == DS_R * DS_STAGE) ? 0 : wro + DS_STAGE;
+        advance(rdo);
+        advance(wro);
         ring_step1(ring + __builtin_amdgcn_readfirstlane(wr_off), ring + __builtin_amdgcn_readfirstlane(rd_off),
-                   [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + DS_R - 1, dst); },
+                   [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + R - 1, dst); },
                    [&](const bf16_t* X) __attribute__((always_inline)) {
 #pragma unroll
                        for (int j = 0; j < DS_T / 16; ++j) step(X, j, (tok0 >> 4) + 4 * s + j);
                    });
         if (SEND && mb_end(tok0 + DS_T * (s + 1))) {
-            Wop[0] = Sop[0];
-            Wop[1] = Sop[1];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                Wop[cb][0] = Sop[cb][0];
+                Wop[cb][1] = Sop[cb][1];
+            }
         }
     }
     wait_vm(V0{});   // the clamped loads still in flight
@@ -946,9 +1021,11 @@ __global__ __launch_bounds__(256) void dual_seg_kernel(DualParams p) {
     if (seg == nseg - 1 && p.W_final) {
         float* Wf = p.W_final + (int64_t)bh * D * DV;
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Wf[feat(16 * t + 4 * g + r) * DV + 16 * w + c16] = Sacc[t][r];
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Wf[feat(16 * t + 4 * g + r) * DV + col0 + 16 * cb + c16] = Sacc[cb][t][r];
     }
 }
 
@@ -964,24 +1041,30 @@ bool dual_supported(int dtype, int d, int dv, int minibatch) {
 namespace {
 
 // Segmented plan for bf16 mini-batches of a multiple of 16: enough segments
-// for one workgroup of four waves per CU (1024 waves: the steps are bound by
-// instruction issue, and a second wave per SIMD measured no faster while it
-// doubles the maps to compose), each a whole number of mini-batches and of
-// 64-token stages, at least 256 tokens long.
+// to fill the CUs with workgroups (kDualNW waves each, one wave per SIMD),
+// each a whole number of mini-batches and of 64-token stages, at least 256
+// tokens long.  Four waves of one column block each: a step is bound by
+// instruction issue, so two column blocks per wave (two-wave workgroups,
+// twice the segments) took twice as long per step and lost the time the
+// shared fragments saved to the longer composition.
+#ifndef DUAL_NW
+#define DUAL_NW 4
+#endif
+constexpr int kDualNW = DUAL_NW;                  // waves per workgroup
+constexpr int kCUs = 256;
+constexpr int kDualSlots = kCUs * 4 / kDualNW;     // workgroups resident at once
+constexpr int kDualMinSeg = 256;
+constexpr int kDualPolls = 1 << 22;   // polls of ~0.1 us before a wait gives up
 struct DualSegPlan {
     int nseg, seg_len;
 };
-constexpr int kDualWaves = 1024;
-constexpr int kCUs = 256;
-constexpr int kDualMinSeg = 256;
-constexpr int kDualPolls = 1 << 22;   // polls of ~0.1 us before a wait gives up
 
 DualSegPlan dual_seg_plan(int dtype, int B, int H, int L, int d, int dv, int mb) {
     DualSegPlan pl{1, L};
     if (dtype != 1 || d != 64 || dv != 64 || mb % 16 != 0) return pl;
     if ((int64_t)L * 128 >= (int64_t)1 << 31) return pl;   // 32-bit buffer ranges
     const int64_t nheads = (int64_t)B * H;
-    if (nheads * 4 >= kDualWaves / 2) return pl;   // two segments or fewer: one chain each
+    if (nheads * 2 > kDualSlots) return pl;   // two segments would not all be resident
     int64_t gcd = 64, x = mb;
     while (x) {
         const int64_t t = gcd % x;
@@ -989,7 +1072,7 @@ DualSegPlan dual_seg_plan(int dtype, int B, int H, int L, int d, int dv, int mb)
         x = t;
     }
     const int64_t unit = (int64_t)mb / gcd * 64;   // lcm(mb, 64)
-    const int64_t want = (kDualWaves / 4 + nheads - 1) / nheads;
+    const int64_t want = (kDualSlots + nheads - 1) / nheads;
     int64_t seg = ((L + want - 1) / want + unit - 1) / unit * unit;
     const int64_t min_seg = (kDualMinSeg + unit - 1) / unit * unit;
     if (seg < min_seg) seg = min_seg;
@@ -1000,6 +1083,13 @@ DualSegPlan dual_seg_plan(int dtype, int B, int H, int L, int d, int dv, int mb)
     return pl;
 }
 size_t dual_flag_bytes(int64_t n) { return (size_t)(((n + 2) * 4 + 255) / 256 * 256); }
+
+void launch_dual_seg(const DualParams& p, unsigned nwg, hipStream_t s) {
+    const dim3 grid(nwg), block(64 * kDualNW);
+    if (p.minibatch == 16) hipLaunchKernelGGL((dual_seg_kernel<0, kDualNW>), grid, block, 0, s, p);
+    else if (p.minibatch % DS_T == 0) hipLaunchKernelGGL((dual_seg_kernel<1, kDualNW>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((dual_seg_kernel<2, kDualNW>), grid, block, 0, s, p);
+}
 
 }  // namespace
 
@@ -1037,25 +1127,19 @@ hipError_t launch_dual_fwd(const DualParams& pin, int dtype, hipStream_t s) {
             hipLaunchKernelGGL(dual_flags_clear_kernel, dim3((nflags + 255) / 256), dim3(256), 0, s, p.flags, nflags);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            const dim3 grid((unsigned)n), block(256);
-            if (p.minibatch == 16) hipLaunchKernelGGL((dual_seg_kernel<0>), grid, block, 0, s, p);
-            else if (p.minibatch % DS_T == 0) hipLaunchKernelGGL((dual_seg_kernel<1>), grid, block, 0, s, p);
-            else hipLaunchKernelGGL((dual_seg_kernel<2>), grid, block, 0, s, p);
+            launch_dual_seg(p, (unsigned)n, s);
             return hipGetLastError();
         }
         const DualParams& p = pin;
         if ((int64_t)p.B * p.H > kCUs / 4) {
             // more sequences than the one-wave-per-CU chain kernel runs at
-            // once: one workgroup of four waves per sequence, unsegmented
+            // once: one workgroup per sequence, unsegmented
             DualParams q = p;
             q.nseg = 1;
             q.seg_len = q.L;
             q.flags = nullptr;
             q.maps = nullptr;
-            const dim3 grid((unsigned)(q.B * q.H)), block(256);
-            if (q.minibatch == 16) hipLaunchKernelGGL((dual_seg_kernel<0>), grid, block, 0, s, q);
-            else if (q.minibatch % DS_T == 0) hipLaunchKernelGGL((dual_seg_kernel<1>), grid, block, 0, s, q);
-            else hipLaunchKernelGGL((dual_seg_kernel<2>), grid, block, 0, s, q);
+            launch_dual_seg(q, (unsigned)(q.B * q.H), s);
             return hipGetLastError();
         }
         // one wave per (b, h, 16-column tile), one wave per CU (its ring takes 92 KB)

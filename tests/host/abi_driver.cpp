@@ -51,7 +51,7 @@ hipError_t launch_state_scan(int, int, int, int, int, int, const float*, const f
 hipError_t launch_dual_fwd(const DualParams&, int, hipStream_t) { return hipSuccess; }
 bool dual_supported(int, int d, int dv, int mb) { return d == 64 && dv == 64 && mb >= 1; }
 size_t dual_workspace(int dtype, int B, int H, int, int d, int dv, int mb) {
-    return (dtype == 1 && d == 64 && dv == 64 && mb % 16 == 0 && B * H < 128) ? 4096 : 0;
+    return (dtype == 1 && d == 64 && dv == 64 && mb % 16 == 0 && B * H <= 128) ? 4096 : 0;
 }
 int64_t dual_error_word(int dtype, int B, int H, int L, int d, int dv, int mb) {
     return dual_workspace(dtype, B, H, L, d, dv, mb) ? 1 : -1;

@@ -256,7 +256,8 @@ def test_dual_segment_workspace(lib):
     assert st == OK and need == 1280 + 64 * 4 * 32768
     st, need2 = ws(4, 16, 8192, 2048)
     assert st == OK and need2 == need                  # 4 segments of one mini-batch
-    assert ws(2, 64, 8192, 16) == (OK, 0)        # 128 sequences: one workgroup per CU unsegmented
+    assert ws(2, 64, 8192, 16) == (OK, 1280 + 128 * 2 * 32768)   # 128 sequences: 2 segments
+    assert ws(4, 64, 8192, 16) == (OK, 0)        # 256 sequences fill the chip unsegmented
     assert ws(1, 3, 1000, 48) == (OK, 256 + 3 * 3 * 32768)    # 3 segments of 384 tokens
     assert ws(4, 16, 8192, 40) == (OK, 0)        # mini-batches not of a multiple of 16
     assert ws(4, 16, 8192, 16, dt=0) == (OK, 0)  # fp32
@@ -280,7 +281,7 @@ def test_dual_segment_workspace(lib):
     assert stat(B, H, L, 64, 64, 16, 1, None, 0, None, ctypes.byref(flag)) == OK and flag.value == 0
     assert stat(B, H, L, 64, 64, 16, 1, big, need, None, None) == ERR_NULL
     assert stat(B, H, L, 64, 64, 16, 1, big, need - 1, None, ctypes.byref(flag)) == ERR_WS
-    assert stat(8, 16, L, 64, 64, 16, 1, big, 0, None, ctypes.byref(flag)) == OK and flag.value == 0
+    assert stat(16, 16, L, 64, 64, 16, 1, big, 0, None, ctypes.byref(flag)) == OK and flag.value == 0
 
 
 def test_decode_rejects_before_launch(lib):

@@ -402,12 +402,12 @@ def test_dual_segmented(mb, L, B, H):
 
 @pytest.mark.parametrize("mb", [16, 64, 48])
 def test_dual_many_sequences(mb):
-    """Enough sequences to fill the chip without segments (B*H = 128, more
-    than one wave per CU covers): one workgroup of four waves per sequence."""
-    inp = W.gen_dual(B=2, H=64, L=300, minibatch=mb)
+    """Enough sequences to fill the chip without segments (B*H = 512, more
+    than one wave per CU covers): one workgroup per sequence."""
+    inp = W.gen_dual(B=4, H=128, L=300, minibatch=mb)
     assert not dual_segments(inp)
-    say(f"dual bf16 B2 H64 b{mb} L300")
-    check_dual(inp, run_dual(inp, True), [(0, 0), (1, 63), (1, 7)], TOL["bf16"], f"dual many b{mb}")
+    say(f"dual bf16 B4 H128 b{mb} L300")
+    check_dual(inp, run_dual(inp, True), [(0, 0), (3, 127), (1, 7)], TOL["bf16"], f"dual many b{mb}")
 
 
 def test_dual_segmented_alternating_inputs():
