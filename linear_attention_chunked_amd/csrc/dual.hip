@@ -524,6 +524,9 @@ __global__ __launch_bounds__(64) void dual_ring_kernel(DualParams p) {
 // ring stages: 4 with one four-wave workgroup per CU (96 KB), 3 with two
 // two-wave workgroups per CU (72 KB each)
 constexpr int dual_ring_stages(int nw) { return nw == 4 ? 4 : 3; }
+#ifndef DUAL_GROUPED
+#define DUAL_GROUPED 1
+#endif
 constexpr int DS_T = 64;                       // tokens per stage (four steps)
 constexpr int DS_TILE = DS_T * 64;             // elements of one [64][64] tile
 constexpr int DS_STAGE = 3 * DS_TILE;          // Q | K | V, elements per stage
@@ -560,6 +563,13 @@ TTT_DEV void split4(const f32x4& x, u32x2& hi, u32x2& lo) {
     lo = u32x2{pack2bf(x[0] - h0, x[1] - h1), pack2bf(x[2] - h2, x[3] - h3)};
 }
 TTT_DEV bf16x8 join2(const u32x2& a, const u32x2& b) { return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]}); }
+// two 16-token products in one 16x16x32 MFMA: lane group g's k slots 0..3
+// are tokens 4g..4g+3 of the first tile, slots 4..7 those of the second
+// (operands a0|a1 and b0|b1 in the same order)
+TTT_DEV void mma2x16(f32x4& acc, const u32x2& a0, const u32x2& a1, const u32x2& b0, const u32x2& b1) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(join2(a0, a1), join2(b0, b1), acc, 0, 0, 0);
+}
+TTT_DEV u32x2 pack4(const f32x4& x) { return u32x2{pack2bf(x[0], x[1]), pack2bf(x[2], x[3])}; }
 // a pointer the compiler may not prove uniform, made scalar (buffer
 // descriptors built from vector registers need a loop per access)
 TTT_DEV void* uniform_ptr(const void* p) {
@@ -581,6 +591,8 @@ __global__ __launch_bounds__(64 * NW) void dual_seg_kernel(DualParams p) {
     constexpr int R = dual_ring_stages(NW);
     constexpr int NLQ = 8 / NW;          // direct loads per wave per [64][64] tile
     constexpr int MB = DS_MB / NCB;      // maps staged per batch of the composition
+    // pass 1 takes a stage as one group of four tiles (see its group lambda)
+    constexpr bool GROUPED = (MBK != 2) && (NCB == 1) && DUAL_GROUPED;
     // the only LDS array (see ring_step1); its first word carries the ticket
     __shared__ __attribute__((aligned(16))) bf16_t ring[R * DS_STAGE];
 
@@ -739,6 +751,82 @@ __global__ __launch_bounds__(64 * NW) void dual_seg_kernel(DualParams p) {
                     }
             }
         };
+        // One stage as a group of four 16-token tiles (one-step mini-batches,
+        // or mini-batches that end only at stage ends, one column block per
+        // wave).  Every E_j takes the state the group starts from, and with
+        // one-step mini-batches the tiles before j add their share through
+        // the Gram blocks G_ji = K_j K_i^T (state-free, off the chain):
+        //     E_j = K_j W + sum_{i<j} G_ji V~_i,
+        // the state takes all four tiles in two 32-token products and its
+        // bf16 copies are refreshed once per stage.  (The same grouping of
+        // pass 3, with the outputs as the start state read by Q plus causal
+        // attention over the group, measured slower: its 28 independent
+        // readout and score products per stage did not pay for the shorter
+        // chain.)
+        auto group = [&](const bf16_t* X) __attribute__((always_inline)) {
+            const bf16_t* Ks = X + DS_TILE;
+            const bf16_t* Vs = X + 2 * DS_TILE;
+            bf16x8 Kf[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) Kf[j][kb] = kfrag(Ks + 16 * j * D, kb);
+            u32x2 G[4][4];   // G[j][i], i < j: A operand of G_ji (row t_j = c16, k = t_i)
+            if (ONE) {
+#pragma unroll
+                for (int j = 1; j < 4; ++j)
+#pragma unroll
+                    for (int i = 0; i < j; ++i) {
+                        f32x4 gt = zero4();
+                        mma(gt, Kf[i][0], Kf[j][0]);
+                        mma(gt, Kf[i][1], Kf[j][1]);
+                        G[j][i] = pack4(gt);
+                    }
+            }
+            f32x4 eB[4], eD[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                eB[j] = eD[j] = zero4();
+                mma(eB[j], Kf[j][0], ONE ? BopS[0][0] : BopW[0][0]);
+                mma(eB[j], Kf[j][1], ONE ? BopS[0][1] : BopW[0][1]);
+                mma(eD[j], Kf[j][0], ONE ? DopS[0][0] : DopW[0][0]);
+                mma(eD[j], Kf[j][1], ONE ? DopS[0][1] : DopW[0][1]);
+            }
+            u32x2 VBb[4], VDb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (ONE) {
+#pragma unroll
+                    for (int i = 0; i < j; ++i) {
+                        mma16(eB[j], G[j][i], VBb[i]);
+                        mma16(eD[j], G[j][i], VDb[i]);
+                    }
+                }
+                const f32x4 ks = to4(tr_read_d(Ks + 16 * j * D + kro[0]));   // the I share of K A
+                const f32x4 vv = to4(tr_read_d(Vs + 16 * j * DV + vro[0]));
+                f32x4 vb, vd;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    vb[r] = eta * (vv[r] - eB[j][r]);
+                    vd[r] = -eta * (eD[j][r] + ks[r]);
+                }
+                VBb[j] = pack4(vb);
+                VDb[j] = pack4(vd);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x2 k0 = kT(Ks, t), k1 = kT(Ks + 16 * D, t), k2 = kT(Ks + 32 * D, t), k3 = kT(Ks + 48 * D, t);
+                mma2x16(SB[0][t], k0, k1, VBb[0], VBb[1]);
+                mma2x16(SB[0][t], k2, k3, VBb[2], VBb[3]);
+                mma2x16(SD[0][t], k0, k1, VDb[0], VDb[1]);
+                mma2x16(SD[0][t], k2, k3, VDb[2], VDb[3]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                BopS[0][kb] = acc_to_frag_bf16(SB[0][2 * kb], SB[0][2 * kb + 1]);
+                DopS[0][kb] = acc_to_frag_bf16(SD[0][2 * kb], SD[0][2 * kb + 1]);
+            }
+        };
         // a wave issues 2 NLQ loads per stage; after the stage read in
         // iteration s it has issued the loads of the R - 2 stages that follow
 #pragma unroll
@@ -754,8 +842,12 @@ __global__ __launch_bounds__(64 * NW) void dual_seg_kernel(DualParams p) {
             ring_step1(ring + __builtin_amdgcn_readfirstlane(wr_off), ring + __builtin_amdgcn_readfirstlane(rd_off),
                        [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + R - 1, dst); },
                        [&](const bf16_t* X) __attribute__((always_inline)) {
+                           if constexpr (GROUPED) {
+                               group(X);
+                           } else {
 #pragma unroll
-                           for (int j = 0; j < DS_T / 16; ++j) step(X, j, (tok0 >> 4) + 4 * s + j);
+                               for (int j = 0; j < DS_T / 16; ++j) step(X, j, (tok0 >> 4) + 4 * s + j);
+                           }
                        });
             if (SEND && mb_end(tok0 + DS_T * (s + 1))) {
 #pragma unroll
