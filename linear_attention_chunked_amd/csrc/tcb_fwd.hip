@@ -498,10 +498,82 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
                 if (c + 1 < c_end) kv_store(buf ^ 1, NXT);
                 __syncthreads();
             };
-            for (int c = c_begin; c < c_end; c += D) {
-                step(c, J0{}, J1{});
-                if (c + 1 < c_end) step(c + 1, J1{}, J2{});
-                if (c + 2 < c_end) step(c + 2, J2{}, J0{});
+            // With momentum (beta <= 0.95) the aggregate of the segment's n
+            // tokens is X = sum_s w_{n-1-s} g_s = (U - beta Y) / (1 - beta)
+            // (w_m = (1 - beta^{m+1}) / (1 - beta)), with U = sum_s g_s and
+            // Y = sum_s beta^{n-1-s} g_s the momentum aggregate.  So every
+            // chunk stages only the eta-scaled copy of V and adds to U, and Y,
+            // whose weights fall below 2^-30 within 30 / -log2(beta) tokens,
+            // runs its recurrence over the last chunks only.  (Closer to 1,
+            // the 1 / (1 - beta) factor would amplify rounding; those betas
+            // take the chunk recurrence of S and m above.)
+            const bool split = MOM && p.beta <= 0.95f;
+            const int tail_from = split ? c_end - min(c_end - c_begin, (int)ceil(30.0 / -log2((double)p.beta) / CS))
+                                        : c_end;
+            auto kv_store_split = [&](int buf, auto SET, bool tail) {
+                constexpr int st = decltype(SET)::value;
+#pragma unroll
+                for (int x = 0; x < UQ; ++x) *reinterpret_cast<u32x4*>(&sK[buf][loff_q[x]]) = ak[st][x];
+                if (tid < NVC) {
+                    const float e = __shfl(ae[st], row_v);
+                    *reinterpret_cast<u32x4*>(&sV[buf][0][loff_v]) = scale_row(av[st], e);
+                    if (tail)
+                        *reinterpret_cast<u32x4*>(&sV[buf][2 % NV][loff_v]) =
+                            scale_row(av[st], e * sTab[(CS + 1) + (CS - 1 - row_v)]);
+                }
+            };
+            auto step_split = [&](int c, auto CUR, auto NXT) {
+                const int buf = (c - c_begin) & 1;
+                const bool tail = c >= tail_from;
+                kv_load(c + 3, CUR);
+                bf16x8 VB[NJB], VM[NJB];
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+                    const bf16_t* V0 = sV[buf][0];
+                    VB[jb] = join(tr_read(V0 + b_v + (32 * jb) * 32), tr_read(V0 + b_v + (32 * jb + 16) * 32));
+                }
+                if (tail) {
+                    const float gamma = sTab[(CS + 1) + CS];
+#pragma unroll
+                    for (int t = 0; t < NTH; ++t) Macc[t] *= gamma;
+#pragma unroll
+                    for (int jb = 0; jb < NJB; ++jb) {
+                        const bf16_t* V2 = sV[buf][2 % NV];
+                        VM[jb] = join(tr_read(V2 + b_v + (32 * jb) * 32), tr_read(V2 + b_v + (32 * jb + 16) * 32));
+                    }
+                }
+                const bf16_t* Kh = sK[buf] + (hf * NTH / 2) * BLK;
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) {
+#pragma unroll
+                    for (int t = 0; t < NTH; ++t) {
+                        const int base = (t >> 1) * BLK + ((t & 1) ? b_tr1 : b_tr0) + (32 * jb) * 32;
+                        const bf16x8 a = join(tr_read(Kh + base), tr_read(Kh + base + 16 * 32));
+                        mma(Sacc[t], a, VB[jb]);
+                        if (tail) mma(Macc[t], a, VM[jb]);
+                    }
+                }
+                if (c + 1 < c_end) kv_store_split(buf ^ 1, NXT, c + 1 >= tail_from);
+                __syncthreads();
+            };
+            if (split) {
+                __syncthreads();   // the first chunk was staged with all copies: restage
+                kv_store_split(0, J0{}, c_begin >= tail_from);
+                __syncthreads();
+                for (int c = c_begin; c < c_end; c += D) {
+                    step_split(c, J0{}, J1{});
+                    if (c + 1 < c_end) step_split(c + 1, J1{}, J2{});
+                    if (c + 2 < c_end) step_split(c + 2, J2{}, J0{});
+                }
+                const float beta = p.beta, inv = (float)(1.0 / (1.0 - (double)p.beta));
+#pragma unroll
+                for (int t = 0; t < NTH; ++t) Sacc[t] = (Sacc[t] - beta * Macc[t]) * inv;
+            } else {
+                for (int c = c_begin; c < c_end; c += D) {
+                    step(c, J0{}, J1{});
+                    if (c + 1 < c_end) step(c + 1, J1{}, J2{});
+                    if (c + 2 < c_end) step(c + 2, J2{}, J0{});
+                }
             }
             publish(0, Sacc, Macc);
         }
