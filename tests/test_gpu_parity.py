@@ -187,12 +187,15 @@ def _seeded(shape, seed, scale):
     return scale * torch.randn(*shape, generator=torch.Generator().manual_seed(seed))
 
 
-@pytest.mark.parametrize("beta", [0.0, 0.9])
+@pytest.mark.parametrize("beta", [0.0, 0.001, 0.5, 0.9, 0.97])
 def test_segmented_sequence_lookback(beta):
     """Two heads of 5000 tokens: too few (head, column tile) pairs to fill the
     chip, so the sequence is cut into segments that run concurrently and
     chain their states through the decoupled look-back (ragged last segment,
-    non-zero S0 and, with momentum, M0)."""
+    non-zero S0 and, with momentum, M0).  With momentum up to 0.95 the
+    segment aggregates come from the plain sum and the momentum aggregate of
+    the last chunks (a one-chunk tail at 0.001); 0.97 takes the chunk
+    recurrence."""
     inp = W.gen_lm_scale(B=1, H=2, L=5000, d=128)
     inp.beta = W.f32(beta)
     if beta:
