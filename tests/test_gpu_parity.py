@@ -428,6 +428,19 @@ def test_dual_segmented_alternating_inputs():
         assert oracle.rel_l2(got[1], ref[id(x)][1]) <= 5e-3
 
 
+def test_dual_segmented_long_composition():
+    """One sequence of 20000 tokens: 79 segments of 256, so the last one
+    composes 78 maps (twenty batches staged through the ring) before its
+    tokens; against the oracle and the one-chain form."""
+    inp = W.gen_dual(B=1, H=1, L=20000, minibatch=16)
+    assert lac.dual_form_workspace_size(1, 1, 20000, 64, 64, minibatch=16) == 512 + 79 * 32768
+    say("dual segmented B1 H1 L20000 b16 (79 segments)")
+    got = run_dual(inp, True)
+    check_dual(inp, got, [(0, 0)], TOL["bf16"], "dual seg 79")
+    ref = run_dual(inp, False)
+    assert oracle.rel_l2(got[0].float(), ref[0].float()) <= 5e-3
+
+
 def test_dual_segmented_repeat_bit_identical():
     """Segments compose their predecessors' maps in a fixed order, so
     repeated calls give the same bits whatever the timing."""
