@@ -486,6 +486,54 @@ def test_dual_is_la_with_corrected_values(oracle_mod):
     close(W, Wf, 1e-12)
 
 
+def test_dual_segment_maps_compose(oracle_mod):
+    """Over whole mini-batches the dual form's update is affine in the state,
+    so a segment maps its start state W to A W + B with B its run from W = 0
+    and A its run from W = I with zero values.  Composing the maps of the
+    segments before s onto W0 gives the state the sequential run has at the
+    start of s, and running s from there gives the sequential outputs."""
+    rng = np.random.default_rng(16)
+    L, d, dv, b, eta, seg = 96, 5, 4, 8, 0.05, 24
+    q, k, v = rnd(1, 1, L, d, rng=rng), rnd(1, 1, L, d, rng=rng), rnd(1, 1, L, dv, rng=rng)
+    W0 = rnd(1, 1, d, dv, rng=rng)
+    out, Wf = oracle_mod.dual_primal(q, k, v, W0, eta, b)
+    I = np.eye(d)[None, None]
+    W = W0
+    for s0 in range(0, L, seg):
+        sl = slice(s0, s0 + seg)
+        # the sequential state at the segment start and the segment's outputs from it
+        if s0:
+            _, Wseq = oracle_mod.dual_primal(q[:, :, :s0], k[:, :, :s0], v[:, :, :s0], W0, eta, b)
+            close(W, Wseq, 1e-12)
+        o, _ = oracle_mod.dual_primal(q[:, :, sl], k[:, :, sl], v[:, :, sl], W, eta, b)
+        close(o, out[:, :, sl], 1e-12)
+        # the segment's map, applied to W
+        _, B = oracle_mod.dual_primal(q[:, :, sl], k[:, :, sl], v[:, :, sl], np.zeros((1, 1, d, dv)), eta, b)
+        _, A = oracle_mod.dual_primal(q[:, :, sl], k[:, :, sl], np.zeros((1, 1, seg, d)), I, eta, b)
+        W = A @ W + B
+    close(W, Wf, 1e-12)
+
+
+@pytest.mark.parametrize("beta", [0.001, 0.5, 0.9, 0.95])
+def test_momentum_aggregate_split(oracle_mod, beta):
+    """A run of n tokens from zero states ends at S = sum_s w_{n-1-s} g_s with
+    w_m = (1 - beta^{m+1}) / (1 - beta), which equals (U - beta Y) / (1 - beta)
+    for U = sum_s g_s and Y the momentum it ends at; Y over only the last T
+    tokens, beta^T < 2^-30, differs from Y below that relative size."""
+    rng = np.random.default_rng(17)
+    L, dk, dv = 300, 5, 4
+    q, k, v = rnd(1, 1, L, dk, rng=rng), rnd(1, 1, L, dk, rng=rng), rnd(1, 1, L, dv, rng=rng)
+    eta = 0.05 + 0.1 * rng.random((1, 1, L))
+    _, S, M = oracle_mod.token_causal(q, k, v, eta, 0.0, beta)
+    U = np.einsum("t,ti,tj->ij", eta[0, 0], k[0, 0], v[0, 0])
+    close(S[0, 0], (U - beta * M[0, 0]) / (1.0 - beta), 1e-12)
+    T = int(np.ceil(30.0 / -np.log2(beta)))
+    if T < L:
+        _, _, Mt = oracle_mod.token_causal(q[:, :, L - T:], k[:, :, L - T:], v[:, :, L - T:], eta[:, :, L - T:],
+                                           0.0, beta)
+        assert np.abs(Mt - M).max() <= 2.0 ** -29 * np.abs(M).max() * L
+
+
 # ----------------------------------------------------------------- backward
 def _bwd_case(beta, rng, B=1, H=2, L=6, dk=3, dv=4):
     q, k, v, eta, S0, M0 = small_case(B, H, L, dk, dv, beta=beta, rng=rng, m0=beta != 0.0)
