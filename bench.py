@@ -490,23 +490,7 @@ def main():
 
     step, info = setup_workload(args.workload, dev)
     stream = torch.cuda.current_stream()
-    # W warm-up steps, continued until the GPU has run the step for at least
-    # --min-warmup-s seconds: its clocks take a few hundred ms of load to reach
-    # their steady level, and a cold start reads up to 25 % slow
-    t_w = time.perf_counter()
-    n_warm = 0
-    for _ in range(args.warmup):
-        step()
-        n_warm += 1
-    torch.cuda.synchronize()
-    while time.perf_counter() - t_w < args.min_warmup_s:
-        for _ in range(10):
-            step()
-            n_warm += 1
-        torch.cuda.synchronize()
-    warm_s = time.perf_counter() - t_w
-
-    # Between timed steps (outside the events) 512 MiB, twice the last-level
+    # Before every step (outside the events) 512 MiB, twice the last-level
     # cache, are written and then another 512 MiB are read: the write pushes
     # out the previous step's inputs and outputs, the read then replaces the
     # write's dirty lines with clean ones, so the timed step neither finds its
@@ -521,6 +505,27 @@ def main():
             evict_w.fill_(i & 0xff)
         if evict_r is not None:
             torch.sum(evict_r, dim=0, out=evict_sink)
+
+    # W warm-up steps, continued until the GPU has run the step for at least
+    # --min-warmup-s seconds: its clocks take a few hundred ms of load to reach
+    # their steady level, and a cold start reads up to 25 % slow.  The warm-up
+    # steps are evicted like the timed ones, so that every dispatch of the
+    # step's kernels (the ones a kernel trace of this command averages over)
+    # starts from the same cache state
+    t_w = time.perf_counter()
+    n_warm = 0
+    for _ in range(args.warmup):
+        evict_pass(n_warm)
+        step()
+        n_warm += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t_w < args.min_warmup_s:
+        for _ in range(10):
+            evict_pass(n_warm)
+            step()
+            n_warm += 1
+        torch.cuda.synchronize()
+    warm_s = time.perf_counter() - t_w
 
     # host time to issue one step (eviction included), after a first pass that
     # loads the eviction kernels

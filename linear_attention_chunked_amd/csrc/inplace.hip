@@ -594,15 +594,18 @@ __global__ __launch_bounds__(IP_NT) void ip_readout_kernel(IpReadoutParams p) {
     const int wm = wave >> 1, wn = wave & 1;
     const int tiles_n = p.dv / IP_BM;                 // dv tiles
     const int tiles_t = p.chunk / IP_BN;              // token tiles per chunk
-    // logical order (bh, chunk, token tile, dv tile): one XCD runs the tiles
+    // logical order (bh, chunk, dv tile, token tile): one XCD runs the tiles
     // of one chunk together, so they share the chunk's Z rows and snapshot
-    // columns through its L2
+    // columns through its L2; with the token tiles innermost, the tiles that
+    // read one snapshot column block run at the same time (read once from
+    // memory; the Z rows, a third of the snapshot's bytes, are the operand
+    // read again when a chunk's tiles straddle two rounds of the XCD's CUs)
     const int lid = xcd_logical(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
     int x = lid % gridDim.x;
-    const int nt = x % tiles_n;
-    x /= tiles_n;
     const int tt = x % tiles_t;
-    const int chunk = x / tiles_t;
+    x /= tiles_t;
+    const int nt = x % tiles_n;
+    const int chunk = x / tiles_n;
     const int n0 = nt * IP_BM;                        // dv offset
     const int t0 = chunk * p.chunk + tt * IP_BN;      // token offset
     const int bh = lid / gridDim.x, b = bh / p.H, h = bh % p.H;

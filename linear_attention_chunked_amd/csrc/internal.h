@@ -28,11 +28,12 @@ struct TcParams {
     float* M_final;
     int B, H, L, dk, dv, chunk;
     int n_vt;     // dv tiles per head
-    int xcd_map;  // 1: keep the dv tiles of one head on one XCD
+    int xcd_map;  // 1: keep the dv tiles (and segments) of one head on one XCD
     // sequence segmentation with decoupled look-back (bf16 kernel only):
     // nseg segments of seg_tiles chunk tiles per (head, dv tile); lb_flags
-    // holds one flag per workgroup plus the ticket counter, lb_data two state
-    // blocks (aggregate, inclusive) of lb_stride floats per workgroup
+    // holds one flag per workgroup, a spare word, the error word and eight
+    // ticket counters, lb_data two state blocks (aggregate, inclusive) of
+    // lb_stride floats per workgroup
     int nseg, seg_tiles;
     int* lb_flags;
     float* lb_data;

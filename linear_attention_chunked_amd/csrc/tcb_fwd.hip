@@ -109,14 +109,22 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
     int bh, vt, seg = 0, c_begin = 0, c_end = ntiles;
     __shared__ int sTicket;
     if (segmented) {
-        // tickets hand out segments in order, so a workgroup only ever waits
-        // for workgroups that took a ticket before it and are running
-        if (tid == 0) sTicket = atomicAdd(p.lb_flags + (int64_t)nbv * p.nseg, 1);
+        // Tickets hand out segments in order, so a workgroup only ever waits
+        // for workgroups that took a ticket before it and are running.  With
+        // xcd_map the workgroups form 8 groups by blockIdx % 8 (the XCD the
+        // dispatcher places them on), each with a counter of its own and
+        // every (segment, dv tile) of the heads bh = 8 i + group: the tiles
+        // of a head then read its K and Q through one XCD's L2, and all a
+        // workgroup waits for is in its own group, ahead of it in segment
+        // order.  Correctness needs only the group's own counts, which
+        // blockIdx fixes, not where the hardware puts the workgroups.
+        const int G = p.xcd_map ? 8 : 1, grp = (int)(blockIdx.x % G);
+        if (tid == 0) sTicket = atomicAdd(p.lb_flags + (int64_t)nbv * p.nseg + 2 + grp, 1);
         __syncthreads();
-        const int t = sTicket, bv = t % nbv;
-        seg = t / nbv;
-        bh = bv / p.n_vt;
-        vt = bv % p.n_vt;
+        const int per = nbv / G, t = sTicket, r = t % per;
+        seg = t / per;
+        bh = (r / p.n_vt) * G + grp;
+        vt = r % p.n_vt;
         c_begin = seg * p.seg_tiles;
         c_end = min(c_begin + p.seg_tiles, ntiles);
     } else {
@@ -1013,8 +1021,9 @@ TcbPlan tcb_plan(int B, int H, int L, int dv, int mode, int chunk) {
 // floats per workgroup state block (S, and m with momentum)
 int64_t lb_block(int dk, int dvt, int mode) { return (int64_t)dk * dvt * (mode == MODE_MOM ? 2 : 1); }
 
-// flags (one per workgroup), the ticket counter and the error word
-size_t lb_flag_bytes(int64_t nwg) { return (size_t)(((nwg + 2) * 4 + 255) / 256 * 256); }
+// flags (one per workgroup), a spare word, the error word and 8 ticket counters
+constexpr int kLbWords = 10;
+size_t lb_flag_bytes(int64_t nwg) { return (size_t)(((nwg + kLbWords) * 4 + 255) / 256 * 256); }
 
 __global__ void lb_clear_kernel(int* flags, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -1042,7 +1051,7 @@ hipError_t launch_tcb_fwd(const TcParams& pin, int mode, hipStream_t s) {
     p.n_vt = pl.n_vt;
     p.nseg = pl.nseg;
     p.seg_tiles = pl.seg_tiles;
-    p.xcd_map = (pl.nseg == 1 && (p.B * p.H) % 8 == 0) ? 1 : 0;
+    p.xcd_map = ((p.B * p.H) % 8 == 0) ? 1 : 0;
     const int64_t nwg = (int64_t)p.B * p.H * pl.n_vt * pl.nseg;
     if (pl.nseg > 1) {
         if (!p.workspace) return hipErrorInvalidValue;
@@ -1052,10 +1061,10 @@ hipError_t launch_tcb_fwd(const TcParams& pin, int mode, hipStream_t s) {
         p.lb_error = p.lb_flags + nwg + 1;
         if (p.lb_max_polls == 0) p.lb_max_polls = kDefaultPolls;
         else if (p.lb_max_polls < 0) p.lb_max_polls = 0;
-        // flags, the ticket counter and the error word start at zero (a fill
-        // kernel, not a memset node, so the call stays valid inside a
+        // flags, the ticket counters and the error word start at zero (a
+        // fill kernel, not a memset node, so the call stays valid inside a
         // captured graph)
-        const int nflags = (int)nwg + 2;
+        const int nflags = (int)nwg + kLbWords;
         hipLaunchKernelGGL(lb_clear_kernel, dim3((nflags + 255) / 256), dim3(256), 0, s, p.lb_flags, nflags);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -7,8 +7,11 @@
 // normalisation is gone; [P2] "In-Place 테스트 시점 학습", paragraph on the
 // associative scan):
 //     (S, m) -> (S + a m + X, g m + Y),  a = beta + ... + beta^n,  g = beta^n.
-// Threads play workgroups.  Each takes a ticket (segment = ticket / nbv),
-// computes its aggregate (X, Y), publishes it behind a release store of its
+// Threads play workgroups.  Thread i belongs to group i % G (G = 8 when the
+// heads split evenly into 8 groups, else 1, as the kernel groups workgroups
+// by blockIdx % 8) and takes a ticket from its group's counter; ticket t of
+// group g runs segment t / per of (head, tile) pair t % per of that group's
+// heads (per = nbv / G; heads bh = 8 i + g).  It computes its aggregate (X, Y), publishes it behind a release store of its
 // flag (1), walks back over earlier segments with acquire loads (aggregates
 // back to the inclusive state of segment s - kChain, or past segment 0 onto
 // (S0, M0)), publishes its inclusive state (flag 2) if a later segment reads
@@ -38,15 +41,18 @@ struct Block {
 };
 
 struct Run {
-    int nbv, nseg;
+    int nbv, nseg, nvt, groups;
     float beta, a_seg, g_seg;
     std::vector<Block> agg, incl, start;   // [nwg] each
     std::vector<Block> S0;                 // [nbv]
-    std::unique_ptr<std::atomic<int>[]> flags;
-    std::atomic<int> ticket{0}, error{0};
+    std::unique_ptr<std::atomic<int>[]> flags, tickets;
+    std::atomic<int> error{0};
 
-    Run(int nbv_, int nseg_, float beta_) : nbv(nbv_), nseg(nseg_), beta(beta_) {
+    Run(int nbv_, int nseg_, int nvt_, float beta_)
+        : nbv(nbv_), nseg(nseg_), nvt(nvt_), groups((nbv_ / nvt_) % 8 == 0 ? 8 : 1), beta(beta_) {
         const int nwg = nbv * nseg;
+        tickets.reset(new std::atomic<int>[groups]);
+        for (int g = 0; g < groups; ++g) tickets[g].store(0, std::memory_order_relaxed);
         agg.resize(nwg);
         incl.resize(nwg);
         start.resize(nwg);
@@ -100,9 +106,11 @@ Block walk(const Run& r, int seg, int bv, Read read) {
     return T;
 }
 
-void workgroup(Run* r) {
-    const int t = r->ticket.fetch_add(1, std::memory_order_relaxed);
-    const int seg = t / r->nbv, bv = t % r->nbv, id = seg * r->nbv + bv;
+void workgroup(Run* r, int index) {
+    const int G = r->groups, grp = index % G;
+    const int t = r->tickets[grp].fetch_add(1, std::memory_order_relaxed);
+    const int per = r->nbv / G, q = t % per;
+    const int seg = t / per, bv = ((q / r->nvt) * G + grp) * r->nvt + q % r->nvt, id = seg * r->nbv + bv;
     const bool last = seg == r->nseg - 1;
     if (!last) {
         Block& a = r->agg[id];
@@ -137,15 +145,15 @@ void workgroup(Run* r) {
     }
 }
 
-int check(int nbv, int nseg, float beta, int rep) {
-    Run r(nbv, nseg, beta);
+int check(int nbv, int nseg, int nvt, float beta, int rep) {
+    Run r(nbv, nseg, nvt, beta);
     for (int bv = 0; bv < nbv; ++bv)
         for (int e = 0; e < kElems; ++e) {
             r.S0[bv].S[e] = value(-1, bv, e, 0);
             r.S0[bv].M[e] = value(-1, bv, e, 1);
         }
     std::vector<std::thread> th;
-    for (int i = 0; i < nbv * nseg; ++i) th.emplace_back(workgroup, &r);
+    for (int i = 0; i < nbv * nseg; ++i) th.emplace_back(workgroup, &r, i);
     for (auto& x : th) x.join();
     if (r.error.load()) {
         std::fprintf(stderr, "rep %d: a wait gave up\n", rep);
@@ -194,13 +202,14 @@ int check(int nbv, int nseg, float beta, int rep) {
 }  // namespace
 
 int main() {
-    const int shapes[][2] = {{2, 4}, {3, 12}, {1, 20}, {4, 17}};
+    // (nbv, nseg, tiles per head); 16 pairs of 8 heads take the grouped tickets
+    const int shapes[][3] = {{2, 4, 2}, {3, 12, 1}, {1, 20, 1}, {4, 17, 2}, {16, 4, 2}, {16, 9, 2}};
     const float betas[] = {0.f, 0.9f, 0.5f};
     int fails = 0, n = 0;
     for (int rep = 0; rep < 4; ++rep)
         for (const auto& sh : shapes)
             for (float b : betas) {
-                fails += check(sh[0], sh[1], b, rep);
+                fails += check(sh[0], sh[1], sh[2], b, rep);
                 ++n;
             }
     std::printf("lookback model: %d runs, %d failures\n", n, fails);
