@@ -23,7 +23,9 @@ reported beside it, and so is the wall time per step with the eviction
 passes (it includes a spin kernel, run once before the timed steps, that
 holds the stream until the host has issued all of them: the host time to
 issue a step, also reported, can exceed the shorter kernels' durations, and
-an event interval must not time the GPU waiting for the host).  The GPU clock is read with rocm-smi before and after the timed steps
+an event interval must not time the GPU waiting for the host).  The GPU
+clock is read with rocm-smi during the warm-up (under load, on a host thread,
+so the GPU never idles before the timed steps) and after the timed steps
 (null when rocm-smi gives none).
 
 Roofline: the dominant kernel's average launch duration is the mean event
@@ -42,6 +44,7 @@ import hashlib
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -511,7 +514,14 @@ def main():
     # their steady level, and a cold start reads up to 25 % slow.  The warm-up
     # steps are evicted like the timed ones, so that every dispatch of the
     # step's kernels (the ones a kernel trace of this command averages over)
-    # starts from the same cache state
+    # starts from the same cache state.
+    # The shader clock is read (rocm-smi, about a quarter of a second) on a
+    # host thread in the second half of the warm-up, while the GPU is loaded
+    # and its clocks have settled.  Read between the warm-up and the timed
+    # steps, it left the GPU idle long enough for its clocks to drop, and the
+    # timed steps then ran up to 15 % slow
+    clk = {}
+    clk_thread = threading.Thread(target=lambda: clk.update(mhz=gpu_sclk_mhz()), daemon=True)
     t_w = time.perf_counter()
     n_warm = 0
     for _ in range(args.warmup):
@@ -519,12 +529,20 @@ def main():
         step()
         n_warm += 1
     torch.cuda.synchronize()
-    while time.perf_counter() - t_w < args.min_warmup_s:
+    while args.min_warmup_s > 0:   # 0: exactly W steps (counter runs), no clock reading
+        elapsed = time.perf_counter() - t_w
+        if clk_thread.ident is None and elapsed >= 0.5 * args.min_warmup_s:
+            clk_thread.start()
+        if elapsed >= args.min_warmup_s and clk_thread.ident is not None and not clk_thread.is_alive():
+            break
         for _ in range(10):
             evict_pass(n_warm)
             step()
             n_warm += 1
         torch.cuda.synchronize()
+    if clk_thread.ident is not None:
+        clk_thread.join()
+    clk_before = clk.get("mhz")
     warm_s = time.perf_counter() - t_w
 
     # host time to issue one step (eviction included), after a first pass that
@@ -555,7 +573,6 @@ def main():
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    clk_before = gpu_sclk_mhz()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if hold_cycles:
