@@ -599,16 +599,32 @@ __global__ __launch_bounds__(64 * NW) void dual_seg_kernel(DualParams p) {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nheads = p.B * p.H, nseg = p.nseg;
-    int ticket = blockIdx.x;   // one segment per sequence: no tickets, no flags
+    int ticket = blockIdx.x, seg_q = nheads, grp = 0, ngrp = 1;   // one segment per sequence: no tickets
     if (nseg > 1) {
-        if (tid == 0) *reinterpret_cast<int*>(ring) = atomicAdd(p.flags + (int64_t)nheads * nseg, 1);
+        // Tickets hand out segments in order, so a workgroup only ever waits
+        // for workgroups that took a ticket before it and are running.  With
+        // B*H a multiple of 8, the workgroups form 8 groups by blockIdx % 8
+        // (the XCD the dispatcher places them on), each with a counter of its
+        // own and every segment of the heads bh = 8 i + group: when segment 0
+        // runs only its forward, the CUs it frees are on the XCD that the
+        // group's last segments are dispatched to
+        ngrp = (nheads % 8 == 0) ? 8 : 1;
+        grp = (int)(blockIdx.x % ngrp);
+        seg_q = nheads / ngrp;
+        if (tid == 0) {
+            const int t = atomicAdd(p.flags + (int64_t)nheads * nseg + 2 + grp, 1);
+            *reinterpret_cast<int*>(ring) = t;
+            // started (bit 1 of the workgroup's flag)
+            __hip_atomic_store(p.flags + (int64_t)((t % seg_q) * ngrp + grp) * nseg + t / seg_q, 2,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         __syncthreads();
         ticket = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(ring));
         __syncthreads();   // every wave holds the ticket before the ring is filled
     }
     // (uniform values: buffer descriptors built from them stay scalar)
-    const int seg = __builtin_amdgcn_readfirstlane(ticket / nheads);
-    const int bh = __builtin_amdgcn_readfirstlane(ticket % nheads);
+    const int seg = __builtin_amdgcn_readfirstlane(ticket / seg_q);
+    const int bh = __builtin_amdgcn_readfirstlane((ticket % seg_q) * ngrp + grp);
     const int L = p.L, mb = p.minibatch;
     const int tok0 = seg * p.seg_len;
     const int len = min(p.seg_len, L - tok0);
@@ -685,8 +701,11 @@ __global__ __launch_bounds__(64 * NW) void dual_seg_kernel(DualParams p) {
     const int64_t id = (int64_t)bh * nseg + seg;
     char* maps = reinterpret_cast<char*>(p.maps);
 
-    // ================= pass 1: the segment's map (Delta, B)
-    if (seg < nseg - 1) {
+    // ================= pass 1: the segment's map (Delta, B).  The last
+    // segment's map is never read; with seg0_state segment 0 hands on its end
+    // state instead (after its forward)
+    const bool from_w0 = (seg == 0) || !p.seg0_state;
+    if ((seg > 0 || !p.seg0_state) && seg < nseg - 1) {
         f32x4 SB[NCB][4], SD[NCB][4];
         bf16x8 BopS[NCB][2], DopS[NCB][2], BopW[NCB][2], DopW[NCB][2];
 #pragma unroll
@@ -887,59 +906,54 @@ __global__ __launch_bounds__(64 * NW) void dual_seg_kernel(DualParams p) {
         }
         wait_vm(V0{});   // this wave's stores are complete
         __syncthreads();
-        if (tid == 0) __hip_atomic_store(p.flags + id, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) __hip_atomic_store(p.flags + id, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 
-    // ================= the start state: W0, then the maps of segments 0 .. seg-1
-    f32x4 Sacc[NCB][4];
-    {
-        const float* W0 = p.W0 + (int64_t)bh * p.W0_stride;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Sacc[cb][t][r] = W0[feat(16 * t + 4 * g + r) * DV + col0 + 16 * cb + c16];
-    }
-    if (seg > 0) {
-        // every map this segment composes was published by a workgroup with
-        // an earlier ticket: one thread waits for all of them, polling with
-        // relaxed loads (an acquire in the loop would invalidate the XCD's L2
-        // on every poll, under the feet of the workgroups still computing).
-        // The maps are then read with device-coherent loads (sc1), which see
-        // the published stores; the other waves' reads follow the barrier.
-        // The wait is bounded; one that gives up raises the error word
-        // (results are then invalid)
+    // Flags: bit 1 when the workgroup of (b, h, segment) has started, bit 0
+    // when its map (or segment 0's end state) is published.  Waiting for
+    // published flags of segments [0, j_end) of this head: one thread polls
+    // with relaxed loads (an acquire in the loop would invalidate the XCD's
+    // L2 on every poll, under the feet of the workgroups still computing);
+    // the maps are then read with device-coherent loads (sc1), which see the
+    // published stores, and the other waves' reads follow the barrier.  The
+    // wait is bounded; one that gives up raises the error word (results are
+    // then invalid)
+    auto wait_published = [&](int j_end) __attribute__((always_inline)) {
         if (tid == 0) {
             bool all = true;
-            for (int j = 0; j < seg; ++j) {
+            for (int j = 0; j < j_end; ++j) {
                 int v = 0;
                 for (int spin = 0; spin < p.max_polls; ++spin) {
                     v = __hip_atomic_load(p.flags + (int64_t)bh * nseg + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (v != 0) break;
+                    if (v & 1) break;
                     __builtin_amdgcn_s_sleep(2);
                 }
-                all = all && v != 0;
+                all = all && (v & 1);
             }
             if (!all)
                 __hip_atomic_store(p.flags + (int64_t)nheads * nseg + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
-        // Delta_j (hi, lo) of up to MB maps at a time go into the ring by
-        // direct loads (16 KB per map; the 16-byte unit u of row r at position
-        // u ^ (r & 7)), B_j into registers; then the maps are applied in order
-        const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
-            uniform_ptr(maps + (int64_t)bh * nseg * DS_MAP), 0, nseg * DS_MAP, 0x00020000);
-        constexpr int NMO = 16 / NW;   // direct loads per wave per map (1024 slots of 16 bytes)
-        uint32_t mo[NMO];
+    };
+    // segment 0's end state sits in the B slots of its map block
+    const __amdgpu_buffer_rsrc_t rM = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(maps + (int64_t)bh * nseg * DS_MAP), 0, nseg * DS_MAP, 0x00020000);
+    constexpr int NMO = 16 / NW;   // direct loads per wave per map (1024 slots of 16 bytes)
+    uint32_t mo[NMO];
 #pragma unroll
-        for (int i = 0; i < NMO; ++i) {
-            const int slot = 64 * (NMO * w + i) + lane, row = (slot >> 3) & 63;
-            // slots 0..511: hi rows, 512..1023: lo rows
-            mo[i] = (uint32_t)((slot >> 9) * D * DV * 2 + row * DV * 2 + 16 * ((slot & 7) ^ (row & 7)));
-        }
-        for (int j0 = 0; j0 < seg; j0 += MB) {
-            const int nb = min(MB, seg - j0);
+    for (int i = 0; i < NMO; ++i) {
+        const int slot = 64 * (NMO * w + i) + lane, row = (slot >> 3) & 63;
+        // slots 0..511: hi rows, 512..1023: lo rows
+        mo[i] = (uint32_t)((slot >> 9) * D * DV * 2 + row * DV * 2 + 16 * ((slot & 7) ^ (row & 7)));
+    }
+    f32x4 Sacc[NCB][4];
+    // Sacc <- f_{j_end-1}(... f_{j_begin}(Sacc)), f_j(W) = W + Delta_j W + B_j:
+    // Delta_j (hi, lo) of up to MB maps at a time go into the ring by direct
+    // loads (16 KB per map; the 16-byte unit u of row r at position u ^ (r &
+    // 7)), B_j into registers; then the maps are applied in order
+    auto compose = [&](int j_begin, int j_end) __attribute__((always_inline)) {
+        for (int j0 = j_begin; j0 < j_end; j0 += MB) {
+            const int nb = min(MB, j_end - j0);
             f32x4 bj[MB][NCB][4];
 #pragma unroll
             for (int x = 0; x < MB; ++x) {
@@ -1001,123 +1015,197 @@ __global__ __launch_bounds__(64 * NW) void dual_seg_kernel(DualParams p) {
             }
             __syncthreads();   // the staged maps are read before the ring is refilled
         }
-    }
+    };
 
-    // ================= pass 3: the forward over this segment's tokens
-    bf16x8 Sop[NCB][2], Wop[NCB][2];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) Sop[cb][kb] = Wop[cb][kb] = acc_to_frag_bf16(Sacc[cb][2 * kb], Sacc[cb][2 * kb + 1]);
-    wait_vm(V0{});
-    __syncthreads();   // every wave is past pass 1 before the ring is refilled
-    const int nst = (len + DS_T - 1) / DS_T;
-    auto issue = [&](int s, bf16_t* dst) __attribute__((always_inline)) {
-        const int sq = (tok0 + DS_T * min(s, nst - 1)) * D * 2;
-        load_tile(rQ, dst, qko, sq);
-        load_tile(rK, dst + DS_TILE, qko, sq);
-        load_tile(rV, dst + 2 * DS_TILE, vdo, sq);
-    };
-    auto step = [&](const bf16_t* X, int j, int s16) __attribute__((always_inline)) {
-        const bf16_t* Qs = X + 16 * j * D;
-        const bf16_t* Ks = X + DS_TILE + 16 * j * D;
-        const bf16_t* Vs = X + 2 * DS_TILE + 16 * j * DV;
-        const bf16x8 Kf0 = kfrag(Ks, 0), Kf1 = kfrag(Ks, 1);
-        const bf16x8 Qf0 = kfrag(Qs, 0), Qf1 = kfrag(Qs, 1);
-        // P^T = K Q^T (causal j <= i), shared by the column blocks
-        f32x4 pt = zero4();
-        mma(pt, Kf0, Qf0);
-        mma(pt, Kf1, Qf1);
-        u32x2 VB[NCB];
-        f32x4 o[NCB];
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-            // E = K W_n;  O^T partial = S~^T Q^T
-            f32x4 e = zero4();
-            o[cb] = zero4();
-            mma(e, Kf0, ONE ? Sop[cb][0] : Wop[cb][0]);
-            mma(e, Kf1, ONE ? Sop[cb][1] : Wop[cb][1]);
-            mma(o[cb], Sop[cb][0], Qf0);
-            mma(o[cb], Sop[cb][1], Qf1);
-            const f32x4 vv = to4(tr_read_d(Vs + vro[cb]));
-            f32x4 vt;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) vt[r] = eta * (vv[r] - e[r]);
-            VB[cb] = u32x2{pack2bf(vt[0], vt[1]), pack2bf(vt[2], vt[3])};
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const u32x2 kt = kT(Ks, t);
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) mma16(Sacc[cb][t], kt, VB[cb]);
-        }
-        const u32x2 pm = u32x2{pack2bf(pt[0], pt[1]) & pmask[0], pack2bf(pt[2], pt[3]) & pmask[1]};
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) Sop[cb][kb] = acc_to_frag_bf16(Sacc[cb][2 * kb], Sacc[cb][2 * kb + 1]);
-            if (MBK == 2 && mb_end(16 * s16 + 16)) {
-                Wop[cb][0] = Sop[cb][0];
-                Wop[cb][1] = Sop[cb][1];
-            }
-            // O^T += V~^T P^T, store O rows (4 consecutive columns per lane)
-            mma16(o[cb], VB[cb], pm);
-            __builtin_amdgcn_raw_buffer_store_b64(
-                __builtin_bit_cast(u32x2, u32x2{pack2bf(o[cb][0], o[cb][1]), pack2bf(o[cb][2], o[cb][3])}), rO,
-                vo + 32 * cb, 16 * s16 * DV * 2, 0);
-        }
-    };
-    // a wave issues NL3 loads and NST stores (one per step and column block)
-    // per stage.  Operations issued after the loads of the stage read in
-    // iteration s: for s < R - 1 (stages of the prologue) the loads of
-    // prologue stages s + 1 .. R - 2 and iterations 0 .. s - 1,
-    // NL3 (R - 2) + NST s; after that the stores of the iteration that
-    // issued them and R - 2 whole iterations, NST + (NL3 + NST) (R - 2)
-    constexpr int NL3 = 3 * NLQ, NST = 4 * NCB;
-#pragma unroll
-    for (int s = 0; s < R - 1; ++s) issue(s, ring + s * DS_STAGE);
-    int rdo = 0, wro = (R - 1) * DS_STAGE;
-    auto wait_stage = [&](int s) __attribute__((always_inline)) {
-        if (s >= R - 1) {
-            wait_vm(std::integral_constant<int, NST + (NL3 + NST) * (R - 2)>{});
-            return;
-        }
-        static_for<R - 1>([&](auto I) __attribute__((always_inline)) {
-            constexpr int i = decltype(I)::value;
-            if (s == i) wait_vm(std::integral_constant<int, NL3 * (R - 2) + NST * i>{});
-        });
-    };
-    for (int s = 0; s < nst; ++s) {
-        wait_stage(s);
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        const int rd_off = rdo, wr_off = wro;
-        advance(rdo);
-        advance(wro);
-        ring_step1(ring + __builtin_amdgcn_readfirstlane(wr_off), ring + __builtin_amdgcn_readfirstlane(rd_off),
-                   [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + R - 1, dst); },
-                   [&](const bf16_t* X) __attribute__((always_inline)) {
-#pragma unroll
-                       for (int j = 0; j < DS_T / 16; ++j) step(X, j, (tok0 >> 4) + 4 * s + j);
-                   });
-        if (SEND && mb_end(tok0 + DS_T * (s + 1))) {
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                Wop[cb][0] = Sop[cb][0];
-                Wop[cb][1] = Sop[cb][1];
-            }
-        }
-    }
-    wait_vm(V0{});   // the clamped loads still in flight
-
-    if (seg == nseg - 1 && p.W_final) {
-        float* Wf = p.W_final + (int64_t)bh * D * DV;
+    // ================= the start state: W0, then the maps of segments
+    // 0 .. seg-1; with seg0_state, segment 0's end state, then the maps of
+    // segments 1 .. seg-1
+    if (from_w0) {
+        const float* W0 = p.W0 + (int64_t)bh * p.W0_stride;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Wf[feat(16 * t + 4 * g + r) * DV + col0 + 16 * cb + c16] = Sacc[cb][t][r];
+                for (int r = 0; r < 4; ++r) Sacc[cb][t][r] = W0[feat(16 * t + 4 * g + r) * DV + col0 + 16 * cb + c16];
+    }
+    if (seg > 0) {
+        wait_published(seg);
+        if (!from_w0) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    Sacc[cb][t] = __builtin_bit_cast(
+                        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                   rM, (uint32_t)(DS_BOFF + 16 * (((NCB * w + cb) * 4 + t) * 64 + lane)), 0, DS_SC1));
+        }
+        compose(from_w0 ? 0 : 1, seg);
+    }
+
+    // With seg0_state the last segment has no workgroup of its own: segment
+    // 0's workgroup, which runs only its forward and finishes first, goes on
+    // to it (composing the maps of segments 1 .. nseg-2 onto the end state it
+    // holds), or, failing that, the workgroup of segment nseg-2, whose end
+    // state is the last segment's start.  Segment 0 claims it only once every
+    // workgroup it would wait for has started, so it never waits for one
+    // that cannot run; segment nseg-2 waits for nothing.  A claim word (the
+    // last segment's flag) makes exactly one of them run it.
+    for (int cur = seg;;) {
+        // ================= pass 3: the forward over segment cur's tokens
+        const int ctok0 = cur * p.seg_len, clen = min(p.seg_len, L - ctok0);
+        bf16x8 Sop[NCB][2], Wop[NCB][2];
+    #pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+    #pragma unroll
+            for (int kb = 0; kb < 2; ++kb) Sop[cb][kb] = Wop[cb][kb] = acc_to_frag_bf16(Sacc[cb][2 * kb], Sacc[cb][2 * kb + 1]);
+        wait_vm(V0{});
+        __syncthreads();   // every wave is past pass 1 before the ring is refilled
+        const int nst = (clen + DS_T - 1) / DS_T;
+        auto issue = [&](int s, bf16_t* dst) __attribute__((always_inline)) {
+            const int sq = (ctok0 + DS_T * min(s, nst - 1)) * D * 2;
+            load_tile(rQ, dst, qko, sq);
+            load_tile(rK, dst + DS_TILE, qko, sq);
+            load_tile(rV, dst + 2 * DS_TILE, vdo, sq);
+        };
+        auto step = [&](const bf16_t* X, int j, int s16) __attribute__((always_inline)) {
+            const bf16_t* Qs = X + 16 * j * D;
+            const bf16_t* Ks = X + DS_TILE + 16 * j * D;
+            const bf16_t* Vs = X + 2 * DS_TILE + 16 * j * DV;
+            const bf16x8 Kf0 = kfrag(Ks, 0), Kf1 = kfrag(Ks, 1);
+            const bf16x8 Qf0 = kfrag(Qs, 0), Qf1 = kfrag(Qs, 1);
+            // P^T = K Q^T (causal j <= i), shared by the column blocks
+            f32x4 pt = zero4();
+            mma(pt, Kf0, Qf0);
+            mma(pt, Kf1, Qf1);
+            u32x2 VB[NCB];
+            f32x4 o[NCB];
+    #pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                // E = K W_n;  O^T partial = S~^T Q^T
+                f32x4 e = zero4();
+                o[cb] = zero4();
+                mma(e, Kf0, ONE ? Sop[cb][0] : Wop[cb][0]);
+                mma(e, Kf1, ONE ? Sop[cb][1] : Wop[cb][1]);
+                mma(o[cb], Sop[cb][0], Qf0);
+                mma(o[cb], Sop[cb][1], Qf1);
+                const f32x4 vv = to4(tr_read_d(Vs + vro[cb]));
+                f32x4 vt;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) vt[r] = eta * (vv[r] - e[r]);
+                VB[cb] = u32x2{pack2bf(vt[0], vt[1]), pack2bf(vt[2], vt[3])};
+            }
+    #pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const u32x2 kt = kT(Ks, t);
+    #pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) mma16(Sacc[cb][t], kt, VB[cb]);
+            }
+            const u32x2 pm = u32x2{pack2bf(pt[0], pt[1]) & pmask[0], pack2bf(pt[2], pt[3]) & pmask[1]};
+    #pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb) Sop[cb][kb] = acc_to_frag_bf16(Sacc[cb][2 * kb], Sacc[cb][2 * kb + 1]);
+                if (MBK == 2 && mb_end(16 * s16 + 16)) {
+                    Wop[cb][0] = Sop[cb][0];
+                    Wop[cb][1] = Sop[cb][1];
+                }
+                // O^T += V~^T P^T, store O rows (4 consecutive columns per lane)
+                mma16(o[cb], VB[cb], pm);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    __builtin_bit_cast(u32x2, u32x2{pack2bf(o[cb][0], o[cb][1]), pack2bf(o[cb][2], o[cb][3])}), rO,
+                    vo + 32 * cb, 16 * s16 * DV * 2, 0);
+            }
+        };
+        // a wave issues NL3 loads and NST stores (one per step and column block)
+        // per stage.  Operations issued after the loads of the stage read in
+        // iteration s: for s < R - 1 (stages of the prologue) the loads of
+        // prologue stages s + 1 .. R - 2 and iterations 0 .. s - 1,
+        // NL3 (R - 2) + NST s; after that the stores of the iteration that
+        // issued them and R - 2 whole iterations, NST + (NL3 + NST) (R - 2)
+        constexpr int NL3 = 3 * NLQ, NST = 4 * NCB;
+    #pragma unroll
+        for (int s = 0; s < R - 1; ++s) issue(s, ring + s * DS_STAGE);
+        int rdo = 0, wro = (R - 1) * DS_STAGE;
+        auto wait_stage = [&](int s) __attribute__((always_inline)) {
+            if (s >= R - 1) {
+                wait_vm(std::integral_constant<int, NST + (NL3 + NST) * (R - 2)>{});
+                return;
+            }
+            static_for<R - 1>([&](auto I) __attribute__((always_inline)) {
+                constexpr int i = decltype(I)::value;
+                if (s == i) wait_vm(std::integral_constant<int, NL3 * (R - 2) + NST * i>{});
+            });
+        };
+        for (int s = 0; s < nst; ++s) {
+            wait_stage(s);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+            const int rd_off = rdo, wr_off = wro;
+            advance(rdo);
+            advance(wro);
+            ring_step1(ring + __builtin_amdgcn_readfirstlane(wr_off), ring + __builtin_amdgcn_readfirstlane(rd_off),
+                       [&](bf16_t* dst) __attribute__((always_inline)) { issue(s + R - 1, dst); },
+                       [&](const bf16_t* X) __attribute__((always_inline)) {
+    #pragma unroll
+                           for (int j = 0; j < DS_T / 16; ++j) step(X, j, (ctok0 >> 4) + 4 * s + j);
+                       });
+            if (SEND && mb_end(ctok0 + DS_T * (s + 1))) {
+    #pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    Wop[cb][0] = Sop[cb][0];
+                    Wop[cb][1] = Sop[cb][1];
+                }
+            }
+        }
+        wait_vm(V0{});   // the clamped loads still in flight
+
+        if (cur == 0 && nseg > 2 && p.seg0_state) {
+            // segment 0's end state, for every later segment to start from: the
+            // same device-coherent stores and relaxed flag as a map
+            const __amdgpu_buffer_rsrc_t rP =
+                __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(maps + id * DS_MAP), 0, DS_MAP, 0x00020000);
+    #pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+    #pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, Sacc[cb][t]), rP,
+                                                           (uint32_t)(DS_BOFF + 16 * (((NCB * w + cb) * 4 + t) * 64 + lane)),
+                                                           0, DS_SC1);
+            wait_vm(V0{});   // this wave's stores are complete
+            __syncthreads();
+            if (tid == 0) __hip_atomic_store(p.flags + id, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+
+        if (cur == nseg - 1 && p.W_final) {
+            float* Wf = p.W_final + (int64_t)bh * D * DV;
+    #pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+    #pragma unroll
+                for (int t = 0; t < 4; ++t)
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) Wf[feat(16 * t + 4 * g + r) * DV + col0 + 16 * cb + c16] = Sacc[cb][t][r];
+        }
+
+        if (!p.seg0_state || cur == nseg - 1 || (cur != 0 && cur != nseg - 2)) break;
+        __syncthreads();   // the ring is free (its first word carries the claim)
+        if (tid == 0) {
+            bool ok = true;
+            for (int j = 1; cur == 0 && j < nseg - 1; ++j)
+                ok = ok && (__hip_atomic_load(p.flags + (int64_t)bh * nseg + j, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) & 2);
+            if (ok) ok = atomicCAS(p.flags + (int64_t)bh * nseg + nseg - 1, 0, 1) == 0;
+            *reinterpret_cast<int*>(ring) = ok ? 1 : 0;
+        }
+        __syncthreads();
+        const int go = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(ring));
+        __syncthreads();
+        if (!go) break;
+        if (cur == 0 && nseg > 2) {
+            wait_published(nseg - 1);
+            compose(1, nseg - 1);
+        }
+        cur = nseg - 1;
     }
 }
 
@@ -1134,8 +1222,8 @@ namespace {
 
 // Segmented plan for bf16 mini-batches of a multiple of 16: enough segments
 // to fill the CUs with workgroups (kDualNW waves each, one wave per SIMD),
-// each a whole number of mini-batches and of 64-token stages, at least 256
-// tokens long.  Four waves of one column block each: a step is bound by
+// and one more, each a whole number of mini-batches and of 64-token stages,
+// at least 256 tokens long.  Four waves of one column block each: a step is bound by
 // instruction issue, so two column blocks per wave (two-wave workgroups,
 // twice the segments) took twice as long per step and lost the time the
 // shared fragments saved to the longer composition.
@@ -1148,15 +1236,25 @@ constexpr int kDualSlots = kCUs * 4 / kDualNW;     // workgroups resident at onc
 constexpr int kDualMinSeg = 256;
 constexpr int kDualPolls = 1 << 22;   // polls of ~0.1 us before a wait gives up
 struct DualSegPlan {
-    int nseg, seg_len;
+    int nseg, seg_len, seg0_state;
 };
 
+// segment length (a whole number of units, at least the minimum) for about
+// `want` segments over L tokens
+int64_t dual_seg_len(int64_t L, int64_t want, int64_t unit) {
+    int64_t seg = ((L + want - 1) / want + unit - 1) / unit * unit;
+    const int64_t min_seg = (kDualMinSeg + unit - 1) / unit * unit;
+    return seg < min_seg ? min_seg : seg;
+}
+
 DualSegPlan dual_seg_plan(int dtype, int B, int H, int L, int d, int dv, int mb) {
-    DualSegPlan pl{1, L};
+    DualSegPlan pl{1, L, 0};
     if (dtype != 1 || d != 64 || dv != 64 || mb % 16 != 0) return pl;
     if ((int64_t)L * 128 >= (int64_t)1 << 31) return pl;   // 32-bit buffer ranges
     const int64_t nheads = (int64_t)B * H;
-    if (nheads * 2 > kDualSlots) return pl;   // two segments would not all be resident
+    // with more sequences than half the slots there would be two segments,
+    // the second waiting for the end of the first: no gain over one chain
+    if (nheads * 2 > kDualSlots) return pl;
     int64_t gcd = 64, x = mb;
     while (x) {
         const int64_t t = gcd % x;
@@ -1164,17 +1262,27 @@ DualSegPlan dual_seg_plan(int dtype, int B, int H, int L, int d, int dv, int mb)
         x = t;
     }
     const int64_t unit = (int64_t)mb / gcd * 64;   // lcm(mb, 64)
-    const int64_t want = (kDualSlots + nheads - 1) / nheads;
-    int64_t seg = ((L + want - 1) / want + unit - 1) / unit * unit;
-    const int64_t min_seg = (kDualMinSeg + unit - 1) / unit * unit;
-    if (seg < min_seg) seg = min_seg;
-    const int64_t nseg = (L + seg - 1) / seg;
+    // Segment 0 may run only its forward and hand on its end state: it then
+    // finishes first, and its workgroup goes on to one more segment than the
+    // slots hold.  That pays when the extra segment exists; otherwise the
+    // later segments would wait for segment 0's forward instead of its
+    // shorter map pass, so segment 0 publishes a map like the others
+    int64_t seg = dual_seg_len(L, kDualSlots / nheads + 1, unit);
+    int64_t nseg = (L + seg - 1) / seg;
+    if (nseg * nheads > kDualSlots) {
+        pl.seg0_state = 1;
+    } else {
+        seg = dual_seg_len(L, (kDualSlots + nheads - 1) / nheads, unit);
+        nseg = (L + seg - 1) / seg;
+    }
     if (nseg <= 1) return pl;
     pl.nseg = (int)nseg;
     pl.seg_len = (int)seg;
     return pl;
 }
-size_t dual_flag_bytes(int64_t n) { return (size_t)(((n + 2) * 4 + 255) / 256 * 256); }
+// flags (one per (b, h, segment)), a spare word, the error word, 8 ticket counters
+constexpr int kDualFlagWords = 10;
+size_t dual_flag_bytes(int64_t n) { return (size_t)(((n + kDualFlagWords) * 4 + 255) / 256 * 256); }
 
 void launch_dual_seg(const DualParams& p, unsigned nwg, hipStream_t s) {
     const dim3 grid(nwg), block(64 * kDualNW);
@@ -1210,16 +1318,20 @@ hipError_t launch_dual_fwd(const DualParams& pin, int dtype, hipStream_t s) {
                 return hipErrorInvalidValue;
             p.nseg = pl.nseg;
             p.seg_len = pl.seg_len;
+            p.seg0_state = pl.seg0_state;
             p.flags = reinterpret_cast<int*>(p.workspace);
             p.maps = reinterpret_cast<float*>(reinterpret_cast<char*>(p.workspace) + dual_flag_bytes(n));
             if (p.max_polls <= 0) p.max_polls = kDualPolls;
-            // flags, ticket and error word start at zero (a fill kernel, not a
+            // flags, tickets and error word start at zero (a fill kernel, not a
             // memset node, so the call stays valid inside a captured graph)
-            const int nflags = (int)n + 2;
+            const int nflags = (int)n + kDualFlagWords;
             hipLaunchKernelGGL(dual_flags_clear_kernel, dim3((nflags + 255) / 256), dim3(256), 0, s, p.flags, nflags);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
-            launch_dual_seg(p, (unsigned)n, s);
+            // with seg0_state the last segment runs on segment 0's (or
+            // segment nseg-2's) workgroup
+            const int64_t nwg = p.seg0_state ? n - p.B * p.H : n;
+            launch_dual_seg(p, (unsigned)nwg, s);
             return hipGetLastError();
         }
         const DualParams& p = pin;
@@ -1229,6 +1341,7 @@ hipError_t launch_dual_fwd(const DualParams& pin, int dtype, hipStream_t s) {
             DualParams q = p;
             q.nseg = 1;
             q.seg_len = q.L;
+            q.seg0_state = 0;
             q.flags = nullptr;
             q.maps = nullptr;
             launch_dual_seg(q, (unsigned)(q.B * q.H), s);

@@ -101,13 +101,14 @@ struct DualParams {
     float eta;
     int B, H, L, d, dv, minibatch;
     // segmented form (set by launch_dual_fwd from the workspace): flags (one
-    // per (b, h, segment), then the ticket counter and the error word) and
-    // the per-segment maps
+    // per (b, h, segment), then a spare word, the error word and eight ticket
+    // counters) and the per-segment maps; seg0_state: segment 0 runs only its
+    // forward and hands on its end state in place of a map
     void* workspace;            // null: the sequential form
     size_t workspace_bytes;
     int* flags;
     float* maps;
-    int nseg, seg_len, max_polls;
+    int nseg, seg_len, max_polls, seg0_state;
 };
 hipError_t launch_dual_fwd(const DualParams& p, int dtype, hipStream_t stream);
 bool dual_supported(int dtype, int d, int dv, int minibatch);

@@ -251,12 +251,13 @@ def test_dual_segment_workspace(lib):
     q = ctypes.c_size_t(0)
     ws = lambda B, H, L, mb, dt=1, d=64: (lib.ttt_dual_form_workspace_size(B, H, L, d, 64, mb, dt, ctypes.byref(q)), q.value)
     st, need = ws(4, 16, 8192, 16)
-    # 4 segments of 2048 tokens: flags (256 + 2 words, in 256-byte units) and
-    # a 32 KB map (Delta as bf16 hi and lo, B in fp32) per (b, h, segment)
-    assert st == OK and need == 1280 + 64 * 4 * 32768
-    st, need2 = ws(4, 16, 8192, 2048)
-    assert st == OK and need2 == need                  # 4 segments of one mini-batch
-    assert ws(2, 64, 8192, 16) == (OK, 1280 + 128 * 2 * 32768)   # 128 sequences: 2 segments
+    # 64 sequences fill the 256 slots with 4 segments, plus a fifth on the CUs
+    # segment 0 frees: 1664-token segments, flags (320 + 2 words, in 256-byte
+    # units) and a 32 KB block (a map: Delta as bf16 hi and lo, B in fp32; or
+    # segment 0's end state) per (b, h, segment)
+    assert st == OK and need == 1536 + 64 * 5 * 32768
+    assert ws(4, 16, 8192, 2048) == (OK, 1280 + 64 * 4 * 32768)   # whole mini-batches: 4 segments
+    assert ws(2, 64, 8192, 16) == (OK, 1792 + 128 * 3 * 32768)   # 128 sequences: 3 segments
     assert ws(4, 64, 8192, 16) == (OK, 0)        # 256 sequences fill the chip unsegmented
     assert ws(1, 3, 1000, 48) == (OK, 256 + 3 * 3 * 32768)    # 3 segments of 384 tokens
     assert ws(4, 16, 8192, 40) == (OK, 0)        # mini-batches not of a multiple of 16
