@@ -21,9 +21,10 @@ timed step to write back (--evict selects other modes).  value and
 ms_per_step use the mean event time of a step; the median and minimum are
 reported beside it, and so is the wall time per step with the eviction
 passes (it includes a spin kernel, run once before the timed steps, that
-holds the stream until the host has issued all of them: the host time to
-issue a step, also reported, can exceed the shorter kernels' durations, and
-an event interval must not time the GPU waiting for the host).  The GPU
+holds the stream until the host is far enough ahead: an event interval must
+not time the GPU waiting for the host.  The hold is a few steps' issue time
+when a step's GPU time is well above it, as it is with the eviction passes,
+and the time to issue every step otherwise; hold_ms reports it).  The GPU
 clock is read with rocm-smi during the warm-up (under load, on a host thread,
 so the GPU never idles before the timed steps) and after the timed steps
 (null when rocm-smi gives none).
@@ -509,6 +510,17 @@ def main():
         if evict_r is not None:
             torch.sum(evict_r, dim=0, out=evict_sink)
 
+    # cycles per ms of torch's spin kernel (for the hold below), measured
+    # before the warm-up, away from the timed steps
+    ms_per_cycle = None
+    if hasattr(torch.cuda, "_sleep"):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        torch.cuda._sleep(1 << 22)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_cycle = max(c0.elapsed_time(c1), 1e-3) / (1 << 22)
+
     # W warm-up steps, continued until the GPU has run the step for at least
     # --min-warmup-s seconds: its clocks take a few hundred ms of load to reach
     # their steady level, and a cold start reads up to 25 % slow.  The warm-up
@@ -546,7 +558,8 @@ def main():
     warm_s = time.perf_counter() - t_w
 
     # host time to issue one step (eviction included), after a first pass that
-    # loads the eviction kernels
+    # loads the eviction kernels, and the step's GPU time (wall time to the
+    # synchronisation, which the GPU bounds when it is the slower side)
     evict_pass(0)
     step()
     torch.cuda.synchronize()
@@ -556,19 +569,20 @@ def main():
         step()
     host_ms = (time.perf_counter() - t_h) * 1000.0 / 10
     torch.cuda.synchronize()
-    # The timed steps are queued behind a spin kernel long enough for the host
-    # to issue all of them, so no event interval contains GPU idle time spent
-    # waiting for the host (the binding's host work per call is comparable to
-    # the shorter workloads' kernel times)
-    hold_cycles = 0
-    if hasattr(torch.cuda, "_sleep"):
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        torch.cuda._sleep(1 << 22)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        ms_per_cycle = max(c0.elapsed_time(c1), 1e-3) / (1 << 22)
-        hold_ms = min(2.0 * args.steps * host_ms + 2.0, 500.0)
+    gpu_ms = (time.perf_counter() - t_h) * 1000.0 / 10
+    # The timed steps are queued behind a spin kernel, so that no event
+    # interval contains GPU idle time spent waiting for the host.  When a
+    # step's GPU time is well above the host's time to issue it (the eviction
+    # alone takes ~0.25 ms), a head start of a few steps' issue time keeps the
+    # host ahead; otherwise the hold covers issuing every step.  A longer hold
+    # than needed costs: after a few ms of a near-idle GPU the timed steps'
+    # kernels ran up to 8 % slower than in the warm-up.
+    hold_cycles, hold_ms = 0, 0.0
+    if ms_per_cycle:
+        if host_ms < 0.5 * gpu_ms:
+            hold_ms = 3.0 * host_ms + 0.05
+        else:
+            hold_ms = min(2.0 * args.steps * host_ms + 2.0, 500.0)
         hold_cycles = int(hold_ms / ms_per_cycle)
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -612,6 +626,7 @@ def main():
         "warmup_s": round(warm_s, 3), "ms_per_step": round(ms_per_step, 5),
         "ms_median": round(median_ms, 5), "ms_min": round(step_ms[0], 5),
         "wall_ms_per_step": round(wall * 1000.0 / args.steps, 5), "host_ms_per_step": round(host_ms, 4),
+        "hold_ms": round(hold_ms, 3),
         "evict": mode,
         "sclk_mhz": {"before": clk_before, "after": clk_after},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
