@@ -1,12 +1,18 @@
 """Host code under the sanitizers (CPU only).
 
-Three programs under ``tests/host/`` are built with g++/gcc and run:
+Four programs under ``tests/host/`` are built with g++/gcc and run:
 
 * ``lookback_model.cpp`` (ThreadSanitizer): a thread-per-workgroup model of
   the segment look-back protocol (tickets, release/acquire flags, the
   fixed-shape walk over aggregates and inclusive states).  Checks that start
   states are bit-identical to a single-threaded walk and match the plain
   sequential chain; TSan reports any slot access the flags do not order.
+* ``dual_segments_model.cpp`` (ThreadSanitizer): a thread-per-workgroup
+  model of the segmented dual form's protocol (grouped tickets, started and
+  published flag bits, segment 0's end state, the claim of the last segment
+  by segment 0 or, failing that, segment n-2).  Checks every start state and
+  the final state against a sequential chain bit for bit, that exactly one
+  workgroup runs each last segment, and forces each claim path in turn.
 * ``abi_driver.cpp`` (AddressSanitizer + UndefinedBehaviorSanitizer): the
   C-ABI's validation (``csrc/api.cpp``) with stubbed launchers, called with
   valid and invalid arguments, extreme sizes and strides.
@@ -43,6 +49,16 @@ def test_lookback_protocol_under_tsan(tmp_path):
     out = build_and_run(tmp_path, ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=thread", "-pthread",
                                    os.path.join(HOST, "lookback_model.cpp")], tmp_path / "lookback_model")
     assert "0 failures" in out
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_dual_segment_protocol_under_tsan(tmp_path):
+    out = build_and_run(tmp_path, ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=thread", "-pthread",
+                                   os.path.join(HOST, "dual_segments_model.cpp")], tmp_path / "dual_segments_model")
+    assert "0 failures" in out
+    late = int(out.split("segment n-2 in ")[1].split(" late")[0])
+    early = int(out.split(" late, ")[1].split(" early")[0])
+    assert late > 0 and early == 0, "late runs take the second claim path, early runs the first"
 
 
 @pytest.mark.skipif(shutil.which("g++") is None or not os.path.exists(os.path.join(ROCM, "include", "hip")),
