@@ -249,7 +249,10 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             if (wq) rq[st][x] = *reinterpret_cast<const u32x4*>(Qc + (__mul24(rr, qL24) + pc_q[x]));
             rk[st][x] = *reinterpret_cast<const u32x4*>(Kc + (__mul24(rr, kL24) + pc_q[x]));
         }
-        rv[st] = *reinterpret_cast<const u32x4*>(Vc + (__mul24(min(row_v, lim), vL24) + pc_v));
+        // V rows are read by this workgroup alone (Q and K rows also by the
+        // other d_v tiles of the head, through L2), output rows are written
+        // once: both stream past the caches (non-temporal)
+        rv[st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vc + (__mul24(min(row_v, lim), vL24) + pc_v)));
         // (tokens past L get eta 0 when the chunk is written to LDS: a select
         // here would make the compiler wait for this load right away)
         re[st] = Eg ? (Eg + (int64_t)t0 * eL)[__mul24(min(tid % CS, lim), eL24)] : p.eta_scalar;
@@ -323,7 +326,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
         if (tid < NVC && row < prev_n) {
             const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[0][row * DVT + 8 * (ch ^ oswz<DVT>(row))]);
             bf16_t* Oc = Og + (int64_t)prev_base * oL;
-            *reinterpret_cast<u32x4*>(Oc + (__mul24(row, (int)oL) + 8 * ch)) = w;
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(Oc + (__mul24(row, (int)oL) + 8 * ch)));
         }
     };
 
@@ -847,7 +850,7 @@ __global__ __launch_bounds__(DVT / 16 * 128) void tcb_fwd_kernel(TcParams p) {
             if (tid < NVC && row < nn) {
                 const u32x4 w = *reinterpret_cast<const u32x4*>(&sO[ob][row * DVT + 8 * (ch ^ oswz<DVT>(row))]);
                 bf16_t* Oc = Og + (int64_t)base * oL;
-                *reinterpret_cast<u32x4*>(Oc + (__mul24(row, (int)oL) + 8 * ch)) = w;
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(Oc + (__mul24(row, (int)oL) + 8 * ch)));
             }
         };
         auto intra_p = [&](int cc, auto PAR) {
