@@ -386,16 +386,17 @@ def test_dual_large_minibatch(mb, L, segmented):
 
 @pytest.mark.parametrize("mb,L,B,H", [(16, 1000, 1, 2), (16, 4111, 1, 3), (48, 1003, 1, 2), (32, 1500, 2, 1),
                                       (64, 2500, 1, 2), (2048, 8192, 1, 2), (16, 2048, 3, 5),
-                                      (16, 2100, 3, 16), (48, 1000, 4, 25)])
+                                      (16, 2100, 3, 16), (48, 1000, 4, 25), (16, 1000, 2, 64)])
 def test_dual_segmented(mb, L, B, H):
     """The segmented form (each segment composes the affine maps of the
     segments before it): several segments per head, ragged last segments
     (L not a multiple of the segment, of 64 or of 16), one-step, per-step
     and stage-end mini-batch ends; against the oracle and against the one-
     chain form, with no look-back wait giving up.  The last two shapes have
-    more segments than the slots hold (48 sequences x 6 segments, 100 x 3),
-    so segment 0 hands on its end state and the last segments run on the CUs
-    it frees; 48 sequences take the per-XCD ticket groups, 100 one counter."""
+    more segments than the slots hold (48 sequences x 6 segments, 100 x 3,
+    128 x 3), so segment 0 hands on its end state and its workgroup goes on
+    to the last segment; 48 and 128 sequences take the per-XCD ticket
+    groups, 100 one counter."""
     inp = W.gen_dual(B=B, H=H, L=L, minibatch=mb)
     assert dual_segments(inp), "this shape should run in segments"
     say(f"dual segmented bf16 B{B} H{H} b{mb} L{L}")
