@@ -267,8 +267,11 @@ ttt_status_t ttt_chunk_state_scan(int32_t B, int32_t H, int32_t L, int32_t chunk
  * of at least ttt_dual_form_workspace_size bytes cuts every sequence into
  * segments of whole mini-batches that run concurrently: each segment
  * computes its (A - I, B) from K and V alone, composes the maps of the
- * segments before it onto W0 in order, then runs its own tokens.  The
- * result equals the one-chain result up to fp32 rounding (the composed
+ * segments before it onto W0 in order, then runs its own tokens.  When
+ * that yields one more segment than the GPU holds at once, segment 0
+ * instead runs only its tokens and hands on its end state, onto which the
+ * later segments compose, and its workgroup then runs the last segment.
+ * The result equals the one-chain result up to fp32 rounding (the composed
  * start states are not bit-identical to the chained ones; repeated calls
  * are).  workspace NULL runs each sequence as one chain; a non-NULL
  * workspace smaller than needed is TTT_ERR_WORKSPACE.  The waits between
