@@ -23,13 +23,20 @@
 // F(i-j) eta_j (q_i . k_j)(do_i . v_j) and three weighted K^T V aggregates.
 // Every column of the three states evolves on its own (column c only meets
 // column c of v and do), so a wave owns 16 state columns of one (b, h) and
-// walks the sequence in 16-token blocks; the per-wave sums are added up in a
-// fixed order by a second kernel (deterministic).
+// walks the sequence in 16-token blocks.  The readouts and the scores are
+// contractions over the state rows (features) and dL/dbeta is linear in
+// them, so the rows split further: a wave holds a slice of 32 rows of its 16
+// columns and adds its slice's share; with d_k = 128 four waves cover a
+// column tile, which fills the chip at a few heads (one wave of all 128 rows
+// per tile left three SIMDs in four idle at the momentum workload).  The
+// per-wave sums are added up in a fixed order by a second kernel
+// (deterministic).
 //
 // Data path: a wave-private ring of 32-token stages in LDS filled by 16-byte
-// direct loads (no VGPR holds data in flight): Q and K rows [32][dk] with the
-// 16-byte units of row r rotated by XOR with r (bank-conflict-free row
-// fragments), the wave's V and dO tiles [32][16] and 32 per-token rates.
+// direct loads (no VGPR holds data in flight): the wave's slice of the Q and K
+// rows [32][32] with the 16-byte units of row r rotated by XOR with r
+// (bank-conflict-free row fragments), its V and dO tiles [32][16] and 32
+// per-token rates.
 // Rows past L load as zero: their q, do and eta are zero, so they add
 // nothing; the last block takes its own length n in the state update.
 #include "common.h"
@@ -79,25 +86,31 @@ struct DbGeo {
     static constexpr int NQ = QKB / 1024, NV = VB / 1024;  // load instructions per part
     static constexpr int STAGE = 2 * QKB + 2 * VB + 256;   // + 64 rates (32 used)
     static constexpr int NL = 2 * NQ + 2 * NV + 1;         // load instructions per stage
-    static constexpr int R = (2 + 63 / NL) < 8 ? (2 + 63 / NL) : 8;   // ring stages
+    // ring stages: as deep as vmcnt counts, and small enough for four
+    // single-wave workgroups per CU (40 KB each)
+    static constexpr int RV = (2 + 63 / NL) < 8 ? (2 + 63 / NL) : 8;
+    static constexpr int R = RV * STAGE <= 40 * 1024 ? RV : 40 * 1024 / STAGE;
     static_assert(QKB % 1024 == 0 && VB % 1024 == 0, "whole 1 KB loads");
     static_assert((R - 2) * NL <= 63 && R >= 3, "vmcnt holds 6 bits");
-    static_assert(R * STAGE <= 150 * 1024, "ring fits the LDS");
 };
 
-template <typename T, int DK>
+// DK: the rows of this wave's slice; NSL slices make the head's d_k
+template <typename T, int DK, int NSL>
 __global__ __launch_bounds__(64) void dbeta_kernel(DbetaParams p) {
     using G = DbGeo<T, DK>;
     constexpr bool BF = sizeof(T) == 2;
+    constexpr int ROWG = DK * NSL * G::ESZ;   // bytes per Q/K row in memory
     __shared__ __attribute__((aligned(16))) char ring[G::R * G::STAGE];
 
     const int lane = threadIdx.x, g = lane >> 4, c16 = lane & 15;
     const int ntile = p.dv / 16;
-    const int lid = xcd_logical(blockIdx.x, gridDim.x);   // the column tiles of a head on one XCD
-    const int bh = lid / ntile, w = lid % ntile;
+    // the column tiles and row slices of a head on one XCD
+    const int lid = xcd_logical(blockIdx.x, gridDim.x);
+    const int bh = lid / (ntile * NSL), w = (lid / NSL) % ntile, sl = lid % NSL;
+    const int row0 = DK * sl;   // first state row of this slice
     const int L = p.L, DV = p.dv;
-    const char* Qg = reinterpret_cast<const char*>(p.q) + (int64_t)bh * L * DK * G::ESZ;
-    const char* Kg = reinterpret_cast<const char*>(p.k) + (int64_t)bh * L * DK * G::ESZ;
+    const char* Qg = reinterpret_cast<const char*>(p.q) + ((int64_t)bh * L * DK * NSL + row0) * G::ESZ;
+    const char* Kg = reinterpret_cast<const char*>(p.k) + ((int64_t)bh * L * DK * NSL + row0) * G::ESZ;
     const char* Vg = reinterpret_cast<const char*>(p.v) + ((int64_t)bh * L * DV + 16 * w) * G::ESZ;
     const char* Dg = reinterpret_cast<const char*>(p.dout) + ((int64_t)bh * L * DV + 16 * w) * G::ESZ;
     const float* Eg = p.eta ? p.eta + (int64_t)bh * L : nullptr;
@@ -111,14 +124,16 @@ __global__ __launch_bounds__(64) void dbeta_kernel(DbetaParams p) {
         Tt[t] = zero4();
         M[t] = zero4();
         if (p.M0) {
-            const float* m0 = p.M0 + (int64_t)bh * DK * DV + (int64_t)(16 * t + 4 * g) * DV + 16 * w + c16;
+            const float* m0 = p.M0 + (int64_t)bh * DK * NSL * DV + (int64_t)(row0 + 16 * t + 4 * g) * DV + 16 * w + c16;
 #pragma unroll
             for (int r = 0; r < 4; ++r) M[t][r] = m0[(int64_t)r * DV];
         }
     }
 
-    const __amdgpu_buffer_rsrc_t rQ = __builtin_amdgcn_make_buffer_rsrc((void*)Qg, 0, L * G::ROWB, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, L * G::ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rQ =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Qg, 0, L * ROWG - row0 * G::ESZ, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rK =
+        __builtin_amdgcn_make_buffer_rsrc((void*)Kg, 0, L * ROWG - row0 * G::ESZ, 0x00020000);
     const __amdgpu_buffer_rsrc_t rV =
         __builtin_amdgcn_make_buffer_rsrc((void*)Vg, 0, (L * DV - 16 * w) * G::ESZ, 0x00020000);
     const __amdgpu_buffer_rsrc_t rD =
@@ -127,12 +142,13 @@ __global__ __launch_bounds__(64) void dbeta_kernel(DbetaParams p) {
     const __amdgpu_buffer_rsrc_t rE =
         __builtin_amdgcn_make_buffer_rsrc(Eg ? (void*)Eg : (void*)Qg, 0, Eg ? L * 4 : 0, 0x00020000);
 
-    // direct-load lane offsets (bytes from the stage's first token row)
+    // direct-load lane offsets (bytes from the stage's first token row): LDS
+    // slot (row, pos) of the slice holds its unit pos ^ (row % U)
     uint32_t qko[G::NQ], vdo[G::NV];
 #pragma unroll
     for (int i = 0; i < G::NQ; ++i) {
         const int o = 1024 * i + 16 * lane, row = o / G::ROWB, pos = (o % G::ROWB) / 16;
-        qko[i] = (uint32_t)(row * G::ROWB + 16 * (pos ^ (row % G::U)));
+        qko[i] = (uint32_t)(row * ROWG + 16 * (pos ^ (row % G::U)));
     }
 #pragma unroll
     for (int i = 0; i < G::NV; ++i) {
@@ -143,9 +159,9 @@ __global__ __launch_bounds__(64) void dbeta_kernel(DbetaParams p) {
     auto issue = [&](int s, char* dst) __attribute__((always_inline)) {
         const int sc = min(s, nst - 1) * DB_T;   // first token of the stage
 #pragma unroll
-        for (int i = 0; i < G::NQ; ++i) dma_b128(rQ, dst + 1024 * i, qko[i], sc * G::ROWB);
+        for (int i = 0; i < G::NQ; ++i) dma_b128(rQ, dst + 1024 * i, qko[i], sc * ROWG);
 #pragma unroll
-        for (int i = 0; i < G::NQ; ++i) dma_b128(rK, dst + G::QKB + 1024 * i, qko[i], sc * G::ROWB);
+        for (int i = 0; i < G::NQ; ++i) dma_b128(rK, dst + G::QKB + 1024 * i, qko[i], sc * ROWG);
 #pragma unroll
         for (int i = 0; i < G::NV; ++i) dma_b128(rV, dst + 2 * G::QKB + 1024 * i, vdo[i], sc * DV * G::ESZ);
 #pragma unroll
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(64) void dbeta_kernel(DbetaParams p) {
     // boundary terms <dS_final, S'_{L-1}> + <dM_final, m'_{L-1}>
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        const int64_t o = (int64_t)bh * DK * DV + (int64_t)(16 * t + 4 * g) * DV + 16 * w + c16;
+        const int64_t o = (int64_t)bh * DK * NSL * DV + (int64_t)(row0 + 16 * t + 4 * g) * DV + 16 * w + c16;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             if (p.dS_final) acc += p.dS_final[o + (int64_t)r * DV] * Tt[t][r];
@@ -344,7 +360,8 @@ bool dbeta_supported(int dtype, int dk, int dv) {
            dv <= 1024;
 }
 
-size_t dbeta_workspace(int B, int H, int dv) { return (size_t)B * H * (dv / 16) * sizeof(float); }
+// one partial sum per wave: up to 4 row slices per column tile
+size_t dbeta_workspace(int B, int H, int dv) { return (size_t)B * H * (dv / 16) * 4 * sizeof(float); }
 
 // weight tables in fp64 (sums, no closed forms: exact for beta near 1 too)
 static void dbeta_tables(double beta, DbetaParams& p) {
@@ -376,22 +393,24 @@ static void dbeta_tables(double beta, DbetaParams& p) {
 hipError_t launch_dbeta(DbetaParams p, int dtype, float beta, hipStream_t s) {
     if (!dbeta_supported(dtype, p.dk, p.dv)) return hipErrorInvalidValue;
     dbeta_tables(beta, p);
-    const int ntile = p.dv / 16, nbh = p.B * p.H;
-    const dim3 grid(nbh * ntile);
-#define DB_LAUNCH(T, DK) hipLaunchKernelGGL((dbeta_kernel<T, DK>), grid, dim3(64), 0, s, p)
+    // row slices of 32: one wave per (head, column tile, slice)
+    const int nsl = p.dk / 32, ntile = p.dv / 16, nbh = p.B * p.H;
+    const dim3 grid(nbh * ntile * nsl);
+#define DB_LAUNCH(T, NSL) hipLaunchKernelGGL((dbeta_kernel<T, 32, NSL>), grid, dim3(64), 0, s, p)
     if (dtype == 1) {
-        if (p.dk == 32) DB_LAUNCH(bf16_t, 32);
-        else if (p.dk == 64) DB_LAUNCH(bf16_t, 64);
-        else DB_LAUNCH(bf16_t, 128);
+        if (nsl == 1) DB_LAUNCH(bf16_t, 1);
+        else if (nsl == 2) DB_LAUNCH(bf16_t, 2);
+        else DB_LAUNCH(bf16_t, 4);
     } else {
-        if (p.dk == 32) DB_LAUNCH(float, 32);
-        else if (p.dk == 64) DB_LAUNCH(float, 64);
-        else DB_LAUNCH(float, 128);
+        if (nsl == 1) DB_LAUNCH(float, 1);
+        else if (nsl == 2) DB_LAUNCH(float, 2);
+        else DB_LAUNCH(float, 4);
     }
 #undef DB_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dbeta_finish_kernel, dim3((nbh + 255) / 256), dim3(256), 0, s, p.partial, ntile, nbh, p.dbeta);
+    hipLaunchKernelGGL(dbeta_finish_kernel, dim3((nbh + 255) / 256), dim3(256), 0, s, p.partial, ntile * nsl, nbh,
+                       p.dbeta);
     return hipGetLastError();
 }
 

@@ -65,7 +65,7 @@ bool dbeta_supported(int dtype, int dk, int dv) {
     return (dtype == 0 || dtype == 1) && (dk == 32 || dk == 64 || dk == 128) && dv % 16 == 0 && dv >= 16 &&
            dv <= 1024;
 }
-size_t dbeta_workspace(int B, int H, int dv) { return (size_t)B * H * (dv / 16) * 4; }
+size_t dbeta_workspace(int B, int H, int dv) { return (size_t)B * H * (dv / 16) * 4 * 4; }
 hipError_t launch_dbeta(DbetaParams, int, float, hipStream_t) { return hipSuccess; }
 bool fe_gemm_supported(int K, int rows) { return K % 128 == 0 && rows % 128 == 0; }
 hipError_t launch_fe_gemm(const FeGemmParams&, bool, hipStream_t) { return hipSuccess; }

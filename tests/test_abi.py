@@ -338,7 +338,7 @@ def test_dbeta_rejects_before_launch(lib):
                 ctypes.c_void_p(kw.get("q", base[0])), ctypes.c_void_p(base[1]), ctypes.c_void_p(base[2]), None,
                 ctypes.c_float(0.1), ctypes.c_float(kw.get("beta", 0.9)), None, ctypes.c_void_p(base[3]), None, None,
                 ctypes.c_void_p(kw.get("dbeta", base[4])), ctypes.c_void_p(kw.get("ws", base[5])),
-                ctypes.c_size_t(kw.get("wsb", 64)), None]
+                ctypes.c_size_t(kw.get("wsb", 256)), None]
     assert f(*args(dtype=4)) == ERR_DTYPE
     assert f(*args(beta=1.0)) == ERR_VALUE
     assert f(*args(beta=-0.5)) == ERR_VALUE
@@ -351,7 +351,8 @@ def test_dbeta_rejects_before_launch(lib):
     assert f(*args(dbeta=FAKE + 256)) == ERR_ALIAS        # output inside q
     assert f(*args(ws=FAKE + 4 * (n + 4096))) == ERR_ALIAS   # workspace on top of dbeta
     ws = ctypes.c_size_t(0)
-    assert lib.ttt_bwd_dbeta_workspace_size(2, 2, 64, ctypes.byref(ws)) == OK and ws.value == 2 * 2 * 4 * 4
+    # one fp32 partial per (head, 16-column tile, 32-row slice), up to 4 slices
+    assert lib.ttt_bwd_dbeta_workspace_size(2, 2, 64, ctypes.byref(ws)) == OK and ws.value == 2 * 2 * 4 * 4 * 4
     assert lib.ttt_bwd_dbeta_workspace_size(2, 2, 64, None) == ERR_NULL
 
 
